@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the gated delta rule workloads.
+
+This module draws random numbers and rounds them to the storage dtype; it holds
+none of the recurrence's arithmetic.  Both the fp64 oracle and the GPU library
+consume the values produced here: the oracle gets them exactly upcast to fp64,
+the GPU gets the identical bf16 / fp32 bit patterns.
+
+Workloads (the mlx-lm PR's "Numerical correctness" toy shape and its
+"Performance" table's Qwen3.5-9B GatedDeltaNet shape; the rest are the edge,
+masking and decode sweeps of the same operation):
+
+  tiny         B=1  T=8    Hk=2  Hv=4  Dk=16  Dv=8    fp32  seed 1
+  9b_t256      B=1  T=256  Hk=16 Hv=64 Dk=192 Dv=128  bf16  seed 2
+  9b_t2048     B=1  T=2048 Hk=16 Hv=64 Dk=192 Dv=128  bf16  seed 3
+  edge         B=4  T in {1,64,65,1024} Hk=4 Hv=8 Dk=64 Dv=32  fp32  seed 4000+T
+  decode       B=64 T=64 (one step per call) Hk=16 Hv=32 Dk=Dv=128 bf16 seed 5
+
+Distributions: q, k, v, a, b ~ N(0,1); A_log ~ U(0, ln 16); dt_bias ~ N(0, 0.5);
+state0 ~ N(0, 0.1) (zeros for the 9B shape); dO ~ N(0,1); dS_final ~ N(0,1)
+where present.  The second argument of N is the standard deviation.  Draw
+order: q, k, v, a, b, A_log, dt_bias, state0, dO, dS_final (numpy PCG64).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+DTYPES = ("f32", "bf16")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even);
+    returns the uint16 bit patterns.  Inputs here are finite."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f32_bits_roundtrip(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+@dataclass
+class Case:
+    """One workload: dims, storage dtype, and the input / cotangent values.
+
+    ``vals`` holds float64 arrays whose values are exactly representable in the
+    storage dtype; ``store(name)`` returns the array to upload (float32, or the
+    uint16 bf16 bit pattern for bf16 tensors)."""
+    name: str
+    B: int
+    T: int
+    Hk: int
+    Hv: int
+    Dk: int
+    Dv: int
+    dtype: str
+    vals: dict = field(default_factory=dict)
+    mask: np.ndarray | None = None
+
+    # tensors that use the input dtype; the rest (A_log, dt_bias, state0,
+    # dS_final) are always fp32
+    IO = ("q", "k", "v", "a", "b", "dO")
+
+    @property
+    def G(self) -> int:
+        return self.Hv // self.Hk
+
+    def store(self, name: str) -> np.ndarray | None:
+        x = self.vals.get(name)
+        if x is None:
+            return None
+        if name in self.IO and self.dtype == "bf16":
+            return f32_to_bf16_bits(x.astype(np.float32))
+        return x.astype(np.float32)
+
+    def oracle_args(self):
+        v = self.vals
+        return (v["q"], v["k"], v["v"], v["a"], v["b"], v["A_log"], v["dt_bias"],
+                v.get("state0"), self.mask)
+
+
+def _round(x: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = np.asarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(f32_to_bf16_bits(x32))
+    return x32.astype(np.float64)
+
+
+def make_case(name: str, B: int, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
+              dtype: str, seed: int, *, state_std: float | None = 0.1,
+              dS_final: bool = True, mask: np.ndarray | None = None,
+              extreme: bool = False) -> Case:
+    """Draw one workload.  ``extreme`` sets A_log = 5 and a = 15 everywhere
+    (after the draws, so the other tensors are unchanged)."""
+    assert dtype in DTYPES and Hv % Hk == 0
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = Case(name, B, T, Hk, Hv, Dk, Dv, dtype)
+    v = c.vals
+    v["q"] = _round(rng.standard_normal((B, T, Hk, Dk)), dtype)
+    v["k"] = _round(rng.standard_normal((B, T, Hk, Dk)), dtype)
+    v["v"] = _round(rng.standard_normal((B, T, Hv, Dv)), dtype)
+    v["a"] = _round(rng.standard_normal((B, T, Hv)), dtype)
+    v["b"] = _round(rng.standard_normal((B, T, Hv)), dtype)
+    v["A_log"] = _round(rng.uniform(0.0, math.log(16.0), (Hv,)), "f32")
+    v["dt_bias"] = _round(0.5 * rng.standard_normal((Hv,)), "f32")
+    if state_std is not None:
+        v["state0"] = _round(state_std * rng.standard_normal((B, Hv, Dk, Dv)), "f32")
+    v["dO"] = _round(rng.standard_normal((B, T, Hv, Dv)), dtype)
+    if dS_final:
+        v["dS_final"] = _round(rng.standard_normal((B, Hv, Dk, Dv)), "f32")
+    if extreme:
+        v["A_log"] = np.full((Hv,), 5.0)
+        v["a"] = np.full((B, T, Hv), 15.0)
+    if mask is not None:
+        c.mask = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+        assert c.mask.shape == (B, T)
+    return c
+
+
+def tiny() -> Case:
+    return make_case("tiny", 1, 8, 2, 4, 16, 8, "f32", 1)
+
+
+def qwen35_9b(T: int = 2048) -> Case:
+    seed = {256: 2, 2048: 3}.get(T, 3000 + T)
+    return make_case("9b_t%d" % T, 1, T, 16, 64, 192, 128, "bf16", seed,
+                     state_std=None, dS_final=False)
+
+
+def edge_mask(B: int, T: int) -> np.ndarray:
+    """Rows 0 and 2 all valid; rows 1 and 3 valid only for t < floor(T/2)."""
+    m = np.ones((B, T), dtype=np.uint8)
+    for r in range(1, B, 2):
+        m[r, T // 2:] = 0
+    return m
+
+
+def edge(T: int, *, masked: bool = True, extreme: bool = False) -> Case:
+    B = 4
+    name = "edge_T%d%s%s" % (T, "_mask" if masked else "", "_extreme" if extreme else "")
+    return make_case(name, B, T, 4, 8, 64, 32, "f32", 4000 + T,
+                     mask=edge_mask(B, T) if masked else None, extreme=extreme)
+
+
+def decode(steps: int = 64) -> Case:
+    """The decode workload as one [B, steps] draw; call i uses column t = i."""
+    return make_case("decode", 64, steps, 16, 32, 128, 128, "bf16", 5,
+                     dS_final=False)
+
+
+def by_name(name: str) -> Case:
+    if name == "tiny":
+        return tiny()
+    if name.startswith("9b_t"):
+        return qwen35_9b(int(name[4:]))
+    if name == "decode":
+        return decode()
+    raise KeyError(name)
