@@ -1,0 +1,130 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library (libgdn.so).
+ *
+ * The operation (mlx-lm PR "Add gated_delta_update VJP -- trainable
+ * GatedDeltaNet on Apple Silicon", section "What this PR adds": a drop-in
+ * gated_delta_update_vjp(q, k, v, a, b, A_log, dt_bias, state, mask) with a
+ * VJP for every primal argument; torch-to-nnef GDN page, "Op contract": the
+ * tensor layouts, GQA head mapping and q/k normalisation):
+ *
+ *   value head h reads query/key head j = h / G, G = Hv / Hk;
+ *   qn = q / sqrt(|q|^2 + 1e-6) / sqrt(Dk),  kn = k / sqrt(|k|^2 + 1e-6);
+ *   x = a + dt_bias[h],  l = -exp(A_log[h]) * softplus(min(x, 20)),
+ *   g = exp(l),  beta = sigmoid(b);
+ *   valid step:  S <- g S;  delta = beta (v - S^T kn);  S <- S + kn delta^T;
+ *   every step:  o = S^T qn   (a masked step leaves S unchanged).
+ *
+ * S is the per-(batch, value head) state, Dk x Dv, fp32.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to dense row-major tensors with
+ *    the layouts given below.  The caller owns all memory: the library never
+ *    allocates or frees device memory and keeps no state between calls.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream): they validate, enqueue kernels and return.  No host sync.
+ *  - All arguments are validated before anything is enqueued; on a non-zero
+ *    return nothing was enqueued (except GDN_ERR_HIP, where a launch failed).
+ *  - q, k, v, a, b, o, dO, dq, dk, dv, da, db use `dtype`; A_log, dt_bias,
+ *    the states, the checkpoints, dstate, dA_log and ddt_bias are fp32.
+ *  - NaN / Inf inputs propagate; nothing traps.
+ *  - Results are deterministic: repeated calls with the same inputs produce
+ *    identical bits (no atomics; every sum runs in a fixed order).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Steps per state checkpoint (PR, "Why chunked instead of single-shot?":
+ * CHUNK_SIZE = 64). */
+#define GDN_CHUNK 64
+
+enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = 1, /* bad dims, NULL required pointer, bad alias   */
+  GDN_ERR_UNSUPPORTED = 2, /* Dk / Dv / dtype / algo not built             */
+  GDN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required      */
+  GDN_ERR_HIP = 4          /* a HIP launch failed                          */
+};
+
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
+
+/* Kernel family.  AUTO picks the chunked MFMA form where it is built for the
+ * shape and dtype, else the sequential scan.  Both produce the same
+ * checkpoint layout, so a checkpoint from one can be used by the other. */
+enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SCAN = 1, GDN_ALGO_CHUNK = 2 };
+
+typedef struct gdn_dims {
+  int64_t B, T, Hk, Hv, Dk, Dv; /* T >= 0; Hv % Hk == 0                     */
+  int32_t dtype;                /* enum gdn_dtype                           */
+  int32_t algo;                 /* enum gdn_algo                            */
+} gdn_dims;
+
+/* Supported sizes: Dk in {16, 32, 64, 128, 192, 256}; Dv a multiple of 8
+ * with Dv <= 256 and (Dv <= 24 or Dv % 32 == 0). */
+
+/* Number of fp32 elements of the checkpoint buffer:
+ * (ceil(T/64) - 1) * B * Hv * Dk * Dv  (0 when T <= 64). */
+int gdn_ckpt_elems(const gdn_dims* d, size_t* out);
+
+/* Device workspace bytes needed by gdn_fwd / gdn_bwd for these dims. */
+int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out);
+int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
+
+/*
+ * Forward scan.
+ *   q, k     [B,T,Hk,Dk] dtype        v  [B,T,Hv,Dv] dtype
+ *   a, b     [B,T,Hv]    dtype        A_log, dt_bias [Hv] fp32
+ *   state0   [B,Hv,Dk,Dv] fp32, NULL = zeros
+ *   mask     [B,T] uint8, nonzero = valid step; NULL = all valid
+ *   o        [B,T,Hv,Dv] dtype (out)
+ *   state_out[B,Hv,Dk,Dv] fp32 (out); may alias state0 exactly (in-place
+ *            decode); no other overlap between outputs and inputs is allowed
+ *   ckpt     [ceil(T/64)-1, B,Hv,Dk,Dv] fp32 (out): ckpt[c-1] = state before
+ *            step 64c.  NULL = not written (inference).  Required by gdn_bwd.
+ *   ws       device workspace of at least gdn_fwd_workspace_bytes()
+ */
+int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v,
+            const void* a, const void* b, const float* A_log,
+            const float* dt_bias, const float* state0, const uint8_t* mask,
+            void* o, float* state_out, float* ckpt, void* ws, size_t ws_bytes,
+            void* stream);
+
+/*
+ * VJP of gdn_fwd (reverse sweep; PR "Design notes": chunk-wise recompute from
+ * the checkpoints, deterministic reductions without atomics).
+ *   q ... mask    the inputs given to gdn_fwd (same values)
+ *   ckpt          the checkpoints gdn_fwd wrote for those inputs (may be NULL
+ *                 only when T <= 64)
+ *   dO            [B,T,Hv,Dv] dtype, cotangent of o
+ *   dS_final      [B,Hv,Dk,Dv] fp32, cotangent of state_out; NULL = zeros
+ *   dq, dk        [B,T,Hk,Dk] dtype (out)     dv [B,T,Hv,Dv] dtype (out)
+ *   da, db        [B,T,Hv] dtype (out)        dA_log, ddt_bias [Hv] fp32 (out)
+ *   dstate        [B,Hv,Dk,Dv] fp32 (out), cotangent of state0
+ * Gradients are overwritten, not accumulated.  The mask gets no gradient;
+ * masked steps get dv = da = db = 0.
+ */
+int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v,
+            const void* a, const void* b, const float* A_log,
+            const float* dt_bias, const float* state0, const uint8_t* mask,
+            const float* ckpt, const void* dO, const float* dS_final, void* dq,
+            void* dk, void* dv, void* da, void* db, float* dA_log,
+            float* ddt_bias, float* dstate, void* ws, size_t ws_bytes,
+            void* stream);
+
+/* Static description of a status code. */
+const char* gdn_status_string(int status);
+
+/* Library version string. */
+const char* gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

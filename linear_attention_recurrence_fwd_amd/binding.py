@@ -1,0 +1,213 @@
+"""ctypes binding of libgdn.so (the C ABI in include/gdn.h).
+
+Argument marshalling only: this module checks dtypes/shapes, allocates the
+outputs and the workspace with torch (device memory), and passes raw pointers
+plus the current HIP stream to the library.  Every step of the computation runs
+in the library's kernels.  There is no fallback: if libgdn.so is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+CHUNK = 64
+
+GDN_F32, GDN_BF16 = 0, 1
+ALGO_AUTO, ALGO_SCAN, ALGO_CHUNK = 0, 1, 2
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
+          3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
+
+# every entry point declared in include/gdn.h
+EXPORTS = ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
+           "gdn_fwd", "gdn_bwd", "gdn_status_string", "gdn_version")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("Hk", ctypes.c_int64),
+                ("Hv", ctypes.c_int64), ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("algo", ctypes.c_int32)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(code, code),
+                                                 lib().gdn_status_string(code).decode()))
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn.so not built (run __graft_entry__.build()): %s" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        PD = ctypes.POINTER(Dims)
+        for n in ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes"):
+            getattr(L, n).argtypes = [PD, ctypes.POINTER(S)]
+            getattr(L, n).restype = ctypes.c_int
+        L.gdn_fwd.argtypes = [PD] + [P] * 13 + [S, P]
+        L.gdn_fwd.restype = ctypes.c_int
+        L.gdn_bwd.argtypes = [PD] + [P] * 21 + [S, P]
+        L.gdn_bwd.restype = ctypes.c_int
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_version.argtypes = []
+        L.gdn_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def make_dims(B, T, Hk, Hv, Dk, Dv, dtype, algo=ALGO_AUTO) -> Dims:
+    dt = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}.get(dtype, dtype)
+    return Dims(B, T, Hk, Hv, Dk, Dv, dt, algo)
+
+
+def _query(fn, d: Dims) -> int:
+    out = ctypes.c_size_t(0)
+    rc = getattr(lib(), fn)(ctypes.byref(d), ctypes.byref(out))
+    if rc:
+        raise GdnError(fn, rc)
+    return out.value
+
+
+def ckpt_elems(d: Dims) -> int:
+    return _query("gdn_ckpt_elems", d)
+
+
+def fwd_workspace_bytes(d: Dims) -> int:
+    return _query("gdn_fwd_workspace_bytes", d)
+
+
+def bwd_workspace_bytes(d: Dims) -> int:
+    return _query("gdn_bwd_workspace_bytes", d)
+
+
+def _p(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _check(x, name, shape, dtype, device):
+    if x.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, x.dtype))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(x.shape)))
+    if x.device != device:
+        raise ValueError("%s: expected device %s, got %s" % (name, device, x.device))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dims_of(q, v, algo):
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    return make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, algo)
+
+
+def _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask):
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("gdn runs on the GPU; got device %s" % dev)
+    B, T, Hk, Hv, Dk, Dv = d.B, d.T, d.Hk, d.Hv, d.Dk, d.Dv
+    _check(q, "q", (B, T, Hk, Dk), dt, dev)
+    _check(k, "k", (B, T, Hk, Dk), dt, dev)
+    _check(v, "v", (B, T, Hv, Dv), dt, dev)
+    _check(a, "a", (B, T, Hv), dt, dev)
+    _check(b, "b", (B, T, Hv), dt, dev)
+    _check(A_log, "A_log", (Hv,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32, dev)
+    if state0 is not None:
+        _check(state0, "state0", (B, Hv, Dk, Dv), torch.float32, dev)
+    if mask is not None:
+        _check(mask, "mask", (B, T), torch.uint8, dev)
+
+
+def fwd(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, need_ckpt=True,
+        state_out=None, algo=ALGO_AUTO):
+    """Forward scan.  Returns (o, state_out, ckpt); ckpt is None when not
+    requested.  Pass state_out=state0 for an in-place state update."""
+    d = _dims_of(q, v, algo)
+    _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask)
+    dev = q.device
+    o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
+    if state_out is None:
+        state_out = torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+    else:
+        _check(state_out, "state_out", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
+    nck = ckpt_elems(d)
+    ckpt = None
+    if need_ckpt:
+        nslab = max((d.T + CHUNK - 1) // CHUNK - 1, 0)
+        ckpt = torch.empty((nslab, d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+    wsb = fwd_workspace_bytes(d)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_fwd(ctypes.byref(d), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log), _p(dt_bias),
+                       _p(state0), _p(mask), _p(o), _p(state_out),
+                       _p(ckpt) if (ckpt is not None and nck) else None,
+                       _p(ws), wsb, _stream(dev))
+    if rc:
+        raise GdnError("gdn_fwd", rc)
+    return o, state_out, ckpt
+
+
+def bwd(q, k, v, a, b, A_log, dt_bias, state0, mask, ckpt, dO, dS_final=None, *,
+        algo=ALGO_AUTO):
+    """VJP.  Returns dict(dq, dk, dv, da, db, dA_log, ddt_bias, dstate)."""
+    d = _dims_of(q, v, algo)
+    _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask)
+    dev = q.device
+    _check(dO, "dO", (d.B, d.T, d.Hv, d.Dv), q.dtype, dev)
+    if dS_final is not None:
+        _check(dS_final, "dS_final", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
+    nck = ckpt_elems(d)
+    if nck:
+        if ckpt is None or ckpt.numel() != nck:
+            raise ValueError("ckpt from gdn_fwd with %d elements is required" % nck)
+        if ckpt.dtype != torch.float32 or not ckpt.is_contiguous() or ckpt.device != dev:
+            raise ValueError("ckpt must be a contiguous fp32 tensor on %s" % dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               da=torch.empty_like(a), db=torch.empty_like(b),
+               dA_log=torch.empty((d.Hv,), dtype=torch.float32, device=dev),
+               ddt_bias=torch.empty((d.Hv,), dtype=torch.float32, device=dev),
+               dstate=torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev))
+    wsb = bwd_workspace_bytes(d)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_bwd(ctypes.byref(d), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log), _p(dt_bias),
+                       _p(state0), _p(mask), _p(ckpt) if nck else None, _p(dO), _p(dS_final),
+                       *[_p(out[n]) for n in ("dq", "dk", "dv", "da", "db", "dA_log", "ddt_bias",
+                                              "dstate")],
+                       _p(ws), wsb, _stream(dev))
+    if rc:
+        raise GdnError("gdn_bwd", rc)
+    return out
+
+
+class GatedDeltaRule(torch.autograd.Function):
+    """Autograd wrapper: forward returns (o, state_out); backward calls gdn_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, a, b, A_log, dt_bias, state0, mask=None):
+        o, st, ck = fwd(q, k, v, a, b, A_log, dt_bias, state0, mask)
+        ctx.save_for_backward(q, k, v, a, b, A_log, dt_bias, state0, mask, ck)
+        return o, st
+
+    @staticmethod
+    def backward(ctx, dO, dS):
+        q, k, v, a, b, A_log, dt_bias, state0, mask, ck = ctx.saved_tensors
+        g = bwd(q, k, v, a, b, A_log, dt_bias, state0, mask, ck, dO.contiguous(),
+                None if dS is None else dS.contiguous())
+        return (g["dq"], g["dk"], g["dv"], g["da"], g["db"], g["dA_log"], g["ddt_bias"],
+                g["dstate"] if state0 is not None else None, None)

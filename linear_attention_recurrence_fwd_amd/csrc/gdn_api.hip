@@ -1,0 +1,185 @@
+// C ABI of libgdn.so (declared in include/gdn.h): argument validation,
+// workspace layout, kernel selection and launch.  No allocation, no host sync.
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+#include <limits.h>
+
+namespace {
+
+using gdn::Dims;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t rq, rk, kq, ell, beta;                 // prep scalars
+  size_t U, E, dHend, pdA, pdt;                 // backward only
+  size_t total;
+};
+
+Layout layout(const Dims& d, bool bwd) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t nfloat) {
+    size_t o = off;
+    off += align_up(nfloat * sizeof(float));
+    return o;
+  };
+  const size_t bt = static_cast<size_t>(d.B) * d.T;
+  L.rq = take(bt * d.Hk);
+  L.rk = take(bt * d.Hk);
+  L.kq = take(bt * d.Hk);
+  L.ell = take(bt * d.Hv);
+  L.beta = take(bt * d.Hv);
+  if (bwd) {
+    const size_t nc = d.nchunk();
+    const size_t col = bt * d.Hv * d.Dv;
+    L.U = take(col);
+    L.E = take(col);
+    L.dHend = take(nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv);
+    L.pdA = take(2 * static_cast<size_t>(d.B) * nc * d.Hv);  // fp64
+    L.pdt = take(2 * static_cast<size_t>(d.B) * nc * d.Hv);
+  }
+  L.total = off;
+  return L;
+}
+
+// Checks everything that does not depend on pointers.
+int check_dims(const gdn_dims* p, Dims* out) {
+  if (!p) return GDN_ERR_INVALID_ARG;
+  if (p->B < 1 || p->T < 0 || p->Hk < 1 || p->Hv < 1 || p->Dk < 1 || p->Dv < 1)
+    return GDN_ERR_INVALID_ARG;
+  if (p->Hv % p->Hk != 0) return GDN_ERR_INVALID_ARG;
+  if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (p->algo != GDN_ALGO_AUTO && p->algo != GDN_ALGO_SCAN && p->algo != GDN_ALGO_CHUNK)
+    return GDN_ERR_INVALID_ARG;
+  if (p->algo == GDN_ALGO_CHUNK) return GDN_ERR_UNSUPPORTED;
+  if (!gdn::scan_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv)))
+    return GDN_ERR_UNSUPPORTED;
+  // every tensor's element count (and the checkpoint slab count) fits in int32
+  const double big = static_cast<double>(INT_MAX);
+  const double bt = static_cast<double>(p->B) * p->T;
+  const double nc = static_cast<double>((p->T + 63) / 64);
+  if (bt * p->Hv * p->Dv > big || bt * p->Hk * p->Dk > big ||
+      nc * p->B * p->Hv * p->Dk * p->Dv > big || static_cast<double>(p->B) * p->Hv > 65535.0 * 1024)
+    return GDN_ERR_UNSUPPORTED;
+  *out = Dims{static_cast<int>(p->B), static_cast<int>(p->T), static_cast<int>(p->Hk),
+              static_cast<int>(p->Hv), static_cast<int>(p->Dk), static_cast<int>(p->Dv)};
+  return GDN_OK;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+gdn::StepScalars scalars(void* ws, const Layout& L) {
+  return gdn::StepScalars{at<float>(ws, L.rq), at<float>(ws, L.rk), at<float>(ws, L.kq),
+                          at<float>(ws, L.ell), at<float>(ws, L.beta)};
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_ckpt_elems(const gdn_dims* d, size_t* out) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  if (!out) return GDN_ERR_INVALID_ARG;
+  const size_t nc = dd.nchunk();
+  *out = nc > 1 ? (nc - 1) * dd.B * dd.Hv * static_cast<size_t>(dd.Dk) * dd.Dv : 0;
+  return GDN_OK;
+}
+
+int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  if (!out) return GDN_ERR_INVALID_ARG;
+  *out = layout(dd, false).total;
+  return GDN_OK;
+}
+
+int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  if (!out) return GDN_ERR_INVALID_ARG;
+  *out = layout(dd, true).total;
+  return GDN_OK;
+}
+
+int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, const void* a,
+            const void* b, const float* A_log, const float* dt_bias, const float* state0,
+            const uint8_t* mask, void* o, float* state_out, float* ckpt, void* ws,
+            size_t ws_bytes, void* stream) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  const bool has_t = dd.T > 0;
+  if (!A_log || !dt_bias || !state_out) return GDN_ERR_INVALID_ARG;
+  if (has_t && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
+  const Layout L = layout(dd, false);
+  if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
+  const bool bf = d->dtype == GDN_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const gdn::StepScalars s = scalars(ws, L);
+
+  gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
+  if (gdn::launch_prep(pa, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt};
+  if (gdn::launch_scan_fwd(fa, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, const void* a,
+            const void* b, const float* A_log, const float* dt_bias, const float* state0,
+            const uint8_t* mask, const float* ckpt, const void* dO, const float* dS_final,
+            void* dq, void* dk, void* dv, void* da, void* db, float* dA_log, float* ddt_bias,
+            float* dstate, void* ws, size_t ws_bytes, void* stream) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  const bool has_t = dd.T > 0;
+  if (!A_log || !dt_bias || !dA_log || !ddt_bias || !dstate) return GDN_ERR_INVALID_ARG;
+  if (has_t && (!q || !k || !v || !a || !b || !dO || !dq || !dk || !dv || !da || !db))
+    return GDN_ERR_INVALID_ARG;
+  if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
+  const Layout L = layout(dd, true);
+  if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
+  const bool bf = d->dtype == GDN_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const gdn::StepScalars s = scalars(ws, L);
+
+  gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
+  if (gdn::launch_prep(pa, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  gdn::ScanBwdArgs ba{dd, q, k, v, dO, state0, ckpt, dS_final, s,
+                      at<float>(ws, L.U), at<float>(ws, L.E), dv, at<float>(ws, L.dHend), dstate};
+  if (gdn::launch_scan_bwd(ba, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  gdn::ChunkGradArgs ca{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, s,
+                        at<float>(ws, L.U), at<float>(ws, L.E), at<float>(ws, L.dHend),
+                        dq, dk, da, db, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
+  if (gdn::launch_chunk_grad(ca, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  gdn::ParamReduceArgs ra{dd.B, dd.nchunk(), dd.Hv, at<double>(ws, L.pdA), at<double>(ws, L.pdt),
+                          dA_log, ddt_bias};
+  if (gdn::launch_param_reduce(ra, st) != hipSuccess) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+const char* gdn_status_string(int s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported shape, dtype or algorithm";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* gdn_version(void) { return "gdn-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Host-side interfaces between the C ABI (gdn_api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct Dims {
+  int B, T, Hk, Hv, Dk, Dv;
+  __host__ __device__ int G() const { return Hv / Hk; }
+  __host__ __device__ int nchunk() const { return (T + 63) / 64; }
+};
+
+// Per-step scalars produced by the prep kernel (fp32, in the workspace).
+struct StepScalars {
+  float* rq;   // [B,T,Hk]  (|q|^2 + eps)^-1/2 / sqrt(Dk)
+  float* rk;   // [B,T,Hk]  (|k|^2 + eps)^-1/2
+  float* kq;   // [B,T,Hk]  kn . qn
+  float* ell;  // [B,T,Hv]  log gate (0 on masked steps)
+  float* beta; // [B,T,Hv]  write strength (0 on masked steps)
+};
+
+struct PrepArgs {
+  Dims d;
+  const void *q, *k, *a, *b;
+  const float *A_log, *dt_bias;
+  const uint8_t* mask;
+  StepScalars s;
+};
+
+struct ScanFwdArgs {
+  Dims d;
+  const void *q, *k, *v;
+  const float* state0;  // may be null
+  StepScalars s;
+  void* o;
+  float* state_out;
+  float* ckpt;  // may be null
+};
+
+// Sweep of the backward: recompute each chunk from its checkpoint, then walk
+// it in reverse carrying dL/dS.  Writes the per-step column quantities and the
+// per-chunk boundary gradients used by the chunk-gradient kernel.
+struct ScanBwdArgs {
+  Dims d;
+  const void *q, *k, *v, *dO;
+  const float *state0, *ckpt, *dS_final;  // state0/dS_final may be null
+  StepScalars s;
+  float* U;       // [B,T,Hv,Dv]  u  = S'^T kn (read of the decayed state)
+  float* E;       // [B,T,Hv,Dv]  Din^T kn (dL/d delta minus its own-step term)
+  void* dv;       // [B,T,Hv,Dv]  dtype
+  float* dHend;   // [NC,B,Hv,Dk,Dv] dL/d(state at the end of chunk c)
+  float* dstate;  // [B,Hv,Dk,Dv]
+};
+
+struct ChunkGradArgs {
+  Dims d;
+  const void *q, *k, *v, *dO, *a;
+  const float *A_log, *dt_bias;
+  const uint8_t* mask;
+  const float *state0, *ckpt;
+  StepScalars s;
+  const float *U, *E, *dHend;
+  void *dq, *dk, *da, *db;
+  double* part_dA;   // [B,NC,Hv] per-chunk sums of dl * l
+  double* part_ddt;  // [B,NC,Hv] per-chunk sums of da
+};
+
+struct ParamReduceArgs {
+  int B, NC, Hv;
+  const double *part_dA, *part_ddt;
+  float *dA_log, *ddt_bias;
+};
+
+hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_chunk_grad(const ChunkGradArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
+
+// Column-slice geometry of the scan kernels: NW waves x 8 columns each.
+inline int scan_waves(int Dv) { return Dv % 32 == 0 ? 4 : 1; }
+inline int scan_nslice(int Dv) { return Dv / (8 * scan_waves(Dv)); }
+inline bool scan_supported(int Dk, int Dv) {
+  bool dk = Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256;
+  bool dv = Dv >= 8 && Dv <= 256 && Dv % 8 == 0 && (Dv <= 24 || Dv % 32 == 0);
+  return dk && dv;
+}
+
+}  // namespace gdn

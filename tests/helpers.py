@@ -1,0 +1,65 @@
+"""Shared helpers for the GPU parity tests: upload a seeded case, run the
+library through its C ABI binding, run the oracle, compare."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from linear_attention_recurrence_fwd_amd import binding
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+GRADS = ("dq", "dk", "dv", "da", "db", "dA_log", "ddt_bias", "dstate")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_tensor(case, name, device="cuda"):
+    x = case.store(name)
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if x.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+def upload(case, device="cuda"):
+    t = {n: dev_tensor(case, n, device) for n in
+         ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state0", "dO", "dS_final")}
+    t["mask"] = None if case.mask is None else torch.from_numpy(case.mask).to(device)
+    return t
+
+
+def to64(x):
+    return x.detach().to(torch.float64).cpu().numpy()
+
+
+def relerr(x, ref):
+    """max |x - ref| / max |ref|  (max |x| when ref is all zero)."""
+    x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(x - ref)) if ref.size else 0.0
+    if den == 0.0:
+        return float(np.max(np.abs(x))) if x.size else 0.0
+    return float(num / den)
+
+
+def gpu_fwd(t, algo=binding.ALGO_AUTO, need_ckpt=True):
+    return binding.fwd(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"],
+                       t["state0"], t["mask"], need_ckpt=need_ckpt, algo=algo)
+
+
+def gpu_bwd(t, ckpt, algo=binding.ALGO_AUTO):
+    return binding.bwd(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"],
+                       t["state0"], t["mask"], ckpt, t["dO"], t["dS_final"], algo=algo)
+
+
+def oracle_all(case, nthreads=8):
+    v = case.vals
+    o, st, ck = oracle.fwd(*case.oracle_args(), nthreads=nthreads)
+    g = oracle.bwd(*case.oracle_args(), v["dO"], v.get("dS_final"), nthreads=nthreads)
+    return o, st, ck, g

@@ -1,0 +1,103 @@
+"""C ABI of libgdn.so on the CPU: the library loads, exports every entry point
+include/gdn.h declares, and validates arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_fwd_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(gdn_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert set(names) == set(B.EXPORTS)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gdn_version().startswith(b"gdn-mi355x")
+
+
+def test_status_strings():
+    lib = B.lib()
+    for code in range(5):
+        assert lib.gdn_status_string(code)
+    assert lib.gdn_status_string(99) == b"unknown status"
+
+
+def test_size_queries():
+    d = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_BF16)
+    assert B.ckpt_elems(d) == 31 * 64 * 192 * 128
+    d = B.make_dims(4, 65, 4, 8, 64, 32, B.GDN_F32)
+    assert B.ckpt_elems(d) == 1 * 4 * 8 * 64 * 32
+    for T in (0, 1, 64):
+        assert B.ckpt_elems(B.make_dims(4, T, 4, 8, 64, 32, B.GDN_F32)) == 0
+    assert B.fwd_workspace_bytes(d) > 0
+    assert B.bwd_workspace_bytes(d) > B.fwd_workspace_bytes(d)
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((1, 8, 3, 4, 16, 8), 1),        # Hv % Hk != 0
+    ((0, 8, 2, 4, 16, 8), 1),        # B < 1
+    ((1, -1, 2, 4, 16, 8), 1),       # T < 0
+    ((1, 8, 2, 4, 48, 8), 2),        # Dk not built
+    ((1, 8, 2, 4, 16, 12), 2),       # Dv not a multiple of 8
+    ((1, 8, 2, 4, 16, 40), 2),       # Dv > 24 and not a multiple of 32
+])
+def test_bad_dims(dims, code):
+    with pytest.raises(B.GdnError) as e:
+        B.fwd_workspace_bytes(B.make_dims(*dims, B.GDN_F32))
+    assert e.value.code == code
+
+
+def test_bad_dtype_and_algo():
+    with pytest.raises(B.GdnError) as e:
+        B.fwd_workspace_bytes(B.make_dims(1, 8, 2, 4, 16, 8, 7))
+    assert e.value.code == 2
+    with pytest.raises(B.GdnError) as e:
+        B.fwd_workspace_bytes(B.make_dims(1, 8, 2, 4, 16, 8, B.GDN_F32, 9))
+    assert e.value.code == 1
+
+
+def _fake(n):
+    return [ctypes.c_void_p(4096 * (i + 1)) for i in range(n)]
+
+
+def test_fwd_rejects_before_launch():
+    """Null required pointers and a short workspace are reported without any
+    kernel launch (the pointers here are never dereferenced)."""
+    lib = B.lib()
+    d = B.make_dims(1, 8, 2, 4, 16, 8, B.GDN_F32)
+    need = B.fwd_workspace_bytes(d)
+    p = _fake(13)  # q k v a b A_log dt_bias state0 mask o state_out ckpt ws
+    args = list(p)
+    args[0] = None  # q
+    assert lib.gdn_fwd(ctypes.byref(d), *args, need, None) == 1
+    args = list(p)
+    args[10] = None  # state_out
+    assert lib.gdn_fwd(ctypes.byref(d), *args, need, None) == 1
+    assert lib.gdn_fwd(ctypes.byref(d), *p, need - 1, None) == 3
+    assert lib.gdn_fwd(ctypes.byref(d), *p[:12], None, need, None) == 3
+    assert lib.gdn_fwd(None, *p, need, None) == 1
+
+
+def test_bwd_rejects_before_launch():
+    lib = B.lib()
+    d = B.make_dims(1, 130, 2, 4, 16, 8, B.GDN_F32)
+    need = B.bwd_workspace_bytes(d)
+    p = _fake(21)  # ... ckpt(9) dO dS_final dq dk dv(14) da db dA_log ddt_bias dstate ws
+    args = list(p)
+    args[9] = None  # ckpt is required when T > 64
+    assert lib.gdn_bwd(ctypes.byref(d), *args, need, None) == 1
+    args = list(p)
+    args[14] = None  # dv
+    assert lib.gdn_bwd(ctypes.byref(d), *args, need, None) == 1
+    assert lib.gdn_bwd(ctypes.byref(d), *p, need - 1, None) == 3
