@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the gated delta rule forward + backward on one MI355X.
+
+Default workload: the Qwen3.5-9B GatedDeltaNet layer shape (B=1, T=2048,
+Hk=16, Hv=64, Dk=192, Dv=128), bf16 q/k/v/a/b/dO, fp32 state, zero initial
+state, synthetic seeded inputs (the workload of the mlx-lm VJP PR's
+performance table).  One step = gdn_fwd (with checkpoints) + gdn_bwd on the
+same resident inputs.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 9b_t2048|9b_t256|decode]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd tokens/sec at Hk16/Hv64/Dk192/Dv128 bf16, T=2048; % HBM roofline"
+HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
+FP32_VEC_PEAK = 157.3e12     # FLOP/s, MI355X fp32 vector (packed FMA)
+# Metal VJP fwd+bwd on an M4 Max (mlx-lm PR, "Performance" table), for context
+PAGES_FWD_BWD_MS = {256: 13.4, 2048: 149.8}
+
+# Kernels launched per step, in order (fwd: 2, bwd: 4).
+KERNELS = ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd", "chunk_grad", "param_reduce"]
+# Algorithmic fp32 flops per state element-step (one (b, t, h, i, j)):
+#   scan_fwd   decay 1 mul, read u 1 fma, update 1 fma, read o 1 fma       = 7
+#   scan_bwd   recompute 5 (as above without o) + reverse step: read ein
+#              1 fma, carry update 1 mul + 2 fma                           = 12
+#   chunk_grad the method's per-step gradient contractions: dq = S dO
+#              1 fma, dk = D delta + S' du 2 fma, dg = <dS', S> 1 fma      = 8
+FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
+
+
+def method_bytes(B, T, Hk, Hv, Dk, Dv, io, mask=False, dS_final=False):
+    """Algorithmic HBM bytes of fwd + bwd: every I/O tensor once, plus the fp32
+    checkpoints (written by fwd, read by bwd)."""
+    Q = B * T * Hk * Dk * io
+    V = B * T * Hv * Dv * io
+    AB = 2 * B * T * Hv * io
+    Par = 2 * Hv * 4
+    Sig = B * Hv * Dk * Dv * 4
+    Mk = B * T if mask else 0
+    CK = max(math.ceil(T / 64) - 1, 0) * Sig
+    fwd = 2 * Q + V + AB + Par + Mk + Sig + V + Sig + CK
+    bwd = (2 * Q + V + AB + Par + Mk + Sig + CK + V + (Sig if dS_final else 0)) \
+        + (2 * Q + V + AB + Par + Sig)
+    return fwd, bwd
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            if self.hip.hipEventCreate(ctypes.byref(self.ev, i * ctypes.sizeof(ctypes.c_void_p))):
+                raise RuntimeError("hipEventCreate failed")
+        self.n = n
+
+    def ptr(self, off):
+        return ctypes.cast(ctypes.byref(self.ev, off * ctypes.sizeof(ctypes.c_void_p)),
+                           ctypes.POINTER(ctypes.c_void_p))
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[i]),
+                                        ctypes.c_void_p(self.ev[j])):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(ctypes.c_void_p(self.ev[i]))
+
+
+def cpu_baseline(T, seconds_hint=True):
+    """The fp64 oracle on a bounded sample of the 9B workload: the same T and
+    per-head shape, 4 of the 16 key heads (16 of 64 value heads), fwd + bwd,
+    timed on the host; tokens/s scaled to all heads (work is linear in heads)."""
+    import oracle
+    from linear_attention_recurrence_fwd_amd import inputs
+    threads = max(1, min(16, os.cpu_count() or 1))
+    c = inputs.make_case("9b_sample", 1, T, 4, 16, 192, 128, "bf16", 3, state_std=None,
+                         dS_final=False)
+    oracle.fwd(*c.oracle_args(), nthreads=threads)  # loads / warms the library
+    t0 = time.perf_counter()
+    oracle.fwd(*c.oracle_args(), nthreads=threads)
+    oracle.bwd(*c.oracle_args(), c.vals["dO"], None, nthreads=threads)
+    dt = time.perf_counter() - t0
+    scale = 64 / 16
+    return {"value": round(c.B * T / (dt * scale), 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "fp64 oracle fwd+bwd (64-step checkpointed recompute), B=1 T=%d, "
+                      "Hk=4 Hv=16 Dk=192 Dv=128 (1/4 of the heads), %.2f s wall on %d threads; "
+                      "tokens/s scaled by 4" % (T, dt, threads)}
+
+
+def bench_train(args, torch, binding, inputs):
+    T = {"9b_t2048": 2048, "9b_t256": 256}[args.config]
+    case = inputs.qwen35_9b(T)
+    dev = torch.device("cuda:0")
+
+    def up(n):
+        import numpy as np
+        x = case.store(n)
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    t = {n: up(n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state0", "dO",
+                            "dS_final")}
+    t["mask"] = None
+    algo = {"auto": binding.ALGO_AUTO, "scan": binding.ALGO_SCAN,
+            "chunk": binding.ALGO_CHUNK}[args.algo]
+    plan = binding.Plan(t, algo=algo)
+    for _ in range(args.warmup):
+        plan.fwd()
+        plan.bwd()
+    torch.cuda.synchronize()
+
+    nk = len(KERNELS)
+    ev = HipEvents(2 * nk * args.steps + 2)
+    lib = binding.lib()
+    start, stop = 2 * nk * args.steps, 2 * nk * args.steps + 1
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[start]), ctypes.c_void_p(plan.stream.cuda_stream))
+    wall0 = time.perf_counter()
+    for s in range(args.steps):
+        lib.gdn_set_kernel_events(ev.ptr(2 * nk * s), 2 * nk)
+        plan.fwd()
+        plan.bwd()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[stop]), ctypes.c_void_p(plan.stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    lib.gdn_set_kernel_events(None, 0)
+    total_ms = ev.elapsed_ms(start, stop)
+    per_kernel = {k: 0.0 for k in KERNELS}
+    for s in range(args.steps):
+        for i, k in enumerate(KERNELS):
+            per_kernel[k] += ev.elapsed_ms(2 * nk * s + 2 * i, 2 * nk * s + 2 * i + 1)
+    ev.close()
+    per_kernel = {k: v / args.steps for k, v in per_kernel.items()}
+    ms = total_ms / args.steps
+
+    B, Hk, Hv, Dk, Dv = case.B, case.Hk, case.Hv, case.Dk, case.Dv
+    tokens = B * T
+    value = tokens / (ms / 1e3)
+    fb, bb = method_bytes(B, T, Hk, Hv, Dk, Dv, 2)
+    hbm_frac = (fb + bb) / (ms / 1e3) / HBM_PEAK
+    E = B * T * Hv * Dk * Dv
+    dom = max(FLOPS_PER_ELEM, key=lambda k: per_kernel[k])
+    flops = FLOPS_PER_ELEM[dom] * E
+    achieved = flops / (per_kernel[dom] / 1e3) / 1e12
+    pages_ms = PAGES_FWD_BWD_MS.get(T)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (tokens / (pages_ms / 1e3)), 2) if pages_ms else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gated delta rule fwd+bwd, Qwen3.5-9B GDN layer shape",
+                   "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                   "io_dtype": "bf16", "state_dtype": "f32", "algo": args.algo},
+        "roofline": {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
+                     "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / FP32_VEC_PEAK, 4), "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": round(per_kernel[dom], 4)},
+        "hbm_roofline_step": {"method_bytes": fb + bb, "achieved_GBps": round(
+            (fb + bb) / (ms / 1e3) / 1e9, 1), "peak_GBps": HBM_PEAK / 1e9,
+            "frac": round(hbm_frac, 5)},
+        "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "wall_s_timed": round(wall, 3),
+    }
+    return out
+
+
+def bench_decode(args, torch, binding, inputs):
+    """Decode workload: B=64, Hk=16, Hv=32, Dk=Dv=128, one token per call, the
+    state updated in place; a step is 64 consecutive calls."""
+    import numpy as np
+    case = inputs.decode(64)
+    dev = torch.device("cuda:0")
+
+    def up(n):
+        x = case.store(n)
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    t = {n: up(n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state0")}
+    calls = [{n: t[n][:, i:i + 1].contiguous() for n in ("q", "k", "v", "a", "b")}
+             for i in range(case.T)]
+    state = t["state0"].clone()
+    d = binding.make_dims(case.B, 1, case.Hk, case.Hv, case.Dk, case.Dv, torch.bfloat16)
+    wsb = binding.fwd_workspace_bytes(d)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((case.B, 1, case.Hv, case.Dv), dtype=torch.bfloat16, device=dev)
+            for _ in range(case.T)]
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = binding._p
+    argl = [(ctypes.byref(d), P(c["q"]), P(c["k"]), P(c["v"]), P(c["a"]), P(c["b"]),
+             P(t["A_log"]), P(t["dt_bias"]), P(state), None, P(o), P(state), None, P(ws), wsb, sp)
+            for c, o in zip(calls, outs)]
+    lib = binding.lib()
+
+    def step():
+        for a in argl:
+            rc = lib.gdn_fwd(*a)
+            if rc:
+                raise binding.GdnError("gdn_fwd", rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_call = ms / case.T
+    Sig = case.B * case.Hv * case.Dk * case.Dv * 4
+    io = case.B * (2 * case.Hk * case.Dk + 2 * case.Hv * case.Dv + 2 * case.Hv) * 2 + 2 * case.Hv * 4
+    call_bytes = 2 * Sig + io
+    frac = call_bytes / (per_call / 1e3) / HBM_PEAK
+    return {
+        "metric": "decode tokens/sec, B=64 Hk16/Hv32/Dk128/Dv128, 1 token per call",
+        "value": round(case.B * case.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gated delta rule decode, 64 single-token calls per step",
+                   "B": case.B, "Hk": case.Hk, "Hv": case.Hv, "Dk": case.Dk, "Dv": case.Dv,
+                   "io_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "scan_fwd+prep (one call)",
+                     "achieved": round(call_bytes / (per_call / 1e3) / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(frac, 4),
+                     "traffic": None, "bytes_per_launch": call_bytes,
+                     "avg_call_ms": round(per_call, 5)},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="9b_t2048", choices=["9b_t2048", "9b_t256", "decode"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunk"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the operation shards by (batch, key-head group) with no exchange); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from linear_attention_recurrence_fwd_amd import binding, inputs
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.lib()
+    if args.config == "decode":
+        out = bench_decode(args, torch, binding, inputs)
+    else:
+        out = bench_train(args, torch, binding, inputs)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(out["config"]["T"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

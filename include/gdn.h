@@ -19,7 +19,8 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to dense row-major tensors with
  *    the layouts given below.  The caller owns all memory: the library never
- *    allocates or frees device memory and keeps no state between calls.
+ *    allocates or frees device memory and keeps no state between calls
+ *    (apart from the optional timing events of gdn_set_kernel_events).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream): they validate, enqueue kernels and return.  No host sync.
  *  - All arguments are validated before anything is enqueued; on a non-zero
@@ -116,6 +117,18 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v,
             void* dk, void* dv, void* da, void* db, float* dA_log,
             float* ddt_bias, float* dstate, void* ws, size_t ws_bytes,
             void* stream);
+
+/*
+ * Optional per-kernel timing, for benchmarks and profilers.  While `events`
+ * is non-NULL, each kernel that the following gdn_fwd / gdn_bwd calls launch
+ * (in launch order, i = 0, 1, ...) records events[2i] on the call's stream
+ * just before it and events[2i+1] just after it, for as long as 2i+1 < n;
+ * later kernels are not timed.  Each call of this function restarts the count
+ * at i = 0.  events are hipEvent_t handles created (and destroyed) by the
+ * caller.  NULL turns timing off.  The setting is process-wide and not
+ * thread-safe.  Returns GDN_ERR_INVALID_ARG if events is non-NULL and n < 2.
+ */
+int gdn_set_kernel_events(void* const* events, int n);
 
 /* Static description of a status code. */
 const char* gdn_status_string(int status);

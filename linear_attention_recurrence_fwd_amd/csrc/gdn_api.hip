@@ -70,6 +70,29 @@ int check_dims(const gdn_dims* p, Dims* out) {
   return GDN_OK;
 }
 
+// Per-kernel timing events (gdn_set_kernel_events).
+struct Timing {
+  void* const* ev = nullptr;
+  int n = 0;
+  int next = 0;
+} g_timing;
+
+// Launches one kernel through `fn`, bracketed by the timing events if set.
+template <typename F>
+bool launch(hipStream_t st, F&& fn) {
+  const bool timed = g_timing.ev && g_timing.next + 1 < g_timing.n;
+  if (timed &&
+      hipEventRecord(static_cast<hipEvent_t>(g_timing.ev[g_timing.next]), st) != hipSuccess)
+    return false;
+  if (fn() != hipSuccess) return false;
+  if (timed) {
+    if (hipEventRecord(static_cast<hipEvent_t>(g_timing.ev[g_timing.next + 1]), st) != hipSuccess)
+      return false;
+    g_timing.next += 2;
+  }
+  return true;
+}
+
 template <typename P>
 P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
@@ -129,9 +152,9 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   const gdn::StepScalars s = scalars(ws, L);
 
   gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
-  if (gdn::launch_prep(pa, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt};
-  if (gdn::launch_scan_fwd(fa, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  if (!launch(st, [&] { return gdn::launch_scan_fwd(fa, bf, st); })) return GDN_ERR_HIP;
   return GDN_OK;
 }
 
@@ -155,17 +178,25 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   const gdn::StepScalars s = scalars(ws, L);
 
   gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
-  if (gdn::launch_prep(pa, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   gdn::ScanBwdArgs ba{dd, q, k, v, dO, state0, ckpt, dS_final, s,
                       at<float>(ws, L.U), at<float>(ws, L.E), dv, at<float>(ws, L.dHend), dstate};
-  if (gdn::launch_scan_bwd(ba, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  if (!launch(st, [&] { return gdn::launch_scan_bwd(ba, bf, st); })) return GDN_ERR_HIP;
   gdn::ChunkGradArgs ca{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, s,
                         at<float>(ws, L.U), at<float>(ws, L.E), at<float>(ws, L.dHend),
                         dq, dk, da, db, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
-  if (gdn::launch_chunk_grad(ca, bf, st) != hipSuccess) return GDN_ERR_HIP;
+  if (!launch(st, [&] { return gdn::launch_chunk_grad(ca, bf, st); })) return GDN_ERR_HIP;
   gdn::ParamReduceArgs ra{dd.B, dd.nchunk(), dd.Hv, at<double>(ws, L.pdA), at<double>(ws, L.pdt),
                           dA_log, ddt_bias};
-  if (gdn::launch_param_reduce(ra, st) != hipSuccess) return GDN_ERR_HIP;
+  if (!launch(st, [&] { return gdn::launch_param_reduce(ra, st); })) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_set_kernel_events(void* const* events, int n) {
+  if (events && n < 2) return GDN_ERR_INVALID_ARG;
+  g_timing.ev = events;
+  g_timing.n = events ? n : 0;
+  g_timing.next = 0;
   return GDN_OK;
 }
 

@@ -1,0 +1,24 @@
+"""Host-side pieces of bench.py (no GPU): the multi-GPU refusal and the
+algorithmic byte count of the headline workload."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_method_bytes_9b_t2048():
+    """fwd + bwd bytes of the 9B layer at T=2048 (bf16 I/O, fp32 state and
+    31 checkpoints): 660.1 MB, i.e. 82.5 us at 8 TB/s."""
+    fb, bb = bench.method_bytes(1, 2048, 16, 64, 192, 128, 2)
+    assert abs((fb + bb) / 1e6 - 660.1) < 0.1
+    assert abs(fb / 1e6 - 300.4) < 0.1
