@@ -28,15 +28,19 @@ FP32_VEC_PEAK = 157.3e12     # FLOP/s, MI355X fp32 vector (packed FMA)
 # Metal VJP fwd+bwd on an M4 Max (mlx-lm PR, "Performance" table), for context
 PAGES_FWD_BWD_MS = {256: 13.4, 2048: 149.8}
 
-# Kernels launched per step, in order (fwd: 2, bwd: 4).
-KERNELS = ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd", "chunk_grad", "param_reduce"]
+# Kernels launched per step, in order, by kernel family.
+KERNELS = {
+    "scan": ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd", "chunk_grad", "param_reduce"],
+    "chunk": ["prep_fwd", "chunk_prep_fwd", "chunk_fwd", "prep_bwd", "scan_bwd", "chunk_grad",
+              "param_reduce"],
+}
 # Algorithmic fp32 flops per state element-step (one (b, t, h, i, j)):
 #   scan_fwd   decay 1 mul, read u 1 fma, update 1 fma, read o 1 fma       = 7
 #   scan_bwd   recompute 5 (as above without o) + reverse step: read ein
 #              1 fma, carry update 1 mul + 2 fma                           = 12
 #   chunk_grad the method's per-step gradient contractions: dq = S dO
 #              1 fma, dk = D delta + S' du 2 fma, dg = <dS', S> 1 fma      = 8
-FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
+FLOPS_PER_ELEM = {"scan_fwd": 7, "chunk_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
 
 
 def method_bytes(B, T, Hk, Hv, Dk, Dv, io, mask=False, dS_final=False):
@@ -128,7 +132,8 @@ def bench_train(args, torch, binding, inputs):
         plan.bwd()
     torch.cuda.synchronize()
 
-    nk = len(KERNELS)
+    kernels = KERNELS["chunk" if args.algo == "chunk" else "scan"]
+    nk = len(kernels)
     ev = HipEvents(2 * nk * args.steps + 2)
     lib = binding.lib()
     start, stop = 2 * nk * args.steps, 2 * nk * args.steps + 1
@@ -144,9 +149,9 @@ def bench_train(args, torch, binding, inputs):
     wall = time.perf_counter() - wall0
     lib.gdn_set_kernel_events(None, 0)
     total_ms = ev.elapsed_ms(start, stop)
-    per_kernel = {k: 0.0 for k in KERNELS}
+    per_kernel = {k: 0.0 for k in kernels}
     for s in range(args.steps):
-        for i, k in enumerate(KERNELS):
+        for i, k in enumerate(kernels):
             per_kernel[k] += ev.elapsed_ms(2 * nk * s + 2 * i, 2 * nk * s + 2 * i + 1)
     ev.close()
     per_kernel = {k: v / args.steps for k, v in per_kernel.items()}
@@ -158,7 +163,7 @@ def bench_train(args, torch, binding, inputs):
     fb, bb = method_bytes(B, T, Hk, Hv, Dk, Dv, 2)
     hbm_frac = (fb + bb) / (ms / 1e3) / HBM_PEAK
     E = B * T * Hv * Dk * Dv
-    dom = max(FLOPS_PER_ELEM, key=lambda k: per_kernel[k])
+    dom = max((k for k in FLOPS_PER_ELEM if k in per_kernel), key=lambda k: per_kernel[k])
     flops = FLOPS_PER_ELEM[dom] * E
     achieved = flops / (per_kernel[dom] / 1e3) / 1e12
     pages_ms = PAGES_FWD_BWD_MS.get(T)

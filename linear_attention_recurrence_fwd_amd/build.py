@@ -1,7 +1,9 @@
 """Build libgdn.so (gfx950) from csrc/*.hip with hipcc, in place.
 
 Each .hip file compiles to its own object (in parallel), then one shared
-library is linked.  Flags: -O3, gfx950 only, packed-fp32 instructions off.
+library is linked.  Flags: -O3, gfx950 only, packed-fp32 instructions off,
+MFMA results in ordinary VGPRs (the accumulators are read by vector ALU code
+every chunk; keeping them out of the accumulation registers saves the copies).
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include")]
 
 

@@ -16,10 +16,11 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t rq, rk, kq, ell, beta;                 // prep scalars
   size_t U, E, dHend, pdA, pdt;                 // backward only
+  size_t Tx, Mq, KT, TxT, AtT, PqT, QT, SC;     // chunk form
   size_t total;
 };
 
-Layout layout(const Dims& d, bool bwd) {
+Layout layout(const Dims& d, bool bwd, bool chunk) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t nfloat) {
@@ -42,6 +43,21 @@ Layout layout(const Dims& d, bool bwd) {
     L.pdA = take(2 * static_cast<size_t>(d.B) * nc * d.Hv);  // fp64
     L.pdt = take(2 * static_cast<size_t>(d.B) * nc * d.Hv);
   }
+  if (chunk) {
+    const size_t nc = d.nchunk();
+    const size_t mats = static_cast<size_t>(d.B) * d.Hv * nc * 64 * 64;  // bf16 each
+    const size_t kts = static_cast<size_t>(d.B) * d.Hk * nc * d.Dk * 64;
+    L.Tx = take((mats + 1) / 2);
+    L.Mq = take((mats + 1) / 2);
+    L.KT = take((kts + 1) / 2);
+    L.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
+    if (bwd) {
+      L.TxT = take((mats + 1) / 2);
+      L.AtT = take((mats + 1) / 2);
+      L.PqT = take((mats + 1) / 2);
+      L.QT = take((kts + 1) / 2);
+    }
+  }
   L.total = off;
   return L;
 }
@@ -55,7 +71,9 @@ int check_dims(const gdn_dims* p, Dims* out) {
   if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
   if (p->algo != GDN_ALGO_AUTO && p->algo != GDN_ALGO_SCAN && p->algo != GDN_ALGO_CHUNK)
     return GDN_ERR_INVALID_ARG;
-  if (p->algo == GDN_ALGO_CHUNK) return GDN_ERR_UNSUPPORTED;
+  if (p->algo == GDN_ALGO_CHUNK &&
+      !gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16))
+    return GDN_ERR_UNSUPPORTED;
   if (!gdn::scan_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv)))
     return GDN_ERR_UNSUPPORTED;
   // every tensor's element count (and the checkpoint slab count) fits in int32
@@ -98,6 +116,26 @@ P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
 }
 
+// Kernel family of a call: the chunk form where asked for (AUTO keeps the
+// sequential scan until the chunk backward is in place).
+bool use_chunk_fwd(const gdn_dims* p) { return p->algo == GDN_ALGO_CHUNK; }
+bool use_chunk_bwd(const gdn_dims* p) { (void)p; return false; }
+
+gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
+  gdn::ChunkBufs cb{};
+  cb.Tx = at<gdn::bf16>(ws, L.Tx);
+  cb.Mq = at<gdn::bf16>(ws, L.Mq);
+  cb.KT = at<gdn::bf16>(ws, L.KT);
+  cb.sc = at<float>(ws, L.SC);
+  if (bwd) {
+    cb.TxT = at<gdn::bf16>(ws, L.TxT);
+    cb.AtT = at<gdn::bf16>(ws, L.AtT);
+    cb.PqT = at<gdn::bf16>(ws, L.PqT);
+    cb.QT = at<gdn::bf16>(ws, L.QT);
+  }
+  return cb;
+}
+
 gdn::StepScalars scalars(void* ws, const Layout& L) {
   return gdn::StepScalars{at<float>(ws, L.rq), at<float>(ws, L.rk), at<float>(ws, L.kq),
                           at<float>(ws, L.ell), at<float>(ws, L.beta)};
@@ -122,7 +160,7 @@ int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = layout(dd, false).total;
+  *out = layout(dd, false, use_chunk_fwd(d)).total;
   return GDN_OK;
 }
 
@@ -131,7 +169,7 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = layout(dd, true).total;
+  *out = layout(dd, true, use_chunk_bwd(d)).total;
   return GDN_OK;
 }
 
@@ -145,7 +183,8 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   const bool has_t = dd.T > 0;
   if (!A_log || !dt_bias || !state_out) return GDN_ERR_INVALID_ARG;
   if (has_t && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
-  const Layout L = layout(dd, false);
+  const bool chunk = use_chunk_fwd(d);
+  const Layout L = layout(dd, false, chunk);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -153,6 +192,14 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
 
   gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
   if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
+  if (chunk) {
+    const gdn::ChunkBufs cb = chunk_bufs(ws, L, false);
+    gdn::ChunkPrepArgs ca{dd, q, k, s, cb, 0};
+    if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, s, cb, o, state_out, ckpt};
+    if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt};
   if (!launch(st, [&] { return gdn::launch_scan_fwd(fa, bf, st); })) return GDN_ERR_HIP;
   return GDN_OK;
@@ -171,7 +218,7 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   if (has_t && (!q || !k || !v || !a || !b || !dO || !dq || !dk || !dv || !da || !db))
     return GDN_ERR_INVALID_ARG;
   if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
-  const Layout L = layout(dd, true);
+  const Layout L = layout(dd, true, use_chunk_bwd(d));
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -22,12 +22,22 @@ __device__ __forceinline__ float to_f32(bf16 v) {
 
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
-// Round to nearest, ties to even; NaN stays NaN.
+// Round to nearest, ties to even (the gfx950 conversion instruction); NaN
+// stays NaN.
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{static_cast<uint16_t>((u >> 16) | 0x40u)};
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16{static_cast<uint16_t>(u >> 16)};
+  return bf16{__builtin_bit_cast(uint16_t, static_cast<__bf16>(v))};
+}
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+// Two floats -> two bf16 (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// Four floats -> four consecutive bf16 (8 bytes).
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
 }
 
 // Unpack 16 bytes of storage into fp32 values.
@@ -81,4 +91,34 @@ __device__ __forceinline__ float sigmoid_f(float x) {
   return e / (1.f + e);
 }
 
+}  // namespace gdn
+
+// ---- bf16 matrix cores (gfx950 v_mfma_f32_16x16x32_bf16)
+// One wave computes a 16x16 fp32 tile D = A (16x32) * B (32x16) + C.
+// Lane l supplies A[l%16][8*(l/16) + 0..7] and B[8*(l/16) + 0..7][l%16], and
+// holds D[4*(l/16) + 0..3][l%16].
+namespace gdn {
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 f4zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// 16 bytes of bf16 storage <-> operand register.
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ bf16 bf16_of(float v) { return from_f32<bf16>(v); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt) and meets the other waves, without waiting for outstanding global
+// loads, so loads issued ahead of time (prefetches) stay in flight across it.
+// The memory clobbers keep the compiler from moving LDS accesses across it.
+// Global memory written before it is NOT made visible to the other waves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 }  // namespace gdn

@@ -7,6 +7,8 @@
 
 namespace gdn {
 
+struct bf16;
+
 struct Dims {
   int B, T, Hk, Hv, Dk, Dv;
   __host__ __device__ int G() const { return Hv / Hk; }
@@ -68,6 +70,50 @@ struct ChunkGradArgs {
   double* part_ddt;  // [B,NC,Hv] per-chunk sums of da
 };
 
+// Chunk-form intermediates (bf16, in the workspace).  L = 64 rows per chunk,
+// rows past the end of the sequence are zero.
+struct ChunkBufs {
+  bf16* Tx;   // [B*Hv, NC, L, L] (I + N)^-1, N[t,s] = [s<t] e^{g_t-g_s} rk_t rk_s beta_s (k_t.k_s)
+  bf16* Mq;   // [B*Hv, NC, L, L] [s<=t] e^{g_t-g_s} rq_t rk_s beta_s (q_t.k_s)
+  bf16* KT;   // [B*Hk, NC, Dk, L] raw k of the chunk, transposed
+  // backward only
+  bf16* TxT;  // [B*Hv, NC, L, L] transpose of Tx
+  bf16* AtT;  // [B*Hv, NC, L, L] transpose of [s<t] e^{g_t-g_s} rk_t rk_s (k_t.k_s)
+  bf16* PqT;  // [B*Hv, NC, L, L] transpose of [s<=t] e^{g_t-g_s} rq_t rk_s (q_t.k_s)
+  bf16* QT;   // [B*Hk, NC, Dk, L] raw q of the chunk, transposed
+  // per-step chunk scalars, fp32 [B*Hv, NC, SC_ROWS, L]
+  float* sc;
+};
+// Rows of ChunkBufs::sc (per chunk, per step t; g = gamma):
+enum : int {
+  SC_CR = 0,     // e^{g_t} rk_t
+  SC_CO = 1,     // e^{g_t} rq_t
+  SC_W = 2,      // beta_t e^{g_L - g_t} rk_t
+  SC_KL = 3,     // e^{g_L - g_t} rk_t
+  SC_BETA = 4,   // beta_t
+  SC_EGL = 5,    // [0] = e^{g_L}
+  SC_ROWS = 6
+};
+
+struct ChunkPrepArgs {
+  Dims d;
+  const void *q, *k;
+  StepScalars s;
+  ChunkBufs cb;
+  int bwd;  // also write the backward-only buffers
+};
+
+struct ChunkFwdArgs {
+  Dims d;
+  const void *q, *k, *v;
+  const float* state0;
+  StepScalars s;
+  ChunkBufs cb;
+  void* o;
+  float* state_out;
+  float* ckpt;
+};
+
 struct ParamReduceArgs {
   int B, NC, Hv;
   const double *part_dA, *part_ddt;
@@ -79,6 +125,13 @@ hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_chunk_grad(const ChunkGradArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
+hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
+hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
+
+// The chunk form runs bf16 I/O with Dk a multiple of 32 and Dv a multiple of 32.
+inline bool chunk_supported(int Dk, int Dv, bool bf16) {
+  return bf16 && (Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256) && Dv % 32 == 0 && Dv <= 256;
+}
 
 // Column-slice geometry of the scan kernels: NW waves x 8 columns each.
 inline int scan_waves(int Dv) { return Dv % 32 == 0 ? 4 : 1; }

@@ -143,10 +143,11 @@ def edge_mask(B: int, T: int) -> np.ndarray:
     return m
 
 
-def edge(T: int, *, masked: bool = True, extreme: bool = False) -> Case:
+def edge(T: int, *, masked: bool = True, extreme: bool = False, dtype: str = "f32") -> Case:
     B = 4
-    name = "edge_T%d%s%s" % (T, "_mask" if masked else "", "_extreme" if extreme else "")
-    return make_case(name, B, T, 4, 8, 64, 32, "f32", 4000 + T,
+    name = "edge_T%d%s%s%s" % (T, "_mask" if masked else "", "_extreme" if extreme else "",
+                               "" if dtype == "f32" else "_" + dtype)
+    return make_case(name, B, T, 4, 8, 64, 32, dtype, 4000 + T,
                      mask=edge_mask(B, T) if masked else None, extreme=extreme)
 
 

@@ -148,3 +148,49 @@ def test_empty_sequence():
     assert torch.equal(st, t["state0"])
     assert torch.equal(g["dstate"], t["dS_final"])
     assert torch.all(g["dA_log"] == 0) and torch.all(g["ddt_bias"] == 0)
+
+
+# ---------------------------------------------------------------- chunk form
+
+CHUNK = binding.ALGO_CHUNK
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 1024])
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("extreme", [False, True])
+def test_chunk_edge_bf16(T, masked, extreme):
+    run_and_compare(inputs.edge(T, masked=masked, extreme=extreme, dtype="bf16"), algo=CHUNK)
+
+
+def test_chunk_ragged_dk128():
+    c = inputs.make_case("chunk_ragged_dk128", 2, 200, 2, 4, 128, 64, "bf16", 79)
+    run_and_compare(c, algo=CHUNK)
+
+
+def test_chunk_ragged_dk256_g1():
+    c = inputs.make_case("chunk_ragged_dk256", 1, 130, 2, 2, 256, 32, "bf16", 80)
+    run_and_compare(c, algo=CHUNK)
+
+
+def test_chunk_qwen35_9b_t256():
+    run_and_compare(inputs.qwen35_9b(256), algo=CHUNK)
+
+
+def test_chunk_qwen35_9b_t2048():
+    run_and_compare(inputs.qwen35_9b(2048), algo=CHUNK, nthreads=16)
+
+
+def test_chunk_deterministic_repeat():
+    c = inputs.qwen35_9b(256)
+    say("[determinism] chunk case=%s" % c.name)
+    t = upload(c)
+    outs = []
+    for _ in range(3):
+        o, st, ck = gpu_fwd(t, algo=CHUNK)
+        g = gpu_bwd(t, ck, algo=CHUNK)
+        outs.append([o, st, ck] + [g[n] for n in GRADS])
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for x, y in zip(outs[0], other):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
