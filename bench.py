@@ -31,8 +31,8 @@ PAGES_FWD_BWD_MS = {256: 13.4, 2048: 149.8}
 # Kernels launched per step, in order, by kernel family.
 KERNELS = {
     "scan": ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd", "chunk_grad", "param_reduce"],
-    "chunk": ["prep_fwd", "chunk_prep_fwd", "chunk_fwd", "prep_bwd", "scan_bwd", "chunk_grad",
-              "param_reduce"],
+    "chunk": ["prep_fwd", "chunk_prep_fwd", "chunk_fwd", "prep_bwd", "chunk_prep_bwd",
+              "chunk_bwd_state", "chunk_bwd_grad", "param_reduce"],
 }
 # Algorithmic fp32 flops per state element-step (one (b, t, h, i, j)):
 #   scan_fwd   decay 1 mul, read u 1 fma, update 1 fma, read o 1 fma       = 7

@@ -37,9 +37,15 @@ Layout layout(const Dims& d, bool bwd, bool chunk) {
   if (bwd) {
     const size_t nc = d.nchunk();
     const size_t col = bt * d.Hv * d.Dv;
-    L.U = take(col);
-    L.E = take(col);
-    L.dHend = take(nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv);
+    const size_t dh = nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv;
+    if (chunk) {  // eps and dH' in bf16
+      L.E = take((col + 1) / 2);
+      L.dHend = take((dh + 1) / 2);
+    } else {
+      L.U = take(col);
+      L.E = take(col);
+      L.dHend = take(dh);
+    }
     L.pdA = take(2 * static_cast<size_t>(d.B) * nc * d.Hv);  // fp64
     L.pdt = take(2 * static_cast<size_t>(d.B) * nc * d.Hv);
   }
@@ -116,10 +122,9 @@ P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
 }
 
-// Kernel family of a call: the chunk form where asked for (AUTO keeps the
-// sequential scan until the chunk backward is in place).
+// Kernel family of a call: the chunk form where asked for.
 bool use_chunk_fwd(const gdn_dims* p) { return p->algo == GDN_ALGO_CHUNK; }
-bool use_chunk_bwd(const gdn_dims* p) { (void)p; return false; }
+bool use_chunk_bwd(const gdn_dims* p) { return p->algo == GDN_ALGO_CHUNK; }
 
 gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   gdn::ChunkBufs cb{};
@@ -218,7 +223,8 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   if (has_t && (!q || !k || !v || !a || !b || !dO || !dq || !dk || !dv || !da || !db))
     return GDN_ERR_INVALID_ARG;
   if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
-  const Layout L = layout(dd, true, use_chunk_bwd(d));
+  const bool chunk = use_chunk_bwd(d);
+  const Layout L = layout(dd, true, chunk);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -226,6 +232,20 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
 
   gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
   if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
+  gdn::ParamReduceArgs ra{dd.B, dd.nchunk(), dd.Hv, at<double>(ws, L.pdA), at<double>(ws, L.pdt),
+                          dA_log, ddt_bias};
+  if (chunk) {
+    const gdn::ChunkBufs cb = chunk_bufs(ws, L, true);
+    gdn::ChunkPrepArgs ca{dd, q, k, s, cb, 1};
+    if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, s, cb,
+                         at<gdn::bf16>(ws, L.E), at<gdn::bf16>(ws, L.dHend),
+                         dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
+    if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
+    if (!launch(st, [&] { return gdn::launch_chunk_bwd_grad(ba, st); })) return GDN_ERR_HIP;
+    if (!launch(st, [&] { return gdn::launch_param_reduce(ra, st); })) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   gdn::ScanBwdArgs ba{dd, q, k, v, dO, state0, ckpt, dS_final, s,
                       at<float>(ws, L.U), at<float>(ws, L.E), dv, at<float>(ws, L.dHend), dstate};
   if (!launch(st, [&] { return gdn::launch_scan_bwd(ba, bf, st); })) return GDN_ERR_HIP;
@@ -233,8 +253,6 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
                         at<float>(ws, L.U), at<float>(ws, L.E), at<float>(ws, L.dHend),
                         dq, dk, da, db, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
   if (!launch(st, [&] { return gdn::launch_chunk_grad(ca, bf, st); })) return GDN_ERR_HIP;
-  gdn::ParamReduceArgs ra{dd.B, dd.nchunk(), dd.Hv, at<double>(ws, L.pdA), at<double>(ws, L.pdt),
-                          dA_log, ddt_bias};
   if (!launch(st, [&] { return gdn::launch_param_reduce(ra, st); })) return GDN_ERR_HIP;
   return GDN_OK;
 }

@@ -1,0 +1,789 @@
+// Chunked (matrix) form of the gated delta rule backward on gfx950 bf16 MFMA.
+//
+// Per chunk of L = 64 steps (local t, H = state at the chunk start, dH' =
+// dL/d(state at the chunk end), gamma_t = l_0 + ... + l_t, X_t = v_t - u_t,
+// delta_t = beta_t X_t, eps_t = dL/d delta_t), the per-step backward of the
+// recurrence (mlx-lm VJP PR, "What this PR adds": the reverse pass carrying
+// dL/dS) unrolls to
+//   eps  = rhs - A^T Ehat,   Ehat = Tx^T diag(beta) rhs  (= dv),
+//   rhs  = diag(e^{gL-g} rk) K dH' + P^T dO,
+//   dH   = e^{gL} dH' + Q^T diag(e^g rq) dO - K^T diag(e^g rk) Ehat,
+// with A[r,t] = [t<r] e^{g_r-g_t} kn_r.kn_t, P[r,t] = [t<=r] e^{g_r-g_t}
+// qn_r.kn_t and Tx = (I + A diag(beta))^-1 (Tx^T inverts the transposed
+// system).  Derivation: dL/dS before step t's output term is
+// e^{gL-g_t} dH' + sum_{r>t} e^{g_r-g_t} (qn_r dO_r^T - beta_r kn_r eps_r^T),
+// and eps_t is its product with kn_t plus (qn_t . kn_t) dO_t.
+//
+// The per-chunk gradients (same expansion as the scan path's chunk assembly):
+//   dQn = diag(e^g) dO H^T + Wq Kn
+//   dKn = diag(e^{gL-g} beta) X dH'^T - diag(e^g beta) eps H^T + Wk1 Qn + Wk2 Kn
+//   Wq[t,s]  = [s<=t] e^{g_t-g_s} beta_s (dO_t . X_s)
+//   Wk1[t,r] = [r>=t] e^{g_r-g_t} beta_t (dO_r . X_t)
+//   Wk2[t,s] = -beta_t beta_s ([s<t] e^{g_t-g_s} (X_s . eps_t) + [s>t] e^{g_s-g_t} (X_t . eps_s))
+//   dl_t = e^{gL} <dH', H> + sum_{s<t} a_s + sum_{r>=t} b_r
+//          + sum_{r>=t} sum_{s<t} e^{g_r-g_s} beta_s [(qn_r.kn_s)(dO_r.X_s) - beta_r (kn_r.kn_s)(eps_r.X_s)]
+//   a_s = e^{gL-g_s} beta_s kn_s^T dH' X_s,  b_r = e^{g_r} (qn_r^T H dO_r - beta_r kn_r^T H eps_r)
+// with X recomputed from the checkpointed H as in the forward.  Every decay is
+// e^{-|g_t - g_s|}; nothing is divided by a decay.
+//
+// Kernels:
+//   chunk_bwd_state  one workgroup per (batch, value head, 32-column slice of
+//                    Dv), walking the chunks from last to first with dH in MFMA
+//                    accumulators (fp32) and the next chunk's operands
+//                    prefetched.  Writes dv, eps (bf16), dH' of every chunk
+//                    (bf16, transposed) and dstate.
+//   chunk_bwd_grad   one workgroup per (chunk, batch, key head), looping over
+//                    the group's value heads and 32-column slabs of Dv.  Writes
+//                    dq, dk (after the L2-normalisation backward), da, db and
+//                    the per-chunk parameter sums.  Fixed summation order
+//                    throughout; no atomics.
+#include "gdn_dev.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int L = kChunk;
+constexpr int LP = L + 1;
+constexpr int NT = 256;
+
+// ------------------------------------------------------- reverse state pass
+
+template <int DK>
+struct ChunkBwdState {
+  static constexpr int NV = 32;        // Dv columns per workgroup
+  static constexpr int RTW = DK / 64;  // dH row tiles per wave
+  static constexpr int HS = DK + 8;    // bf16 row stride of dH^T
+  static constexpr int XS = L + 8;     // bf16 row stride of the [v][t] tiles
+  struct Smem {
+    alignas(16) bf16 hb[NV * HS];   // dH'^T, the B operand of K dH'
+    alignas(16) bf16 dob[NV * XS];  // dO^T
+    alignas(16) bf16 dos[NV * XS];  // (diag(e^g rq) dO)^T
+    alignas(16) bf16 rb[NV * XS];   // (diag(beta) rhs)^T
+    alignas(16) bf16 eb[NV * XS];   // Ehat^T
+    alignas(16) bf16 es[NV * XS];   // -(diag(e^g rk) Ehat)^T
+  };
+  // Operands of one chunk, prefetched a chunk ahead from clamped addresses
+  // (rows past the end of the sequence repeat its last row; their chunk
+  // scalars are zero and the chunk matrices are zero there).
+  struct Stage {
+    bf16x8 ka[DK / 32];               // k rows t = 16 w + lr
+    bf16x8 pqa[2], txa[2], ata[2];    // P^T, Tx^T, A^T rows t = 16 w + lr
+    bf16x8 qta[RTW][2], kta[RTW][2];  // Q^T, K^T rows i = 16 (w RTW + it) + lr
+    unsigned short dov[2][4];         // dO bits at rows 16 w + 4 lg + r, cols 16 ct + lr
+    float4 kl, bt, co, cr;            // chunk scalars at rows 16 w + 4 lg + r
+    float egl;
+  };
+  struct Lane {
+    int b, h, j, bh, bj, col0, w, lr, lg, ta, tc0, last, NC;
+    uint32_t qk_row, v_row;
+  };
+
+  __device__ static void load_stage(const ChunkBwdArgs& p, const Lane& q, int c, Stage& s) {
+    const Dims& d = p.d;
+    const int t0 = c * L, tl = q.last - t0;
+    const bf16* kc = static_cast<const bf16*>(p.k) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hk + q.j) * DK;
+    const uint32_t ko = static_cast<uint32_t>(min(q.ta, tl)) * q.qk_row + 8 * q.lg;
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = load_bf16x8(kc + ko + 32 * kt);
+    const size_t mat = (static_cast<size_t>(q.bh) * q.NC + c) * L * L;
+    const uint32_t mo = q.ta * L + 8 * q.lg;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s.pqa[kt] = load_bf16x8(p.cb.PqT + mat + mo + 32 * kt);
+      s.txa[kt] = load_bf16x8(p.cb.TxT + mat + mo + 32 * kt);
+      s.ata[kt] = load_bf16x8(p.cb.AtT + mat + mo + 32 * kt);
+    }
+    const size_t kt0 = (static_cast<size_t>(q.bj) * q.NC + c) * DK * L;
+    const uint32_t kto = (16 * q.w * RTW + q.lr) * L + 8 * q.lg;
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s.qta[it][kt] = load_bf16x8(p.cb.QT + kt0 + kto + (it * 16 * L + 32 * kt));
+        s.kta[it][kt] = load_bf16x8(p.cb.KT + kt0 + kto + (it * 16 * L + 32 * kt));
+      }
+    const unsigned short* dc = static_cast<const unsigned short*>(p.dO) +
+                               ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t vo = static_cast<uint32_t>(min(q.tc0 + r, tl)) * q.v_row + q.lr;
+      s.dov[0][r] = dc[vo];
+      s.dov[1][r] = (dc + vo)[16];
+    }
+    const float* scc = p.cb.sc + (static_cast<size_t>(q.bh) * q.NC + c) * SC_ROWS * L;
+    const float* scl = scc + q.tc0;
+    s.kl = *reinterpret_cast<const float4*>(scl + SC_KL * L);
+    s.bt = *reinterpret_cast<const float4*>(scl + SC_BETA * L);
+    s.co = *reinterpret_cast<const float4*>(scl + SC_CO * L);
+    s.cr = *reinterpret_cast<const float4*>(scl + SC_CR * L);
+    s.egl = scc[SC_EGL * L];
+  }
+
+  __device__ static void put_h(Smem& sm, const Lane& q, const f32x4 (&H)[RTW][2]) {
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        *reinterpret_cast<uint2*>(&sm.hb[(16 * ct + q.lr) * HS + 16 * (q.w * RTW + it) + 4 * q.lg]) =
+            pack4_bf16(H[it][ct][0], H[it][ct][1], H[it][ct][2], H[it][ct][3]);
+  }
+
+  __device__ static void step(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c,
+                              const Stage& cur, f32x4 (&dH)[RTW][2]) {
+    const Dims& d = p.d;
+    const int t0 = c * L, Lc = min(L, d.T - t0);
+    const int lr = q.lr, lg = q.lg;
+    const float klv[4] = {cur.kl.x, cur.kl.y, cur.kl.z, cur.kl.w};
+    const float btv[4] = {cur.bt.x, cur.bt.y, cur.bt.z, cur.bt.w};
+    const float cov[4] = {cur.co.x, cur.co.y, cur.co.z, cur.co.w};
+    const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
+
+    // dH' of this chunk for the gradient pass: [v][i], bf16
+    {
+      bf16* dh = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * d.Dv * DK +
+                 static_cast<size_t>(q.col0) * DK;
+#pragma unroll
+      for (int it = 0; it < RTW; ++it)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          *reinterpret_cast<uint2*>(dh + (16 * ct + lr) * DK + 16 * (q.w * RTW + it) + 4 * lg) =
+              pack4_bf16(dH[it][ct][0], dH[it][ct][1], dH[it][ct][2], dH[it][ct][3]);
+    }
+    // dO^T and diag(e^g rq) dO^T
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float dv4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dv4[r] = __uint_as_float(static_cast<uint32_t>(cur.dov[ct][r]) << 16);
+      *reinterpret_cast<uint2*>(&sm.dob[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(dv4[0], dv4[1], dv4[2], dv4[3]);
+      *reinterpret_cast<uint2*>(&sm.dos[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(cov[0] * dv4[0], cov[1] * dv4[1], cov[2] * dv4[2], cov[3] * dv4[3]);
+    }
+    lds_barrier();
+    // rhs = diag(e^{gL-g} rk) K dH' + P^T dO for row tile w
+    f32x4 kdh[2], rhs[2];
+    kdh[0] = kdh[1] = rhs[0] = rhs[1] = f4zero();
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        kdh[ct] = mfma16(cur.ka[kt], load_bf16x8(&sm.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), kdh[ct]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        rhs[ct] = mfma16(cur.pqa[kt], load_bf16x8(&sm.dob[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), rhs[ct]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rhs[ct][r] += klv[r] * kdh[ct][r];
+      *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(btv[0] * rhs[ct][0], btv[1] * rhs[ct][1], btv[2] * rhs[ct][2], btv[3] * rhs[ct][3]);
+    }
+    lds_barrier();
+    // Ehat = Tx^T diag(beta) rhs  (= dv)
+    f32x4 eh[2];
+    eh[0] = eh[1] = f4zero();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        eh[ct] = mfma16(cur.txa[kt], load_bf16x8(&sm.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), eh[ct]);
+    const size_t row0 = ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
+    {
+      bf16* dvc = static_cast<bf16*>(p.dv) + row0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = q.tc0 + r;
+        if (t < Lc) {
+          const uint32_t oo = static_cast<uint32_t>(t) * q.v_row + lr;
+          dvc[oo] = bf16_of(eh[0][r]);
+          (dvc + oo)[16] = bf16_of(eh[1][r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      *reinterpret_cast<uint2*>(&sm.eb[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(eh[ct][0], eh[ct][1], eh[ct][2], eh[ct][3]);
+      *reinterpret_cast<uint2*>(&sm.es[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(-crv[0] * eh[ct][0], -crv[1] * eh[ct][1], -crv[2] * eh[ct][2], -crv[3] * eh[ct][3]);
+    }
+    lds_barrier();
+    // eps = rhs - A^T Ehat
+    {
+      f32x4 ng[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ng[ct][r] = -rhs[ct][r];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          ng[ct] = mfma16(cur.ata[kt], load_bf16x8(&sm.eb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), ng[ct]);
+      bf16* ec = p.E + row0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = q.tc0 + r;
+        if (t < Lc) {
+          const uint32_t oo = static_cast<uint32_t>(t) * q.v_row + lr;
+          ec[oo] = bf16_of(-ng[0][r]);
+          (ec + oo)[16] = bf16_of(-ng[1][r]);
+        }
+      }
+    }
+    // dH = e^{gL} dH' + Q^T diag(e^g rq) dO - K^T diag(e^g rk) Ehat
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dH[it][ct][r] *= cur.egl;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 bq[2], be[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        bq[ct] = load_bf16x8(&sm.dos[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
+        be[ct] = load_bf16x8(&sm.es[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
+      }
+#pragma unroll
+      for (int it = 0; it < RTW; ++it)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          dH[it][ct] = mfma16(cur.qta[it][kt], bq[ct], dH[it][ct]);
+          dH[it][ct] = mfma16(cur.kta[it][kt], be[ct], dH[it][ct]);
+        }
+    }
+    put_h(sm, q, dH);
+    lds_barrier();
+  }
+
+  __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
+    const Dims& d = p.d;
+    Lane q;
+    const int nslice = d.Dv / NV;
+    int slice;
+    block_coords(d, nslice, q.b, q.h, slice);
+    q.NC = d.nchunk();
+    q.j = q.h / d.G();
+    q.bh = q.b * d.Hv + q.h;
+    q.bj = q.b * d.Hk + q.j;
+    q.col0 = slice * NV;
+    const int tid = threadIdx.x, l = tid & 63;
+    q.w = tid >> 6;
+    q.lr = l & 15;
+    q.lg = l >> 4;
+    q.ta = 16 * q.w + q.lr;
+    q.tc0 = 16 * q.w + 4 * q.lg;
+    q.last = d.T - 1;
+    q.qk_row = d.Hk * DK;
+    q.v_row = d.Hv * d.Dv;
+    const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
+
+    // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
+    f32x4 dH[RTW][2];
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
+          dH[it][ct][r] = p.dS_final ? p.dS_final[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
+        }
+    put_h(sm, q, dH);
+    lds_barrier();
+
+    Stage s0, s1;
+    if (q.NC > 0) load_stage(p, q, q.NC - 1, s0);
+    for (int c = q.NC - 1; c >= 0; c -= 2) {
+      if (c >= 1) load_stage(p, q, c - 1, s1);
+      step(p, sm, q, c, s0, dH);
+      if (c < 1) break;
+      if (c >= 2) load_stage(p, q, c - 2, s0);
+      step(p, sm, q, c - 1, s1, dH);
+    }
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
+          p.dstate[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = dH[it][ct][r];
+        }
+  }
+};
+
+template <int DK>
+__global__ void __launch_bounds__(NT) chunk_bwd_state_kernel(ChunkBwdArgs p) {
+  __shared__ typename ChunkBwdState<DK>::Smem sm;
+  ChunkBwdState<DK>::run(p, sm);
+}
+
+// ------------------------------------------------------------ gradient pass
+
+template <int DK>
+struct ChunkBwdGrad {
+  static constexpr int NS = 32;         // Dv columns per slab
+  static constexpr int IT = DK / 16;    // 16-row tiles of Dk
+  static constexpr int KS = DK / 32;    // MFMA steps over Dk
+  static constexpr int VS = NS + 8;     // bf16 row stride of [i][v] and [t][v] tiles
+  static constexpr int IS = DK + 8;     // bf16 row stride of [v][i] tiles
+  static constexpr int TS = L + 8;      // bf16 row stride of [v][t] tiles and Wq rows
+  static constexpr int WS = 2 * L + 8;  // bf16 row stride of [Wk1 | Wk2] rows
+  static constexpr int FS = DK + 4;     // fp32 row stride of the final accumulators
+  struct Slab {
+    bf16 hv[DK * VS];   // H   [i][v]
+    bf16 hi[NS * IS];   // H   [v][i]
+    bf16 dhv[DK * VS];  // dH' [i][v]
+    bf16 dhi[NS * IS];  // dH' [v][i]
+    bf16 rt[NS * TS];   // R   [v][t]
+    bf16 xr[L * VS];    // X   [t][v]
+    bf16 xs[L * VS];    // diag(e^{gL-g} beta) X   [t][v]
+  };
+  struct Head {
+    float dox[L * LP];  // dO_t . X_s
+    float xe[L * LP];   // X_t . eps_s
+    float m[L * LP];    // rectangle terms of dl (row r, column s), then row prefix sums
+    bf16 wq[L * TS];    // Wq diag(rk)   [t][s]
+    bf16 wk[L * WS];    // [Wk1 diag(rq) | Wk2 diag(rk)]   [t][r]
+  };
+  struct Fin {
+    float acc[L * FS];
+  };
+  union Big {
+    Slab s;
+    Head h;
+    Fin f;
+  };
+  struct Smem {
+    alignas(16) Big u;
+    float qk[L * LP], kk[L * LP];  // q_t . k_s and k_t . k_s (raw rows)
+    float rk[L], rq[L];
+    float gam[L], eg[L], el[L], beta[L], ell[L];
+    float av[L], bv[L], dbv[L];
+    float dll[L], dav[L];
+    float red[NT];
+  };
+
+  __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
+    const Dims& d = p.d;
+    const int c = blockIdx.x, bj = blockIdx.y;
+    const int b = bj / d.Hk, j = bj % d.Hk, G = d.G(), NC = d.nchunk();
+    const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int ta = 16 * w + lr, tc0 = 16 * w + 4 * lg;
+    const size_t qk0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;  // [B,T,Hk] index of step t0
+    const uint32_t qk_row = d.Hk * DK, v_row = d.Hv * d.Dv;
+    const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
+    const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
+    const size_t slab_sz = static_cast<size_t>(d.B) * d.Hv * DK * d.Dv;
+
+    if (tid < L) {
+      const bool in = tid < Lc;
+      sm.rk[tid] = in ? p.s.rk[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
+      sm.rq[tid] = in ? p.s.rq[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
+    }
+    // k, q rows of row tile w (clamped into the sequence), read from L2 where used
+    const bf16* kra = kc + static_cast<uint32_t>(min(ta, tl)) * qk_row + 8 * lg;
+    const bf16* qra = qc + static_cast<uint32_t>(min(ta, tl)) * qk_row + 8 * lg;
+    // raw Gram matrices of the chunk
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f32x4 gq = f4zero(), gk = f4zero();
+      const uint32_t o = static_cast<uint32_t>(min(16 * st + lr, tl)) * qk_row + 8 * lg;
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        const bf16x8 bk = load_bf16x8(kc + o + 32 * kt);
+        gq = mfma16(load_bf16x8(qra + 32 * kt), bk, gq);
+        gk = mfma16(load_bf16x8(kra + 32 * kt), bk, gk);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.qk[(tc0 + r) * LP + 16 * st + lr] = gq[r];
+        sm.kk[(tc0 + r) * LP + 16 * st + lr] = gk[r];
+      }
+    }
+    f32x4 accQ[IT], accK[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) accQ[it] = accK[it] = f4zero();
+    const bf16* ktc = p.cb.KT + (static_cast<size_t>(bj) * NC + c) * DK * L;
+    const bf16* qtc = p.cb.QT + (static_cast<size_t>(bj) * NC + c) * DK * L;
+
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = j * G + hh, bh = b * d.Hv + h;
+      const float* scc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
+      __syncthreads();  // the previous head is done with every shared array
+      if (tid < L) {
+        sm.gam[tid] = scc[SC_GAM * L + tid];
+        sm.eg[tid] = scc[SC_EG * L + tid];
+        sm.el[tid] = scc[SC_EL * L + tid];
+        sm.beta[tid] = scc[SC_BETA * L + tid];
+        sm.ell[tid] = tid < Lc ? p.s.ell[(static_cast<size_t>(b) * d.T + t0 + tid) * d.Hv + h] : 0.f;
+      }
+      const float egl = scc[SC_EGL * L];
+      __syncthreads();
+      const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta], sx = sm.el[ta] * sm.beta[ta];
+      float crv[4], cov[4], bev[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        crv[r] = sm.eg[tc0 + r] * sm.rk[tc0 + r];
+        cov[r] = sm.eg[tc0 + r] * sm.rq[tc0 + r];
+        bev[r] = sm.beta[tc0 + r];
+      }
+      bf16x8 txb[2];
+      {
+        const bf16* txc = p.cb.Tx + (static_cast<size_t>(bh) * NC + c) * L * L + ta * L + 8 * lg;
+        txb[0] = load_bf16x8(txc);
+        txb[1] = load_bf16x8(txc + 32);
+      }
+      const float* Hs = c == 0 ? p.state0 : p.ckpt + static_cast<size_t>(c - 1) * slab_sz;
+      if (Hs) Hs += static_cast<size_t>(bh) * DK * d.Dv;
+      const unsigned short* dHs = reinterpret_cast<const unsigned short*>(p.dHend) +
+                                  (static_cast<size_t>(c) * d.B * d.Hv + bh) * d.Dv * DK;
+      const size_t vbase = ((static_cast<size_t>(b) * d.T + t0) * d.Hv + h) * d.Dv;
+      const unsigned short* vg = static_cast<const unsigned short*>(p.v) + vbase;
+      const unsigned short* dog = static_cast<const unsigned short*>(p.dO) + vbase;
+      const unsigned short* eg_ = reinterpret_cast<const unsigned short*>(p.E) + vbase;
+      const uint32_t ra = static_cast<uint32_t>(min(ta, tl)) * v_row;  // row ta, clamped
+
+      f32x4 dox[4], xe[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) dox[st] = xe[st] = f4zero();
+      float pb[4] = {0.f, 0.f, 0.f, 0.f}, pa = 0.f, pdb = 0.f, phdh = 0.f;
+
+      for (int v0 = 0; v0 < d.Dv; v0 += NS) {
+        // ---- H and dH' slabs, both orientations, and <dH', H>
+        for (int blk = tid; blk < (DK / 4) * (NS / 4); blk += NT) {
+          const int i0 = 4 * (blk / (NS / 4)), vv0 = 4 * (blk % (NS / 4));
+          float hx[4][4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (Hs) f = *reinterpret_cast<const float4*>(Hs + static_cast<size_t>(i0 + a) * d.Dv + v0 + vv0);
+            hx[a][0] = f.x;
+            hx[a][1] = f.y;
+            hx[a][2] = f.z;
+            hx[a][3] = f.w;
+          }
+          uint2 dq[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dq[e] = *reinterpret_cast<const uint2*>(dHs + static_cast<size_t>(v0 + vv0 + e) * DK + i0);
+          unsigned short dv16[4][4];  // [a = i][e = v]
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dv16[0][e] = dq[e].x & 0xffffu;
+            dv16[1][e] = dq[e].x >> 16;
+            dv16[2][e] = dq[e].y & 0xffffu;
+            dv16[3][e] = dq[e].y >> 16;
+          }
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
+            *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) =
+                make_uint2(dv16[a][0] | (static_cast<uint32_t>(dv16[a][1]) << 16),
+                           dv16[a][2] | (static_cast<uint32_t>(dv16[a][3]) << 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              phdh = fmaf(hx[a][e], __uint_as_float(static_cast<uint32_t>(dv16[a][e]) << 16), phdh);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<uint2*>(&sm.u.s.hi[(vv0 + e) * IS + i0]) = pack4_bf16(hx[0][e], hx[1][e], hx[2][e], hx[3][e]);
+            *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) = dq[e];
+          }
+        }
+        __syncthreads();
+        // ---- K H, Q H (rows t = tc0 + r, cols 16 vt + lr) and (K dH')^T (rows v = 16 vt + 4 lg + r, col t = ta)
+        f32x4 kh[2], qh[2], kdt[2];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) kh[vt] = qh[vt] = kdt[vt] = f4zero();
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+          const bf16x8 ka = load_bf16x8(kra + 32 * kt), qa = load_bf16x8(qra + 32 * kt);
+#pragma unroll
+          for (int vt = 0; vt < 2; ++vt) {
+            const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * vt + lr) * IS + 32 * kt + 8 * lg]);
+            kh[vt] = mfma16(ka, bh8, kh[vt]);
+            qh[vt] = mfma16(qa, bh8, qh[vt]);
+            kdt[vt] = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * vt + lr) * IS + 32 * kt + 8 * lg]), ka, kdt[vt]);
+          }
+        }
+        // ---- R = V - diag(e^g rk) K H -> R^T; the b_r partial sums
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+          float rv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t o = static_cast<uint32_t>(min(tc0 + r, tl)) * v_row + v0 + 16 * vt + lr;
+            const float vv = __uint_as_float(static_cast<uint32_t>(vg[o]) << 16);
+            const float dov = __uint_as_float(static_cast<uint32_t>(dog[o]) << 16);
+            const float epv = __uint_as_float(static_cast<uint32_t>(eg_[o]) << 16);
+            rv[r] = vv - crv[r] * kh[vt][r];
+            pb[r] = fmaf(cov[r] * qh[vt][r], dov, pb[r]);
+            pb[r] = fmaf(-bev[r] * crv[r] * kh[vt][r], epv, pb[r]);
+          }
+          *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * vt + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
+        }
+        __syncthreads();
+        // ---- X^T = R^T Tx^T: the lane holds X[ta][16 vt + 4 lg + r]
+        {
+          f32x4 xt[2];
+          xt[0] = xt[1] = f4zero();
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt)
+              xt[vt] = mfma16(load_bf16x8(&sm.u.s.rt[(16 * vt + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt[vt]);
+#pragma unroll
+          for (int vt = 0; vt < 2; ++vt) {
+            const int vc = 16 * vt + 4 * lg;
+            *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = pack4_bf16(xt[vt][0], xt[vt][1], xt[vt][2], xt[vt][3]);
+            *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) =
+                pack4_bf16(sx * xt[vt][0], sx * xt[vt][1], sx * xt[vt][2], sx * xt[vt][3]);
+            const uint2 e4 = *reinterpret_cast<const uint2*>(eg_ + ra + v0 + vc);
+            pdb = fmaf(__uint_as_float(e4.x << 16), xt[vt][0], pdb);
+            pdb = fmaf(__uint_as_float(e4.x & 0xffff0000u), xt[vt][1], pdb);
+            pdb = fmaf(__uint_as_float(e4.y << 16), xt[vt][2], pdb);
+            pdb = fmaf(__uint_as_float(e4.y & 0xffff0000u), xt[vt][3], pdb);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pa = fmaf(kdt[vt][r], xt[vt][r], pa);
+          }
+        }
+        __syncthreads();
+        // ---- contractions over the slab's columns
+        {
+          const bf16x8 do8 = load_bf16x8(dog + ra + v0 + 8 * lg);
+          const bf16x8 dos8 = scale8(do8, sq);
+          const bf16x8 eps8 = scale8(load_bf16x8(eg_ + ra + v0 + 8 * lg), se);
+          const bf16x8 xs8 = load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]);
+          const bf16x8 xr8 = load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]);
+#pragma unroll
+          for (int it = 0; it < IT; ++it) {
+            const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
+            const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
+            accQ[it] = mfma16(dos8, bhv, accQ[it]);
+            accK[it] = mfma16(eps8, bhv, accK[it]);
+            accK[it] = mfma16(xs8, bdh, accK[it]);
+          }
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            dox[st] = mfma16(do8, load_bf16x8(&sm.u.s.xr[(16 * st + lr) * VS + 8 * lg]), dox[st]);
+            const uint32_t o = static_cast<uint32_t>(min(16 * st + lr, tl)) * v_row + v0 + 8 * lg;
+            xe[st] = mfma16(xr8, load_bf16x8(eg_ + o), xe[st]);
+          }
+        }
+        __syncthreads();
+      }
+
+      // ---- per-row sums of head h
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = row_sum16(pb[r]);
+        if (lr == 0) sm.bv[tc0 + r] = tc0 + r < Lc ? v : 0.f;
+      }
+      pa += __shfl_xor(pa, 16);
+      pa += __shfl_xor(pa, 32);
+      pdb += __shfl_xor(pdb, 16);
+      pdb += __shfl_xor(pdb, 32);
+      if (lg == 0) {
+        const bool in = ta < Lc;
+        sm.av[ta] = in ? sm.el[ta] * sm.beta[ta] * sm.rk[ta] * pa : 0.f;
+        sm.dbv[ta] = in ? pdb : 0.f;
+      }
+      sm.red[tid] = phdh;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sm.u.h.dox[(tc0 + r) * LP + 16 * st + lr] = dox[st][r];
+          sm.u.h.xe[(tc0 + r) * LP + 16 * st + lr] = xe[st][r];
+        }
+      __syncthreads();
+      // ---- L x L weights of head h and the rectangle terms of dl
+      {
+        const int t = tid >> 2, s0 = 16 * (tid & 3);
+        const bool tv = t < Lc;
+        const float gt = sm.gam[t], bt = sm.beta[t], rqt = sm.rq[t], rkt = sm.rk[t];
+        uint32_t wq2[8], w12[8], w22[8];
+        float lo[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int s = s0 + e;
+          const bool ok = tv && s < Lc;
+          const float dec = expf(-fabsf(gt - sm.gam[s]));
+          const float bs = sm.beta[s], rks = sm.rk[s];
+          const float doxts = sm.u.h.dox[t * LP + s], doxst = sm.u.h.dox[s * LP + t];
+          const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
+          const float wq = ok && s <= t ? dec * bs * doxts * rks : 0.f;
+          const float wk1 = ok && s >= t ? dec * bt * doxst * sm.rq[s] : 0.f;
+          const float wk2 = ok && s != t ? -bt * bs * dec * (s < t ? xest : xets) * rks : 0.f;
+          const float m = ok && s < t
+                              ? dec * bs * rks * (rqt * sm.qk[t * LP + s] * doxts - bt * rkt * sm.kk[t * LP + s] * xest)
+                              : 0.f;
+          sm.u.h.m[t * LP + s] = m;
+          if (e & 1) {
+            wq2[e >> 1] = pack2_bf16(lo[0], wq);
+            w12[e >> 1] = pack2_bf16(lo[1], wk1);
+            w22[e >> 1] = pack2_bf16(lo[2], wk2);
+          } else {
+            lo[0] = wq;
+            lo[1] = wk1;
+            lo[2] = wk2;
+          }
+        }
+        // m lives in its own array; the W rows go to their own arrays too
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          *reinterpret_cast<uint4*>(&sm.u.h.wq[t * TS + s0 + 8 * u]) =
+              make_uint4(wq2[4 * u], wq2[4 * u + 1], wq2[4 * u + 2], wq2[4 * u + 3]);
+          *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + s0 + 8 * u]) =
+              make_uint4(w12[4 * u], w12[4 * u + 1], w12[4 * u + 2], w12[4 * u + 3]);
+          *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + L + s0 + 8 * u]) =
+              make_uint4(w22[4 * u], w22[4 * u + 1], w22[4 * u + 2], w22[4 * u + 3]);
+        }
+      }
+      __syncthreads();
+      // ---- final products of head h: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 aq = load_bf16x8(&sm.u.h.wq[ta * TS + 32 * kt + 8 * lg]);
+        const bf16x8 a1 = load_bf16x8(&sm.u.h.wk[ta * WS + 32 * kt + 8 * lg]);
+        const bf16x8 a2 = load_bf16x8(&sm.u.h.wk[ta * WS + L + 32 * kt + 8 * lg]);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const uint32_t o = (16 * it + lr) * L + 32 * kt + 8 * lg;
+          const bf16x8 bk = load_bf16x8(ktc + o), bq = load_bf16x8(qtc + o);
+          accQ[it] = mfma16(aq, bk, accQ[it]);
+          accK[it] = mfma16(a1, bq, accK[it]);
+          accK[it] = mfma16(a2, bk, accK[it]);
+        }
+      }
+      // ---- dl: row prefix sums of the rectangle terms, then column sums
+      if (tid < L) {
+        float run = 0.f;
+        for (int s = 0; s < L; ++s) {
+          const float v = sm.u.h.m[tid * LP + s];
+          sm.u.h.m[tid * LP + s] = run;
+          run += v;
+        }
+      }
+      __syncthreads();
+      if (tid < L) {
+        const int t = tid;
+        float hdh = 0.f;
+        for (int i = 0; i < NT; ++i) hdh += sm.red[i];
+        float acc = egl * hdh;
+        for (int s = 0; s < t; ++s) acc += sm.av[s];
+        for (int r = t; r < L; ++r) acc += sm.bv[r] + sm.u.h.m[r * LP + t];
+        const float ell = sm.ell[t];
+        const float dl = expf(ell) == 0.f ? 0.f : acc;
+        float da = 0.f, db = 0.f, dll = 0.f;
+        if (t < Lc) {
+          const size_t ri = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
+          const bool valid = p.mask == nullptr || p.mask[static_cast<size_t>(b) * d.T + t0 + t] != 0;
+          if (valid) {
+            const float x = to_f32(static_cast<const bf16*>(p.a)[ri]) + p.dt_bias[h];
+            da = x <= kClamp ? dl * (-expf(p.A_log[h])) * sigmoid_f(fminf(x, kClamp)) : 0.f;
+            const float beta = sm.beta[t];
+            db = sm.dbv[t] * beta * (1.f - beta);
+            dll = dl != 0.f ? dl * ell : 0.f;
+          }
+          static_cast<bf16*>(p.da)[ri] = bf16_of(da);
+          static_cast<bf16*>(p.db)[ri] = bf16_of(db);
+        }
+        sm.dll[t] = dll;
+        sm.dav[t] = da;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        double sa = 0.0, sd = 0.0;
+        for (int t = 0; t < Lc; ++t) {
+          sa += sm.dll[t];
+          sd += sm.dav[t];
+        }
+        const size_t pi = (static_cast<size_t>(b) * NC + c) * d.Hv + h;
+        p.part_dA[pi] = sa;
+        p.part_ddt[pi] = sd;
+      }
+    }
+
+    // ---- L2-normalisation backward: dq = rq (dQn - Dk qn (qn . dQn)), dk = rk (dKn - kn (kn . dKn))
+    for (int pass = 0; pass < 2; ++pass) {
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sm.u.f.acc[(tc0 + r) * FS + 16 * it + lr] = pass == 0 ? accQ[it][r] : accK[it][r];
+      __syncthreads();
+      const int t = tid >> 2, qd = tid & 3;
+      constexpr int QW = DK / 4;  // columns per thread
+      const bf16* src = (pass == 0 ? qc : kc) + static_cast<size_t>(min(t, tl)) * qk_row + qd * QW;
+      float dot = 0.f;
+#pragma unroll
+      for (int u = 0; u < QW; u += 8) {
+        float x[8];
+        Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot = fmaf(x[e], sm.u.f.acc[t * FS + qd * QW + u + e], dot);
+      }
+      dot = quad_sum(dot);
+      if (t < Lc) {
+        const float r1 = pass == 0 ? sm.rq[t] : sm.rk[t];
+        const float coef = (pass == 0 ? static_cast<float>(DK) : 1.f) * r1 * r1 * dot;
+        bf16* dst = static_cast<bf16*>(pass == 0 ? p.dq : p.dk) + (qk0 + static_cast<size_t>(t) * d.Hk) * DK + qd * QW;
+#pragma unroll
+        for (int u = 0; u < QW; u += 8) {
+          float x[8];
+          Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), x);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = r1 * (sm.u.f.acc[t * FS + qd * QW + u + e] - coef * x[e]);
+          *reinterpret_cast<uint4*>(dst + u) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
+                                                          pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
+        }
+      }
+    }
+  }
+};
+
+template <int DK>
+__global__ void __launch_bounds__(NT) chunk_bwd_grad_kernel(ChunkBwdArgs p) {
+  __shared__ typename ChunkBwdGrad<DK>::Smem sm;
+  ChunkBwdGrad<DK>::run(p, sm);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
+  const int nblk = a.d.B * a.d.Hv * (a.d.Dv / ChunkBwdState<64>::NV);
+  switch (a.d.Dk) {
+    case 64: chunk_bwd_state_kernel<64><<<nblk, NT, 0, st>>>(a); break;
+    case 128: chunk_bwd_state_kernel<128><<<nblk, NT, 0, st>>>(a); break;
+    case 192: chunk_bwd_state_kernel<192><<<nblk, NT, 0, st>>>(a); break;
+    case 256: chunk_bwd_state_kernel<256><<<nblk, NT, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t st) {
+  if (a.d.T == 0) return hipSuccess;
+  dim3 grid(a.d.nchunk(), a.d.B * a.d.Hk);
+  switch (a.d.Dk) {
+    case 64: chunk_bwd_grad_kernel<64><<<grid, NT, 0, st>>>(a); break;
+    case 128: chunk_bwd_grad_kernel<128><<<grid, NT, 0, st>>>(a); break;
+    case 192: chunk_bwd_grad_kernel<192><<<grid, NT, 0, st>>>(a); break;
+    case 256: chunk_bwd_grad_kernel<256><<<grid, NT, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -37,14 +37,6 @@ constexpr int L = kChunk;
 constexpr int LP = L + 1;
 constexpr int NT = 256;
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<kQuadXor1>(v);
-  v += dpp<kQuadXor2>(v);
-  return v;
-}
-
-__device__ __forceinline__ bf16x8 zero8() { return as_bf16x8(make_uint4(0, 0, 0, 0)); }
-
 // ------------------------------------------------------------------ prep
 
 template <int DK>
@@ -105,6 +97,9 @@ struct ChunkPrep {
       sc[SC_KL * L + t] = el * sm.rk[t];
       sc[SC_BETA * L + t] = sm.beta[t];
       sc[SC_EGL * L + t] = t == 0 ? expf(gl) : 0.f;
+      sc[SC_GAM * L + t] = sm.gam[t];
+      sc[SC_EG * L + t] = eg;
+      sc[SC_EL * L + t] = el;
     }
 
     // ---- K K^T and Q K^T (raw rows): wave w computes row tile w
@@ -220,25 +215,6 @@ __global__ void __launch_bounds__(NT) chunk_prep_kernel(ChunkPrepArgs p) {
 }
 
 // ------------------------------------------------------------ state pass
-
-// Block index -> (b, h, slice).  Blocks of one (batch, key head) group go to
-// one XCD when the group count is a multiple of the XCD count (8); workgroups
-// are dealt to the XCDs round-robin in launch order.
-__device__ __forceinline__ void block_coords(const Dims& d, int nslice, int& b, int& h, int& slice) {
-  const int n = blockIdx.x, G = d.G(), groups = d.B * d.Hk, per = G * nslice;
-  int g, r;
-  if (groups % 8 == 0) {
-    const int xcd = n % 8, m = n / 8;
-    g = xcd + 8 * (m / per);
-    r = m % per;
-  } else {
-    g = n / per;
-    r = n % per;
-  }
-  b = g / d.Hk;
-  h = (g % d.Hk) * G + r / nslice;
-  slice = r % nslice;
-}
 
 template <int DK>
 struct ChunkFwd {

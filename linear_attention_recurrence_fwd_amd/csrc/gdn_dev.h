@@ -112,6 +112,23 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
   return as_bf16x8(*reinterpret_cast<const uint4*>(p));
 }
 __device__ __forceinline__ bf16 bf16_of(float v) { return from_f32<bf16>(v); }
+__device__ __forceinline__ bf16x8 zero8() { return as_bf16x8(make_uint4(0, 0, 0, 0)); }
+// Every bf16 of x multiplied by s (fp32 product, rounded to nearest even).
+__device__ __forceinline__ bf16x8 scale8(const bf16x8& x, float s) {
+  const uint4 u = __builtin_bit_cast(uint4, x);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack2_bf16(__uint_as_float(w[i] << 16) * s, __uint_as_float(w[i] & 0xffff0000u) * s);
+  return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+}
+// Sum over the 4 lanes of a DPP quad; every lane of the quad gets the same bits.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  return v;
+}
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // (lgkmcnt) and meets the other waves, without waiting for outstanding global

@@ -92,8 +92,30 @@ enum : int {
   SC_KL = 3,     // e^{g_L - g_t} rk_t
   SC_BETA = 4,   // beta_t
   SC_EGL = 5,    // [0] = e^{g_L}
-  SC_ROWS = 6
+  SC_GAM = 6,    // g_t
+  SC_EG = 7,     // e^{g_t}
+  SC_EL = 8,     // e^{g_L - g_t}
+  SC_ROWS = 9
 };
+
+// Block index -> (b, h, slice).  Blocks of one (batch, key head) group go to
+// one XCD when the group count is a multiple of the XCD count (8); workgroups
+// are dealt to the XCDs round-robin in launch order.
+__device__ inline void block_coords(const Dims& d, int nslice, int& b, int& h, int& slice) {
+  const int n = blockIdx.x, G = d.G(), groups = d.B * d.Hk, per = G * nslice;
+  int g, r;
+  if (groups % 8 == 0) {
+    const int xcd = n % 8, m = n / 8;
+    g = xcd + 8 * (m / per);
+    r = m % per;
+  } else {
+    g = n / per;
+    r = n % per;
+  }
+  b = g / d.Hk;
+  h = (g % d.Hk) * G + r / nslice;
+  slice = r % nslice;
+}
 
 struct ChunkPrepArgs {
   Dims d;
@@ -114,6 +136,25 @@ struct ChunkFwdArgs {
   float* ckpt;
 };
 
+// Chunk-form backward.  The reverse state pass writes dv, eps (dL/d delta) and
+// the per-chunk gradients w.r.t. the state at each chunk's end; the gradient
+// pass turns them into dq, dk, da, db and the per-chunk parameter sums.
+struct ChunkBwdArgs {
+  Dims d;
+  const void *q, *k, *v, *dO, *a;
+  const float *A_log, *dt_bias;
+  const uint8_t* mask;
+  const float *state0, *ckpt, *dS_final;  // state0 / dS_final may be null
+  StepScalars s;
+  ChunkBufs cb;
+  bf16* E;        // [B,T,Hv,Dv]  eps, rows t < T
+  bf16* dHend;    // [NC, B*Hv, Dv, Dk]  dL/d(state at the end of chunk c), transposed
+  void *dq, *dk, *dv, *da, *db;
+  float* dstate;     // [B,Hv,Dk,Dv]
+  double* part_dA;   // [B,NC,Hv] per-chunk sums of dl * l
+  double* part_ddt;  // [B,NC,Hv] per-chunk sums of da
+};
+
 struct ParamReduceArgs {
   int B, NC, Hv;
   const double *part_dA, *part_ddt;
@@ -127,6 +168,8 @@ hipError_t launch_chunk_grad(const ChunkGradArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t st);
 
 // The chunk form runs bf16 I/O with Dk a multiple of 32 and Dv a multiple of 32.
 inline bool chunk_supported(int Dk, int Dv, bool bf16) {
