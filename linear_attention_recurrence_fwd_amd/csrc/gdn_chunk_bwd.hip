@@ -326,16 +326,57 @@ __global__ void __launch_bounds__(NT) chunk_bwd_state_kernel(ChunkBwdArgs p) {
 
 // ------------------------------------------------------------ gradient pass
 
+constexpr int NTG = 512;  // threads of a gradient-pass workgroup (8 waves)
+
+// Scans over the 64 lanes of a wave, in lane order.
+__device__ __forceinline__ float wave_incl_prefix(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(v, off);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_incl_suffix(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_down(v, off);
+    if (lane + off < 64) v += y;
+  }
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+// Sum over the 8 lanes of a half DPP row (lanes 8k .. 8k+7); every lane of
+// the group ends with the same bits.
+__device__ __forceinline__ float oct_sum(float v) {
+  v = quad_sum(v);
+  return v + dpp<kRowHalfMirror>(v);
+}
+
 template <int DK>
 struct ChunkBwdGrad {
-  static constexpr int NS = 32;         // Dv columns per slab
-  static constexpr int IT = DK / 16;    // 16-row tiles of Dk
-  static constexpr int KS = DK / 32;    // MFMA steps over Dk
-  static constexpr int VS = NS + 8;     // bf16 row stride of [i][v] and [t][v] tiles
-  static constexpr int IS = DK + 8;     // bf16 row stride of [v][i] tiles
-  static constexpr int TS = L + 8;      // bf16 row stride of [v][t] tiles and Wq rows
-  static constexpr int WS = 2 * L + 8;  // bf16 row stride of [Wk1 | Wk2] rows
-  static constexpr int FS = DK + 4;     // fp32 row stride of the final accumulators
+  static constexpr int NS = 32;          // Dv columns per slab
+  static constexpr int IT = DK / 16;     // 16-row tiles of Dk
+  static constexpr int IH = IT / 2;      // tiles of Dk per wave
+  static constexpr int KS = DK / 32;     // MFMA steps over Dk
+  static constexpr int VS = NS + 8;      // bf16 row stride of [i][v] and [t][v] tiles
+  static constexpr int IS = DK + 8;      // bf16 row stride of [v][i] tiles
+  static constexpr int TS = L + 8;       // bf16 row stride of [v][t] tiles and Wq rows
+  static constexpr int WS = 2 * L + 8;   // bf16 row stride of [Wk1 | Wk2] rows
+  static constexpr int FS = DK + 4;      // fp32 row stride of the final accumulators
+  static constexpr int NB = (DK / 4) * (NS / 4);  // 4x4 blocks of one slab (<= NTG)
+  static_assert(NB <= NTG, "one block per thread");
   struct Slab {
     bf16 hv[DK * VS];   // H   [i][v]
     bf16 hi[NS * IS];   // H   [v][i]
@@ -344,11 +385,12 @@ struct ChunkBwdGrad {
     bf16 rt[NS * TS];   // R   [v][t]
     bf16 xr[L * VS];    // X   [t][v]
     bf16 xs[L * VS];    // diag(e^{gL-g} beta) X   [t][v]
+    bf16 vt[3][L * VS]; // v, dO, eps of the slab   [t][v]
   };
   struct Head {
     float dox[L * LP];  // dO_t . X_s
     float xe[L * LP];   // X_t . eps_s
-    float m[L * LP];    // rectangle terms of dl (row r, column s), then row prefix sums
+    float m[L * LP];    // rectangle terms of dl (row r, column s < r)
     bf16 wq[L * TS];    // Wq diag(rk)   [t][s]
     bf16 wk[L * WS];    // [Wk1 diag(rq) | Wk2 diag(rk)]   [t][r]
   };
@@ -362,271 +404,310 @@ struct ChunkBwdGrad {
   };
   struct Smem {
     alignas(16) Big u;
-    float qk[L * LP], kk[L * LP];  // q_t . k_s and k_t . k_s (raw rows)
     float rk[L], rq[L];
     float gam[L], eg[L], el[L], beta[L], ell[L];
-    float av[L], bv[L], dbv[L];
-    float dll[L], dav[L];
-    float red[NT];
+    float bv[2][L], pa[2][L], pdb[2][L], cs[L], rs[L];
+    float red[NTG / 64];
+  };
+  // Global data of one slab, loaded a slab ahead.
+  static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the v / dO / eps tiles
+  struct Pf {
+    float4 h[4];   // H rows i0 + a, cols vv0 .. vv0+3 (this thread's block)
+    uint2 dh[4];   // dH' at v = vv0 + e, rows i0 .. i0+3
+    uint4 ch[2];   // chunks tid and tid + NTG of the v / dO / eps tiles
+  };
+  struct Ctx {
+    int b, j, c, NC, t0, Lc, tl, i0, vv0;
+    uint32_t v_row;
+  };
+
+  __device__ static void prefetch(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, int v0, Pf& f) {
+    const Dims& d = p.d;
+    const int bh = x.b * d.Hv + h;
+    const float* Hs = x.c == 0 ? p.state0 : p.ckpt + (static_cast<size_t>(x.c - 1) * d.B * d.Hv) * DK * d.Dv;
+    if (Hs) {
+      const float* hp = Hs + static_cast<size_t>(bh) * DK * d.Dv + static_cast<size_t>(x.i0) * d.Dv + v0 + x.vv0;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) f.h[a] = *reinterpret_cast<const float4*>(hp + a * d.Dv);
+    } else {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) f.h[a] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const bf16* dhp = p.dHend + (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * d.Dv * DK +
+                      static_cast<size_t>(v0 + x.vv0) * DK + x.i0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.dh[e] = *reinterpret_cast<const uint2*>(dhp + e * DK);
+    const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv + v0;
+    const bf16* src[3] = {static_cast<const bf16*>(p.v) + vbase, static_cast<const bf16*>(p.dO) + vbase, p.E + vbase};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ci = min(tid + u * NTG, NCH - 1);
+      const int ten = ci / (L * NS / 8), row = (ci / (NS / 8)) % L, c8 = 8 * (ci % (NS / 8));
+      f.ch[u] = *reinterpret_cast<const uint4*>(src[ten] + static_cast<uint32_t>(min(row, x.tl)) * x.v_row + c8);
+    }
+  }
+  __device__ static void put_chunks(Smem& sm, int tid, const Pf& f) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ci = tid + u * NTG;
+      if (ci < NCH) {
+        const int ten = ci / (L * NS / 8), row = (ci / (NS / 8)) % L, c8 = 8 * (ci % (NS / 8));
+        *reinterpret_cast<uint4*>(&sm.u.s.vt[ten][row * VS + c8]) = f.ch[u];
+      }
+    }
+  }
+
+  // Lane coordinates.  Recomputed from an opaque copy of the thread index at
+  // the top of each loop so that the compiler rebuilds the addresses derived
+  // from them there instead of keeping them all live across the loops.
+  struct Lanes {
+    int tid, l, w, tt, hw, lr, lg, ta, tc0;
+    __device__ Lanes() {
+      tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      l = tid & 63;
+      w = tid >> 6;
+      tt = w & 3;
+      hw = w >> 2;
+      lr = l & 15;
+      lg = l >> 4;
+      ta = 16 * tt + lr;
+      tc0 = 16 * tt + 4 * lg;
+    }
   };
 
   __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
     const Dims& d = p.d;
-    const int c = blockIdx.x, bj = blockIdx.y;
-    const int b = bj / d.Hk, j = bj % d.Hk, G = d.G(), NC = d.nchunk();
-    const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int ta = 16 * w + lr, tc0 = 16 * w + 4 * lg;
-    const size_t qk0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;  // [B,T,Hk] index of step t0
-    const uint32_t qk_row = d.Hk * DK, v_row = d.Hv * d.Dv;
+    Ctx x;
+    x.c = blockIdx.x;
+    const int bj = blockIdx.y;
+    x.b = bj / d.Hk;
+    x.j = bj % d.Hk;
+    const int G = d.G();
+    x.NC = d.nchunk();
+    x.t0 = x.c * L;
+    x.Lc = min(L, d.T - x.t0);
+    x.tl = x.Lc - 1;
+    x.v_row = d.Hv * d.Dv;
+    const int Lc = x.Lc, c = x.c, NC = x.NC;
+    const size_t qk0 = (static_cast<size_t>(x.b) * d.T + x.t0) * d.Hk + x.j;  // [B,T,Hk] index of step t0
+    const uint32_t qk_row = d.Hk * DK;
     const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
     const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
-    const size_t slab_sz = static_cast<size_t>(d.B) * d.Hv * DK * d.Dv;
-
-    if (tid < L) {
-      const bool in = tid < Lc;
-      sm.rk[tid] = in ? p.s.rk[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
-      sm.rq[tid] = in ? p.s.rq[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
-    }
-    // k, q rows of row tile w (clamped into the sequence), read from L2 where used
-    const bf16* kra = kc + static_cast<uint32_t>(min(ta, tl)) * qk_row + 8 * lg;
-    const bf16* qra = qc + static_cast<uint32_t>(min(ta, tl)) * qk_row + 8 * lg;
-    // raw Gram matrices of the chunk
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      f32x4 gq = f4zero(), gk = f4zero();
-      const uint32_t o = static_cast<uint32_t>(min(16 * st + lr, tl)) * qk_row + 8 * lg;
-#pragma unroll
-      for (int kt = 0; kt < KS; ++kt) {
-        const bf16x8 bk = load_bf16x8(kc + o + 32 * kt);
-        gq = mfma16(load_bf16x8(qra + 32 * kt), bk, gq);
-        gk = mfma16(load_bf16x8(kra + 32 * kt), bk, gk);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sm.qk[(tc0 + r) * LP + 16 * st + lr] = gq[r];
-        sm.kk[(tc0 + r) * LP + 16 * st + lr] = gk[r];
-      }
-    }
-    f32x4 accQ[IT], accK[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) accQ[it] = accK[it] = f4zero();
     const bf16* ktc = p.cb.KT + (static_cast<size_t>(bj) * NC + c) * DK * L;
     const bf16* qtc = p.cb.QT + (static_cast<size_t>(bj) * NC + c) * DK * L;
+    const int tid0 = threadIdx.x;
+    const bool has_blk = tid0 < NB;
+    {
+      const int blk = min(tid0, NB - 1);
+      x.i0 = 4 * (blk / (NS / 4));
+      x.vv0 = 4 * (blk % (NS / 4));
+    }
+    if (tid0 < L) {
+      const bool in = tid0 < Lc;
+      sm.rk[tid0] = in ? p.s.rk[qk0 + static_cast<size_t>(tid0) * d.Hk] : 0.f;
+      sm.rq[tid0] = in ? p.s.rq[qk0 + static_cast<size_t>(tid0) * d.Hk] : 0.f;
+    }
+    f32x4 accQ[IH], accK[IH];
+#pragma unroll
+    for (int k = 0; k < IH; ++k) accQ[k] = accK[k] = f4zero();
 
+    const int nsl = d.Dv / NS;
+    Pf pf;
+    prefetch(p, x, tid0, x.j * G, 0, pf);
     for (int hh = 0; hh < G; ++hh) {
-      const int h = j * G + hh, bh = b * d.Hv + h;
+      const int h = x.j * G + hh, bh = x.b * d.Hv + h;
+      const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
       const float* scc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
+      const Lanes ln;
       __syncthreads();  // the previous head is done with every shared array
-      if (tid < L) {
-        sm.gam[tid] = scc[SC_GAM * L + tid];
-        sm.eg[tid] = scc[SC_EG * L + tid];
-        sm.el[tid] = scc[SC_EL * L + tid];
-        sm.beta[tid] = scc[SC_BETA * L + tid];
-        sm.ell[tid] = tid < Lc ? p.s.ell[(static_cast<size_t>(b) * d.T + t0 + tid) * d.Hv + h] : 0.f;
+      if (ln.tid < L) {
+        const int t = ln.tid;
+        sm.gam[t] = scc[SC_GAM * L + t];
+        sm.eg[t] = scc[SC_EG * L + t];
+        sm.el[t] = scc[SC_EL * L + t];
+        sm.beta[t] = scc[SC_BETA * L + t];
+        sm.ell[t] = t < Lc ? p.s.ell[(static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h] : 0.f;
       }
       const float egl = scc[SC_EGL * L];
-      __syncthreads();
-      const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta], sx = sm.el[ta] * sm.beta[ta];
-      float crv[4], cov[4], bev[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        crv[r] = sm.eg[tc0 + r] * sm.rk[tc0 + r];
-        cov[r] = sm.eg[tc0 + r] * sm.rq[tc0 + r];
-        bev[r] = sm.beta[tc0 + r];
-      }
       bf16x8 txb[2];
-      {
-        const bf16* txc = p.cb.Tx + (static_cast<size_t>(bh) * NC + c) * L * L + ta * L + 8 * lg;
-        txb[0] = load_bf16x8(txc);
-        txb[1] = load_bf16x8(txc + 32);
-      }
-      const float* Hs = c == 0 ? p.state0 : p.ckpt + static_cast<size_t>(c - 1) * slab_sz;
-      if (Hs) Hs += static_cast<size_t>(bh) * DK * d.Dv;
-      const unsigned short* dHs = reinterpret_cast<const unsigned short*>(p.dHend) +
-                                  (static_cast<size_t>(c) * d.B * d.Hv + bh) * d.Dv * DK;
-      const size_t vbase = ((static_cast<size_t>(b) * d.T + t0) * d.Hv + h) * d.Dv;
-      const unsigned short* vg = static_cast<const unsigned short*>(p.v) + vbase;
-      const unsigned short* dog = static_cast<const unsigned short*>(p.dO) + vbase;
-      const unsigned short* eg_ = reinterpret_cast<const unsigned short*>(p.E) + vbase;
-      const uint32_t ra = static_cast<uint32_t>(min(ta, tl)) * v_row;  // row ta, clamped
-
-      f32x4 dox[4], xe[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) dox[st] = xe[st] = f4zero();
+      txb[0] = load_bf16x8(p.cb.Tx + mat + ln.ta * L + 8 * ln.lg);
+      txb[1] = load_bf16x8(p.cb.Tx + mat + ln.ta * L + 32 + 8 * ln.lg);
+      __syncthreads();
+      f32x4 dox[2], xe[2];
+      dox[0] = dox[1] = xe[0] = xe[1] = f4zero();
       float pb[4] = {0.f, 0.f, 0.f, 0.f}, pa = 0.f, pdb = 0.f, phdh = 0.f;
 
-      for (int v0 = 0; v0 < d.Dv; v0 += NS) {
-        // ---- H and dH' slabs, both orientations, and <dH', H>
-        for (int blk = tid; blk < (DK / 4) * (NS / 4); blk += NT) {
-          const int i0 = 4 * (blk / (NS / 4)), vv0 = 4 * (blk % (NS / 4));
+      for (int si = 0; si < nsl; ++si) {
+        const Lanes q;
+        const int lr = q.lr, lg = q.lg, ta = q.ta, tc0 = q.tc0, hw = q.hw;
+        // ---- this slab's H and dH' into LDS (both orientations), <dH', H>; v / dO / eps tiles
+        if (has_blk) {
+          const int i0 = x.i0, vv0 = x.vv0;
           float hx[4][4];
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (Hs) f = *reinterpret_cast<const float4*>(Hs + static_cast<size_t>(i0 + a) * d.Dv + v0 + vv0);
-            hx[a][0] = f.x;
-            hx[a][1] = f.y;
-            hx[a][2] = f.z;
-            hx[a][3] = f.w;
-          }
-          uint2 dq[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dq[e] = *reinterpret_cast<const uint2*>(dHs + static_cast<size_t>(v0 + vv0 + e) * DK + i0);
-          unsigned short dv16[4][4];  // [a = i][e = v]
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dv16[0][e] = dq[e].x & 0xffffu;
-            dv16[1][e] = dq[e].x >> 16;
-            dv16[2][e] = dq[e].y & 0xffffu;
-            dv16[3][e] = dq[e].y >> 16;
+            hx[a][0] = pf.h[a].x;
+            hx[a][1] = pf.h[a].y;
+            hx[a][2] = pf.h[a].z;
+            hx[a][3] = pf.h[a].w;
           }
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
-            *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) =
-                make_uint2(dv16[a][0] | (static_cast<uint32_t>(dv16[a][1]) << 16),
-                           dv16[a][2] | (static_cast<uint32_t>(dv16[a][3]) << 16));
+            const uint32_t sh = a & 1 ? 16u : 0u;
+            uint32_t dv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              phdh = fmaf(hx[a][e], __uint_as_float(static_cast<uint32_t>(dv16[a][e]) << 16), phdh);
+            for (int e = 0; e < 4; ++e) dv[e] = ((a >> 1 ? pf.dh[e].y : pf.dh[e].x) >> sh) & 0xffffu;
+            *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
+            *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = make_uint2(dv[0] | (dv[1] << 16), dv[2] | (dv[3] << 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) phdh = fmaf(hx[a][e], __uint_as_float(dv[e] << 16), phdh);
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             *reinterpret_cast<uint2*>(&sm.u.s.hi[(vv0 + e) * IS + i0]) = pack4_bf16(hx[0][e], hx[1][e], hx[2][e], hx[3][e]);
-            *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) = dq[e];
+            *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) = pf.dh[e];
           }
         }
-        __syncthreads();
-        // ---- K H, Q H (rows t = tc0 + r, cols 16 vt + lr) and (K dH')^T (rows v = 16 vt + 4 lg + r, col t = ta)
-        f32x4 kh[2], qh[2], kdt[2];
+        put_chunks(sm, q.tid, pf);
+        {  // next slab (of this head or the next one)
+          const int nsi = si + 1 < nsl ? si + 1 : 0;
+          const int nh = si + 1 < nsl ? h : h + 1;
+          if (nh < x.j * G + G) prefetch(p, x, q.tid, nh, nsi * NS, pf);
+        }
+        lds_barrier();
+        const bf16* vt = sm.u.s.vt[0];
+        const bf16* dt = sm.u.s.vt[1];
+        const bf16* et = sm.u.s.vt[2];
+        // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta)
+        f32x4 kh = f4zero(), qh = f4zero(), kdt = f4zero();
+        {
+          const bf16* kra = kc + static_cast<uint32_t>(min(ta, x.tl)) * qk_row + 8 * lg;
+          const bf16* qra = qc + static_cast<uint32_t>(min(ta, x.tl)) * qk_row + 8 * lg;
 #pragma unroll
-        for (int vt = 0; vt < 2; ++vt) kh[vt] = qh[vt] = kdt[vt] = f4zero();
-#pragma unroll
-        for (int kt = 0; kt < KS; ++kt) {
-          const bf16x8 ka = load_bf16x8(kra + 32 * kt), qa = load_bf16x8(qra + 32 * kt);
-#pragma unroll
-          for (int vt = 0; vt < 2; ++vt) {
-            const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * vt + lr) * IS + 32 * kt + 8 * lg]);
-            kh[vt] = mfma16(ka, bh8, kh[vt]);
-            qh[vt] = mfma16(qa, bh8, qh[vt]);
-            kdt[vt] = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * vt + lr) * IS + 32 * kt + 8 * lg]), ka, kdt[vt]);
+          for (int kt = 0; kt < KS; ++kt) {
+            const bf16x8 ka = load_bf16x8(kra + 32 * kt), qa = load_bf16x8(qra + 32 * kt);
+            const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]);
+            kh = mfma16(ka, bh8, kh);
+            qh = mfma16(qa, bh8, qh);
+            kdt = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]), ka, kdt);
           }
         }
-        // ---- R = V - diag(e^g rk) K H -> R^T; the b_r partial sums
-#pragma unroll
-        for (int vt = 0; vt < 2; ++vt) {
+        // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
+        {
           float rv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t o = static_cast<uint32_t>(min(tc0 + r, tl)) * v_row + v0 + 16 * vt + lr;
-            const float vv = __uint_as_float(static_cast<uint32_t>(vg[o]) << 16);
-            const float dov = __uint_as_float(static_cast<uint32_t>(dog[o]) << 16);
-            const float epv = __uint_as_float(static_cast<uint32_t>(eg_[o]) << 16);
-            rv[r] = vv - crv[r] * kh[vt][r];
-            pb[r] = fmaf(cov[r] * qh[vt][r], dov, pb[r]);
-            pb[r] = fmaf(-bev[r] * crv[r] * kh[vt][r], epv, pb[r]);
+            const int t = tc0 + r, o = t * VS + 16 * hw + lr;
+            const float eg = sm.eg[t], cr = eg * sm.rk[t];
+            const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), epv = to_f32(et[o]);
+            rv[r] = vv - cr * kh[r];
+            pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, pb[r]);
+            pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, pb[r]);
           }
-          *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * vt + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
+          *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
         }
-        __syncthreads();
-        // ---- X^T = R^T Tx^T: the lane holds X[ta][16 vt + 4 lg + r]
+        lds_barrier();
+        // ---- X^T = R^T Tx^T: the lane holds X[ta][16 hw + 4 lg + r]
         {
-          f32x4 xt[2];
-          xt[0] = xt[1] = f4zero();
+          f32x4 xt = f4zero();
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
+            xt = mfma16(load_bf16x8(&sm.u.s.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
+          const int vc = 16 * hw + 4 * lg;
+          const float sx = sm.el[ta] * sm.beta[ta];
+          *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
+          *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) = pack4_bf16(sx * xt[0], sx * xt[1], sx * xt[2], sx * xt[3]);
+          const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
+          const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
+                                __uint_as_float(e4.y << 16), __uint_as_float(e4.y & 0xffff0000u)};
 #pragma unroll
-            for (int vt = 0; vt < 2; ++vt)
-              xt[vt] = mfma16(load_bf16x8(&sm.u.s.rt[(16 * vt + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt[vt]);
-#pragma unroll
-          for (int vt = 0; vt < 2; ++vt) {
-            const int vc = 16 * vt + 4 * lg;
-            *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = pack4_bf16(xt[vt][0], xt[vt][1], xt[vt][2], xt[vt][3]);
-            *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) =
-                pack4_bf16(sx * xt[vt][0], sx * xt[vt][1], sx * xt[vt][2], sx * xt[vt][3]);
-            const uint2 e4 = *reinterpret_cast<const uint2*>(eg_ + ra + v0 + vc);
-            pdb = fmaf(__uint_as_float(e4.x << 16), xt[vt][0], pdb);
-            pdb = fmaf(__uint_as_float(e4.x & 0xffff0000u), xt[vt][1], pdb);
-            pdb = fmaf(__uint_as_float(e4.y << 16), xt[vt][2], pdb);
-            pdb = fmaf(__uint_as_float(e4.y & 0xffff0000u), xt[vt][3], pdb);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pa = fmaf(kdt[vt][r], xt[vt][r], pa);
+          for (int r = 0; r < 4; ++r) {
+            pdb = fmaf(e4f[r], xt[r], pdb);
+            pa = fmaf(kdt[r], xt[r], pa);
           }
         }
-        __syncthreads();
+        lds_barrier();
         // ---- contractions over the slab's columns
         {
-          const bf16x8 do8 = load_bf16x8(dog + ra + v0 + 8 * lg);
-          const bf16x8 dos8 = scale8(do8, sq);
-          const bf16x8 eps8 = scale8(load_bf16x8(eg_ + ra + v0 + 8 * lg), se);
+          const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta];
+          const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
+          const bf16x8 dos8 = scale8(do8, sq), eps8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), se);
           const bf16x8 xs8 = load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]);
           const bf16x8 xr8 = load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]);
 #pragma unroll
-          for (int it = 0; it < IT; ++it) {
+          for (int k = 0; k < IH; ++k) {
+            const int it = hw * IH + k;
             const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
             const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
-            accQ[it] = mfma16(dos8, bhv, accQ[it]);
-            accK[it] = mfma16(eps8, bhv, accK[it]);
-            accK[it] = mfma16(xs8, bdh, accK[it]);
+            accQ[k] = mfma16(dos8, bhv, accQ[k]);
+            accK[k] = mfma16(eps8, bhv, accK[k]);
+            accK[k] = mfma16(xs8, bdh, accK[k]);
           }
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            dox[st] = mfma16(do8, load_bf16x8(&sm.u.s.xr[(16 * st + lr) * VS + 8 * lg]), dox[st]);
-            const uint32_t o = static_cast<uint32_t>(min(16 * st + lr, tl)) * v_row + v0 + 8 * lg;
-            xe[st] = mfma16(xr8, load_bf16x8(eg_ + o), xe[st]);
+          for (int u = 0; u < 2; ++u) {
+            const int sr = (16 * (2 * hw + u) + lr) * VS + 8 * lg;
+            dox[u] = mfma16(do8, load_bf16x8(&sm.u.s.xr[sr]), dox[u]);
+            xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), xe[u]);
           }
         }
-        __syncthreads();
+        lds_barrier();
       }
 
       // ---- per-row sums of head h
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = row_sum16(pb[r]);
-        if (lr == 0) sm.bv[tc0 + r] = tc0 + r < Lc ? v : 0.f;
-      }
-      pa += __shfl_xor(pa, 16);
-      pa += __shfl_xor(pa, 32);
-      pdb += __shfl_xor(pdb, 16);
-      pdb += __shfl_xor(pdb, 32);
-      if (lg == 0) {
-        const bool in = ta < Lc;
-        sm.av[ta] = in ? sm.el[ta] * sm.beta[ta] * sm.rk[ta] * pa : 0.f;
-        sm.dbv[ta] = in ? pdb : 0.f;
-      }
-      sm.red[tid] = phdh;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
+      {
+        const Lanes q;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          sm.u.h.dox[(tc0 + r) * LP + 16 * st + lr] = dox[st][r];
-          sm.u.h.xe[(tc0 + r) * LP + 16 * st + lr] = xe[st][r];
+          const float v = row_sum16(pb[r]);
+          if (q.lr == 0) sm.bv[q.hw][q.tc0 + r] = v;
         }
-      __syncthreads();
-      // ---- L x L weights of head h and the rectangle terms of dl
-      {
-        const int t = tid >> 2, s0 = 16 * (tid & 3);
-        const bool tv = t < Lc;
-        const float gt = sm.gam[t], bt = sm.beta[t], rqt = sm.rq[t], rkt = sm.rk[t];
-        uint32_t wq2[8], w12[8], w22[8];
-        float lo[3] = {0.f, 0.f, 0.f};
+        pa += __shfl_xor(pa, 16);
+        pa += __shfl_xor(pa, 32);
+        pdb += __shfl_xor(pdb, 16);
+        pdb += __shfl_xor(pdb, 32);
+        if (q.lg == 0) {
+          sm.pa[q.hw][q.ta] = pa;
+          sm.pdb[q.hw][q.ta] = pdb;
+        }
+        phdh = wave_sum(phdh);
+        if (q.l == 0) sm.red[q.w] = phdh;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sm.u.h.dox[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = dox[u][r];
+            sm.u.h.xe[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = xe[u][r];
+          }
+      }
+      __syncthreads();
+      // ---- L x L weights of head h, the rectangle terms of dl and their row sums
+      {
+        const Lanes q;
+        const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
+        const bool tv = t < Lc;
+        const float gt = sm.gam[t], bt = sm.beta[t];
+        // P[t][s] = P^T[s][t] and A[t][s] = A^T[s][t] of the chunk (bf16, with decays and norms)
+        const unsigned short* pqc = reinterpret_cast<const unsigned short*>(p.cb.PqT) + mat + t;
+        const unsigned short* atc = reinterpret_cast<const unsigned short*>(p.cb.AtT) + mat + t;
+        uint32_t wq2[4], w12[4], w22[4];
+        float lo[3] = {0.f, 0.f, 0.f}, rsum = 0.f;
+#pragma unroll 2
+        for (int e = 0; e < 8; ++e) {
           const int s = s0 + e;
           const bool ok = tv && s < Lc;
           const float dec = expf(-fabsf(gt - sm.gam[s]));
           const float bs = sm.beta[s], rks = sm.rk[s];
           const float doxts = sm.u.h.dox[t * LP + s], doxst = sm.u.h.dox[s * LP + t];
           const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
+          const float ptv = __uint_as_float(static_cast<uint32_t>(pqc[s * L]) << 16);
+          const float atv = __uint_as_float(static_cast<uint32_t>(atc[s * L]) << 16);
           const float wq = ok && s <= t ? dec * bs * doxts * rks : 0.f;
           const float wk1 = ok && s >= t ? dec * bt * doxst * sm.rq[s] : 0.f;
           const float wk2 = ok && s != t ? -bt * bs * dec * (s < t ? xest : xets) * rks : 0.f;
-          const float m = ok && s < t
-                              ? dec * bs * rks * (rqt * sm.qk[t * LP + s] * doxts - bt * rkt * sm.kk[t * LP + s] * xest)
-                              : 0.f;
+          const float m = ok && s < t ? bs * (ptv * doxts - bt * atv * xest) : 0.f;
           sm.u.h.m[t * LP + s] = m;
+          rsum += m;
           if (e & 1) {
             wq2[e >> 1] = pack2_bf16(lo[0], wq);
             w12[e >> 1] = pack2_bf16(lo[1], wk1);
@@ -637,114 +718,112 @@ struct ChunkBwdGrad {
             lo[2] = wk2;
           }
         }
-        // m lives in its own array; the W rows go to their own arrays too
+        *reinterpret_cast<uint4*>(&sm.u.h.wq[t * TS + s0]) = make_uint4(wq2[0], wq2[1], wq2[2], wq2[3]);
+        *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + s0]) = make_uint4(w12[0], w12[1], w12[2], w12[3]);
+        *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + L + s0]) = make_uint4(w22[0], w22[1], w22[2], w22[3]);
+        rsum = oct_sum(rsum);
+        if ((q.tid & 7) == 0) sm.rs[t] = rsum;
+      }
+      __syncthreads();
+      // ---- column sums of the rectangle terms; final products of head h
+      {
+        const Lanes q;
+        {
+          const int s = q.tid >> 3, r0 = 8 * (q.tid & 7);
+          float csum = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          *reinterpret_cast<uint4*>(&sm.u.h.wq[t * TS + s0 + 8 * u]) =
-              make_uint4(wq2[4 * u], wq2[4 * u + 1], wq2[4 * u + 2], wq2[4 * u + 3]);
-          *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + s0 + 8 * u]) =
-              make_uint4(w12[4 * u], w12[4 * u + 1], w12[4 * u + 2], w12[4 * u + 3]);
-          *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + L + s0 + 8 * u]) =
-              make_uint4(w22[4 * u], w22[4 * u + 1], w22[4 * u + 2], w22[4 * u + 3]);
+          for (int e = 0; e < 8; ++e) csum += sm.u.h.m[(r0 + e) * LP + s];
+          csum = oct_sum(csum);
+          if ((q.tid & 7) == 0) sm.cs[s] = csum;
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 aq = load_bf16x8(&sm.u.h.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
+          const bf16x8 a1 = load_bf16x8(&sm.u.h.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
+          const bf16x8 a2 = load_bf16x8(&sm.u.h.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
+#pragma unroll
+          for (int k = 0; k < IH; ++k) {
+            const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
+            const bf16x8 bk = load_bf16x8(ktc + o), bq = load_bf16x8(qtc + o);
+            accQ[k] = mfma16(aq, bk, accQ[k]);
+            accK[k] = mfma16(a1, bq, accK[k]);
+            accK[k] = mfma16(a2, bk, accK[k]);
+          }
         }
       }
       __syncthreads();
-      // ---- final products of head h: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 aq = load_bf16x8(&sm.u.h.wq[ta * TS + 32 * kt + 8 * lg]);
-        const bf16x8 a1 = load_bf16x8(&sm.u.h.wk[ta * WS + 32 * kt + 8 * lg]);
-        const bf16x8 a2 = load_bf16x8(&sm.u.h.wk[ta * WS + L + 32 * kt + 8 * lg]);
-#pragma unroll
-        for (int it = 0; it < IT; ++it) {
-          const uint32_t o = (16 * it + lr) * L + 32 * kt + 8 * lg;
-          const bf16x8 bk = load_bf16x8(ktc + o), bq = load_bf16x8(qtc + o);
-          accQ[it] = mfma16(aq, bk, accQ[it]);
-          accK[it] = mfma16(a1, bq, accK[it]);
-          accK[it] = mfma16(a2, bk, accK[it]);
-        }
-      }
-      // ---- dl: row prefix sums of the rectangle terms, then column sums
-      if (tid < L) {
-        float run = 0.f;
-        for (int s = 0; s < L; ++s) {
-          const float v = sm.u.h.m[tid * LP + s];
-          sm.u.h.m[tid * LP + s] = run;
-          run += v;
-        }
-      }
-      __syncthreads();
-      if (tid < L) {
-        const int t = tid;
+      // ---- dl_t = e^{gL} <dH', H> + sum_{u<t} (a_u + cs_u - rs_u) + sum_{r>=t} b_r; da, db
+      if (tid0 < 64) {
+        const int t = tid0;
+        const bool in = t < Lc;
         float hdh = 0.f;
-        for (int i = 0; i < NT; ++i) hdh += sm.red[i];
-        float acc = egl * hdh;
-        for (int s = 0; s < t; ++s) acc += sm.av[s];
-        for (int r = t; r < L; ++r) acc += sm.bv[r] + sm.u.h.m[r * LP + t];
+#pragma unroll
+        for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[i];
+        const float av = in ? sm.el[t] * sm.beta[t] * sm.rk[t] * (sm.pa[0][t] + sm.pa[1][t]) : 0.f;
+        const float bvv = in ? sm.bv[0][t] + sm.bv[1][t] : 0.f;
+        const float uv = av + sm.cs[t] - sm.rs[t];
+        float pre = __shfl_up(wave_incl_prefix(uv), 1);
+        if (t == 0) pre = 0.f;
+        const float suf = wave_incl_suffix(bvv);
         const float ell = sm.ell[t];
-        const float dl = expf(ell) == 0.f ? 0.f : acc;
+        const float dl = expf(ell) == 0.f ? 0.f : egl * hdh + pre + suf;
         float da = 0.f, db = 0.f, dll = 0.f;
-        if (t < Lc) {
-          const size_t ri = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
-          const bool valid = p.mask == nullptr || p.mask[static_cast<size_t>(b) * d.T + t0 + t] != 0;
+        if (in) {
+          const size_t ri = (static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h;
+          const bool valid = p.mask == nullptr || p.mask[static_cast<size_t>(x.b) * d.T + x.t0 + t] != 0;
           if (valid) {
-            const float x = to_f32(static_cast<const bf16*>(p.a)[ri]) + p.dt_bias[h];
-            da = x <= kClamp ? dl * (-expf(p.A_log[h])) * sigmoid_f(fminf(x, kClamp)) : 0.f;
+            const float xa = to_f32(static_cast<const bf16*>(p.a)[ri]) + p.dt_bias[h];
+            da = xa <= kClamp ? dl * (-expf(p.A_log[h])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
             const float beta = sm.beta[t];
-            db = sm.dbv[t] * beta * (1.f - beta);
+            db = (sm.pdb[0][t] + sm.pdb[1][t]) * beta * (1.f - beta);
             dll = dl != 0.f ? dl * ell : 0.f;
           }
           static_cast<bf16*>(p.da)[ri] = bf16_of(da);
           static_cast<bf16*>(p.db)[ri] = bf16_of(db);
         }
-        sm.dll[t] = dll;
-        sm.dav[t] = da;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        double sa = 0.0, sd = 0.0;
-        for (int t = 0; t < Lc; ++t) {
-          sa += sm.dll[t];
-          sd += sm.dav[t];
+        const double sa = wave_sum_f64(static_cast<double>(dll));
+        const double sd = wave_sum_f64(static_cast<double>(da));
+        if (t == 0) {
+          const size_t pi = (static_cast<size_t>(x.b) * NC + c) * d.Hv + h;
+          p.part_dA[pi] = sa;
+          p.part_ddt[pi] = sd;
         }
-        const size_t pi = (static_cast<size_t>(b) * NC + c) * d.Hv + h;
-        p.part_dA[pi] = sa;
-        p.part_ddt[pi] = sd;
       }
     }
 
     // ---- L2-normalisation backward: dq = rq (dQn - Dk qn (qn . dQn)), dk = rk (dKn - kn (kn . dKn))
     for (int pass = 0; pass < 2; ++pass) {
+      const Lanes q;
       __syncthreads();
 #pragma unroll
-      for (int it = 0; it < IT; ++it)
+      for (int k = 0; k < IH; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          sm.u.f.acc[(tc0 + r) * FS + 16 * it + lr] = pass == 0 ? accQ[it][r] : accK[it][r];
+          sm.u.f.acc[(q.tc0 + r) * FS + 16 * (q.hw * IH + k) + q.lr] = pass == 0 ? accQ[k][r] : accK[k][r];
       __syncthreads();
-      const int t = tid >> 2, qd = tid & 3;
-      constexpr int QW = DK / 4;  // columns per thread
-      const bf16* src = (pass == 0 ? qc : kc) + static_cast<size_t>(min(t, tl)) * qk_row + qd * QW;
+      const int t = q.tid >> 3, qd = q.tid & 7;
+      constexpr int QW = DK / 8;  // columns per thread
+      const bf16* src = (pass == 0 ? qc : kc) + static_cast<size_t>(min(t, x.tl)) * qk_row + qd * QW;
+      const float* ac = &sm.u.f.acc[t * FS + qd * QW];
       float dot = 0.f;
 #pragma unroll
       for (int u = 0; u < QW; u += 8) {
-        float x[8];
-        Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), x);
+        float xv[8];
+        Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), xv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(x[e], sm.u.f.acc[t * FS + qd * QW + u + e], dot);
+        for (int e = 0; e < 8; ++e) dot = fmaf(xv[e], ac[u + e], dot);
       }
-      dot = quad_sum(dot);
+      dot = oct_sum(dot);
       if (t < Lc) {
         const float r1 = pass == 0 ? sm.rq[t] : sm.rk[t];
         const float coef = (pass == 0 ? static_cast<float>(DK) : 1.f) * r1 * r1 * dot;
         bf16* dst = static_cast<bf16*>(pass == 0 ? p.dq : p.dk) + (qk0 + static_cast<size_t>(t) * d.Hk) * DK + qd * QW;
 #pragma unroll
         for (int u = 0; u < QW; u += 8) {
-          float x[8];
-          Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), x);
-          float y[8];
+          float xv[8], y[8];
+          Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), xv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = r1 * (sm.u.f.acc[t * FS + qd * QW + u + e] - coef * x[e]);
+          for (int e = 0; e < 8; ++e) y[e] = r1 * (ac[u + e] - coef * xv[e]);
           *reinterpret_cast<uint4*>(dst + u) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
                                                           pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
         }
@@ -754,7 +833,7 @@ struct ChunkBwdGrad {
 };
 
 template <int DK>
-__global__ void __launch_bounds__(NT) chunk_bwd_grad_kernel(ChunkBwdArgs p) {
+__global__ void __launch_bounds__(NTG) chunk_bwd_grad_kernel(ChunkBwdArgs p) {
   __shared__ typename ChunkBwdGrad<DK>::Smem sm;
   ChunkBwdGrad<DK>::run(p, sm);
 }
@@ -777,10 +856,10 @@ hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t st) {
   if (a.d.T == 0) return hipSuccess;
   dim3 grid(a.d.nchunk(), a.d.B * a.d.Hk);
   switch (a.d.Dk) {
-    case 64: chunk_bwd_grad_kernel<64><<<grid, NT, 0, st>>>(a); break;
-    case 128: chunk_bwd_grad_kernel<128><<<grid, NT, 0, st>>>(a); break;
-    case 192: chunk_bwd_grad_kernel<192><<<grid, NT, 0, st>>>(a); break;
-    case 256: chunk_bwd_grad_kernel<256><<<grid, NT, 0, st>>>(a); break;
+    case 64: chunk_bwd_grad_kernel<64><<<grid, NTG, 0, st>>>(a); break;
+    case 128: chunk_bwd_grad_kernel<128><<<grid, NTG, 0, st>>>(a); break;
+    case 192: chunk_bwd_grad_kernel<192><<<grid, NTG, 0, st>>>(a); break;
+    case 256: chunk_bwd_grad_kernel<256><<<grid, NTG, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
