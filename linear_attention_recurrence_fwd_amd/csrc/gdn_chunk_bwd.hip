@@ -391,8 +391,12 @@ struct ChunkBwdGrad {
     float dox[L * LP];  // dO_t . X_s
     float xe[L * LP];   // X_t . eps_s
     float m[L * LP];    // rectangle terms of dl (row r, column s < r)
-    bf16 wq[L * TS];    // Wq diag(rk)   [t][s]
-    bf16 wk[L * WS];    // [Wk1 diag(rq) | Wk2 diag(rk)]   [t][r]
+    bf16 pt[L * TS];    // P^T of the chunk   [s][t]
+    bf16 at[L * TS];    // A^T of the chunk   [s][t]
+  };
+  struct Wts {
+    bf16 wq[L * TS];    // sum over the group of Wq diag(rk)   [t][s]
+    bf16 wk[L * WS];    // sum over the group of [Wk1 diag(rq) | Wk2 diag(rk)]   [t][r]
   };
   struct Fin {
     float acc[L * FS];
@@ -400,14 +404,27 @@ struct ChunkBwdGrad {
   union Big {
     Slab s;
     Head h;
+    Wts w;
     Fin f;
   };
   struct Smem {
     alignas(16) Big u;
+    float wsq[L * LP], ws1[L * LP], ws2[L * LP];  // fp32 sums over the group's heads of Wq, Wk1, Wk2
     float rk[L], rq[L];
     float gam[L], eg[L], el[L], beta[L], ell[L];
     float bv[2][L], pa[2][L], pdb[2][L], cs[L], rs[L];
     float red[NTG / 64];
+  };
+  // Per-head data loaded ahead: the scalars and Tx rows a head starts with,
+  // and what its tail needs (the chunk's P^T / A^T tiles, a and the mask).
+  struct HeadStart {
+    float gam, eg, el, beta, ell, egl;  // step t = tid (tid < L)
+    bf16x8 txb[2];                      // Tx row ta
+  };
+  struct HeadTail {
+    uint4 pt, at;           // chunk tid of P^T / A^T (row tid >> 3, cols 8 (tid & 7) ..)
+    unsigned short a_bits;  // a at step t = tid (tid < L)
+    unsigned char valid;
   };
   // Global data of one slab, loaded a slab ahead.
   static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the v / dO / eps tiles
@@ -446,6 +463,33 @@ struct ChunkBwdGrad {
       f.ch[u] = *reinterpret_cast<const uint4*>(src[ten] + static_cast<uint32_t>(min(row, x.tl)) * x.v_row + c8);
     }
   }
+  __device__ static void load_start(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, HeadStart& hs) {
+    const Dims& d = p.d;
+    const int bh = x.b * d.Hv + h;
+    const float* scc = p.cb.sc + (static_cast<size_t>(bh) * x.NC + x.c) * SC_ROWS * L;
+    const int t = tid & 63;
+    hs.gam = scc[SC_GAM * L + t];
+    hs.eg = scc[SC_EG * L + t];
+    hs.el = scc[SC_EL * L + t];
+    hs.beta = scc[SC_BETA * L + t];
+    hs.ell = p.s.ell[(static_cast<size_t>(x.b) * d.T + x.t0 + min(t, x.tl)) * d.Hv + h];
+    hs.egl = scc[SC_EGL * L];
+    const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
+    const bf16* txr = p.cb.Tx + (static_cast<size_t>(bh) * x.NC + x.c) * L * L + ta * L + 8 * lg;
+    hs.txb[0] = load_bf16x8(txr);
+    hs.txb[1] = load_bf16x8(txr + 32);
+  }
+  __device__ static void load_tail(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, HeadTail& ht) {
+    const Dims& d = p.d;
+    const size_t mat = (static_cast<size_t>(x.b * d.Hv + h) * x.NC + x.c) * L * L;
+    const int u = tid & (L * L / 8 - 1);
+    ht.pt = *reinterpret_cast<const uint4*>(p.cb.PqT + mat + 8 * u);
+    ht.at = *reinterpret_cast<const uint4*>(p.cb.AtT + mat + 8 * u);
+    const int t = min(tid & 63, x.tl);
+    ht.a_bits = static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h];
+    ht.valid = p.mask == nullptr ? 1 : p.mask[static_cast<size_t>(x.b) * d.T + x.t0 + t];
+  }
+
   __device__ static void put_chunks(Smem& sm, int tid, const Pf& f) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -508,31 +552,44 @@ struct ChunkBwdGrad {
       sm.rk[tid0] = in ? p.s.rk[qk0 + static_cast<size_t>(tid0) * d.Hk] : 0.f;
       sm.rq[tid0] = in ? p.s.rq[qk0 + static_cast<size_t>(tid0) * d.Hk] : 0.f;
     }
+    for (int e = tid0; e < L * LP; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
     f32x4 accQ[IH], accK[IH];
 #pragma unroll
     for (int k = 0; k < IH; ++k) accQ[k] = accK[k] = f4zero();
+    // k and q rows of this wave's row tile, for every head and slab of the
+    // workgroup (loading them inside the slab loop would make each wait for
+    // them also wait for the next slab's prefetch, issued before them)
+    bf16x8 ka[KS], qa[KS];
+    {
+      const int ta = 16 * ((tid0 >> 6) & 3) + (tid0 & 15), lg = (tid0 & 63) >> 4;
+      const uint32_t o = static_cast<uint32_t>(min(ta, x.tl)) * qk_row + 8 * lg;
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        ka[kt] = load_bf16x8(kc + o + 32 * kt);
+        qa[kt] = load_bf16x8(qc + o + 32 * kt);
+      }
+    }
 
     const int nsl = d.Dv / NS;
     Pf pf;
+    HeadStart hs;
+    HeadTail ht;
+    load_start(p, x, tid0, x.j * G, hs);
     prefetch(p, x, tid0, x.j * G, 0, pf);
     for (int hh = 0; hh < G; ++hh) {
-      const int h = x.j * G + hh, bh = x.b * d.Hv + h;
-      const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
-      const float* scc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
+      const int h = x.j * G + hh;
       const Lanes ln;
       __syncthreads();  // the previous head is done with every shared array
       if (ln.tid < L) {
         const int t = ln.tid;
-        sm.gam[t] = scc[SC_GAM * L + t];
-        sm.eg[t] = scc[SC_EG * L + t];
-        sm.el[t] = scc[SC_EL * L + t];
-        sm.beta[t] = scc[SC_BETA * L + t];
-        sm.ell[t] = t < Lc ? p.s.ell[(static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h] : 0.f;
+        sm.gam[t] = hs.gam;
+        sm.eg[t] = hs.eg;
+        sm.el[t] = hs.el;
+        sm.beta[t] = hs.beta;
+        sm.ell[t] = t < Lc ? hs.ell : 0.f;
       }
-      const float egl = scc[SC_EGL * L];
-      bf16x8 txb[2];
-      txb[0] = load_bf16x8(p.cb.Tx + mat + ln.ta * L + 8 * ln.lg);
-      txb[1] = load_bf16x8(p.cb.Tx + mat + ln.ta * L + 32 + 8 * ln.lg);
+      const float egl = hs.egl;
+      const bf16x8 txb[2] = {hs.txb[0], hs.txb[1]};
       __syncthreads();
       f32x4 dox[2], xe[2];
       dox[0] = dox[1] = xe[0] = xe[1] = f4zero();
@@ -570,10 +627,15 @@ struct ChunkBwdGrad {
           }
         }
         put_chunks(sm, q.tid, pf);
-        {  // next slab (of this head or the next one)
+        {  // next slab (of this head or the next one); in the last slab, what
+           // this head's tail and the next head's start need
           const int nsi = si + 1 < nsl ? si + 1 : 0;
           const int nh = si + 1 < nsl ? h : h + 1;
           if (nh < x.j * G + G) prefetch(p, x, q.tid, nh, nsi * NS, pf);
+          if (si + 1 == nsl) {
+            load_tail(p, x, q.tid, h, ht);
+            if (hh + 1 < G) load_start(p, x, q.tid, h + 1, hs);
+          }
         }
         lds_barrier();
         const bf16* vt = sm.u.s.vt[0];
@@ -581,17 +643,12 @@ struct ChunkBwdGrad {
         const bf16* et = sm.u.s.vt[2];
         // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta)
         f32x4 kh = f4zero(), qh = f4zero(), kdt = f4zero();
-        {
-          const bf16* kra = kc + static_cast<uint32_t>(min(ta, x.tl)) * qk_row + 8 * lg;
-          const bf16* qra = qc + static_cast<uint32_t>(min(ta, x.tl)) * qk_row + 8 * lg;
 #pragma unroll
-          for (int kt = 0; kt < KS; ++kt) {
-            const bf16x8 ka = load_bf16x8(kra + 32 * kt), qa = load_bf16x8(qra + 32 * kt);
-            const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]);
-            kh = mfma16(ka, bh8, kh);
-            qh = mfma16(qa, bh8, qh);
-            kdt = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]), ka, kdt);
-          }
+        for (int kt = 0; kt < KS; ++kt) {
+          const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]);
+          kh = mfma16(ka[kt], bh8, kh);
+          qh = mfma16(qa[kt], bh8, qh);
+          kdt = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]), ka[kt], kdt);
         }
         // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
         {
@@ -672,6 +729,11 @@ struct ChunkBwdGrad {
         }
         phdh = wave_sum(phdh);
         if (q.l == 0) sm.red[q.w] = phdh;
+        {
+          const int row = q.tid >> 3, c8 = 8 * (q.tid & 7);
+          *reinterpret_cast<uint4*>(&sm.u.h.pt[row * TS + c8]) = ht.pt;
+          *reinterpret_cast<uint4*>(&sm.u.h.at[row * TS + c8]) = ht.at;
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -681,17 +743,14 @@ struct ChunkBwdGrad {
           }
       }
       __syncthreads();
-      // ---- L x L weights of head h, the rectangle terms of dl and their row sums
+      // ---- L x L weights of head h (added to the group sums), the rectangle
+      // terms of dl and their row sums
       {
         const Lanes q;
         const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
         const bool tv = t < Lc;
         const float gt = sm.gam[t], bt = sm.beta[t];
-        // P[t][s] = P^T[s][t] and A[t][s] = A^T[s][t] of the chunk (bf16, with decays and norms)
-        const unsigned short* pqc = reinterpret_cast<const unsigned short*>(p.cb.PqT) + mat + t;
-        const unsigned short* atc = reinterpret_cast<const unsigned short*>(p.cb.AtT) + mat + t;
-        uint32_t wq2[4], w12[4], w22[4];
-        float lo[3] = {0.f, 0.f, 0.f}, rsum = 0.f;
+        float rsum = 0.f;
 #pragma unroll 2
         for (int e = 0; e < 8; ++e) {
           const int s = s0 + e;
@@ -700,56 +759,30 @@ struct ChunkBwdGrad {
           const float bs = sm.beta[s], rks = sm.rk[s];
           const float doxts = sm.u.h.dox[t * LP + s], doxst = sm.u.h.dox[s * LP + t];
           const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
-          const float ptv = __uint_as_float(static_cast<uint32_t>(pqc[s * L]) << 16);
-          const float atv = __uint_as_float(static_cast<uint32_t>(atc[s * L]) << 16);
-          const float wq = ok && s <= t ? dec * bs * doxts * rks : 0.f;
-          const float wk1 = ok && s >= t ? dec * bt * doxst * sm.rq[s] : 0.f;
-          const float wk2 = ok && s != t ? -bt * bs * dec * (s < t ? xest : xets) * rks : 0.f;
+          // P[t][s] = P^T[s][t], A[t][s] = A^T[s][t] (decays and norms included)
+          const float ptv = to_f32(sm.u.h.pt[s * TS + t]), atv = to_f32(sm.u.h.at[s * TS + t]);
+          if (ok) {
+            if (s <= t) sm.wsq[t * LP + s] += dec * bs * doxts * rks;
+            if (s >= t) sm.ws1[t * LP + s] += dec * bt * doxst * sm.rq[s];
+            if (s != t) sm.ws2[t * LP + s] += -bt * bs * dec * (s < t ? xest : xets) * rks;
+          }
           const float m = ok && s < t ? bs * (ptv * doxts - bt * atv * xest) : 0.f;
           sm.u.h.m[t * LP + s] = m;
           rsum += m;
-          if (e & 1) {
-            wq2[e >> 1] = pack2_bf16(lo[0], wq);
-            w12[e >> 1] = pack2_bf16(lo[1], wk1);
-            w22[e >> 1] = pack2_bf16(lo[2], wk2);
-          } else {
-            lo[0] = wq;
-            lo[1] = wk1;
-            lo[2] = wk2;
-          }
         }
-        *reinterpret_cast<uint4*>(&sm.u.h.wq[t * TS + s0]) = make_uint4(wq2[0], wq2[1], wq2[2], wq2[3]);
-        *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + s0]) = make_uint4(w12[0], w12[1], w12[2], w12[3]);
-        *reinterpret_cast<uint4*>(&sm.u.h.wk[t * WS + L + s0]) = make_uint4(w22[0], w22[1], w22[2], w22[3]);
         rsum = oct_sum(rsum);
         if ((q.tid & 7) == 0) sm.rs[t] = rsum;
       }
       __syncthreads();
-      // ---- column sums of the rectangle terms; final products of head h
+      // ---- column sums of the rectangle terms
       {
         const Lanes q;
-        {
-          const int s = q.tid >> 3, r0 = 8 * (q.tid & 7);
-          float csum = 0.f;
+        const int s = q.tid >> 3, r0 = 8 * (q.tid & 7);
+        float csum = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) csum += sm.u.h.m[(r0 + e) * LP + s];
-          csum = oct_sum(csum);
-          if ((q.tid & 7) == 0) sm.cs[s] = csum;
-        }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 aq = load_bf16x8(&sm.u.h.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
-          const bf16x8 a1 = load_bf16x8(&sm.u.h.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
-          const bf16x8 a2 = load_bf16x8(&sm.u.h.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
-#pragma unroll
-          for (int k = 0; k < IH; ++k) {
-            const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
-            const bf16x8 bk = load_bf16x8(ktc + o), bq = load_bf16x8(qtc + o);
-            accQ[k] = mfma16(aq, bk, accQ[k]);
-            accK[k] = mfma16(a1, bq, accK[k]);
-            accK[k] = mfma16(a2, bk, accK[k]);
-          }
-        }
+        for (int e = 0; e < 8; ++e) csum += sm.u.h.m[(r0 + e) * LP + s];
+        csum = oct_sum(csum);
+        if ((q.tid & 7) == 0) sm.cs[s] = csum;
       }
       __syncthreads();
       // ---- dl_t = e^{gL} <dH', H> + sum_{u<t} (a_u + cs_u - rs_u) + sum_{r>=t} b_r; da, db
@@ -770,9 +803,8 @@ struct ChunkBwdGrad {
         float da = 0.f, db = 0.f, dll = 0.f;
         if (in) {
           const size_t ri = (static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h;
-          const bool valid = p.mask == nullptr || p.mask[static_cast<size_t>(x.b) * d.T + x.t0 + t] != 0;
-          if (valid) {
-            const float xa = to_f32(static_cast<const bf16*>(p.a)[ri]) + p.dt_bias[h];
+          if (ht.valid != 0) {
+            const float xa = __uint_as_float(static_cast<uint32_t>(ht.a_bits) << 16) + p.dt_bias[h];
             da = xa <= kClamp ? dl * (-expf(p.A_log[h])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
             const float beta = sm.beta[t];
             db = (sm.pdb[0][t] + sm.pdb[1][t]) * beta * (1.f - beta);
@@ -787,6 +819,41 @@ struct ChunkBwdGrad {
           const size_t pi = (static_cast<size_t>(x.b) * NC + c) * d.Hv + h;
           p.part_dA[pi] = sa;
           p.part_ddt[pi] = sd;
+        }
+      }
+    }
+
+    // ---- final products with the group sums: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn
+    __syncthreads();
+    {
+      const Lanes q;
+      const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
+      uint32_t w0[4], w1[4], w2[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        w0[e >> 1] = pack2_bf16(sm.wsq[t * LP + s0 + e], sm.wsq[t * LP + s0 + e + 1]);
+        w1[e >> 1] = pack2_bf16(sm.ws1[t * LP + s0 + e], sm.ws1[t * LP + s0 + e + 1]);
+        w2[e >> 1] = pack2_bf16(sm.ws2[t * LP + s0 + e], sm.ws2[t * LP + s0 + e + 1]);
+      }
+      *reinterpret_cast<uint4*>(&sm.u.w.wq[t * TS + s0]) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+      *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + s0]) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + L + s0]) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+    }
+    __syncthreads();
+    {
+      const Lanes q;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 aq = load_bf16x8(&sm.u.w.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
+        const bf16x8 a1 = load_bf16x8(&sm.u.w.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
+        const bf16x8 a2 = load_bf16x8(&sm.u.w.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
+#pragma unroll
+        for (int k = 0; k < IH; ++k) {
+          const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
+          const bf16x8 bk = load_bf16x8(ktc + o), bq = load_bf16x8(qtc + o);
+          accQ[k] = mfma16(aq, bk, accQ[k]);
+          accK[k] = mfma16(a1, bq, accK[k]);
+          accK[k] = mfma16(a2, bk, accK[k]);
         }
       }
     }
