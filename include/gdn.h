@@ -55,9 +55,17 @@ enum gdn_status {
 
 enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
 
-/* Kernel family.  AUTO picks the chunked MFMA form where it is built for the
- * shape and dtype, else the sequential scan.  Both produce the same
- * checkpoint layout, so a checkpoint from one can be used by the other. */
+/* Kernel family.
+ *   SCAN   the per-step recurrence in fp32 (every dtype and supported size).
+ *   CHUNK  the chunked matrix form over 64-step chunks: bf16 matrix-core
+ *          products with fp32 accumulation and an fp32 state carried between
+ *          chunks.  Built for dtype bf16, Dk in {64, 128, 192, 256} and Dv a
+ *          multiple of 32 up to 256; other shapes return GDN_ERR_UNSUPPORTED.
+ *          Its results agree with SCAN to bf16 rounding (about 1e-2 relative,
+ *          normwise), not bitwise.
+ *   AUTO   CHUNK where it is built and T > 1, else SCAN.
+ * Both produce the same checkpoint layout, so a checkpoint from one can be
+ * used by the other. */
 enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SCAN = 1, GDN_ALGO_CHUNK = 2 };
 
 typedef struct gdn_dims {

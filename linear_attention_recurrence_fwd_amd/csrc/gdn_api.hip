@@ -122,9 +122,16 @@ P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
 }
 
-// Kernel family of a call: the chunk form where asked for.
-bool use_chunk_fwd(const gdn_dims* p) { return p->algo == GDN_ALGO_CHUNK; }
-bool use_chunk_bwd(const gdn_dims* p) { return p->algo == GDN_ALGO_CHUNK; }
+// Kernel family of a call: the chunk form where asked for, and under AUTO for
+// bf16 with a supported head size and more than one step (single steps, the
+// decode case, stay on the scan).
+bool use_chunk(const gdn_dims* p) {
+  if (p->algo == GDN_ALGO_CHUNK) return true;
+  if (p->algo == GDN_ALGO_SCAN) return false;
+  return p->T > 1 && gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16);
+}
+bool use_chunk_fwd(const gdn_dims* p) { return use_chunk(p); }
+bool use_chunk_bwd(const gdn_dims* p) { return use_chunk(p); }
 
 gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   gdn::ChunkBufs cb{};

@@ -101,3 +101,24 @@ def test_bwd_rejects_before_launch():
     args[14] = None  # dv
     assert lib.gdn_bwd(ctypes.byref(d), *args, need, None) == 1
     assert lib.gdn_bwd(ctypes.byref(d), *p, need - 1, None) == 3
+
+
+def test_auto_selects_chunk_for_bf16():
+    """AUTO runs the chunk form for bf16 with a built head size and T > 1 (its
+    workspace equals CHUNK's), and the scan otherwise."""
+    def ws(T, dtype, Dk, algo):
+        d = B.make_dims(1, T, 16, 64, Dk, 128, dtype, algo)
+        return B.fwd_workspace_bytes(d), B.bwd_workspace_bytes(d)
+    assert ws(2048, B.GDN_BF16, 192, B.ALGO_AUTO) == ws(2048, B.GDN_BF16, 192, B.ALGO_CHUNK)
+    assert ws(2048, B.GDN_BF16, 192, B.ALGO_AUTO) != ws(2048, B.GDN_BF16, 192, B.ALGO_SCAN)
+    assert ws(2048, B.GDN_F32, 192, B.ALGO_AUTO) == ws(2048, B.GDN_F32, 192, B.ALGO_SCAN)
+    assert ws(1, B.GDN_BF16, 192, B.ALGO_AUTO) == ws(1, B.GDN_BF16, 192, B.ALGO_SCAN)
+    assert ws(2048, B.GDN_BF16, 32, B.ALGO_AUTO) == ws(2048, B.GDN_BF16, 32, B.ALGO_SCAN)
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [(B.GDN_F32, 192, 128), (B.GDN_BF16, 32, 128),
+                                         (B.GDN_BF16, 192, 16)])
+def test_chunk_unsupported(dtype, Dk, Dv):
+    with pytest.raises(B.GdnError) as e:
+        B.fwd_workspace_bytes(B.make_dims(1, 128, 2, 4, Dk, Dv, dtype, B.ALGO_CHUNK))
+    assert e.value.code == 2

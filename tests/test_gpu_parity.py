@@ -4,8 +4,9 @@ Tolerances (normwise per tensor, max|x - ref| / max|ref|): 1e-4 for fp32
 workloads, 2e-2 for bf16 workloads.  Workloads: the PR's toy shape, the edge
 and masking sweep (T in {1, 64, 65, 1024}, masks, extreme gates), the
 Qwen3.5-9B GDN layer shape at T = 256 and T = 2048 (every element compared),
-a ragged shape with Dk = 128, and the decode chain.  Repeated runs must be
-bit-identical.
+ragged shapes, and the decode chain.  Repeated runs must be bit-identical.
+The first group runs the sequential scan (ALGO_SCAN; AUTO for fp32), the
+second the chunked form (ALGO_CHUNK, bf16), which AUTO picks for bf16.
 """
 import numpy as np
 import pytest
@@ -58,9 +59,12 @@ def test_edge(T, masked, extreme):
     run_and_compare(inputs.edge(T, masked=masked, extreme=extreme))
 
 
+SCAN = binding.ALGO_SCAN
+
+
 def test_ragged_dk128():
     c = inputs.make_case("ragged_dk128", 2, 200, 2, 4, 128, 64, "bf16", 77)
-    run_and_compare(c)
+    run_and_compare(c, algo=SCAN)
 
 
 def test_ragged_dk32_dv16_fp32():
@@ -70,11 +74,11 @@ def test_ragged_dk32_dv16_fp32():
 
 
 def test_qwen35_9b_t256():
-    run_and_compare(inputs.qwen35_9b(256))
+    run_and_compare(inputs.qwen35_9b(256), algo=SCAN)
 
 
 def test_qwen35_9b_t2048():
-    run_and_compare(inputs.qwen35_9b(2048), nthreads=16)
+    run_and_compare(inputs.qwen35_9b(2048), algo=SCAN, nthreads=16)
 
 
 def test_deterministic_repeat():
@@ -83,8 +87,8 @@ def test_deterministic_repeat():
     t = upload(c)
     outs = []
     for _ in range(3):
-        o, st, ck = gpu_fwd(t)
-        g = gpu_bwd(t, ck)
+        o, st, ck = gpu_fwd(t, algo=SCAN)
+        g = gpu_bwd(t, ck, algo=SCAN)
         outs.append([o, st, ck] + [g[n] for n in GRADS])
     torch.cuda.synchronize()
     for other in outs[1:]:
@@ -194,3 +198,35 @@ def test_chunk_deterministic_repeat():
         for x, y in zip(outs[0], other):
             assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                                y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+
+
+def test_auto_runs_chunk_for_bf16():
+    """AUTO on a bf16 workload gives the chunk form's bits exactly."""
+    c = inputs.qwen35_9b(256)
+    say("[auto] case=%s" % c.name)
+    t = upload(c)
+    o1, s1, k1 = gpu_fwd(t)
+    g1 = gpu_bwd(t, k1)
+    o2, s2, k2 = gpu_fwd(t, algo=CHUNK)
+    g2 = gpu_bwd(t, k2, algo=CHUNK)
+    torch.cuda.synchronize()
+    for x, y in [(o1, o2), (s1, s2), (k1, k2)] + [(g1[n], g2[n]) for n in GRADS]:
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+
+
+def test_chunk_checkpoint_interchange():
+    """A checkpoint from the scan forward drives the chunk backward (and the
+    reverse) to the oracle's gradients within the bf16 bound."""
+    c = inputs.qwen35_9b(256)
+    say("[interchange] case=%s" % c.name)
+    t = upload(c)
+    ro, rst, rck, rg = oracle_all(c, nthreads=8)
+    for fa, ba in ((SCAN, CHUNK), (CHUNK, SCAN)):
+        _, _, ck = gpu_fwd(t, algo=fa)
+        g = gpu_bwd(t, ck, algo=ba)
+        torch.cuda.synchronize()
+        errs = {n: relerr(to64(g[n]), rg[n]) for n in GRADS}
+        say("[interchange] fwd=%d bwd=%d errors " % (fa, ba) +
+            " ".join("%s=%.2e" % kv for kv in errs.items()))
+        assert all(e <= TOL["bf16"] for e in errs.values()), errs
