@@ -14,11 +14,12 @@
 // only as e^{g_t - g_s} with s <= t, never as e^{-g}.
 //
 // Kernels:
-//   chunk_prep  one workgroup per (chunk, batch, value head): K K^T and Q K^T on
-//               MFMA, N, Tx by forward substitution (fp32), Mq and the per-step
-//               chunk scalars; the first head of each key-head group also
-//               writes K^T.  With `bwd` set it also writes the transposes the
-//               backward needs.  All outputs go to the workspace (bf16 / fp32).
+//   chunk_prep  one workgroup per (chunk, batch, key head): K K^T and Q K^T on
+//               MFMA once, then for each value head of the group N, Tx by
+//               forward substitution (fp32), Mq and the per-step chunk
+//               scalars; K^T of the chunk.  With `bwd` set it writes the
+//               transposes the backward needs instead of Mq, and Q^T.  All
+//               outputs go to the workspace (bf16 / fp32), 16 bytes per store.
 //   chunk_fwd   one workgroup per (batch, value head, 32-column slice of Dv),
 //               walking the chunks in order with H in MFMA accumulators (fp32),
 //               the next chunk's operands prefetched into registers while the
@@ -41,168 +42,221 @@ constexpr int NT = 256;
 
 template <int DK>
 struct ChunkPrep {
-  static constexpr int KS = DK + 8;  // bf16 row stride of the staged K / Q tile
-  static constexpr int MAT_BYTES = 2 * L * LP * 4;
-  static constexpr int TILE_BYTES = L * KS * 2;
-  static constexpr int BUF_BYTES = MAT_BYTES > TILE_BYTES ? MAT_BYTES : TILE_BYTES;
+  static constexpr int SP = L + 4;  // fp32 row stride of the staging matrix (16-byte aligned rows)
+  struct Mats {
+    float np[L * L];   // N, row t holding N[t][4m + q] at q L/4 + m
+    float st[L * SP];  // staging of the matrices written out
+  };
+  // The k / q column block of this workgroup's share of the transposes.
+  static constexpr int TW = DK + 8;
+  struct Tile {
+    bf16 t[L * TW];
+  };
+  union Big {
+    Mats m;
+    Tile k;
+  };
   struct Smem {
-    alignas(16) char buf[BUF_BYTES];  // N / Tx and a transpose stage, or a K / Q tile
+    alignas(16) Big u;
     float gam[L], rk[L], rq[L], beta[L];
   };
 
+  // st (fp32 [L][SP]) -> dst (bf16 [L][L]), 8 elements per store.
+  __device__ static void store_mat(const Smem& sm, bf16* dst, int tid) {
+    for (int u = tid; u < L * L / 8; u += NT) {
+      const int r = u >> 3, c8 = 8 * (u & 7);
+      const float4 a = *reinterpret_cast<const float4*>(&sm.u.m.st[r * SP + c8]);
+      const float4 b = *reinterpret_cast<const float4*>(&sm.u.m.st[r * SP + c8 + 4]);
+      *reinterpret_cast<uint4*>(dst + r * L + c8) =
+          make_uint4(pack2_bf16(a.x, a.y), pack2_bf16(a.z, a.w), pack2_bf16(b.x, b.y), pack2_bf16(b.z, b.w));
+    }
+  }
+
   __device__ static void run(const ChunkPrepArgs& p, Smem& sm) {
     const Dims& d = p.d;
-    const int c = blockIdx.x, bh = blockIdx.y;
+    const int c = blockIdx.x, bj = blockIdx.y;
     const int G = d.G(), NC = d.nchunk();
-    const int b = bh / d.Hv, h = bh % d.Hv, j = h / G, hh = h % G, bj = b * d.Hk + j;
-    const int t0 = c * L, Lc = min(L, d.T - t0);
+    const int b = bj / d.Hk, j = bj % d.Hk;
+    const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const bf16* kg = static_cast<const bf16*>(p.k);
-    const bf16* qg = static_cast<const bf16*>(p.q);
-    float* nm = reinterpret_cast<float*>(sm.buf);   // [L][LP]
-    float* st = nm + L * LP;                         // [L][LP] transpose stage
-    const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
-    auto qk_row = [&](int t) { return (static_cast<size_t>(b) * d.T + t0 + t) * d.Hk + j; };
+    const size_t qk0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;
+    const uint32_t qk_row = d.Hk * DK;
+    const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
+    const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
 
-    // ---- per-step scalars; gamma by a wave-wide inclusive scan
-    if (w == 0) {
-      float ell = 0.f, beta = 0.f, rk = 0.f, rq = 0.f;
-      if (l < Lc) {
-        const size_t bt = static_cast<size_t>(b) * d.T + t0 + l;
-        ell = p.s.ell[bt * d.Hv + h];
-        beta = p.s.beta[bt * d.Hv + h];
-        rk = p.s.rk[bt * d.Hk + j];
-        rq = p.s.rq[bt * d.Hk + j];
-      }
-      float g = ell;
-#pragma unroll
-      for (int off = 1; off < L; off <<= 1) {
-        const float y = __shfl_up(g, off);
-        if (l >= off) g += y;
-      }
-      sm.gam[l] = g;
-      sm.rk[l] = rk;
-      sm.rq[l] = rq;
-      sm.beta[l] = beta;
-    }
-    __syncthreads();
-    if (tid < L) {
-      const int t = tid;
-      const float gl = sm.gam[Lc - 1];
-      const float eg = expf(sm.gam[t]), el = expf(gl - sm.gam[t]);
-      float* sc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
-      sc[SC_CR * L + t] = eg * sm.rk[t];
-      sc[SC_CO * L + t] = eg * sm.rq[t];
-      sc[SC_W * L + t] = sm.beta[t] * el * sm.rk[t];
-      sc[SC_KL * L + t] = el * sm.rk[t];
-      sc[SC_BETA * L + t] = sm.beta[t];
-      sc[SC_EGL * L + t] = t == 0 ? expf(gl) : 0.f;
-      sc[SC_GAM * L + t] = sm.gam[t];
-      sc[SC_EG * L + t] = eg;
-      sc[SC_EL * L + t] = el;
-    }
-
-    // ---- K K^T and Q K^T (raw rows): wave w computes row tile w
+    // ---- K K^T and Q K^T (raw rows, clamped into the sequence), shared by
+    // the G value heads of the key head: wave w, row tile w
     f32x4 akk[4], aqk[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) akk[ct] = aqk[ct] = f4zero();
     {
-      const int ta = 16 * w + lr;
+      const uint32_t oa = static_cast<uint32_t>(min(16 * w + lr, tl)) * qk_row + 8 * lg;
+      uint32_t ob[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) ob[ct] = static_cast<uint32_t>(min(16 * ct + lr, tl)) * qk_row + 8 * lg;
 #pragma unroll
       for (int kt = 0; kt < DK / 32; ++kt) {
-        const int e0 = 32 * kt + 8 * lg;
-        const bf16x8 ak = ta < Lc ? load_bf16x8(kg + qk_row(ta) * DK + e0) : zero8();
-        const bf16x8 aq = ta < Lc ? load_bf16x8(qg + qk_row(ta) * DK + e0) : zero8();
+        const bf16x8 ak = load_bf16x8(kc + oa + 32 * kt), aq = load_bf16x8(qc + oa + 32 * kt);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const int tb = 16 * ct + lr;
-          const bf16x8 bk = tb < Lc ? load_bf16x8(kg + qk_row(tb) * DK + e0) : zero8();
+          const bf16x8 bk = load_bf16x8(kc + ob[ct] + 32 * kt);
           akk[ct] = mfma16(ak, bk, akk[ct]);
           aqk[ct] = mfma16(aq, bk, aqk[ct]);
         }
       }
     }
-    // ---- N, Mq (and the backward's A~, P) from the accumulators
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * lg + r, s = 16 * ct + lr;
-        float nv = 0.f, mq = 0.f, at = 0.f, pq = 0.f;
-        if (s <= t) {
-          const float dec = expf(sm.gam[t] - sm.gam[s]);
-          const float krs = dec * sm.rk[t] * sm.rk[s];
-          if (s < t) {
-            at = krs * akk[ct][r];
-            nv = at * sm.beta[s];
-          }
-          pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
-          mq = pq * sm.beta[s];
+    if (tid < L) {
+      const bool in = tid < Lc;
+      sm.rk[tid] = in ? p.s.rk[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
+      sm.rq[tid] = in ? p.s.rq[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
+    }
+    // gates of the first head (wave 0, lane t); later heads' are loaded a head ahead
+    float ell_n = 0.f, beta_n = 0.f;
+    if (w == 0 && l < Lc) {
+      const size_t bt = static_cast<size_t>(b) * d.T + t0 + l;
+      ell_n = p.s.ell[bt * d.Hv + j * G];
+      beta_n = p.s.beta[bt * d.Hv + j * G];
+    }
+
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = j * G + hh, bh = b * d.Hv + h;
+      const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
+      __syncthreads();  // the previous head is done with the shared arrays
+      // ---- per-step scalars; gamma by a wave-wide inclusive scan
+      if (w == 0) {
+        float g = ell_n;
+        const float beta = beta_n;
+        if (hh + 1 < G && l < Lc) {
+          const size_t bt = static_cast<size_t>(b) * d.T + t0 + l;
+          ell_n = p.s.ell[bt * d.Hv + h + 1];
+          beta_n = p.s.beta[bt * d.Hv + h + 1];
         }
-        nm[t * LP + s] = nv;
-        p.cb.Mq[mat + t * L + s] = bf16_of(mq);
-        if (p.bwd) {
-          st[s * LP + t] = at;   // staged transposed
-          akk[ct][r] = pq;       // keep P for the second stage
+#pragma unroll
+        for (int off = 1; off < L; off <<= 1) {
+          const float y = __shfl_up(g, off);
+          if (l >= off) g += y;
         }
+        sm.gam[l] = g;
+        sm.beta[l] = beta;
       }
-    __syncthreads();
-    if (p.bwd) {
-      for (int e = tid; e < L * L; e += NT) p.cb.AtT[mat + e] = bf16_of(st[(e / L) * LP + e % L]);
       __syncthreads();
+      if (tid < L) {
+        const int t = tid;
+        const float gl = sm.gam[Lc - 1];
+        const float eg = expf(sm.gam[t]), el = expf(gl - sm.gam[t]);
+        float* sc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
+        sc[SC_CR * L + t] = eg * sm.rk[t];
+        sc[SC_CO * L + t] = eg * sm.rq[t];
+        sc[SC_W * L + t] = sm.beta[t] * el * sm.rk[t];
+        sc[SC_KL * L + t] = el * sm.rk[t];
+        sc[SC_BETA * L + t] = sm.beta[t];
+        sc[SC_EGL * L + t] = t == 0 ? expf(gl) : 0.f;
+        sc[SC_GAM * L + t] = sm.gam[t];
+        sc[SC_EG * L + t] = eg;
+        sc[SC_EL * L + t] = el;
+      }
+
+      // ---- N (permuted, fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward)
+      float mq[4][4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st[(16 * ct + lr) * LP + 16 * w + 4 * lg + r] = akk[ct][r];
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * w + 4 * lg + r, s = 16 * ct + lr;
+          float nv = 0.f, pq = 0.f, at = 0.f;
+          if (s <= t) {
+            const float dec = expf(sm.gam[t] - sm.gam[s]);
+            if (s < t) {
+              at = dec * sm.rk[t] * sm.rk[s] * akk[ct][r];
+              nv = at * sm.beta[s];
+            }
+            pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
+          }
+          sm.u.m.np[t * L + (s & 3) * (L / 4) + (s >> 2)] = nv;
+          if (p.bwd) {
+            sm.u.m.st[s * SP + t] = at;  // A^T
+            mq[ct][r] = pq;
+          } else {
+            sm.u.m.st[t * SP + s] = pq * sm.beta[s];  // Mq
+          }
+        }
       __syncthreads();
-      for (int e = tid; e < L * L; e += NT) p.cb.PqT[mat + e] = bf16_of(st[(e / L) * LP + e % L]);
-    }
-
-    // ---- Tx = (I + N)^-1 by forward substitution: column `col`, four threads
-    // per column, thread q4 holding the entries at rows 4m + q4.
-    float x[L / 4];
-    {
-      const int col = tid >> 2, q4 = tid & 3;
+      if (p.bwd) {
+        store_mat(sm, p.cb.AtT + mat, tid);
+        __syncthreads();
 #pragma unroll
-      for (int m = 0; m < L / 4; ++m) x[m] = 0.f;
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int t = 0; t < L; ++t) {
-        float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-        for (int m = 0; m < L / 4; m += 2) {
-          p0 = fmaf(nm[t * LP + 4 * m + q4], x[m], p0);
-          p1 = fmaf(nm[t * LP + 4 * m + 4 + q4], x[m + 1], p1);
-        }
-        const float xt = (t == col ? 1.f : 0.f) - quad_sum(p0 + p1);
-        if ((t & 3) == q4) x[t >> 2] = xt;
+          for (int r = 0; r < 4; ++r) sm.u.m.st[(16 * ct + lr) * SP + 16 * w + 4 * lg + r] = mq[ct][r];  // P^T
+        __syncthreads();
+        store_mat(sm, p.cb.PqT + mat, tid);
+      } else {
+        store_mat(sm, p.cb.Mq + mat, tid);
       }
-      __syncthreads();  // every thread is done reading N
+
+      // ---- Tx = (I + N)^-1 by forward substitution in fp32: column `col`,
+      // four threads per column, thread q holding the entries at rows 4m + q.
+      // Only rows above step t enter step t, so step t reads ceil(t/4) entries.
+      {
+        const int col = tid >> 2, q = tid & 3;
+        float x[L / 4];
 #pragma unroll
-      for (int m = 0; m < L / 4; ++m) nm[(4 * m + q4) * LP + col] = x[m];
-    }
-    __syncthreads();
-    for (int e = tid; e < L * L; e += NT) {
-      const int t = e / L, s = e % L;
-      p.cb.Tx[mat + e] = bf16_of(nm[t * LP + s]);
-      if (p.bwd) p.cb.TxT[mat + e] = bf16_of(nm[s * LP + t]);
+        for (int m = 0; m < L / 4; ++m) x[m] = 0.f;
+        const float* nrow = &sm.u.m.np[q * (L / 4)];
+#pragma unroll
+        for (int t = 0; t < L; ++t) {
+          const int nm = (t + 3) / 4;  // entries m with 4m + q < t possible
+          float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+          for (int m4 = 0; m4 < nm; m4 += 4) {
+            const float4 nv = *reinterpret_cast<const float4*>(nrow + t * L + m4);
+            p0 = fmaf(nv.x, x[m4], p0);
+            if (m4 + 1 < nm) p1 = fmaf(nv.y, x[m4 + 1], p1);
+            if (m4 + 2 < nm) p0 = fmaf(nv.z, x[m4 + 2], p0);
+            if (m4 + 3 < nm) p1 = fmaf(nv.w, x[m4 + 3], p1);
+          }
+          const float xt = (t == col ? 1.f : 0.f) - quad_sum(p0 + p1);
+          if ((t & 3) == q) x[t >> 2] = xt;
+        }
+        __syncthreads();  // the staging matrix is free (P^T / Mq stored) and N is read
+#pragma unroll
+        for (int m = 0; m < L / 4; ++m) sm.u.m.st[(4 * m + q) * SP + col] = x[m];
+      }
+      __syncthreads();
+      store_mat(sm, p.cb.Tx + mat, tid);
+      if (p.bwd) {  // Tx^T: row r is column r of the staged Tx
+        for (int u = tid; u < L * L / 8; u += NT) {
+          const int r = u >> 3, c8 = 8 * (u & 7);
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = sm.u.m.st[(c8 + e) * SP + r];
+          *reinterpret_cast<uint4*>(p.cb.TxT + mat + r * L + c8) =
+              make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
+        }
+      }
     }
 
-    // ---- raw k (and q) of the chunk transposed, once per key-head group
-    if (hh == 0) {
-      bf16* tile = reinterpret_cast<bf16*>(sm.buf);
-      const size_t base = (static_cast<size_t>(bj) * NC + c) * DK * L;
-      for (int pass = 0; pass < (p.bwd ? 2 : 1); ++pass) {
-        const bf16* src = pass == 0 ? kg : qg;
-        bf16* dst = pass == 0 ? p.cb.KT : p.cb.QT;
-        __syncthreads();
-        for (int u = tid; u < L * DK / 8; u += NT) {
-          const int t = u / (DK / 8), e0 = (u % (DK / 8)) * 8;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (t < Lc) v = *reinterpret_cast<const uint4*>(src + qk_row(t) * DK + e0);
-          *reinterpret_cast<uint4*>(&tile[t * KS + e0]) = v;
-        }
-        __syncthreads();
-        for (int e = tid; e < DK * L; e += NT) dst[base + e] = tile[(e % L) * KS + e / L];
+    // ---- raw k (and q) of the chunk, transposed
+    const size_t base = (static_cast<size_t>(bj) * NC + c) * DK * L;
+    for (int pass = 0; pass < (p.bwd ? 2 : 1); ++pass) {
+      const bf16* src = pass == 0 ? kc : qc;
+      bf16* dst = (pass == 0 ? p.cb.KT : p.cb.QT) + base;
+      __syncthreads();
+      for (int u = tid; u < L * DK / 8; u += NT) {
+        const int t = u / (DK / 8), e0 = 8 * (u % (DK / 8));
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (t < Lc) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(t) * qk_row + e0);
+        *reinterpret_cast<uint4*>(&sm.u.k.t[t * TW + e0]) = v;
+      }
+      __syncthreads();
+      for (int u = tid; u < DK * L / 8; u += NT) {
+        const int i = u % DK, t8 = 8 * (u / DK);
+        uint32_t wv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          wv[e] = static_cast<uint32_t>(sm.u.k.t[(t8 + 2 * e) * TW + i].x) |
+                  (static_cast<uint32_t>(sm.u.k.t[(t8 + 2 * e + 1) * TW + i].x) << 16);
+        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(i) * L + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
       }
     }
   }
@@ -218,8 +272,17 @@ __global__ void __launch_bounds__(NT) chunk_prep_kernel(ChunkPrepArgs p) {
 
 template <int DK>
 struct ChunkFwd {
+  // Twelve waves in three groups of four (w = wave index within the group):
+  //   A (waves 0-3):  K H, R and X = Tx R for row tile w;
+  //   B (waves 4-7):  the state update H <- e^{gL} H + K^T diag(w) X for its
+  //                   row tiles of H, and the checkpoints;
+  //   C (waves 8-11): Q H and the output O = diag(e^g rq) Q H + Mq X for row
+  //                   tile w.
+  // B and C work at the same time once X is in LDS; each group keeps its own
+  // operands in registers, prefetched two chunks ahead.
+  static constexpr int NTS = 768;
   static constexpr int NV = 32;             // Dv columns per workgroup
-  static constexpr int RTW = DK / 64;       // H row tiles per wave
+  static constexpr int RTW = DK / 64;       // H row tiles per group-B wave
   static constexpr int HS = DK + 8;         // bf16 row stride of H^T
   static constexpr int XS = L + 8;          // bf16 row stride of R^T / X^T
   struct Smem {
@@ -235,61 +298,72 @@ struct ChunkFwd {
   // sequence hold copies of its last row and need no zeroing: their chunk
   // scalars (rk, w) are zero, Tx and Mq are lower triangular and their outputs
   // are not stored, so they never reach a stored value (inputs are finite).
-  struct Stage {
-    bf16x8 ka[DK / 32], qa[DK / 32];  // k, q rows t = 16 w + lr
-    bf16x8 txa[2], mqa[2];            // Tx, Mq rows t = 16 w + lr
+  struct StageA {
+    bf16x8 ka[DK / 32];               // k rows t = 16 w + lr
+    bf16x8 txa[2];                    // Tx rows t = 16 w + lr
+    unsigned short vv[2][4];          // v at rows t = 16 w + 4 lg + r, cols 16 ct + lr
+    float4 cr;                        // e^{g_t} rk_t at rows 16 w + 4 lg + r
+    float4 wv;                        // w at rows 16 w + 4 lg + r
+  };
+  struct StageB {
     bf16x8 kta[RTW][2];               // K^T rows i = 16 (w RTW + it) + lr
-    unsigned short vv[2][4];          // v bits at rows t = 16 w + 4 lg + r, cols 16 ct + lr
-    float4 cr, co, wv;                // chunk scalars at rows 16 w + 4 lg + r
     float egl;
   };
-  // Per-workgroup values (uniform) and per-lane 32-bit offsets.  Addresses are
-  // formed as a uniform 64-bit base plus a 32-bit lane offset.
+  struct StageC {
+    bf16x8 qa[DK / 32];               // q rows t = 16 w + lr
+    bf16x8 mqa[2];                    // Mq rows t = 16 w + lr
+    float co;                         // e^{g_t} rq_t at t = 16 w + lr
+  };
+  // Per-workgroup values (uniform) and per-lane coordinates (w = wave index
+  // within the group).  Addresses are a uniform 64-bit base plus a 32-bit
+  // lane offset.
   struct Lane {
     int b, h, j, bh, bj, col0, w, lr, lg, ta, tc0, last, NC;
-    uint32_t qk_row, v_row, o_row;   // element strides of one step in q/k, v, o
+    uint32_t qk_row, v_row;   // element strides of one step in q/k and v/o
+    rsrc_t rk, rq, rv, rtx, rmq, rkt, rsc;  // buffer descriptors of the operands
   };
 
-  __device__ static void load_stage(const ChunkFwdArgs& p, const Lane& q, int c, Stage& s) {
+  // Operand loads are buffer loads at byte offsets from the tensor's base.
+  __device__ static void load_a(const ChunkFwdArgs& p, const Lane& q, int c, StageA& s) {
     const Dims& d = p.d;
     const int t0 = c * L, tl = q.last - t0;
-    const bf16* kc = static_cast<const bf16*>(p.k) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hk + q.j) * DK;
-    const bf16* qc = static_cast<const bf16*>(p.q) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hk + q.j) * DK;
-    const uint32_t ko = static_cast<uint32_t>(min(q.ta, tl)) * q.qk_row + 8 * q.lg;
+    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.ta, tl)) * d.Hk + q.j) * DK + 8 * q.lg);
 #pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) {
-      s.ka[kt] = load_bf16x8(kc + ko + 32 * kt);
-      s.qa[kt] = load_bf16x8(qc + ko + 32 * kt);
-    }
-    const size_t mat = (static_cast<size_t>(q.bh) * q.NC + c) * L * L;
-    const bf16* txc = p.cb.Tx + mat;
-    const bf16* mqc = p.cb.Mq + mat;
-    const uint32_t mo = q.ta * L + 8 * q.lg;
+    for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = buf_bf16x8(q.rk, ko + 64 * kt);
+    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + q.ta * L + 8 * q.lg);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s.txa[kt] = load_bf16x8(txc + mo + 32 * kt);
-      s.mqa[kt] = load_bf16x8(mqc + mo + 32 * kt);
+    for (int kt = 0; kt < 2; ++kt) s.txa[kt] = buf_bf16x8(q.rtx, mo + 64 * kt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t vo = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.tc0 + r, tl)) * d.Hv + q.h) * d.Dv + q.col0 + q.lr);
+      s.vv[0][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rv, vo, 0, 0));
+      s.vv[1][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rv, vo + 32, 0, 0));
     }
-    const bf16* ktc = p.cb.KT + (static_cast<size_t>(q.bj) * q.NC + c) * DK * L;
-    const uint32_t kto = (16 * q.w * RTW + q.lr) * L + 8 * q.lg;
+    const uint32_t so = 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L);
+    s.cr = buf_f4(q.rsc, so + 4 * (SC_CR * L + q.tc0));
+    s.wv = buf_f4(q.rsc, so + 4 * (SC_W * L + q.tc0));
+  }
+
+  __device__ static void load_b(const ChunkFwdArgs& p, const Lane& q, int c, StageB& s) {
+    (void)p;
+    const uint32_t kto = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + q.lr) * L + 8 * q.lg);
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s.kta[it][kt] = load_bf16x8(ktc + kto + (it * 16 * L + 32 * kt));
-    const unsigned short* vc = static_cast<const unsigned short*>(p.v) +
-                               ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
+      for (int kt = 0; kt < 2; ++kt) s.kta[it][kt] = buf_bf16x8(q.rkt, kto + 2 * (it * 16 * L) + 64 * kt);
+    s.egl = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_EGL * L));
+  }
+
+  __device__ static void load_c(const ChunkFwdArgs& p, const Lane& q, int c, StageC& s) {
+    const Dims& d = p.d;
+    const int t0 = c * L, tl = q.last - t0;
+    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.ta, tl)) * d.Hk + q.j) * DK + 8 * q.lg);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t vo = static_cast<uint32_t>(min(q.tc0 + r, tl)) * q.v_row + q.lr;
-      s.vv[0][r] = vc[vo];
-      s.vv[1][r] = (vc + vo)[16];
-    }
-    const float* scc = p.cb.sc + (static_cast<size_t>(q.bh) * q.NC + c) * SC_ROWS * L;
-    const float* scl = scc + q.tc0;
-    s.cr = *reinterpret_cast<const float4*>(scl + SC_CR * L);
-    s.co = *reinterpret_cast<const float4*>(scl + SC_CO * L);
-    s.wv = *reinterpret_cast<const float4*>(scl + SC_W * L);
-    s.egl = scc[SC_EGL * L];
+    for (int kt = 0; kt < DK / 32; ++kt) s.qa[kt] = buf_bf16x8(q.rq, ko + 64 * kt);
+    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + q.ta * L + 8 * q.lg);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s.mqa[kt] = buf_bf16x8(q.rmq, mo + 64 * kt);
+    s.co = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_CO * L + q.ta));
   }
 
   __device__ static void put_h(Smem& sm, const Lane& q, const f32x4 (&H)[RTW][2]) {
@@ -301,78 +375,50 @@ struct ChunkFwd {
             pack4_bf16(H[it][ct][0], H[it][ct][1], H[it][ct][2], H[it][ct][3]);
   }
 
-  // One chunk: o for its rows, H advanced to the next chunk's start.
-  __device__ static void step(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c,
-                              const Stage& cur, f32x4 (&H)[RTW][2]) {
-    const Dims& d = p.d;
-    const int t0 = c * L, Lc = min(L, d.T - t0);
+  // Group A, one chunk: K H -> R -> X.
+  __device__ static void step_a(const Smem& smc, Smem& sm, const Lane& q, const StageA& cur) {
     const int lr = q.lr, lg = q.lg;
-    const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
-    const float cov[4] = {cur.co.x, cur.co.y, cur.co.z, cur.co.w};
     const float wvv[4] = {cur.wv.x, cur.wv.y, cur.wv.z, cur.wv.w};
-
-    // step 1: K H and Q H for row tile w
-    f32x4 kh[2], qh[2];
-    kh[0] = kh[1] = qh[0] = qh[1] = f4zero();
+    const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
+    f32x4 kh[2];
+    kh[0] = kh[1] = f4zero();
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const bf16x8 bh8 = load_bf16x8(&sm.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]);
-        kh[ct] = mfma16(cur.ka[kt], bh8, kh[ct]);
-        qh[ct] = mfma16(cur.qa[kt], bh8, qh[ct]);
-      }
-    // step 2: R = V - diag(e^gamma rk) K H  -> rb (transposed, bf16)
+      for (int ct = 0; ct < 2; ++ct)
+        kh[ct] = mfma16(cur.ka[kt], load_bf16x8(&smc.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), kh[ct]);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       float rv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rv[r] = __uint_as_float(static_cast<uint32_t>(cur.vv[ct][r]) << 16) - crv[r] * kh[ct][r];
-      }
+      for (int r = 0; r < 4; ++r) rv[r] = __uint_as_float(static_cast<uint32_t>(cur.vv[ct][r]) << 16) - crv[r] * kh[ct][r];
       *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
     }
-    lds_barrier();
-    // step 3: X = Tx R for row tile w; X and diag(w) X to LDS
+    lds_barrier();  // 1: R complete
     f32x4 x[2];
     x[0] = x[1] = f4zero();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        x[ct] = mfma16(cur.txa[kt], load_bf16x8(&sm.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), x[ct]);
+        x[ct] = mfma16(cur.txa[kt], load_bf16x8(&smc.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), x[ct]);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      *reinterpret_cast<uint2*>(&sm.xb[(16 * ct + lr) * XS + q.tc0]) =
-          pack4_bf16(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
+      *reinterpret_cast<uint2*>(&sm.xb[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
       *reinterpret_cast<uint2*>(&sm.xw[(16 * ct + lr) * XS + q.tc0]) =
           pack4_bf16(wvv[0] * x[ct][0], wvv[1] * x[ct][1], wvv[2] * x[ct][2], wvv[3] * x[ct][3]);
     }
-    lds_barrier();
-    // step 4: O = diag(e^gamma rq) Q H + Mq X for row tile w
-    {
-      f32x4 o[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[ct][r] = cov[r] * qh[ct][r];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          o[ct] = mfma16(cur.mqa[kt], load_bf16x8(&sm.xb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), o[ct]);
-      bf16* oc = static_cast<bf16*>(p.o) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = q.tc0 + r;
-        if (t < Lc) {
-          const uint32_t oo = static_cast<uint32_t>(t) * q.o_row + lr;
-          oc[oo] = bf16_of(o[0][r]);
-          (oc + oo)[16] = bf16_of(o[1][r]);
-        }
-      }
-    }
-    // step 5: H = e^{gamma_L} H + K^T diag(w) X for the wave's row tiles
+    lds_barrier();  // 2: X complete
+    lds_barrier();  // 3: H of the next chunk complete
+  }
+
+  // Group B, one chunk: H update and checkpoint.
+  __device__ static void step_b(const ChunkFwdArgs& p, const Smem& smc, Smem& sm, const Lane& q, int c,
+                                const StageB& cur, f32x4 (&H)[RTW][2]) {
+    const Dims& d = p.d;
+    const int lr = q.lr, lg = q.lg;
+    lds_barrier();  // 1
+    lds_barrier();  // 2: X complete
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
@@ -383,14 +429,15 @@ struct ChunkFwd {
     for (int kt = 0; kt < 2; ++kt) {
       bf16x8 bx[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) bx[ct] = load_bf16x8(&sm.xw[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
+      for (int ct = 0; ct < 2; ++ct) bx[ct] = load_bf16x8(&smc.xw[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) H[it][ct] = mfma16(cur.kta[it][kt], bx[ct], H[it][ct]);
     }
-    // step 6: H^T for the next chunk; checkpoint of the state at chunk c+1's start
     put_h(sm, q, H);
+    // checkpoint of the state at chunk c+1's start: a transpose inside each
+    // quad of lanes gives every lane 4 consecutive columns of one row
     if (p.ckpt && c + 1 < q.NC) {
       float* ck = p.ckpt + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv + q.col0 +
                   (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg) * d.Dv + lr);
@@ -403,7 +450,128 @@ struct ChunkFwd {
           cp[16] = H[it][1][r];
         }
     }
-    lds_barrier();
+    lds_barrier();  // 3: H of the next chunk complete
+  }
+
+  // Group C, one chunk: (Q H)^T, then O^T = (Q H)^T diag(e^gamma rq) + X^T Mq^T,
+  // which gives each lane one step and four consecutive columns to store.
+  __device__ static void step_c(const ChunkFwdArgs& p, const Smem& smc, const Lane& q, int c, const StageC& cur) {
+    const Dims& d = p.d;
+    const int t0 = c * L, Lc = min(L, d.T - t0);
+    const int lr = q.lr, lg = q.lg;
+    f32x4 o[2];  // rows v = 16 ct + 4 lg + r, column t = 16 w + lr
+    o[0] = o[1] = f4zero();
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        o[ct] = mfma16(load_bf16x8(&smc.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), cur.qa[kt], o[ct]);
+    lds_barrier();  // 1
+    lds_barrier();  // 2: X complete
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[ct][r] *= cur.co;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        o[ct] = mfma16(load_bf16x8(&smc.xb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), cur.mqa[kt], o[ct]);
+    if (q.ta < Lc) {
+      bf16* oc = static_cast<bf16*>(p.o) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0 +
+                 (static_cast<uint32_t>(q.ta) * q.v_row + 4 * lg);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        *reinterpret_cast<uint2*>(oc + 16 * ct) = pack4_bf16(o[ct][0], o[ct][1], o[ct][2], o[ct][3]);
+    }
+    lds_barrier();  // 3
+  }
+
+  __device__ static void run_a(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
+    lds_barrier();  // 0: initial H
+    // Prefetch two chunks ahead through three register stages.  The loads are
+    // unconditional, from a chunk index clamped to the last chunk: a load under
+    // a branch makes the compiler wait for every outstanding load where the
+    // branch joins, which would void the prefetch.
+    const int cl = q.NC - 1;
+    StageA s0, s1, s2;
+    if (q.NC > 0) {
+      load_a(p, q, 0, s0);
+      load_a(p, q, min(1, cl), s1);
+    }
+    for (int c = 0; c < q.NC; c += 3) {
+      load_a(p, q, min(c + 2, cl), s2);
+      step_a(sm, sm, q, s0);
+      if (c + 1 >= q.NC) break;
+      load_a(p, q, min(c + 3, cl), s0);
+      step_a(sm, sm, q, s1);
+      if (c + 2 >= q.NC) break;
+      load_a(p, q, min(c + 4, cl), s1);
+      step_a(sm, sm, q, s2);
+    }
+  }
+
+  __device__ static void run_b(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
+    const Dims& d = p.d;
+    const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
+    // H: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
+    f32x4 H[RTW][2];
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
+          H[it][ct][r] = p.state0 ? p.state0[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
+        }
+    put_h(sm, q, H);
+    lds_barrier();  // 0
+    const int cl = q.NC - 1;
+    StageB s0, s1, s2;
+    if (q.NC > 0) {
+      load_b(p, q, 0, s0);
+      load_b(p, q, min(1, cl), s1);
+    }
+    for (int c = 0; c < q.NC; c += 3) {
+      load_b(p, q, min(c + 2, cl), s2);
+      step_b(p, sm, sm, q, c, s0, H);
+      if (c + 1 >= q.NC) break;
+      load_b(p, q, min(c + 3, cl), s0);
+      step_b(p, sm, sm, q, c + 1, s1, H);
+      if (c + 2 >= q.NC) break;
+      load_b(p, q, min(c + 4, cl), s1);
+      step_b(p, sm, sm, q, c + 2, s2, H);
+    }
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
+          p.state_out[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = H[it][ct][r];
+        }
+  }
+
+  __device__ static void run_c(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
+    lds_barrier();  // 0: initial H
+    const int cl = q.NC - 1;
+    StageC s0, s1, s2;
+    if (q.NC > 0) {
+      load_c(p, q, 0, s0);
+      load_c(p, q, min(1, cl), s1);
+    }
+    for (int c = 0; c < q.NC; c += 3) {
+      load_c(p, q, min(c + 2, cl), s2);
+      step_c(p, sm, q, c, s0);
+      if (c + 1 >= q.NC) break;
+      load_c(p, q, min(c + 3, cl), s0);
+      step_c(p, sm, q, c + 1, s1);
+      if (c + 2 >= q.NC) break;
+      load_c(p, q, min(c + 4, cl), s1);
+      step_c(p, sm, q, c + 2, s2);
+    }
   }
 
   __device__ static void run(const ChunkFwdArgs& p, Smem& sm) {
@@ -418,53 +586,35 @@ struct ChunkFwd {
     q.bj = q.b * d.Hk + q.j;
     q.col0 = slice * NV;
     const int tid = threadIdx.x, l = tid & 63;
-    q.w = tid >> 6;
+    q.w = (tid >> 6) & 3;
     q.lr = l & 15;
     q.lg = l >> 4;
     q.ta = 16 * q.w + q.lr;
     q.tc0 = 16 * q.w + 4 * q.lg;
     q.last = d.T - 1;
     q.qk_row = d.Hk * DK;
-    q.v_row = q.o_row = d.Hv * d.Dv;
-    const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
-
-    // H: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
-    f32x4 H[RTW][2];
-#pragma unroll
-    for (int it = 0; it < RTW; ++it)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          H[it][ct][r] = p.state0 ? p.state0[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
-        }
-    put_h(sm, q, H);
-    lds_barrier();
-
-    Stage s0, s1;
-    if (q.NC > 0) load_stage(p, q, 0, s0);
-    for (int c = 0; c < q.NC; c += 2) {
-      if (c + 1 < q.NC) load_stage(p, q, c + 1, s1);
-      step(p, sm, q, c, s0, H);
-      if (c + 1 >= q.NC) break;
-      if (c + 2 < q.NC) load_stage(p, q, c + 2, s0);
-      step(p, sm, q, c + 1, s1, H);
+    q.v_row = d.Hv * d.Dv;
+    {
+      const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
+      q.rk = make_rsrc(p.k, bt * d.Hk * DK * 2);
+      q.rq = make_rsrc(p.q, bt * d.Hk * DK * 2);
+      q.rv = make_rsrc(p.v, bt * d.Hv * d.Dv * 2);
+      q.rtx = make_rsrc(p.cb.Tx, nmat * L * L * 2);
+      q.rmq = make_rsrc(p.cb.Mq, nmat * L * L * 2);
+      q.rkt = make_rsrc(p.cb.KT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);
+      q.rsc = make_rsrc(p.cb.sc, nmat * SC_ROWS * L * 4);
     }
-#pragma unroll
-    for (int it = 0; it < RTW; ++it)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          p.state_out[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = H[it][ct][r];
-        }
+    if (tid < 256)
+      run_a(p, sm, q);
+    else if (tid < 512)
+      run_b(p, sm, q);
+    else
+      run_c(p, sm, q);
   }
 };
 
 template <int DK>
-__global__ void __launch_bounds__(NT) chunk_fwd_kernel(ChunkFwdArgs p) {
+__global__ void __launch_bounds__(768) chunk_fwd_kernel(ChunkFwdArgs p) {
   __shared__ typename ChunkFwd<DK>::Smem sm;
   ChunkFwd<DK>::run(p, sm);
 }
@@ -473,7 +623,7 @@ __global__ void __launch_bounds__(NT) chunk_fwd_kernel(ChunkFwdArgs p) {
 
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st) {
   if (a.d.T == 0) return hipSuccess;
-  dim3 grid(a.d.nchunk(), a.d.B * a.d.Hv);
+  dim3 grid(a.d.nchunk(), a.d.B * a.d.Hk);
   switch (a.d.Dk) {
     case 64: chunk_prep_kernel<64><<<grid, NT, 0, st>>>(a); break;
     case 128: chunk_prep_kernel<128><<<grid, NT, 0, st>>>(a); break;
@@ -487,10 +637,10 @@ hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st) {
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st) {
   const int nblk = a.d.B * a.d.Hv * (a.d.Dv / ChunkFwd<64>::NV);
   switch (a.d.Dk) {
-    case 64: chunk_fwd_kernel<64><<<nblk, NT, 0, st>>>(a); break;
-    case 128: chunk_fwd_kernel<128><<<nblk, NT, 0, st>>>(a); break;
-    case 192: chunk_fwd_kernel<192><<<nblk, NT, 0, st>>>(a); break;
-    case 256: chunk_fwd_kernel<256><<<nblk, NT, 0, st>>>(a); break;
+    case 64: chunk_fwd_kernel<64><<<nblk, ChunkFwd<64>::NTS, 0, st>>>(a); break;
+    case 128: chunk_fwd_kernel<128><<<nblk, ChunkFwd<128>::NTS, 0, st>>>(a); break;
+    case 192: chunk_fwd_kernel<192><<<nblk, ChunkFwd<192>::NTS, 0, st>>>(a); break;
+    case 256: chunk_fwd_kernel<256><<<nblk, ChunkFwd<256>::NTS, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

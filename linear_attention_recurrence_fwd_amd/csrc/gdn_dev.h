@@ -123,11 +123,52 @@ __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, float s) {
     o[i] = pack2_bf16(__uint_as_float(w[i] << 16) * s, __uint_as_float(w[i] & 0xffff0000u) * s);
   return as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
 }
+// 4x4 transpose inside each DPP quad: lane e of the quad returns element e
+// of every lane's x, i.e. out[r] on lane e = (x[e] on lane r).  Two
+// butterfly exchanges (lane xor 1, lane xor 2), moves and selects only.
+__device__ __forceinline__ f32x4 quad_transpose(const f32x4& x) {
+  const int e = threadIdx.x & 3;
+  f32x4 y, z;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float o = dpp<kQuadXor1>(x[r ^ 1]);
+    y[r] = ((e ^ r) & 1) ? o : x[r];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float o = dpp<kQuadXor2>(y[r ^ 2]);
+    z[r] = ((e ^ r) & 2) ? o : y[r];
+  }
+  return z;
+}
 // Sum over the 4 lanes of a DPP quad; every lane of the quad gets the same bits.
 __device__ __forceinline__ float quad_sum(float v) {
   v += dpp<kQuadXor1>(v);
   v += dpp<kQuadXor2>(v);
   return v;
+}
+
+// Buffer loads: a wave-uniform resource descriptor (base, byte size) in
+// scalar registers plus a 32-bit byte offset per lane.  Reads at or past the
+// size return zeros.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), 0x00020000);
+}
+__device__ __forceinline__ bf16x8 buf_bf16x8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 buf_u2(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ float4 buf_f4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_f1(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
