@@ -438,29 +438,36 @@ struct ChunkBwdGrad {
     uint32_t v_row;
   };
 
+  // All loads are unconditional buffer loads, so no load sits under a branch
+  // (where a branch joins, the compiler waits for every outstanding load).  An
+  // absent initial state reads through a zero-size descriptor, i.e. as zeros.
   __device__ static void prefetch(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, int v0, Pf& f) {
     const Dims& d = p.d;
     const int bh = x.b * d.Hv + h;
-    const float* Hs = x.c == 0 ? p.state0 : p.ckpt + (static_cast<size_t>(x.c - 1) * d.B * d.Hv) * DK * d.Dv;
-    if (Hs) {
-      const float* hp = Hs + static_cast<size_t>(bh) * DK * d.Dv + static_cast<size_t>(x.i0) * d.Dv + v0 + x.vv0;
+    const size_t hsz = static_cast<size_t>(DK) * d.Dv;
+    const float* Hs = x.c == 0 ? p.state0 : p.ckpt + (static_cast<size_t>(x.c - 1) * d.B * d.Hv) * hsz;
+    const rsrc_t rh = make_rsrc(Hs ? static_cast<const void*>(Hs + bh * hsz) : static_cast<const void*>(p.dHend), Hs ? hsz * 4 : 0);
+    const uint32_t ho = 4 * (x.i0 * d.Dv + v0 + x.vv0);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) f.h[a] = *reinterpret_cast<const float4*>(hp + a * d.Dv);
-    } else {
+    for (int a = 0; a < 4; ++a) f.h[a] = buf_f4(rh, ho + 4 * a * d.Dv);
+    const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * hsz, hsz * 2);
+    const uint32_t dho = 2 * ((v0 + x.vv0) * DK + x.i0);
 #pragma unroll
-      for (int a = 0; a < 4; ++a) f.h[a] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const bf16* dhp = p.dHend + (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * d.Dv * DK +
-                      static_cast<size_t>(v0 + x.vv0) * DK + x.i0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.dh[e] = *reinterpret_cast<const uint2*>(dhp + e * DK);
+    for (int e = 0; e < 4; ++e) f.dh[e] = buf_u2(rdh, dho + 2 * e * DK);
     const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv + v0;
-    const bf16* src[3] = {static_cast<const bf16*>(p.v) + vbase, static_cast<const bf16*>(p.dO) + vbase, p.E + vbase};
+    const size_t vrem = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
+    const rsrc_t rs[3] = {make_rsrc(static_cast<const bf16*>(p.v) + vbase, vrem),
+                          make_rsrc(static_cast<const bf16*>(p.dO) + vbase, vrem), make_rsrc(p.E + vbase, vrem)};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int ci = min(tid + u * NTG, NCH - 1);
-      const int ten = ci / (L * NS / 8), row = (ci / (NS / 8)) % L, c8 = 8 * (ci % (NS / 8));
-      f.ch[u] = *reinterpret_cast<const uint4*>(src[ten] + static_cast<uint32_t>(min(row, x.tl)) * x.v_row + c8);
+      const int row = (ci / (NS / 8)) % L, c8 = 8 * (ci % (NS / 8));
+      // the tensor of a chunk is the same for the 64 lanes of a wave (256
+      // chunks per tensor), so the descriptor stays in scalar registers
+      const int ten = __builtin_amdgcn_readfirstlane(ci / (L * NS / 8));
+      const uint32_t o = 2 * (static_cast<uint32_t>(min(row, x.tl)) * x.v_row + c8);
+      const rsrc_t r = ten == 0 ? rs[0] : ten == 1 ? rs[1] : rs[2];
+      f.ch[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
     }
   }
   __device__ static void load_start(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, HeadStart& hs) {
@@ -487,7 +494,9 @@ struct ChunkBwdGrad {
     ht.at = *reinterpret_cast<const uint4*>(p.cb.AtT + mat + 8 * u);
     const int t = min(tid & 63, x.tl);
     ht.a_bits = static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h];
-    ht.valid = p.mask == nullptr ? 1 : p.mask[static_cast<size_t>(x.b) * d.T + x.t0 + t];
+    const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a, p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+    const uint32_t mv = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + t, 0, 0));
+    ht.valid = p.mask ? static_cast<unsigned char>(mv) : 1;
   }
 
   __device__ static void put_chunks(Smem& sm, int tid, const Pf& f) {
@@ -519,6 +528,128 @@ struct ChunkBwdGrad {
       tc0 = 16 * tt + 4 * lg;
     }
   };
+
+  struct HeadAcc {
+    f32x4 dox[2], xe[2];
+    float pb[4], pa, pdb, phdh;
+  };
+  // One 32-column slab of head h: stage the prefetched H, dH', v, dO, eps
+  // in LDS, issue the next slab's loads (unconditional, so the prefetch stays
+  // in flight), and accumulate.
+  __device__ static void slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, bool has_blk, int h, int hlast,
+                              int si, int nsl, Pf& pf, const bf16x8 (&ka)[KS],
+                              const bf16x8 (&qa)[KS], const bf16x8 (&txb)[2], f32x4 (&accQ)[IH],
+                              f32x4 (&accK)[IH], HeadAcc& ac) {
+    const Lanes q;
+    const int lr = q.lr, lg = q.lg, ta = q.ta, tc0 = q.tc0, hw = q.hw;
+    // ---- this slab's H and dH' into LDS (both orientations), <dH', H>; v / dO / eps tiles
+    if (has_blk) {
+      const int i0 = x.i0, vv0 = x.vv0;
+      float hx[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        hx[a][0] = pf.h[a].x;
+        hx[a][1] = pf.h[a].y;
+        hx[a][2] = pf.h[a].z;
+        hx[a][3] = pf.h[a].w;
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t sh = a & 1 ? 16u : 0u;
+        uint32_t dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[e] = ((a >> 1 ? pf.dh[e].y : pf.dh[e].x) >> sh) & 0xffffu;
+        *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
+        *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = make_uint2(dv[0] | (dv[1] << 16), dv[2] | (dv[3] << 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ac.phdh = fmaf(hx[a][e], __uint_as_float(dv[e] << 16), ac.phdh);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<uint2*>(&sm.u.s.hi[(vv0 + e) * IS + i0]) = pack4_bf16(hx[0][e], hx[1][e], hx[2][e], hx[3][e]);
+        *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) = pf.dh[e];
+      }
+    }
+    put_chunks(sm, q.tid, pf);
+    {  // the next slab: of this head, or the first of the next head (the last
+       // head's last slab reloads its own first slab: harmless, never used)
+      const bool more = si + 1 < nsl;
+      const int nh = min(h + 1, hlast);
+      prefetch(p, x, q.tid, more ? h : nh, more ? (si + 1) * NS : 0, pf);
+    }
+    lds_barrier();
+    const bf16* vt = sm.u.s.vt[0];
+    const bf16* dt = sm.u.s.vt[1];
+    const bf16* et = sm.u.s.vt[2];
+    // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta)
+    f32x4 kh = f4zero(), qh = f4zero(), kdt = f4zero();
+#pragma unroll
+    for (int kt = 0; kt < KS; ++kt) {
+      const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]);
+      kh = mfma16(ka[kt], bh8, kh);
+      qh = mfma16(qa[kt], bh8, qh);
+      kdt = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]), ka[kt], kdt);
+    }
+    // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
+    {
+      float rv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tc0 + r, o = t * VS + 16 * hw + lr;
+        const float eg = sm.eg[t], cr = eg * sm.rk[t];
+        const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), epv = to_f32(et[o]);
+        rv[r] = vv - cr * kh[r];
+        ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
+        ac.pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, ac.pb[r]);
+      }
+      *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
+    }
+    lds_barrier();
+    // ---- X^T = R^T Tx^T: the lane holds X[ta][16 hw + 4 lg + r]
+    {
+      f32x4 xt = f4zero();
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        xt = mfma16(load_bf16x8(&sm.u.s.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
+      const int vc = 16 * hw + 4 * lg;
+      const float sx = sm.el[ta] * sm.beta[ta];
+      *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
+      *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) = pack4_bf16(sx * xt[0], sx * xt[1], sx * xt[2], sx * xt[3]);
+      const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
+      const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
+                            __uint_as_float(e4.y << 16), __uint_as_float(e4.y & 0xffff0000u)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ac.pdb = fmaf(e4f[r], xt[r], ac.pdb);
+        ac.pa = fmaf(kdt[r], xt[r], ac.pa);
+      }
+    }
+    lds_barrier();
+    // ---- contractions over the slab's columns
+    {
+      const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta];
+      const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
+      const bf16x8 dos8 = scale8(do8, sq), eps8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), se);
+      const bf16x8 xs8 = load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]);
+      const bf16x8 xr8 = load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]);
+#pragma unroll
+      for (int k = 0; k < IH; ++k) {
+        const int it = hw * IH + k;
+        const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
+        const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
+        accQ[k] = mfma16(dos8, bhv, accQ[k]);
+        accK[k] = mfma16(eps8, bhv, accK[k]);
+        accK[k] = mfma16(xs8, bdh, accK[k]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int sr = (16 * (2 * hw + u) + lr) * VS + 8 * lg;
+        ac.dox[u] = mfma16(do8, load_bf16x8(&sm.u.s.xr[sr]), ac.dox[u]);
+        ac.xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), ac.xe[u]);
+      }
+    }
+    lds_barrier();
+  }
 
   __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
     const Dims& d = p.d;
@@ -571,14 +702,14 @@ struct ChunkBwdGrad {
     }
 
     const int nsl = d.Dv / NS;
+    const int hlast = x.j * G + G - 1;
     Pf pf;
-    HeadStart hs;
-    HeadTail ht;
-    load_start(p, x, tid0, x.j * G, hs);
     prefetch(p, x, tid0, x.j * G, 0, pf);
     for (int hh = 0; hh < G; ++hh) {
       const int h = x.j * G + hh;
       const Lanes ln;
+      HeadStart hs;
+      load_start(p, x, ln.tid, h, hs);
       __syncthreads();  // the previous head is done with every shared array
       if (ln.tid < L) {
         const int t = ln.tid;
@@ -591,134 +722,23 @@ struct ChunkBwdGrad {
       const float egl = hs.egl;
       const bf16x8 txb[2] = {hs.txb[0], hs.txb[1]};
       __syncthreads();
-      f32x4 dox[2], xe[2];
-      dox[0] = dox[1] = xe[0] = xe[1] = f4zero();
-      float pb[4] = {0.f, 0.f, 0.f, 0.f}, pa = 0.f, pdb = 0.f, phdh = 0.f;
-
-      for (int si = 0; si < nsl; ++si) {
-        const Lanes q;
-        const int lr = q.lr, lg = q.lg, ta = q.ta, tc0 = q.tc0, hw = q.hw;
-        // ---- this slab's H and dH' into LDS (both orientations), <dH', H>; v / dO / eps tiles
-        if (has_blk) {
-          const int i0 = x.i0, vv0 = x.vv0;
-          float hx[4][4];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            hx[a][0] = pf.h[a].x;
-            hx[a][1] = pf.h[a].y;
-            hx[a][2] = pf.h[a].z;
-            hx[a][3] = pf.h[a].w;
-          }
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const uint32_t sh = a & 1 ? 16u : 0u;
-            uint32_t dv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dv[e] = ((a >> 1 ? pf.dh[e].y : pf.dh[e].x) >> sh) & 0xffffu;
-            *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
-            *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = make_uint2(dv[0] | (dv[1] << 16), dv[2] | (dv[3] << 16));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) phdh = fmaf(hx[a][e], __uint_as_float(dv[e] << 16), phdh);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            *reinterpret_cast<uint2*>(&sm.u.s.hi[(vv0 + e) * IS + i0]) = pack4_bf16(hx[0][e], hx[1][e], hx[2][e], hx[3][e]);
-            *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) = pf.dh[e];
-          }
-        }
-        put_chunks(sm, q.tid, pf);
-        {  // next slab (of this head or the next one); in the last slab, what
-           // this head's tail and the next head's start need
-          const int nsi = si + 1 < nsl ? si + 1 : 0;
-          const int nh = si + 1 < nsl ? h : h + 1;
-          if (nh < x.j * G + G) prefetch(p, x, q.tid, nh, nsi * NS, pf);
-          if (si + 1 == nsl) {
-            load_tail(p, x, q.tid, h, ht);
-            if (hh + 1 < G) load_start(p, x, q.tid, h + 1, hs);
-          }
-        }
-        lds_barrier();
-        const bf16* vt = sm.u.s.vt[0];
-        const bf16* dt = sm.u.s.vt[1];
-        const bf16* et = sm.u.s.vt[2];
-        // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta)
-        f32x4 kh = f4zero(), qh = f4zero(), kdt = f4zero();
-#pragma unroll
-        for (int kt = 0; kt < KS; ++kt) {
-          const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]);
-          kh = mfma16(ka[kt], bh8, kh);
-          qh = mfma16(qa[kt], bh8, qh);
-          kdt = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]), ka[kt], kdt);
-        }
-        // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
-        {
-          float rv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tc0 + r, o = t * VS + 16 * hw + lr;
-            const float eg = sm.eg[t], cr = eg * sm.rk[t];
-            const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), epv = to_f32(et[o]);
-            rv[r] = vv - cr * kh[r];
-            pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, pb[r]);
-            pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, pb[r]);
-          }
-          *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
-        }
-        lds_barrier();
-        // ---- X^T = R^T Tx^T: the lane holds X[ta][16 hw + 4 lg + r]
-        {
-          f32x4 xt = f4zero();
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-            xt = mfma16(load_bf16x8(&sm.u.s.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
-          const int vc = 16 * hw + 4 * lg;
-          const float sx = sm.el[ta] * sm.beta[ta];
-          *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
-          *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) = pack4_bf16(sx * xt[0], sx * xt[1], sx * xt[2], sx * xt[3]);
-          const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
-          const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
-                                __uint_as_float(e4.y << 16), __uint_as_float(e4.y & 0xffff0000u)};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pdb = fmaf(e4f[r], xt[r], pdb);
-            pa = fmaf(kdt[r], xt[r], pa);
-          }
-        }
-        lds_barrier();
-        // ---- contractions over the slab's columns
-        {
-          const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta];
-          const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
-          const bf16x8 dos8 = scale8(do8, sq), eps8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), se);
-          const bf16x8 xs8 = load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]);
-          const bf16x8 xr8 = load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]);
-#pragma unroll
-          for (int k = 0; k < IH; ++k) {
-            const int it = hw * IH + k;
-            const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
-            const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
-            accQ[k] = mfma16(dos8, bhv, accQ[k]);
-            accK[k] = mfma16(eps8, bhv, accK[k]);
-            accK[k] = mfma16(xs8, bdh, accK[k]);
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int sr = (16 * (2 * hw + u) + lr) * VS + 8 * lg;
-            dox[u] = mfma16(do8, load_bf16x8(&sm.u.s.xr[sr]), dox[u]);
-            xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), xe[u]);
-          }
-        }
-        lds_barrier();
-      }
+      HeadAcc ac;
+      ac.dox[0] = ac.dox[1] = ac.xe[0] = ac.xe[1] = f4zero();
+      ac.pb[0] = ac.pb[1] = ac.pb[2] = ac.pb[3] = ac.pa = ac.pdb = ac.phdh = 0.f;
+      for (int si = 0; si < nsl; ++si)
+        slab(p, sm, x, has_blk, h, hlast, si, nsl, pf, ka, qa, txb, accQ, accK, ac);
 
       // ---- per-row sums of head h
+      HeadTail ht;
+      load_tail(p, x, threadIdx.x, h, ht);
       {
         const Lanes q;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v = row_sum16(pb[r]);
+          const float v = row_sum16(ac.pb[r]);
           if (q.lr == 0) sm.bv[q.hw][q.tc0 + r] = v;
         }
+        float pa = ac.pa, pdb = ac.pdb;
         pa += __shfl_xor(pa, 16);
         pa += __shfl_xor(pa, 32);
         pdb += __shfl_xor(pdb, 16);
@@ -727,7 +747,7 @@ struct ChunkBwdGrad {
           sm.pa[q.hw][q.ta] = pa;
           sm.pdb[q.hw][q.ta] = pdb;
         }
-        phdh = wave_sum(phdh);
+        const float phdh = wave_sum(ac.phdh);
         if (q.l == 0) sm.red[q.w] = phdh;
         {
           const int row = q.tid >> 3, c8 = 8 * (q.tid & 7);
@@ -738,8 +758,8 @@ struct ChunkBwdGrad {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sm.u.h.dox[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = dox[u][r];
-            sm.u.h.xe[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = xe[u][r];
+            sm.u.h.dox[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = ac.dox[u][r];
+            sm.u.h.xe[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = ac.xe[u][r];
           }
       }
       __syncthreads();
