@@ -75,49 +75,48 @@ struct ChunkBwdState {
     float egl;
   };
   struct Lane {
-    int b, h, j, bh, bj, col0, w, lr, lg, ta, tc0, last, NC;
+    int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
     uint32_t qk_row, v_row;
+    rsrc_t rk, rdo, rpq, rtx, rat, rqt, rkt, rsc;  // buffer descriptors of the operands
   };
 
+  // Operand loads are buffer loads at byte offsets from the tensor's base.
   __device__ static void load_stage(const ChunkBwdArgs& p, const Lane& q, int c, Stage& s) {
     const Dims& d = p.d;
     const int t0 = c * L, tl = q.last - t0;
-    const bf16* kc = static_cast<const bf16*>(p.k) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hk + q.j) * DK;
-    const uint32_t ko = static_cast<uint32_t>(min(q.ta, tl)) * q.qk_row + 8 * q.lg;
+    // quad-coalesced operand loads (see to_mfma_layout), permuted at use
+    const int cr_ = 16 * q.w + coal_row(q.l), cp_ = coal_piece(q.l);
+    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
 #pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = load_bf16x8(kc + ko + 32 * kt);
-    const size_t mat = (static_cast<size_t>(q.bh) * q.NC + c) * L * L;
-    const uint32_t mo = q.ta * L + 8 * q.lg;
+    for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = buf_bf16x8(q.rk, ko + 64 * kt);
+    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      s.pqa[kt] = load_bf16x8(p.cb.PqT + mat + mo + 32 * kt);
-      s.txa[kt] = load_bf16x8(p.cb.TxT + mat + mo + 32 * kt);
-      s.ata[kt] = load_bf16x8(p.cb.AtT + mat + mo + 32 * kt);
+      s.pqa[kt] = buf_bf16x8(q.rpq, mo + 64 * kt);
+      s.txa[kt] = buf_bf16x8(q.rtx, mo + 64 * kt);
+      s.ata[kt] = buf_bf16x8(q.rat, mo + 64 * kt);
     }
-    const size_t kt0 = (static_cast<size_t>(q.bj) * q.NC + c) * DK * L;
-    const uint32_t kto = (16 * q.w * RTW + q.lr) * L + 8 * q.lg;
+    const uint32_t kto = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + coal_row(q.l)) * L +
+                              8 * coal_piece(q.l));
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        s.qta[it][kt] = load_bf16x8(p.cb.QT + kt0 + kto + (it * 16 * L + 32 * kt));
-        s.kta[it][kt] = load_bf16x8(p.cb.KT + kt0 + kto + (it * 16 * L + 32 * kt));
+        s.qta[it][kt] = buf_bf16x8(q.rqt, kto + 2 * (it * 16 * L) + 64 * kt);
+        s.kta[it][kt] = buf_bf16x8(q.rkt, kto + 2 * (it * 16 * L) + 64 * kt);
       }
-    const unsigned short* dc = static_cast<const unsigned short*>(p.dO) +
-                               ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const uint32_t vo = static_cast<uint32_t>(min(q.tc0 + r, tl)) * q.v_row + q.lr;
-      s.dov[0][r] = dc[vo];
-      s.dov[1][r] = (dc + vo)[16];
+      const uint32_t vo = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.tc0 + r, tl)) * d.Hv + q.h) * d.Dv + q.col0 + q.lr);
+      s.dov[0][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rdo, vo, 0, 0));
+      s.dov[1][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rdo, vo + 32, 0, 0));
     }
-    const float* scc = p.cb.sc + (static_cast<size_t>(q.bh) * q.NC + c) * SC_ROWS * L;
-    const float* scl = scc + q.tc0;
-    s.kl = *reinterpret_cast<const float4*>(scl + SC_KL * L);
-    s.bt = *reinterpret_cast<const float4*>(scl + SC_BETA * L);
-    s.co = *reinterpret_cast<const float4*>(scl + SC_CO * L);
-    s.cr = *reinterpret_cast<const float4*>(scl + SC_CR * L);
-    s.egl = scc[SC_EGL * L];
+    const uint32_t so = 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + q.tc0);
+    s.kl = buf_f4(q.rsc, so + 4 * SC_KL * L);
+    s.bt = buf_f4(q.rsc, so + 4 * SC_BETA * L);
+    s.co = buf_f4(q.rsc, so + 4 * SC_CO * L);
+    s.cr = buf_f4(q.rsc, so + 4 * SC_CR * L);
+    s.egl = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_EGL * L));
   }
 
   __device__ static void put_h(Smem& sm, const Lane& q, const f32x4 (&H)[RTW][2]) {
@@ -130,7 +129,22 @@ struct ChunkBwdState {
   }
 
   __device__ static void step(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c,
-                              const Stage& cur, f32x4 (&dH)[RTW][2]) {
+                              Stage& cur, f32x4 (&dH)[RTW][2]) {
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt) cur.ka[kt] = to_mfma_layout(cur.ka[kt]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      cur.pqa[kt] = to_mfma_layout(cur.pqa[kt]);
+      cur.txa[kt] = to_mfma_layout(cur.txa[kt]);
+      cur.ata[kt] = to_mfma_layout(cur.ata[kt]);
+    }
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        cur.qta[it][kt] = to_mfma_layout(cur.qta[it][kt]);
+        cur.kta[it][kt] = to_mfma_layout(cur.kta[it][kt]);
+      }
     const Dims& d = p.d;
     const int t0 = c * L, Lc = min(L, d.T - t0);
     const int lr = q.lr, lg = q.lg;
@@ -139,16 +153,21 @@ struct ChunkBwdState {
     const float cov[4] = {cur.co.x, cur.co.y, cur.co.z, cur.co.w};
     const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
 
-    // dH' of this chunk for the gradient pass: [v][i], bf16
+    // dH' of this chunk for the gradient pass: [i][v], bf16, the layout of the
+    // checkpoints; a transpose inside each quad of lanes gives every lane 4
+    // consecutive columns of one row
     {
-      bf16* dh = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * d.Dv * DK +
-                 static_cast<size_t>(q.col0) * DK;
+      const int e = lr & 3;
+      bf16* dh = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv + q.col0 +
+                 (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + e) * d.Dv + (lr & ~3));
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          *reinterpret_cast<uint2*>(dh + (16 * ct + lr) * DK + 16 * (q.w * RTW + it) + 4 * lg) =
-              pack4_bf16(dH[it][ct][0], dH[it][ct][1], dH[it][ct][2], dH[it][ct][3]);
+        for (int ct = 0; ct < 2; ++ct) {
+          const f32x4 tr = quad_transpose(dH[it][ct]);
+          *reinterpret_cast<uint2*>(dh + static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct) =
+              pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
+        }
     }
     // dO^T and diag(e^g rq) dO^T
 #pragma unroll
@@ -274,6 +293,7 @@ struct ChunkBwdState {
     q.col0 = slice * NV;
     const int tid = threadIdx.x, l = tid & 63;
     q.w = tid >> 6;
+    q.l = l;
     q.lr = l & 15;
     q.lg = l >> 4;
     q.ta = 16 * q.w + q.lr;
@@ -281,6 +301,18 @@ struct ChunkBwdState {
     q.last = d.T - 1;
     q.qk_row = d.Hk * DK;
     q.v_row = d.Hv * d.Dv;
+    {
+      const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
+      const size_t nkt = static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2;
+      q.rk = make_rsrc(p.k, bt * d.Hk * DK * 2);
+      q.rdo = make_rsrc(p.dO, bt * d.Hv * d.Dv * 2);
+      q.rpq = make_rsrc(p.cb.PqT, nmat * L * L * 2);
+      q.rtx = make_rsrc(p.cb.TxT, nmat * L * L * 2);
+      q.rat = make_rsrc(p.cb.AtT, nmat * L * L * 2);
+      q.rqt = make_rsrc(p.cb.QT, nkt);
+      q.rkt = make_rsrc(p.cb.KT, nkt);
+      q.rsc = make_rsrc(p.cb.sc, nmat * SC_ROWS * L * 4);
+    }
     const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
 
     // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
@@ -297,13 +329,16 @@ struct ChunkBwdState {
     put_h(sm, q, dH);
     lds_barrier();
 
+    // The prefetches are unconditional, from a chunk index clamped to the
+    // first chunk: a load under a branch makes the compiler wait for every
+    // outstanding load where the branch joins, which would void the prefetch.
     Stage s0, s1;
     if (q.NC > 0) load_stage(p, q, q.NC - 1, s0);
     for (int c = q.NC - 1; c >= 0; c -= 2) {
-      if (c >= 1) load_stage(p, q, c - 1, s1);
+      load_stage(p, q, max(c - 1, 0), s1);
       step(p, sm, q, c, s0, dH);
       if (c < 1) break;
-      if (c >= 2) load_stage(p, q, c - 2, s0);
+      load_stage(p, q, max(c - 2, 0), s0);
       step(p, sm, q, c - 1, s1, dH);
     }
 #pragma unroll
@@ -430,7 +465,7 @@ struct ChunkBwdGrad {
   static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the v / dO / eps tiles
   struct Pf {
     float4 h[4];   // H rows i0 + a, cols vv0 .. vv0+3 (this thread's block)
-    uint2 dh[4];   // dH' at v = vv0 + e, rows i0 .. i0+3
+    uint2 dh[4];   // dH' rows i0 + a, cols vv0 .. vv0+3 (bf16)
     uint4 ch[2];   // chunks tid and tid + NTG of the v / dO / eps tiles
   };
   struct Ctx {
@@ -451,9 +486,9 @@ struct ChunkBwdGrad {
 #pragma unroll
     for (int a = 0; a < 4; ++a) f.h[a] = buf_f4(rh, ho + 4 * a * d.Dv);
     const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * hsz, hsz * 2);
-    const uint32_t dho = 2 * ((v0 + x.vv0) * DK + x.i0);
+    const uint32_t dho = 2 * (x.i0 * d.Dv + v0 + x.vv0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f.dh[e] = buf_u2(rdh, dho + 2 * e * DK);
+    for (int a = 0; a < 4; ++a) f.dh[a] = buf_u2(rdh, dho + 2 * a * d.Dv);
     const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv + v0;
     const size_t vrem = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
     const rsrc_t rs[3] = {make_rsrc(static_cast<const bf16*>(p.v) + vbase, vrem),
@@ -553,21 +588,23 @@ struct ChunkBwdGrad {
         hx[a][2] = pf.h[a].z;
         hx[a][3] = pf.h[a].w;
       }
+      uint32_t dv[4][4];  // dH' bits, [a = row i0 + a][e = column vv0 + e]
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const uint32_t sh = a & 1 ? 16u : 0u;
-        uint32_t dv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dv[e] = ((a >> 1 ? pf.dh[e].y : pf.dh[e].x) >> sh) & 0xffffu;
+        dv[a][0] = pf.dh[a].x & 0xffffu;
+        dv[a][1] = pf.dh[a].x >> 16;
+        dv[a][2] = pf.dh[a].y & 0xffffu;
+        dv[a][3] = pf.dh[a].y >> 16;
         *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
-        *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = make_uint2(dv[0] | (dv[1] << 16), dv[2] | (dv[3] << 16));
+        *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = pf.dh[a];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ac.phdh = fmaf(hx[a][e], __uint_as_float(dv[e] << 16), ac.phdh);
+        for (int e = 0; e < 4; ++e) ac.phdh = fmaf(hx[a][e], __uint_as_float(dv[a][e] << 16), ac.phdh);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         *reinterpret_cast<uint2*>(&sm.u.s.hi[(vv0 + e) * IS + i0]) = pack4_bf16(hx[0][e], hx[1][e], hx[2][e], hx[3][e]);
-        *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) = pf.dh[e];
+        *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) =
+            make_uint2(dv[0][e] | (dv[1][e] << 16), dv[2][e] | (dv[3][e] << 16));
       }
     }
     put_chunks(sm, q.tid, pf);

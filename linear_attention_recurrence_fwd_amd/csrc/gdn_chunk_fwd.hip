@@ -318,7 +318,7 @@ struct ChunkFwd {
   // within the group).  Addresses are a uniform 64-bit base plus a 32-bit
   // lane offset.
   struct Lane {
-    int b, h, j, bh, bj, col0, w, lr, lg, ta, tc0, last, NC;
+    int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
     uint32_t qk_row, v_row;   // element strides of one step in q/k and v/o
     rsrc_t rk, rq, rv, rtx, rmq, rkt, rsc;  // buffer descriptors of the operands
   };
@@ -327,10 +327,11 @@ struct ChunkFwd {
   __device__ static void load_a(const ChunkFwdArgs& p, const Lane& q, int c, StageA& s) {
     const Dims& d = p.d;
     const int t0 = c * L, tl = q.last - t0;
-    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.ta, tl)) * d.Hk + q.j) * DK + 8 * q.lg);
+    const int cr_ = 16 * q.w + coal_row(q.l), cp_ = coal_piece(q.l);  // quad-coalesced (see to_mfma_layout)
+    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = buf_bf16x8(q.rk, ko + 64 * kt);
-    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + q.ta * L + 8 * q.lg);
+    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s.txa[kt] = buf_bf16x8(q.rtx, mo + 64 * kt);
 #pragma unroll
@@ -346,7 +347,8 @@ struct ChunkFwd {
 
   __device__ static void load_b(const ChunkFwdArgs& p, const Lane& q, int c, StageB& s) {
     (void)p;
-    const uint32_t kto = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + q.lr) * L + 8 * q.lg);
+    const uint32_t kto = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + coal_row(q.l)) * L +
+                              8 * coal_piece(q.l));
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
@@ -357,10 +359,11 @@ struct ChunkFwd {
   __device__ static void load_c(const ChunkFwdArgs& p, const Lane& q, int c, StageC& s) {
     const Dims& d = p.d;
     const int t0 = c * L, tl = q.last - t0;
-    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.ta, tl)) * d.Hk + q.j) * DK + 8 * q.lg);
+    const int cr_ = 16 * q.w + coal_row(q.l), cp_ = coal_piece(q.l);  // quad-coalesced (see to_mfma_layout)
+    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt) s.qa[kt] = buf_bf16x8(q.rq, ko + 64 * kt);
-    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + q.ta * L + 8 * q.lg);
+    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s.mqa[kt] = buf_bf16x8(q.rmq, mo + 64 * kt);
     s.co = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_CO * L + q.ta));
@@ -376,7 +379,11 @@ struct ChunkFwd {
   }
 
   // Group A, one chunk: K H -> R -> X.
-  __device__ static void step_a(const Smem& smc, Smem& sm, const Lane& q, const StageA& cur) {
+  __device__ static void step_a(const Smem& smc, Smem& sm, const Lane& q, StageA& cur) {
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt) cur.ka[kt] = to_mfma_layout(cur.ka[kt]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) cur.txa[kt] = to_mfma_layout(cur.txa[kt]);
     const int lr = q.lr, lg = q.lg;
     const float wvv[4] = {cur.wv.x, cur.wv.y, cur.wv.z, cur.wv.w};
     const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
@@ -414,7 +421,11 @@ struct ChunkFwd {
 
   // Group B, one chunk: H update and checkpoint.
   __device__ static void step_b(const ChunkFwdArgs& p, const Smem& smc, Smem& sm, const Lane& q, int c,
-                                const StageB& cur, f32x4 (&H)[RTW][2]) {
+                                StageB& cur, f32x4 (&H)[RTW][2]) {
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) cur.kta[it][kt] = to_mfma_layout(cur.kta[it][kt]);
     const Dims& d = p.d;
     const int lr = q.lr, lg = q.lg;
     lds_barrier();  // 1
@@ -455,7 +466,11 @@ struct ChunkFwd {
 
   // Group C, one chunk: (Q H)^T, then O^T = (Q H)^T diag(e^gamma rq) + X^T Mq^T,
   // which gives each lane one step and four consecutive columns to store.
-  __device__ static void step_c(const ChunkFwdArgs& p, const Smem& smc, const Lane& q, int c, const StageC& cur) {
+  __device__ static void step_c(const ChunkFwdArgs& p, const Smem& smc, const Lane& q, int c, StageC& cur) {
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt) cur.qa[kt] = to_mfma_layout(cur.qa[kt]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) cur.mqa[kt] = to_mfma_layout(cur.mqa[kt]);
     const Dims& d = p.d;
     const int t0 = c * L, Lc = min(L, d.T - t0);
     const int lr = q.lr, lg = q.lg;
@@ -587,6 +602,7 @@ struct ChunkFwd {
     q.col0 = slice * NV;
     const int tid = threadIdx.x, l = tid & 63;
     q.w = (tid >> 6) & 3;
+    q.l = l;
     q.lr = l & 15;
     q.lg = l >> 4;
     q.ta = 16 * q.w + q.lr;

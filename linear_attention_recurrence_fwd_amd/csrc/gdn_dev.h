@@ -148,6 +148,24 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+// MFMA operands are loaded quad-coalesced -- lane m reads 16-byte piece m % 4
+// of tile row m / 4, so four lanes cover 64 contiguous bytes -- and then moved
+// to the operand layout (lane l: row l % 16, piece l / 16) by this lane
+// permutation: lane l takes the register of lane 4 (l % 16) + l / 16.
+__device__ __forceinline__ int coal_row(int l) { return l >> 2; }
+__device__ __forceinline__ int coal_piece(int l) { return l & 3; }
+__device__ __forceinline__ bf16x8 to_mfma_layout(const bf16x8& v) {
+  const int l = threadIdx.x & 63;
+  const int src = 4 * (4 * (l & 15) + (l >> 4));
+  const uint4 u = __builtin_bit_cast(uint4, v);
+  uint4 o;
+  o.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(u.x)));
+  o.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(u.y)));
+  o.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(u.z)));
+  o.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(u.w)));
+  return __builtin_bit_cast(bf16x8, o);
+}
+
 // Buffer loads: a wave-uniform resource descriptor (base, byte size) in
 // scalar registers plus a 32-bit byte offset per lane.  Reads at or past the
 // size return zeros.

@@ -148,7 +148,7 @@ struct ChunkBwdArgs {
   StepScalars s;
   ChunkBufs cb;
   bf16* E;        // [B,T,Hv,Dv]  eps, rows t < T
-  bf16* dHend;    // [NC, B*Hv, Dv, Dk]  dL/d(state at the end of chunk c), transposed
+  bf16* dHend;    // [NC, B*Hv, Dk, Dv]  dL/d(state at the end of chunk c)
   void *dq, *dk, *dv, *da, *db;
   float* dstate;     // [B,Hv,Dk,Dv]
   double* part_dA;   // [B,NC,Hv] per-chunk sums of dl * l
