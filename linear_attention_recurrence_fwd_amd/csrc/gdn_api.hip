@@ -29,11 +29,13 @@ Layout layout(const Dims& d, bool bwd, bool chunk) {
     return o;
   };
   const size_t bt = static_cast<size_t>(d.B) * d.T;
-  L.rq = take(bt * d.Hk);
-  L.rk = take(bt * d.Hk);
-  L.kq = take(bt * d.Hk);
-  L.ell = take(bt * d.Hv);
-  L.beta = take(bt * d.Hv);
+  if (!chunk) {  // the chunk form computes its per-step scalars in chunk_prep
+    L.rq = take(bt * d.Hk);
+    L.rk = take(bt * d.Hk);
+    L.kq = take(bt * d.Hk);
+    L.ell = take(bt * d.Hv);
+    L.beta = take(bt * d.Hv);
+  }
   if (bwd) {
     const size_t nc = d.nchunk();
     const size_t col = bt * d.Hv * d.Dv;
@@ -202,16 +204,16 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const gdn::StepScalars s = scalars(ws, L);
 
-  gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
-  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   if (chunk) {
     const gdn::ChunkBufs cb = chunk_bufs(ws, L, false);
-    gdn::ChunkPrepArgs ca{dd, q, k, s, cb, 0};
+    gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 0};
     if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
-    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, s, cb, o, state_out, ckpt};
+    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, ckpt};
     if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
     return GDN_OK;
   }
+  gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
+  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt};
   if (!launch(st, [&] { return gdn::launch_scan_fwd(fa, bf, st); })) return GDN_ERR_HIP;
   return GDN_OK;
@@ -237,15 +239,13 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const gdn::StepScalars s = scalars(ws, L);
 
-  gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
-  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   gdn::ParamReduceArgs ra{dd.B, dd.nchunk(), dd.Hv, at<double>(ws, L.pdA), at<double>(ws, L.pdt),
                           dA_log, ddt_bias};
   if (chunk) {
     const gdn::ChunkBufs cb = chunk_bufs(ws, L, true);
-    gdn::ChunkPrepArgs ca{dd, q, k, s, cb, 1};
+    gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 1};
     if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
-    gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, s, cb,
+    gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
                          at<gdn::bf16>(ws, L.E), at<gdn::bf16>(ws, L.dHend),
                          dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
@@ -253,6 +253,8 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     if (!launch(st, [&] { return gdn::launch_param_reduce(ra, st); })) return GDN_ERR_HIP;
     return GDN_OK;
   }
+  gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
+  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   gdn::ScanBwdArgs ba{dd, q, k, v, dO, state0, ckpt, dS_final, s,
                       at<float>(ws, L.U), at<float>(ws, L.E), dv, at<float>(ws, L.dHend), dstate};
   if (!launch(st, [&] { return gdn::launch_scan_bwd(ba, bf, st); })) return GDN_ERR_HIP;

@@ -514,7 +514,7 @@ struct ChunkBwdGrad {
     hs.eg = scc[SC_EG * L + t];
     hs.el = scc[SC_EL * L + t];
     hs.beta = scc[SC_BETA * L + t];
-    hs.ell = p.s.ell[(static_cast<size_t>(x.b) * d.T + x.t0 + min(t, x.tl)) * d.Hv + h];
+    hs.ell = scc[SC_ELL * L + t];
     hs.egl = scc[SC_EGL * L];
     const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
     const bf16* txr = p.cb.Tx + (static_cast<size_t>(bh) * x.NC + x.c) * L * L + ta * L + 8 * lg;
@@ -715,10 +715,10 @@ struct ChunkBwdGrad {
       x.i0 = 4 * (blk / (NS / 4));
       x.vv0 = 4 * (blk % (NS / 4));
     }
-    if (tid0 < L) {
-      const bool in = tid0 < Lc;
-      sm.rk[tid0] = in ? p.s.rk[qk0 + static_cast<size_t>(tid0) * d.Hk] : 0.f;
-      sm.rq[tid0] = in ? p.s.rq[qk0 + static_cast<size_t>(tid0) * d.Hk] : 0.f;
+    if (tid0 < L) {  // norm factors (the same for every value head of the group; 0 past the end)
+      const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + x.j * G) * NC + c) * SC_ROWS * L;
+      sm.rk[tid0] = scc[SC_RK * L + tid0];
+      sm.rq[tid0] = scc[SC_RQ * L + tid0];
     }
     for (int e = tid0; e < L * LP; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
     f32x4 accQ[IH], accK[IH];

@@ -35,7 +35,6 @@ namespace gdn {
 namespace {
 
 constexpr int L = kChunk;
-constexpr int LP = L + 1;
 constexpr int NT = 256;
 
 // ------------------------------------------------------------------ prep
@@ -58,7 +57,7 @@ struct ChunkPrep {
   };
   struct Smem {
     alignas(16) Big u;
-    float gam[L], rk[L], rq[L], beta[L];
+    float gam[L], rk[L], rq[L], beta[L], ell[L];
   };
 
   // st (fp32 [L][SP]) -> dst (bf16 [L][L]), 8 elements per store.
@@ -86,7 +85,7 @@ struct ChunkPrep {
 
     // ---- K K^T and Q K^T (raw rows, clamped into the sequence), shared by
     // the G value heads of the key head: wave w, row tile w
-    f32x4 akk[4], aqk[4];
+    f32x4 akk[4], aqk[4], aqq = f4zero();
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) akk[ct] = aqk[ct] = f4zero();
     {
@@ -97,6 +96,7 @@ struct ChunkPrep {
 #pragma unroll
       for (int kt = 0; kt < DK / 32; ++kt) {
         const bf16x8 ak = load_bf16x8(kc + oa + 32 * kt), aq = load_bf16x8(qc + oa + 32 * kt);
+        aqq = mfma16(aq, aq, aqq);  // Q Q^T on the diagonal tile: |q_t|^2
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const bf16x8 bk = load_bf16x8(kc + ob[ct] + 32 * kt);
@@ -105,18 +105,40 @@ struct ChunkPrep {
         }
       }
     }
-    if (tid < L) {
-      const bool in = tid < Lc;
-      sm.rk[tid] = in ? p.s.rk[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
-      sm.rq[tid] = in ? p.s.rq[qk0 + static_cast<size_t>(tid) * d.Hk] : 0.f;
-    }
-    // gates of the first head (wave 0, lane t); later heads' are loaded a head ahead
+    // norm factors from the Gram diagonals: (|x|^2 + eps)^-1/2, q also / sqrt(Dk)
+    // (the lane holding element (t, t) of tile (w, w) writes them)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (lr == 4 * lg + r) {
+        const int t = 16 * w + 4 * lg + r;
+        float kk = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (ct == w) kk = akk[ct][r];
+        const bool in = t < Lc;
+        sm.rk[t] = in ? 1.f / sqrtf(kk + kNormEps) : 0.f;
+        sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(aqq[r] + kNormEps) : 0.f;
+      }
+    // gates (wave 0, lane t): l = -e^{A_log} softplus(min(a + dt_bias, 20)),
+    // beta = sigmoid(b); a masked step gets l = 0, beta = 0
+    auto gates = [&](int h, float& ell, float& beta) {
+      ell = 0.f;
+      beta = 0.f;
+      const int t = min(l, tl);
+      const size_t o = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
+      const float av = to_f32(static_cast<const bf16*>(p.a)[o]), bv = to_f32(static_cast<const bf16*>(p.b)[o]);
+      const uint32_t mrow = static_cast<uint32_t>(b * d.T + t0 + t);
+      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
+                                  p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+      const bool valid = l < Lc && (p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, mrow, 0, 0) != 0);
+      if (valid) {
+        const float x = av + p.dt_bias[h];
+        ell = -expf(p.A_log[h]) * softplus_f(fminf(x, kClamp));
+        beta = sigmoid_f(bv);
+      }
+    };
     float ell_n = 0.f, beta_n = 0.f;
-    if (w == 0 && l < Lc) {
-      const size_t bt = static_cast<size_t>(b) * d.T + t0 + l;
-      ell_n = p.s.ell[bt * d.Hv + j * G];
-      beta_n = p.s.beta[bt * d.Hv + j * G];
-    }
+    if (w == 0) gates(j * G, ell_n, beta_n);
 
     for (int hh = 0; hh < G; ++hh) {
       const int h = j * G + hh, bh = b * d.Hv + h;
@@ -125,12 +147,9 @@ struct ChunkPrep {
       // ---- per-step scalars; gamma by a wave-wide inclusive scan
       if (w == 0) {
         float g = ell_n;
-        const float beta = beta_n;
-        if (hh + 1 < G && l < Lc) {
-          const size_t bt = static_cast<size_t>(b) * d.T + t0 + l;
-          ell_n = p.s.ell[bt * d.Hv + h + 1];
-          beta_n = p.s.beta[bt * d.Hv + h + 1];
-        }
+        const float ell = ell_n, beta = beta_n;
+        gates(min(h + 1, j * G + G - 1), ell_n, beta_n);  // next head's (the last reloads its own)
+        sm.ell[l] = ell;
 #pragma unroll
         for (int off = 1; off < L; off <<= 1) {
           const float y = __shfl_up(g, off);
@@ -154,6 +173,9 @@ struct ChunkPrep {
         sc[SC_GAM * L + t] = sm.gam[t];
         sc[SC_EG * L + t] = eg;
         sc[SC_EL * L + t] = el;
+        sc[SC_RK * L + t] = sm.rk[t];
+        sc[SC_RQ * L + t] = sm.rq[t];
+        sc[SC_ELL * L + t] = sm.ell[t];
       }
 
       // ---- N (permuted, fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward)

@@ -95,7 +95,10 @@ enum : int {
   SC_GAM = 6,    // g_t
   SC_EG = 7,     // e^{g_t}
   SC_EL = 8,     // e^{g_L - g_t}
-  SC_ROWS = 9
+  SC_RK = 9,     // rk_t  (k norm factor)
+  SC_RQ = 10,    // rq_t  (q norm factor, with 1/sqrt(Dk))
+  SC_ELL = 11,   // l_t   (log gate; 0 on masked steps)
+  SC_ROWS = 12
 };
 
 // Block index -> (b, h, slice).  Blocks of one (batch, key head) group go to
@@ -117,10 +120,13 @@ __device__ inline void block_coords(const Dims& d, int nslice, int& b, int& h, i
   slice = r % nslice;
 }
 
+// The chunk form computes its per-step scalars (norm factors, gates) in
+// chunk_prep itself; it does not use StepScalars.
 struct ChunkPrepArgs {
   Dims d;
-  const void *q, *k;
-  StepScalars s;
+  const void *q, *k, *a, *b;
+  const float *A_log, *dt_bias;
+  const uint8_t* mask;
   ChunkBufs cb;
   int bwd;  // also write the backward-only buffers
 };
@@ -129,7 +135,6 @@ struct ChunkFwdArgs {
   Dims d;
   const void *q, *k, *v;
   const float* state0;
-  StepScalars s;
   ChunkBufs cb;
   void* o;
   float* state_out;
@@ -145,7 +150,6 @@ struct ChunkBwdArgs {
   const float *A_log, *dt_bias;
   const uint8_t* mask;
   const float *state0, *ckpt, *dS_final;  // state0 / dS_final may be null
-  StepScalars s;
   ChunkBufs cb;
   bf16* E;        // [B,T,Hv,Dv]  eps, rows t < T
   bf16* dHend;    // [NC, B*Hv, Dk, Dv]  dL/d(state at the end of chunk c)
