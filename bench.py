@@ -159,21 +159,30 @@ def bench_train(args, torch, binding, inputs):
 
     kernels = KERNELS[family]
     nk = len(kernels)
-    ev = HipEvents(2 * nk * args.steps + 2)
     lib = binding.lib()
-    start, stop = 2 * nk * args.steps, 2 * nk * args.steps + 1
+    sp = ctypes.c_void_p(plan.stream.cuda_stream)
+    # headline: K steps bracketed by two events, no per-kernel events inside
+    ev = HipEvents(2)
     torch.cuda.synchronize()
-    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[start]), ctypes.c_void_p(plan.stream.cuda_stream))
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
     wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan.fwd()
+        plan.bwd()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.elapsed_ms(0, 1)
+    ev.close()
+    # per-kernel breakdown: the same K steps again, each kernel between events
+    ev = HipEvents(2 * nk * args.steps)
+    torch.cuda.synchronize()
     for s in range(args.steps):
         lib.gdn_set_kernel_events(ev.ptr(2 * nk * s), 2 * nk)
         plan.fwd()
         plan.bwd()
-    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[stop]), ctypes.c_void_p(plan.stream.cuda_stream))
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     lib.gdn_set_kernel_events(None, 0)
-    total_ms = ev.elapsed_ms(start, stop)
     per_kernel = {k: 0.0 for k in kernels}
     for s in range(args.steps):
         for i, k in enumerate(kernels):

@@ -489,20 +489,28 @@ hipError_t launch_t(const ChunkGradArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// dA_log[h] = sum over (b, chunk) of the per-chunk sums, ddt_bias likewise;
-// one thread per head, (b, chunk) ascending, in fp64.
-__global__ void param_reduce_kernel(ParamReduceArgs p) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= p.Hv) return;
+// dA_log[h] = sum over (b, chunk) of the per-chunk sums, ddt_bias likewise,
+// in fp64: one wave per head; lane l adds the entries l, l + 64, ... in that
+// order, then the 64 lane sums meet in a fixed butterfly, so the result does
+// not depend on timing.
+__global__ void __launch_bounds__(64) param_reduce_kernel(ParamReduceArgs p) {
+  const int h = blockIdx.x, l = threadIdx.x;
+  const int n = p.B * p.NC;
   double sa = 0.0, sd = 0.0;
-  for (int b = 0; b < p.B; ++b)
-    for (int c = 0; c < p.NC; ++c) {
-      const size_t i = (static_cast<size_t>(b) * p.NC + c) * p.Hv + h;
-      sa += p.part_dA[i];
-      sd += p.part_ddt[i];
-    }
-  p.dA_log[h] = static_cast<float>(sa);
-  p.ddt_bias[h] = static_cast<float>(sd);
+  for (int e = l; e < n; e += 64) {
+    const size_t i = static_cast<size_t>(e) * p.Hv + h;  // e = b * NC + c
+    sa += p.part_dA[i];
+    sd += p.part_ddt[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    sd += __shfl_xor(sd, off);
+  }
+  if (l == 0) {
+    p.dA_log[h] = static_cast<float>(sa);
+    p.ddt_bias[h] = static_cast<float>(sd);
+  }
 }
 
 }  // namespace
@@ -513,7 +521,7 @@ hipError_t launch_chunk_grad(const ChunkGradArgs& a, bool bf16, hipStream_t st) 
 }
 
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st) {
-  param_reduce_kernel<<<(a.Hv + 63) / 64, 64, 0, st>>>(a);
+  param_reduce_kernel<<<a.Hv, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
