@@ -110,24 +110,24 @@ class HipEvents:
 
 def cpu_baseline(T, seconds_hint=True):
     """The fp64 oracle on a bounded sample of the 9B workload: the same T and
-    per-head shape, 4 of the 16 key heads (16 of 64 value heads), fwd + bwd,
+    per-head shape, 8 of the 16 key heads (32 of 64 value heads), fwd + bwd,
     timed on the host; tokens/s scaled to all heads (work is linear in heads)."""
     import oracle
     from linear_attention_recurrence_fwd_amd import inputs
     threads = max(1, min(16, os.cpu_count() or 1))
-    c = inputs.make_case("9b_sample", 1, T, 4, 16, 192, 128, "bf16", 3, state_std=None,
+    c = inputs.make_case("9b_sample", 1, T, 8, 32, 192, 128, "bf16", 3, state_std=None,
                          dS_final=False)
     oracle.fwd(*c.oracle_args(), nthreads=threads)  # loads / warms the library
     t0 = time.perf_counter()
     oracle.fwd(*c.oracle_args(), nthreads=threads)
     oracle.bwd(*c.oracle_args(), c.vals["dO"], None, nthreads=threads)
     dt = time.perf_counter() - t0
-    scale = 64 / 16
+    scale = 64 / 32
     return {"value": round(c.B * T / (dt * scale), 3), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "fp64 oracle fwd+bwd (64-step checkpointed recompute), B=1 T=%d, "
-                      "Hk=4 Hv=16 Dk=192 Dv=128 (1/4 of the heads), %.2f s wall on %d threads; "
-                      "tokens/s scaled by 4" % (T, dt, threads)}
+                      "Hk=8 Hv=32 Dk=192 Dv=128 (1/2 of the heads), %.2f s wall on %d threads; "
+                      "tokens/s scaled by 2" % (T, dt, threads)}
 
 
 def bench_train(args, torch, binding, inputs):
@@ -310,6 +310,20 @@ def bench_decode(args, torch, binding, inputs):
     }
 
 
+def copy_probe(torch, mib):
+    """A plain device-to-device copy of `mib` MiB, three times: under
+    `rocprofv3 --pmc FETCH_SIZE` (or WRITE_SIZE) its per-dispatch reading is
+    the counter's value for a known number of bytes read (or written)."""
+    n = mib << 20
+    src = torch.empty((n,), dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("copy probe: %d bytes per copy, 3 copies" % n, file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +332,9 @@ def main():
     ap.add_argument("--config", default="9b_t2048", choices=["9b_t2048", "9b_t256", "decode"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB device to device 3 times "
+                         "(the known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -336,6 +353,8 @@ def main():
         out = bench_train(args, torch, binding, inputs)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(out["config"]["T"])
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
     print(json.dumps(out), flush=True)
 
 

@@ -14,12 +14,14 @@
 // only as e^{g_t - g_s} with s <= t, never as e^{-g}.
 //
 // Kernels:
-//   chunk_prep  one workgroup per (chunk, batch, key head): K K^T and Q K^T on
-//               MFMA once, then for each value head of the group N, Tx by
-//               forward substitution (fp32), Mq and the per-step chunk
-//               scalars; K^T of the chunk.  With `bwd` set it writes the
-//               transposes the backward needs instead of Mq, and Q^T.  All
-//               outputs go to the workspace (bf16 / fp32), 16 bytes per store.
+//   chunk_prep  one workgroup per (chunk, batch, value head): the chunk's k and
+//               q rows staged in LDS by coalesced loads, K K^T and Q K^T on
+//               MFMA, the gates and gamma by a wave scan, N, Tx by forward
+//               substitution (fp32), Mq and the per-step chunk scalars; the
+//               first value head of each key head also writes K^T.  With
+//               `bwd` set it writes the transposes the backward needs instead
+//               of Mq, and Q^T.  All outputs go to the workspace (bf16 /
+//               fp32), 16 bytes per store.
 //   chunk_fwd   one workgroup per (batch, value head, 32-column slice of Dv),
 //               walking the chunks in order with H in MFMA accumulators (fp32),
 //               the next chunk's operands prefetched into registers while the
@@ -41,19 +43,21 @@ constexpr int NT = 256;
 
 template <int DK>
 struct ChunkPrep {
-  static constexpr int SP = L + 4;  // fp32 row stride of the staging matrix (16-byte aligned rows)
+  static constexpr int RS = DK + 8;  // bf16 row stride of the staged k / q rows (conflict-free operand reads)
+  static constexpr int SP = L + 4;   // fp32 row stride of the staging matrix (16-byte aligned rows)
+  static constexpr int NLD = L * DK / 8 / NT;  // 16-byte pieces of one of k, q per thread
+  static_assert(L * DK / 8 % NT == 0, "whole pieces per thread");
+  struct Rows {
+    bf16 k[L * RS];
+    bf16 q[L * RS];
+  };
   struct Mats {
     float np[L * L];   // N, row t holding N[t][4m + q] at q L/4 + m
     float st[L * SP];  // staging of the matrices written out
   };
-  // The k / q column block of this workgroup's share of the transposes.
-  static constexpr int TW = DK + 8;
-  struct Tile {
-    bf16 t[L * TW];
-  };
   union Big {
+    Rows r;
     Mats m;
-    Tile k;
   };
   struct Smem {
     alignas(16) Big u;
@@ -71,38 +75,98 @@ struct ChunkPrep {
     }
   }
 
+  // Rows [t][i] of the staged chunk -> dst [i][t] (bf16, L steps per row).
+  __device__ static void store_transposed(const bf16* rows, bf16* dst, int tid) {
+    for (int u = tid; u < DK * L / 8; u += NT) {
+      const int i = u % DK, t8 = 8 * (u / DK);
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        wv[e] = static_cast<uint32_t>(rows[(t8 + 2 * e) * RS + i].x) |
+                (static_cast<uint32_t>(rows[(t8 + 2 * e + 1) * RS + i].x) << 16);
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(i) * L + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+  }
+
+  // One workgroup per (chunk, batch, value head).  The G workgroups of a key
+  // head recompute its K K^T and Q K^T (cheap on the matrix cores; the k / q
+  // rows come from L2) and the first of them writes K^T (and Q^T).
   __device__ static void run(const ChunkPrepArgs& p, Smem& sm) {
     const Dims& d = p.d;
-    const int c = blockIdx.x, bj = blockIdx.y;
+    const int c = blockIdx.x, bh = blockIdx.y;
     const int G = d.G(), NC = d.nchunk();
-    const int b = bj / d.Hk, j = bj % d.Hk;
+    const int b = bh / d.Hv, h = bh % d.Hv, j = h / G;
+    const bool first = h % G == 0;
     const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
     const size_t qk0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;
     const uint32_t qk_row = d.Hk * DK;
     const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
     const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
+    const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
 
-    // ---- K K^T and Q K^T (raw rows, clamped into the sequence), shared by
-    // the G value heads of the key head: wave w, row tile w
+    // ---- k / q rows of the chunk (clamped into the sequence), coalesced
+    // 16-byte loads, all issued before any is used; the gate inputs of step
+    // t = l (wave 0)
+    uint4 kv[NLD], qv[NLD];
+#pragma unroll
+    for (int e = 0; e < NLD; ++e) {
+      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
+      const uint32_t o = static_cast<uint32_t>(min(t, tl)) * qk_row + i8;
+      kv[e] = *reinterpret_cast<const uint4*>(kc + o);
+      qv[e] = *reinterpret_cast<const uint4*>(qc + o);
+    }
+    float ell = 0.f, beta = 0.f;
+    if (w == 0) {
+      // l = -e^{A_log} softplus(min(a + dt_bias, 20)), beta = sigmoid(b);
+      // a masked step (or a row past the end) gets l = 0, beta = 0
+      const int t = min(l, tl);
+      const size_t o = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
+      const float av = to_f32(static_cast<const bf16*>(p.a)[o]), bv = to_f32(static_cast<const bf16*>(p.b)[o]);
+      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
+                                  p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+      const uint32_t mrow = static_cast<uint32_t>(b * d.T + t0 + t);
+      const bool valid = l < Lc && (p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, mrow, 0, 0) != 0);
+      const float x = av + p.dt_bias[h], alog = p.A_log[h];
+      if (valid) {
+        ell = -expf(alog) * softplus_f(fminf(x, kClamp));
+        beta = sigmoid_f(bv);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NLD; ++e) {
+      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
+      *reinterpret_cast<uint4*>(&sm.u.r.k[t * RS + i8]) = kv[e];
+      *reinterpret_cast<uint4*>(&sm.u.r.q[t * RS + i8]) = qv[e];
+    }
+    if (w == 0) {  // gamma by a wave-wide inclusive scan
+      float g = ell;
+#pragma unroll
+      for (int off = 1; off < L; off <<= 1) {
+        const float y = __shfl_up(g, off);
+        if (l >= off) g += y;
+      }
+      sm.gam[l] = g;
+      sm.ell[l] = ell;
+      sm.beta[l] = beta;
+    }
+    __syncthreads();
+
+    // ---- K K^T and Q K^T (raw rows), wave w = row tile w; Q Q^T on the
+    // diagonal tile gives |q_t|^2
     f32x4 akk[4], aqk[4], aqq = f4zero();
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) akk[ct] = aqk[ct] = f4zero();
-    {
-      const uint32_t oa = static_cast<uint32_t>(min(16 * w + lr, tl)) * qk_row + 8 * lg;
-      uint32_t ob[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) ob[ct] = static_cast<uint32_t>(min(16 * ct + lr, tl)) * qk_row + 8 * lg;
+    for (int kt = 0; kt < DK / 32; ++kt) {
+      const int oa = (16 * w + lr) * RS + 32 * kt + 8 * lg;
+      const bf16x8 ak = load_bf16x8(&sm.u.r.k[oa]), aq = load_bf16x8(&sm.u.r.q[oa]);
+      aqq = mfma16(aq, aq, aqq);
 #pragma unroll
-      for (int kt = 0; kt < DK / 32; ++kt) {
-        const bf16x8 ak = load_bf16x8(kc + oa + 32 * kt), aq = load_bf16x8(qc + oa + 32 * kt);
-        aqq = mfma16(aq, aq, aqq);  // Q Q^T on the diagonal tile: |q_t|^2
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const bf16x8 bk = load_bf16x8(kc + ob[ct] + 32 * kt);
-          akk[ct] = mfma16(ak, bk, akk[ct]);
-          aqk[ct] = mfma16(aq, bk, aqk[ct]);
-        }
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16x8 bk = load_bf16x8(&sm.u.r.k[(16 * ct + lr) * RS + 32 * kt + 8 * lg]);
+        akk[ct] = mfma16(ak, bk, akk[ct]);
+        aqk[ct] = mfma16(aq, bk, aqk[ct]);
       }
     }
     // norm factors from the Gram diagonals: (|x|^2 + eps)^-1/2, q also / sqrt(Dk)
@@ -119,166 +183,110 @@ struct ChunkPrep {
         sm.rk[t] = in ? 1.f / sqrtf(kk + kNormEps) : 0.f;
         sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(aqq[r] + kNormEps) : 0.f;
       }
-    // gates (wave 0, lane t): l = -e^{A_log} softplus(min(a + dt_bias, 20)),
-    // beta = sigmoid(b); a masked step gets l = 0, beta = 0
-    auto gates = [&](int h, float& ell, float& beta) {
-      ell = 0.f;
-      beta = 0.f;
-      const int t = min(l, tl);
-      const size_t o = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
-      const float av = to_f32(static_cast<const bf16*>(p.a)[o]), bv = to_f32(static_cast<const bf16*>(p.b)[o]);
-      const uint32_t mrow = static_cast<uint32_t>(b * d.T + t0 + t);
-      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
-                                  p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-      const bool valid = l < Lc && (p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, mrow, 0, 0) != 0);
-      if (valid) {
-        const float x = av + p.dt_bias[h];
-        ell = -expf(p.A_log[h]) * softplus_f(fminf(x, kClamp));
-        beta = sigmoid_f(bv);
-      }
-    };
-    float ell_n = 0.f, beta_n = 0.f;
-    if (w == 0) gates(j * G, ell_n, beta_n);
+    // ---- raw k (and q) of the chunk, transposed, written once per key head
+    if (first) {
+      const size_t base = (static_cast<size_t>(b * d.Hk + j) * NC + c) * DK * L;
+      store_transposed(sm.u.r.k, p.cb.KT + base, tid);
+      if (p.bwd) store_transposed(sm.u.r.q, p.cb.QT + base, tid);
+    }
+    __syncthreads();  // the staged rows are dead from here on; rk, rq visible
 
-    for (int hh = 0; hh < G; ++hh) {
-      const int h = j * G + hh, bh = b * d.Hv + h;
-      const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
-      __syncthreads();  // the previous head is done with the shared arrays
-      // ---- per-step scalars; gamma by a wave-wide inclusive scan
-      if (w == 0) {
-        float g = ell_n;
-        const float ell = ell_n, beta = beta_n;
-        gates(min(h + 1, j * G + G - 1), ell_n, beta_n);  // next head's (the last reloads its own)
-        sm.ell[l] = ell;
+    // ---- per-step chunk scalars
+    if (tid < L) {
+      const int t = tid;
+      const float gl = sm.gam[Lc - 1];
+      const float eg = expf(sm.gam[t]), el = expf(gl - sm.gam[t]);
+      float* sc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
+      sc[SC_CR * L + t] = eg * sm.rk[t];
+      sc[SC_CO * L + t] = eg * sm.rq[t];
+      sc[SC_W * L + t] = sm.beta[t] * el * sm.rk[t];
+      sc[SC_KL * L + t] = el * sm.rk[t];
+      sc[SC_BETA * L + t] = sm.beta[t];
+      sc[SC_EGL * L + t] = t == 0 ? expf(gl) : 0.f;
+      sc[SC_GAM * L + t] = sm.gam[t];
+      sc[SC_EG * L + t] = eg;
+      sc[SC_EL * L + t] = el;
+      sc[SC_RK * L + t] = sm.rk[t];
+      sc[SC_RQ * L + t] = sm.rq[t];
+      sc[SC_ELL * L + t] = sm.ell[t];
+    }
+
+    // ---- N (permuted, fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward)
+    float mq[4][4];
 #pragma unroll
-        for (int off = 1; off < L; off <<= 1) {
-          const float y = __shfl_up(g, off);
-          if (l >= off) g += y;
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * lg + r, s = 16 * ct + lr;
+        float nv = 0.f, pq = 0.f, at = 0.f;
+        if (s <= t) {
+          const float dec = expf(sm.gam[t] - sm.gam[s]);
+          if (s < t) {
+            at = dec * sm.rk[t] * sm.rk[s] * akk[ct][r];
+            nv = at * sm.beta[s];
+          }
+          pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
         }
-        sm.gam[l] = g;
-        sm.beta[l] = beta;
+        sm.u.m.np[t * L + (s & 3) * (L / 4) + (s >> 2)] = nv;
+        if (p.bwd) {
+          sm.u.m.st[s * SP + t] = at;  // A^T
+          mq[ct][r] = pq;
+        } else {
+          sm.u.m.st[t * SP + s] = pq * sm.beta[s];  // Mq
+        }
       }
+    __syncthreads();
+    if (p.bwd) {
+      store_mat(sm, p.cb.AtT + mat, tid);
       __syncthreads();
-      if (tid < L) {
-        const int t = tid;
-        const float gl = sm.gam[Lc - 1];
-        const float eg = expf(sm.gam[t]), el = expf(gl - sm.gam[t]);
-        float* sc = p.cb.sc + (static_cast<size_t>(bh) * NC + c) * SC_ROWS * L;
-        sc[SC_CR * L + t] = eg * sm.rk[t];
-        sc[SC_CO * L + t] = eg * sm.rq[t];
-        sc[SC_W * L + t] = sm.beta[t] * el * sm.rk[t];
-        sc[SC_KL * L + t] = el * sm.rk[t];
-        sc[SC_BETA * L + t] = sm.beta[t];
-        sc[SC_EGL * L + t] = t == 0 ? expf(gl) : 0.f;
-        sc[SC_GAM * L + t] = sm.gam[t];
-        sc[SC_EG * L + t] = eg;
-        sc[SC_EL * L + t] = el;
-        sc[SC_RK * L + t] = sm.rk[t];
-        sc[SC_RQ * L + t] = sm.rq[t];
-        sc[SC_ELL * L + t] = sm.ell[t];
-      }
-
-      // ---- N (permuted, fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward)
-      float mq[4][4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * w + 4 * lg + r, s = 16 * ct + lr;
-          float nv = 0.f, pq = 0.f, at = 0.f;
-          if (s <= t) {
-            const float dec = expf(sm.gam[t] - sm.gam[s]);
-            if (s < t) {
-              at = dec * sm.rk[t] * sm.rk[s] * akk[ct][r];
-              nv = at * sm.beta[s];
-            }
-            pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
-          }
-          sm.u.m.np[t * L + (s & 3) * (L / 4) + (s >> 2)] = nv;
-          if (p.bwd) {
-            sm.u.m.st[s * SP + t] = at;  // A^T
-            mq[ct][r] = pq;
-          } else {
-            sm.u.m.st[t * SP + s] = pq * sm.beta[s];  // Mq
-          }
-        }
+        for (int r = 0; r < 4; ++r) sm.u.m.st[(16 * ct + lr) * SP + 16 * w + 4 * lg + r] = mq[ct][r];  // P^T
       __syncthreads();
-      if (p.bwd) {
-        store_mat(sm, p.cb.AtT + mat, tid);
-        __syncthreads();
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.u.m.st[(16 * ct + lr) * SP + 16 * w + 4 * lg + r] = mq[ct][r];  // P^T
-        __syncthreads();
-        store_mat(sm, p.cb.PqT + mat, tid);
-      } else {
-        store_mat(sm, p.cb.Mq + mat, tid);
-      }
-
-      // ---- Tx = (I + N)^-1 by forward substitution in fp32: column `col`,
-      // four threads per column, thread q holding the entries at rows 4m + q.
-      // Only rows above step t enter step t, so step t reads ceil(t/4) entries.
-      {
-        const int col = tid >> 2, q = tid & 3;
-        float x[L / 4];
-#pragma unroll
-        for (int m = 0; m < L / 4; ++m) x[m] = 0.f;
-        const float* nrow = &sm.u.m.np[q * (L / 4)];
-#pragma unroll
-        for (int t = 0; t < L; ++t) {
-          const int nm = (t + 3) / 4;  // entries m with 4m + q < t possible
-          float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-          for (int m4 = 0; m4 < nm; m4 += 4) {
-            const float4 nv = *reinterpret_cast<const float4*>(nrow + t * L + m4);
-            p0 = fmaf(nv.x, x[m4], p0);
-            if (m4 + 1 < nm) p1 = fmaf(nv.y, x[m4 + 1], p1);
-            if (m4 + 2 < nm) p0 = fmaf(nv.z, x[m4 + 2], p0);
-            if (m4 + 3 < nm) p1 = fmaf(nv.w, x[m4 + 3], p1);
-          }
-          const float xt = (t == col ? 1.f : 0.f) - quad_sum(p0 + p1);
-          if ((t & 3) == q) x[t >> 2] = xt;
-        }
-        __syncthreads();  // the staging matrix is free (P^T / Mq stored) and N is read
-#pragma unroll
-        for (int m = 0; m < L / 4; ++m) sm.u.m.st[(4 * m + q) * SP + col] = x[m];
-      }
-      __syncthreads();
-      store_mat(sm, p.cb.Tx + mat, tid);
-      if (p.bwd) {  // Tx^T: row r is column r of the staged Tx
-        for (int u = tid; u < L * L / 8; u += NT) {
-          const int r = u >> 3, c8 = 8 * (u & 7);
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = sm.u.m.st[(c8 + e) * SP + r];
-          *reinterpret_cast<uint4*>(p.cb.TxT + mat + r * L + c8) =
-              make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
-        }
-      }
+      store_mat(sm, p.cb.PqT + mat, tid);
+    } else {
+      store_mat(sm, p.cb.Mq + mat, tid);
     }
 
-    // ---- raw k (and q) of the chunk, transposed
-    const size_t base = (static_cast<size_t>(bj) * NC + c) * DK * L;
-    for (int pass = 0; pass < (p.bwd ? 2 : 1); ++pass) {
-      const bf16* src = pass == 0 ? kc : qc;
-      bf16* dst = (pass == 0 ? p.cb.KT : p.cb.QT) + base;
-      __syncthreads();
-      for (int u = tid; u < L * DK / 8; u += NT) {
-        const int t = u / (DK / 8), e0 = 8 * (u % (DK / 8));
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (t < Lc) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(t) * qk_row + e0);
-        *reinterpret_cast<uint4*>(&sm.u.k.t[t * TW + e0]) = v;
-      }
-      __syncthreads();
-      for (int u = tid; u < DK * L / 8; u += NT) {
-        const int i = u % DK, t8 = 8 * (u / DK);
-        uint32_t wv[4];
+    // ---- Tx = (I + N)^-1 by forward substitution in fp32: column `col`,
+    // four threads per column, thread q holding the entries at rows 4m + q.
+    // Only rows above step t enter step t, so step t reads ceil(t/4) entries.
+    {
+      const int col = tid >> 2, q = tid & 3;
+      float x[L / 4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          wv[e] = static_cast<uint32_t>(sm.u.k.t[(t8 + 2 * e) * TW + i].x) |
-                  (static_cast<uint32_t>(sm.u.k.t[(t8 + 2 * e + 1) * TW + i].x) << 16);
-        *reinterpret_cast<uint4*>(dst + static_cast<size_t>(i) * L + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      for (int m = 0; m < L / 4; ++m) x[m] = 0.f;
+      const float* nrow = &sm.u.m.np[q * (L / 4)];
+#pragma unroll
+      for (int t = 0; t < L; ++t) {
+        const int nm = (t + 3) / 4;  // entries m with 4m + q < t possible
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int m4 = 0; m4 < nm; m4 += 4) {
+          const float4 nv = *reinterpret_cast<const float4*>(nrow + t * L + m4);
+          p0 = fmaf(nv.x, x[m4], p0);
+          if (m4 + 1 < nm) p1 = fmaf(nv.y, x[m4 + 1], p1);
+          if (m4 + 2 < nm) p0 = fmaf(nv.z, x[m4 + 2], p0);
+          if (m4 + 3 < nm) p1 = fmaf(nv.w, x[m4 + 3], p1);
+        }
+        const float xt = (t == col ? 1.f : 0.f) - quad_sum(p0 + p1);
+        if ((t & 3) == q) x[t >> 2] = xt;
+      }
+      __syncthreads();  // the staging matrix is free (P^T / Mq stored) and N is read
+#pragma unroll
+      for (int m = 0; m < L / 4; ++m) sm.u.m.st[(4 * m + q) * SP + col] = x[m];
+    }
+    __syncthreads();
+    store_mat(sm, p.cb.Tx + mat, tid);
+    if (p.bwd) {  // Tx^T: row r is column r of the staged Tx
+      for (int u = tid; u < L * L / 8; u += NT) {
+        const int r = u >> 3, c8 = 8 * (u & 7);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = sm.u.m.st[(c8 + e) * SP + r];
+        *reinterpret_cast<uint4*>(p.cb.TxT + mat + r * L + c8) =
+            make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
       }
     }
   }
@@ -661,7 +669,7 @@ __global__ void __launch_bounds__(768) chunk_fwd_kernel(ChunkFwdArgs p) {
 
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st) {
   if (a.d.T == 0) return hipSuccess;
-  dim3 grid(a.d.nchunk(), a.d.B * a.d.Hk);
+  dim3 grid(a.d.nchunk(), a.d.B * a.d.Hv);
   switch (a.d.Dk) {
     case 64: chunk_prep_kernel<64><<<grid, NT, 0, st>>>(a); break;
     case 128: chunk_prep_kernel<128><<<grid, NT, 0, st>>>(a); break;

@@ -166,15 +166,35 @@ __device__ __forceinline__ bf16x8 to_mfma_layout(const bf16x8& v) {
   return __builtin_bit_cast(bf16x8, o);
 }
 
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces addressed by lanes
+// i / 4 + 4 e of its group, as element e (e = 0..3).  Used on a row-major tile
+// with lane s of a group addressing row r0 + s / 4, columns c0 + 4 (s % 4)
+// .. + 3, lane s gets rows r0 .. r0 + 3 of column c0 + s: four rows of one
+// column, the layout of an MFMA accumulator or of a transposed operand.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // Buffer loads: a wave-uniform resource descriptor (base, byte size) in
 // scalar registers plus a 32-bit byte offset per lane.  Reads at or past the
 // size return zeros.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+// Every descriptor here is built from wave-uniform values; reading them
+// through readfirstlane states that to the compiler, which otherwise may not
+// prove it and wraps each buffer access in a loop over distinct descriptors.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
   const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(n), 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* pu = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(n)), 0x00020000);
 }
 __device__ __forceinline__ bf16x8 buf_bf16x8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -187,6 +207,19 @@ __device__ __forceinline__ float4 buf_f4(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ float buf_f1(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Buffer stores: a store at or past the descriptor's size is dropped.  Used
+// where a store would otherwise sit under a branch: after a branch that
+// issued stores on one path only, the compiler's wait for an earlier load
+// must also wait for those stores, which voids the prefetch.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+__device__ __forceinline__ void buf_store_u4(rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_u2(rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 0);
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
