@@ -183,11 +183,12 @@ struct ChunkPrep {
         sm.rk[t] = in ? 1.f / sqrtf(kk + kNormEps) : 0.f;
         sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(aqq[r] + kNormEps) : 0.f;
       }
-    // ---- raw k (and q) of the chunk, transposed, written once per key head
-    if (first) {
+    // ---- raw k and q of the chunk, transposed, for the backward (written
+    // once per key head)
+    if (first && p.bwd) {
       const size_t base = (static_cast<size_t>(b * d.Hk + j) * NC + c) * DK * L;
       store_transposed(sm.u.r.k, p.cb.KT + base, tid);
-      if (p.bwd) store_transposed(sm.u.r.q, p.cb.QT + base, tid);
+      store_transposed(sm.u.r.q, p.cb.QT + base, tid);
     }
     __syncthreads();  // the staged rows are dead from here on; rk, rq visible
 
@@ -303,87 +304,122 @@ __global__ void __launch_bounds__(NT) chunk_prep_kernel(ChunkPrepArgs p) {
 template <int DK>
 struct ChunkFwd {
   // Twelve waves in three groups of four (w = wave index within the group):
-  //   A (waves 0-3):  K H, R and X = Tx R for row tile w;
+  //   A (waves 0-3):  K H, R and X = Tx R for row tile w.  A also streams the
+  //                   chunk's k rows, Tx, v slice and chunk scalars into a
+  //                   ring of LDS slots with direct-to-LDS buffer loads, PD
+  //                   chunks ahead, so these operands never pass through
+  //                   registers;
   //   B (waves 4-7):  the state update H <- e^{gL} H + K^T diag(w) X for its
-  //                   row tiles of H, and the checkpoints;
+  //                   row tiles of H (K^T read transposed from the ring), and
+  //                   the checkpoints;
   //   C (waves 8-11): Q H and the output O = diag(e^g rq) Q H + Mq X for row
-  //                   tile w.
-  // B and C work at the same time once X is in LDS; each group keeps its own
-  // operands in registers, prefetched two chunks ahead.
+  //                   tile w (q and Mq prefetched two chunks ahead in
+  //                   registers).
+  // B and C work at the same time once X is in LDS.
   static constexpr int NTS = 768;
-  static constexpr int NV = 32;             // Dv columns per workgroup
-  static constexpr int RTW = DK / 64;       // H row tiles per group-B wave
-  static constexpr int HS = DK + 8;         // bf16 row stride of H^T
-  static constexpr int XS = L + 8;          // bf16 row stride of R^T / X^T
+  static constexpr int NV = 32;                   // Dv columns per workgroup
+  static constexpr int RTW = DK / 64;             // H row tiles per group-B wave
+  static constexpr int HS = DK + 8;               // bf16 row stride of H^T
+  static constexpr int XS = L + 8;                // bf16 row stride of R^T / X^T
+  static constexpr int NPK = DK / 8;              // 16-byte pieces of a k row
+  static constexpr int NSL = DK <= 192 ? 3 : 2;   // ring slots
+  static constexpr int PD = NSL - 1;              // chunks loaded ahead
+  static constexpr int KDMA = DK / 32;            // k loads per group-A wave per chunk
+  static constexpr int NDMA = KDMA + 2 + 1 + 1;   // ring loads per group-A wave per chunk
+  // A ring slot.  Lane i of a direct-to-LDS load writes its 16 (or 4) bytes at
+  // the load's base + 16 i (4 i), so the layouts are set through the global
+  // addresses: 16-byte piece p of row t sits at t * (pieces per row) +
+  // (p ^ swizzle(t)), which keeps the operand reads free of bank conflicts.
+  struct Slot {
+    bf16 k[L * DK];   // k rows [t][i], swizzle t & 7
+    bf16 tx[L * L];   // Tx rows, swizzle t & 7
+    bf16 v[L * NV];   // v rows of this slice's columns, swizzle t & 3
+    float sc[4 * L];  // chunk scalar rows 0 .. 3 (SC_CR, SC_CO, SC_W, SC_EGL)
+  };
+  static_assert(SC_CR < 4 && SC_CO < 4 && SC_W < 4 && SC_EGL < 4, "rows held in a ring slot");
   struct Smem {
+    alignas(16) Slot ring[NSL];
     alignas(16) bf16 hb[NV * HS];   // H^T (bf16), the B operand of K H and Q H
     alignas(16) bf16 rb[NV * XS];   // R^T
     alignas(16) bf16 xb[NV * XS];   // X^T
     alignas(16) bf16 xw[NV * XS];   // (diag(w) X)^T
   };
-  // The operands of one chunk, held in registers (prefetched one chunk ahead).
-  // Every load is unconditional, from an address clamped into the sequence, so
-  // no load sits in a branch (a load in a branch makes the compiler wait for
-  // all outstanding loads, prefetch included).  Rows past the end of the
-  // sequence hold copies of its last row and need no zeroing: their chunk
-  // scalars (rk, w) are zero, Tx and Mq are lower triangular and their outputs
-  // are not stored, so they never reach a stored value (inputs are finite).
-  struct StageA {
-    bf16x8 ka[DK / 32];               // k rows t = 16 w + lr
-    bf16x8 txa[2];                    // Tx rows t = 16 w + lr
-    unsigned short vv[2][4];          // v at rows t = 16 w + 4 lg + r, cols 16 ct + lr
-    float4 cr;                        // e^{g_t} rk_t at rows 16 w + 4 lg + r
-    float4 wv;                        // w at rows 16 w + 4 lg + r
-  };
-  struct StageB {
-    bf16x8 kta[RTW][2];               // K^T rows i = 16 (w RTW + it) + lr
-    float egl;
-  };
+  // Group C's operands of one chunk, held in registers.  Every load is
+  // unconditional, from an address clamped into the sequence, so no load sits
+  // in a branch (a load in a branch makes the compiler wait for all
+  // outstanding loads, prefetch included).  Rows past the end of the sequence
+  // hold copies of its last row and need no zeroing: their chunk scalars (rk,
+  // rq, w) are zero, Tx and Mq are lower triangular and their outputs are not
+  // stored, so they never reach a stored value (inputs are finite).
   struct StageC {
     bf16x8 qa[DK / 32];               // q rows t = 16 w + lr
     bf16x8 mqa[2];                    // Mq rows t = 16 w + lr
-    float co;                         // e^{g_t} rq_t at t = 16 w + lr
   };
   // Per-workgroup values (uniform) and per-lane coordinates (w = wave index
-  // within the group).  Addresses are a uniform 64-bit base plus a 32-bit
-  // lane offset.
+  // within the group, uniform).  Addresses are a uniform descriptor plus a
+  // 32-bit lane offset.
   struct Lane {
     int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
     uint32_t qk_row, v_row;   // element strides of one step in q/k and v/o
-    rsrc_t rk, rq, rv, rtx, rmq, rkt, rsc;  // buffer descriptors of the operands
+    rsrc_t rq, rmq;              // buffer descriptors of group C's operands
+    i32x4 dk, dv, dtx, dsc;      // raw descriptors of the ring's operands
   };
 
-  // Operand loads are buffer loads at byte offsets from the tensor's base.
-  __device__ static void load_a(const ChunkFwdArgs& p, const Lane& q, int c, StageA& s) {
-    const Dims& d = p.d;
-    const int t0 = c * L, tl = q.last - t0;
-    const int cr_ = 16 * q.w + coal_row(q.l), cp_ = coal_piece(q.l);  // quad-coalesced (see to_mfma_layout)
-    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
-#pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = buf_bf16x8(q.rk, ko + 64 * kt);
-    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) s.txa[kt] = buf_bf16x8(q.rtx, mo + 64 * kt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t vo = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.tc0 + r, tl)) * d.Hv + q.h) * d.Dv + q.col0 + q.lr);
-      s.vv[0][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rv, vo, 0, 0));
-      s.vv[1][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rv, vo + 32, 0, 0));
-    }
-    const uint32_t so = 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L);
-    s.cr = buf_f4(q.rsc, so + 4 * (SC_CR * L + q.tc0));
-    s.wv = buf_f4(q.rsc, so + 4 * (SC_W * L + q.tc0));
+  // element offsets of 16-byte piece p of row t in the ring tiles
+  __device__ static __forceinline__ int kpos(int t, int p) { return 8 * (t * NPK + (p ^ (t & 7))); }
+  __device__ static __forceinline__ int xpos(int t, int p) { return 8 * (t * 8 + (p ^ (t & 7))); }
+  __device__ static __forceinline__ int vpos(int t, int p) { return 8 * (t * 4 + (p ^ (t & 3))); }
+
+  // Direct-to-LDS buffer loads, issued through inline assembly: the compiler
+  // does not see them, so it does not make every later LDS read wait for
+  // them; the waits are explicit (wait_vm before barrier 3).  M0 holds the
+  // wave's LDS base; the s_nop is the wait state required between an M0
+  // write and a load to LDS.
+  __device__ static __forceinline__ uint32_t lds_addr(const void* p) {
+    typedef __attribute__((address_space(3))) const void lds_cvoid;
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)p)));
+  }
+  __device__ static __forceinline__ void dma16(const i32x4& r, const void* lds, uint32_t off) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
+  }
+  __device__ static __forceinline__ void dma4(const i32x4& r, const void* lds, uint32_t off) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
+  }
+  // raw buffer descriptor words (as make_rsrc) for the inline loads
+  __device__ static __forceinline__ i32x4 desc(const void* p, size_t bytes) {
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return i32x4{static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
+                 static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu)),
+                 static_cast<int>(__builtin_amdgcn_readfirstlane(n)), 0x00020000};
+  }
+  // Wait until at most N of this wave's vector memory operations are pending.
+  template <int N> __device__ static __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
   }
 
-  __device__ static void load_b(const ChunkFwdArgs& p, const Lane& q, int c, StageB& s) {
-    (void)p;
-    const uint32_t kto = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + coal_row(q.l)) * L +
-                              8 * coal_piece(q.l));
+  // Group A: the NDMA ring loads of this wave for chunk c into slot sl.  Load
+  // n of a tile covers its 16-byte positions 64 n .. 64 n + 63.
+  __device__ static void issue_ring(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c, int sl) {
+    const Dims& d = p.d;
+    const int t0 = c * L, tl = q.last - t0, l = q.l;
+    Slot& s = sm.ring[sl];
 #pragma unroll
-    for (int it = 0; it < RTW; ++it)
+    for (int jj = 0; jj < KDMA; ++jj) {
+      const int n = KDMA * q.w + jj, pos = 64 * n + l, t = pos / NPK, pc = (pos % NPK) ^ (t & 7);
+      dma16(q.dk, &s.k[512 * n], 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hk + q.j) * DK + 8 * pc));
+    }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s.kta[it][kt] = buf_bf16x8(q.rkt, kto + 2 * (it * 16 * L) + 64 * kt);
-    s.egl = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_EGL * L));
+    for (int jj = 0; jj < 2; ++jj) {
+      const int n = 2 * q.w + jj, pos = 64 * n + l, t = pos / 8, pc = (pos % 8) ^ (t & 7);
+      dma16(q.dtx, &s.tx[512 * n], 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + t * L + 8 * pc));
+    }
+    {
+      const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
+      dma16(q.dv, &s.v[512 * q.w],
+            2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hv + q.h) * d.Dv + q.col0 + 8 * pc));
+    }
+    dma4(q.dsc, &s.sc[L * q.w], 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + L * q.w + l));
   }
 
   __device__ static void load_c(const ChunkFwdArgs& p, const Lane& q, int c, StageC& s) {
@@ -396,7 +432,6 @@ struct ChunkFwd {
     const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s.mqa[kt] = buf_bf16x8(q.rmq, mo + 64 * kt);
-    s.co = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_CO * L + q.ta));
   }
 
   __device__ static void put_h(Smem& sm, const Lane& q, const f32x4 (&H)[RTW][2]) {
@@ -408,27 +443,41 @@ struct ChunkFwd {
             pack4_bf16(H[it][ct][0], H[it][ct][1], H[it][ct][2], H[it][ct][3]);
   }
 
-  // Group A, one chunk: K H -> R -> X.
-  __device__ static void step_a(const Smem& smc, Smem& sm, const Lane& q, StageA& cur) {
+  // Group A, one chunk: issue the ring loads of chunk c + PD, then K H -> R ->
+  // X from slot c.  Before barrier 3 each wave waits for its loads of chunk
+  // c + 1 (the loads of PD - 1 later chunks may stay in flight); barrier 3
+  // then makes slot c + 1 complete for every wave.  The slot refilled here
+  // was last read (by B and C) before barrier 3 of the previous chunk.
+  __device__ static void step_a(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c) {
+    issue_ring(p, sm, q, min(c + PD, q.NC - 1), (c + PD) % NSL);
+    const Slot& s = sm.ring[c % NSL];
+    const int lr = q.lr, lg = q.lg, ta = q.ta;
+    bf16x8 ka[DK / 32], txa[2];
 #pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) cur.ka[kt] = to_mfma_layout(cur.ka[kt]);
+    for (int kt = 0; kt < DK / 32; ++kt) ka[kt] = load_bf16x8(&s.k[kpos(ta, 4 * kt + lg)]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) cur.txa[kt] = to_mfma_layout(cur.txa[kt]);
-    const int lr = q.lr, lg = q.lg;
-    const float wvv[4] = {cur.wv.x, cur.wv.y, cur.wv.z, cur.wv.w};
-    const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
+    for (int kt = 0; kt < 2; ++kt) txa[kt] = load_bf16x8(&s.tx[xpos(ta, 4 * kt + lg)]);
+    const float4 cr = *reinterpret_cast<const float4*>(&s.sc[SC_CR * L + q.tc0]);
+    const float4 wv = *reinterpret_cast<const float4*>(&s.sc[SC_W * L + q.tc0]);
+    const float wvv[4] = {wv.x, wv.y, wv.z, wv.w};
+    const float crv[4] = {cr.x, cr.y, cr.z, cr.w};
     f32x4 kh[2];
     kh[0] = kh[1] = f4zero();
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        kh[ct] = mfma16(cur.ka[kt], load_bf16x8(&smc.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), kh[ct]);
+        kh[ct] = mfma16(ka[kt], load_bf16x8(&sm.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), kh[ct]);
+    // R = V - diag(e^g rk) K H; v read transposed: rows q.tc0 .. + 3 of column 16 ct + lr
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
+      const int tv = q.tc0 + (lr >> 2);
+      const uint2 v4 = lds_read_tr16(&s.v[vpos(tv, 2 * ct + ((lr >> 1) & 1)) + 4 * (lr & 1)]);
+      const float vr[4] = {__uint_as_float(v4.x << 16), __uint_as_float(v4.x & 0xffff0000u),
+                           __uint_as_float(v4.y << 16), __uint_as_float(v4.y & 0xffff0000u)};
       float rv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rv[r] = __uint_as_float(static_cast<uint32_t>(cur.vv[ct][r]) << 16) - crv[r] * kh[ct][r];
+      for (int r = 0; r < 4; ++r) rv[r] = vr[r] - crv[r] * kh[ct][r];
       *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
     }
     lds_barrier();  // 1: R complete
@@ -438,7 +487,7 @@ struct ChunkFwd {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        x[ct] = mfma16(cur.txa[kt], load_bf16x8(&smc.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), x[ct]);
+        x[ct] = mfma16(txa[kt], load_bf16x8(&sm.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), x[ct]);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       *reinterpret_cast<uint2*>(&sm.xb[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(x[ct][0], x[ct][1], x[ct][2], x[ct][3]);
@@ -446,49 +495,64 @@ struct ChunkFwd {
           pack4_bf16(wvv[0] * x[ct][0], wvv[1] * x[ct][1], wvv[2] * x[ct][2], wvv[3] * x[ct][3]);
     }
     lds_barrier();  // 2: X complete
-    lds_barrier();  // 3: H of the next chunk complete
+    wait_vm<(PD - 1) * NDMA>();
+    lds_barrier();  // 3: H of the next chunk complete; slot c + 1 complete
   }
 
-  // Group B, one chunk: H update and checkpoint.
-  __device__ static void step_b(const ChunkFwdArgs& p, const Smem& smc, Smem& sm, const Lane& q, int c,
-                                StageB& cur, f32x4 (&H)[RTW][2]) {
+  // Group B, one chunk: H update and checkpoint.  The K^T operand comes from
+  // the ring's k tile through transposing LDS reads: for row tile it and
+  // steps 32 kt + 8 lg .. + 7, lane (lr, lg) gets column i = 16 (w RTW + it) + lr.
+  __device__ static void step_b(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c, f32x4 (&H)[RTW][2]) {
+    const Dims& d = p.d;
+    const int lr = q.lr, lg = q.lg;
+    const Slot& s = sm.ring[c % NSL];
+    lds_barrier();  // 1
+    lds_barrier();  // 2: X complete
+    const float egl = s.sc[SC_EGL * L];
+    bf16x8 kta[RTW][2];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) cur.kta[it][kt] = to_mfma_layout(cur.kta[it][kt]);
-    const Dims& d = p.d;
-    const int lr = q.lr, lg = q.lg;
-    lds_barrier();  // 1
-    lds_barrier();  // 2: X complete
+      for (int kt = 0; kt < 2; ++kt) {
+        const int t = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * (q.w * RTW + it) + ((lr >> 1) & 1);
+        const uint2 lo = lds_read_tr16(&s.k[kpos(t, pc) + 4 * (lr & 1)]);
+        const uint2 hi = lds_read_tr16(&s.k[kpos(t + 4, pc) + 4 * (lr & 1)]);
+        kta[it][kt] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      }
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) H[it][ct][r] *= cur.egl;
+        for (int r = 0; r < 4; ++r) H[it][ct][r] *= egl;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       bf16x8 bx[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) bx[ct] = load_bf16x8(&smc.xw[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
+      for (int ct = 0; ct < 2; ++ct) bx[ct] = load_bf16x8(&sm.xw[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) H[it][ct] = mfma16(cur.kta[it][kt], bx[ct], H[it][ct]);
+        for (int ct = 0; ct < 2; ++ct) H[it][ct] = mfma16(kta[it][kt], bx[ct], H[it][ct]);
     }
     put_h(sm, q, H);
-    // checkpoint of the state at chunk c+1's start: a transpose inside each
-    // quad of lanes gives every lane 4 consecutive columns of one row
-    if (p.ckpt && c + 1 < q.NC) {
-      float* ck = p.ckpt + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv + q.col0 +
-                  (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg) * d.Dv + lr);
+    // checkpoint of the state at chunk c+1's start.  The stores are
+    // unconditional; without a checkpoint slot (last chunk, or none
+    // requested) the descriptor is empty and they are dropped.
+    {
+      const size_t hsz = static_cast<size_t>(DK) * d.Dv;
+      const bool ck = p.ckpt != nullptr && c + 1 < q.NC;
+      const rsrc_t rck = make_rsrc(ck ? static_cast<const void*>(p.ckpt + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * hsz)
+                                      : static_cast<const void*>(p.state_out),
+                                   ck ? hsz * 4 : 0);
+      const uint32_t co = 4 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg) * d.Dv + q.col0 + lr);
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float* cp = ck + static_cast<uint32_t>(16 * it + r) * d.Dv;
-          cp[0] = H[it][0][r];
-          cp[16] = H[it][1][r];
+          const uint32_t o = co + 4 * static_cast<uint32_t>(16 * it + r) * d.Dv;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(H[it][0][r]), rck, o, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(H[it][1][r]), rck, o + 64, 0, 0);
         }
     }
     lds_barrier();  // 3: H of the next chunk complete
@@ -496,7 +560,7 @@ struct ChunkFwd {
 
   // Group C, one chunk: (Q H)^T, then O^T = (Q H)^T diag(e^gamma rq) + X^T Mq^T,
   // which gives each lane one step and four consecutive columns to store.
-  __device__ static void step_c(const ChunkFwdArgs& p, const Smem& smc, const Lane& q, int c, StageC& cur) {
+  __device__ static void step_c(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c, StageC& cur) {
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt) cur.qa[kt] = to_mfma_layout(cur.qa[kt]);
 #pragma unroll
@@ -504,56 +568,42 @@ struct ChunkFwd {
     const Dims& d = p.d;
     const int t0 = c * L, Lc = min(L, d.T - t0);
     const int lr = q.lr, lg = q.lg;
+    const float co = sm.ring[c % NSL].sc[SC_CO * L + q.ta];
     f32x4 o[2];  // rows v = 16 ct + 4 lg + r, column t = 16 w + lr
     o[0] = o[1] = f4zero();
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        o[ct] = mfma16(load_bf16x8(&smc.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), cur.qa[kt], o[ct]);
+        o[ct] = mfma16(load_bf16x8(&sm.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), cur.qa[kt], o[ct]);
     lds_barrier();  // 1
     lds_barrier();  // 2: X complete
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[ct][r] *= cur.co;
+      for (int r = 0; r < 4; ++r) o[ct][r] *= co;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        o[ct] = mfma16(load_bf16x8(&smc.xb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), cur.mqa[kt], o[ct]);
-    if (q.ta < Lc) {
-      bf16* oc = static_cast<bf16*>(p.o) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0 +
-                 (static_cast<uint32_t>(q.ta) * q.v_row + 4 * lg);
+        o[ct] = mfma16(load_bf16x8(&sm.xb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), cur.mqa[kt], o[ct]);
+    {  // rows past the end of the sequence fall outside the descriptor: dropped
+      const rsrc_t ro = make_rsrc(static_cast<bf16*>(p.o) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv,
+                                  (static_cast<size_t>(Lc - 1) * q.v_row + d.Dv) * 2);
+      const uint32_t oo = 2 * (static_cast<uint32_t>(q.ta) * q.v_row + q.col0 + 4 * lg);
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        *reinterpret_cast<uint2*>(oc + 16 * ct) = pack4_bf16(o[ct][0], o[ct][1], o[ct][2], o[ct][3]);
+      for (int ct = 0; ct < 2; ++ct) buf_store_u2(ro, oo + 32 * ct, pack4_bf16(o[ct][0], o[ct][1], o[ct][2], o[ct][3]));
     }
     lds_barrier();  // 3
   }
 
   __device__ static void run_a(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
-    lds_barrier();  // 0: initial H
-    // Prefetch two chunks ahead through three register stages.  The loads are
-    // unconditional, from a chunk index clamped to the last chunk: a load under
-    // a branch makes the compiler wait for every outstanding load where the
-    // branch joins, which would void the prefetch.
-    const int cl = q.NC - 1;
-    StageA s0, s1, s2;
-    if (q.NC > 0) {
-      load_a(p, q, 0, s0);
-      load_a(p, q, min(1, cl), s1);
-    }
-    for (int c = 0; c < q.NC; c += 3) {
-      load_a(p, q, min(c + 2, cl), s2);
-      step_a(sm, sm, q, s0);
-      if (c + 1 >= q.NC) break;
-      load_a(p, q, min(c + 3, cl), s0);
-      step_a(sm, sm, q, s1);
-      if (c + 2 >= q.NC) break;
-      load_a(p, q, min(c + 4, cl), s1);
-      step_a(sm, sm, q, s2);
-    }
+#pragma unroll
+    for (int c = 0; c < PD; ++c) issue_ring(p, sm, q, min(c, q.NC - 1), c);
+    wait_vm<(PD - 1) * NDMA>();
+    lds_barrier();  // 0: initial H; slot 0 complete
+    for (int c = 0; c < q.NC; ++c) step_a(p, sm, q, c);
+    wait_vm<0>();  // no direct-to-LDS load may land after the workgroup ends
   }
 
   __device__ static void run_b(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
@@ -572,22 +622,7 @@ struct ChunkFwd {
         }
     put_h(sm, q, H);
     lds_barrier();  // 0
-    const int cl = q.NC - 1;
-    StageB s0, s1, s2;
-    if (q.NC > 0) {
-      load_b(p, q, 0, s0);
-      load_b(p, q, min(1, cl), s1);
-    }
-    for (int c = 0; c < q.NC; c += 3) {
-      load_b(p, q, min(c + 2, cl), s2);
-      step_b(p, sm, sm, q, c, s0, H);
-      if (c + 1 >= q.NC) break;
-      load_b(p, q, min(c + 3, cl), s0);
-      step_b(p, sm, sm, q, c + 1, s1, H);
-      if (c + 2 >= q.NC) break;
-      load_b(p, q, min(c + 4, cl), s1);
-      step_b(p, sm, sm, q, c + 2, s2, H);
-    }
+    for (int c = 0; c < q.NC; ++c) step_b(p, sm, q, c, H);
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
@@ -601,6 +636,10 @@ struct ChunkFwd {
 
   __device__ static void run_c(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
     lds_barrier();  // 0: initial H
+    // Prefetch two chunks ahead through three register stages.  The loads are
+    // unconditional, from a chunk index clamped to the last chunk: a load under
+    // a branch makes the compiler wait for every outstanding load where the
+    // branch joins, which would void the prefetch.
     const int cl = q.NC - 1;
     StageC s0, s1, s2;
     if (q.NC > 0) {
@@ -631,7 +670,7 @@ struct ChunkFwd {
     q.bj = q.b * d.Hk + q.j;
     q.col0 = slice * NV;
     const int tid = threadIdx.x, l = tid & 63;
-    q.w = (tid >> 6) & 3;
+    q.w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     q.l = l;
     q.lr = l & 15;
     q.lg = l >> 4;
@@ -642,14 +681,14 @@ struct ChunkFwd {
     q.v_row = d.Hv * d.Dv;
     {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
-      q.rk = make_rsrc(p.k, bt * d.Hk * DK * 2);
+      q.dk = desc(p.k, bt * d.Hk * DK * 2);
       q.rq = make_rsrc(p.q, bt * d.Hk * DK * 2);
-      q.rv = make_rsrc(p.v, bt * d.Hv * d.Dv * 2);
-      q.rtx = make_rsrc(p.cb.Tx, nmat * L * L * 2);
+      q.dv = desc(p.v, bt * d.Hv * d.Dv * 2);
+      q.dtx = desc(p.cb.Tx, nmat * L * L * 2);
       q.rmq = make_rsrc(p.cb.Mq, nmat * L * L * 2);
-      q.rkt = make_rsrc(p.cb.KT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);
-      q.rsc = make_rsrc(p.cb.sc, nmat * SC_ROWS * L * 4);
+      q.dsc = desc(p.cb.sc, nmat * SC_ROWS * L * 4);
     }
+    if (q.NC == 0) return;
     if (tid < 256)
       run_a(p, sm, q);
     else if (tid < 512)

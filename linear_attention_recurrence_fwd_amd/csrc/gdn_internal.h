@@ -89,9 +89,9 @@ enum : int {
   SC_CR = 0,     // e^{g_t} rk_t
   SC_CO = 1,     // e^{g_t} rq_t
   SC_W = 2,      // beta_t e^{g_L - g_t} rk_t
-  SC_KL = 3,     // e^{g_L - g_t} rk_t
-  SC_BETA = 4,   // beta_t
-  SC_EGL = 5,    // [0] = e^{g_L}
+  SC_EGL = 3,    // [0] = e^{g_L}   (rows 0..3: what the forward state pass reads)
+  SC_KL = 4,     // e^{g_L - g_t} rk_t
+  SC_BETA = 5,   // beta_t
   SC_GAM = 6,    // g_t
   SC_EG = 7,     // e^{g_t}
   SC_EL = 8,     // e^{g_L - g_t}
