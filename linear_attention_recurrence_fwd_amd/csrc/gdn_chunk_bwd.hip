@@ -45,78 +45,111 @@ namespace {
 
 constexpr int L = kChunk;
 constexpr int LP = L + 1;
-constexpr int NT = 256;
 
 // ------------------------------------------------------- reverse state pass
 
 template <int DK>
 struct ChunkBwdState {
+  // Eight waves in two groups of four (w = wave index within the group):
+  //   A (waves 0-3): for row tile w of the chunk, the dependent chain
+  //                  rhs = diag(e^{gL-g} rk) K dH' + P^T dO, Ehat = Tx^T diag(beta) rhs
+  //                  (= dv), eps = rhs - A^T Ehat.  A also streams the chunk's k
+  //                  rows, P^T, Tx^T, A^T, dO slice and chunk scalars into a
+  //                  2-slot LDS ring with direct-to-LDS loads, one chunk ahead.
+  //   B (waves 4-7): dH for its RTW row tiles, in MFMA accumulators: stores dH'
+  //                  of the chunk, adds e^{gL} dH' + Q^T diag(e^g rq) dO while A
+  //                  works (it does not depend on Ehat), then - K^T diag(e^g rk)
+  //                  Ehat with K^T read transposed from the ring.
+  // Three barriers per chunk: Y (rhs ready), Z (Ehat ready), X (dH of the
+  // previous chunk ready, next ring slot complete).
+  static constexpr int NTS = 512;
   static constexpr int NV = 32;        // Dv columns per workgroup
-  static constexpr int RTW = DK / 64;  // dH row tiles per wave
+  static constexpr int RTW = DK / 64;  // dH row tiles per group-B wave
   static constexpr int HS = DK + 8;    // bf16 row stride of dH^T
   static constexpr int XS = L + 8;     // bf16 row stride of the [v][t] tiles
+  static constexpr int NPK = DK / 8;   // 16-byte pieces of a k row
+  static constexpr int KDMA = DK / 32;
+  static constexpr int NDMA = KDMA + 6 + 1 + 2;  // ring loads per group-A wave per chunk
+  // A ring slot (layouts as in the forward state pass: 16-byte piece p of row
+  // t at t * (pieces per row) + (p ^ swizzle(t))).
+  struct Slot {
+    bf16 k[L * DK];    // k rows, swizzle t & 7
+    bf16 pt[L * L];    // P^T rows, swizzle t & 7
+    bf16 tt[L * L];    // Tx^T rows, swizzle t & 7
+    bf16 at[L * L];    // A^T rows, swizzle t & 7
+    bf16 dO[L * NV];   // dO rows of this slice's columns, swizzle t & 3
+    float sc[8 * L];   // chunk scalar rows 0 .. 7
+  };
+  static_assert(SC_CR < 8 && SC_CO < 8 && SC_EGL < 8 && SC_KL < 8 && SC_BETA < 8, "rows held in a ring slot");
   struct Smem {
+    alignas(16) Slot ring[2];
     alignas(16) bf16 hb[NV * HS];   // dH'^T, the B operand of K dH'
-    alignas(16) bf16 dob[NV * XS];  // dO^T
-    alignas(16) bf16 dos[NV * XS];  // (diag(e^g rq) dO)^T
     alignas(16) bf16 rb[NV * XS];   // (diag(beta) rhs)^T
     alignas(16) bf16 eb[NV * XS];   // Ehat^T
     alignas(16) bf16 es[NV * XS];   // -(diag(e^g rk) Ehat)^T
   };
-  // Operands of one chunk, prefetched a chunk ahead from clamped addresses
-  // (rows past the end of the sequence repeat its last row; their chunk
-  // scalars are zero and the chunk matrices are zero there).
-  struct Stage {
-    bf16x8 ka[DK / 32];               // k rows t = 16 w + lr
-    bf16x8 pqa[2], txa[2], ata[2];    // P^T, Tx^T, A^T rows t = 16 w + lr
-    bf16x8 qta[RTW][2], kta[RTW][2];  // Q^T, K^T rows i = 16 (w RTW + it) + lr
-    unsigned short dov[2][4];         // dO bits at rows 16 w + 4 lg + r, cols 16 ct + lr
-    float4 kl, bt, co, cr;            // chunk scalars at rows 16 w + 4 lg + r
-    float egl;
+  // Group B's Q^T operand of one chunk, in registers (quad-coalesced loads,
+  // permuted at use), loaded a chunk ahead from clamped addresses.
+  struct StageB {
+    bf16x8 qta[RTW][2];  // Q^T rows i = 16 (w RTW + it) + lr
   };
   struct Lane {
     int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
-    uint32_t qk_row, v_row;
-    rsrc_t rk, rdo, rpq, rtx, rat, rqt, rkt, rsc;  // buffer descriptors of the operands
+    uint32_t v_row;
+    rsrc_t rqt;
+    i32x4 dk, dpt, dtt, dat, ddo, dsc;  // raw descriptors of the ring's operands
   };
 
-  // Operand loads are buffer loads at byte offsets from the tensor's base.
-  __device__ static void load_stage(const ChunkBwdArgs& p, const Lane& q, int c, Stage& s) {
+  __device__ static __forceinline__ int kpos(int t, int p) { return 8 * (t * NPK + (p ^ (t & 7))); }
+  __device__ static __forceinline__ int xpos(int t, int p) { return 8 * (t * 8 + (p ^ (t & 7))); }
+  __device__ static __forceinline__ int vpos(int t, int p) { return 8 * (t * 4 + (p ^ (t & 3))); }
+
+  // Group A: the NDMA ring loads of this wave for chunk c into slot sl.
+  __device__ static void issue_ring(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c, int sl) {
     const Dims& d = p.d;
-    const int t0 = c * L, tl = q.last - t0;
-    // quad-coalesced operand loads (see to_mfma_layout), permuted at use
-    const int cr_ = 16 * q.w + coal_row(q.l), cp_ = coal_piece(q.l);
-    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
+    const int t0 = c * L, tl = q.last - t0, l = q.l;
+    Slot& s = sm.ring[sl];
 #pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) s.ka[kt] = buf_bf16x8(q.rk, ko + 64 * kt);
-    const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s.pqa[kt] = buf_bf16x8(q.rpq, mo + 64 * kt);
-      s.txa[kt] = buf_bf16x8(q.rtx, mo + 64 * kt);
-      s.ata[kt] = buf_bf16x8(q.rat, mo + 64 * kt);
+    for (int jj = 0; jj < KDMA; ++jj) {
+      const int n = KDMA * q.w + jj, pos = 64 * n + l, t = pos / NPK, pc = (pos % NPK) ^ (t & 7);
+      dma16(q.dk, &s.k[512 * n], 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hk + q.j) * DK + 8 * pc));
     }
-    const uint32_t kto = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + coal_row(q.l)) * L +
-                              8 * coal_piece(q.l));
+    const uint32_t mat = static_cast<uint32_t>(q.bh * q.NC + c) * L * L;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int n = 2 * q.w + jj, pos = 64 * n + l, t = pos / 8, pc = (pos % 8) ^ (t & 7);
+      const uint32_t o = 2 * (mat + t * L + 8 * pc);
+      dma16(q.dpt, &s.pt[512 * n], o);
+      dma16(q.dtt, &s.tt[512 * n], o);
+      dma16(q.dat, &s.at[512 * n], o);
+    }
+    {
+      const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
+      dma16(q.ddo, &s.dO[512 * q.w],
+            2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hv + q.h) * d.Dv + q.col0 + 8 * pc));
+    }
+    const uint32_t so = static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) dma4(q.dsc, &s.sc[L * (2 * q.w + e)], 4 * (so + L * (2 * q.w + e) + l));
+  }
+
+  __device__ static void load_b(const ChunkBwdArgs& p, const Lane& q, int c, StageB& st) {
+    (void)p;
+    const uint32_t o = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + coal_row(q.l)) * L +
+                            8 * coal_piece(q.l));
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s.qta[it][kt] = buf_bf16x8(q.rqt, kto + 2 * (it * 16 * L) + 64 * kt);
-        s.kta[it][kt] = buf_bf16x8(q.rkt, kto + 2 * (it * 16 * L) + 64 * kt);
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t vo = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(q.tc0 + r, tl)) * d.Hv + q.h) * d.Dv + q.col0 + q.lr);
-      s.dov[0][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rdo, vo, 0, 0));
-      s.dov[1][r] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(q.rdo, vo + 32, 0, 0));
-    }
-    const uint32_t so = 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + q.tc0);
-    s.kl = buf_f4(q.rsc, so + 4 * SC_KL * L);
-    s.bt = buf_f4(q.rsc, so + 4 * SC_BETA * L);
-    s.co = buf_f4(q.rsc, so + 4 * SC_CO * L);
-    s.cr = buf_f4(q.rsc, so + 4 * SC_CR * L);
-    s.egl = buf_f1(q.rsc, 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + SC_EGL * L));
+      for (int kt = 0; kt < 2; ++kt) st.qta[it][kt] = buf_bf16x8(q.rqt, o + 2 * (it * 16 * L) + 64 * kt);
+  }
+
+  // The B operand of a product with dO^T over the chunk's steps: steps
+  // 32 kt + 8 lg .. + 7 of column 16 ct + lr, read transposed from the ring.
+  __device__ static __forceinline__ uint4 dO_operand(const Slot& s, const Lane& q, int kt, int ct) {
+    const int t = 32 * kt + 8 * q.lg + (q.lr >> 2), pc = 2 * ct + ((q.lr >> 1) & 1), sub = 4 * (q.lr & 1);
+    const uint2 lo = lds_read_tr16(&s.dO[vpos(t, pc) + sub]);
+    const uint2 hi = lds_read_tr16(&s.dO[vpos(t + 4, pc) + sub]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 
   __device__ static void put_h(Smem& sm, const Lane& q, const f32x4 (&H)[RTW][2]) {
@@ -128,31 +161,110 @@ struct ChunkBwdState {
             pack4_bf16(H[it][ct][0], H[it][ct][1], H[it][ct][2], H[it][ct][3]);
   }
 
-  __device__ static void step(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c,
-                              Stage& cur, f32x4 (&dH)[RTW][2]) {
+  // dv / eps rows of this wave: a transpose inside each quad of lanes gives
+  // every lane 4 consecutive columns of one step; steps past the end of the
+  // sequence fall outside the descriptor and are dropped.
+  __device__ static void store_rows(const ChunkBwdArgs& p, const Lane& q, void* dst, int t0, int Lc,
+                                    const f32x4 (&x)[2], float sign) {
+    const Dims& d = p.d;
+    const rsrc_t r = make_rsrc(static_cast<bf16*>(dst) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv,
+                               (static_cast<size_t>(Lc - 1) * q.v_row + d.Dv) * 2);
+    const uint32_t o = 2 * (static_cast<uint32_t>(q.tc0 + (q.lr & 3)) * q.v_row + q.col0 + (q.lr & ~3));
 #pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) cur.ka[kt] = to_mfma_layout(cur.ka[kt]);
+    for (int ct = 0; ct < 2; ++ct) {
+      const f32x4 tr = quad_transpose(x[ct]);
+      buf_store_u2(r, o + 32 * ct, pack4_bf16(sign * tr[0], sign * tr[1], sign * tr[2], sign * tr[3]));
+    }
+  }
+
+  // Group A, one chunk (chunks run last to first).  The slot refilled here
+  // (chunk c - 1) was last read before barrier X of the previous chunk; before
+  // barrier X of this chunk each wave waits for its ring loads (its 4 later
+  // stores may stay pending), so the slot is complete for every wave after X.
+  __device__ static void step_a(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c) {
+    issue_ring(p, sm, q, max(c - 1, 0), (c - 1) & 1);
+    const Dims& d = p.d;
+    const int t0 = c * L, Lc = min(L, d.T - t0);
+    const Slot& s = sm.ring[c & 1];
+    const int lr = q.lr, lg = q.lg, ta = q.ta;
+    bf16x8 ka[DK / 32], pqa[2], txa[2], ata[2];
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt) ka[kt] = load_bf16x8(&s.k[kpos(ta, 4 * kt + lg)]);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      cur.pqa[kt] = to_mfma_layout(cur.pqa[kt]);
-      cur.txa[kt] = to_mfma_layout(cur.txa[kt]);
-      cur.ata[kt] = to_mfma_layout(cur.ata[kt]);
+      pqa[kt] = load_bf16x8(&s.pt[xpos(ta, 4 * kt + lg)]);
+      txa[kt] = load_bf16x8(&s.tt[xpos(ta, 4 * kt + lg)]);
+      ata[kt] = load_bf16x8(&s.at[xpos(ta, 4 * kt + lg)]);
     }
+    const float4 kl4 = *reinterpret_cast<const float4*>(&s.sc[SC_KL * L + q.tc0]);
+    const float4 bt4 = *reinterpret_cast<const float4*>(&s.sc[SC_BETA * L + q.tc0]);
+    const float4 cr4 = *reinterpret_cast<const float4*>(&s.sc[SC_CR * L + q.tc0]);
+    const float klv[4] = {kl4.x, kl4.y, kl4.z, kl4.w};
+    const float btv[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+    const float crv[4] = {cr4.x, cr4.y, cr4.z, cr4.w};
+    // rhs = diag(e^{gL-g} rk) K dH' + P^T dO for row tile w
+    f32x4 kdh[2], rhs[2];
+    kdh[0] = kdh[1] = rhs[0] = rhs[1] = f4zero();
+#pragma unroll
+    for (int kt = 0; kt < DK / 32; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        kdh[ct] = mfma16(ka[kt], load_bf16x8(&sm.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), kdh[ct]);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) rhs[ct] = mfma16(pqa[kt], as_bf16x8(dO_operand(s, q, kt, ct)), rhs[ct]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rhs[ct][r] += klv[r] * kdh[ct][r];
+      *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(btv[0] * rhs[ct][0], btv[1] * rhs[ct][1], btv[2] * rhs[ct][2], btv[3] * rhs[ct][3]);
+    }
+    lds_barrier();  // Y: diag(beta) rhs complete
+    // Ehat = Tx^T diag(beta) rhs  (= dv)
+    f32x4 eh[2];
+    eh[0] = eh[1] = f4zero();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        eh[ct] = mfma16(txa[kt], load_bf16x8(&sm.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), eh[ct]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      *reinterpret_cast<uint2*>(&sm.eb[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(eh[ct][0], eh[ct][1], eh[ct][2], eh[ct][3]);
+      *reinterpret_cast<uint2*>(&sm.es[(16 * ct + lr) * XS + q.tc0]) =
+          pack4_bf16(-crv[0] * eh[ct][0], -crv[1] * eh[ct][1], -crv[2] * eh[ct][2], -crv[3] * eh[ct][3]);
+    }
+    lds_barrier();  // Z: Ehat complete
+    store_rows(p, q, p.dv, t0, Lc, eh, 1.f);
+    // eps = rhs - A^T Ehat
+    f32x4 ng[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ng[ct][r] = -rhs[ct][r];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        ng[ct] = mfma16(ata[kt], load_bf16x8(&sm.eb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), ng[ct]);
+    store_rows(p, q, p.E, t0, Lc, ng, -1.f);
+    wait_vm<4>();
+    lds_barrier();  // X: dH of the next chunk complete; slot c - 1 complete
+  }
+
+  // Group B, one chunk.
+  __device__ static void step_b(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c, StageB& cur,
+                                f32x4 (&dH)[RTW][2]) {
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        cur.qta[it][kt] = to_mfma_layout(cur.qta[it][kt]);
-        cur.kta[it][kt] = to_mfma_layout(cur.kta[it][kt]);
-      }
+      for (int kt = 0; kt < 2; ++kt) cur.qta[it][kt] = to_mfma_layout(cur.qta[it][kt]);
     const Dims& d = p.d;
-    const int t0 = c * L, Lc = min(L, d.T - t0);
     const int lr = q.lr, lg = q.lg;
-    const float klv[4] = {cur.kl.x, cur.kl.y, cur.kl.z, cur.kl.w};
-    const float btv[4] = {cur.bt.x, cur.bt.y, cur.bt.z, cur.bt.w};
-    const float cov[4] = {cur.co.x, cur.co.y, cur.co.z, cur.co.w};
-    const float crv[4] = {cur.cr.x, cur.cr.y, cur.cr.z, cur.cr.w};
-
+    const Slot& s = sm.ring[c & 1];
     // dH' of this chunk for the gradient pass: [i][v], bf16, the layout of the
     // checkpoints; a transpose inside each quad of lanes gives every lane 4
     // consecutive columns of one row
@@ -169,115 +281,99 @@ struct ChunkBwdState {
               pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
         }
     }
-    // dO^T and diag(e^g rq) dO^T
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      float dv4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dv4[r] = __uint_as_float(static_cast<uint32_t>(cur.dov[ct][r]) << 16);
-      *reinterpret_cast<uint2*>(&sm.dob[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(dv4[0], dv4[1], dv4[2], dv4[3]);
-      *reinterpret_cast<uint2*>(&sm.dos[(16 * ct + lr) * XS + q.tc0]) =
-          pack4_bf16(cov[0] * dv4[0], cov[1] * dv4[1], cov[2] * dv4[2], cov[3] * dv4[3]);
-    }
-    lds_barrier();
-    // rhs = diag(e^{gL-g} rk) K dH' + P^T dO for row tile w
-    f32x4 kdh[2], rhs[2];
-    kdh[0] = kdh[1] = rhs[0] = rhs[1] = f4zero();
-#pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        kdh[ct] = mfma16(cur.ka[kt], load_bf16x8(&sm.hb[(16 * ct + lr) * HS + 32 * kt + 8 * lg]), kdh[ct]);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        rhs[ct] = mfma16(cur.pqa[kt], load_bf16x8(&sm.dob[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), rhs[ct]);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rhs[ct][r] += klv[r] * kdh[ct][r];
-      *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) =
-          pack4_bf16(btv[0] * rhs[ct][0], btv[1] * rhs[ct][1], btv[2] * rhs[ct][2], btv[3] * rhs[ct][3]);
-    }
-    lds_barrier();
-    // Ehat = Tx^T diag(beta) rhs  (= dv)
-    f32x4 eh[2];
-    eh[0] = eh[1] = f4zero();
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        eh[ct] = mfma16(cur.txa[kt], load_bf16x8(&sm.rb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), eh[ct]);
-    const size_t row0 = ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
-    {
-      bf16* dvc = static_cast<bf16*>(p.dv) + row0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = q.tc0 + r;
-        if (t < Lc) {
-          const uint32_t oo = static_cast<uint32_t>(t) * q.v_row + lr;
-          dvc[oo] = bf16_of(eh[0][r]);
-          (dvc + oo)[16] = bf16_of(eh[1][r]);
-        }
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      *reinterpret_cast<uint2*>(&sm.eb[(16 * ct + lr) * XS + q.tc0]) =
-          pack4_bf16(eh[ct][0], eh[ct][1], eh[ct][2], eh[ct][3]);
-      *reinterpret_cast<uint2*>(&sm.es[(16 * ct + lr) * XS + q.tc0]) =
-          pack4_bf16(-crv[0] * eh[ct][0], -crv[1] * eh[ct][1], -crv[2] * eh[ct][2], -crv[3] * eh[ct][3]);
-    }
-    lds_barrier();
-    // eps = rhs - A^T Ehat
-    {
-      f32x4 ng[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ng[ct][r] = -rhs[ct][r];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          ng[ct] = mfma16(cur.ata[kt], load_bf16x8(&sm.eb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), ng[ct]);
-      bf16* ec = p.E + row0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = q.tc0 + r;
-        if (t < Lc) {
-          const uint32_t oo = static_cast<uint32_t>(t) * q.v_row + lr;
-          ec[oo] = bf16_of(-ng[0][r]);
-          (ec + oo)[16] = bf16_of(-ng[1][r]);
-        }
-      }
-    }
-    // dH = e^{gL} dH' + Q^T diag(e^g rq) dO - K^T diag(e^g rk) Ehat
+    // dH <- e^{gL} dH' + Q^T diag(e^g rq) dO (the operand scaled by e^g rq per step)
+    const float egl = s.sc[SC_EGL * L];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dH[it][ct][r] *= cur.egl;
+        for (int r = 0; r < 4; ++r) dH[it][ct][r] *= egl;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      bf16x8 bq[2], be[2];
+      const float4 c0 = *reinterpret_cast<const float4*>(&s.sc[SC_CO * L + 32 * kt + 8 * lg]);
+      const float4 c1 = *reinterpret_cast<const float4*>(&s.sc[SC_CO * L + 32 * kt + 8 * lg + 4]);
+      const float cov[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        bq[ct] = load_bf16x8(&sm.dos[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
-        be[ct] = load_bf16x8(&sm.es[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
+        const uint4 u = dO_operand(s, q, kt, ct);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        uint32_t o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o4[i] = pack2_bf16(cov[2 * i] * __uint_as_float(w4[i] << 16), cov[2 * i + 1] * __uint_as_float(w4[i] & 0xffff0000u));
+        const bf16x8 bq = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+#pragma unroll
+        for (int it = 0; it < RTW; ++it) dH[it][ct] = mfma16(cur.qta[it][kt], bq, dH[it][ct]);
       }
+    }
+    lds_barrier();  // Y
+    lds_barrier();  // Z: Ehat complete
+    // dH -= K^T diag(e^g rk) Ehat, K^T read transposed from the ring's k tile
 #pragma unroll
-      for (int it = 0; it < RTW; ++it)
+    for (int kt = 0; kt < 2; ++kt) {
+      bf16x8 be[2];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          dH[it][ct] = mfma16(cur.qta[it][kt], bq[ct], dH[it][ct]);
-          dH[it][ct] = mfma16(cur.kta[it][kt], be[ct], dH[it][ct]);
-        }
+      for (int ct = 0; ct < 2; ++ct) be[ct] = load_bf16x8(&sm.es[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
+#pragma unroll
+      for (int it = 0; it < RTW; ++it) {
+        const int t = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * (q.w * RTW + it) + ((lr >> 1) & 1);
+        const uint2 lo = lds_read_tr16(&s.k[kpos(t, pc) + 4 * (lr & 1)]);
+        const uint2 hi = lds_read_tr16(&s.k[kpos(t + 4, pc) + 4 * (lr & 1)]);
+        const bf16x8 kta = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) dH[it][ct] = mfma16(kta, be[ct], dH[it][ct]);
+      }
     }
     put_h(sm, q, dH);
-    lds_barrier();
+    lds_barrier();  // X
+  }
+
+  __device__ static void run_a(const ChunkBwdArgs& p, Smem& sm, const Lane& q) {
+    issue_ring(p, sm, q, q.NC - 1, (q.NC - 1) & 1);
+    wait_vm<0>();
+    lds_barrier();  // X: initial dH; first slot complete
+    for (int c = q.NC - 1; c >= 0; --c) step_a(p, sm, q, c);
+    wait_vm<0>();  // no direct-to-LDS load may land after the workgroup ends
+  }
+
+  __device__ static void run_b(const ChunkBwdArgs& p, Smem& sm, const Lane& q) {
+    const Dims& d = p.d;
+    const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
+    // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
+    f32x4 dH[RTW][2];
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
+          dH[it][ct][r] = p.dS_final ? p.dS_final[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
+        }
+    put_h(sm, q, dH);
+    StageB s0, s1;
+    load_b(p, q, q.NC - 1, s0);
+    lds_barrier();  // X
+    // The prefetches are unconditional, from a chunk index clamped to the
+    // first chunk: a load under a branch makes the compiler wait for every
+    // outstanding load where the branch joins, which would void the prefetch.
+    for (int c = q.NC - 1; c >= 0; c -= 2) {
+      load_b(p, q, max(c - 1, 0), s1);
+      step_b(p, sm, q, c, s0, dH);
+      if (c < 1) break;
+      load_b(p, q, max(c - 2, 0), s0);
+      step_b(p, sm, q, c - 1, s1, dH);
+    }
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
+          p.dstate[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = dH[it][ct][r];
+        }
   }
 
   __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
@@ -292,69 +388,34 @@ struct ChunkBwdState {
     q.bj = q.b * d.Hk + q.j;
     q.col0 = slice * NV;
     const int tid = threadIdx.x, l = tid & 63;
-    q.w = tid >> 6;
+    q.w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     q.l = l;
     q.lr = l & 15;
     q.lg = l >> 4;
     q.ta = 16 * q.w + q.lr;
     q.tc0 = 16 * q.w + 4 * q.lg;
     q.last = d.T - 1;
-    q.qk_row = d.Hk * DK;
     q.v_row = d.Hv * d.Dv;
     {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
-      const size_t nkt = static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2;
-      q.rk = make_rsrc(p.k, bt * d.Hk * DK * 2);
-      q.rdo = make_rsrc(p.dO, bt * d.Hv * d.Dv * 2);
-      q.rpq = make_rsrc(p.cb.PqT, nmat * L * L * 2);
-      q.rtx = make_rsrc(p.cb.TxT, nmat * L * L * 2);
-      q.rat = make_rsrc(p.cb.AtT, nmat * L * L * 2);
-      q.rqt = make_rsrc(p.cb.QT, nkt);
-      q.rkt = make_rsrc(p.cb.KT, nkt);
-      q.rsc = make_rsrc(p.cb.sc, nmat * SC_ROWS * L * 4);
+      q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
+      q.ddo = raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
+      q.dpt = raw_desc(p.cb.PqT, nmat * L * L * 2);
+      q.dtt = raw_desc(p.cb.TxT, nmat * L * L * 2);
+      q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
+      q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
+      q.rqt = make_rsrc(p.cb.QT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);
     }
-    const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
-
-    // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
-    f32x4 dH[RTW][2];
-#pragma unroll
-    for (int it = 0; it < RTW; ++it)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          dH[it][ct][r] = p.dS_final ? p.dS_final[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
-        }
-    put_h(sm, q, dH);
-    lds_barrier();
-
-    // The prefetches are unconditional, from a chunk index clamped to the
-    // first chunk: a load under a branch makes the compiler wait for every
-    // outstanding load where the branch joins, which would void the prefetch.
-    Stage s0, s1;
-    if (q.NC > 0) load_stage(p, q, q.NC - 1, s0);
-    for (int c = q.NC - 1; c >= 0; c -= 2) {
-      load_stage(p, q, max(c - 1, 0), s1);
-      step(p, sm, q, c, s0, dH);
-      if (c < 1) break;
-      load_stage(p, q, max(c - 2, 0), s0);
-      step(p, sm, q, c - 1, s1, dH);
-    }
-#pragma unroll
-    for (int it = 0; it < RTW; ++it)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          p.dstate[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = dH[it][ct][r];
-        }
+    if (q.NC == 0) return;
+    if (tid < 256)
+      run_a(p, sm, q);
+    else
+      run_b(p, sm, q);
   }
 };
 
 template <int DK>
-__global__ void __launch_bounds__(NT) chunk_bwd_state_kernel(ChunkBwdArgs p) {
+__global__ void __launch_bounds__(512) chunk_bwd_state_kernel(ChunkBwdArgs p) {
   __shared__ typename ChunkBwdState<DK>::Smem sm;
   ChunkBwdState<DK>::run(p, sm);
 }
@@ -967,10 +1028,10 @@ __global__ void __launch_bounds__(NTG) chunk_bwd_grad_kernel(ChunkBwdArgs p) {
 hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
   const int nblk = a.d.B * a.d.Hv * (a.d.Dv / ChunkBwdState<64>::NV);
   switch (a.d.Dk) {
-    case 64: chunk_bwd_state_kernel<64><<<nblk, NT, 0, st>>>(a); break;
-    case 128: chunk_bwd_state_kernel<128><<<nblk, NT, 0, st>>>(a); break;
-    case 192: chunk_bwd_state_kernel<192><<<nblk, NT, 0, st>>>(a); break;
-    case 256: chunk_bwd_state_kernel<256><<<nblk, NT, 0, st>>>(a); break;
+    case 64: chunk_bwd_state_kernel<64><<<nblk, ChunkBwdState<64>::NTS, 0, st>>>(a); break;
+    case 128: chunk_bwd_state_kernel<128><<<nblk, ChunkBwdState<128>::NTS, 0, st>>>(a); break;
+    case 192: chunk_bwd_state_kernel<192><<<nblk, ChunkBwdState<192>::NTS, 0, st>>>(a); break;
+    case 256: chunk_bwd_state_kernel<256><<<nblk, ChunkBwdState<256>::NTS, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -370,34 +370,6 @@ struct ChunkFwd {
   __device__ static __forceinline__ int xpos(int t, int p) { return 8 * (t * 8 + (p ^ (t & 7))); }
   __device__ static __forceinline__ int vpos(int t, int p) { return 8 * (t * 4 + (p ^ (t & 3))); }
 
-  // Direct-to-LDS buffer loads, issued through inline assembly: the compiler
-  // does not see them, so it does not make every later LDS read wait for
-  // them; the waits are explicit (wait_vm before barrier 3).  M0 holds the
-  // wave's LDS base; the s_nop is the wait state required between an M0
-  // write and a load to LDS.
-  __device__ static __forceinline__ uint32_t lds_addr(const void* p) {
-    typedef __attribute__((address_space(3))) const void lds_cvoid;
-    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)p)));
-  }
-  __device__ static __forceinline__ void dma16(const i32x4& r, const void* lds, uint32_t off) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
-  }
-  __device__ static __forceinline__ void dma4(const i32x4& r, const void* lds, uint32_t off) {
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
-  }
-  // raw buffer descriptor words (as make_rsrc) for the inline loads
-  __device__ static __forceinline__ i32x4 desc(const void* p, size_t bytes) {
-    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    return i32x4{static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
-                 static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu)),
-                 static_cast<int>(__builtin_amdgcn_readfirstlane(n)), 0x00020000};
-  }
-  // Wait until at most N of this wave's vector memory operations are pending.
-  template <int N> __device__ static __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  }
-
   // Group A: the NDMA ring loads of this wave for chunk c into slot sl.  Load
   // n of a tile covers its 16-byte positions 64 n .. 64 n + 63.
   __device__ static void issue_ring(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c, int sl) {
@@ -681,12 +653,12 @@ struct ChunkFwd {
     q.v_row = d.Hv * d.Dv;
     {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
-      q.dk = desc(p.k, bt * d.Hk * DK * 2);
+      q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
       q.rq = make_rsrc(p.q, bt * d.Hk * DK * 2);
-      q.dv = desc(p.v, bt * d.Hv * d.Dv * 2);
-      q.dtx = desc(p.cb.Tx, nmat * L * L * 2);
+      q.dv = raw_desc(p.v, bt * d.Hv * d.Dv * 2);
+      q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
       q.rmq = make_rsrc(p.cb.Mq, nmat * L * L * 2);
-      q.dsc = desc(p.cb.sc, nmat * SC_ROWS * L * 4);
+      q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
     }
     if (q.NC == 0) return;
     if (tid < 256)

@@ -222,6 +222,36 @@ __device__ __forceinline__ void buf_store_u2(rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 0);
 }
 
+// Direct-to-LDS buffer loads (lane i of a load writes its 16 or 4 bytes at
+// the wave's LDS base + 16 i or 4 i), issued through inline assembly: the
+// compiler does not see them, so it does not make every later LDS read wait
+// for them.  The caller waits explicitly (wait_vm) before the barrier that
+// publishes the data.  M0 holds the wave's LDS base; the s_nop is the wait
+// state required between an M0 write and a load to LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef __attribute__((address_space(3))) const void lds_cvoid;
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cvoid*)p)));
+}
+__device__ __forceinline__ void dma16(const i32x4& r, const void* lds, uint32_t off) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4& r, const void* lds, uint32_t off) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
+}
+// Raw buffer descriptor words (as make_rsrc) for the inline loads.
+__device__ __forceinline__ i32x4 raw_desc(const void* p, size_t bytes) {
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a))),
+               static_cast<int>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xffffu)),
+               static_cast<int>(__builtin_amdgcn_readfirstlane(n)), 0x00020000};
+}
+// Wait until at most N of this wave's vector memory operations (loads, stores
+// and direct-to-LDS loads, counted in issue order) are pending.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
 // (lgkmcnt) and meets the other waves, without waiting for outstanding global
 // loads, so loads issued ahead of time (prefetches) stay in flight across it.
