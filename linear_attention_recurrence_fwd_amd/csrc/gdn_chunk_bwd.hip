@@ -467,7 +467,6 @@ struct ChunkBwdGrad {
   static constexpr int IH = IT / 2;      // tiles of Dk per wave
   static constexpr int KS = DK / 32;     // MFMA steps over Dk
   static constexpr int VS = NS + 8;      // bf16 row stride of [i][v] and [t][v] tiles
-  static constexpr int IS = DK + 8;      // bf16 row stride of [v][i] tiles
   static constexpr int TS = L + 8;       // bf16 row stride of [v][t] tiles and Wq rows
   static constexpr int WS = 2 * L + 8;   // bf16 row stride of [Wk1 | Wk2] rows
   static constexpr int FS = DK + 4;      // fp32 row stride of the final accumulators
@@ -475,9 +474,7 @@ struct ChunkBwdGrad {
   static_assert(NB <= NTG, "one block per thread");
   struct Slab {
     bf16 hv[DK * VS];   // H   [i][v]
-    bf16 hi[NS * IS];   // H   [v][i]
     bf16 dhv[DK * VS];  // dH' [i][v]
-    bf16 dhi[NS * IS];  // dH' [v][i]
     bf16 rt[NS * TS];   // R   [v][t]
     bf16 xr[L * VS];    // X   [t][v]
     bf16 xs[L * VS];    // diag(e^{gL-g} beta) X   [t][v]
@@ -503,13 +500,18 @@ struct ChunkBwdGrad {
     Wts w;
     Fin f;
   };
+  static constexpr int HB = 4;  // value heads per batch of the deferred gate-gradient section (one wave each)
   struct Smem {
     alignas(16) Big u;
     float wsq[L * LP], ws1[L * LP], ws2[L * LP];  // fp32 sums over the group's heads of Wq, Wk1, Wk2
     float rk[L], rq[L];
     float gam[L], eg[L], el[L], beta[L], ell[L];
-    float bv[2][L], pa[2][L], pdb[2][L], cs[L], rs[L];
+    float bv[2][L], pa[2][L], pdb[2][L], rs[L];
     float red[NTG / 64];
+    // per value head (slot = head % HB), for the deferred section: the
+    // prefix-summed and suffix-summed terms of dl, the db factor, l, and the
+    // per-head scalars <dH', H> and e^{gamma_L}
+    float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB];
   };
   // Per-head data loaded ahead: the scalars and Tx rows a head starts with,
   // and what its tail needs (the chunk's P^T / A^T tiles, a and the mask).
@@ -518,9 +520,7 @@ struct ChunkBwdGrad {
     bf16x8 txb[2];                      // Tx row ta
   };
   struct HeadTail {
-    uint4 pt, at;           // chunk tid of P^T / A^T (row tid >> 3, cols 8 (tid & 7) ..)
-    unsigned short a_bits;  // a at step t = tid (tid < L)
-    unsigned char valid;
+    uint4 pt, at;  // chunk tid of P^T / A^T (row tid >> 3, cols 8 (tid & 7) ..)
   };
   // Global data of one slab, loaded a slab ahead.
   static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the v / dO / eps tiles
@@ -588,11 +588,6 @@ struct ChunkBwdGrad {
     const int u = tid & (L * L / 8 - 1);
     ht.pt = *reinterpret_cast<const uint4*>(p.cb.PqT + mat + 8 * u);
     ht.at = *reinterpret_cast<const uint4*>(p.cb.AtT + mat + 8 * u);
-    const int t = min(tid & 63, x.tl);
-    ht.a_bits = static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h];
-    const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a, p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-    const uint32_t mv = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + t, 0, 0));
-    ht.valid = p.mask ? static_cast<unsigned char>(mv) : 1;
   }
 
   __device__ static void put_chunks(Smem& sm, int tid, const Pf& f) {
@@ -638,7 +633,7 @@ struct ChunkBwdGrad {
                               f32x4 (&accK)[IH], HeadAcc& ac) {
     const Lanes q;
     const int lr = q.lr, lg = q.lg, ta = q.ta, tc0 = q.tc0, hw = q.hw;
-    // ---- this slab's H and dH' into LDS (both orientations), <dH', H>; v / dO / eps tiles
+    // ---- this slab's H and dH' into LDS ([i][v]), <dH', H>; v / dO / eps tiles
     if (has_blk) {
       const int i0 = x.i0, vv0 = x.vv0;
       float hx[4][4];
@@ -661,12 +656,6 @@ struct ChunkBwdGrad {
 #pragma unroll
         for (int e = 0; e < 4; ++e) ac.phdh = fmaf(hx[a][e], __uint_as_float(dv[a][e] << 16), ac.phdh);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint2*>(&sm.u.s.hi[(vv0 + e) * IS + i0]) = pack4_bf16(hx[0][e], hx[1][e], hx[2][e], hx[3][e]);
-        *reinterpret_cast<uint2*>(&sm.u.s.dhi[(vv0 + e) * IS + i0]) =
-            make_uint2(dv[0][e] | (dv[1][e] << 16), dv[2][e] | (dv[3][e] << 16));
-      }
     }
     put_chunks(sm, q.tid, pf);
     {  // the next slab: of this head, or the first of the next head (the last
@@ -679,14 +668,19 @@ struct ChunkBwdGrad {
     const bf16* vt = sm.u.s.vt[0];
     const bf16* dt = sm.u.s.vt[1];
     const bf16* et = sm.u.s.vt[2];
-    // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta)
+    // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta).
+    // The H and dH' operands (rows 32 kt + 8 lg .. + 7 of column 16 hw + lr)
+    // are read transposed from the [i][v] tiles.
     f32x4 kh = f4zero(), qh = f4zero(), kdt = f4zero();
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
-      const bf16x8 bh8 = load_bf16x8(&sm.u.s.hi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]);
+      const int o0 = (32 * kt + 8 * lg + (lr >> 2)) * VS + 16 * hw + 4 * (lr & 3);
+      const uint2 h0 = lds_read_tr16(&sm.u.s.hv[o0]), h1 = lds_read_tr16(&sm.u.s.hv[o0 + 4 * VS]);
+      const uint2 d0 = lds_read_tr16(&sm.u.s.dhv[o0]), d1 = lds_read_tr16(&sm.u.s.dhv[o0 + 4 * VS]);
+      const bf16x8 bh8 = as_bf16x8(make_uint4(h0.x, h0.y, h1.x, h1.y));
       kh = mfma16(ka[kt], bh8, kh);
       qh = mfma16(qa[kt], bh8, qh);
-      kdt = mfma16(load_bf16x8(&sm.u.s.dhi[(16 * hw + lr) * IS + 32 * kt + 8 * lg]), ka[kt], kdt);
+      kdt = mfma16(as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), ka[kt], kdt);
     }
     // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
     {
@@ -804,7 +798,7 @@ struct ChunkBwdGrad {
     Pf pf;
     prefetch(p, x, tid0, x.j * G, 0, pf);
     for (int hh = 0; hh < G; ++hh) {
-      const int h = x.j * G + hh;
+      const int h = x.j * G + hh, slot = hh % HB;
       const Lanes ln;
       HeadStart hs;
       load_start(p, x, ln.tid, h, hs);
@@ -892,7 +886,8 @@ struct ChunkBwdGrad {
         if ((q.tid & 7) == 0) sm.rs[t] = rsum;
       }
       __syncthreads();
-      // ---- column sums of the rectangle terms
+      // ---- column sums of the rectangle terms, and this head's inputs of the
+      // deferred gate-gradient section
       {
         const Lanes q;
         const int s = q.tid >> 3, r0 = 8 * (q.tid & 7);
@@ -900,43 +895,64 @@ struct ChunkBwdGrad {
 #pragma unroll
         for (int e = 0; e < 8; ++e) csum += sm.u.h.m[(r0 + e) * LP + s];
         csum = oct_sum(csum);
-        if ((q.tid & 7) == 0) sm.cs[s] = csum;
-      }
-      __syncthreads();
-      // ---- dl_t = e^{gL} <dH', H> + sum_{u<t} (a_u + cs_u - rs_u) + sum_{r>=t} b_r; da, db
-      if (tid0 < 64) {
-        const int t = tid0;
-        const bool in = t < Lc;
-        float hdh = 0.f;
+        if ((q.tid & 7) == 0) {
+          const bool in = s < Lc;
+          const float av = in ? sm.el[s] * sm.beta[s] * sm.rk[s] * (sm.pa[0][s] + sm.pa[1][s]) : 0.f;
+          sm.hu[slot][s] = av + csum - sm.rs[s];
+          sm.hb[slot][s] = in ? sm.bv[0][s] + sm.bv[1][s] : 0.f;
+          const float beta = sm.beta[s];
+          sm.hdb[slot][s] = (sm.pdb[0][s] + sm.pdb[1][s]) * beta * (1.f - beta);
+          sm.hell[slot][s] = sm.ell[s];
+        }
+        if (q.tid == 0) {
+          float hdh = 0.f;
 #pragma unroll
-        for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[i];
-        const float av = in ? sm.el[t] * sm.beta[t] * sm.rk[t] * (sm.pa[0][t] + sm.pa[1][t]) : 0.f;
-        const float bvv = in ? sm.bv[0][t] + sm.bv[1][t] : 0.f;
-        const float uv = av + sm.cs[t] - sm.rs[t];
-        float pre = __shfl_up(wave_incl_prefix(uv), 1);
-        if (t == 0) pre = 0.f;
-        const float suf = wave_incl_suffix(bvv);
-        const float ell = sm.ell[t];
-        const float dl = expf(ell) == 0.f ? 0.f : egl * hdh + pre + suf;
-        float da = 0.f, db = 0.f, dll = 0.f;
-        if (in) {
-          const size_t ri = (static_cast<size_t>(x.b) * d.T + x.t0 + t) * d.Hv + h;
-          if (ht.valid != 0) {
-            const float xa = __uint_as_float(static_cast<uint32_t>(ht.a_bits) << 16) + p.dt_bias[h];
-            da = xa <= kClamp ? dl * (-expf(p.A_log[h])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
-            const float beta = sm.beta[t];
-            db = (sm.pdb[0][t] + sm.pdb[1][t]) * beta * (1.f - beta);
+          for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[i];
+          sm.hdh[slot] = hdh;
+          sm.hegl[slot] = egl;
+        }
+      }
+      // ---- deferred section, one wave per value head of the batch:
+      // dl_t = e^{gL} <dH', H> + sum_{u<t} (a_u + cs_u - rs_u) + sum_{r>=t} b_r; da, db
+      if (slot == HB - 1 || hh == G - 1) {
+        __syncthreads();
+        const Lanes q;
+        const int hb0 = hh - slot, nh = slot + 1;
+        if (q.w < nh) {
+          const int k = q.w, hd = x.j * G + hb0 + k, t = q.l;
+          const bool in = t < Lc;
+          const int tc = min(t, x.tl);
+          const float av = __uint_as_float(
+              static_cast<uint32_t>(static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + hd]) << 16);
+          const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
+                                      p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+          const uint32_t mv = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0));
+          const bool valid = p.mask == nullptr || mv != 0;
+          float pre = __shfl_up(wave_incl_prefix(sm.hu[k][t]), 1);
+          if (t == 0) pre = 0.f;
+          const float suf = wave_incl_suffix(sm.hb[k][t]);
+          const float ell = sm.hell[k][t];
+          const float dl = expf(ell) == 0.f ? 0.f : sm.hegl[k] * sm.hdh[k] + pre + suf;
+          float da = 0.f, db = 0.f, dll = 0.f;
+          if (in && valid) {
+            const float xa = av + p.dt_bias[hd];
+            da = xa <= kClamp ? dl * (-expf(p.A_log[hd])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
+            db = sm.hdb[k][t];
             dll = dl != 0.f ? dl * ell : 0.f;
           }
-          static_cast<bf16*>(p.da)[ri] = bf16_of(da);
-          static_cast<bf16*>(p.db)[ri] = bf16_of(db);
-        }
-        const double sa = wave_sum_f64(static_cast<double>(dll));
-        const double sd = wave_sum_f64(static_cast<double>(da));
-        if (t == 0) {
-          const size_t pi = (static_cast<size_t>(x.b) * NC + c) * d.Hv + h;
-          p.part_dA[pi] = sa;
-          p.part_ddt[pi] = sd;
+          // steps past the end of the sequence fall outside the descriptors
+          const size_t r0 = (static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + hd;
+          const size_t nb = (static_cast<size_t>(Lc - 1) * d.Hv + 1) * 2;
+          const uint32_t ro = 2 * static_cast<uint32_t>(t * d.Hv);
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_of(da).x, make_rsrc(static_cast<bf16*>(p.da) + r0, nb), ro, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_of(db).x, make_rsrc(static_cast<bf16*>(p.db) + r0, nb), ro, 0, 0);
+          const double sa = wave_sum_f64(static_cast<double>(dll));
+          const double sd = wave_sum_f64(static_cast<double>(da));
+          if (t == 0) {
+            const size_t pi = (static_cast<size_t>(x.b) * NC + c) * d.Hv + hd;
+            p.part_dA[pi] = sa;
+            p.part_ddt[pi] = sd;
+          }
         }
       }
     }
