@@ -31,8 +31,10 @@ PAGES_FWD_BWD_MS = {256: 13.4, 2048: 149.8}
 # Kernels launched per step, in order, by kernel family.
 KERNELS = {
     "scan": ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd", "chunk_grad", "param_reduce"],
-    "chunk": ["chunk_prep_fwd", "chunk_fwd", "chunk_prep_bwd", "chunk_bwd_state", "chunk_bwd_grad",
-              "param_reduce"],
+    # the forward's chunk_prep also saves the backward's chunk matrices in the
+    # checkpoint buffer (gdn_dims.save, as in training), so the backward has
+    # no chunk_prep of its own
+    "chunk": ["chunk_prep", "chunk_fwd", "chunk_bwd_state", "chunk_bwd_grad", "param_reduce"],
 }
 # Algorithmic fp32 flops per state element-step (one (b, t, h, i, j)):
 #   scan_fwd   decay 1 mul, read u 1 fma, update 1 fma, read o 1 fma       = 7
@@ -56,9 +58,8 @@ def kernel_bytes(B, T, Hk, Hv, Dk, Dv, io, state0=False, dS_final=False):
     CK = max(math.ceil(T / 64) - 1, 0) * Sig
     s0 = Sig if state0 else 0
     return {
-        "chunk_prep_fwd": 2 * Q1 + 2 * A1 + Par,
+        "chunk_prep": 2 * Q1 + 2 * A1 + Par,
         "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + CK,
-        "chunk_prep_bwd": 2 * Q1 + 2 * A1 + Par,
         "chunk_bwd_state": Q1 + 2 * V1 + (Sig if dS_final else 0) + Sig,
         "chunk_bwd_grad": 2 * Q1 + 2 * V1 + A1 + CK + s0 + 2 * Q1 + 2 * A1,
         "param_reduce": Par,

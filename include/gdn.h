@@ -65,23 +65,37 @@ enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
  *          normwise), not bitwise.
  *   AUTO   CHUNK where it is built and T > 1, else SCAN.
  * Both produce the same checkpoint layout, so a checkpoint from one can be
- * used by the other. */
+ * used by the other (with save unset; see gdn_ckpt_elems). */
 enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SCAN = 1, GDN_ALGO_CHUNK = 2 };
 
 typedef struct gdn_dims {
   int64_t B, T, Hk, Hv, Dk, Dv; /* T >= 0; Hv % Hk == 0                     */
   int32_t dtype;                /* enum gdn_dtype                           */
   int32_t algo;                 /* enum gdn_algo                            */
+  int32_t save;                 /* CHUNK family only: nonzero = gdn_fwd also
+                                   saves the backward's chunk matrices in
+                                   the checkpoint buffer's tail, and gdn_bwd
+                                   uses them instead of recomputing them
+                                   (see gdn_ckpt_elems).  Ignored by SCAN.  */
 } gdn_dims;
 
 /* Supported sizes: Dk in {16, 32, 64, 128, 192, 256}; Dv a multiple of 8
  * with Dv <= 256 and (Dv <= 24 or Dv % 32 == 0). */
 
 /* Number of fp32 elements of the checkpoint buffer:
- * (ceil(T/64) - 1) * B * Hv * Dk * Dv  (0 when T <= 64). */
+ * (ceil(T/64) - 1) * B * Hv * Dk * Dv  (0 when T <= 64), the states; when
+ * d->save is set and the call runs the CHUNK family, plus a tail that gdn_fwd
+ * fills with the per-chunk matrices the backward needs (the in-chunk inverse
+ * and its transpose, the decayed key/key and query/key Gram matrices, the
+ * chunk's k and q transposed, the per-step chunk scalars: about
+ * B * Hv * ceil(T/64) * 14k + B * Hk * ceil(T/64) * Dk * 64 elements).  The
+ * tail's contents are private to the library.  A checkpoint written with save
+ * set is read only by a gdn_bwd with the same dims (including save); the
+ * state part keeps the layout given at gdn_fwd. */
 int gdn_ckpt_elems(const gdn_dims* d, size_t* out);
 
-/* Device workspace bytes needed by gdn_fwd / gdn_bwd for these dims. */
+/* Device workspace bytes needed by gdn_fwd / gdn_bwd for these dims (less
+ * with d->save set, which moves the chunk matrices into the checkpoints). */
 int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out);
 int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
 
@@ -95,7 +109,10 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
  *   state_out[B,Hv,Dk,Dv] fp32 (out); may alias state0 exactly (in-place
  *            decode); no other overlap between outputs and inputs is allowed
  *   ckpt     [ceil(T/64)-1, B,Hv,Dk,Dv] fp32 (out): ckpt[c-1] = state before
- *            step 64c.  NULL = not written (inference).  Required by gdn_bwd.
+ *            step 64c, followed by the saved chunk matrices when d->save is
+ *            set (gdn_ckpt_elems elements in all).  NULL = not written
+ *            (inference; GDN_ERR_INVALID_ARG when save applies).  Required
+ *            by gdn_bwd.
  *   ws       device workspace of at least gdn_fwd_workspace_bytes()
  */
 int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v,
@@ -109,7 +126,7 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v,
  * the checkpoints, deterministic reductions without atomics).
  *   q ... mask    the inputs given to gdn_fwd (same values)
  *   ckpt          the checkpoints gdn_fwd wrote for those inputs (may be NULL
- *                 only when T <= 64)
+ *                 only when T <= 64 and save is unset)
  *   dO            [B,T,Hv,Dv] dtype, cotangent of o
  *   dS_final      [B,Hv,Dk,Dv] fp32, cotangent of state_out; NULL = zeros
  *   dq, dk        [B,T,Hk,Dk] dtype (out)     dv [B,T,Hv,Dv] dtype (out)

@@ -30,7 +30,7 @@ EXPORTS = ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("Hk", ctypes.c_int64),
                 ("Hv", ctypes.c_int64), ("Dk", ctypes.c_int64), ("Dv", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("algo", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("algo", ctypes.c_int32), ("save", ctypes.c_int32)]
 
 
 class GdnError(RuntimeError):
@@ -69,9 +69,9 @@ def lib():
     return _lib
 
 
-def make_dims(B, T, Hk, Hv, Dk, Dv, dtype, algo=ALGO_AUTO) -> Dims:
+def make_dims(B, T, Hk, Hv, Dk, Dv, dtype, algo=ALGO_AUTO, save=False) -> Dims:
     dt = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}.get(dtype, dtype)
-    return Dims(B, T, Hk, Hv, Dk, Dv, dt, algo)
+    return Dims(B, T, Hk, Hv, Dk, Dv, dt, algo, 1 if save else 0)
 
 
 def _query(fn, d: Dims) -> int:
@@ -113,10 +113,21 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _dims_of(q, v, algo):
+def _dims_of(q, v, algo, save=False):
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
-    return make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, algo)
+    return make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, algo, save)
+
+
+def _alloc_ckpt(d, dev):
+    """The checkpoint buffer: [ceil(T/64)-1, B, Hv, Dk, Dv] fp32, or, when the
+    dims save the chunk matrices, a flat fp32 buffer of gdn_ckpt_elems
+    elements whose first part is that tensor."""
+    nslab = max((d.T + CHUNK - 1) // CHUNK - 1, 0)
+    nck = ckpt_elems(d)
+    if nck == nslab * d.B * d.Hv * d.Dk * d.Dv:
+        return torch.empty((nslab, d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+    return torch.empty((nck,), dtype=torch.float32, device=dev)
 
 
 def _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask):
@@ -138,10 +149,14 @@ def _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask):
 
 
 def fwd(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, need_ckpt=True,
-        state_out=None, algo=ALGO_AUTO):
+        state_out=None, algo=ALGO_AUTO, save=False):
     """Forward scan.  Returns (o, state_out, ckpt); ckpt is None when not
-    requested.  Pass state_out=state0 for an in-place state update."""
-    d = _dims_of(q, v, algo)
+    requested.  Pass state_out=state0 for an in-place state update.  With
+    save=True the chunk form also saves the backward's chunk matrices in the
+    checkpoint buffer (pass the same save to bwd)."""
+    d = _dims_of(q, v, algo, save)
+    if save and not need_ckpt:
+        raise ValueError("save=True needs the checkpoint buffer (need_ckpt=True)")
     _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask)
     dev = q.device
     o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
@@ -150,10 +165,7 @@ def fwd(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, need_ckpt=True
     else:
         _check(state_out, "state_out", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
     nck = ckpt_elems(d)
-    ckpt = None
-    if need_ckpt:
-        nslab = max((d.T + CHUNK - 1) // CHUNK - 1, 0)
-        ckpt = torch.empty((nslab, d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+    ckpt = _alloc_ckpt(d, dev) if need_ckpt else None
     wsb = fwd_workspace_bytes(d)
     ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
     rc = lib().gdn_fwd(ctypes.byref(d), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log), _p(dt_bias),
@@ -166,9 +178,10 @@ def fwd(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, need_ckpt=True
 
 
 def bwd(q, k, v, a, b, A_log, dt_bias, state0, mask, ckpt, dO, dS_final=None, *,
-        algo=ALGO_AUTO):
-    """VJP.  Returns dict(dq, dk, dv, da, db, dA_log, ddt_bias, dstate)."""
-    d = _dims_of(q, v, algo)
+        algo=ALGO_AUTO, save=False):
+    """VJP.  Returns dict(dq, dk, dv, da, db, dA_log, ddt_bias, dstate).
+    `save` must match the fwd call that wrote ckpt."""
+    d = _dims_of(q, v, algo, save)
     _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask)
     dev = q.device
     _check(dO, "dO", (d.B, d.T, d.Hv, d.Dv), q.dtype, dev)
@@ -202,7 +215,7 @@ class GatedDeltaRule(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, a, b, A_log, dt_bias, state0, mask=None):
-        o, st, ck = fwd(q, k, v, a, b, A_log, dt_bias, state0, mask)
+        o, st, ck = fwd(q, k, v, a, b, A_log, dt_bias, state0, mask, save=True)
         ctx.save_for_backward(q, k, v, a, b, A_log, dt_bias, state0, mask, ck)
         return o, st
 
@@ -210,7 +223,7 @@ class GatedDeltaRule(torch.autograd.Function):
     def backward(ctx, dO, dS):
         q, k, v, a, b, A_log, dt_bias, state0, mask, ck = ctx.saved_tensors
         g = bwd(q, k, v, a, b, A_log, dt_bias, state0, mask, ck, dO.contiguous(),
-                None if dS is None else dS.contiguous())
+                None if dS is None else dS.contiguous(), save=True)
         return (g["dq"], g["dk"], g["dv"], g["da"], g["db"], g["dA_log"], g["ddt_bias"],
                 g["dstate"] if state0 is not None else None, None)
 
@@ -221,19 +234,20 @@ class Plan:
     call costs one C-ABI call (used by the benchmark's timed loop).
 
     `t` maps q, k, v, a, b, A_log, dt_bias, state0, mask, dO, dS_final to
-    device tensors (state0, mask, dS_final may be None)."""
+    device tensors (state0, mask, dS_final may be None).  save: the forward
+    saves the chunk matrices for the backward (as in training)."""
 
-    def __init__(self, t, algo=ALGO_AUTO, stream=None):
+    def __init__(self, t, algo=ALGO_AUTO, stream=None, save=True):
         q, v = t["q"], t["v"]
-        self.d = d = _dims_of(q, v, algo)
+        self.d = d = _dims_of(q, v, algo, save)
         _check_inputs(d, q, k=t["k"], v=v, a=t["a"], b=t["b"], A_log=t["A_log"],
                       dt_bias=t["dt_bias"], state0=t["state0"], mask=t["mask"])
         dev = q.device
         self.t = t
         self.o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
         self.state_out = torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
-        nslab = max((d.T + CHUNK - 1) // CHUNK - 1, 0)
-        self.ckpt = torch.empty((nslab, d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+        self.ckpt = _alloc_ckpt(d, dev)
+        nck = self.ckpt.numel()
         self.g = dict(dq=torch.empty_like(q), dk=torch.empty_like(t["k"]), dv=torch.empty_like(v),
                       da=torch.empty_like(t["a"]), db=torch.empty_like(t["b"]),
                       dA_log=torch.empty((d.Hv,), dtype=torch.float32, device=dev),
@@ -245,7 +259,7 @@ class Plan:
         st = stream if stream is not None else torch.cuda.current_stream(dev)
         self.stream = st
         sp = ctypes.c_void_p(st.cuda_stream)
-        ck = _p(self.ckpt) if nslab else None
+        ck = _p(self.ckpt) if nck else None
         ins = [_p(t[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state0", "mask")]
         self._fargs = (ctypes.byref(d), *ins, _p(self.o), _p(self.state_out), ck,
                        _p(self.ws_f), fws, sp)

@@ -20,7 +20,41 @@ struct Layout {
   size_t total;
 };
 
-Layout layout(const Dims& d, bool bwd, bool chunk) {
+// The chunk matrices kept in the checkpoint buffer's tail under gdn_dims.save
+// (offsets in fp32 elements from the tail's start, 256-byte aligned).
+struct Saved {
+  size_t Tx, TxT, AtT, PqT, KT, QT, SC, total;
+};
+
+Saved saved_layout(const Dims& d) {
+  Saved S{};
+  size_t off = 0;
+  auto take = [&](size_t nfloat) {
+    size_t o = off;
+    off += align_up(nfloat * sizeof(float)) / sizeof(float);
+    return o;
+  };
+  const size_t nc = d.nchunk();
+  const size_t mats = static_cast<size_t>(d.B) * d.Hv * nc * 64 * 64;  // bf16 each
+  const size_t kts = static_cast<size_t>(d.B) * d.Hk * nc * d.Dk * 64;
+  S.Tx = take((mats + 1) / 2);
+  S.TxT = take((mats + 1) / 2);
+  S.AtT = take((mats + 1) / 2);
+  S.PqT = take((mats + 1) / 2);
+  S.KT = take((kts + 1) / 2);
+  S.QT = take((kts + 1) / 2);
+  S.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
+  S.total = off;
+  return S;
+}
+
+size_t ckpt_state_elems(const Dims& d) {
+  const size_t nc = d.nchunk();
+  return nc > 1 ? (nc - 1) * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv : 0;
+}
+
+// Workspace layout.  `saved`: the chunk matrices live in the checkpoint tail.
+Layout layout(const Dims& d, bool bwd, bool chunk, bool saved) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t nfloat) {
@@ -55,15 +89,17 @@ Layout layout(const Dims& d, bool bwd, bool chunk) {
     const size_t nc = d.nchunk();
     const size_t mats = static_cast<size_t>(d.B) * d.Hv * nc * 64 * 64;  // bf16 each
     const size_t kts = static_cast<size_t>(d.B) * d.Hk * nc * d.Dk * 64;
-    L.Tx = take((mats + 1) / 2);
-    L.Mq = take((mats + 1) / 2);
-    L.KT = take((kts + 1) / 2);
-    L.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
-    if (bwd) {
-      L.TxT = take((mats + 1) / 2);
-      L.AtT = take((mats + 1) / 2);
-      L.PqT = take((mats + 1) / 2);
-      L.QT = take((kts + 1) / 2);
+    if (!bwd) L.Mq = take((mats + 1) / 2);
+    if (!saved) {
+      L.Tx = take((mats + 1) / 2);
+      L.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
+      if (bwd) {
+        L.TxT = take((mats + 1) / 2);
+        L.AtT = take((mats + 1) / 2);
+        L.PqT = take((mats + 1) / 2);
+        L.KT = take((kts + 1) / 2);
+        L.QT = take((kts + 1) / 2);
+      }
     }
   }
   L.total = off;
@@ -134,20 +170,35 @@ bool use_chunk(const gdn_dims* p) {
 }
 bool use_chunk_fwd(const gdn_dims* p) { return use_chunk(p); }
 bool use_chunk_bwd(const gdn_dims* p) { return use_chunk(p); }
+// The chunk matrices go through the checkpoint tail.
+bool use_saved(const gdn_dims* p) { return p->save != 0 && use_chunk(p); }
 
 gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   gdn::ChunkBufs cb{};
   cb.Tx = at<gdn::bf16>(ws, L.Tx);
-  cb.Mq = at<gdn::bf16>(ws, L.Mq);
-  cb.KT = at<gdn::bf16>(ws, L.KT);
   cb.sc = at<float>(ws, L.SC);
+  if (!bwd) cb.Mq = at<gdn::bf16>(ws, L.Mq);
   if (bwd) {
     cb.TxT = at<gdn::bf16>(ws, L.TxT);
     cb.AtT = at<gdn::bf16>(ws, L.AtT);
     cb.PqT = at<gdn::bf16>(ws, L.PqT);
+    cb.KT = at<gdn::bf16>(ws, L.KT);
     cb.QT = at<gdn::bf16>(ws, L.QT);
   }
   return cb;
+}
+
+// The saved matrices in the checkpoint buffer's tail (every pointer but Mq).
+void saved_bufs(const Dims& d, const float* ckpt, gdn::ChunkBufs& cb) {
+  const Saved S = saved_layout(d);
+  float* tail = const_cast<float*>(ckpt) + align_up(ckpt_state_elems(d) * sizeof(float)) / sizeof(float);
+  cb.Tx = reinterpret_cast<gdn::bf16*>(tail + S.Tx);
+  cb.TxT = reinterpret_cast<gdn::bf16*>(tail + S.TxT);
+  cb.AtT = reinterpret_cast<gdn::bf16*>(tail + S.AtT);
+  cb.PqT = reinterpret_cast<gdn::bf16*>(tail + S.PqT);
+  cb.KT = reinterpret_cast<gdn::bf16*>(tail + S.KT);
+  cb.QT = reinterpret_cast<gdn::bf16*>(tail + S.QT);
+  cb.sc = tail + S.SC;
 }
 
 gdn::StepScalars scalars(void* ws, const Layout& L) {
@@ -164,8 +215,8 @@ int gdn_ckpt_elems(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  const size_t nc = dd.nchunk();
-  *out = nc > 1 ? (nc - 1) * dd.B * dd.Hv * static_cast<size_t>(dd.Dk) * dd.Dv : 0;
+  *out = use_saved(d) ? align_up(ckpt_state_elems(dd) * sizeof(float)) / sizeof(float) + saved_layout(dd).total
+                      : ckpt_state_elems(dd);
   return GDN_OK;
 }
 
@@ -174,7 +225,7 @@ int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = layout(dd, false, use_chunk_fwd(d)).total;
+  *out = layout(dd, false, use_chunk_fwd(d), use_saved(d)).total;
   return GDN_OK;
 }
 
@@ -183,7 +234,7 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = layout(dd, true, use_chunk_bwd(d)).total;
+  *out = layout(dd, true, use_chunk_bwd(d), use_saved(d)).total;
   return GDN_OK;
 }
 
@@ -197,16 +248,21 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   const bool has_t = dd.T > 0;
   if (!A_log || !dt_bias || !state_out) return GDN_ERR_INVALID_ARG;
   if (has_t && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
+  if (use_saved(d) && !ckpt) return GDN_ERR_INVALID_ARG;  // the matrices are saved there
   const bool chunk = use_chunk_fwd(d);
-  const Layout L = layout(dd, false, chunk);
+  const Layout L = layout(dd, false, chunk, use_saved(d));
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const gdn::StepScalars s = scalars(ws, L);
 
   if (chunk) {
-    const gdn::ChunkBufs cb = chunk_bufs(ws, L, false);
-    gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 0};
+    gdn::ChunkBufs cb = chunk_bufs(ws, L, false);
+    // under save chunk_prep also writes the backward's matrices, into the
+    // checkpoint tail
+    const bool save = use_saved(d);
+    if (save) saved_bufs(dd, ckpt, cb);
+    gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, save ? 2 : 0};
     if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
     gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, ckpt};
     if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
@@ -231,9 +287,9 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   if (!A_log || !dt_bias || !dA_log || !ddt_bias || !dstate) return GDN_ERR_INVALID_ARG;
   if (has_t && (!q || !k || !v || !a || !b || !dO || !dq || !dk || !dv || !da || !db))
     return GDN_ERR_INVALID_ARG;
-  if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
+  if ((dd.nchunk() > 1 || use_saved(d)) && !ckpt) return GDN_ERR_INVALID_ARG;
   const bool chunk = use_chunk_bwd(d);
-  const Layout L = layout(dd, true, chunk);
+  const Layout L = layout(dd, true, chunk, use_saved(d));
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -242,9 +298,13 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   gdn::ParamReduceArgs ra{dd.B, dd.nchunk(), dd.Hv, at<double>(ws, L.pdA), at<double>(ws, L.pdt),
                           dA_log, ddt_bias};
   if (chunk) {
-    const gdn::ChunkBufs cb = chunk_bufs(ws, L, true);
-    gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 1};
-    if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    gdn::ChunkBufs cb = chunk_bufs(ws, L, true);
+    if (use_saved(d)) {  // the forward saved the chunk matrices
+      saved_bufs(dd, ckpt, cb);
+    } else {
+      gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 1};
+      if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    }
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
                          at<gdn::bf16>(ws, L.E), at<gdn::bf16>(ws, L.dHend),
                          dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};

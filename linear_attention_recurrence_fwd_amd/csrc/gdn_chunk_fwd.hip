@@ -183,9 +183,10 @@ struct ChunkPrep {
         sm.rk[t] = in ? 1.f / sqrtf(kk + kNormEps) : 0.f;
         sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(aqq[r] + kNormEps) : 0.f;
       }
+    const bool fwd_out = p.bwd != 1, bwd_out = p.bwd != 0;
     // ---- raw k and q of the chunk, transposed, for the backward (written
     // once per key head)
-    if (first && p.bwd) {
+    if (first && bwd_out) {
       const size_t base = (static_cast<size_t>(b * d.Hk + j) * NC + c) * DK * L;
       store_transposed(sm.u.r.k, p.cb.KT + base, tid);
       store_transposed(sm.u.r.q, p.cb.QT + base, tid);
@@ -229,15 +230,15 @@ struct ChunkPrep {
           pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
         }
         sm.u.m.np[t * L + (s & 3) * (L / 4) + (s >> 2)] = nv;
-        if (p.bwd) {
+        if (bwd_out) {
           sm.u.m.st[s * SP + t] = at;  // A^T
-          mq[ct][r] = pq;
         } else {
           sm.u.m.st[t * SP + s] = pq * sm.beta[s];  // Mq
         }
+        mq[ct][r] = pq;
       }
     __syncthreads();
-    if (p.bwd) {
+    if (bwd_out) {
       store_mat(sm, p.cb.AtT + mat, tid);
       __syncthreads();
 #pragma unroll
@@ -246,6 +247,18 @@ struct ChunkPrep {
         for (int r = 0; r < 4; ++r) sm.u.m.st[(16 * ct + lr) * SP + 16 * w + 4 * lg + r] = mq[ct][r];  // P^T
       __syncthreads();
       store_mat(sm, p.cb.PqT + mat, tid);
+      if (fwd_out) {
+        __syncthreads();
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = 16 * ct + lr;
+            sm.u.m.st[(16 * w + 4 * lg + r) * SP + s] = mq[ct][r] * sm.beta[s];  // Mq
+          }
+        __syncthreads();
+        store_mat(sm, p.cb.Mq + mat, tid);
+      }
     } else {
       store_mat(sm, p.cb.Mq + mat, tid);
     }
@@ -280,7 +293,7 @@ struct ChunkPrep {
     }
     __syncthreads();
     store_mat(sm, p.cb.Tx + mat, tid);
-    if (p.bwd) {  // Tx^T: row r is column r of the staged Tx
+    if (bwd_out) {  // Tx^T: row r is column r of the staged Tx
       for (int u = tid; u < L * L / 8; u += NT) {
         const int r = u >> 3, c8 = 8 * (u & 7);
         float v[8];

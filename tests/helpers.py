@@ -48,14 +48,14 @@ def relerr(x, ref):
     return float(num / den)
 
 
-def gpu_fwd(t, algo=binding.ALGO_AUTO, need_ckpt=True):
+def gpu_fwd(t, algo=binding.ALGO_AUTO, need_ckpt=True, save=False):
     return binding.fwd(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"],
-                       t["state0"], t["mask"], need_ckpt=need_ckpt, algo=algo)
+                       t["state0"], t["mask"], need_ckpt=need_ckpt, algo=algo, save=save)
 
 
-def gpu_bwd(t, ckpt, algo=binding.ALGO_AUTO):
+def gpu_bwd(t, ckpt, algo=binding.ALGO_AUTO, save=False):
     return binding.bwd(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"],
-                       t["state0"], t["mask"], ckpt, t["dO"], t["dS_final"], algo=algo)
+                       t["state0"], t["mask"], ckpt, t["dO"], t["dS_final"], algo=algo, save=save)
 
 
 def oracle_all(case, nthreads=8):

@@ -122,3 +122,39 @@ def test_chunk_unsupported(dtype, Dk, Dv):
     with pytest.raises(B.GdnError) as e:
         B.fwd_workspace_bytes(B.make_dims(1, 128, 2, 4, Dk, Dv, dtype, B.ALGO_CHUNK))
     assert e.value.code == 2
+
+
+def test_saved_chunk_matrices_sizes():
+    """gdn_dims.save (chunk family) adds the saved chunk matrices to the
+    checkpoint buffer and takes them out of the workspaces; the scan family
+    ignores it."""
+    plain = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_BF16)
+    saved = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_BF16, save=True)
+    states = 31 * 64 * 192 * 128
+    mats = 64 * 32 * 64 * 64 // 2        # one bf16 64x64 matrix per (head, chunk), in fp32 elements
+    kts = 16 * 32 * 192 * 64 // 2
+    scal = 64 * 32 * 12 * 64
+    assert B.ckpt_elems(plain) == states
+    assert B.ckpt_elems(saved) == states + 4 * mats + 2 * kts + scal
+    assert B.bwd_workspace_bytes(saved) < B.bwd_workspace_bytes(plain)
+    assert B.fwd_workspace_bytes(saved) < B.fwd_workspace_bytes(plain)
+    f32 = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_F32, save=True)
+    assert B.ckpt_elems(f32) == states
+    assert B.bwd_workspace_bytes(f32) == B.bwd_workspace_bytes(B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_F32))
+    one = B.make_dims(1, 1, 16, 64, 192, 128, B.GDN_BF16, B.ALGO_CHUNK, save=True)
+    assert B.ckpt_elems(one) > 0      # no states, only the saved matrices
+
+
+def test_saved_needs_the_checkpoint_buffer():
+    lib = B.lib()
+    d = B.make_dims(1, 32, 2, 4, 64, 32, B.GDN_BF16, B.ALGO_CHUNK, save=True)
+    p = _fake(13)
+    need = B.fwd_workspace_bytes(d)
+    args = list(p)
+    args[11] = None  # ckpt
+    assert lib.gdn_fwd(ctypes.byref(d), *args, need, None) == 1
+    need = B.bwd_workspace_bytes(d)
+    p = _fake(21)
+    args = list(p)
+    args[9] = None  # ckpt (T <= 64, but the saved matrices live there)
+    assert lib.gdn_bwd(ctypes.byref(d), *args, need, None) == 1
