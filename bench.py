@@ -82,6 +82,28 @@ def method_bytes(B, T, Hk, Hv, Dk, Dv, io, mask=False, dS_final=False):
     return fwd, bwd
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_9b_t2048.txt")
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` at the default workload, from the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by the copy probe), or
+    None when there is none or the library source has changed since."""
+    from linear_attention_recurrence_fwd_amd.srcsha import source_sha
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = next((l.split()[1] for l in lines if l.startswith("source_sha ")), None)
+    if sha != source_sha():
+        return None
+    for l in lines:
+        f = l.split()
+        if f and f[0] == kernel and len(f) == 6:
+            return int(float(f[5]))
+    return None
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch already loaded."""
 
@@ -204,9 +226,10 @@ def bench_train(args, torch, binding, inputs):
         kb = kernel_bytes(B, T, Hk, Hv, Dk, Dv, 2, state0=t["state0"] is not None,
                           dS_final=t["dS_final"] is not None)
         achieved = kb[dom] / (per_kernel[dom] / 1e3) / 1e9
+        traffic = recorded_traffic(dom) if T == 2048 else None
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                    "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                    "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
                     "bytes_per_launch": kb[dom], "avg_launch_ms": round(per_kernel[dom], 4)}
     else:
         # fp32 vector roofline of the slowest kernel, over its algorithmic flops
