@@ -470,6 +470,7 @@ struct ChunkBwdGrad {
   static constexpr int TS = L + 8;       // bf16 row stride of [v][t] tiles and Wq rows
   static constexpr int WS = 2 * L + 8;   // bf16 row stride of [Wk1 | Wk2] rows
   static constexpr int FS = DK + 4;      // fp32 row stride of the final accumulators
+  static constexpr int WR = L + 8;       // fp32 row stride of the weight sums
   static constexpr int NB = (DK / 4) * (NS / 4);  // 4x4 blocks of one slab (<= NTG)
   static_assert(NB <= NTG, "one block per thread");
   struct Slab {
@@ -503,7 +504,10 @@ struct ChunkBwdGrad {
   static constexpr int HB = 4;  // value heads per batch of the deferred gate-gradient section (one wave each)
   struct Smem {
     alignas(16) Big u;
-    float wsq[L * LP], ws1[L * LP], ws2[L * LP];  // fp32 sums over the group's heads of Wq, Wk1, Wk2
+    // fp32 sums over the group's heads of Wq, Wk1, Wk2 (rows of WR: 16-byte aligned)
+    alignas(16) float wsq[L * WR];
+    alignas(16) float ws1[L * WR];
+    alignas(16) float ws2[L * WR];
     float rk[L], rq[L];
     float gam[L], eg[L], el[L], beta[L], ell[L];
     float bv[2][L], pa[2][L], pdb[2][L], rs[L];
@@ -775,7 +779,7 @@ struct ChunkBwdGrad {
       sm.rk[tid0] = scc[SC_RK * L + tid0];
       sm.rq[tid0] = scc[SC_RQ * L + tid0];
     }
-    for (int e = tid0; e < L * LP; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
+    for (int e = tid0; e < L * WR; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
     f32x4 accQ[IH], accK[IH];
 #pragma unroll
     for (int k = 0; k < IH; ++k) accQ[k] = accK[k] = f4zero();
@@ -862,8 +866,16 @@ struct ChunkBwdGrad {
         const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
         const bool tv = t < Lc;
         const float gt = sm.gam[t], bt = sm.beta[t];
+        float* pw[3] = {&sm.wsq[t * WR + s0], &sm.ws1[t * WR + s0], &sm.ws2[t * WR + s0]};
+        float wv[3][8];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          const float4 lo = *reinterpret_cast<const float4*>(pw[a]), hi = *reinterpret_cast<const float4*>(pw[a] + 4);
+          wv[a][0] = lo.x; wv[a][1] = lo.y; wv[a][2] = lo.z; wv[a][3] = lo.w;
+          wv[a][4] = hi.x; wv[a][5] = hi.y; wv[a][6] = hi.z; wv[a][7] = hi.w;
+        }
         float rsum = 0.f;
-#pragma unroll 2
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int s = s0 + e;
           const bool ok = tv && s < Lc;
@@ -873,14 +885,17 @@ struct ChunkBwdGrad {
           const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
           // P[t][s] = P^T[s][t], A[t][s] = A^T[s][t] (decays and norms included)
           const float ptv = to_f32(sm.u.h.pt[s * TS + t]), atv = to_f32(sm.u.h.at[s * TS + t]);
-          if (ok) {
-            if (s <= t) sm.wsq[t * LP + s] += dec * bs * doxts * rks;
-            if (s >= t) sm.ws1[t * LP + s] += dec * bt * doxst * sm.rq[s];
-            if (s != t) sm.ws2[t * LP + s] += -bt * bs * dec * (s < t ? xest : xets) * rks;
-          }
+          if (ok && s <= t) wv[0][e] += dec * bs * doxts * rks;
+          if (ok && s >= t) wv[1][e] += dec * bt * doxst * sm.rq[s];
+          if (ok && s != t) wv[2][e] += -bt * bs * dec * (s < t ? xest : xets) * rks;
           const float m = ok && s < t ? bs * (ptv * doxts - bt * atv * xest) : 0.f;
           sm.u.h.m[t * LP + s] = m;
           rsum += m;
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          *reinterpret_cast<float4*>(pw[a]) = make_float4(wv[a][0], wv[a][1], wv[a][2], wv[a][3]);
+          *reinterpret_cast<float4*>(pw[a] + 4) = make_float4(wv[a][4], wv[a][5], wv[a][6], wv[a][7]);
         }
         rsum = oct_sum(rsum);
         if ((q.tid & 7) == 0) sm.rs[t] = rsum;
@@ -965,9 +980,9 @@ struct ChunkBwdGrad {
       uint32_t w0[4], w1[4], w2[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        w0[e >> 1] = pack2_bf16(sm.wsq[t * LP + s0 + e], sm.wsq[t * LP + s0 + e + 1]);
-        w1[e >> 1] = pack2_bf16(sm.ws1[t * LP + s0 + e], sm.ws1[t * LP + s0 + e + 1]);
-        w2[e >> 1] = pack2_bf16(sm.ws2[t * LP + s0 + e], sm.ws2[t * LP + s0 + e + 1]);
+        w0[e >> 1] = pack2_bf16(sm.wsq[t * WR + s0 + e], sm.wsq[t * WR + s0 + e + 1]);
+        w1[e >> 1] = pack2_bf16(sm.ws1[t * WR + s0 + e], sm.ws1[t * WR + s0 + e + 1]);
+        w2[e >> 1] = pack2_bf16(sm.ws2[t * WR + s0 + e], sm.ws2[t * WR + s0 + e + 1]);
       }
       *reinterpret_cast<uint4*>(&sm.u.w.wq[t * TS + s0]) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
       *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + s0]) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
