@@ -326,7 +326,7 @@ def bench_decode(args, torch, binding, inputs):
         "config": {"workload": "gated delta rule decode, 64 single-token calls per step",
                    "B": case.B, "Hk": case.Hk, "Hv": case.Hv, "Dk": case.Dk, "Dv": case.Dv,
                    "io_dtype": "bf16"},
-        "roofline": {"bound": "hbm", "kernel": "scan_fwd+prep (one call)",
+        "roofline": {"bound": "hbm", "kernel": "decode (one call)",
                      "achieved": round(call_bytes / (per_call / 1e3) / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(frac, 4),
                      "traffic": None, "bytes_per_launch": call_bytes,

@@ -268,6 +268,11 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
     return GDN_OK;
   }
+  if (dd.T == 1 && gdn::decode_supported(dd.Dk, dd.Dv)) {  // one token: the fused single-step kernel
+    gdn::DecodeArgs da{dd, q, k, v, a, b, A_log, dt_bias, state0, mask, o, state_out};
+    if (!launch(st, [&] { return gdn::launch_decode(da, bf, st); })) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   gdn::PrepArgs pa{dd, q, k, a, b, A_log, dt_bias, mask, s};
   if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt};

@@ -166,6 +166,21 @@ struct ParamReduceArgs {
   float *dA_log, *ddt_bias;
 };
 
+// Single-step forward (T = 1), fused prep and update.
+struct DecodeArgs {
+  Dims d;
+  const void *q, *k, *v, *a, *b;
+  const float *A_log, *dt_bias;
+  const float* state0;  // may be null; may alias state_out exactly
+  const uint8_t* mask;
+  void* o;
+  float* state_out;
+};
+inline bool decode_supported(int Dk, int Dv) {
+  return (Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256) && Dv % 32 == 0 && Dv <= 256;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);
