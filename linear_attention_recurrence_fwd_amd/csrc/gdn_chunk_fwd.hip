@@ -16,8 +16,8 @@
 // Kernels:
 //   chunk_prep  one workgroup per (chunk, batch, value head): the chunk's k and
 //               q rows staged in LDS by coalesced loads, K K^T and Q K^T on
-//               MFMA, the gates and gamma by a wave scan, N, Tx by forward
-//               substitution (fp32), Mq and the per-step chunk scalars; the
+//               MFMA, the gates and gamma by a wave scan, N, Tx by blocked
+//               forward substitution (fp32), Mq and the per-step chunk scalars; the
 //               first value head of each key head also writes K^T.  With
 //               `bwd` set it writes the transposes the backward needs instead
 //               of Mq, and Q^T.  All outputs go to the workspace (bf16 /
@@ -44,7 +44,7 @@ constexpr int NT = 256;
 template <int DK>
 struct ChunkPrep {
   static constexpr int RS = DK + 8;  // bf16 row stride of the staged k / q rows (conflict-free operand reads)
-  static constexpr int SP = L + 4;   // fp32 row stride of the staging matrix (16-byte aligned rows)
+  static constexpr int SP = L + 4;   // fp32 row stride of N and the staging matrix (16-byte aligned rows)
   static constexpr int NLD = L * DK / 8 / NT;  // 16-byte pieces of one of k, q per thread
   static_assert(L * DK / 8 % NT == 0, "whole pieces per thread");
   struct Rows {
@@ -52,7 +52,7 @@ struct ChunkPrep {
     bf16 q[L * RS];
   };
   struct Mats {
-    float np[L * L];   // N, row t holding N[t][4m + q] at q L/4 + m
+    float nf[L * SP];  // N; its diagonal 16x16 blocks are replaced by their inverses
     float st[L * SP];  // staging of the matrices written out
   };
   union Big {
@@ -85,6 +85,52 @@ struct ChunkPrep {
         wv[e] = static_cast<uint32_t>(rows[(t8 + 2 * e) * RS + i].x) |
                 (static_cast<uint32_t>(rows[(t8 + 2 * e + 1) * RS + i].x) << 16);
       *reinterpret_cast<uint4*>(dst + static_cast<size_t>(i) * L + t8) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+  }
+
+  // Tx = (I + N)^-1 in 16x16 blocks (fp32).  N is strictly lower triangular,
+  // so Tx is unit lower triangular with diagonal blocks D_i = (I + N_ii)^-1
+  // and, for i > j, Tx_ij = -D_i (sum over j <= k < i of N_ik Tx_kj) (the
+  // block rows of (I + N) Tx = I).  Wave w inverts D_w by forward
+  // substitution -- lane 4c + q holds rows 4m + q of column c -- and writes it
+  // over N_ww.
+  __device__ static void invert_diagonal_block(Smem& sm, int w, int l) {
+    const int c = l >> 2, q = l & 3;
+    float* nb = &sm.u.m.nf[16 * w * SP + 16 * w];
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      // rows s >= t of x are still zero, and N[t][s] = 0 for s >= t
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < (t + 3) / 4; ++m) acc = fmaf(nb[t * SP + 4 * m + q], x[m], acc);
+      const float xt = (t == c ? 1.f : 0.f) - quad_sum(acc);
+      if ((t & 3) == q) x[t >> 2] = xt;
+    }
+    wave_lds_sync();  // every lane's reads of N_ww are done
+#pragma unroll
+    for (int m = 0; m < 4; ++m) nb[(4 * m + q) * SP + c] = x[m];
+  }
+
+  // Block column j < 3 of Tx below the diagonal, top to bottom, on fp32 MFMA,
+  // into the staging matrix.  The partial sums pass through the (zero, unused)
+  // block (0, j + 1) of nf to become an operand.
+  __device__ static void lower_blocks(Smem& sm, int j) {
+    const int l = threadIdx.x & 63, lr = l & 15, lg = l >> 4;
+    float* nf = sm.u.m.nf;
+    float* st = sm.u.m.st;
+    float* part = &nf[16 * (j + 1)];
+    for (int i = j + 1; i < 4; ++i) {
+      f32x4 acc = f4zero();
+      acc = mm16f(acc, &nf[16 * i * SP + 16 * j], SP, &nf[16 * j * SP + 16 * j], SP);
+      for (int k = j + 1; k < i; ++k) acc = mm16f(acc, &nf[16 * i * SP + 16 * k], SP, &st[16 * k * SP + 16 * j], SP);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(4 * lg + r) * SP + lr] = acc[r];
+      wave_lds_sync();
+      const f32x4 tij = mm16f(f4zero(), &nf[16 * i * SP + 16 * i], SP, part, SP);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[(16 * i + 4 * lg + r) * SP + 16 * j + lr] = -tij[r];
+      wave_lds_sync();  // Tx_ij is an operand of the next block; part is rewritten
     }
   }
 
@@ -229,7 +275,7 @@ struct ChunkPrep {
           }
           pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
         }
-        sm.u.m.np[t * L + (s & 3) * (L / 4) + (s >> 2)] = nv;
+        sm.u.m.nf[t * SP + s] = nv;
         if (bwd_out) {
           sm.u.m.st[s * SP + t] = at;  // A^T
         } else {
@@ -238,6 +284,7 @@ struct ChunkPrep {
         mq[ct][r] = pq;
       }
     __syncthreads();
+    invert_diagonal_block(sm, w, l);
     if (bwd_out) {
       store_mat(sm, p.cb.AtT + mat, tid);
       __syncthreads();
@@ -263,33 +310,21 @@ struct ChunkPrep {
       store_mat(sm, p.cb.Mq + mat, tid);
     }
 
-    // ---- Tx = (I + N)^-1 by forward substitution in fp32: column `col`,
-    // four threads per column, thread q holding the entries at rows 4m + q.
-    // Only rows above step t enter step t, so step t reads ceil(t/4) entries.
-    {
-      const int col = tid >> 2, q = tid & 3;
-      float x[L / 4];
+    // ---- the blocks of Tx below the diagonal (the diagonal ones are in nf)
+    __syncthreads();  // the staging matrix is free (P^T / Mq stored); the D_i are visible
+    if (w < 3) {
+      lower_blocks(sm, w);
+    } else {  // diagonal blocks into the staging matrix, zeros above them
 #pragma unroll
-      for (int m = 0; m < L / 4; ++m) x[m] = 0.f;
-      const float* nrow = &sm.u.m.np[q * (L / 4)];
+      for (int blk = 0; blk < 16; ++blk) {
+        const int bi = blk >> 2, bj = blk & 3;
+        if (bi > bj) continue;
 #pragma unroll
-      for (int t = 0; t < L; ++t) {
-        const int nm = (t + 3) / 4;  // entries m with 4m + q < t possible
-        float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-        for (int m4 = 0; m4 < nm; m4 += 4) {
-          const float4 nv = *reinterpret_cast<const float4*>(nrow + t * L + m4);
-          p0 = fmaf(nv.x, x[m4], p0);
-          if (m4 + 1 < nm) p1 = fmaf(nv.y, x[m4 + 1], p1);
-          if (m4 + 2 < nm) p0 = fmaf(nv.z, x[m4 + 2], p0);
-          if (m4 + 3 < nm) p1 = fmaf(nv.w, x[m4 + 3], p1);
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * bi + 4 * e + (l >> 4), col = 16 * bj + (l & 15);
+          sm.u.m.st[row * SP + col] = bi == bj ? sm.u.m.nf[row * SP + col] : 0.f;
         }
-        const float xt = (t == col ? 1.f : 0.f) - quad_sum(p0 + p1);
-        if ((t & 3) == q) x[t >> 2] = xt;
       }
-      __syncthreads();  // the staging matrix is free (P^T / Mq stored) and N is read
-#pragma unroll
-      for (int m = 0; m < L / 4; ++m) sm.u.m.st[(4 * m + q) * SP + col] = x[m];
     }
     __syncthreads();
     store_mat(sm, p.cb.Tx + mat, tid);

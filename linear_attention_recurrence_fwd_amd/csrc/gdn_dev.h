@@ -106,6 +106,19 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 __device__ __forceinline__ f32x4 f4zero() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// fp32 matrix cores (v_mfma_f32_16x16x4f32): D = A (16x4) * B (4x16) + C with
+// lane l supplying A[l%16][l/16] and B[l/16][l%16] and holding D as above.
+__device__ __forceinline__ f32x4 mfma16f(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// acc + A B for 16x16 fp32 tiles in LDS (row strides as, bs), 4 MFMAs.
+__device__ __forceinline__ f32x4 mm16f(f32x4 acc, const float* A, int as, const float* B, int bs) {
+  const int l = threadIdx.x & 63, lr = l & 15, lg = l >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) acc = mfma16f(A[lr * as + 4 * kb + lg], B[(4 * kb + lg) * bs + lr], acc);
+  return acc;
+}
+
 // 16 bytes of bf16 storage <-> operand register.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
@@ -259,5 +272,12 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 // Global memory written before it is NOT made visible to the other waves.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Orders LDS accesses within one wave: waits for this wave's LDS operations,
+// which the LDS executes in issue order, so that lanes read what other lanes
+// of the same wave wrote before it.  No cross-wave effect.
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 }  // namespace gdn
