@@ -46,22 +46,25 @@ FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
 
 
 def kernel_bytes(B, T, Hk, Hv, Dk, Dv, io, state0=False, dS_final=False):
-    """Algorithmic HBM bytes of each chunk-form kernel: the tensors of the
-    method-bytes formula (I/O tensors and the fp32 checkpoints) that the kernel
-    reads or writes, each counted once.  Intermediates in the workspace (chunk
+    """Algorithmic HBM bytes of each chunk-form kernel under gdn_dims.save (the
+    benchmarked path): the I/O tensors each kernel reads or writes, each
+    counted once, and the states the forward hands to the backward -- bf16
+    copies of the state at every chunk start, written by chunk_fwd and read by
+    chunk_bwd_grad (in place of the fp32 checkpoints of the method-bytes
+    formula).  Intermediates in the workspace or the checkpoint buffer (chunk
     matrices, eps, per-chunk state gradients) are not counted."""
     Q1 = B * T * Hk * Dk * io            # one of q, k (or dq, dk)
     V1 = B * T * Hv * Dv * io            # one of v, o, dO, dv
     A1 = B * T * Hv * io                 # one of a, b, da, db
     Par = 2 * Hv * 4
     Sig = B * Hv * Dk * Dv * 4
-    CK = max(math.ceil(T / 64) - 1, 0) * Sig
+    HB = math.ceil(T / 64) * Sig // 2    # bf16 chunk-start states
     s0 = Sig if state0 else 0
     return {
         "chunk_prep": 2 * Q1 + 2 * A1 + Par,
-        "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + CK,
+        "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + HB,
         "chunk_bwd_state": Q1 + 2 * V1 + (Sig if dS_final else 0) + Sig,
-        "chunk_bwd_grad": 2 * Q1 + 2 * V1 + A1 + CK + s0 + 2 * Q1 + 2 * A1,
+        "chunk_bwd_grad": 2 * Q1 + 2 * V1 + A1 + HB + 2 * Q1 + 2 * A1,
         "param_reduce": Par,
     }
 

@@ -72,30 +72,35 @@ typedef struct gdn_dims {
   int64_t B, T, Hk, Hv, Dk, Dv; /* T >= 0; Hv % Hk == 0                     */
   int32_t dtype;                /* enum gdn_dtype                           */
   int32_t algo;                 /* enum gdn_algo                            */
-  int32_t save;                 /* CHUNK family only: nonzero = gdn_fwd also
-                                   saves the backward's chunk matrices in
-                                   the checkpoint buffer's tail, and gdn_bwd
-                                   uses them instead of recomputing them
-                                   (see gdn_ckpt_elems).  Ignored by SCAN.  */
+  int32_t save;                 /* CHUNK family only: nonzero = the checkpoint
+                                   buffer becomes the library's own record of
+                                   what gdn_bwd needs -- the chunk-start
+                                   states in bf16 and the chunk matrices --
+                                   written by gdn_fwd so that gdn_bwd neither
+                                   recomputes nor converts anything (see
+                                   gdn_ckpt_elems).  Ignored by SCAN.        */
 } gdn_dims;
 
 /* Supported sizes: Dk in {16, 32, 64, 128, 192, 256}; Dv a multiple of 8
  * with Dv <= 256 and (Dv <= 24 or Dv % 32 == 0). */
 
 /* Number of fp32 elements of the checkpoint buffer:
- * (ceil(T/64) - 1) * B * Hv * Dk * Dv  (0 when T <= 64), the states; when
- * d->save is set and the call runs the CHUNK family, plus a tail that gdn_fwd
- * fills with the per-chunk matrices the backward needs (the in-chunk inverse
- * and its transpose, the decayed key/key and query/key Gram matrices, the
- * chunk's k and q transposed, the per-step chunk scalars: about
- * B * Hv * ceil(T/64) * 14k + B * Hk * ceil(T/64) * Dk * 64 elements).  The
- * tail's contents are private to the library.  A checkpoint written with save
- * set is read only by a gdn_bwd with the same dims (including save); the
- * state part keeps the layout given at gdn_fwd. */
+ * (ceil(T/64) - 1) * B * Hv * Dk * Dv  (0 when T <= 64), the fp32 states at
+ * steps 64, 128, ... in the layout given at gdn_fwd.
+ * When d->save is set and the call runs the CHUNK family, instead a buffer
+ * whose contents are private to the library: the state at the start of every
+ * chunk (initial state included) rounded to bf16, which is the precision the
+ * chunk products consume it in, and the per-chunk matrices the backward needs
+ * (the in-chunk inverse and its transpose, the decayed key/key and query/key
+ * Gram matrices, the chunk's k and q transposed, the per-step chunk scalars):
+ * about ceil(T/64) * (B * Hv * (Dk * Dv / 2 + 14k) + B * Hk * Dk * 64)
+ * elements.  It holds no fp32 states; such a checkpoint is read only by a
+ * gdn_bwd with the same dims (including save). */
 int gdn_ckpt_elems(const gdn_dims* d, size_t* out);
 
 /* Device workspace bytes needed by gdn_fwd / gdn_bwd for these dims (less
- * with d->save set, which moves the chunk matrices into the checkpoints). */
+ * with d->save set, which moves the chunk matrices and the bf16 states into
+ * the checkpoint buffer). */
 int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out);
 int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
 
@@ -109,8 +114,8 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
  *   state_out[B,Hv,Dk,Dv] fp32 (out); may alias state0 exactly (in-place
  *            decode); no other overlap between outputs and inputs is allowed
  *   ckpt     [ceil(T/64)-1, B,Hv,Dk,Dv] fp32 (out): ckpt[c-1] = state before
- *            step 64c, followed by the saved chunk matrices when d->save is
- *            set (gdn_ckpt_elems elements in all).  NULL = not written
+ *            step 64c; when d->save applies, the library's own record
+ *            instead (gdn_ckpt_elems elements).  NULL = not written
  *            (inference; GDN_ERR_INVALID_ARG when save applies).  Required
  *            by gdn_bwd.
  *   ws       device workspace of at least gdn_fwd_workspace_bytes()

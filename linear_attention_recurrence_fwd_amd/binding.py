@@ -121,8 +121,8 @@ def _dims_of(q, v, algo, save=False):
 
 def _alloc_ckpt(d, dev):
     """The checkpoint buffer: [ceil(T/64)-1, B, Hv, Dk, Dv] fp32, or, when the
-    dims save the chunk matrices, a flat fp32 buffer of gdn_ckpt_elems
-    elements whose first part is that tensor."""
+    dims save (chunk family), a flat buffer of gdn_ckpt_elems fp32 elements
+    with contents private to the library."""
     nslab = max((d.T + CHUNK - 1) // CHUNK - 1, 0)
     nck = ckpt_elems(d)
     if nck == nslab * d.B * d.Hv * d.Dk * d.Dv:
@@ -152,8 +152,9 @@ def fwd(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, need_ckpt=True
         state_out=None, algo=ALGO_AUTO, save=False):
     """Forward scan.  Returns (o, state_out, ckpt); ckpt is None when not
     requested.  Pass state_out=state0 for an in-place state update.  With
-    save=True the chunk form also saves the backward's chunk matrices in the
-    checkpoint buffer (pass the same save to bwd)."""
+    save=True the chunk form writes what the backward needs (bf16 chunk-start
+    states, chunk matrices) into the checkpoint buffer instead of fp32 states
+    (pass the same save to bwd)."""
     d = _dims_of(q, v, algo, save)
     if save and not need_ckpt:
         raise ValueError("save=True needs the checkpoint buffer (need_ckpt=True)")
@@ -235,7 +236,8 @@ class Plan:
 
     `t` maps q, k, v, a, b, A_log, dt_bias, state0, mask, dO, dS_final to
     device tensors (state0, mask, dS_final may be None).  save: the forward
-    saves the chunk matrices for the backward (as in training)."""
+    saves the bf16 states and chunk matrices for the backward (as in
+    training)."""
 
     def __init__(self, t, algo=ALGO_AUTO, stream=None, save=True):
         q, v = t["q"], t["v"]

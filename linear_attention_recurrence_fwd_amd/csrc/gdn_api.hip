@@ -17,13 +17,20 @@ struct Layout {
   size_t rq, rk, kq, ell, beta;                 // prep scalars
   size_t U, E, dHend, pdA, pdt;                 // backward only
   size_t Tx, Mq, KT, TxT, AtT, PqT, QT, SC;     // chunk form
+  size_t HB;                                    // chunk backward: bf16 chunk-start states
   size_t total;
 };
 
-// The chunk matrices kept in the checkpoint buffer's tail under gdn_dims.save
-// (offsets in fp32 elements from the tail's start, 256-byte aligned).
+// Elements of the bf16 chunk-start states (one slot per chunk).
+size_t state_slots_elems(const Dims& d) {
+  return static_cast<size_t>(d.nchunk()) * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv;
+}
+
+// The checkpoint buffer under gdn_dims.save (chunk family): the bf16
+// chunk-start states and the chunk matrices (offsets in fp32 elements,
+// 256-byte aligned).
 struct Saved {
-  size_t Tx, TxT, AtT, PqT, KT, QT, SC, total;
+  size_t HB, Tx, TxT, AtT, PqT, KT, QT, SC, total;
 };
 
 Saved saved_layout(const Dims& d) {
@@ -37,6 +44,7 @@ Saved saved_layout(const Dims& d) {
   const size_t nc = d.nchunk();
   const size_t mats = static_cast<size_t>(d.B) * d.Hv * nc * 64 * 64;  // bf16 each
   const size_t kts = static_cast<size_t>(d.B) * d.Hk * nc * d.Dk * 64;
+  S.HB = take((state_slots_elems(d) + 1) / 2);
   S.Tx = take((mats + 1) / 2);
   S.TxT = take((mats + 1) / 2);
   S.AtT = take((mats + 1) / 2);
@@ -77,6 +85,7 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved) {
     if (chunk) {  // eps and dH' in bf16
       L.E = take((col + 1) / 2);
       L.dHend = take((dh + 1) / 2);
+      if (!saved) L.HB = take((state_slots_elems(d) + 1) / 2);
     } else {
       L.U = take(col);
       L.E = take(col);
@@ -188,10 +197,11 @@ gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   return cb;
 }
 
-// The saved matrices in the checkpoint buffer's tail (every pointer but Mq).
+// The saved states and matrices in the checkpoint buffer (every pointer but Mq).
 void saved_bufs(const Dims& d, const float* ckpt, gdn::ChunkBufs& cb) {
   const Saved S = saved_layout(d);
-  float* tail = const_cast<float*>(ckpt) + align_up(ckpt_state_elems(d) * sizeof(float)) / sizeof(float);
+  float* tail = const_cast<float*>(ckpt);
+  cb.Hb = reinterpret_cast<gdn::bf16*>(tail + S.HB);
   cb.Tx = reinterpret_cast<gdn::bf16*>(tail + S.Tx);
   cb.TxT = reinterpret_cast<gdn::bf16*>(tail + S.TxT);
   cb.AtT = reinterpret_cast<gdn::bf16*>(tail + S.AtT);
@@ -215,8 +225,7 @@ int gdn_ckpt_elems(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = use_saved(d) ? align_up(ckpt_state_elems(dd) * sizeof(float)) / sizeof(float) + saved_layout(dd).total
-                      : ckpt_state_elems(dd);
+  *out = use_saved(d) ? saved_layout(dd).total : ckpt_state_elems(dd);
   return GDN_OK;
 }
 
@@ -264,7 +273,8 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     if (save) saved_bufs(dd, ckpt, cb);
     gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, save ? 2 : 0};
     if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
-    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, ckpt};
+    // under save the states go to the checkpoint buffer as bf16 only
+    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, save ? nullptr : ckpt};
     if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
     return GDN_OK;
   }
@@ -309,6 +319,9 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     } else {
       gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 1};
       if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+      cb.Hb = at<gdn::bf16>(ws, L.HB);
+      gdn::StateBf16Args sa{dd.nchunk(), static_cast<size_t>(dd.B) * dd.Hv * dd.Dk * dd.Dv, state0, ckpt, cb.Hb};
+      if (!launch(st, [&] { return gdn::launch_state_bf16(sa, st); })) return GDN_ERR_HIP;
     }
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
                          at<gdn::bf16>(ws, L.E), at<gdn::bf16>(ws, L.dHend),

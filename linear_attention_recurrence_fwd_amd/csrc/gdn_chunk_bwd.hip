@@ -33,10 +33,15 @@
 //                    prefetched.  Writes dv, eps (bf16), dH' of every chunk
 //                    (bf16, transposed) and dstate.
 //   chunk_bwd_grad   one workgroup per (chunk, batch, key head), looping over
-//                    the group's value heads and 32-column slabs of Dv.  Writes
-//                    dq, dk (after the L2-normalisation backward), da, db and
-//                    the per-chunk parameter sums.  Fixed summation order
-//                    throughout; no atomics.
+//                    the group's value heads and 32-column slabs of Dv, with H
+//                    read from the bf16 copies of the chunk-start states.
+//                    Writes dq, dk (after the L2-normalisation backward), da,
+//                    db and the per-chunk parameter sums.  Fixed summation
+//                    order throughout; no atomics.
+//   state_bf16       the bf16 copies of the chunk-start states from fp32
+//                    checkpoints (when the forward did not write them).
+#include <algorithm>
+
 #include "gdn_dev.h"
 #include "gdn_internal.h"
 
@@ -529,7 +534,7 @@ struct ChunkBwdGrad {
   // Global data of one slab, loaded a slab ahead.
   static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the v / dO / eps tiles
   struct Pf {
-    float4 h[4];   // H rows i0 + a, cols vv0 .. vv0+3 (this thread's block)
+    uint2 h[4];    // H rows i0 + a, cols vv0 .. vv0+3 (this thread's block, bf16)
     uint2 dh[4];   // dH' rows i0 + a, cols vv0 .. vv0+3 (bf16)
     uint4 ch[2];   // chunks tid and tid + NTG of the v / dO / eps tiles
   };
@@ -539,21 +544,20 @@ struct ChunkBwdGrad {
   };
 
   // All loads are unconditional buffer loads, so no load sits under a branch
-  // (where a branch joins, the compiler waits for every outstanding load).  An
-  // absent initial state reads through a zero-size descriptor, i.e. as zeros.
+  // (where a branch joins, the compiler waits for every outstanding load).
+  // H is the bf16 copy of the state at the chunk's start, in the layout of dH'.
   __device__ static void prefetch(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, int v0, Pf& f) {
     const Dims& d = p.d;
     const int bh = x.b * d.Hv + h;
     const size_t hsz = static_cast<size_t>(DK) * d.Dv;
-    const float* Hs = x.c == 0 ? p.state0 : p.ckpt + (static_cast<size_t>(x.c - 1) * d.B * d.Hv) * hsz;
-    const rsrc_t rh = make_rsrc(Hs ? static_cast<const void*>(Hs + bh * hsz) : static_cast<const void*>(p.dHend), Hs ? hsz * 4 : 0);
-    const uint32_t ho = 4 * (x.i0 * d.Dv + v0 + x.vv0);
+    const size_t slot = (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * hsz;
+    const rsrc_t rh = make_rsrc(p.cb.Hb + slot, hsz * 2);
+    const rsrc_t rdh = make_rsrc(p.dHend + slot, hsz * 2);
+    const uint32_t ho = 2 * (x.i0 * d.Dv + v0 + x.vv0);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) f.h[a] = buf_f4(rh, ho + 4 * a * d.Dv);
-    const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * hsz, hsz * 2);
-    const uint32_t dho = 2 * (x.i0 * d.Dv + v0 + x.vv0);
+    for (int a = 0; a < 4; ++a) f.h[a] = buf_u2(rh, ho + 2 * a * d.Dv);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) f.dh[a] = buf_u2(rdh, dho + 2 * a * d.Dv);
+    for (int a = 0; a < 4; ++a) f.dh[a] = buf_u2(rdh, ho + 2 * a * d.Dv);
     const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv + v0;
     const size_t vrem = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
     const rsrc_t rs[3] = {make_rsrc(static_cast<const bf16*>(p.v) + vbase, vrem),
@@ -640,25 +644,16 @@ struct ChunkBwdGrad {
     // ---- this slab's H and dH' into LDS ([i][v]), <dH', H>; v / dO / eps tiles
     if (has_blk) {
       const int i0 = x.i0, vv0 = x.vv0;
-      float hx[4][4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        hx[a][0] = pf.h[a].x;
-        hx[a][1] = pf.h[a].y;
-        hx[a][2] = pf.h[a].z;
-        hx[a][3] = pf.h[a].w;
-      }
-      uint32_t dv[4][4];  // dH' bits, [a = row i0 + a][e = column vv0 + e]
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        dv[a][0] = pf.dh[a].x & 0xffffu;
-        dv[a][1] = pf.dh[a].x >> 16;
-        dv[a][2] = pf.dh[a].y & 0xffffu;
-        dv[a][3] = pf.dh[a].y >> 16;
-        *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pack4_bf16(hx[a][0], hx[a][1], hx[a][2], hx[a][3]);
+        *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pf.h[a];
         *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = pf.dh[a];
+        const uint32_t hw2[2] = {pf.h[a].x, pf.h[a].y}, dw2[2] = {pf.dh[a].x, pf.dh[a].y};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ac.phdh = fmaf(hx[a][e], __uint_as_float(dv[a][e] << 16), ac.phdh);
+        for (int e = 0; e < 2; ++e) {
+          ac.phdh = fmaf(__uint_as_float(hw2[e] << 16), __uint_as_float(dw2[e] << 16), ac.phdh);
+          ac.phdh = fmaf(__uint_as_float(hw2[e] & 0xffff0000u), __uint_as_float(dw2[e] & 0xffff0000u), ac.phdh);
+        }
       }
     }
     put_chunks(sm, q.tid, pf);
@@ -1054,7 +1049,31 @@ __global__ void __launch_bounds__(NTG) chunk_bwd_grad_kernel(ChunkBwdArgs p) {
   ChunkBwdGrad<DK>::run(p, sm);
 }
 
+// bf16 copies of the chunk-start states: 8 elements per thread, grid-stride.
+__global__ void __launch_bounds__(256) state_bf16_kernel(StateBf16Args a) {
+  const size_t per = a.slot / 8, n = per * a.nslot;
+  for (size_t u = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; u < n; u += static_cast<size_t>(gridDim.x) * 256) {
+    const size_t sl = u / per, e = 8 * (u % per);
+    const float* src = sl == 0 ? a.state0 : a.ckpt + (sl - 1) * a.slot;
+    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+    if (src != nullptr) {
+      x0 = *reinterpret_cast<const float4*>(src + e);
+      x1 = *reinterpret_cast<const float4*>(src + e + 4);
+    }
+    *reinterpret_cast<uint4*>(a.Hb + sl * a.slot + e) =
+        make_uint4(pack2_bf16(x0.x, x0.y), pack2_bf16(x0.z, x0.w), pack2_bf16(x1.x, x1.y), pack2_bf16(x1.z, x1.w));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_state_bf16(const StateBf16Args& a, hipStream_t st) {
+  const size_t n = a.slot / 8 * a.nslot;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 8192));
+  state_bf16_kernel<<<blocks, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
   const int nblk = a.d.B * a.d.Hv * (a.d.Dv / ChunkBwdState<64>::NV);

@@ -359,7 +359,8 @@ struct ChunkFwd {
   //                   registers;
   //   B (waves 4-7):  the state update H <- e^{gL} H + K^T diag(w) X for its
   //                   row tiles of H (K^T read transposed from the ring), and
-  //                   the checkpoints;
+  //                   the checkpoints (fp32, and / or the bf16 copies the
+  //                   backward's gradient pass reads);
   //   C (waves 8-11): Q H and the output O = diag(e^g rq) Q H + Mq X for row
   //                   tile w (q and Mq prefetched two chunks ahead in
   //                   registers).
@@ -556,15 +557,15 @@ struct ChunkFwd {
         for (int ct = 0; ct < 2; ++ct) H[it][ct] = mfma16(kta[it][kt], bx[ct], H[it][ct]);
     }
     put_h(sm, q, H);
-    // checkpoint of the state at chunk c+1's start.  The stores are
-    // unconditional; without a checkpoint slot (last chunk, or none
-    // requested) the descriptor is empty and they are dropped.
-    {
+    // the state at chunk c+1's start: the fp32 checkpoint and / or its bf16
+    // copy.  The stores are unconditional within each kind; without a slot
+    // (last chunk) the descriptor is empty and they are dropped.
+    const bool slot = c + 1 < q.NC;
+    if (p.ckpt != nullptr) {
       const size_t hsz = static_cast<size_t>(DK) * d.Dv;
-      const bool ck = p.ckpt != nullptr && c + 1 < q.NC;
-      const rsrc_t rck = make_rsrc(ck ? static_cast<const void*>(p.ckpt + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * hsz)
-                                      : static_cast<const void*>(p.state_out),
-                                   ck ? hsz * 4 : 0);
+      const rsrc_t rck = make_rsrc(slot ? static_cast<const void*>(p.ckpt + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * hsz)
+                                        : static_cast<const void*>(p.state_out),
+                                   slot ? hsz * 4 : 0);
       const uint32_t co = 4 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg) * d.Dv + q.col0 + lr);
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
@@ -575,7 +576,26 @@ struct ChunkFwd {
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(H[it][1][r]), rck, o + 64, 0, 0);
         }
     }
+    if (p.cb.Hb != nullptr) store_hb(p, q, H, slot ? c + 1 : -1);
     lds_barrier();  // 3: H of the next chunk complete
+  }
+
+  // bf16 copy of H as the state at the start of chunk `slot` ([i][v] rows;
+  // dropped when slot < 0).  A quad transpose gives each lane four
+  // consecutive columns of one row: one 8-byte store per tile.
+  __device__ static void store_hb(const ChunkFwdArgs& p, const Lane& q, const f32x4 (&H)[RTW][2], int slot) {
+    const Dims& d = p.d;
+    const size_t hsz = static_cast<size_t>(DK) * d.Dv;
+    const rsrc_t r = make_rsrc(p.cb.Hb + (static_cast<size_t>(max(slot, 0)) * d.B * d.Hv + q.bh) * hsz,
+                               slot >= 0 ? hsz * 2 : 0);
+    const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * q.lg + (q.lr & 3)) * d.Dv + q.col0 + (q.lr & ~3));
+#pragma unroll
+    for (int it = 0; it < RTW; ++it)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const f32x4 tr = quad_transpose(H[it][ct]);
+        buf_store_u2(r, o + 2 * (16 * it * d.Dv + 16 * ct), pack4_bf16(tr[0], tr[1], tr[2], tr[3]));
+      }
   }
 
   // Group C, one chunk: (Q H)^T, then O^T = (Q H)^T diag(e^gamma rq) + X^T Mq^T,
@@ -641,6 +661,7 @@ struct ChunkFwd {
           H[it][ct][r] = p.state0 ? p.state0[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
         }
     put_h(sm, q, H);
+    if (p.cb.Hb != nullptr) store_hb(p, q, H, 0);
     lds_barrier();  // 0
     for (int c = 0; c < q.NC; ++c) step_b(p, sm, q, c, H);
 #pragma unroll

@@ -83,6 +83,9 @@ struct ChunkBufs {
   bf16* QT;   // [B*Hk, NC, Dk, L] raw q of the chunk, transposed
   // per-step chunk scalars, fp32 [B*Hv, NC, SC_ROWS, L]
   float* sc;
+  // [NC, B*Hv, Dk, Dv] the state at the start of chunk c, bf16 (the operand
+  // precision of the chunk products); written by chunk_fwd when non-null
+  bf16* Hb;
 };
 // Rows of ChunkBufs::sc (per chunk, per step t; g = gamma):
 enum : int {
@@ -160,6 +163,15 @@ struct ChunkBwdArgs {
   double* part_ddt;  // [B,NC,Hv] per-chunk sums of da
 };
 
+// bf16 copies of the states at the chunk starts from the fp32 checkpoints:
+// Hb[0] = state0 (zeros when null), Hb[c] = ckpt[c - 1].
+struct StateBf16Args {
+  int nslot;            // chunks
+  size_t slot;          // elements per slot (B*Hv*Dk*Dv, a multiple of 8)
+  const float *state0, *ckpt;
+  bf16* Hb;
+};
+
 struct ParamReduceArgs {
   int B, NC, Hv;
   const double *part_dA, *part_ddt;
@@ -190,6 +202,7 @@ hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t st);
+hipError_t launch_state_bf16(const StateBf16Args& a, hipStream_t st);
 
 // The chunk form runs bf16 I/O with Dk a multiple of 32 and Dv a multiple of 32.
 inline bool chunk_supported(int Dk, int Dv, bool bf16) {

@@ -125,9 +125,10 @@ def test_chunk_unsupported(dtype, Dk, Dv):
 
 
 def test_saved_chunk_matrices_sizes():
-    """gdn_dims.save (chunk family) adds the saved chunk matrices to the
-    checkpoint buffer and takes them out of the workspaces; the scan family
-    ignores it."""
+    """gdn_dims.save (chunk family) turns the checkpoint buffer into the
+    library's own: the chunk-start states in bf16 (one slot per chunk, chunk 0
+    included) and the saved chunk matrices, which leave the workspaces; the
+    scan family ignores it."""
     plain = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_BF16)
     saved = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_BF16, save=True)
     states = 31 * 64 * 192 * 128
@@ -135,14 +136,15 @@ def test_saved_chunk_matrices_sizes():
     kts = 16 * 32 * 192 * 64 // 2
     scal = 64 * 32 * 12 * 64
     assert B.ckpt_elems(plain) == states
-    assert B.ckpt_elems(saved) == states + 4 * mats + 2 * kts + scal
+    slots = 32 * 64 * 192 * 128 // 2     # bf16, in fp32 elements
+    assert B.ckpt_elems(saved) == slots + 4 * mats + 2 * kts + scal
     assert B.bwd_workspace_bytes(saved) < B.bwd_workspace_bytes(plain)
     assert B.fwd_workspace_bytes(saved) < B.fwd_workspace_bytes(plain)
     f32 = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_F32, save=True)
     assert B.ckpt_elems(f32) == states
     assert B.bwd_workspace_bytes(f32) == B.bwd_workspace_bytes(B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_F32))
     one = B.make_dims(1, 1, 16, 64, 192, 128, B.GDN_BF16, B.ALGO_CHUNK, save=True)
-    assert B.ckpt_elems(one) > 0      # no states, only the saved matrices
+    assert B.ckpt_elems(one) > 0      # the initial state's slot and the saved matrices
 
 
 def test_saved_needs_the_checkpoint_buffer():

@@ -234,10 +234,10 @@ def test_chunk_checkpoint_interchange():
 
 @pytest.mark.parametrize("case", ["9b_t256", "ragged_dk128", "edge65_masked", "edge1"])
 def test_chunk_saved_matrices_bitwise(case):
-    """Under gdn_dims.save the forward saves the chunk matrices and the
-    backward uses them instead of recomputing them: every output, the
-    checkpointed states and every gradient are bit-identical to the run
-    without save."""
+    """Under gdn_dims.save the forward saves the chunk matrices and the bf16
+    chunk-start states, and the backward uses them instead of recomputing the
+    matrices and converting the fp32 checkpoints: every output and every
+    gradient is bit-identical to the run without save."""
     c = {"9b_t256": lambda: inputs.qwen35_9b(256),
          "ragged_dk128": lambda: inputs.make_case("chunk_ragged_dk128", 2, 200, 2, 4, 128, 64, "bf16", 79),
          "edge65_masked": lambda: inputs.edge(65, masked=True, extreme=False, dtype="bf16"),
@@ -249,8 +249,6 @@ def test_chunk_saved_matrices_bitwise(case):
     o2, s2, k2 = gpu_fwd(t, algo=CHUNK, save=True)
     g2 = gpu_bwd(t, k2, algo=CHUNK, save=True)
     torch.cuda.synchronize()
-    assert k2.numel() > k1.numel()
-    k2s = k2.view(-1)[:k1.numel()].view(k1.shape)
-    for x, y in [(o1, o2), (s1, s2), (k1, k2s)] + [(g1[n], g2[n]) for n in GRADS]:
+    for x, y in [(o1, o2), (s1, s2)] + [(g1[n], g2[n]) for n in GRADS]:
         assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
