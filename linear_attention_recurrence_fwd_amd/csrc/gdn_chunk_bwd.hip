@@ -490,8 +490,8 @@ struct ChunkBwdGrad {
     float dox[L * LP];  // dO_t . X_s
     float xe[L * LP];   // X_t . eps_s
     float m[L * LP];    // rectangle terms of dl (row r, column s < r)
-    bf16 pt[L * TS];    // P^T of the chunk   [s][t]
-    bf16 at[L * TS];    // A^T of the chunk   [s][t]
+    bf16 pt[L * L];     // P^T of the chunk   [s][t], 16-byte piece p of row s at p ^ ((s >> 3) & 7)
+    bf16 at[L * L];     // A^T of the chunk   [s][t], swizzled alike
   };
   struct Wts {
     bf16 wq[L * TS];    // sum over the group of Wq diag(rk)   [t][s]
@@ -769,12 +769,15 @@ struct ChunkBwdGrad {
       x.i0 = 4 * (blk / (NS / 4));
       x.vv0 = 4 * (blk % (NS / 4));
     }
-    if (tid0 < L) {  // norm factors (the same for every value head of the group; 0 past the end)
+    // norm factors (the same for every value head of the group; 0 past the
+    // end), loaded first and stored last, so that every load of the start is
+    // in flight before the first wait
+    float rk0, rq0;
+    {
       const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + x.j * G) * NC + c) * SC_ROWS * L;
-      sm.rk[tid0] = scc[SC_RK * L + tid0];
-      sm.rq[tid0] = scc[SC_RQ * L + tid0];
+      rk0 = scc[SC_RK * L + (tid0 & 63)];
+      rq0 = scc[SC_RQ * L + (tid0 & 63)];
     }
-    for (int e = tid0; e < L * WR; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
     f32x4 accQ[IH], accK[IH];
 #pragma unroll
     for (int k = 0; k < IH; ++k) accQ[k] = accK[k] = f4zero();
@@ -796,11 +799,18 @@ struct ChunkBwdGrad {
     const int hlast = x.j * G + G - 1;
     Pf pf;
     prefetch(p, x, tid0, x.j * G, 0, pf);
+    for (int e = tid0; e < L * WR; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
+    if (tid0 < L) {
+      sm.rk[tid0] = rk0;
+      sm.rq[tid0] = rq0;
+    }
     for (int hh = 0; hh < G; ++hh) {
       const int h = x.j * G + hh, slot = hh % HB;
       const Lanes ln;
       HeadStart hs;
       load_start(p, x, ln.tid, h, hs);
+      HeadTail ht;  // issued now, used after the slabs
+      load_tail(p, x, ln.tid, h, ht);
       __syncthreads();  // the previous head is done with every shared array
       if (ln.tid < L) {
         const int t = ln.tid;
@@ -820,8 +830,6 @@ struct ChunkBwdGrad {
         slab(p, sm, x, has_blk, h, hlast, si, nsl, pf, ka, qa, txb, accQ, accK, ac);
 
       // ---- per-row sums of head h
-      HeadTail ht;
-      load_tail(p, x, threadIdx.x, h, ht);
       {
         const Lanes q;
 #pragma unroll
@@ -842,8 +850,9 @@ struct ChunkBwdGrad {
         if (q.l == 0) sm.red[q.w] = phdh;
         {
           const int row = q.tid >> 3, c8 = 8 * (q.tid & 7);
-          *reinterpret_cast<uint4*>(&sm.u.h.pt[row * TS + c8]) = ht.pt;
-          *reinterpret_cast<uint4*>(&sm.u.h.at[row * TS + c8]) = ht.at;
+          const int o = row * L + 8 * ((c8 >> 3) ^ ((row >> 3) & 7));
+          *reinterpret_cast<uint4*>(&sm.u.h.pt[o]) = ht.pt;
+          *reinterpret_cast<uint4*>(&sm.u.h.at[o]) = ht.at;
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -879,7 +888,9 @@ struct ChunkBwdGrad {
           const float doxts = sm.u.h.dox[t * LP + s], doxst = sm.u.h.dox[s * LP + t];
           const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
           // P[t][s] = P^T[s][t], A[t][s] = A^T[s][t] (decays and norms included)
-          const float ptv = to_f32(sm.u.h.pt[s * TS + t]), atv = to_f32(sm.u.h.at[s * TS + t]);
+          // (the swizzle spreads a column's 64 rows over distinct banks)
+          const int po = s * L + 8 * ((t >> 3) ^ ((s >> 3) & 7)) + (t & 7);
+          const float ptv = to_f32(sm.u.h.pt[po]), atv = to_f32(sm.u.h.at[po]);
           if (ok && s <= t) wv[0][e] += dec * bs * doxts * rks;
           if (ok && s >= t) wv[1][e] += dec * bt * doxst * sm.rq[s];
           if (ok && s != t) wv[2][e] += -bt * bs * dec * (s < t ? xest : xets) * rks;
