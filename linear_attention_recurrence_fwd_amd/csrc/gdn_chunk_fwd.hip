@@ -464,13 +464,14 @@ struct ChunkFwd {
             pack4_bf16(H[it][ct][0], H[it][ct][1], H[it][ct][2], H[it][ct][3]);
   }
 
-  // Group A, one chunk: issue the ring loads of chunk c + PD, then K H -> R ->
-  // X from slot c.  Before barrier 3 each wave waits for its loads of chunk
+  // Group A, one chunk: K H -> R -> X from slot c, with the ring loads of
+  // chunk c + PD issued after barrier 1 (so that they do not hold up the
+  // chain to barrier 1, nor the other groups' global accesses at the start of
+  // the chunk).  Before barrier 3 each wave waits for its loads of chunk
   // c + 1 (the loads of PD - 1 later chunks may stay in flight); barrier 3
   // then makes slot c + 1 complete for every wave.  The slot refilled here
   // was last read (by B and C) before barrier 3 of the previous chunk.
   __device__ static void step_a(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c) {
-    issue_ring(p, sm, q, min(c + PD, q.NC - 1), (c + PD) % NSL);
     const Slot& s = sm.ring[c % NSL];
     const int lr = q.lr, lg = q.lg, ta = q.ta;
     bf16x8 ka[DK / 32], txa[2];
@@ -502,6 +503,7 @@ struct ChunkFwd {
       *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
     }
     lds_barrier();  // 1: R complete
+    issue_ring(p, sm, q, min(c + PD, q.NC - 1), (c + PD) % NSL);
     f32x4 x[2];
     x[0] = x[1] = f4zero();
 #pragma unroll
