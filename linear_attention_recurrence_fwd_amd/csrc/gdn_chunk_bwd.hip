@@ -272,20 +272,17 @@ struct ChunkBwdState {
     const Slot& s = sm.ring[c & 1];
     // dH' of this chunk for the gradient pass: [i][v], bf16, the layout of the
     // checkpoints; a transpose inside each quad of lanes gives every lane 4
-    // consecutive columns of one row
-    {
-      const int e = lr & 3;
-      bf16* dh = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv + q.col0 +
-                 (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + e) * d.Dv + (lr & ~3));
+    // consecutive columns of one row.  Packed now, stored after barrier Z:
+    // stores issued here would wait behind group A's ring loads and hold up
+    // the products below.
+    uint2 dhp[RTW][2];
 #pragma unroll
-      for (int it = 0; it < RTW; ++it)
+    for (int it = 0; it < RTW; ++it)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const f32x4 tr = quad_transpose(dH[it][ct]);
-          *reinterpret_cast<uint2*>(dh + static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct) =
-              pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
-        }
-    }
+      for (int ct = 0; ct < 2; ++ct) {
+        const f32x4 tr = quad_transpose(dH[it][ct]);
+        dhp[it][ct] = pack4_bf16(tr[0], tr[1], tr[2], tr[3]);
+      }
     // dH <- e^{gL} dH' + Q^T diag(e^g rq) dO (the operand scaled by e^g rq per step)
     const float egl = s.sc[SC_EGL * L];
 #pragma unroll
@@ -314,6 +311,15 @@ struct ChunkBwdState {
     }
     lds_barrier();  // Y
     lds_barrier();  // Z: Ehat complete
+    {
+      const int e = lr & 3;
+      bf16* dh = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv + q.col0 +
+                 (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + e) * d.Dv + (lr & ~3));
+#pragma unroll
+      for (int it = 0; it < RTW; ++it)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) *reinterpret_cast<uint2*>(dh + static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct) = dhp[it][ct];
+    }
     // dH -= K^T diag(e^g rk) Ehat, K^T read transposed from the ring's k tile
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -978,8 +984,34 @@ struct ChunkBwdGrad {
       }
     }
 
+    // ---- operands of the final products (K^T, Q^T tiles) and the q / k rows
+    // of the normalisation backward, loaded now (k and q rows of the slabs
+    // are dead) so that their latency overlaps the conversion of the group
+    // sums; the barriers below wait for LDS only
+    constexpr int QW = DK / 8;                // columns per thread in the normalisation backward
+    constexpr int KTP = DK <= 192 ? 2 : 1;    // K^T / Q^T halves loaded ahead (registers permitting)
+    bf16x8 bk[KTP][IH], bq[KTP][IH];
+    uint4 qrow[QW / 8], krow[QW / 8];
+    {
+      const Lanes q;
+#pragma unroll
+      for (int kt = 0; kt < KTP; ++kt)
+#pragma unroll
+        for (int k = 0; k < IH; ++k) {
+          const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
+          bk[kt][k] = load_bf16x8(ktc + o);
+          bq[kt][k] = load_bf16x8(qtc + o);
+        }
+      const uint32_t ro = static_cast<uint32_t>(min(q.tid >> 3, x.tl)) * qk_row + (q.tid & 7) * QW;
+#pragma unroll
+      for (int u = 0; u < QW / 8; ++u) {
+        qrow[u] = *reinterpret_cast<const uint4*>(qc + ro + 8 * u);
+        krow[u] = *reinterpret_cast<const uint4*>(kc + ro + 8 * u);
+      }
+    }
+
     // ---- final products with the group sums: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn
-    __syncthreads();
+    lds_barrier();
     {
       const Lanes q;
       const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
@@ -994,7 +1026,7 @@ struct ChunkBwdGrad {
       *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + s0]) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
       *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + L + s0]) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
     }
-    __syncthreads();
+    lds_barrier();
     {
       const Lanes q;
 #pragma unroll
@@ -1005,33 +1037,34 @@ struct ChunkBwdGrad {
 #pragma unroll
         for (int k = 0; k < IH; ++k) {
           const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
-          const bf16x8 bk = load_bf16x8(ktc + o), bq = load_bf16x8(qtc + o);
-          accQ[k] = mfma16(aq, bk, accQ[k]);
-          accK[k] = mfma16(a1, bq, accK[k]);
-          accK[k] = mfma16(a2, bk, accK[k]);
+          const bf16x8 vk = kt < KTP ? bk[kt < KTP ? kt : 0][k] : load_bf16x8(ktc + o);
+          const bf16x8 vq = kt < KTP ? bq[kt < KTP ? kt : 0][k] : load_bf16x8(qtc + o);
+          accQ[k] = mfma16(aq, vk, accQ[k]);
+          accK[k] = mfma16(a1, vq, accK[k]);
+          accK[k] = mfma16(a2, vk, accK[k]);
         }
       }
     }
 
     // ---- L2-normalisation backward: dq = rq (dQn - Dk qn (qn . dQn)), dk = rk (dKn - kn (kn . dKn))
+#pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       const Lanes q;
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int k = 0; k < IH; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           sm.u.f.acc[(q.tc0 + r) * FS + 16 * (q.hw * IH + k) + q.lr] = pass == 0 ? accQ[k][r] : accK[k][r];
-      __syncthreads();
+      lds_barrier();
       const int t = q.tid >> 3, qd = q.tid & 7;
-      constexpr int QW = DK / 8;  // columns per thread
-      const bf16* src = (pass == 0 ? qc : kc) + static_cast<size_t>(min(t, x.tl)) * qk_row + qd * QW;
+      const uint4* xr = pass == 0 ? qrow : krow;
       const float* ac = &sm.u.f.acc[t * FS + qd * QW];
       float dot = 0.f;
 #pragma unroll
       for (int u = 0; u < QW; u += 8) {
         float xv[8];
-        Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), xv);
+        Vec16<bf16>::unpack(xr[u / 8], xv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dot = fmaf(xv[e], ac[u + e], dot);
       }
@@ -1043,7 +1076,7 @@ struct ChunkBwdGrad {
 #pragma unroll
         for (int u = 0; u < QW; u += 8) {
           float xv[8], y[8];
-          Vec16<bf16>::unpack(*reinterpret_cast<const uint4*>(src + u), xv);
+          Vec16<bf16>::unpack(xr[u / 8], xv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) y[e] = r1 * (ac[u + e] - coef * xv[e]);
           *reinterpret_cast<uint4*>(dst + u) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
