@@ -889,7 +889,7 @@ struct ChunkBwdGrad {
         for (int e = 0; e < 8; ++e) {
           const int s = s0 + e;
           const bool ok = tv && s < Lc;
-          const float dec = expf(-fabsf(gt - sm.gam[s]));
+          const float dec = __expf(-fabsf(gt - sm.gam[s]));  // hardware exp (bf16-level weights)
           const float bs = sm.beta[s], rks = sm.rk[s];
           const float doxts = sm.u.h.dox[t * LP + s], doxst = sm.u.h.dox[s * LP + t];
           const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
