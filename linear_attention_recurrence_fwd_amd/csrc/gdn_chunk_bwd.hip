@@ -260,9 +260,9 @@ struct ChunkBwdState {
     lds_barrier();  // X: dH of the next chunk complete; slot c - 1 complete
   }
 
-  // Group B, one chunk.
+  // Group B, one chunk, with Q^T of chunk cn loaded into nxt (a chunk ahead).
   __device__ static void step_b(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c, StageB& cur,
-                                f32x4 (&dH)[RTW][2]) {
+                                f32x4 (&dH)[RTW][2], StageB& nxt, int cn) {
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
@@ -310,6 +310,7 @@ struct ChunkBwdState {
       }
     }
     lds_barrier();  // Y
+    load_b(p, q, cn, nxt);  // the next chunk's Q^T, issued while waiting for Ehat
     lds_barrier();  // Z: Ehat complete
     {
       const int e = lr & 3;
@@ -370,11 +371,9 @@ struct ChunkBwdState {
     // first chunk: a load under a branch makes the compiler wait for every
     // outstanding load where the branch joins, which would void the prefetch.
     for (int c = q.NC - 1; c >= 0; c -= 2) {
-      load_b(p, q, max(c - 1, 0), s1);
-      step_b(p, sm, q, c, s0, dH);
+      step_b(p, sm, q, c, s0, dH, s1, max(c - 1, 0));
       if (c < 1) break;
-      load_b(p, q, max(c - 2, 0), s0);
-      step_b(p, sm, q, c - 1, s1, dH);
+      step_b(p, sm, q, c - 1, s1, dH, s0, max(c - 2, 0));
     }
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
