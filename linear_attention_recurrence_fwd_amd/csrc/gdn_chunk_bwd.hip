@@ -518,8 +518,12 @@ struct ChunkBwdGrad {
     alignas(16) float wsq[L * WR];
     alignas(16) float ws1[L * WR];
     alignas(16) float ws2[L * WR];
-    float rk[L], rq[L];
-    float gam[L], eg[L], el[L], beta[L], ell[L];
+    alignas(16) float rk[L];
+    alignas(16) float rq[L];
+    alignas(16) float gam[L];
+    float eg[L], el[L];
+    alignas(16) float beta[L];
+    float ell[L];
     float bv[2][L], pa[2][L], pdb[2][L], rs[L];
     float red[NTG / 64];
     // per value head (slot = head % HB), for the deferred section: the
@@ -883,25 +887,49 @@ struct ChunkBwdGrad {
           wv[a][0] = lo.x; wv[a][1] = lo.y; wv[a][2] = lo.z; wv[a][3] = lo.w;
           wv[a][4] = hi.x; wv[a][5] = hi.y; wv[a][6] = hi.z; wv[a][7] = hi.w;
         }
+        // per half of the thread's 8 columns, every operand is read before any
+        // is used and the terms are selected, not branched on (a branch would
+        // wait for each element's reads in turn)
         float rsum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int s = s0 + e;
-          const bool ok = tv && s < Lc;
-          const float dec = __expf(-fabsf(gt - sm.gam[s]));  // hardware exp (bf16-level weights)
-          const float bs = sm.beta[s], rks = sm.rk[s];
-          const float doxts = sm.u.h.dox[t * LP + s], doxst = sm.u.h.dox[s * LP + t];
-          const float xets = sm.u.h.xe[t * LP + s], xest = sm.u.h.xe[s * LP + t];
-          // P[t][s] = P^T[s][t], A[t][s] = A^T[s][t] (decays and norms included)
-          // (the swizzle spreads a column's 64 rows over distinct banks)
-          const int po = s * L + 8 * ((t >> 3) ^ ((s >> 3) & 7)) + (t & 7);
-          const float ptv = to_f32(sm.u.h.pt[po]), atv = to_f32(sm.u.h.at[po]);
-          if (ok && s <= t) wv[0][e] += dec * bs * doxts * rks;
-          if (ok && s >= t) wv[1][e] += dec * bt * doxst * sm.rq[s];
-          if (ok && s != t) wv[2][e] += -bt * bs * dec * (s < t ? xest : xets) * rks;
-          const float m = ok && s < t ? bs * (ptv * doxts - bt * atv * xest) : 0.f;
-          sm.u.h.m[t * LP + s] = m;
-          rsum += m;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int sb = s0 + 4 * h2;
+          const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[sb]);
+          const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[sb]);
+          const float4 k4 = *reinterpret_cast<const float4*>(&sm.rk[sb]);
+          const float4 q4 = *reinterpret_cast<const float4*>(&sm.rq[sb]);
+          const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, bs[4] = {b4.x, b4.y, b4.z, b4.w};
+          const float rks[4] = {k4.x, k4.y, k4.z, k4.w}, rqs[4] = {q4.x, q4.y, q4.z, q4.w};
+          float doxts[4], doxst[4], xets[4], xest[4], ptv[4], atv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = sb + e;
+            doxts[e] = sm.u.h.dox[t * LP + s];
+            doxst[e] = sm.u.h.dox[s * LP + t];
+            xets[e] = sm.u.h.xe[t * LP + s];
+            xest[e] = sm.u.h.xe[s * LP + t];
+            // P[t][s] = P^T[s][t], A[t][s] = A^T[s][t] (decays and norms included)
+            // (the swizzle spreads a column's 64 rows over distinct banks)
+            const int po = s * L + 8 * ((t >> 3) ^ ((s >> 3) & 7)) + (t & 7);
+            ptv[e] = to_f32(sm.u.h.pt[po]);
+            atv[e] = to_f32(sm.u.h.at[po]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int s = sb + e, ew = 4 * h2 + e;
+            const bool ok = tv && s < Lc;
+            const float dec = __expf(-fabsf(gt - gs[e]));  // hardware exp (bf16-level weights)
+            const float w0 = dec * bs[e] * doxts[e] * rks[e];
+            const float w1 = dec * bt * doxst[e] * rqs[e];
+            const float w2 = -bt * bs[e] * dec * (s < t ? xest[e] : xets[e]) * rks[e];
+            wv[0][ew] += ok && s <= t ? w0 : 0.f;
+            wv[1][ew] += ok && s >= t ? w1 : 0.f;
+            wv[2][ew] += ok && s != t ? w2 : 0.f;
+            const float m = ok && s < t ? bs[e] * (ptv[e] * doxts[e] - bt * atv[e] * xest[e]) : 0.f;
+            sm.u.h.m[t * LP + s] = m;
+            rsum += m;
+          }
+          asm volatile("" ::: "memory");  // keeps the halves' reads apart (register pressure)
         }
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
