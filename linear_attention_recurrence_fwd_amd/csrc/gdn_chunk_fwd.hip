@@ -259,29 +259,43 @@ struct ChunkPrep {
       sc[SC_ELL * L + t] = sm.ell[t];
     }
 
-    // ---- N (permuted, fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward)
+    // ---- N (fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward).
+    // The per-step values are read first and the terms selected, not branched
+    // on (a branch would wait for each element's reads in turn).
+    float gt[4], rkt[4], rqt[4], gs[4], rks[4], bs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * lg + r;
+      gt[r] = sm.gam[t];
+      rkt[r] = sm.rk[t];
+      rqt[r] = sm.rq[t];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int s = 16 * ct + lr;
+      gs[ct] = sm.gam[s];
+      rks[ct] = sm.rk[s];
+      bs[ct] = sm.beta[s];
+    }
     float mq[4][4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * w + 4 * lg + r, s = 16 * ct + lr;
-        float nv = 0.f, pq = 0.f, at = 0.f;
-        if (s <= t) {
-          // hardware exp: its error (about |x| 2^-24 relative) is far below
-          // the bf16 rounding of every matrix this decay enters
-          const float dec = __expf(sm.gam[t] - sm.gam[s]);
-          if (s < t) {
-            at = dec * sm.rk[t] * sm.rk[s] * akk[ct][r];
-            nv = at * sm.beta[s];
-          }
-          pq = dec * sm.rq[t] * sm.rk[s] * aqk[ct][r];
-        }
+        const bool le = s <= t, lt = s < t;
+        // hardware exp: its error (about |x| 2^-24 relative) is far below the
+        // bf16 rounding of every matrix this decay enters; for s > t (term
+        // unused) the argument is 0, so no overflow is computed
+        const float dec = __expf(le ? gt[r] - gs[ct] : 0.f);
+        const float at = lt ? dec * rkt[r] * rks[ct] * akk[ct][r] : 0.f;
+        const float nv = at * bs[ct];
+        const float pq = le ? dec * rqt[r] * rks[ct] * aqk[ct][r] : 0.f;
         sm.u.m.nf[t * SP + s] = nv;
         if (bwd_out) {
           sm.u.m.st[s * SP + t] = at;  // A^T
         } else {
-          sm.u.m.st[t * SP + s] = pq * sm.beta[s];  // Mq
+          sm.u.m.st[t * SP + s] = pq * bs[ct];  // Mq
         }
         mq[ct][r] = pq;
       }
