@@ -352,7 +352,11 @@ struct ChunkBwdState {
   __device__ static void run_b(const ChunkBwdArgs& p, Smem& sm, const Lane& q) {
     const Dims& d = p.d;
     const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
-    // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
+    // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr.
+    // Unconditional buffer loads; an absent dS_final reads through an empty
+    // descriptor, i.e. as zeros (a load under a branch would wait alone).
+    const rsrc_t rsf = make_rsrc(p.dS_final ? static_cast<const void*>(p.dS_final + sbase) : static_cast<const void*>(p.dstate),
+                                 p.dS_final ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
     f32x4 dH[RTW][2];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
@@ -361,7 +365,7 @@ struct ChunkBwdState {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          dH[it][ct][r] = p.dS_final ? p.dS_final[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
+          dH[it][ct][r] = buf_f1(rsf, 4 * static_cast<uint32_t>(i * d.Dv + q.col0 + 16 * ct + q.lr));
         }
     put_h(sm, q, dH);
     StageB s0, s1;

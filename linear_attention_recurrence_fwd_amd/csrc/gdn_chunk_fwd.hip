@@ -667,7 +667,11 @@ struct ChunkFwd {
   __device__ static void run_b(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
     const Dims& d = p.d;
     const size_t sbase = static_cast<size_t>(q.bh) * DK * d.Dv;
-    // H: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr
+    // H: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr.
+    // Unconditional buffer loads; an absent initial state reads through an
+    // empty descriptor, i.e. as zeros (a load under a branch would wait alone).
+    const rsrc_t rs0 = make_rsrc(p.state0 ? static_cast<const void*>(p.state0 + sbase) : static_cast<const void*>(p.state_out),
+                                 p.state0 ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
     f32x4 H[RTW][2];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
@@ -676,7 +680,7 @@ struct ChunkFwd {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          H[it][ct][r] = p.state0 ? p.state0[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] : 0.f;
+          H[it][ct][r] = buf_f1(rs0, 4 * static_cast<uint32_t>(i * d.Dv + q.col0 + 16 * ct + q.lr));
         }
     put_h(sm, q, H);
     if (p.cb.Hb != nullptr) store_hb(p, q, H, 0);

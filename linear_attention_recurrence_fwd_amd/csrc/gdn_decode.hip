@@ -62,13 +62,16 @@ __global__ void __launch_bounds__(512) decode_kernel(DecodeArgs p) {
     kn[r] = to_f32(kr[rg * RL + r]) * rk;
     qn[r] = to_f32(qr[rg * RL + r]) * rq;
   }
-  // the state slice of this lane; absent initial state = zeros
+  // the state slice of this lane, by unconditional buffer loads; an absent
+  // initial state reads through an empty descriptor, i.e. as zeros (loads
+  // under a branch would wait one by one)
   const size_t sb = static_cast<size_t>(bh) * DK * d.Dv + static_cast<size_t>(rg * RL) * d.Dv + col;
+  const size_t hs = static_cast<size_t>(bh) * DK * d.Dv;
+  const rsrc_t rs0 = make_rsrc(p.state0 ? static_cast<const void*>(p.state0 + hs) : static_cast<const void*>(p.state_out),
+                               p.state0 ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
   float4 s[RL];
 #pragma unroll
-  for (int r = 0; r < RL; ++r)
-    s[r] = p.state0 ? *reinterpret_cast<const float4*>(p.state0 + sb + static_cast<size_t>(r) * d.Dv)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int r = 0; r < RL; ++r) s[r] = buf_f4(rs0, 4 * static_cast<uint32_t>((rg * RL + r) * d.Dv + col));
   // S' = g S, u = S'^T kn
   float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
