@@ -438,30 +438,6 @@ __global__ void __launch_bounds__(512) chunk_bwd_state_kernel(ChunkBwdArgs p) {
 
 constexpr int NTG = 512;  // threads of a gradient-pass workgroup (8 waves)
 
-// Scans over the 64 lanes of a wave, in lane order.
-__device__ __forceinline__ float wave_incl_prefix(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(v, off);
-    if (lane >= off) v += y;
-  }
-  return v;
-}
-__device__ __forceinline__ float wave_incl_suffix(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_down(v, off);
-    if (lane + off < 64) v += y;
-  }
-  return v;
-}
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -534,6 +510,9 @@ struct ChunkBwdGrad {
     // prefix-summed and suffix-summed terms of dl, the db factor, l, and the
     // per-head scalars <dH', H> and e^{gamma_L}
     float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB];
+    // a (fp32) and the mask (1 = valid step) of the first batch of value heads,
+    // loaded when the workgroup starts
+    float ha[HB][L], hm[HB][L];
   };
   // Per-head data loaded ahead: the scalars and Tx rows a head starts with,
   // and what its tail needs (the chunk's P^T / A^T tiles, a and the mask).
@@ -785,11 +764,19 @@ struct ChunkBwdGrad {
     // norm factors (the same for every value head of the group; 0 past the
     // end), loaded first and stored last, so that every load of the start is
     // in flight before the first wait
-    float rk0, rq0;
+    float rk0, rq0, a0;
+    uint32_t m0;
     {
       const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + x.j * G) * NC + c) * SC_ROWS * L;
       rk0 = scc[SC_RK * L + (tid0 & 63)];
       rq0 = scc[SC_RQ * L + (tid0 & 63)];
+      // a and the mask of step t = lane for value head j G + (wave % HB) of
+      // the group (clamped); every wave loads, waves < HB store
+      const int tc = min(tid0 & 63, x.tl), hd = x.j * G + min((tid0 >> 6) % HB, G - 1);
+      a0 = __uint_as_float(static_cast<uint32_t>(
+               static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + hd]) << 16);
+      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a, p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+      m0 = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0));
     }
     f32x4 accQ[IH], accK[IH];
 #pragma unroll
@@ -816,6 +803,10 @@ struct ChunkBwdGrad {
     if (tid0 < L) {
       sm.rk[tid0] = rk0;
       sm.rq[tid0] = rq0;
+    }
+    if (tid0 < HB * 64) {
+      sm.ha[tid0 >> 6][tid0 & 63] = a0;
+      sm.hm[tid0 >> 6][tid0 & 63] = p.mask == nullptr || m0 != 0 ? 1.f : 0.f;
     }
     for (int hh = 0; hh < G; ++hh) {
       const int h = x.j * G + hh, slot = hh % HB;
@@ -979,16 +970,24 @@ struct ChunkBwdGrad {
         if (q.w < nh) {
           const int k = q.w, hd = x.j * G + hb0 + k, t = q.l;
           const bool in = t < Lc;
-          const int tc = min(t, x.tl);
-          const float av = __uint_as_float(
-              static_cast<uint32_t>(static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + hd]) << 16);
-          const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
-                                      p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-          const uint32_t mv = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0));
-          const bool valid = p.mask == nullptr || mv != 0;
-          float pre = __shfl_up(wave_incl_prefix(sm.hu[k][t]), 1);
-          if (t == 0) pre = 0.f;
-          const float suf = wave_incl_suffix(sm.hb[k][t]);
+          float av;
+          bool valid;
+          if (hb0 == 0) {  // loaded when the workgroup started
+            av = sm.ha[k][t];
+            valid = sm.hm[k][t] != 0.f;
+          } else {
+            const int tc = min(t, x.tl);
+            av = __uint_as_float(static_cast<uint32_t>(
+                     static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + hd]) << 16);
+            const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
+                                        p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+            valid = p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0) != 0;
+          }
+          // sum over u < t: the prefix sum of the terms shifted by one step;
+          // sum over r >= t: the prefix sum of the terms in reverse order,
+          // taken back from lane 63 - t
+          const float pre = wave_prefix_sum(t > 0 ? sm.hu[k][t - 1] : 0.f);
+          const float suf = __shfl(wave_prefix_sum(sm.hb[k][L - 1 - t]), L - 1 - t);
           const float ell = sm.hell[k][t];
           const float dl = expf(ell) == 0.f ? 0.f : sm.hegl[k] * sm.hdh[k] + pre + suf;
           float da = 0.f, db = 0.f, dll = 0.f;
@@ -1004,8 +1003,8 @@ struct ChunkBwdGrad {
           const uint32_t ro = 2 * static_cast<uint32_t>(t * d.Hv);
           __builtin_amdgcn_raw_buffer_store_b16(bf16_of(da).x, make_rsrc(static_cast<bf16*>(p.da) + r0, nb), ro, 0, 0);
           __builtin_amdgcn_raw_buffer_store_b16(bf16_of(db).x, make_rsrc(static_cast<bf16*>(p.db) + r0, nb), ro, 0, 0);
-          const double sa = wave_sum_f64(static_cast<double>(dll));
-          const double sd = wave_sum_f64(static_cast<double>(da));
+          const double sa = wave_sum_f64_dpp(static_cast<double>(dll));
+          const double sd = wave_sum_f64_dpp(static_cast<double>(da));
           if (t == 0) {
             const size_t pi = (static_cast<size_t>(x.b) * NC + c) * d.Hv + hd;
             p.part_dA[pi] = sa;

@@ -82,6 +82,50 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// DPP move with a row mask: lanes of disabled rows, and lanes whose source is
+// outside their row, receive 0.
+template <int CTRL, int ROW_MASK = 0xf> __device__ __forceinline__ float dpp_or0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row to the next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order: shifted
+// adds within each row of 16 lanes, then each row's total carried into the
+// rows after it (row 0 -> 1 and 2 -> 3, then rows 0-1 -> 2 and 3).
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_or0<kRowShr1>(v);
+  v += dpp_or0<kRowShr2>(v);
+  v += dpp_or0<kRowShr4>(v);
+  v += dpp_or0<kRowShr8>(v);
+  v += dpp_or0<kRowBcast15, 0xa>(v);
+  v += dpp_or0<kRowBcast31, 0xc>(v);
+  return v;
+}
+
+// Sum over the 64 lanes of a wave in fp64, the same bits in every lane: the
+// sum of each row of 16 lanes (butterfly), then the four row sums in order.
+template <int CTRL> __device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), CTRL, 0xf, 0xf, true);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ double lane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  v += dpp_f64<kQuadXor1>(v);
+  v += dpp_f64<kQuadXor2>(v);
+  v += dpp_f64<kRowHalfMirror>(v);
+  v += dpp_f64<kRowMirror>(v);
+  return (lane_f64(v, 0) + lane_f64(v, 16)) + (lane_f64(v, 32) + lane_f64(v, 48));
+}
+
 __device__ __forceinline__ float softplus_f(float x) {
   return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
 }
