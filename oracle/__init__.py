@@ -58,6 +58,9 @@ def _load():
         PD = ctypes.POINTER(ctypes.c_double)
         lib.oracle_gates.argtypes = [D, D, D, D, PD, PD, PD]
         lib.oracle_gates.restype = None
+        I64 = ctypes.c_int64
+        lib.oracle_conv_update.argtypes = [I64, I64, I64, I64] + [P] * 5
+        lib.oracle_conv_update.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -137,3 +140,46 @@ def bwd(q, k, v, a, b, A_log, dt_bias, state0, mask, dO, dS_final=None,
     if rc:
         raise RuntimeError("oracle_gdn_bwd failed with code %d" % rc)
     return out
+
+
+def conv_update(x, state, w):
+    """Depthwise causal conv1d + SiLU update (see oracle_conv_update).
+
+    x: [B, C, S] new samples; state: [B, C, K] carried samples (oldest first);
+    w: [C, K] taps.  Returns (out [B, C, S], final_state [B, C, K]) as float64.
+    """
+    x, state, w = map(_f64, (x, state, w))
+    B, C, S = x.shape
+    K = w.shape[1]
+    assert state.shape == (B, C, K) and w.shape == (C, K)
+    out = np.empty((B, C, S))
+    fin = np.empty((B, C, K))
+    rc = _load().oracle_conv_update(B, C, K, S, *map(_ptr, (x, state, w, out, fin)))
+    if rc:
+        raise RuntimeError("oracle_conv_update failed with code %d" % rc)
+    return out, fin
+
+
+def decode_conv(x, conv_state, conv_w, a, b, A_log, dt_bias, Hk, Dk, Hv, Dv, state0=None, mask=None):
+    """One decode step with the preceding conv update: the conv update of the
+    token's mixed projection x [B, C] (C = 2 Hk Dk + Hv Dv channels, in the
+    order q, k, v, each head-major), then the recurrence step (fwd with T = 1)
+    on the q, k, v it yields.  A masked batch row (mask[b] == 0) keeps its conv
+    state as well as its recurrent state.  a, b: [B, Hv]; mask: [B] or None.
+    Returns (o [B, Hv, Dv], state_out [B, Hv, Dk, Dv], conv_state_out [B, C, K]).
+    """
+    x = _f64(x)
+    B, C = x.shape
+    assert C == 2 * Hk * Dk + Hv * Dv
+    out, fin = conv_update(x[:, :, None], conv_state, conv_w)
+    out = out[:, :, 0]
+    if mask is not None:
+        keep = np.asarray(mask).reshape(B) == 0
+        fin[keep] = _f64(conv_state)[keep]
+    q = out[:, :Hk * Dk].reshape(B, 1, Hk, Dk)
+    k = out[:, Hk * Dk:2 * Hk * Dk].reshape(B, 1, Hk, Dk)
+    v = out[:, 2 * Hk * Dk:].reshape(B, 1, Hv, Dv)
+    m = None if mask is None else np.asarray(mask).reshape(B, 1)
+    o, st, _ = fwd(q, k, v, _f64(a).reshape(B, 1, Hv), _f64(b).reshape(B, 1, Hv), A_log, dt_bias,
+                   state0=state0, mask=m)
+    return o[:, 0], st, fin

@@ -461,3 +461,34 @@ int oracle_gdn_bwd(const oracle_dims* d, const double* q, const double* k,
   free(dqt_h); free(dkt_h); free(dAl_part);
   return err;
 }
+
+/*
+ * Depthwise causal conv1d + SiLU update with a k-sample carry state, the op
+ * that precedes the recurrence in a decode step (torch-to-nnef GDN page, the
+ * causal-conv-update drop-in: layout hidden_states [b, C, S], conv_state
+ * [b, C, k], weight [C, k] -> out [b, C, S], final_state [b, C, k]; the conv is
+ * an unfold, a multiply and a sum).  Per batch row and channel the S new
+ * samples follow the k carried ones; output s is SiLU(z) = z sigmoid(z) of the
+ * tap-weighted sum z of the k most recent samples up to and including new
+ * sample s (taps oldest first), and the final state holds the last k samples.
+ * Returns 0, or 2 when out of memory.
+ */
+int oracle_conv_update(int64_t B, int64_t C, int64_t K, int64_t S, const double* x, const double* state,
+                       const double* w, double* out, double* final_state) {
+  double* ext = malloc((size_t)(K + S) * sizeof(double));
+  if (!ext) return 2;
+  for (int64_t bi = 0; bi < B; ++bi)
+    for (int64_t c = 0; c < C; ++c) {
+      const size_t row = (size_t)(bi * C + c);
+      for (int64_t j = 0; j < K; ++j) ext[j] = state[row * K + j];
+      for (int64_t s = 0; s < S; ++s) ext[K + s] = x[row * S + s];
+      for (int64_t s = 0; s < S; ++s) {
+        double z = 0.0;
+        for (int64_t j = 0; j < K; ++j) z += w[c * K + j] * ext[s + 1 + j];
+        out[row * S + s] = z * sigmoid(z);
+      }
+      for (int64_t j = 0; j < K; ++j) final_state[row * K + j] = ext[S + j];
+    }
+  free(ext);
+  return 0;
+}

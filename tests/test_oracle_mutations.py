@@ -4,7 +4,8 @@ Each case plants one mistake in a temporary copy of the oracle's C source
 (never in the GPU path), builds it, and re-runs the pin suite against it; the
 suite has to fail.  Mistakes covered: step order, eps placement, clamp, every
 term of the reverse step, the normalisation backward, the gate chain, the GQA
-mapping, the checkpoint index, the masked-step semantics.
+mapping, the checkpoint index, the masked-step semantics, and in the conv
+update of the decode path: tap order, window position, state carry, SiLU.
 """
 import os
 import subprocess
@@ -56,6 +57,11 @@ MUTATIONS = {
     "db_chain": ("db[gi] = dbeta * beta * (1.0 - beta);", "db[gi] = dbeta * beta;"),
     "group_sum_first_head_only": ("for (int64_t hh = j * G; hh < (j + 1) * G; ++hh) {",
                                   "for (int64_t hh = j * G; hh < j * G + 1; ++hh) {"),
+    "conv_taps_reversed": ("z += w[c * K + j] * ext[s + 1 + j];",
+                           "z += w[c * K + (K - 1 - j)] * ext[s + 1 + j];"),
+    "conv_window_one_late": ("z += w[c * K + j] * ext[s + 1 + j];", "z += w[c * K + j] * ext[s + j];"),
+    "conv_state_not_advanced": ("final_state[row * K + j] = ext[S + j];", "final_state[row * K + j] = ext[j];"),
+    "conv_no_silu": ("out[row * S + s] = z * sigmoid(z);", "out[row * S + s] = z;"),
 }
 
 

@@ -465,3 +465,92 @@ def test_empty_sequence():
     g = oracle.bwd(*c.oracle_args(), v["dO"], v["dS_final"])
     assert np.array_equal(g["dstate"], v["dS_final"])
     assert np.all(g["dA_log"] == 0) and np.all(g["ddt_bias"] == 0)
+
+
+# ------------------------------------------------- conv update (decode path)
+# Depthwise causal conv1d + SiLU with a k-sample carry state (torch-to-nnef
+# GDN page, the causal-conv-update drop-in: hidden_states [b, C, S],
+# conv_state [b, C, k], weight [C, k] -> out [b, C, S], final_state [b, C, k]).
+
+def silu_ref(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def test_silu_closed_form():
+    """SiLU(0) = 0 and SiLU(ln 3) = (3/4) ln 3 (sigmoid(ln 3) = 3/4): a zero
+    state and a single unit tap turn the conv update into SiLU of the input."""
+    x = np.array([0.0, math.log(3.0), -math.log(3.0)]).reshape(1, 3, 1)
+    w = np.zeros((3, 2))
+    w[:, 1] = 1.0
+    out, _ = oracle.conv_update(x, np.zeros((1, 3, 2)), w)
+    assert out[0, 0, 0] == 0.0
+    assert abs(out[0, 1, 0] - 0.75 * math.log(3.0)) < 1e-15
+    assert abs(out[0, 2, 0] + 0.25 * math.log(3.0)) < 1e-15
+
+
+def test_conv_delta_taps_shift_the_state():
+    """Taps (0, .., 0, 1): the output is SiLU of the newest sample, and the
+    state shifts by one sample per step with the new sample appended."""
+    rng = np.random.default_rng(60)
+    B, C, K = 2, 5, 4
+    x = rng.standard_normal((B, C, 1))
+    st = rng.standard_normal((B, C, K))
+    w = np.zeros((C, K))
+    w[:, -1] = 1.0
+    out, fin = oracle.conv_update(x, st, w)
+    assert np.allclose(out, silu_ref(x), rtol=1e-15, atol=0)
+    assert np.array_equal(fin[:, :, :-1], st[:, :, 1:]) and np.array_equal(fin[:, :, -1], x[:, :, 0])
+
+
+def test_conv_matches_library_convolution():
+    """Brute force against numpy's convolution of the carried samples followed
+    by the new ones: output s is the 'valid' convolution at position s + 1
+    (the window of the k newest samples ending at new sample s)."""
+    rng = np.random.default_rng(61)
+    B, C, K, S = 2, 3, 4, 6
+    x = rng.standard_normal((B, C, S))
+    st = rng.standard_normal((B, C, K))
+    w = rng.standard_normal((C, K))
+    out, fin = oracle.conv_update(x, st, w)
+    for bi in range(B):
+        for c in range(C):
+            ext = np.concatenate([st[bi, c], x[bi, c]])
+            z = np.convolve(ext, w[c][::-1], mode="valid")[1:]
+            assert np.allclose(out[bi, c], silu_ref(z), rtol=1e-13, atol=1e-15)
+            assert np.array_equal(fin[bi, c], ext[-K:])
+
+
+def test_conv_single_steps_equal_one_call():
+    """S single-sample updates, each from the previous final state, reproduce
+    one update over the S samples."""
+    rng = np.random.default_rng(62)
+    B, C, K, S = 2, 4, 3, 7
+    x = rng.standard_normal((B, C, S))
+    st = rng.standard_normal((B, C, K))
+    w = rng.standard_normal((C, K))
+    out, fin = oracle.conv_update(x, st, w)
+    cur = st
+    for s in range(S):
+        o1, cur = oracle.conv_update(x[:, :, s:s + 1], cur, w)
+        assert np.array_equal(o1[:, :, 0], out[:, :, s])
+    assert np.array_equal(cur, fin)
+
+
+def test_decode_conv_masked_row_keeps_both_states():
+    """A masked batch row of the decode step with conv update keeps its conv
+    state and its recurrent state; the unmasked rows equal the unmasked call."""
+    rng = np.random.default_rng(63)
+    B, Hk, Hv, Dk, Dv, K = 3, 1, 2, 8, 4, 4
+    C = 2 * Hk * Dk + Hv * Dv
+    x = rng.standard_normal((B, C))
+    cs = rng.standard_normal((B, C, K))
+    w = rng.standard_normal((C, K)) * 0.5
+    a, b = rng.standard_normal((B, Hv)), rng.standard_normal((B, Hv))
+    A_log, dt_bias = rng.uniform(0, 2, Hv), rng.standard_normal(Hv) * 0.5
+    s0 = rng.standard_normal((B, Hv, Dk, Dv)) * 0.1
+    mask = np.array([1, 0, 1])
+    o, st, fin = oracle.decode_conv(x, cs, w, a, b, A_log, dt_bias, Hk, Dk, Hv, Dv, state0=s0, mask=mask)
+    o1, st1, fin1 = oracle.decode_conv(x, cs, w, a, b, A_log, dt_bias, Hk, Dk, Hv, Dv, state0=s0)
+    assert np.array_equal(fin[1], cs[1]) and np.array_equal(st[1], s0[1])
+    for r in (0, 2):
+        assert np.array_equal(fin[r], fin1[r]) and np.array_equal(st[r], st1[r]) and np.array_equal(o[r], o1[r])
