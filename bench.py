@@ -7,7 +7,7 @@ state, synthetic seeded inputs (the workload of the mlx-lm VJP PR's
 performance table).  One step = gdn_fwd (with checkpoints) + gdn_bwd on the
 same resident inputs.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 9b_t2048|9b_t256|decode]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 9b_t2048|9b_t256|decode|decode_conv]
 """
 from __future__ import annotations
 
@@ -337,6 +337,71 @@ def bench_decode(args, torch, binding, inputs):
     }
 
 
+def bench_decode_conv(args, torch, binding, inputs):
+    """Decode workload with the conv update (gdn_decode_conv): B=64, Hk=16,
+    Hv=32, Dk=Dv=128, 4 taps, one token per call, the conv state and the state
+    updated in place; a step is 64 consecutive calls."""
+    import numpy as np
+    case = inputs.decode_conv(64)
+    dev = torch.device("cuda:0")
+
+    def up(n):
+        x = case.store(n)
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    t = {n: up(n) for n in ("x", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias", "state0")}
+    calls = [{n: t[n][:, i].contiguous() for n in ("x", "a", "b")} for i in range(case.steps)]
+    state, cstate = t["state0"].clone(), t["conv_state"].clone()
+    d = binding.make_dims(case.B, 1, case.Hk, case.Hv, case.Dk, case.Dv, torch.bfloat16)
+    outs = [torch.empty((case.B, case.Hv, case.Dv), dtype=torch.bfloat16, device=dev) for _ in range(case.steps)]
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = binding._p
+    argl = [(ctypes.byref(d), P(c["x"]), P(t["conv_w"]), P(cstate), P(cstate), case.K, P(c["a"]), P(c["b"]),
+             P(t["A_log"]), P(t["dt_bias"]), P(state), None, P(o), P(state), sp)
+            for c, o in zip(calls, outs)]
+    lib = binding.lib()
+
+    def step():
+        for a in argl:
+            rc = lib.gdn_decode_conv(*a)
+            if rc:
+                raise binding.GdnError("gdn_decode_conv", rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per_call = ms / case.steps
+    Sig = case.B * case.Hv * case.Dk * case.Dv * 4
+    # state read + written; conv state read + written, x, taps, a, b, o (bf16); A_log, dt_bias
+    io = (2 * case.B * case.C * case.K + case.B * case.C + case.C * case.K + 2 * case.B * case.Hv
+          + case.B * case.Hv * case.Dv) * 2 + 2 * case.Hv * 4
+    call_bytes = 2 * Sig + io
+    frac = call_bytes / (per_call / 1e3) / HBM_PEAK
+    return {
+        "metric": "decode tokens/sec with the conv update, B=64 Hk16/Hv32/Dk128/Dv128, 4 taps, 1 token per call",
+        "value": round(case.B * case.steps / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gated delta rule decode with conv1d + SiLU update, 64 single-token calls per step",
+                   "B": case.B, "Hk": case.Hk, "Hv": case.Hv, "Dk": case.Dk, "Dv": case.Dv, "conv_taps": case.K,
+                   "io_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "kernel": "decode_conv (one call)",
+                     "achieved": round(call_bytes / (per_call / 1e3) / 1e9, 1),
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(frac, 4),
+                     "traffic": None, "bytes_per_launch": call_bytes,
+                     "avg_call_ms": round(per_call, 5)},
+    }
+
+
 def copy_probe(torch, mib):
     """A plain device-to-device copy of `mib` MiB, three times: under
     `rocprofv3 --pmc FETCH_SIZE` (or WRITE_SIZE) its per-dispatch reading is
@@ -356,7 +421,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="9b_t2048", choices=["9b_t2048", "9b_t256", "decode"])
+    ap.add_argument("--config", default="9b_t2048", choices=["9b_t2048", "9b_t256", "decode", "decode_conv"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -376,6 +441,8 @@ def main():
     binding.lib()
     if args.config == "decode":
         out = bench_decode(args, torch, binding, inputs)
+    elif args.config == "decode_conv":
+        out = bench_decode_conv(args, torch, binding, inputs)
     else:
         out = bench_train(args, torch, binding, inputs)
         if not args.no_cpu_baseline:

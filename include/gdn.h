@@ -149,6 +149,37 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v,
             void* stream);
 
 /*
+ * One decode step (T = 1) preceded by the depthwise causal conv1d + SiLU
+ * update of the token's mixed projection (torch-to-nnef GDN page, the
+ * causal-conv-update drop-in: hidden_states [b, C, S], conv_state [b, C, k],
+ * weight [C, k] -> out, final_state; mlx-lm PR, "Extension 2 -- Inference
+ * kernel fusion": the T = 1 steps fused into one kernel), in one kernel.
+ *   d         dims with T == 1 (else GDN_ERR_INVALID_ARG); algo and save are
+ *             ignored; Dk, Dv as for the decode kernel (Dk in {16, 32, 64,
+ *             128, 192, 256}, Dv a multiple of 32 up to 256), else
+ *             GDN_ERR_UNSUPPORTED
+ *   x         [B, C] dtype, C = 2 Hk Dk + Hv Dv: the token's projection before
+ *             the conv, channels q (Hk heads of Dk), then k, then v (Hv heads
+ *             of Dv), each head-major
+ *   conv_w    [C, conv_k] dtype: taps, oldest sample first
+ *   conv_state[B, C, conv_k] dtype: the conv_k carried samples, oldest first
+ *   conv_state_out [B, C, conv_k] dtype (out): the carried samples shifted by
+ *             one with x appended; may alias conv_state exactly (in place)
+ *   conv_k    taps, 1 .. 8 (else GDN_ERR_INVALID_ARG)
+ *   a, b, A_log, dt_bias, state0, mask, o, state_out: as gdn_fwd with T = 1
+ *             (state_out may alias state0 exactly)
+ * Per channel, out_c = SiLU(sum_i conv_w[c][i] w_i) over the window w of the
+ * conv_k newest samples (the newest conv_k - 1 carried ones, then x); q, k, v
+ * are those outputs, kept in fp32, and the step is gdn_fwd's.  A masked batch
+ * row (mask[b] == 0) keeps both its carried samples and its state (its o is
+ * still read from the state).  No workspace.
+ */
+int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_state,
+                    void* conv_state_out, int32_t conv_k, const void* a, const void* b,
+                    const float* A_log, const float* dt_bias, const float* state0,
+                    const uint8_t* mask, void* o, float* state_out, void* stream);
+
+/*
  * Optional per-kernel timing, for benchmarks and profilers.  While `events`
  * is non-NULL, each kernel that the following gdn_fwd / gdn_bwd calls launch
  * (in launch order, i = 0, 1, ...) records events[2i] on the call's stream

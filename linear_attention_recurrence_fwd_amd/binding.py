@@ -24,7 +24,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-           "gdn_fwd", "gdn_bwd", "gdn_set_kernel_events", "gdn_status_string", "gdn_version")
+           "gdn_fwd", "gdn_bwd", "gdn_decode_conv", "gdn_set_kernel_events", "gdn_status_string",
+           "gdn_version")
 
 
 class Dims(ctypes.Structure):
@@ -59,6 +60,8 @@ def lib():
         L.gdn_fwd.restype = ctypes.c_int
         L.gdn_bwd.argtypes = [PD] + [P] * 21 + [S, P]
         L.gdn_bwd.restype = ctypes.c_int
+        L.gdn_decode_conv.argtypes = [PD] + [P] * 4 + [ctypes.c_int32] + [P] * 9
+        L.gdn_decode_conv.restype = ctypes.c_int
         L.gdn_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         L.gdn_set_kernel_events.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -280,3 +283,46 @@ class Plan:
         rc = lib().gdn_bwd(*self._bargs)
         if rc:
             raise GdnError("gdn_bwd", rc)
+
+
+def decode_conv(x, conv_w, conv_state, a, b, A_log, dt_bias, Hk, Dk, Hv, Dv, state0=None,
+                mask=None, *, conv_state_out=None, state_out=None):
+    """One decode step preceded by the conv update (gdn_decode_conv).
+
+    x: [B, C] (C = 2 Hk Dk + Hv Dv: q, k, v channels); conv_w: [C, K];
+    conv_state: [B, C, K]; a, b: [B, Hv]; A_log, dt_bias: [Hv] fp32; state0:
+    [B, Hv, Dk, Dv] fp32 or None; mask: [B] uint8 or None.  Pass
+    conv_state_out=conv_state and / or state_out=state0 to update in place.
+    Returns (o [B, Hv, Dv], state_out, conv_state_out)."""
+    B, C = x.shape
+    K = conv_w.shape[1]
+    dt, dev = x.dtype, x.device
+    if C != 2 * Hk * Dk + Hv * Dv:
+        raise ValueError("x has %d channels, expected 2 Hk Dk + Hv Dv = %d" % (C, 2 * Hk * Dk + Hv * Dv))
+    d = make_dims(B, 1, Hk, Hv, Dk, Dv, dt)
+    _check(x, "x", (B, C), dt, dev)
+    _check(conv_w, "conv_w", (C, K), dt, dev)
+    _check(conv_state, "conv_state", (B, C, K), dt, dev)
+    _check(a, "a", (B, Hv), dt, dev)
+    _check(b, "b", (B, Hv), dt, dev)
+    _check(A_log, "A_log", (Hv,), torch.float32, dev)
+    _check(dt_bias, "dt_bias", (Hv,), torch.float32, dev)
+    if state0 is not None:
+        _check(state0, "state0", (B, Hv, Dk, Dv), torch.float32, dev)
+    if mask is not None:
+        _check(mask, "mask", (B,), torch.uint8, dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty_like(conv_state)
+    else:
+        _check(conv_state_out, "conv_state_out", (B, C, K), dt, dev)
+    if state_out is None:
+        state_out = torch.empty((B, Hv, Dk, Dv), dtype=torch.float32, device=dev)
+    else:
+        _check(state_out, "state_out", (B, Hv, Dk, Dv), torch.float32, dev)
+    o = torch.empty((B, Hv, Dv), dtype=dt, device=dev)
+    rc = lib().gdn_decode_conv(ctypes.byref(d), _p(x), _p(conv_w), _p(conv_state), _p(conv_state_out), K,
+                               _p(a), _p(b), _p(A_log), _p(dt_bias), _p(state0), _p(mask), _p(o),
+                               _p(state_out), _stream(dev))
+    if rc:
+        raise GdnError("gdn_decode_conv", rc)
+    return o, state_out, conv_state_out

@@ -344,6 +344,26 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   return GDN_OK;
 }
 
+int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_state,
+                    void* conv_state_out, int32_t conv_k, const void* a, const void* b,
+                    const float* A_log, const float* dt_bias, const float* state0,
+                    const uint8_t* mask, void* o, float* state_out, void* stream) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  if (dd.T != 1) return GDN_ERR_INVALID_ARG;
+  if (conv_k < 1 || conv_k > gdn::kMaxConvTaps) return GDN_ERR_INVALID_ARG;
+  if (!x || !conv_w || !conv_state || !conv_state_out || !a || !b || !A_log || !dt_bias || !o || !state_out)
+    return GDN_ERR_INVALID_ARG;
+  if (!gdn::decode_supported(dd.Dk, dd.Dv) || gdn::conv_lds_bytes(dd) > gdn::kMaxConvLds)
+    return GDN_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  gdn::DecodeConvArgs ca{dd, x, conv_w, conv_state, conv_state_out, conv_k, a, b, A_log, dt_bias,
+                         state0, mask, o, state_out};
+  if (!launch(st, [&] { return gdn::launch_decode_conv(ca, d->dtype == GDN_BF16, st); })) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
 int gdn_set_kernel_events(void* const* events, int n) {
   if (events && n < 2) return GDN_ERR_INVALID_ARG;
   g_timing.ev = events;

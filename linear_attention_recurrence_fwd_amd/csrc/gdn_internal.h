@@ -188,11 +188,32 @@ struct DecodeArgs {
   void* o;
   float* state_out;
 };
+// Single-step forward with the preceding depthwise causal conv1d + SiLU
+// update of the token's mixed projection (channels q, k, v).
+constexpr int kMaxConvTaps = 8;
+struct DecodeConvArgs {
+  Dims d;
+  const void* x;           // [B, C] input dtype, C = 2 Hk Dk + Hv Dv
+  const void* conv_w;      // [C, K] input dtype
+  const void* conv_state;  // [B, C, K] input dtype
+  void* conv_state_out;    // [B, C, K]; may alias conv_state exactly
+  int K;                   // taps, 1 .. kMaxConvTaps
+  const void *a, *b;       // [B, Hv] input dtype
+  const float *A_log, *dt_bias;
+  const float* state0;     // may be null; may alias state_out exactly
+  const uint8_t* mask;     // [B] or null
+  void* o;                 // [B, Hv, Dv] input dtype
+  float* state_out;
+};
 inline bool decode_supported(int Dk, int Dv) {
   return (Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256) && Dv % 32 == 0 && Dv <= 256;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_decode_conv(const DecodeConvArgs& a, bool bf16, hipStream_t st);
+// LDS of the decode-with-conv kernel: the conv outputs of one key-head group.
+inline size_t conv_lds_bytes(const Dims& d) { return (2 * static_cast<size_t>(d.Dk) + static_cast<size_t>(d.G()) * d.Dv) * 4; }
+constexpr size_t kMaxConvLds = 64 * 1024;
 hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);

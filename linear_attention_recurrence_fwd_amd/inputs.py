@@ -14,6 +14,7 @@ masking and decode sweeps of the same operation):
   9b_t2048     B=1  T=2048 Hk=16 Hv=64 Dk=192 Dv=128  bf16  seed 3
   edge         B=4  T in {1,64,65,1024} Hk=4 Hv=8 Dk=64 Dv=32  fp32  seed 4000+T
   decode       B=64 T=64 (one step per call) Hk=16 Hv=32 Dk=Dv=128 bf16 seed 5
+  decode_conv  as decode, each step preceded by the conv update (K = 4 taps), seed 6
 
 Distributions: q, k, v, a, b ~ N(0,1); A_log ~ U(0, ln 16); dt_bias ~ N(0, 0.5);
 state0 ~ N(0, 0.1) (zeros for the 9B shape); dO ~ N(0,1); dS_final ~ N(0,1)
@@ -155,6 +156,57 @@ def decode(steps: int = 64) -> Case:
     """The decode workload as one [B, steps] draw; call i uses column t = i."""
     return make_case("decode", 64, steps, 16, 32, 128, 128, "bf16", 5,
                      dS_final=False)
+
+
+class ConvCase:
+    """The decode step with the preceding conv update: per call, one token's
+    mixed projection x [B, C] (C = 2 Hk Dk + Hv Dv channels: q, k, v, each
+    head-major), conv taps [C, K], the carried conv samples [B, C, K], gates
+    a, b [B, Hv] and the recurrent state [B, Hv, Dk, Dv].  ``vals`` holds float64
+    arrays exactly representable in the storage dtype; x, conv_w, conv_state,
+    a, b use the input dtype, the rest fp32."""
+    IO = ("x", "conv_w", "conv_state", "a", "b")
+
+    def __init__(self, name, B, steps, Hk, Hv, Dk, Dv, K, dtype, vals, mask):
+        self.name, self.B, self.steps, self.Hk, self.Hv, self.Dk, self.Dv, self.K = name, B, steps, Hk, Hv, Dk, Dv, K
+        self.dtype, self.vals, self.mask = dtype, vals, mask
+        self.C = 2 * Hk * Dk + Hv * Dv
+
+    def store(self, name: str) -> np.ndarray | None:
+        x = self.vals.get(name)
+        if x is None:
+            return None
+        if name in self.IO and self.dtype == "bf16":
+            return f32_to_bf16_bits(x.astype(np.float32))
+        return x.astype(np.float32)
+
+
+def make_conv_case(name: str, B: int, steps: int, Hk: int, Hv: int, Dk: int, Dv: int, K: int,
+                   dtype: str, seed: int, *, mask: np.ndarray | None = None) -> ConvCase:
+    """Draw a conv-decode workload: x ~ N(0,1) per call ([B, steps, C]); the
+    carried conv samples ~ N(0,1); taps ~ U(-1/sqrt(K), 1/sqrt(K)) (the usual
+    fan-in range of a depthwise kernel of K taps); a, b ~ N(0,1) per call;
+    A_log ~ U(0, ln 16); dt_bias ~ N(0, 0.5); state0 ~ N(0, 0.1).  mask: [B]
+    (nonzero = valid), the same for every call, or None."""
+    assert dtype in DTYPES and Hv % Hk == 0
+    rng = np.random.Generator(np.random.PCG64(seed))
+    C = 2 * Hk * Dk + Hv * Dv
+    v = {}
+    v["x"] = _round(rng.standard_normal((B, steps, C)), dtype)
+    v["conv_state"] = _round(rng.standard_normal((B, C, K)), dtype)
+    v["conv_w"] = _round(rng.uniform(-1.0, 1.0, (C, K)) / math.sqrt(K), dtype)
+    v["a"] = _round(rng.standard_normal((B, steps, Hv)), dtype)
+    v["b"] = _round(rng.standard_normal((B, steps, Hv)), dtype)
+    v["A_log"] = _round(rng.uniform(0.0, math.log(16.0), (Hv,)), "f32")
+    v["dt_bias"] = _round(0.5 * rng.standard_normal((Hv,)), "f32")
+    v["state0"] = _round(0.1 * rng.standard_normal((B, Hv, Dk, Dv)), "f32")
+    m = None if mask is None else np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    return ConvCase(name, B, steps, Hk, Hv, Dk, Dv, K, dtype, v, m)
+
+
+def decode_conv(steps: int = 64) -> ConvCase:
+    """The decode workload with the conv update (kernel of 4 taps)."""
+    return make_conv_case("decode_conv", 64, steps, 16, 32, 128, 128, 4, "bf16", 6)
 
 
 def by_name(name: str) -> Case:

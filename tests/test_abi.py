@@ -160,3 +160,25 @@ def test_saved_needs_the_checkpoint_buffer():
     args = list(p)
     args[9] = None  # ckpt (T <= 64, but the saved matrices live there)
     assert lib.gdn_bwd(ctypes.byref(d), *args, need, None) == 1
+
+
+def test_decode_conv_rejects_before_launch():
+    """gdn_decode_conv validates T == 1, the tap count, the head sizes and the
+    required pointers before any launch (the pointers here are never
+    dereferenced)."""
+    lib = B.lib()
+    p = _fake(13)  # x conv_w conv_state conv_state_out | a b A_log dt_bias state0 mask o state_out stream
+
+    def call(d, k=4, args=None):
+        a = list(p) if args is None else args
+        return lib.gdn_decode_conv(ctypes.byref(d), a[0], a[1], a[2], a[3], k, a[4], a[5], a[6], a[7],
+                                   a[8], a[9], a[10], a[11], None)
+    ok = B.make_dims(2, 1, 2, 4, 64, 32, B.GDN_BF16)
+    assert call(B.make_dims(2, 2, 2, 4, 64, 32, B.GDN_BF16)) == 1   # T != 1
+    assert call(ok, k=0) == 1 and call(ok, k=9) == 1                # taps
+    assert call(B.make_dims(2, 1, 2, 4, 48, 32, B.GDN_BF16)) == 2   # Dk not built
+    assert call(B.make_dims(2, 1, 2, 4, 64, 40, B.GDN_BF16)) == 2   # Dv not a multiple of 32
+    for i in (0, 1, 2, 3, 4, 5, 6, 7, 10, 11):                      # required pointers
+        args = list(p)
+        args[i] = None
+        assert call(ok, args=args) == 1, i
