@@ -15,6 +15,9 @@ masking and decode sweeps of the same operation):
   edge         B=4  T in {1,64,65,1024} Hk=4 Hv=8 Dk=64 Dv=32  fp32  seed 4000+T
   decode       B=64 T=64 (one step per call) Hk=16 Hv=32 Dk=Dv=128 bf16 seed 5
   decode_conv  as decode, each step preceded by the conv update (K = 4 taps), seed 6
+  vg_*         the per-key-channel-gate form (log-gates lg [B,T,Hv,Dk] in place of
+               a, A_log, dt_bias): vg_tiny (tiny's dims, seed 7), vg_edge (edge's
+               dims, seed 7000+T), vg_9b_t* (the 9B shape, seed 8000+T)
 
 Distributions: q, k, v, a, b ~ N(0,1); A_log ~ U(0, ln 16); dt_bias ~ N(0, 0.5);
 state0 ~ N(0, 0.1) (zeros for the 9B shape); dO ~ N(0,1); dS_final ~ N(0,1)
@@ -86,6 +89,11 @@ class Case:
         v = self.vals
         return (v["q"], v["k"], v["v"], v["a"], v["b"], v["A_log"], v["dt_bias"],
                 v.get("state0"), self.mask)
+
+    def vg_args(self):
+        """Inputs of the per-key-channel-gate form (``make_vg_case``)."""
+        v = self.vals
+        return (v["q"], v["k"], v["v"], v["lg"], v["b"], v.get("state0"), self.mask)
 
 
 def _round(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -207,6 +215,51 @@ def make_conv_case(name: str, B: int, steps: int, Hk: int, Hv: int, Dk: int, Dv:
 def decode_conv(steps: int = 64) -> ConvCase:
     """The decode workload with the conv update (kernel of 4 taps)."""
     return make_conv_case("decode_conv", 64, steps, 16, 32, 128, 128, 4, "bf16", 6)
+
+
+def make_vg_case(name: str, B: int, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
+                 dtype: str, seed: int, *, state_std: float | None = 0.1,
+                 dS_final: bool = True, mask: np.ndarray | None = None) -> Case:
+    """Draw a workload of the per-key-channel-gate form: the gate is given as
+    log-gates lg [B,T,Hv,Dk] (fp32), lg = -exp(z) with z ~ N(-1.5, 1.5), so
+    per-channel decays g = e^lg range from nearly 1 (long memory) to nearly 0
+    (median e^-0.22 = 0.80).  q, k, v, b, dO ~ N(0,1); state0 ~ N(0, 0.1);
+    dS_final ~ N(0,1).  Draw order: q, k, v, lg, b, state0, dO, dS_final."""
+    assert dtype in DTYPES and Hv % Hk == 0
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = Case(name, B, T, Hk, Hv, Dk, Dv, dtype)
+    v = c.vals
+    v["q"] = _round(rng.standard_normal((B, T, Hk, Dk)), dtype)
+    v["k"] = _round(rng.standard_normal((B, T, Hk, Dk)), dtype)
+    v["v"] = _round(rng.standard_normal((B, T, Hv, Dv)), dtype)
+    v["lg"] = _round(-np.exp(-1.5 + 1.5 * rng.standard_normal((B, T, Hv, Dk))), "f32")
+    v["b"] = _round(rng.standard_normal((B, T, Hv)), dtype)
+    if state_std is not None:
+        v["state0"] = _round(state_std * rng.standard_normal((B, Hv, Dk, Dv)), "f32")
+    v["dO"] = _round(rng.standard_normal((B, T, Hv, Dv)), dtype)
+    if dS_final:
+        v["dS_final"] = _round(rng.standard_normal((B, Hv, Dk, Dv)), "f32")
+    if mask is not None:
+        c.mask = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+        assert c.mask.shape == (B, T)
+    return c
+
+
+def vg_tiny() -> Case:
+    return make_vg_case("vg_tiny", 1, 8, 2, 4, 16, 8, "f32", 7)
+
+
+def vg_edge(T: int, *, masked: bool = True, dtype: str = "f32") -> Case:
+    B = 4
+    name = "vg_edge_T%d%s%s" % (T, "_mask" if masked else "", "" if dtype == "f32" else "_" + dtype)
+    return make_vg_case(name, B, T, 4, 8, 64, 32, dtype, 7000 + T,
+                        mask=edge_mask(B, T) if masked else None)
+
+
+def vg_qwen35_9b(T: int = 2048) -> Case:
+    """The 9B layer shape with a per-channel gate in place of the scalar one."""
+    return make_vg_case("vg_9b_t%d" % T, 1, T, 16, 64, 192, 128, "bf16", 8000 + T,
+                        state_std=None, dS_final=False)
 
 
 def by_name(name: str) -> Case:

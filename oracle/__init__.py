@@ -58,6 +58,11 @@ def _load():
         PD = ctypes.POINTER(ctypes.c_double)
         lib.oracle_gates.argtypes = [D, D, D, D, PD, PD, PD]
         lib.oracle_gates.restype = None
+        lib.oracle_gdn_fwd_vg.argtypes = [ctypes.POINTER(_Dims)] + [P] * 10 + [ctypes.c_int]
+        lib.oracle_gdn_fwd_vg.restype = ctypes.c_int
+        lib.oracle_gdn_bwd_vg.argtypes = ([ctypes.POINTER(_Dims)] + [P] * 15
+                                          + [ctypes.c_int64, ctypes.c_int])
+        lib.oracle_gdn_bwd_vg.restype = ctypes.c_int
         I64 = ctypes.c_int64
         lib.oracle_conv_update.argtypes = [I64, I64, I64, I64] + [P] * 5
         lib.oracle_conv_update.restype = ctypes.c_int
@@ -139,6 +144,45 @@ def bwd(q, k, v, a, b, A_log, dt_bias, state0, mask, dO, dS_final=None,
         int(chunk), int(nthreads))
     if rc:
         raise RuntimeError("oracle_gdn_bwd failed with code %d" % rc)
+    return out
+
+
+def fwd_vg(q, k, v, lg, b, state0=None, mask=None, nthreads=1):
+    """Forward scan with a per-key-channel gate (see oracle_gdn_fwd_vg).
+
+    lg: [B,T,Hv,Dk] log-gates (g = exp(lg) scales the state's rows); b:
+    [B,T,Hv] (beta = sigmoid(b)); the rest as ``fwd``.  Returns (o,
+    state_out, ckpt)."""
+    q, k, v, lg, b, state0 = map(_f64, (q, k, v, lg, b, state0))
+    d = _dims(q, v)
+    assert lg.shape == (d.B, d.T, d.Hv, d.Dk)
+    m = _mask_u8(mask, d.B, d.T)
+    nck = max((d.T + CKPT - 1) // CKPT - 1, 0)
+    o = np.empty((d.B, d.T, d.Hv, d.Dv))
+    st = np.empty((d.B, d.Hv, d.Dk, d.Dv))
+    ck = np.empty((nck, d.B, d.Hv, d.Dk, d.Dv))
+    rc = _load().oracle_gdn_fwd_vg(ctypes.byref(d), *map(_ptr, (q, k, v, lg, b, state0)), _ptr(m),
+                                   _ptr(o), _ptr(st), _ptr(ck) if nck else None, int(nthreads))
+    if rc:
+        raise RuntimeError("oracle_gdn_fwd_vg failed with code %d" % rc)
+    return o, st, ck
+
+
+def bwd_vg(q, k, v, lg, b, state0, mask, dO, dS_final=None, chunk=CKPT, nthreads=1):
+    """Reverse sweep of ``fwd_vg``.  Returns a dict with dq, dk, dv, dlg,
+    db, dstate (float64); chunk as in ``bwd``."""
+    q, k, v, lg, b, state0, dO, dS_final = map(_f64, (q, k, v, lg, b, state0, dO, dS_final))
+    d = _dims(q, v)
+    m = _mask_u8(mask, d.B, d.T)
+    out = dict(dq=np.empty_like(q), dk=np.empty_like(k), dv=np.empty_like(v),
+               dlg=np.empty_like(lg), db=np.empty_like(b),
+               dstate=np.empty((d.B, d.Hv, d.Dk, d.Dv)))
+    rc = _load().oracle_gdn_bwd_vg(
+        ctypes.byref(d), *map(_ptr, (q, k, v, lg, b, state0)), _ptr(m), _ptr(dO), _ptr(dS_final),
+        *[_ptr(out[n]) for n in ("dq", "dk", "dv", "dlg", "db", "dstate")],
+        int(chunk), int(nthreads))
+    if rc:
+        raise RuntimeError("oracle_gdn_bwd_vg failed with code %d" % rc)
     return out
 
 

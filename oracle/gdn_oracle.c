@@ -34,6 +34,9 @@
  * inside each chunk; both modes perform the same fp64 operations in the same
  * order, so they agree bit for bit.
  *
+ * The per-key-channel gate (oracle_gdn_fwd_vg / oracle_gdn_bwd_vg) replaces the
+ * scalar g by a vector that scales the state's rows; see its section below.
+ *
  * Everything is sequential per (b, h); the optional OpenMP loop only runs
  * independent (b, h) pairs on different threads.  The sums over the G value
  * heads of a key head and over (b, t) for the per-head parameters run
@@ -459,6 +462,308 @@ int oracle_gdn_bwd(const oracle_dims* d, const double* q, const double* k,
     }
   }
   free(dqt_h); free(dkt_h); free(dAl_part);
+  return err;
+}
+
+/* ------------------------------------------------- per-channel (vector) gate */
+
+/*
+ * Vectorised gating (mlx-lm PR, "Models covered": Kimi-Linear runs the same
+ * rule with a gate per key channel, g.ndim == 4; "Scope and follow-ups": the
+ * Python path supports it).  The gate of step t, value head h is a vector
+ * g_t in R^Dk that scales the rows of the state: S' = diag(g_t) S.  The pages
+ * give no formula that produces it, so the caller passes its logarithm
+ * lg[b,t,h,i] = log g_{t,i} directly (as the torch-to-nnef op contract passes
+ * a log-decay).  beta = sigmoid(b) and everything else is the scalar-gate
+ * step above:
+ *   S' = diag(g) S;  u = S'^T k;  delta = beta (v - u);  S = S' + k delta^T;
+ *   o = S^T q.
+ * A masked step leaves S unchanged and reads o from it.
+ */
+typedef struct {
+  double *khat, *qhat, *qt, *g; /* Dk each; g = exp(lg) */
+  double beta;
+  int valid;
+} step_vg;
+
+static size_t at_lg(const oracle_dims* d, int64_t b, int64_t t, int64_t h) {
+  return ((size_t)(b * d->T + t) * d->Hv + h) * d->Dk;
+}
+
+static void load_step_vg(const oracle_dims* d, int64_t b, int64_t t, int64_t h,
+                         const double* q, const double* k, const double* lg,
+                         const double* bb, const uint8_t* mask, step_vg* s) {
+  int64_t G = d->Hv / d->Hk, j = h / G;
+  double scale = 1.0 / sqrt((double)d->Dk);
+  l2norm(k + at_qk(d, b, t, j), d->Dk, s->khat);
+  l2norm(q + at_qk(d, b, t, j), d->Dk, s->qhat);
+  for (int64_t i = 0; i < d->Dk; ++i) s->qt[i] = scale * s->qhat[i];
+  const double* l = lg + at_lg(d, b, t, h);
+  for (int64_t i = 0; i < d->Dk; ++i) s->g[i] = exp(l[i]);
+  s->beta = sigmoid(bb[at_g(d, b, t, h)]);
+  s->valid = mask ? (mask[b * d->T + t] != 0) : 1;
+}
+
+static void fwd_step_vg(const oracle_dims* d, double* S, const step_vg* s,
+                        const double* v, double* u, double* delta, double* o) {
+  int64_t Dk = d->Dk, Dv = d->Dv;
+  if (s->valid) {
+    for (int64_t i = 0; i < Dk; ++i)
+      for (int64_t c = 0; c < Dv; ++c) S[i * Dv + c] *= s->g[i];
+    for (int64_t c = 0; c < Dv; ++c) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < Dk; ++i) acc += S[i * Dv + c] * s->khat[i];
+      u[c] = acc;
+      delta[c] = s->beta * (v[c] - acc);
+    }
+    for (int64_t i = 0; i < Dk; ++i)
+      for (int64_t c = 0; c < Dv; ++c) S[i * Dv + c] += s->khat[i] * delta[c];
+  }
+  for (int64_t c = 0; c < Dv; ++c) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < Dk; ++i) acc += S[i * Dv + c] * s->qt[i];
+    o[c] = acc;
+  }
+}
+
+static int vg_alloc(const oracle_dims* d, scratch_t* w, step_vg* s) {
+  memset(s, 0, sizeof *s);
+  int bad = scratch_alloc(d, w);
+  s->g = malloc(sizeof(double) * d->Dk);
+  s->khat = w->khat;
+  s->qhat = w->qhat;
+  s->qt = w->qt;
+  return bad || !s->g;
+}
+
+/*
+ * lg [B,T,Hv,Dk] log-gates; the rest as oracle_gdn_fwd without the scalar
+ * gate inputs.  Returns 0, 1 on bad dims, 2 on allocation failure.
+ */
+int oracle_gdn_fwd_vg(const oracle_dims* d, const double* q, const double* k,
+                      const double* v, const double* lg, const double* b,
+                      const double* state0, const uint8_t* mask, double* o,
+                      double* state_out, double* ckpt, int nthreads) {
+  if (check_dims(d)) return 1;
+  int64_t BH = d->B * d->Hv;
+  size_t SS = (size_t)d->Dk * d->Dv;
+  int err = 0;
+  (void)nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    int64_t bi = bh / d->Hv, h = bh % d->Hv;
+    scratch_t w;
+    step_vg s;
+    double* S = malloc(sizeof(double) * SS);
+    if (vg_alloc(d, &w, &s) || !S) {
+#pragma omp atomic write
+      err = 2;
+      free(S); free(s.g);
+      scratch_free(&w);
+      continue;
+    }
+    if (state0) memcpy(S, state0 + at_s(d, bi, h), sizeof(double) * SS);
+    else memset(S, 0, sizeof(double) * SS);
+    for (int64_t t = 0; t < d->T; ++t) {
+      load_step_vg(d, bi, t, h, q, k, lg, b, mask, &s);
+      fwd_step_vg(d, S, &s, v + at_v(d, bi, t, h), w.u, w.delta, o + at_v(d, bi, t, h));
+      if (ckpt && (t + 1) % ORACLE_CKPT == 0 && t + 1 < d->T) {
+        int64_t c = (t + 1) / ORACLE_CKPT - 1;
+        memcpy(ckpt + (size_t)c * BH * SS + at_s(d, bi, h), S, sizeof(double) * SS);
+      }
+    }
+    memcpy(state_out + at_s(d, bi, h), S, sizeof(double) * SS);
+    free(S); free(s.g);
+    scratch_free(&w);
+  }
+  return err;
+}
+
+/*
+ * Reverse sweep of the per-channel-gate step.  Outputs (overwritten):
+ *   dq, dk [B,T,Hk,Dk]; dv [B,T,Hv,Dv]; dlg [B,T,Hv,Dk]; db [B,T,Hv];
+ *   dstate [B,Hv,Dk,Dv].  chunk as in oracle_gdn_bwd.
+ * With S' = diag(g) S_prev the gate enters row by row, so its gradient is a
+ * row-wise sum:  dg_i = sum_c dS'[i,c] S_prev[i,c],  dlg_i = g_i dg_i, and
+ * dL/dS_prev = diag(g) dS'.  Masked steps get dv = dlg = db = 0.
+ */
+int oracle_gdn_bwd_vg(const oracle_dims* d, const double* q, const double* k,
+                      const double* v, const double* lg, const double* b,
+                      const double* state0, const uint8_t* mask, const double* dO,
+                      const double* dS_final, double* dq, double* dk, double* dv,
+                      double* dlg, double* db, double* dstate, int64_t chunk,
+                      int nthreads) {
+  if (check_dims(d) || chunk < 0) return 1;
+  int64_t B = d->B, T = d->T, Hk = d->Hk, Hv = d->Hv, Dk = d->Dk, Dv = d->Dv;
+  int64_t G = Hv / Hk, BH = B * Hv;
+  size_t SS = (size_t)Dk * Dv;
+  int64_t span = chunk > 0 ? chunk : (T > 0 ? T : 1);
+  int64_t nspan = T > 0 ? (T + span - 1) / span : 0;
+  size_t nvk = (size_t)B * T * Hv * Dk;
+  double* dqt_h = calloc(nvk ? nvk : 1, sizeof(double));
+  double* dkt_h = calloc(nvk ? nvk : 1, sizeof(double));
+  if (!dqt_h || !dkt_h) {
+    free(dqt_h); free(dkt_h);
+    return 2;
+  }
+  int err = 0;
+  (void)nthreads;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    int64_t bi = bh / Hv, h = bh % Hv;
+    scratch_t w;
+    step_vg s;
+    double* S = malloc(sizeof(double) * SS);
+    double* D = malloc(sizeof(double) * SS);
+    double* Sp = malloc(sizeof(double) * SS);
+    double* St = malloc(sizeof(double) * SS);
+    double* dSp = malloc(sizeof(double) * SS);
+    double* starts = malloc(sizeof(double) * SS * (nspan ? nspan : 1));
+    double* hist = malloc(sizeof(double) * SS * span);
+    double* ddel = malloc(sizeof(double) * Dv);
+    double* du = malloc(sizeof(double) * Dv);
+    if (vg_alloc(d, &w, &s) || !S || !D || !Sp || !St || !dSp || !starts || !hist ||
+        !ddel || !du) {
+#pragma omp atomic write
+      err = 2;
+      free(S); free(D); free(Sp); free(St); free(dSp); free(starts);
+      free(hist); free(ddel); free(du); free(s.g);
+      scratch_free(&w);
+      continue;
+    }
+
+    if (state0) memcpy(S, state0 + at_s(d, bi, h), sizeof(double) * SS);
+    else memset(S, 0, sizeof(double) * SS);
+    for (int64_t t = 0; t < T; ++t) {
+      if (t % span == 0) memcpy(starts + (size_t)(t / span) * SS, S, sizeof(double) * SS);
+      load_step_vg(d, bi, t, h, q, k, lg, b, mask, &s);
+      fwd_step_vg(d, S, &s, v + at_v(d, bi, t, h), w.u, w.delta, w.otmp);
+    }
+
+    if (dS_final) memcpy(D, dS_final + at_s(d, bi, h), sizeof(double) * SS);
+    else memset(D, 0, sizeof(double) * SS);
+    for (int64_t c = nspan - 1; c >= 0; --c) {
+      int64_t t0 = c * span, t1 = t0 + span < T ? t0 + span : T;
+      memcpy(S, starts + (size_t)c * SS, sizeof(double) * SS);
+      for (int64_t t = t0; t < t1; ++t) {
+        memcpy(hist + (size_t)(t - t0) * SS, S, sizeof(double) * SS);
+        load_step_vg(d, bi, t, h, q, k, lg, b, mask, &s);
+        fwd_step_vg(d, S, &s, v + at_v(d, bi, t, h), w.u, w.delta, w.otmp);
+      }
+      for (int64_t t = t1 - 1; t >= t0; --t) {
+        const double* Sprev = hist + (size_t)(t - t0) * SS;
+        const double* vt = v + at_v(d, bi, t, h);
+        const double* dOt = dO + at_v(d, bi, t, h);
+        load_step_vg(d, bi, t, h, q, k, lg, b, mask, &s);
+        double* dqt = dqt_h + ((size_t)(bi * T + t) * Hv + h) * Dk;
+        double* dkt = dkt_h + ((size_t)(bi * T + t) * Hv + h) * Dk;
+        double* dlt = dlg + at_lg(d, bi, t, h);
+        double* dvt = dv + at_v(d, bi, t, h);
+        double beta = s.beta;
+
+        if (s.valid) {
+          for (int64_t i = 0; i < Dk; ++i)
+            for (int64_t cc = 0; cc < Dv; ++cc) Sp[i * Dv + cc] = s.g[i] * Sprev[i * Dv + cc];
+          for (int64_t cc = 0; cc < Dv; ++cc) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < Dk; ++i) acc += Sp[i * Dv + cc] * s.khat[i];
+            w.u[cc] = acc;
+            w.delta[cc] = beta * (vt[cc] - acc);
+          }
+          for (int64_t i = 0; i < Dk; ++i)
+            for (int64_t cc = 0; cc < Dv; ++cc)
+              St[i * Dv + cc] = Sp[i * Dv + cc] + s.khat[i] * w.delta[cc];
+        } else {
+          memcpy(St, Sprev, sizeof(double) * SS);
+        }
+
+        /* o_t = S_t^T qt. */
+        for (int64_t i = 0; i < Dk; ++i)
+          for (int64_t cc = 0; cc < Dv; ++cc) D[i * Dv + cc] += s.qt[i] * dOt[cc];
+        for (int64_t i = 0; i < Dk; ++i) {
+          double acc = 0.0;
+          for (int64_t cc = 0; cc < Dv; ++cc) acc += St[i * Dv + cc] * dOt[cc];
+          dqt[i] = acc;
+        }
+
+        if (!s.valid) {
+          for (int64_t i = 0; i < Dk; ++i) dkt[i] = dlt[i] = 0.0;
+          for (int64_t cc = 0; cc < Dv; ++cc) dvt[cc] = 0.0;
+          db[at_g(d, bi, t, h)] = 0.0;
+          continue;
+        }
+
+        /* S_t = S' + k delta^T;  delta = beta (v - u). */
+        for (int64_t cc = 0; cc < Dv; ++cc) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < Dk; ++i) acc += D[i * Dv + cc] * s.khat[i];
+          ddel[cc] = acc;
+        }
+        double dbeta = 0.0;
+        for (int64_t cc = 0; cc < Dv; ++cc) {
+          dvt[cc] = beta * ddel[cc];
+          dbeta += ddel[cc] * (vt[cc] - w.u[cc]);
+          du[cc] = -beta * ddel[cc];
+        }
+        /* u = S'^T k. */
+        for (int64_t i = 0; i < Dk; ++i)
+          for (int64_t cc = 0; cc < Dv; ++cc)
+            dSp[i * Dv + cc] = D[i * Dv + cc] + s.khat[i] * du[cc];
+        for (int64_t i = 0; i < Dk; ++i) {
+          double acc = 0.0;
+          for (int64_t cc = 0; cc < Dv; ++cc)
+            acc += D[i * Dv + cc] * w.delta[cc] + Sp[i * Dv + cc] * du[cc];
+          dkt[i] = acc;
+        }
+        /* S' = diag(g) S_prev:  dg_i = sum_c dS'[i,c] S_prev[i,c],
+         * dlg_i = g_i dg_i,  dL/dS_prev = diag(g) dS'. */
+        for (int64_t i = 0; i < Dk; ++i) {
+          double acc = 0.0;
+          for (int64_t cc = 0; cc < Dv; ++cc) acc += dSp[i * Dv + cc] * Sprev[i * Dv + cc];
+          dlt[i] = s.g[i] * acc;
+        }
+        for (int64_t i = 0; i < Dk; ++i)
+          for (int64_t cc = 0; cc < Dv; ++cc) D[i * Dv + cc] = s.g[i] * dSp[i * Dv + cc];
+        db[at_g(d, bi, t, h)] = dbeta * beta * (1.0 - beta);
+      }
+    }
+    memcpy(dstate + at_s(d, bi, h), D, sizeof(double) * SS);
+
+    free(S); free(D); free(Sp); free(St); free(dSp); free(starts);
+    free(hist); free(ddel); free(du); free(s.g);
+    scratch_free(&w);
+  }
+
+  if (!err) {
+    /* Group sums over the G value heads (h ascending), then the L2 backward,
+     * exactly as for the scalar gate. */
+    double scale = 1.0 / sqrt((double)Dk);
+    double* tmp = malloc(sizeof(double) * Dk * 2);
+    double *xhat = tmp, *acc = tmp ? tmp + Dk : NULL;
+    for (int64_t bi = 0; bi < B && tmp; ++bi)
+      for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < Hk; ++j)
+          for (int pass = 0; pass < 2; ++pass) {
+            const double* src = pass == 0 ? dqt_h : dkt_h;
+            const double* x = (pass == 0 ? q : k) + at_qk(d, bi, t, j);
+            double* out = (pass == 0 ? dq : dk) + at_qk(d, bi, t, j);
+            for (int64_t i = 0; i < Dk; ++i) acc[i] = 0.0;
+            for (int64_t hh = j * G; hh < (j + 1) * G; ++hh) {
+              const double* p = src + ((size_t)(bi * T + t) * Hv + hh) * Dk;
+              for (int64_t i = 0; i < Dk; ++i) acc[i] += p[i];
+            }
+            if (pass == 0)
+              for (int64_t i = 0; i < Dk; ++i) acc[i] *= scale;
+            double r = l2norm(x, Dk, xhat);
+            double dotp = 0.0;
+            for (int64_t i = 0; i < Dk; ++i) dotp += xhat[i] * acc[i];
+            for (int64_t i = 0; i < Dk; ++i) out[i] = r * (acc[i] - xhat[i] * dotp);
+          }
+    if (!tmp) err = 2;
+    free(tmp);
+  }
+  free(dqt_h); free(dkt_h);
   return err;
 }
 

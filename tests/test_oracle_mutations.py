@@ -4,7 +4,9 @@ Each case plants one mistake in a temporary copy of the oracle's C source
 (never in the GPU path), builds it, and re-runs the pin suite against it; the
 suite has to fail.  Mistakes covered: step order, eps placement, clamp, every
 term of the reverse step, the normalisation backward, the gate chain, the GQA
-mapping, the checkpoint index, the masked-step semantics, and in the conv
+mapping, the checkpoint index, the masked-step semantics, the per-channel gate
+(row vs column, its gradient's factor and state, the carry, masking, head
+index), and in the conv
 update of the decode path: tap order, window position, state carry, SiLU.
 """
 import os
@@ -57,6 +59,25 @@ MUTATIONS = {
     "db_chain": ("db[gi] = dbeta * beta * (1.0 - beta);", "db[gi] = dbeta * beta;"),
     "group_sum_first_head_only": ("for (int64_t hh = j * G; hh < (j + 1) * G; ++hh) {",
                                   "for (int64_t hh = j * G; hh < j * G + 1; ++hh) {"),
+    "vg_gate_on_columns": ("for (int64_t c = 0; c < Dv; ++c) S[i * Dv + c] *= s->g[i];",
+                           "for (int64_t c = 0; c < Dv; ++c) S[i * Dv + c] *= s->g[c % Dk];"),
+    "vg_recompute_gate_on_columns": ("Sp[i * Dv + cc] = s.g[i] * Sprev[i * Dv + cc];",
+                                     "Sp[i * Dv + cc] = s.g[cc % Dk] * Sprev[i * Dv + cc];"),
+    "vg_dlg_no_gate_factor": ("dlt[i] = s.g[i] * acc;", "dlt[i] = acc;"),
+    "vg_dlg_uses_decayed_state": (
+        "for (int64_t cc = 0; cc < Dv; ++cc) acc += dSp[i * Dv + cc] * Sprev[i * Dv + cc];",
+        "for (int64_t cc = 0; cc < Dv; ++cc) acc += dSp[i * Dv + cc] * Sp[i * Dv + cc];"),
+    "vg_carry_without_decay": (
+        "for (int64_t cc = 0; cc < Dv; ++cc) D[i * Dv + cc] = s.g[i] * dSp[i * Dv + cc];",
+        "for (int64_t cc = 0; cc < Dv; ++cc) D[i * Dv + cc] = dSp[i * Dv + cc];"),
+    "vg_masked_step_decays": (
+        "  if (s->valid) {\n    for (int64_t i = 0; i < Dk; ++i)\n"
+        "      for (int64_t c = 0; c < Dv; ++c) S[i * Dv + c] *= s->g[i];",
+        "  for (int64_t i = 0; i < Dk; ++i)\n"
+        "      for (int64_t c = 0; c < Dv; ++c) S[i * Dv + c] *= s->g[i];\n"
+        "  if (s->valid) {\n    if (0) {}"),
+    "vg_gate_head_index": ("return ((size_t)(b * d->T + t) * d->Hv + h) * d->Dk;",
+                           "return ((size_t)(b * d->T + t) * d->Hv + h / (d->Hv / d->Hk)) * d->Dk;"),
     "conv_taps_reversed": ("z += w[c * K + j] * ext[s + 1 + j];",
                            "z += w[c * K + (K - 1 - j)] * ext[s + 1 + j];"),
     "conv_window_one_late": ("z += w[c * K + j] * ext[s + 1 + j];", "z += w[c * K + j] * ext[s + j];"),

@@ -554,3 +554,171 @@ def test_decode_conv_masked_row_keeps_both_states():
     assert np.array_equal(fin[1], cs[1]) and np.array_equal(st[1], s0[1])
     for r in (0, 2):
         assert np.array_equal(fin[r], fin1[r]) and np.array_equal(st[r], st1[r]) and np.array_equal(o[r], o1[r])
+
+
+# ------------------------------------------ per-key-channel (vector) gates
+#
+# mlx-lm PR, "Models covered" / "Scope and follow-ups": Kimi-Linear runs the
+# rule with a gate per key channel (g.ndim == 4).  The gate vector g_t scales
+# the rows of the state; the caller gives lg = log g.
+
+def _nrm(x):
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + EPS)
+
+
+def vg_brute_fwd(q, k, v, lg, b, state0, mask):
+    """The step as a transition map, S_t = (I - beta k k^T) diag(g) S + beta k v^T,
+    o_t = S_t^T q / sqrt(Dk), with dense numpy products per (b, h); masked steps
+    are the identity map.  Returns (o, S_T, states at t = 64, 128, ...)."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    G = Hv // Hk
+    kn, qn = _nrm(k), _nrm(q) / math.sqrt(Dk)
+    beta = 1.0 / (1.0 + np.exp(-b))
+    o = np.zeros((B, T, Hv, Dv))
+    ST = np.zeros((B, Hv, Dk, Dv))
+    nck = max((T + 63) // 64 - 1, 0)
+    ck = np.zeros((nck, B, Hv, Dk, Dv))
+    for bi in range(B):
+        for h in range(Hv):
+            S = np.zeros((Dk, Dv)) if state0 is None else state0[bi, h].copy()
+            for t in range(T):
+                if mask is None or mask[bi, t]:
+                    kk = kn[bi, t, h // G]
+                    A = (np.eye(Dk) - beta[bi, t, h] * np.outer(kk, kk)) @ np.diag(np.exp(lg[bi, t, h]))
+                    S = A @ S + beta[bi, t, h] * np.outer(kk, v[bi, t, h])
+                o[bi, t, h] = S.T @ qn[bi, t, h // G]
+                if (t + 1) % 64 == 0 and t + 1 < T:
+                    ck[(t + 1) // 64 - 1, bi, h] = S
+            ST[bi, h] = S
+    return o, ST, ck
+
+
+def test_vg_matches_transition_map_form():
+    """Forward with per-channel gates equals the dense transition-map form,
+    including masked steps and a checkpoint (T = 70)."""
+    c = inputs.make_vg_case("vgb", 2, 70, 1, 2, 8, 5, "f32", 31,
+                            mask=np.array([[1] * 70, [1] * 30 + [0, 1] * 20]))
+    args = c.vg_args()
+    o, st, ck = oracle.fwd_vg(*args)
+    o_r, st_r, ck_r = vg_brute_fwd(*args)
+    assert rel(o, o_r) < 1e-12 and rel(st, st_r) < 1e-12
+    assert ck.shape == ck_r.shape and rel(ck, ck_r) < 1e-12
+
+
+def test_vg_t1_closed_form_gradients():
+    """One step, S1 = P diag(g) S0 + beta k v^T with P = I - beta k k^T.  With
+    M = dS1 + q dO^T: dS0 = diag(g) P M and d(lg)_i = g_i ((P M) o S0)_i summed
+    over the row, dv = beta M^T k.  Distinct gates per channel, so a gate
+    applied to columns, a missing g_i factor or a gradient taken against the
+    decayed state all show."""
+    rng = np.random.default_rng(32)
+    Dk, Dv = 6, 4
+    q = unit_rows(rng, (1, 1, 1, Dk))
+    k = unit_rows(rng, (1, 1, 1, Dk))
+    v = rng.standard_normal((1, 1, 1, Dv))
+    lg = -rng.uniform(0.05, 2.0, (1, 1, 1, Dk))
+    b = np.full((1, 1, 1), math.log(3.0))   # beta = 3/4
+    S0 = rng.standard_normal((1, 1, Dk, Dv))
+    dO = rng.standard_normal((1, 1, 1, Dv))
+    dS = rng.standard_normal((1, 1, Dk, Dv))
+    beta, g = 0.75, np.exp(lg[0, 0, 0])
+    kk, qq = k[0, 0, 0], q[0, 0, 0] / math.sqrt(Dk)
+    P = np.eye(Dk) - beta * np.outer(kk, kk)
+    S1 = P @ np.diag(g) @ S0[0, 0] + beta * np.outer(kk, v[0, 0, 0])
+    o, st, _ = oracle.fwd_vg(q, k, v, lg, b, S0)
+    assert rel(st[0, 0], S1) < 1e-13 and rel(o[0, 0, 0], S1.T @ qq) < 1e-13
+    gr = oracle.bwd_vg(q, k, v, lg, b, S0, None, dO, dS)
+    M = dS[0, 0] + np.outer(qq, dO[0, 0, 0])
+    assert rel(gr["dstate"][0, 0], np.diag(g) @ P @ M) < 1e-12
+    assert rel(gr["dlg"][0, 0, 0], g * np.sum((P @ M) * S0[0, 0], axis=1)) < 1e-12
+    assert rel(gr["dv"][0, 0, 0], beta * M.T @ kk) < 1e-12
+
+
+def fd_check_vg(c, h=2.0 ** -20, tol=2e-7):
+    vals = {n: x.copy() for n, x in c.vals.items()}
+    gr = oracle.bwd_vg(*c.vg_args(), vals["dO"], vals.get("dS_final"))
+    gmap = dict(q="dq", k="dk", v="dv", lg="dlg", b="db", state0="dstate")
+
+    def L():
+        o, st, _ = oracle.fwd_vg(vals["q"], vals["k"], vals["v"], vals["lg"], vals["b"],
+                                 vals.get("state0"), c.mask)
+        return loss(vals, c.mask, o, st)
+
+    for n in gmap:
+        x = vals[n]
+        fd = np.empty_like(x)
+        flat, ff = x.reshape(-1), fd.reshape(-1)
+        for i in range(flat.size):
+            x0 = flat[i]
+            flat[i] = x0 + h
+            lp = L()
+            flat[i] = x0 - h
+            lm = L()
+            flat[i] = x0
+            ff[i] = (lp - lm) / (2 * h)
+        err = rel(gr[gmap[n]], fd)
+        assert err < tol, (n, err)
+    return gr
+
+
+def test_vg_fd_all_gradients():
+    """Central differences for all six gradients of the per-channel-gate form
+    on the PR's toy shape."""
+    fd_check_vg(inputs.vg_tiny())
+
+
+def test_vg_fd_masked():
+    """FD through masked steps; masked steps get dv = dlg = db = 0."""
+    c = inputs.make_vg_case("vgfdm", 2, 6, 1, 2, 8, 4, "f32", 33,
+                            mask=np.array([[1, 1, 0, 1, 0, 0], [1, 1, 1, 1, 1, 1]]))
+    gr = fd_check_vg(c)
+    assert np.all(gr["dlg"][0, [2, 4, 5]] == 0.0)
+    assert np.all(gr["db"][0, [2, 4, 5]] == 0.0)
+    assert np.all(gr["dv"][0, [2, 4, 5]] == 0.0)
+
+
+def test_vg_uniform_channels_equal_scalar_gate():
+    """With every channel's log-gate equal to the scalar gate's l, the
+    per-channel form is the scalar one: same o and state, and the channel sum
+    of d(lg) equals dl = da / (-exp(A_log) sigmoid(x)) (x below the clamp)."""
+    c = inputs.edge(65, masked=True)
+    v = c.vals
+    B, T, Hv, Dk = c.B, c.T, c.Hv, c.Dk
+    ell = np.empty((B, T, Hv))
+    for bi in range(B):
+        for t in range(T):
+            for h in range(Hv):
+                ell[bi, t, h] = oracle.gates(v["a"][bi, t, h], 0.0, v["A_log"][h], v["dt_bias"][h])[1]
+    lg = np.repeat(ell[..., None], Dk, axis=3)
+    o, st, ck = oracle.fwd(*c.oracle_args())
+    o2, st2, ck2 = oracle.fwd_vg(v["q"], v["k"], v["v"], lg, v["b"], v["state0"], c.mask)
+    assert rel(o2, o) < 1e-13 and rel(st2, st) < 1e-13 and rel(ck2, ck) < 1e-13
+    g1 = oracle.bwd(*c.oracle_args(), v["dO"], v["dS_final"])
+    g2 = oracle.bwd_vg(v["q"], v["k"], v["v"], lg, v["b"], v["state0"], c.mask, v["dO"],
+                       v["dS_final"])
+    for n in ("dq", "dk", "dv", "db", "dstate"):
+        assert rel(g2[n], g1[n]) < 1e-12, n
+    x = v["a"] + v["dt_bias"]
+    dl = g1["da"] / (-np.exp(v["A_log"]) / (1.0 + np.exp(-x)))
+    assert rel(g2["dlg"].sum(axis=3), dl) < 1e-10
+
+
+def test_vg_chunked_equals_unchunked_bitwise():
+    c = inputs.vg_edge(65, masked=True)
+    ref = oracle.bwd_vg(*c.vg_args(), c.vals["dO"], c.vals["dS_final"], chunk=0)
+    for ch in (64, 5):
+        got = oracle.bwd_vg(*c.vg_args(), c.vals["dO"], c.vals["dS_final"], chunk=ch)
+        for n in ref:
+            assert np.array_equal(ref[n], got[n]), (ch, n)
+
+
+def test_vg_euler_homogeneity():
+    """(o, S_T) are jointly linear in (v, S0) for any gates."""
+    c = inputs.vg_edge(65, masked=True)
+    v = c.vals
+    o, st, _ = oracle.fwd_vg(*c.vg_args())
+    gr = oracle.bwd_vg(*c.vg_args(), v["dO"], v["dS_final"])
+    lhs = np.sum(gr["dv"] * v["v"]) + np.sum(gr["dstate"] * v["state0"])
+    rhs = np.sum(v["dO"] * o) + np.sum(v["dS_final"] * st)
+    assert abs(lhs - rhs) <= 1e-12 * (abs(rhs) + np.sum(np.abs(v["dO"] * o)))
