@@ -180,6 +180,43 @@ int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const 
                     const uint8_t* mask, void* o, float* state_out, void* stream);
 
 /*
+ * Per-key-channel gate (mlx-lm VJP PR, "Models covered" and "Scope and
+ * follow-ups": Kimi-Linear runs the same rule with a gate that holds one
+ * value per key channel, g.ndim == 4).  The gate of step t and value head h
+ * is a vector g in R^Dk that scales the rows of the state:
+ *   S' = diag(g) S;  u = S'^T kn;  delta = beta (v - u);  S = S' + kn delta^T;
+ *   o = S^T qn,
+ * with kn, qn, beta = sigmoid(b) and masking as in gdn_fwd.  The pages give
+ * no formula that produces g, so the caller passes its logarithm directly
+ * (as the torch-to-nnef op contract passes a log-decay):
+ *   lg        [B,T,Hv,Dk] fp32, lg = log g (finite; -inf is not allowed)
+ * Runs the SCAN family only: d->algo AUTO or SCAN (CHUNK gives
+ * GDN_ERR_UNSUPPORTED); d->save is ignored.  Sizes and dtypes as gdn_fwd.
+ * ckpt has gdn_fwd's SCAN layout (gdn_ckpt_elems with save unset).  The
+ * workspace sizes come from the _vg queries; the backward's holds the
+ * states every 4 steps of every chunk being swept and per-slice row partials
+ * (about B*Hv*Dv*Dk*64 + B*T*Hv*Dv/8*3*Dk floats for Dk >= 64, Dv % 32 == 0).
+ */
+int gdn_fwd_vg_workspace_bytes(const gdn_dims* d, size_t* out);
+int gdn_bwd_vg_workspace_bytes(const gdn_dims* d, size_t* out);
+
+/* Forward with the per-key-channel gate.  Arguments as gdn_fwd, with lg in
+ * place of a, A_log, dt_bias. */
+int gdn_fwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, const float* lg,
+               const void* b, const float* state0, const uint8_t* mask, void* o,
+               float* state_out, float* ckpt, void* ws, size_t ws_bytes, void* stream);
+
+/* VJP of gdn_fwd_vg.  Arguments as gdn_bwd, with lg in place of a, A_log,
+ * dt_bias, and
+ *   dlg       [B,T,Hv,Dk] fp32 (out), the cotangent of lg
+ * in place of da, dA_log, ddt_bias.  Masked steps get dv = dlg = db = 0.
+ * Deterministic: every sum runs in a fixed order. */
+int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, const float* lg,
+               const void* b, const float* state0, const uint8_t* mask, const float* ckpt,
+               const void* dO, const float* dS_final, void* dq, void* dk, void* dv, float* dlg,
+               void* db, float* dstate, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Optional per-kernel timing, for benchmarks and profilers.  While `events`
  * is non-NULL, each kernel that the following gdn_fwd / gdn_bwd calls launch
  * (in launch order, i = 0, 1, ...) records events[2i] on the call's stream

@@ -24,8 +24,9 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-           "gdn_fwd", "gdn_bwd", "gdn_decode_conv", "gdn_set_kernel_events", "gdn_status_string",
-           "gdn_version")
+           "gdn_fwd", "gdn_bwd", "gdn_decode_conv", "gdn_fwd_vg_workspace_bytes",
+           "gdn_bwd_vg_workspace_bytes", "gdn_fwd_vg", "gdn_bwd_vg", "gdn_set_kernel_events",
+           "gdn_status_string", "gdn_version")
 
 
 class Dims(ctypes.Structure):
@@ -53,7 +54,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, S = ctypes.c_void_p, ctypes.c_size_t
         PD = ctypes.POINTER(Dims)
-        for n in ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes"):
+        for n in ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
+                  "gdn_fwd_vg_workspace_bytes", "gdn_bwd_vg_workspace_bytes"):
             getattr(L, n).argtypes = [PD, ctypes.POINTER(S)]
             getattr(L, n).restype = ctypes.c_int
         L.gdn_fwd.argtypes = [PD] + [P] * 13 + [S, P]
@@ -62,6 +64,10 @@ def lib():
         L.gdn_bwd.restype = ctypes.c_int
         L.gdn_decode_conv.argtypes = [PD] + [P] * 4 + [ctypes.c_int32] + [P] * 9
         L.gdn_decode_conv.restype = ctypes.c_int
+        L.gdn_fwd_vg.argtypes = [PD] + [P] * 11 + [S, P]
+        L.gdn_fwd_vg.restype = ctypes.c_int
+        L.gdn_bwd_vg.argtypes = [PD] + [P] * 17 + [S, P]
+        L.gdn_bwd_vg.restype = ctypes.c_int
         L.gdn_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
         L.gdn_set_kernel_events.restype = ctypes.c_int
         L.gdn_status_string.argtypes = [ctypes.c_int]
@@ -283,6 +289,120 @@ class Plan:
         rc = lib().gdn_bwd(*self._bargs)
         if rc:
             raise GdnError("gdn_bwd", rc)
+
+
+# ---- per-key-channel gate (gdn_fwd_vg / gdn_bwd_vg)
+
+def _check_inputs_vg(d, q, k, v, lg, b, state0, mask):
+    dev, dt = q.device, q.dtype
+    if dev.type != "cuda":
+        raise ValueError("gdn runs on the GPU; got device %s" % dev)
+    B, T, Hk, Hv, Dk, Dv = d.B, d.T, d.Hk, d.Hv, d.Dk, d.Dv
+    _check(q, "q", (B, T, Hk, Dk), dt, dev)
+    _check(k, "k", (B, T, Hk, Dk), dt, dev)
+    _check(v, "v", (B, T, Hv, Dv), dt, dev)
+    _check(lg, "lg", (B, T, Hv, Dk), torch.float32, dev)
+    _check(b, "b", (B, T, Hv), dt, dev)
+    if state0 is not None:
+        _check(state0, "state0", (B, Hv, Dk, Dv), torch.float32, dev)
+    if mask is not None:
+        _check(mask, "mask", (B, T), torch.uint8, dev)
+
+
+def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=None):
+    """Forward scan with a per-key-channel gate: lg [B,T,Hv,Dk] fp32 holds
+    log g, and g scales the state's rows.  Returns (o, state_out, ckpt)."""
+    d = _dims_of(q, v, ALGO_SCAN)
+    _check_inputs_vg(d, q, k, v, lg, b, state0, mask)
+    dev = q.device
+    o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
+    if state_out is None:
+        state_out = torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+    else:
+        _check(state_out, "state_out", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
+    nck = ckpt_elems(d)
+    ckpt = _alloc_ckpt(d, dev) if need_ckpt else None
+    wsb = _query("gdn_fwd_vg_workspace_bytes", d)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_fwd_vg(ctypes.byref(d), _p(q), _p(k), _p(v), _p(lg), _p(b), _p(state0),
+                          _p(mask), _p(o), _p(state_out),
+                          _p(ckpt) if (ckpt is not None and nck) else None,
+                          _p(ws), wsb, _stream(dev))
+    if rc:
+        raise GdnError("gdn_fwd_vg", rc)
+    return o, state_out, ckpt
+
+
+def bwd_vg(q, k, v, lg, b, state0, mask, ckpt, dO, dS_final=None):
+    """VJP of fwd_vg.  Returns dict(dq, dk, dv, dlg, db, dstate)."""
+    d = _dims_of(q, v, ALGO_SCAN)
+    _check_inputs_vg(d, q, k, v, lg, b, state0, mask)
+    dev = q.device
+    _check(dO, "dO", (d.B, d.T, d.Hv, d.Dv), q.dtype, dev)
+    if dS_final is not None:
+        _check(dS_final, "dS_final", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
+    nck = ckpt_elems(d)
+    if nck:
+        if ckpt is None or ckpt.numel() != nck:
+            raise ValueError("ckpt from gdn_fwd_vg with %d elements is required" % nck)
+        if ckpt.dtype != torch.float32 or not ckpt.is_contiguous() or ckpt.device != dev:
+            raise ValueError("ckpt must be a contiguous fp32 tensor on %s" % dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dlg=torch.empty_like(lg), db=torch.empty_like(b),
+               dstate=torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev))
+    wsb = _query("gdn_bwd_vg_workspace_bytes", d)
+    ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+    rc = lib().gdn_bwd_vg(ctypes.byref(d), _p(q), _p(k), _p(v), _p(lg), _p(b), _p(state0),
+                          _p(mask), _p(ckpt) if nck else None, _p(dO), _p(dS_final),
+                          *[_p(out[n]) for n in ("dq", "dk", "dv", "dlg", "db", "dstate")],
+                          _p(ws), wsb, _stream(dev))
+    if rc:
+        raise GdnError("gdn_bwd_vg", rc)
+    return out
+
+
+class PlanVg:
+    """Plan (above) for the per-key-channel-gate form: `t` maps q, k, v, lg,
+    b, state0, mask, dO, dS_final to device tensors."""
+
+    def __init__(self, t, stream=None):
+        q, v = t["q"], t["v"]
+        self.d = d = _dims_of(q, v, ALGO_SCAN)
+        _check_inputs_vg(d, q, t["k"], v, t["lg"], t["b"], t["state0"], t["mask"])
+        dev = q.device
+        self.t = t
+        self.o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
+        self.state_out = torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
+        self.ckpt = _alloc_ckpt(d, dev)
+        nck = self.ckpt.numel()
+        self.g = dict(dq=torch.empty_like(q), dk=torch.empty_like(t["k"]), dv=torch.empty_like(v),
+                      dlg=torch.empty_like(t["lg"]), db=torch.empty_like(t["b"]),
+                      dstate=torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev))
+        fws = _query("gdn_fwd_vg_workspace_bytes", d)
+        bws = _query("gdn_bwd_vg_workspace_bytes", d)
+        self.ws_f = torch.empty((max(fws, 1),), dtype=torch.uint8, device=dev)
+        self.ws_b = torch.empty((max(bws, 1),), dtype=torch.uint8, device=dev)
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        self.stream = st
+        sp = ctypes.c_void_p(st.cuda_stream)
+        ck = _p(self.ckpt) if nck else None
+        ins = [_p(t[n]) for n in ("q", "k", "v", "lg", "b", "state0", "mask")]
+        self._fargs = (ctypes.byref(d), *ins, _p(self.o), _p(self.state_out), ck,
+                       _p(self.ws_f), fws, sp)
+        self._bargs = (ctypes.byref(d), *ins, ck, _p(t["dO"]), _p(t["dS_final"]),
+                       *[_p(self.g[n]) for n in ("dq", "dk", "dv", "dlg", "db", "dstate")],
+                       _p(self.ws_b), bws, sp)
+        self.fwd_ws_bytes, self.bwd_ws_bytes = fws, bws
+
+    def fwd(self):
+        rc = lib().gdn_fwd_vg(*self._fargs)
+        if rc:
+            raise GdnError("gdn_fwd_vg", rc)
+
+    def bwd(self):
+        rc = lib().gdn_bwd_vg(*self._bargs)
+        if rc:
+            raise GdnError("gdn_bwd_vg", rc)
 
 
 def decode_conv(x, conv_w, conv_state, a, b, A_log, dt_bias, Hk, Dk, Hv, Dv, state0=None,

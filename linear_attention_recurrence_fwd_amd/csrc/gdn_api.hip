@@ -216,6 +216,49 @@ gdn::StepScalars scalars(void* ws, const Layout& L) {
                           at<float>(ws, L.ell), at<float>(ws, L.beta)};
 }
 
+// ---- per-key-channel gate (scan family only)
+
+struct VgLayout {
+  size_t rq, rk, kq, beta, sub, part, pdb, total;
+};
+
+VgLayout vg_layout(const Dims& d, bool bwd) {
+  VgLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t nfloat) {
+    size_t o = off;
+    off += align_up(nfloat * sizeof(float));
+    return o;
+  };
+  const size_t bt = static_cast<size_t>(d.B) * d.T;
+  L.rq = take(bt * d.Hk);
+  L.rk = take(bt * d.Hk);
+  L.kq = take(bt * d.Hk);
+  L.beta = take(bt * d.Hv);
+  if (bwd) {
+    const size_t ns = gdn::vg_nslice(d.Dv);
+    L.sub = take(gdn::vg_sub_floats(d));
+    L.part = take(bt * d.Hv * ns * 3 * d.Dk);
+    L.pdb = take(bt * d.Hv * ns);
+  }
+  L.total = off;
+  return L;
+}
+
+gdn::StepScalars vg_scalars(void* ws, const VgLayout& L) {
+  return gdn::StepScalars{at<float>(ws, L.rq), at<float>(ws, L.rk), at<float>(ws, L.kq), nullptr,
+                          at<float>(ws, L.beta)};
+}
+
+int check_vg(const gdn_dims* p, Dims* out) {
+  int rc = check_dims(p, out);
+  if (rc) return rc;
+  if (p->algo == GDN_ALGO_CHUNK) return GDN_ERR_UNSUPPORTED;
+  if (static_cast<double>(p->B) * p->T * p->Hv * p->Dk > static_cast<double>(INT_MAX))
+    return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -361,6 +404,71 @@ int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const 
   gdn::DecodeConvArgs ca{dd, x, conv_w, conv_state, conv_state_out, conv_k, a, b, A_log, dt_bias,
                          state0, mask, o, state_out};
   if (!launch(st, [&] { return gdn::launch_decode_conv(ca, d->dtype == GDN_BF16, st); })) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_fwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
+  Dims dd;
+  int rc = check_vg(d, &dd);
+  if (rc) return rc;
+  if (!out) return GDN_ERR_INVALID_ARG;
+  *out = vg_layout(dd, false).total;
+  return GDN_OK;
+}
+
+int gdn_bwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
+  Dims dd;
+  int rc = check_vg(d, &dd);
+  if (rc) return rc;
+  if (!out) return GDN_ERR_INVALID_ARG;
+  *out = vg_layout(dd, true).total;
+  return GDN_OK;
+}
+
+int gdn_fwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, const float* lg,
+               const void* b, const float* state0, const uint8_t* mask, void* o,
+               float* state_out, float* ckpt, void* ws, size_t ws_bytes, void* stream) {
+  Dims dd;
+  int rc = check_vg(d, &dd);
+  if (rc) return rc;
+  if (!state_out) return GDN_ERR_INVALID_ARG;
+  if (dd.T > 0 && (!q || !k || !v || !lg || !b || !o)) return GDN_ERR_INVALID_ARG;
+  const VgLayout L = vg_layout(dd, false);
+  if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
+  const bool bf = d->dtype == GDN_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const gdn::StepScalars s = vg_scalars(ws, L);
+  gdn::PrepArgs pa{dd, q, k, nullptr, b, nullptr, nullptr, mask, s};
+  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
+  gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt, lg, mask};
+  if (!launch(st, [&] { return gdn::launch_scan_fwd(fa, bf, st); })) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, const float* lg,
+               const void* b, const float* state0, const uint8_t* mask, const float* ckpt,
+               const void* dO, const float* dS_final, void* dq, void* dk, void* dv, float* dlg,
+               void* db, float* dstate, void* ws, size_t ws_bytes, void* stream) {
+  Dims dd;
+  int rc = check_vg(d, &dd);
+  if (rc) return rc;
+  if (!dstate) return GDN_ERR_INVALID_ARG;
+  if (dd.T > 0 && (!q || !k || !v || !lg || !b || !dO || !dq || !dk || !dv || !dlg || !db))
+    return GDN_ERR_INVALID_ARG;
+  if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
+  const VgLayout L = vg_layout(dd, true);
+  if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
+  const bool bf = d->dtype == GDN_BF16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const gdn::StepScalars s = vg_scalars(ws, L);
+  gdn::PrepArgs pa{dd, q, k, nullptr, b, nullptr, nullptr, mask, s};
+  if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
+  gdn::ScanBwdVgArgs ba{dd, q, k, v, dO, lg, mask, state0, ckpt, dS_final, s,
+                        at<float>(ws, L.sub), at<float>(ws, L.part), at<float>(ws, L.pdb), dv, dstate};
+  if (!launch(st, [&] { return gdn::launch_scan_bwd_vg(ba, bf, st); })) return GDN_ERR_HIP;
+  gdn::VgReduceArgs ra{dd, gdn::vg_nslice(dd.Dv), q, k, s, at<float>(ws, L.part), at<float>(ws, L.pdb),
+                       dq, dk, db, dlg};
+  if (!launch(st, [&] { return gdn::launch_vg_reduce(ra, bf, st); })) return GDN_ERR_HIP;
   return GDN_OK;
 }
 

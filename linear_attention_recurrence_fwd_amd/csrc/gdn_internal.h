@@ -40,6 +40,10 @@ struct ScanFwdArgs {
   void* o;
   float* state_out;
   float* ckpt;  // may be null
+  // Per-key-channel gate: log-gates [B,T,Hv,Dk] fp32 (null = the scalar gate
+  // s.ell) and the mask they need (a masked step has gate 1).
+  const float* lg;
+  const uint8_t* mask;
 };
 
 // Sweep of the backward: recompute each chunk from its checkpoint, then walk
@@ -56,6 +60,37 @@ struct ScanBwdArgs {
   float* dHend;   // [NC,B,Hv,Dk,Dv] dL/d(state at the end of chunk c)
   float* dstate;  // [B,Hv,Dk,Dv]
 };
+
+// Reverse sweep with a per-key-channel gate (log-gates lg [B,T,Hv,Dk]).
+struct ScanBwdVgArgs {
+  Dims d;
+  const void *q, *k, *v, *dO;
+  const float* lg;
+  const uint8_t* mask;
+  const float *state0, *ckpt, *dS_final;  // state0 / dS_final may be null
+  StepScalars s;                          // rq, rk, beta (ell unused)
+  float* sub;     // sub-checkpoints, vg_sub_floats(d)
+  float* part;    // [B,T,Hv,nslice,3,Dk] row partials of dqn, dkn, dlg per column slice
+  float* pdb;     // [B,T,Hv,nslice] partials of dL/dbeta
+  void* dv;       // [B,T,Hv,Dv] dtype
+  float* dstate;  // [B,Hv,Dk,Dv]
+};
+struct VgReduceArgs {
+  Dims d;
+  int nslice;
+  const void *q, *k;
+  StepScalars s;
+  const float *part, *pdb;
+  void *dq, *dk, *db;  // dtype
+  float* dlg;          // [B,T,Hv,Dk]
+};
+// Lane rows of the per-channel-gate sweep (rows l + 64 m, m < vg_rows).
+inline int vg_rows(int Dk) { return Dk <= 64 ? 1 : Dk / 64; }
+// Sub-checkpoint floats: every 4 steps, the states of all (b, h) (rows padded
+// to 64 vg_rows).
+inline size_t vg_sub_floats(const Dims& d) {
+  return static_cast<size_t>(d.B) * d.Hv * d.Dv * vg_rows(d.Dk) * 64 * (64 / 4);
+}
 
 struct ChunkGradArgs {
   Dims d;
@@ -218,6 +253,8 @@ hipError_t launch_prep(const PrepArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_fwd(const ScanFwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_chunk_grad(const ChunkGradArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_scan_bwd_vg(const ScanBwdVgArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_vg_reduce(const VgReduceArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
@@ -233,6 +270,7 @@ inline bool chunk_supported(int Dk, int Dv, bool bf16) {
 // Column-slice geometry of the scan kernels: NW waves x 8 columns each.
 inline int scan_waves(int Dv) { return Dv % 32 == 0 ? 4 : 1; }
 inline int scan_nslice(int Dv) { return Dv / (8 * scan_waves(Dv)); }
+inline int vg_nslice(int Dv) { return scan_nslice(Dv); }
 inline bool scan_supported(int Dk, int Dv) {
   bool dk = Dk == 16 || Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256;
   bool dv = Dv >= 8 && Dv <= 256 && Dv % 8 == 0 && (Dv <= 24 || Dv % 32 == 0);

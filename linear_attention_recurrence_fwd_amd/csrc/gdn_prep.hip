@@ -3,7 +3,8 @@
 // 1e-6, q scaled by 1/sqrt(width); mlx-lm VJP PR: g = exp(-exp(A_log) *
 // softplus(a + dt_bias)) with the softplus argument clamped, beta = sigmoid(b)).
 // A masked step is stored as l = 0 (g = 1) and beta = 0, which leaves the state
-// unchanged and still reads o from it.
+// unchanged and still reads o from it.  With a per-key-channel gate (a null)
+// only the norms and beta are produced.
 #include "gdn_dev.h"
 #include "gdn_internal.h"
 
@@ -49,12 +50,14 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepArgs p) {
     const size_t o = static_cast<size_t>(bt) * d.Hv + h;
     float ell = 0.f, beta = 0.f;
     if (valid) {
-      const float x = to_f32(a[o]) + p.dt_bias[h];
-      const float xc = fminf(x, kClamp);
-      ell = -expf(p.A_log[h]) * softplus_f(xc);
+      if (a) {
+        const float x = to_f32(a[o]) + p.dt_bias[h];
+        const float xc = fminf(x, kClamp);
+        ell = -expf(p.A_log[h]) * softplus_f(xc);
+      }
       beta = sigmoid_f(to_f32(b[o]));
     }
-    p.s.ell[o] = ell;
+    if (p.s.ell) p.s.ell[o] = ell;
     p.s.beta[o] = beta;
   }
 }

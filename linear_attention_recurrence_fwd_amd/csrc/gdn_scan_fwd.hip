@@ -18,6 +18,11 @@
 // the current tile is computed (register prefetch), so their latency hides
 // behind the scan.  States go to/from global memory through an LDS transpose
 // so every global access is row-contiguous.
+//
+// Per-key-channel gate (mlx-lm VJP PR, "Models covered": Kimi-Linear's gate
+// has one value per key channel): the rows of S are scaled by g_i = e^{lg_i}
+// instead of one scalar; the lane multiplies its rows' kn, qn by g_i before
+// the two reads and its rows of S by g_i in the update.
 #include "gdn_dev.h"
 #include "gdn_internal.h"
 
@@ -26,7 +31,7 @@ namespace {
 
 constexpr int TS = 16;  // steps per staged tile (divides the checkpoint period)
 
-template <int RI, int NW, typename T>
+template <int RI, int NW, typename T, bool VG>
 struct ScanFwd {
   static constexpr int DK = 16 * RI;
   static constexpr int JS = 8 * NW;   // columns per workgroup
@@ -36,12 +41,15 @@ struct ScanFwd {
   static constexpr int QK_PER_T = (QK_UNITS + NT - 1) / NT;
   static constexpr int V_UNITS = TS * JS / EPU;
   static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  static constexpr int LG_UNITS = VG ? TS * DK / 4 : 0;   // fp32 log-gates, 4 per unit
+  static constexpr int LG_PER_T = VG ? (LG_UNITS + NT - 1) / NT : 1;
 
   struct Smem {
     float k[2][TS][DK];
     float q[2][TS][DK];
     float v[2][TS][JS];
     float ell[2][TS], beta[2][TS], kq[2][TS];
+    float g[VG ? 2 : 1][TS][VG ? DK : 1];  // per-channel gates e^lg (1 on masked steps)
     float o[TS][JS];
     float st[DK][JS + 1];
   };
@@ -51,6 +59,7 @@ struct ScanFwd {
     uint4 k[QK_PER_T], q[QK_PER_T], v[V_PER_T];
     float rk[QK_PER_T], rq[QK_PER_T];
     float ell, beta, kq;
+    float4 lg[LG_PER_T];
   };
 
   __device__ static void load_tile(const ScanFwdArgs& p, int b, int h, int j, int col0,
@@ -86,12 +95,26 @@ struct ScanFwd {
         s.v[n] = *reinterpret_cast<const uint4*>(static_cast<const T*>(p.v) + row * d.Dv + col0 + e0);
       }
     }
+    if constexpr (VG) {
+#pragma unroll
+      for (int n = 0; n < LG_PER_T; ++n) {
+        const int u = tid + n * NT;
+        const int tt = u / (DK / 4), e0 = (u % (DK / 4)) * 4;
+        const int t = t0 + tt;
+        s.lg[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u < LG_UNITS && t < d.T) {
+          const size_t r = static_cast<size_t>(b) * d.T + t;
+          if (p.mask == nullptr || p.mask[r] != 0)
+            s.lg[n] = *reinterpret_cast<const float4*>(p.lg + (r * d.Hv + h) * DK + e0);
+        }
+      }
+    }
     s.ell = 0.f;
     s.beta = 0.f;
     s.kq = 0.f;
     if (tid < TS && t0 + tid < d.T) {
       const size_t r = static_cast<size_t>(b) * d.T + t0 + tid;
-      s.ell = p.s.ell[r * d.Hv + h];
+      if constexpr (!VG) s.ell = p.s.ell[r * d.Hv + h];
       s.beta = p.s.beta[r * d.Hv + h];
       s.kq = p.s.kq[r * d.Hk + j];
     }
@@ -127,6 +150,19 @@ struct ScanFwd {
       sm.ell[buf][tid] = s.ell;
       sm.beta[buf][tid] = s.beta;
       sm.kq[buf][tid] = s.kq;
+    }
+    if constexpr (VG) {
+#pragma unroll
+      for (int n = 0; n < LG_PER_T; ++n) {
+        const int u = tid + n * NT;
+        if (u < LG_UNITS) {
+          const int tt = u / (DK / 4), e0 = (u % (DK / 4)) * 4;
+          sm.g[buf][tt][e0 + 0] = expf(s.lg[n].x);
+          sm.g[buf][tt][e0 + 1] = expf(s.lg[n].y);
+          sm.g[buf][tt][e0 + 2] = expf(s.lg[n].z);
+          sm.g[buf][tt][e0 + 3] = expf(s.lg[n].w);
+        }
+      }
     }
   }
 
@@ -189,33 +225,39 @@ struct ScanFwd {
       if (it + 1 < ntile) load_tile(p, b, h, j, col0, t0 + TS, stg);
       const int nsteps = min(TS, d.T - t0);
       for (int tt = 0; tt < nsteps; ++tt) {
-        float kr[RI], qr[RI];
+        float kr[RI], qr[RI], gr[RI];
 #pragma unroll
         for (int r = 0; r < RI; ++r) {
           kr[r] = sm.k[buf][tt][li * RI + r];
           qr[r] = sm.q[buf][tt][li * RI + r];
+          if constexpr (VG) gr[r] = sm.g[buf][tt][li * RI + r];
         }
+        // Per-channel gate: both reads see the decayed rows, u = S^T (g o kn),
+        // p = S^T (g o qn), and o = p + (kn . qn) delta.
         float pu0 = 0.f, pu1 = 0.f, pp0 = 0.f, pp1 = 0.f;
 #pragma unroll
         for (int r = 0; r < RI; ++r) {
-          pu0 = fmaf(S[r][0], kr[r], pu0);
-          pu1 = fmaf(S[r][1], kr[r], pu1);
-          pp0 = fmaf(S[r][0], qr[r], pp0);
-          pp1 = fmaf(S[r][1], qr[r], pp1);
+          const float kg = VG ? kr[r] * gr[r] : kr[r];
+          const float qg = VG ? qr[r] * gr[r] : qr[r];
+          pu0 = fmaf(S[r][0], kg, pu0);
+          pu1 = fmaf(S[r][1], kg, pu1);
+          pp0 = fmaf(S[r][0], qg, pp0);
+          pp1 = fmaf(S[r][1], qg, pp1);
         }
         pu0 = row_sum16(pu0);
         pu1 = row_sum16(pu1);
         pp0 = row_sum16(pp0);
         pp1 = row_sum16(pp1);
-        const float g = expf(sm.ell[buf][tt]);
+        const float g = VG ? 1.f : expf(sm.ell[buf][tt]);
         const float beta = sm.beta[buf][tt], kq = sm.kq[buf][tt];
         float d0 = beta * (sm.v[buf][tt][lc] - g * pu0);
         float d1 = beta * (sm.v[buf][tt][lc + 1] - g * pu1);
         if (beta == 0.f) d0 = d1 = 0.f;  // masked step: v is not read
 #pragma unroll
         for (int r = 0; r < RI; ++r) {
-          S[r][0] = fmaf(kr[r], d0, g * S[r][0]);
-          S[r][1] = fmaf(kr[r], d1, g * S[r][1]);
+          const float gg = VG ? gr[r] : g;
+          S[r][0] = fmaf(kr[r], d0, gg * S[r][0]);
+          S[r][1] = fmaf(kr[r], d1, gg * S[r][1]);
         }
         if (li == 0) {
           sm.o[tt][lc] = fmaf(kq, d0, g * pp0);
@@ -239,9 +281,9 @@ struct ScanFwd {
   }
 };
 
-template <int RI, int NW, typename T>
+template <int RI, int NW, typename T, bool VG>
 __global__ void __launch_bounds__(64 * NW) scan_fwd_kernel(ScanFwdArgs p) {
-  using K = ScanFwd<RI, NW, T>;
+  using K = ScanFwd<RI, NW, T, VG>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }
@@ -250,10 +292,17 @@ template <int RI, typename T>
 hipError_t launch_nw(const ScanFwdArgs& a, hipStream_t st) {
   const int nw = scan_waves(a.d.Dv);
   dim3 grid(a.d.B * a.d.Hv, scan_nslice(a.d.Dv));
-  if (nw == 4)
-    scan_fwd_kernel<RI, 4, T><<<grid, 256, 0, st>>>(a);
-  else
-    scan_fwd_kernel<RI, 1, T><<<grid, 64, 0, st>>>(a);
+  if (a.lg) {
+    if (nw == 4)
+      scan_fwd_kernel<RI, 4, T, true><<<grid, 256, 0, st>>>(a);
+    else
+      scan_fwd_kernel<RI, 1, T, true><<<grid, 64, 0, st>>>(a);
+  } else {
+    if (nw == 4)
+      scan_fwd_kernel<RI, 4, T, false><<<grid, 256, 0, st>>>(a);
+    else
+      scan_fwd_kernel<RI, 1, T, false><<<grid, 64, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

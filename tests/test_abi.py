@@ -182,3 +182,33 @@ def test_decode_conv_rejects_before_launch():
         args = list(p)
         args[i] = None
         assert call(ok, args=args) == 1, i
+
+
+def test_vg_rejects_before_launch():
+    """gdn_fwd_vg / gdn_bwd_vg: the chunk family is not built for the
+    per-channel gate, and required pointers and the workspace are checked
+    before any launch (the pointers here are never dereferenced)."""
+    lib = B.lib()
+    out = ctypes.c_size_t(0)
+    chunk = B.make_dims(1, 128, 2, 4, 64, 32, B.GDN_BF16, B.ALGO_CHUNK)
+    assert lib.gdn_fwd_vg_workspace_bytes(ctypes.byref(chunk), ctypes.byref(out)) == 2
+    assert lib.gdn_bwd_vg_workspace_bytes(ctypes.byref(chunk), ctypes.byref(out)) == 2
+    d = B.make_dims(1, 128, 2, 4, 64, 32, B.GDN_F32)
+    assert lib.gdn_fwd_vg_workspace_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
+    fws = out.value
+    assert lib.gdn_bwd_vg_workspace_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
+    bws = out.value
+    # sub-checkpoints (every 4 steps of a chunk, rows padded to 64) + partials
+    assert bws >= fws + 4 * (1 * 4 * 32 * 64 * 16 + 1 * 128 * 4 * 1 * 3 * 64)
+    f = _fake(10)  # q k v lg b state0 mask o state_out ckpt
+    for i in (0, 1, 2, 3, 4, 7, 8):
+        args = list(f)
+        args[i] = None
+        assert lib.gdn_fwd_vg(ctypes.byref(d), *args, f[0], fws, None) == 1, i
+    assert lib.gdn_fwd_vg(ctypes.byref(d), *f, f[0], fws - 1, None) == 3
+    g = _fake(16)  # q k v lg b state0 mask ckpt dO dS dq dk dv dlg db dstate
+    for i in (0, 1, 2, 3, 4, 7, 8, 10, 11, 12, 13, 14, 15):
+        args = list(g)
+        args[i] = None
+        assert lib.gdn_bwd_vg(ctypes.byref(d), *args, g[0], bws, None) == 1, i
+    assert lib.gdn_bwd_vg(ctypes.byref(d), *g, g[0], bws - 1, None) == 3

@@ -1,0 +1,120 @@
+"""GPU parity of the per-key-channel gate (gdn_fwd_vg / gdn_bwd_vg through
+the C ABI) against the fp64 oracle (oracle.fwd_vg / oracle.bwd_vg).
+
+Tolerances as for the scalar gate (normwise per tensor, max|x - ref| /
+max|ref|): 1e-4 for fp32 workloads, 2e-2 for bf16.  Shapes cover every lane
+layout of the reverse sweep (Dk = 16 .. 256: one to four rows per lane, rows
+padded below 64; Dv with one or four waves per workgroup), ragged chunk tails
+and recompute blocks, masks, the Qwen3.5-9B layer shape at T = 256 and 2048
+with a per-channel gate, and a Kimi-Linear-like shape (32 heads of 128; the
+pages name the model but not its sizes, so the sizes are an assumption).
+Repeated runs must be bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL, dev_tensor, relerr, say, to64
+from linear_attention_recurrence_fwd_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+VG_GRADS = ("dq", "dk", "dv", "dlg", "db", "dstate")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.lib()
+
+
+def upload_vg(case):
+    t = {n: dev_tensor(case, n) for n in ("q", "k", "v", "lg", "b", "state0", "dO", "dS_final")}
+    t["mask"] = None if case.mask is None else torch.from_numpy(case.mask).cuda()
+    return t
+
+
+def run_vg(t):
+    o, st, ck = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"])
+    g = binding.bwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"], ck,
+                       t["dO"], t["dS_final"])
+    return o, st, ck, g
+
+
+def compare_vg(case, nthreads=8):
+    tol = TOL[case.dtype]
+    say("[vg] case=%s B=%d T=%d Hk=%d Hv=%d Dk=%d Dv=%d dtype=%s" % (
+        case.name, case.B, case.T, case.Hk, case.Hv, case.Dk, case.Dv, case.dtype))
+    t = upload_vg(case)
+    o, st, ck, g = run_vg(t)
+    torch.cuda.synchronize()
+    v = case.vals
+    ro, rst, rck = oracle.fwd_vg(*case.vg_args(), nthreads=nthreads)
+    rg = oracle.bwd_vg(*case.vg_args(), v["dO"], v.get("dS_final"), nthreads=nthreads)
+    errs = {"o": relerr(to64(o), ro), "state": relerr(to64(st), rst)}
+    if rck.shape[0]:
+        errs["ckpt"] = relerr(to64(ck), rck)
+    for n in VG_GRADS:
+        errs[n] = relerr(to64(g[n]), rg[n])
+    say("[vg] errors " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    for n, x in list(g.items()) + [("o", o), ("state", st)]:
+        assert torch.isfinite(x.float()).all(), n
+    if case.mask is not None:   # masked steps: exact zeros
+        m = torch.from_numpy(case.mask == 0)
+        for n in ("dlg", "db", "dv"):
+            assert torch.all(g[n].cpu()[m] == 0), n
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, bad
+    return t, (o, st, ck, g)
+
+
+def test_vg_tiny():
+    compare_vg(inputs.vg_tiny())
+
+
+@pytest.mark.parametrize("T", [1, 3, 64, 65, 130, 1024])
+@pytest.mark.parametrize("masked", [False, True])
+def test_vg_edge(T, masked):
+    compare_vg(inputs.vg_edge(T, masked=masked))
+
+
+@pytest.mark.parametrize("Dk,Dv,dtype", [(16, 8, "f32"), (32, 16, "f32"), (32, 24, "bf16"),
+                                         (128, 64, "bf16"), (256, 32, "f32"), (256, 8, "f32"),
+                                         (192, 96, "f32")])
+def test_vg_shapes(Dk, Dv, dtype):
+    B, T = 2, 77
+    mask = np.ones((B, T), dtype=np.uint8)
+    mask[1, 40:] = 0
+    mask[0, 5] = 0
+    c = inputs.make_vg_case("vg_Dk%d_Dv%d_%s" % (Dk, Dv, dtype), B, T, 2, 4, Dk, Dv, dtype,
+                            9000 + Dk + Dv, mask=mask)
+    compare_vg(c)
+
+
+def test_vg_kimi_like():
+    compare_vg(inputs.make_vg_case("vg_kimi_like", 1, 256, 32, 32, 128, 128, "bf16", 9100,
+                                   state_std=None, dS_final=False))
+
+
+def test_vg_qwen35_9b_t256():
+    compare_vg(inputs.vg_qwen35_9b(256))
+
+
+def test_vg_qwen35_9b_t2048():
+    compare_vg(inputs.vg_qwen35_9b(2048), nthreads=16)
+
+
+def test_vg_deterministic_repeat():
+    c = inputs.vg_qwen35_9b(256)
+    say("[vg determinism] case=%s" % c.name)
+    t = upload_vg(c)
+    outs = []
+    for _ in range(3):
+        o, st, ck, g = run_vg(t)
+        outs.append([o, st, ck] + [g[n] for n in VG_GRADS])
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for x, y in zip(outs[0], other):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
