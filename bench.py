@@ -7,7 +7,8 @@ state, synthetic seeded inputs (the workload of the mlx-lm VJP PR's
 performance table).  One step = gdn_fwd (with checkpoints) + gdn_bwd on the
 same resident inputs.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 9b_t2048|9b_t256|decode|decode_conv]
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+                  [--config 9b_t2048|9b_t256|decode|decode_conv|vg_t2048|vg_t256]
 """
 from __future__ import annotations
 
@@ -43,6 +44,15 @@ KERNELS = {
 #   chunk_grad the method's per-step gradient contractions: dq = S dO
 #              1 fma, dk = D delta + S' du 2 fma, dg = <dS', S> 1 fma      = 8
 FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
+# Per-key-channel gate (gdn_fwd_vg / gdn_bwd_vg): the same forward (the gate
+# is applied per row, not per element), and the reverse sweep as one kernel:
+#   scan_bwd_vg  recompute 5 (decay 1 mul, read u 1 fma, update 1 fma) +
+#                reverse: D += qn dO^T 1 fma, dqn = S dO 1 fma, eps = D^T kn
+#                1 fma, dS' = D + kn du^T 1 fma, dkn = D delta + S' du 2 fma,
+#                dlg = <dS', S> along the row 1 fma, carry D = g dS' 1 mul    = 20
+KERNELS["vg"] = ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd_vg", "vg_reduce"]
+FLOPS_PER_ELEM.update({"scan_bwd_vg": 20})
+VG_METRIC = "fwd+bwd tokens/sec with a per-key-channel gate at Hk16/Hv64/Dk192/Dv128 bf16, T=2048"
 
 
 def kernel_bytes(B, T, Hk, Hv, Dk, Dv, io, state0=False, dS_final=False):
@@ -271,6 +281,130 @@ def bench_train(args, torch, binding, inputs):
     return out
 
 
+def vg_method_bytes(B, T, Hk, Hv, Dk, Dv, io):
+    """method_bytes with the per-channel log-gates (fp32 [B,T,Hv,Dk]) in place
+    of a and the parameters, and their gradient in place of da."""
+    Q = B * T * Hk * Dk * io
+    V = B * T * Hv * Dv * io
+    Bt = B * T * Hv * io
+    LG = B * T * Hv * Dk * 4
+    Sig = B * Hv * Dk * Dv * 4
+    CK = max(math.ceil(T / 64) - 1, 0) * Sig
+    fwd = 2 * Q + V + LG + Bt + V + Sig + CK
+    bwd = (2 * Q + V + LG + Bt + CK + V) + (2 * Q + V + LG + Bt + Sig)
+    return fwd, bwd
+
+
+def cpu_baseline_vg(T):
+    """The fp64 oracle of the per-channel-gate form on the same bounded sample
+    as cpu_baseline (half of the heads of the 9B shape)."""
+    import oracle
+    from linear_attention_recurrence_fwd_amd import inputs
+    threads = max(1, min(16, os.cpu_count() or 1))
+    c = inputs.make_vg_case("vg_9b_sample", 1, T, 8, 32, 192, 128, "bf16", 8000 + T,
+                            state_std=None, dS_final=False)
+    oracle.fwd_vg(*c.vg_args(), nthreads=threads)
+    t0 = time.perf_counter()
+    oracle.fwd_vg(*c.vg_args(), nthreads=threads)
+    oracle.bwd_vg(*c.vg_args(), c.vals["dO"], None, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(c.B * T / (dt * 2), 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "fp64 oracle fwd+bwd with per-channel gates, B=1 T=%d, Hk=8 Hv=32 Dk=192 "
+                      "Dv=128 (1/2 of the heads), %.2f s wall on %d threads; tokens/s scaled by 2"
+                      % (T, dt, threads)}
+
+
+def bench_vg(args, torch, binding, inputs):
+    """The 9B layer shape with a per-key-channel gate (scan kernels, fp32
+    arithmetic, bf16 I/O), fwd + bwd per step."""
+    T = {"vg_t2048": 2048, "vg_t256": 256}[args.config]
+    case = inputs.vg_qwen35_9b(T)
+    dev = torch.device("cuda:0")
+
+    def up(n):
+        import numpy as np
+        x = case.store(n)
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    t = {n: up(n) for n in ("q", "k", "v", "lg", "b", "state0", "dO", "dS_final")}
+    t["mask"] = None
+    plan = binding.PlanVg(t)
+    for _ in range(args.warmup):
+        plan.fwd()
+        plan.bwd()
+    torch.cuda.synchronize()
+    kernels = KERNELS["vg"]
+    nk = len(kernels)
+    lib = binding.lib()
+    sp = ctypes.c_void_p(plan.stream.cuda_stream)
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan.fwd()
+        plan.bwd()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.elapsed_ms(0, 1)
+    ev.close()
+    ev = HipEvents(2 * nk * args.steps)
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        lib.gdn_set_kernel_events(ev.ptr(2 * nk * s_), 2 * nk)
+        plan.fwd()
+        plan.bwd()
+    torch.cuda.synchronize()
+    lib.gdn_set_kernel_events(None, 0)
+    per_kernel = {k: 0.0 for k in kernels}
+    for s_ in range(args.steps):
+        for i, k in enumerate(kernels):
+            per_kernel[k] += ev.elapsed_ms(2 * nk * s_ + 2 * i, 2 * nk * s_ + 2 * i + 1)
+    ev.close()
+    per_kernel = {k: v / args.steps for k, v in per_kernel.items()}
+    ms = total_ms / args.steps
+    B, Hk, Hv, Dk, Dv = case.B, case.Hk, case.Hv, case.Dk, case.Dv
+    tokens = B * T
+    value = tokens / (ms / 1e3)
+    E = B * T * Hv * Dk * Dv
+    dom = max(per_kernel, key=lambda k: per_kernel[k])
+    flops = FLOPS_PER_ELEM.get(dom, 0) * E
+    achieved = flops / (per_kernel[dom] / 1e3) / 1e12
+    fb, bb = vg_method_bytes(B, T, Hk, Hv, Dk, Dv, 2)
+    return {
+        "metric": VG_METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gated delta rule fwd+bwd with a per-key-channel gate, "
+                               "Qwen3.5-9B GDN layer shape",
+                   "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                   "io_dtype": "bf16", "state_dtype": "f32", "algo": "scan"},
+        "roofline": {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
+                     "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved * 1e12 / FP32_VEC_PEAK, 4), "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": round(per_kernel[dom], 4)},
+        "hbm_roofline_step": {"method_bytes": fb + bb, "achieved_GBps": round(
+            (fb + bb) / (ms / 1e3) / 1e9, 1), "peak_GBps": HBM_PEAK / 1e9,
+            "frac": round((fb + bb) / (ms / 1e3) / HBM_PEAK, 5)},
+        "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "wall_s_timed": round(wall, 3),
+    }
+
+
 def bench_decode(args, torch, binding, inputs):
     """Decode workload: B=64, Hk=16, Hv=32, Dk=Dv=128, one token per call, the
     state updated in place; a step is 64 consecutive calls."""
@@ -421,7 +555,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="9b_t2048", choices=["9b_t2048", "9b_t256", "decode", "decode_conv"])
+    ap.add_argument("--config", default="9b_t2048",
+                    choices=["9b_t2048", "9b_t256", "decode", "decode_conv", "vg_t2048", "vg_t256"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -443,6 +578,10 @@ def main():
         out = bench_decode(args, torch, binding, inputs)
     elif args.config == "decode_conv":
         out = bench_decode_conv(args, torch, binding, inputs)
+    elif args.config.startswith("vg_"):
+        out = bench_vg(args, torch, binding, inputs)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_vg(out["config"]["T"])
     else:
         out = bench_train(args, torch, binding, inputs)
         if not args.no_cpu_baseline:

@@ -28,6 +28,8 @@
 // are summed over the workgroup's waves and written per column slice; a
 // second kernel sums the slices (and the value heads of a key head) in a fixed
 // order and applies the normalisation backward.
+#include <type_traits>
+
 #include "gdn_dev.h"
 #include "gdn_internal.h"
 
@@ -57,12 +59,20 @@ __device__ __forceinline__ void put8(float* dst, const float (&x)[8], float s, i
   }
 }
 
-template <int RM, int NW, typename T>
+template <int DK, int NW, typename T>
 struct ScanBwdVg {
-  static constexpr int DKP = 64 * RM;  // rows per lane layout (padded)
-  static constexpr int JS = 8 * NW;    // columns per workgroup
+  static constexpr int RM = DK <= 64 ? 1 : DK / 64;  // rows per lane
+  static constexpr int DKP = 64 * RM;                // rows of the lane layout (padded)
+  static constexpr int JS = 8 * NW;                  // columns per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr int NRB = RM <= 3 ? 2 : 1;  // buffers of the partials
+  static constexpr int NRB = RM <= 3 ? 2 : 1;        // buffers of the partials
+  static constexpr int EPU = 16 / sizeof(T);         // elements per 16-byte unit
+  static constexpr int KU = TS * DK / EPU;           // units of k (or q) per tile
+  static constexpr int KPT = (KU + NT - 1) / NT;
+  static constexpr int LU = TS * DK / 4;             // float4 units of lg per tile
+  static constexpr int LPT = (LU + NT - 1) / NT;
+  static constexpr int CU = TS * JS / EPU;           // units of v or dO per tile
+  static constexpr int CPT = (CU + NT - 1) / NT;
 
   struct alignas(16) Smem {
     float k[TS][DKP];  // kn; 0 on padded rows
@@ -72,55 +82,121 @@ struct ScanBwdVg {
     float dO[TS][JS];
     float beta[TS], valid[TS];
     alignas(16) float X[kChunk][JS];      // v - u, per step of the chunk
-    float red[NRB][NB][3][NW][DKP];       // per-wave row partials: dqn, dkn, dlg
+    alignas(16) float red[NRB][NB][3][NW][DKP];  // per-wave row partials: dqn, dkn, dlg
     float rdb[NRB][NB][NW];               // per-wave dbeta
     alignas(16) float dv[TS][JS];
   };
 
-  // Stages steps [t0, t0 + n) of the tile: kn, g always; v (phase 1) or qn
-  // and dO (phase 2).
-  __device__ static void stage(const ScanBwdVgArgs& p, Smem& sm, int b, int h, int j, int col0,
-                               int t0, int n, bool ph2) {
+  // One tile's inputs in flight (16-byte loads, all issued before any use).
+  struct Stage {
+    uint4 k[KPT], q[KPT], c[CPT];
+    float rk[KPT], rq[KPT];
+    float4 lg[LPT];
+    float lv[LPT];  // 1: a valid step inside the tile
+    float beta, valid;
+  };
+
+  // Loads steps [t0, t0 + n) of the tile: kn, lg always; v (phase 1) or qn
+  // and dO (phase 2).  Addresses are clamped into the tensors and values past
+  // the tile zeroed by selects, so no load sits behind a branch.
+  template <bool PH2>
+  __device__ static void load_tile(const ScanBwdVgArgs& p, int b, int h, int j, int col0, int t0,
+                                   int n, Stage& s) {
     const Dims& d = p.d;
     const int tid = threadIdx.x;
     const T* kg = static_cast<const T*>(p.k);
     const T* qg = static_cast<const T*>(p.q);
-    for (int e = tid; e < TS * DKP; e += NT) {
-      const int tt = e / DKP, i = e % DKP;
-      float kv = 0.f, qv = 0.f, gv = 1.f;
-      if (tt < n && i < d.Dk) {
-        const size_t r = static_cast<size_t>(b) * d.T + t0 + tt;
-        const size_t row = r * d.Hk + j;
-        kv = to_f32(kg[row * d.Dk + i]) * p.s.rk[row];
-        if (ph2) qv = to_f32(qg[row * d.Dk + i]) * p.s.rq[row];
-        if (p.mask == nullptr || p.mask[r] != 0) gv = expf(p.lg[(r * d.Hv + h) * d.Dk + i]);
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const int u0 = tid + m * NT, u = min(u0, KU - 1);
+      const int tt = u / (DK / EPU), e0 = (u % (DK / EPU)) * EPU;
+      const size_t row = (static_cast<size_t>(b) * d.T + min(t0 + tt, d.T - 1)) * d.Hk + j;
+      const bool ok = u0 < KU && tt < n;
+      s.k[m] = *reinterpret_cast<const uint4*>(kg + row * DK + e0);
+      s.rk[m] = ok ? p.s.rk[row] : 0.f;
+      if constexpr (PH2) {
+        s.q[m] = *reinterpret_cast<const uint4*>(qg + row * DK + e0);
+        s.rq[m] = ok ? p.s.rq[row] : 0.f;
       }
-      sm.k[tt][i] = kv;
-      sm.q[tt][i] = qv;
-      sm.g[tt][i] = gv;
     }
-    const T* cg = static_cast<const T*>(ph2 ? p.dO : p.v);
-    for (int e = tid; e < TS * JS; e += NT) {
-      const int tt = e / JS, c = e % JS;
-      float x = 0.f;
-      if (tt < n) {
-        const size_t r = (static_cast<size_t>(b) * d.T + t0 + tt) * d.Hv + h;
-        x = to_f32(cg[r * d.Dv + col0 + c]);
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int u0 = tid + m * NT, u = min(u0, LU - 1);
+      const int tt = u / (DK / 4), e0 = (u % (DK / 4)) * 4;
+      const size_t r = static_cast<size_t>(b) * d.T + min(t0 + tt, d.T - 1);
+      s.lg[m] = *reinterpret_cast<const float4*>(p.lg + (r * d.Hv + h) * DK + e0);
+      const bool mv = p.mask == nullptr || p.mask[r] != 0;
+      s.lv[m] = (u0 < LU && tt < n && mv) ? 1.f : 0.f;
+    }
+    const T* cg = static_cast<const T*>(PH2 ? p.dO : p.v);
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int u0 = tid + m * NT, u = min(u0, CU - 1);
+      const int tt = u / (JS / EPU), e0 = (u % (JS / EPU)) * EPU;
+      const size_t r = (static_cast<size_t>(b) * d.T + min(t0 + tt, d.T - 1)) * d.Hv + h;
+      const uint4 x = *reinterpret_cast<const uint4*>(cg + r * d.Dv + col0 + e0);
+      s.c[m] = (u0 < CU && tt < n) ? x : zero;
+    }
+    {
+      const int tt = min(tid, TS - 1);
+      const size_t r = static_cast<size_t>(b) * d.T + min(t0 + tt, d.T - 1);
+      const float bv = p.s.beta[r * d.Hv + h];
+      const bool mv = p.mask == nullptr || p.mask[r] != 0;
+      s.beta = tt < n ? bv : 0.f;
+      s.valid = (tt < n && mv) ? 1.f : 0.f;
+    }
+  }
+
+  template <bool PH2>
+  __device__ static void store_tile(Smem& sm, const Stage& s) {
+    const int tid = threadIdx.x;
+    float f[EPU];
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const int u = tid + m * NT;
+      if (u < KU) {
+        const int tt = u / (DK / EPU), e0 = (u % (DK / EPU)) * EPU;
+        Vec16<T>::unpack(s.k[m], f);
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) sm.k[tt][e0 + e] = f[e] * s.rk[m];
+        if constexpr (PH2) {
+          Vec16<T>::unpack(s.q[m], f);
+#pragma unroll
+          for (int e = 0; e < EPU; ++e) sm.q[tt][e0 + e] = f[e] * s.rq[m];
+        }
       }
-      if (ph2)
-        sm.dO[tt][c] = x;
-      else
-        sm.v[tt][c] = x;
+    }
+#pragma unroll
+    for (int m = 0; m < LPT; ++m) {
+      const int u = tid + m * NT;
+      if (u < LU) {
+        const int tt = u / (DK / 4), e0 = (u % (DK / 4)) * 4;
+        const bool on = s.lv[m] != 0.f;
+        sm.g[tt][e0 + 0] = on ? expf(s.lg[m].x) : 1.f;
+        sm.g[tt][e0 + 1] = on ? expf(s.lg[m].y) : 1.f;
+        sm.g[tt][e0 + 2] = on ? expf(s.lg[m].z) : 1.f;
+        sm.g[tt][e0 + 3] = on ? expf(s.lg[m].w) : 1.f;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int u = tid + m * NT;
+      if (u < CU) {
+        const int tt = u / (JS / EPU), e0 = (u % (JS / EPU)) * EPU;
+        Vec16<T>::unpack(s.c[m], f);
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+          if constexpr (PH2)
+            sm.dO[tt][e0 + e] = f[e];
+          else
+            sm.v[tt][e0 + e] = f[e];
+        }
+      }
     }
     if (tid < TS) {
-      float bv = 0.f, vv = 0.f;
-      if (tid < n) {
-        const size_t r = static_cast<size_t>(b) * d.T + t0 + tid;
-        bv = p.s.beta[r * d.Hv + h];
-        vv = (p.mask == nullptr || p.mask[r] != 0) ? 1.f : 0.f;
-      }
-      sm.beta[tid] = bv;
-      sm.valid[tid] = vv;
+      sm.beta[tid] = s.beta;
+      sm.valid[tid] = s.valid;
     }
   }
 
@@ -184,9 +260,18 @@ struct ScanBwdVg {
     float* sub = p.sub + (static_cast<size_t>(bh) * nslice + slice) * NSUB * subsz;
     T* dvg = static_cast<T*>(p.dv);
 
+    if constexpr (DK < DKP) {  // padded rows: never staged, kn = qn = 0, g = 1
+      for (int e = tid; e < TS * (DKP - DK); e += NT) {
+        const int tt = e / (DKP - DK), i = DK + e % (DKP - DK);
+        sm.k[tt][i] = 0.f;
+        sm.q[tt][i] = 0.f;
+        sm.g[tt][i] = 1.f;
+      }
+    }
     float D[RM][8];
     load_state(p.dS_final ? p.dS_final + sbase : nullptr, d.Dk, d.Dv, col0 + lcol, lane, D);
     int rb = 0;  // partials buffer
+    Stage stg;
 
     for (int c = d.nchunk() - 1; c >= 0; --c) {
       const int c0 = c * kChunk, Lc = min(kChunk, d.T - c0);
@@ -197,8 +282,9 @@ struct ScanBwdVg {
       // ---- phase 1: forward over the chunk
       for (int t0 = c0; t0 < c0 + Lc; t0 += TS) {
         const int n = min(TS, c0 + Lc - t0);
+        load_tile<false>(p, b, h, j, col0, t0, n, stg);
         __syncthreads();
-        stage(p, sm, b, h, j, col0, t0, n, false);
+        store_tile<false>(sm, stg);
         __syncthreads();
         for (int tt = 0; tt < n; ++tt) {
           const int tl = t0 + tt - c0;
@@ -229,23 +315,32 @@ struct ScanBwdVg {
         }
       }
       wave_lds_sync();  // X: each wave reads back only its own columns
+      float Pf[RM][8];  // the next block's sub-checkpoint, loaded a block ahead
+      get_sub(sub + ((Lc - 1) / NB) * subsz, Pf);
 
       // ---- phase 2: blocks of NB steps, last to first
       const int ntile = (Lc + TS - 1) / TS;
       for (int it = ntile - 1; it >= 0; --it) {
         const int t0 = c0 + it * TS, n = min(TS, c0 + Lc - t0);
+        load_tile<true>(p, b, h, j, col0, t0, n, stg);
         __syncthreads();
-        stage(p, sm, b, h, j, col0, t0, n, true);
+        store_tile<true>(sm, stg);
         __syncthreads();
         const int nblk = (n + NB - 1) / NB;
         for (int bl = nblk - 1; bl >= 0; --bl) {
           const int tb = bl * NB, nb = min(NB, n - tb);  // tile-local first step, steps
           const int tl0 = t0 + tb - c0;                   // chunk-local first step
+          auto walk = [&](auto full) {
+          constexpr bool FULL = decltype(full)::value;
           float St[NB][RM][8];
-          get_sub(sub + (tl0 / NB) * subsz, S);
+#pragma unroll
+          for (int m = 0; m < RM; ++m)
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) S[m][cc] = Pf[m][cc];
+          if (tl0 >= NB) get_sub(sub + (tl0 / NB - 1) * subsz, Pf);
 #pragma unroll
           for (int jj = 0; jj < NB; ++jj) {
-            if (jj < nb) {
+            if (FULL || jj < nb) {
               const int tt = tb + jj;
               const float beta = sm.beta[tt];
 #pragma unroll
@@ -261,7 +356,7 @@ struct ScanBwdVg {
           }
 #pragma unroll
           for (int jj = NB - 1; jj >= 0; --jj) {
-            if (jj < nb) {
+            if (FULL || jj < nb) {
               const int tt = tb + jj;
               const float beta = sm.beta[tt], valid = sm.valid[tt];
               float X[8], dOc[8], del[8];
@@ -315,16 +410,30 @@ struct ScanBwdVg {
               put8(&sm.dv[tt][lcol], eps, beta, lane);
             }
           }
+          };
+          if (nb == NB)
+            walk(std::true_type{});
+          else
+            walk(std::false_type{});
           __syncthreads();
-          // sums over the waves (in order) -> per-slice partials of the block's steps
+          // sums over the waves (in order) -> per-slice partials of the block's
+          // steps, 4 rows per thread and item
           const int t_abs = t0 + tb;
-          for (int e = tid; e < nb * 3 * d.Dk; e += NT) {
-            const int jj = e / (3 * d.Dk), r = e % (3 * d.Dk), qq = r / d.Dk, i = r % d.Dk;
-            float s = 0.f;
+          constexpr int Q4 = 3 * DK / 4;
+          const size_t o0 = ((static_cast<size_t>(b) * d.T + t_abs) * d.Hv + h) * nslice + slice;
+          const size_t ostep = static_cast<size_t>(d.Hv) * nslice * 3 * DK;
+          for (int e = tid; e < nb * Q4; e += NT) {
+            const int jj = e / Q4, r4 = e - jj * Q4, qq = r4 / (DK / 4), i = (r4 - qq * (DK / 4)) * 4;
+            float4 a = *reinterpret_cast<const float4*>(&sm.red[rb][jj][qq][0][i]);
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) s += sm.red[rb][jj][qq][ww][i];
-            const size_t o = ((static_cast<size_t>(b) * d.T + t_abs + jj) * d.Hv + h) * nslice + slice;
-            p.part[o * 3 * d.Dk + qq * d.Dk + i] = s;
+            for (int ww = 1; ww < NW; ++ww) {
+              const float4 x = *reinterpret_cast<const float4*>(&sm.red[rb][jj][qq][ww][i]);
+              a.x += x.x;
+              a.y += x.y;
+              a.z += x.z;
+              a.w += x.w;
+            }
+            *reinterpret_cast<float4*>(p.part + o0 * 3 * DK + jj * ostep + qq * DK + i) = a;
           }
           if (tid < nb) {
             float s = 0.f;
@@ -349,9 +458,9 @@ struct ScanBwdVg {
   }
 };
 
-template <int RM, int NW, typename T>
+template <int DK, int NW, typename T>
 __global__ void __launch_bounds__(64 * NW) scan_bwd_vg_kernel(ScanBwdVgArgs p) {
-  using K = ScanBwdVg<RM, NW, T>;
+  using K = ScanBwdVg<DK, NW, T>;
   __shared__ typename K::Smem sm;
   K::run(p, sm);
 }
@@ -426,23 +535,25 @@ __global__ void __launch_bounds__(64) vg_reduce_kernel(VgReduceArgs p) {
   }
 }
 
-template <int RM, typename T>
-hipError_t launch_rm(const ScanBwdVgArgs& a, hipStream_t st) {
+template <int DK, typename T>
+hipError_t launch_dk(const ScanBwdVgArgs& a, hipStream_t st) {
   dim3 grid(a.d.B * a.d.Hv, vg_nslice(a.d.Dv));
   if (scan_waves(a.d.Dv) == 4)
-    scan_bwd_vg_kernel<RM, 4, T><<<grid, 256, 0, st>>>(a);
+    scan_bwd_vg_kernel<DK, 4, T><<<grid, 256, 0, st>>>(a);
   else
-    scan_bwd_vg_kernel<RM, 1, T><<<grid, 64, 0, st>>>(a);
+    scan_bwd_vg_kernel<DK, 1, T><<<grid, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_t(const ScanBwdVgArgs& a, hipStream_t st) {
-  switch (vg_rows(a.d.Dk)) {
-    case 1: return launch_rm<1, T>(a, st);
-    case 2: return launch_rm<2, T>(a, st);
-    case 3: return launch_rm<3, T>(a, st);
-    case 4: return launch_rm<4, T>(a, st);
+  switch (a.d.Dk) {
+    case 16: return launch_dk<16, T>(a, st);
+    case 32: return launch_dk<32, T>(a, st);
+    case 64: return launch_dk<64, T>(a, st);
+    case 128: return launch_dk<128, T>(a, st);
+    case 192: return launch_dk<192, T>(a, st);
+    case 256: return launch_dk<256, T>(a, st);
   }
   return hipErrorInvalidValue;
 }
