@@ -8,7 +8,7 @@ performance table).  One step = gdn_fwd (with checkpoints) + gdn_bwd on the
 same resident inputs.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--config 9b_t2048|9b_t256|decode|decode_conv|vg_t2048|vg_t256]
+                  [--config 9b_t2048|9b_t256|decode|decode_conv|vg_t2048|vg_t256|long_t32k]
 """
 from __future__ import annotations
 
@@ -405,6 +405,115 @@ def bench_vg(args, torch, binding, inputs):
     }
 
 
+LONG = dict(B=1, T=32768, Hk=2, Hv=4, Dk=128, Dv=128)
+
+
+def bench_long(args, torch, binding, inputs):
+    """A long single sequence with few heads (inference prefill, forward only,
+    no checkpoints): the T-parallel chunk forward (segment maps, their chain,
+    every segment's outputs) against the single-pass chunk forward.  Slow
+    decays (A_log in (-7, -4)) so that the state carries across chunks."""
+    L = LONG
+    case = inputs.make_case("long_t32k", L["B"], L["T"], L["Hk"], L["Hv"], L["Dk"], L["Dv"], "bf16",
+                            11, state_std=None, dS_final=False, A_log_range=(-7.0, -4.0))
+    dev = torch.device("cuda:0")
+
+    def up(n):
+        import numpy as np
+        x = case.store(n)
+        if x is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+
+    t = {n: up(n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    lib = binding.lib()
+    st = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(st.cuda_stream)
+    P = binding._p
+    out = {}
+    for name, algo in (("tpar", binding.ALGO_CHUNK_TPAR), ("single", binding.ALGO_CHUNK)):
+        d = binding.make_dims(L["B"], L["T"], L["Hk"], L["Hv"], L["Dk"], L["Dv"], binding.GDN_BF16, algo)
+        o = torch.empty((L["B"], L["T"], L["Hv"], L["Dv"]), dtype=torch.bfloat16, device=dev)
+        so = torch.empty((L["B"], L["Hv"], L["Dk"], L["Dv"]), dtype=torch.float32, device=dev)
+        wsb = binding.fwd_workspace_bytes(d)
+        ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
+        fargs = (ctypes.byref(d), P(t["q"]), P(t["k"]), P(t["v"]), P(t["a"]), P(t["b"]), P(t["A_log"]),
+                 P(t["dt_bias"]), None, None, P(o), P(so), None, P(ws), wsb, sp)
+
+        def run():
+            rc = lib.gdn_fwd(*fargs)
+            if rc:
+                raise binding.GdnError("gdn_fwd", rc)
+        for _ in range(args.warmup):
+            run()
+        ev = HipEvents(2)
+        torch.cuda.synchronize()
+        ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
+        for _ in range(args.steps):
+            run()
+        ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
+        torch.cuda.synchronize()
+        ms = ev.elapsed_ms(0, 1) / args.steps
+        ev.close()
+        kms = None
+        if name == "tpar":
+            ks = ["chunk_prep", "fill_zero", "chunk_fwd_maps", "seg_chain", "chunk_fwd"]
+            ev = HipEvents(2 * len(ks))
+            lib.gdn_set_kernel_events(ev.ptr(0), 2 * len(ks))
+            run()
+            torch.cuda.synchronize()
+            lib.gdn_set_kernel_events(None, 0)
+            kms = {k: round(ev.elapsed_ms(2 * i, 2 * i + 1), 4) for i, k in enumerate(ks)}
+            ev.close()
+        out[name] = (ms, kms, wsb)
+    B, T, Hk, Hv, Dk, Dv = (L[k] for k in ("B", "T", "Hk", "Hv", "Dk", "Dv"))
+    ms, kms, wsb = out["tpar"]
+    ms1 = out["single"][0]
+    # algorithmic HBM bytes of the prefill: q, k, v, a, b, o once, the final state
+    byts = (2 * B * T * Hk * Dk + 2 * B * T * Hv * Dv + 2 * B * T * Hv) * 2 + B * Hv * Dk * Dv * 4
+    dom = max(kms, key=lambda k: kms[k])
+    # per kernel: what it reads and writes of the inputs, outputs and the
+    # segment maps / start states (chunk matrices and scalars not counted)
+    # segments, from the extra workspace: maps n (Dk + Dv) + starts (n - 1) Dv floats per state row
+    x = (wsb - out["single"][2] - 256) / (4 * B * Hv * Dk)
+    nseg = max(int(round((x + Dv) / (Dk + 2 * Dv))), 1)
+    maps = nseg * B * Hv * Dk * (Dk + Dv) * 4
+    starts = (nseg - 1) * B * Hv * Dk * Dv * 4
+    kb = {"chunk_prep": (2 * B * T * Hk * Dk + 2 * B * T * Hv) * 2,
+          "fill_zero": 256,
+          "chunk_fwd_maps": (B * T * Hk * Dk + B * T * Hv * Dv) * 2 + maps,
+          "seg_chain": maps + starts,
+          "chunk_fwd": (2 * B * T * Hk * Dk + 2 * B * T * Hv * Dv) * 2 + starts + B * Hv * Dk * Dv * 4}
+    return {
+        "metric": "prefill (forward) tokens/sec of one long sequence, B=1 T=32768 Hk2/Hv4/Dk128/Dv128 bf16",
+        "value": round(B * T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gated delta rule forward, one long sequence with few heads, T-parallel "
+                               "chunk form", "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
+                   "io_dtype": "bf16", "algo": "chunk_tpar"},
+        "single_pass_ms": round(ms1, 4),
+        "speedup_vs_single_pass": round(ms1 / ms, 3),
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": round(kb[dom] / (kms[dom] / 1e3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(kb[dom] / (kms[dom] / 1e3) / HBM_PEAK, 4),
+                     "traffic": None, "bytes_per_launch": kb[dom], "avg_launch_ms": kms[dom]},
+        "hbm_roofline_prefill": {"bytes": byts, "achieved_GBps": round(byts / (ms / 1e3) / 1e9, 1),
+                                 "frac": round(byts / (ms / 1e3) / HBM_PEAK, 4)},
+        "segments": nseg,
+        "kernels_ms": kms,
+    }
+
+
 def bench_decode(args, torch, binding, inputs):
     """Decode workload: B=64, Hk=16, Hv=32, Dk=Dv=128, one token per call, the
     state updated in place; a step is 64 consecutive calls."""
@@ -556,7 +665,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="9b_t2048",
-                    choices=["9b_t2048", "9b_t256", "decode", "decode_conv", "vg_t2048", "vg_t256"])
+                    choices=["9b_t2048", "9b_t256", "decode", "decode_conv", "vg_t2048", "vg_t256",
+                             "long_t32k"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -578,6 +688,8 @@ def main():
         out = bench_decode(args, torch, binding, inputs)
     elif args.config == "decode_conv":
         out = bench_decode_conv(args, torch, binding, inputs)
+    elif args.config == "long_t32k":
+        out = bench_long(args, torch, binding, inputs)
     elif args.config.startswith("vg_"):
         out = bench_vg(args, torch, binding, inputs)
         if not args.no_cpu_baseline:

@@ -66,7 +66,20 @@ enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
  *   AUTO   CHUNK where it is built and T > 1, else SCAN.
  * Both produce the same checkpoint layout, so a checkpoint from one can be
  * used by the other (with save unset; see gdn_ckpt_elems). */
-enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SCAN = 1, GDN_ALGO_CHUNK = 2 };
+/*   CHUNK_TPAR  the CHUNK family with a T-parallel forward (mlx-lm PR,
+ *          "Associative prefix-scan scaffold": each step, and so each chunk,
+ *          is an affine map of the state, and maps compose associatively).
+ *          The chunks are grouped into segments; each segment's composed map
+ *          [A | B] (A: Dk x Dk, B: Dk x Dv) is computed in parallel over the
+ *          segments, a short fp32 chain over the segment maps gives every
+ *          segment's start state, and the segments then run their outputs in
+ *          parallel.  This pays when B * Hv * Dv / 32 is small against the
+ *          GPU's 256 compute units and T is long (a long single sequence with
+ *          few heads); the library picks the segment count from the sizes and
+ *          falls back to CHUNK's single pass when one segment is best.  Same
+ *          sizes, checkpoints and saved record as CHUNK; gdn_bwd runs CHUNK.
+ *          Results agree with CHUNK to bf16 rounding, not bitwise. */
+enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SCAN = 1, GDN_ALGO_CHUNK = 2, GDN_ALGO_CHUNK_TPAR = 3 };
 
 typedef struct gdn_dims {
   int64_t B, T, Hk, Hv, Dk, Dv; /* T >= 0; Hv % Hk == 0                     */

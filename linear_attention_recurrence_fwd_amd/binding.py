@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn.so")
 CHUNK = 64
 
 GDN_F32, GDN_BF16 = 0, 1
-ALGO_AUTO, ALGO_SCAN, ALGO_CHUNK = 0, 1, 2
+ALGO_AUTO, ALGO_SCAN, ALGO_CHUNK, ALGO_CHUNK_TPAR = 0, 1, 2, 3
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
 

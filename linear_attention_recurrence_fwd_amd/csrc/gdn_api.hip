@@ -18,6 +18,7 @@ struct Layout {
   size_t U, E, dHend, pdA, pdt;                 // backward only
   size_t Tx, Mq, KT, TxT, AtT, PqT, QT, SC;     // chunk form
   size_t HB;                                    // chunk backward: bf16 chunk-start states
+  size_t maps, hseg, vzero;                     // T-parallel chunk forward
   size_t total;
 };
 
@@ -62,7 +63,8 @@ size_t ckpt_state_elems(const Dims& d) {
 }
 
 // Workspace layout.  `saved`: the chunk matrices live in the checkpoint tail.
-Layout layout(const Dims& d, bool bwd, bool chunk, bool saved) {
+// `tseg`: chunks per segment of the T-parallel forward (0: none).
+Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t nfloat) {
@@ -111,6 +113,12 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved) {
       }
     }
   }
+  if (chunk && !bwd && tseg) {
+    const size_t ns = gdn::tpar_nseg(d, tseg), BH = static_cast<size_t>(d.B) * d.Hv;
+    L.maps = take(ns * BH * d.Dk * (static_cast<size_t>(d.Dk) + d.Dv));
+    L.hseg = take((ns - 1) * BH * d.Dk * d.Dv);
+    L.vzero = take(64);
+  }
   L.total = off;
   return L;
 }
@@ -122,9 +130,10 @@ int check_dims(const gdn_dims* p, Dims* out) {
     return GDN_ERR_INVALID_ARG;
   if (p->Hv % p->Hk != 0) return GDN_ERR_INVALID_ARG;
   if (p->dtype != GDN_F32 && p->dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
-  if (p->algo != GDN_ALGO_AUTO && p->algo != GDN_ALGO_SCAN && p->algo != GDN_ALGO_CHUNK)
+  if (p->algo != GDN_ALGO_AUTO && p->algo != GDN_ALGO_SCAN && p->algo != GDN_ALGO_CHUNK &&
+      p->algo != GDN_ALGO_CHUNK_TPAR)
     return GDN_ERR_INVALID_ARG;
-  if (p->algo == GDN_ALGO_CHUNK &&
+  if ((p->algo == GDN_ALGO_CHUNK || p->algo == GDN_ALGO_CHUNK_TPAR) &&
       !gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16))
     return GDN_ERR_UNSUPPORTED;
   if (!gdn::scan_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv)))
@@ -173,11 +182,15 @@ P* at(void* ws, size_t off) {
 // bf16 with a supported head size and more than one step (single steps, the
 // decode case, stay on the scan).
 bool use_chunk(const gdn_dims* p) {
-  if (p->algo == GDN_ALGO_CHUNK) return true;
+  if (p->algo == GDN_ALGO_CHUNK || p->algo == GDN_ALGO_CHUNK_TPAR) return true;
   if (p->algo == GDN_ALGO_SCAN) return false;
   return p->T > 1 && gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16);
 }
 bool use_chunk_fwd(const gdn_dims* p) { return use_chunk(p); }
+// Chunks per segment of the T-parallel forward (0: the single-pass forward).
+int tpar_seg(const gdn_dims* p, const Dims& d) {
+  return p->algo == GDN_ALGO_CHUNK_TPAR && d.T > 0 ? gdn::tpar_seg_len(d) : 0;
+}
 bool use_chunk_bwd(const gdn_dims* p) { return use_chunk(p); }
 // The chunk matrices go through the checkpoint tail.
 bool use_saved(const gdn_dims* p) { return p->save != 0 && use_chunk(p); }
@@ -277,7 +290,7 @@ int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = layout(dd, false, use_chunk_fwd(d), use_saved(d)).total;
+  *out = layout(dd, false, use_chunk_fwd(d), use_saved(d), tpar_seg(d, dd)).total;
   return GDN_OK;
 }
 
@@ -302,7 +315,8 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   if (has_t && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
   if (use_saved(d) && !ckpt) return GDN_ERR_INVALID_ARG;  // the matrices are saved there
   const bool chunk = use_chunk_fwd(d);
-  const Layout L = layout(dd, false, chunk, use_saved(d));
+  const int tseg = chunk ? tpar_seg(d, dd) : 0;
+  const Layout L = layout(dd, false, chunk, use_saved(d), tseg);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -318,6 +332,22 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
     // under save the states go to the checkpoint buffer as bf16 only
     gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, save ? nullptr : ckpt};
+    if (tseg) {  // T-parallel: segment maps, their chain, then every segment's outputs
+      const int nseg = gdn::tpar_nseg(dd, tseg);
+      float* maps = at<float>(ws, L.maps);
+      float* hseg = at<float>(ws, L.hseg);
+      float* vz = at<float>(ws, L.vzero);
+      if (!launch(st, [&] { return gdn::launch_fill_zero(vz, 64, st); })) return GDN_ERR_HIP;
+      gdn::ChunkBufs mcb = cb;
+      mcb.Hb = nullptr;
+      gdn::ChunkFwdArgs ma{dd, q, k, v, nullptr, mcb, nullptr, nullptr, nullptr,
+                           tseg, 1, nullptr, maps, reinterpret_cast<const gdn::bf16*>(vz)};
+      if (!launch(st, [&] { return gdn::launch_chunk_fwd(ma, st); })) return GDN_ERR_HIP;
+      gdn::SegChainArgs sa{dd, nseg, state0, maps, hseg};
+      if (!launch(st, [&] { return gdn::launch_seg_chain(sa, st); })) return GDN_ERR_HIP;
+      fa.seg = tseg;
+      fa.hseg = hseg;
+    }
     if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
     return GDN_OK;
   }

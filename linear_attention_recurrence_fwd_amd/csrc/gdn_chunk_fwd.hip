@@ -425,6 +425,9 @@ struct ChunkFwd {
   // 32-bit lane offset.
   struct Lane {
     int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
+    int cs, ce, seg, mode;       // chunk range of the segment; 0 output, 1 map identity, 2 map values
+    int scol;                    // first state column of the slice (Dk + Dv columns in map mode)
+    uint32_t vstep, vbase;       // v elements per step and offset (0, 0: the zero rows)
     uint32_t qk_row, v_row;   // element strides of one step in q/k and v/o
     rsrc_t rq, rmq;              // buffer descriptors of group C's operands
     i32x4 dk, dv, dtx, dsc;      // raw descriptors of the ring's operands
@@ -454,7 +457,7 @@ struct ChunkFwd {
     {
       const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
       dma16(q.dv, &s.v[512 * q.w],
-            2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hv + q.h) * d.Dv + q.col0 + 8 * pc));
+            2 * (static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * q.vstep + q.vbase + 8 * pc));
     }
     dma4(q.dsc, &s.sc[L * q.w], 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + L * q.w + l));
   }
@@ -519,7 +522,7 @@ struct ChunkFwd {
       *reinterpret_cast<uint2*>(&sm.rb[(16 * ct + lr) * XS + q.tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
     }
     lds_barrier();  // 1: R complete
-    issue_ring(p, sm, q, min(c + PD, q.NC - 1), (c + PD) % NSL);
+    issue_ring(p, sm, q, min(c + PD, q.ce - 1), (c + PD) % NSL);
     f32x4 x[2];
     x[0] = x[1] = f4zero();
 #pragma unroll
@@ -657,10 +660,10 @@ struct ChunkFwd {
 
   __device__ static void run_a(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
 #pragma unroll
-    for (int c = 0; c < PD; ++c) issue_ring(p, sm, q, min(c, q.NC - 1), c);
+    for (int c = 0; c < PD; ++c) issue_ring(p, sm, q, min(q.cs + c, q.ce - 1), (q.cs + c) % NSL);
     wait_vm<(PD - 1) * NDMA>();
-    lds_barrier();  // 0: initial H; slot 0 complete
-    for (int c = 0; c < q.NC; ++c) step_a(p, sm, q, c);
+    lds_barrier();  // 0: initial H; slot of chunk cs complete
+    for (int c = q.cs; c < q.ce; ++c) step_a(p, sm, q, c);
     wait_vm<0>();  // no direct-to-LDS load may land after the workgroup ends
   }
 
@@ -670,8 +673,13 @@ struct ChunkFwd {
     // H: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr.
     // Unconditional buffer loads; an absent initial state reads through an
     // empty descriptor, i.e. as zeros (a load under a branch would wait alone).
-    const rsrc_t rs0 = make_rsrc(p.state0 ? static_cast<const void*>(p.state0 + sbase) : static_cast<const void*>(p.state_out),
-                                 p.state0 ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
+    // The start state: state0 (first segment), the segment's start state, the
+    // identity columns (map mode) or zeros (map mode, value columns).
+    const float* h0 = q.mode != 0 ? nullptr
+                      : q.seg == 0 ? p.state0
+                                   : p.hseg + static_cast<size_t>(q.seg - 1) * d.B * d.Hv * DK * d.Dv;
+    const rsrc_t rs0 = make_rsrc(h0 ? static_cast<const void*>(h0 + sbase) : static_cast<const void*>(p.k),
+                                 h0 ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
     f32x4 H[RTW][2];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
@@ -681,11 +689,19 @@ struct ChunkFwd {
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
           H[it][ct][r] = buf_f1(rs0, 4 * static_cast<uint32_t>(i * d.Dv + q.col0 + 16 * ct + q.lr));
+          if (q.mode == 1) H[it][ct][r] = i == q.scol + 16 * ct + q.lr ? 1.f : 0.f;
         }
     put_h(sm, q, H);
-    if (p.cb.Hb != nullptr) store_hb(p, q, H, 0);
+    // the bf16 start state of chunk cs: here for the first segment only; a
+    // later segment's start slot is the previous segment's end state (written
+    // by its last chunk, as the fp32 checkpoint of that boundary is)
+    if (p.cb.Hb != nullptr && q.seg == 0) store_hb(p, q, H, 0);
     lds_barrier();  // 0
-    for (int c = 0; c < q.NC; ++c) step_b(p, sm, q, c, H);
+    for (int c = q.cs; c < q.ce; ++c) step_b(p, sm, q, c, H);
+    if (q.mode == 0 && q.ce < q.NC) return;  // not the last segment: no final state
+    const int ostride = q.mode == 0 ? d.Dv : DK + d.Dv;
+    float* out = q.mode == 0 ? p.state_out + sbase
+                             : p.maps + (static_cast<size_t>(q.seg) * d.B * d.Hv + q.bh) * DK * ostride;
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
@@ -693,29 +709,35 @@ struct ChunkFwd {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          p.state_out[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = H[it][ct][r];
+          out[static_cast<size_t>(i) * ostride + q.scol + 16 * ct + q.lr] = H[it][ct][r];
         }
   }
 
   __device__ static void run_c(const ChunkFwdArgs& p, Smem& sm, const Lane& q) {
     lds_barrier();  // 0: initial H
-    // Prefetch two chunks ahead through three register stages.  The loads are
-    // unconditional, from a chunk index clamped to the last chunk: a load under
-    // a branch makes the compiler wait for every outstanding load where the
-    // branch joins, which would void the prefetch.
-    const int cl = q.NC - 1;
-    StageC s0, s1, s2;
-    if (q.NC > 0) {
-      load_c(p, q, 0, s0);
-      load_c(p, q, min(1, cl), s1);
+    if (q.mode != 0) {  // map mode: no outputs; keep the chunk's barriers
+      for (int c = q.cs; c < q.ce; ++c) {
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+      }
+      return;
     }
-    for (int c = 0; c < q.NC; c += 3) {
+    // Prefetch two chunks ahead through three register stages.  The loads are
+    // unconditional, from a chunk index clamped to the segment's last chunk: a
+    // load under a branch makes the compiler wait for every outstanding load
+    // where the branch joins, which would void the prefetch.
+    const int cl = q.ce - 1;
+    StageC s0, s1, s2;
+    load_c(p, q, q.cs, s0);
+    load_c(p, q, min(q.cs + 1, cl), s1);
+    for (int c = q.cs; c < q.ce; c += 3) {
       load_c(p, q, min(c + 2, cl), s2);
       step_c(p, sm, q, c, s0);
-      if (c + 1 >= q.NC) break;
+      if (c + 1 >= q.ce) break;
       load_c(p, q, min(c + 3, cl), s0);
       step_c(p, sm, q, c + 1, s1);
-      if (c + 2 >= q.NC) break;
+      if (c + 2 >= q.ce) break;
       load_c(p, q, min(c + 4, cl), s1);
       step_c(p, sm, q, c + 2, s2);
     }
@@ -724,14 +746,19 @@ struct ChunkFwd {
   __device__ static void run(const ChunkFwdArgs& p, Smem& sm) {
     const Dims& d = p.d;
     Lane q;
-    const int nslice = d.Dv / NV;
+    const int nslice = (p.map ? DK + d.Dv : d.Dv) / NV;
     int slice;
     block_coords(d, nslice, q.b, q.h, slice);
     q.NC = d.nchunk();
+    q.seg = blockIdx.y;
+    q.cs = p.seg ? q.seg * p.seg : 0;
+    q.ce = p.seg ? min(q.cs + p.seg, q.NC) : q.NC;
+    q.mode = !p.map ? 0 : slice < DK / NV ? 1 : 2;
     q.j = q.h / d.G();
     q.bh = q.b * d.Hv + q.h;
     q.bj = q.b * d.Hk + q.j;
-    q.col0 = slice * NV;
+    q.scol = slice * NV;
+    q.col0 = q.mode == 0 ? q.scol : q.mode == 1 ? 0 : q.scol - DK;  // v / o columns
     const int tid = threadIdx.x, l = tid & 63;
     q.w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     q.l = l;
@@ -746,12 +773,14 @@ struct ChunkFwd {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
       q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
       q.rq = make_rsrc(p.q, bt * d.Hk * DK * 2);
-      q.dv = raw_desc(p.v, bt * d.Hv * d.Dv * 2);
+      q.dv = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.v, bt * d.Hv * d.Dv * 2);
+      q.vstep = q.mode == 1 ? 0u : static_cast<uint32_t>(d.Hv * d.Dv);
+      q.vbase = q.mode == 1 ? 0u : static_cast<uint32_t>(q.h * d.Dv + q.col0);
       q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
       q.rmq = make_rsrc(p.cb.Mq, nmat * L * L * 2);
       q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
     }
-    if (q.NC == 0) return;
+    if (q.ce <= q.cs) return;
     if (tid < 256)
       run_a(p, sm, q);
     else if (tid < 512)
@@ -765,6 +794,102 @@ template <int DK>
 __global__ void __launch_bounds__(768) chunk_fwd_kernel(ChunkFwdArgs p) {
   __shared__ typename ChunkFwd<DK>::Smem sm;
   ChunkFwd<DK>::run(p, sm);
+}
+
+// ------------------------------------------------ T-parallel segment chain
+//
+// The chunked forward is an affine map per chunk, H -> A_c H + B_c (the
+// associative form of the mlx-lm PR's "Associative prefix-scan scaffold"
+// extension, with A_c = e^{gL} I - K^T diag(w) Tx diag(e^g rk) K and
+// B_c = K^T diag(w) Tx V), and the composition of maps is associative.  The
+// T-parallel forward composes the chunks of each segment in parallel (the
+// chunk kernel's map mode) and chains only the segments here:
+// H_{s+1} = A_s H_s + B_s, in fp32 on the matrix cores (16x16x4 f32).  One
+// workgroup per (b, h, 16 columns of Dv) (the chain is bound by latency: more,
+// smaller workgroups); wave w owns the output row tiles w, w + 4, ...; A is
+// staged through LDS in blocks of 32 columns, the next block loaded while the
+// current one is multiplied.
+template <int DK>
+struct SegChain {
+  static constexpr int NTC = 256;
+  static constexpr int NCOL = 16;           // columns of H per workgroup
+  static constexpr int HSTR = 36;           // row stride of H (and of the A block)
+  static constexpr int RT = DK / 16 / 4;    // row tiles per wave
+  static constexpr int APT = DK * 32 / NTC; // A block floats per thread
+  struct Smem {
+    float h[DK * HSTR];
+    float a[DK * HSTR];
+  };
+
+  __device__ static void load_a(const float* M, int W, int m0, float (&r)[APT]) {
+#pragma unroll
+    for (int n = 0; n < APT; ++n) {
+      const int e = threadIdx.x + n * NTC, i = e / 32, m = e % 32;
+      r[n] = M[static_cast<size_t>(i) * W + m0 + m];
+    }
+  }
+
+  __device__ static void run(const SegChainArgs& p, Smem& sm) {
+    const Dims& d = p.d;
+    const int bh = blockIdx.x, c0 = blockIdx.y * NCOL;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const size_t BH = static_cast<size_t>(d.B) * d.Hv;
+    const int W = DK + d.Dv;
+    for (int e = tid; e < DK * NCOL; e += NTC) {
+      const int i = e / NCOL, c = e % NCOL;
+      sm.h[i * HSTR + c] = p.state0 ? p.state0[(static_cast<size_t>(bh) * DK + i) * d.Dv + c0 + c] : 0.f;
+    }
+    float ar[APT];
+    load_a(p.maps + static_cast<size_t>(bh) * DK * W, W, 0, ar);
+    for (int s = 0; s + 1 < p.nseg; ++s) {
+      const float* M = p.maps + (static_cast<size_t>(s) * BH + bh) * DK * W;
+      f32x4 acc[RT];
+#pragma unroll
+      for (int it = 0; it < RT; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[it][r] = M[static_cast<size_t>(16 * (w + 4 * it) + 4 * lg + r) * W + DK + c0 + lr];
+      for (int m0 = 0; m0 < DK; m0 += 32) {
+        __syncthreads();  // the previous block of A is consumed; H complete
+#pragma unroll
+        for (int n = 0; n < APT; ++n) {
+          const int e = tid + n * NTC;
+          sm.a[(e / 32) * HSTR + e % 32] = ar[n];
+        }
+        __syncthreads();
+        // the next block: this step's next columns, or the next step's first
+        if (m0 + 32 < DK)
+          load_a(M, W, m0 + 32, ar);
+        else if (s + 2 < p.nseg)
+          load_a(M + BH * DK * W, W, 0, ar);
+#pragma unroll
+        for (int it = 0; it < RT; ++it)
+#pragma unroll
+          for (int kk = 0; kk < 32; kk += 16)
+            acc[it] = mm16f(acc[it], &sm.a[16 * (w + 4 * it) * HSTR + kk], HSTR, &sm.h[(m0 + kk) * HSTR], HSTR);
+      }
+      __syncthreads();  // every read of H done
+      float* out = p.hseg + (static_cast<size_t>(s) * BH + bh) * DK * d.Dv;
+#pragma unroll
+      for (int it = 0; it < RT; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * (w + 4 * it) + 4 * lg + r;
+          sm.h[i * HSTR + lr] = acc[it][r];
+          out[static_cast<size_t>(i) * d.Dv + c0 + lr] = acc[it][r];
+        }
+    }
+  }
+};
+
+template <int DK>
+__global__ void __launch_bounds__(256) seg_chain_kernel(SegChainArgs p) {
+  __shared__ typename SegChain<DK>::Smem sm;
+  SegChain<DK>::run(p, sm);
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* p, size_t n) {
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < n; i += 256ull * gridDim.x) p[i] = 0.f;
 }
 
 }  // namespace
@@ -782,8 +907,30 @@ hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t st) {
+  if (a.nseg < 2) return hipSuccess;
+  const dim3 grid(a.d.B * a.d.Hv, a.d.Dv / SegChain<64>::NCOL);
+  switch (a.d.Dk) {
+    case 64: seg_chain_kernel<64><<<grid, 256, 0, st>>>(a); break;
+    case 128: seg_chain_kernel<128><<<grid, 256, 0, st>>>(a); break;
+    case 192: seg_chain_kernel<192><<<grid, 256, 0, st>>>(a); break;
+    case 256: seg_chain_kernel<256><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t nb = (n + 255) / 256;
+  fill_zero_kernel<<<static_cast<unsigned>(nb < 1024 ? nb : 1024), 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st) {
-  const int nblk = a.d.B * a.d.Hv * (a.d.Dv / ChunkFwd<64>::NV);
+  const int NV = ChunkFwd<64>::NV;
+  const int nseg = a.seg ? (a.d.nchunk() + a.seg - 1) / a.seg : 1;
+  const dim3 nblk(a.d.B * a.d.Hv * ((a.map ? a.d.Dk + a.d.Dv : a.d.Dv) / NV), nseg);
   switch (a.d.Dk) {
     case 64: chunk_fwd_kernel<64><<<nblk, ChunkFwd<64>::NTS, 0, st>>>(a); break;
     case 128: chunk_fwd_kernel<128><<<nblk, ChunkFwd<128>::NTS, 0, st>>>(a); break;

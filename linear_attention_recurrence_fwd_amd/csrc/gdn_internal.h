@@ -178,6 +178,26 @@ struct ChunkFwdArgs {
   void* o;
   float* state_out;
   float* ckpt;
+  // Segments of the T-parallel forward (seg = chunks per segment, 0: one
+  // segment, the whole sequence; blockIdx.y = segment).  Output mode (map = 0):
+  // segment s > 0 starts from hseg[s - 1] ([nseg - 1, B*Hv, Dk, Dv] fp32).
+  // Map mode (map = 1): each segment's chain runs on the augmented state
+  // [I | 0] with values [0 | V] (Dk + Dv columns: the identity columns read
+  // v from vzero, 64 zero bytes) and its final state, the segment's affine
+  // map [A | B], goes to maps ([nseg, B*Hv, Dk, Dk + Dv] fp32); nothing else
+  // is written.
+  int seg, map;
+  const float* hseg;
+  float* maps;
+  const bf16* vzero;
+};
+// Start states of the segments: H_{s+1} = A_s H_s + B_s over the segment maps.
+struct SegChainArgs {
+  Dims d;
+  int nseg;
+  const float* state0;  // may be null
+  const float* maps;    // [nseg, B*Hv, Dk, Dk + Dv]
+  float* hseg;          // [nseg - 1, B*Hv, Dk, Dv]
 };
 
 // Chunk-form backward.  The reverse state pass writes dv, eps (dL/d delta) and
@@ -258,9 +278,31 @@ hipError_t launch_vg_reduce(const VgReduceArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
+hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t st);
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);
 hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t st);
 hipError_t launch_state_bf16(const StateBf16Args& a, hipStream_t st);
+
+// Segments of the T-parallel chunk forward.  The segment maps cost
+// (Dk + Dv) / Dv times a chunk pass on top of the output pass, so segments pay
+// only when the single pass (B Hv Dv / 32 workgroups, one per compute unit)
+// leaves at least three quarters of the 256 compute units idle.  Then: enough
+// segments that the output pass has about one workgroup per compute unit (the
+// segment passes are then bound by the chip's throughput, and the chain over
+// the segments, which is bound by latency, stays short), at least 8 chunks
+// each.  Returns the chunks per segment (0: one segment).
+inline int tpar_seg_len(const Dims& d) {
+  const int nc = d.nchunk();
+  const long wgs = static_cast<long>(d.B) * d.Hv * (d.Dv / 32);
+  if (wgs * 4 > 256) return 0;
+  long p = (256 + wgs - 1) / wgs;
+  if (p > nc / 8) p = nc / 8;
+  if (p < 2) return 0;
+  const int seg = static_cast<int>((nc + p - 1) / p);
+  return (nc + seg - 1) / seg >= 2 ? seg : 0;
+}
+inline int tpar_nseg(const Dims& d, int seg) { return seg ? (d.nchunk() + seg - 1) / seg : 1; }
 
 // The chunk form runs bf16 I/O with Dk a multiple of 32 and Dv a multiple of 32.
 inline bool chunk_supported(int Dk, int Dv, bool bf16) {

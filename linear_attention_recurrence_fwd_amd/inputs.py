@@ -106,9 +106,12 @@ def _round(x: np.ndarray, dtype: str) -> np.ndarray:
 def make_case(name: str, B: int, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
               dtype: str, seed: int, *, state_std: float | None = 0.1,
               dS_final: bool = True, mask: np.ndarray | None = None,
-              extreme: bool = False) -> Case:
+              extreme: bool = False, A_log_range: tuple | None = None) -> Case:
     """Draw one workload.  ``extreme`` sets A_log = 5 and a = 15 everywhere
-    (after the draws, so the other tensors are unchanged)."""
+    (after the draws, so the other tensors are unchanged).  ``A_log_range``
+    redraws A_log ~ U(lo, hi) after all other draws (slow decays for long
+    memory: A_log in (-7, -4) keeps 10 % to 98 % of the state over a 64-step
+    chunk)."""
     assert dtype in DTYPES and Hv % Hk == 0
     rng = np.random.Generator(np.random.PCG64(seed))
     c = Case(name, B, T, Hk, Hv, Dk, Dv, dtype)
@@ -128,6 +131,8 @@ def make_case(name: str, B: int, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
     if extreme:
         v["A_log"] = np.full((Hv,), 5.0)
         v["a"] = np.full((B, T, Hv), 15.0)
+    if A_log_range is not None:
+        v["A_log"] = _round(rng.uniform(A_log_range[0], A_log_range[1], (Hv,)), "f32")
     if mask is not None:
         c.mask = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
         assert c.mask.shape == (B, T)

@@ -212,3 +212,19 @@ def test_vg_rejects_before_launch():
         args[i] = None
         assert lib.gdn_bwd_vg(ctypes.byref(d), *args, g[0], bws, None) == 1, i
     assert lib.gdn_bwd_vg(ctypes.byref(d), *g, g[0], bws - 1, None) == 3
+
+
+def test_tpar_segments_only_when_they_pay():
+    """GDN_ALGO_CHUNK_TPAR splits a long sequence into segments (more
+    workspace: the segment maps and start states) only when the single pass
+    leaves most compute units idle; at the 9B shape it is the single pass."""
+    def ws(algo, dims):
+        return B.fwd_workspace_bytes(B.make_dims(*dims, B.GDN_BF16, algo))
+    head = (1, 2048, 16, 64, 192, 128)
+    assert ws(B.ALGO_CHUNK_TPAR, head) == ws(B.ALGO_CHUNK, head)
+    long1 = (1, 32768, 2, 4, 128, 128)
+    extra = ws(B.ALGO_CHUNK_TPAR, long1) - ws(B.ALGO_CHUNK, long1)
+    # 16 segments (512 chunks / 32 each): maps [16, 4, 128, 256] + starts [15, 4, 128, 128]
+    assert extra == 4 * (16 * 4 * 128 * 256 + 15 * 4 * 128 * 128) + 256
+    assert B.ckpt_elems(B.make_dims(*long1, B.GDN_BF16, B.ALGO_CHUNK_TPAR)) == \
+        B.ckpt_elems(B.make_dims(*long1, B.GDN_BF16, B.ALGO_CHUNK))
