@@ -63,7 +63,8 @@ enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
  *          multiple of 32 up to 256; other shapes return GDN_ERR_UNSUPPORTED.
  *          Its results agree with SCAN to bf16 rounding (about 1e-2 relative,
  *          normwise), not bitwise.
- *   AUTO   CHUNK where it is built and T > 1, else SCAN.
+ *   AUTO   CHUNK where it is built and T > 1, else SCAN; the CHUNK forward
+ *          runs T-parallel (as CHUNK_TPAR) where that pays.
  * Both produce the same checkpoint layout, so a checkpoint from one can be
  * used by the other (with save unset; see gdn_ckpt_elems). */
 /*   CHUNK_TPAR  the CHUNK family with a T-parallel forward (mlx-lm PR,

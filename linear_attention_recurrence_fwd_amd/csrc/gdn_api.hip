@@ -188,8 +188,10 @@ bool use_chunk(const gdn_dims* p) {
 }
 bool use_chunk_fwd(const gdn_dims* p) { return use_chunk(p); }
 // Chunks per segment of the T-parallel forward (0: the single-pass forward).
+// AUTO takes it where the chunk form runs and the segments pay.
 int tpar_seg(const gdn_dims* p, const Dims& d) {
-  return p->algo == GDN_ALGO_CHUNK_TPAR && d.T > 0 ? gdn::tpar_seg_len(d) : 0;
+  const bool on = p->algo == GDN_ALGO_CHUNK_TPAR || (p->algo == GDN_ALGO_AUTO && use_chunk(p));
+  return on && d.T > 0 ? gdn::tpar_seg_len(d) : 0;
 }
 bool use_chunk_bwd(const gdn_dims* p) { return use_chunk(p); }
 // The chunk matrices go through the checkpoint tail.
