@@ -426,7 +426,7 @@ def bench_long(args, torch, binding, inputs):
         t = torch.from_numpy(np.ascontiguousarray(x))
         return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
 
-    t = {n: up(n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+    t = {n: up(n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "dO")}
     lib = binding.lib()
     st = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(st.cuda_stream)
@@ -466,10 +466,27 @@ def bench_long(args, torch, binding, inputs):
             lib.gdn_set_kernel_events(None, 0)
             kms = {k: round(ev.elapsed_ms(2 * i, 2 * i + 1), 4) for i, k in enumerate(ks)}
             ev.close()
-        out[name] = (ms, kms, wsb)
+        # a training step on the same sequence: fwd (saving for the backward) + bwd
+        tp = dict(t, state0=None, mask=None, dS_final=None)
+        plan = binding.Plan(tp, algo=algo, save=True)
+        for _ in range(args.warmup):
+            plan.fwd()
+            plan.bwd()
+        ev = HipEvents(2)
+        torch.cuda.synchronize()
+        ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
+        for _ in range(args.steps):
+            plan.fwd()
+            plan.bwd()
+        ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
+        torch.cuda.synchronize()
+        train_ms = ev.elapsed_ms(0, 1) / args.steps
+        ev.close()
+        del plan
+        out[name] = (ms, kms, wsb, train_ms)
     B, T, Hk, Hv, Dk, Dv = (L[k] for k in ("B", "T", "Hk", "Hv", "Dk", "Dv"))
-    ms, kms, wsb = out["tpar"]
-    ms1 = out["single"][0]
+    ms, kms, wsb, tr = out["tpar"]
+    ms1, tr1 = out["single"][0], out["single"][3]
     # algorithmic HBM bytes of the prefill: q, k, v, a, b, o once, the final state
     byts = (2 * B * T * Hk * Dk + 2 * B * T * Hv * Dv + 2 * B * T * Hv) * 2 + B * Hv * Dk * Dv * 4
     dom = max(kms, key=lambda k: kms[k])
@@ -503,6 +520,8 @@ def bench_long(args, torch, binding, inputs):
                    "io_dtype": "bf16", "algo": "chunk_tpar"},
         "single_pass_ms": round(ms1, 4),
         "speedup_vs_single_pass": round(ms1 / ms, 3),
+        "train_step_ms": {"tpar": round(tr, 4), "single_pass": round(tr1, 4),
+                          "speedup": round(tr1 / tr, 3)},
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": round(kb[dom] / (kms[dom] / 1e3) / 1e9, 1), "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": round(kb[dom] / (kms[dom] / 1e3) / HBM_PEAK, 4),

@@ -113,7 +113,7 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
       }
     }
   }
-  if (chunk && !bwd && tseg) {
+  if (chunk && tseg) {  // the segment maps (forward or reverse) and start states
     const size_t ns = gdn::tpar_nseg(d, tseg), BH = static_cast<size_t>(d.B) * d.Hv;
     L.maps = take(ns * BH * d.Dk * (static_cast<size_t>(d.Dk) + d.Dv));
     L.hseg = take((ns - 1) * BH * d.Dk * d.Dv);
@@ -301,7 +301,7 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_dims(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = layout(dd, true, use_chunk_bwd(d), use_saved(d)).total;
+  *out = layout(dd, true, use_chunk_bwd(d), use_saved(d), use_chunk_bwd(d) ? tpar_seg(d, dd) : 0).total;
   return GDN_OK;
 }
 
@@ -345,7 +345,7 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
       gdn::ChunkFwdArgs ma{dd, q, k, v, nullptr, mcb, nullptr, nullptr, nullptr,
                            tseg, 1, nullptr, maps, reinterpret_cast<const gdn::bf16*>(vz)};
       if (!launch(st, [&] { return gdn::launch_chunk_fwd(ma, st); })) return GDN_ERR_HIP;
-      gdn::SegChainArgs sa{dd, nseg, state0, maps, hseg};
+      gdn::SegChainArgs sa{dd, nseg, state0, maps, hseg, 0};
       if (!launch(st, [&] { return gdn::launch_seg_chain(sa, st); })) return GDN_ERR_HIP;
       fa.seg = tseg;
       fa.hseg = hseg;
@@ -379,7 +379,8 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     return GDN_ERR_INVALID_ARG;
   if ((dd.nchunk() > 1 || use_saved(d)) && !ckpt) return GDN_ERR_INVALID_ARG;
   const bool chunk = use_chunk_bwd(d);
-  const Layout L = layout(dd, true, chunk, use_saved(d));
+  const int tseg = chunk ? tpar_seg(d, dd) : 0;
+  const Layout L = layout(dd, true, chunk, use_saved(d), tseg);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -401,6 +402,23 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
                          at<gdn::bf16>(ws, L.E), at<gdn::bf16>(ws, L.dHend),
                          dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
+    if (tseg) {  // T-parallel reverse pass: segment maps, their chain (last to first), then the segments
+      const int nseg = gdn::tpar_nseg(dd, tseg);
+      float* maps = at<float>(ws, L.maps);
+      float* hseg = at<float>(ws, L.hseg);
+      float* vz = at<float>(ws, L.vzero);
+      if (!launch(st, [&] { return gdn::launch_fill_zero(vz, 64, st); })) return GDN_ERR_HIP;
+      gdn::ChunkBwdArgs ma = ba;
+      ma.map = 1;
+      ma.seg = tseg;
+      ma.maps = maps;
+      ma.vzero = reinterpret_cast<const gdn::bf16*>(vz);
+      if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ma, st); })) return GDN_ERR_HIP;
+      gdn::SegChainArgs sa{dd, nseg, dS_final, maps, hseg, 1};
+      if (!launch(st, [&] { return gdn::launch_seg_chain(sa, st); })) return GDN_ERR_HIP;
+      ba.seg = tseg;
+      ba.hseg = hseg;
+    }
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_grad(ba, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_param_reduce(ra, st); })) return GDN_ERR_HIP;

@@ -100,6 +100,9 @@ struct ChunkBwdState {
   };
   struct Lane {
     int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
+    int cs, ce, seg, mode;       // chunk range of the segment; 0 output, 1 map identity, 2 map values
+    int scol;                    // first state column of the slice (Dk + Dv columns in map mode)
+    uint32_t ostep, obase;       // dO elements per step and offset (0, 0: the zero rows)
     uint32_t v_row;
     rsrc_t rqt;
     i32x4 dk, dpt, dtt, dat, ddo, dsc;  // raw descriptors of the ring's operands
@@ -131,7 +134,7 @@ struct ChunkBwdState {
     {
       const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
       dma16(q.ddo, &s.dO[512 * q.w],
-            2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hv + q.h) * d.Dv + q.col0 + 8 * pc));
+            2 * (static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * q.ostep + q.obase + 8 * pc));
     }
     const uint32_t so = static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L;
 #pragma unroll
@@ -173,7 +176,7 @@ struct ChunkBwdState {
                                     const f32x4 (&x)[2], float sign) {
     const Dims& d = p.d;
     const rsrc_t r = make_rsrc(static_cast<bf16*>(dst) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv,
-                               (static_cast<size_t>(Lc - 1) * q.v_row + d.Dv) * 2);
+                               q.mode == 0 ? (static_cast<size_t>(Lc - 1) * q.v_row + d.Dv) * 2 : 0);
     const uint32_t o = 2 * (static_cast<uint32_t>(q.tc0 + (q.lr & 3)) * q.v_row + q.col0 + (q.lr & ~3));
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -187,7 +190,7 @@ struct ChunkBwdState {
   // barrier X of this chunk each wave waits for its ring loads (its 4 later
   // stores may stay pending), so the slot is complete for every wave after X.
   __device__ static void step_a(const ChunkBwdArgs& p, Smem& sm, const Lane& q, int c) {
-    issue_ring(p, sm, q, max(c - 1, 0), (c - 1) & 1);
+    issue_ring(p, sm, q, max(c - 1, q.cs), (c - 1) & 1);
     const Dims& d = p.d;
     const int t0 = c * L, Lc = min(L, d.T - t0);
     const Slot& s = sm.ring[c & 1];
@@ -312,14 +315,15 @@ struct ChunkBwdState {
     lds_barrier();  // Y
     load_b(p, q, cn, nxt);  // the next chunk's Q^T, issued while waiting for Ehat
     lds_barrier();  // Z: Ehat complete
-    {
+    {  // map mode: an empty descriptor, nothing stored
       const int e = lr & 3;
-      bf16* dh = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv + q.col0 +
-                 (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + e) * d.Dv + (lr & ~3));
+      const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv,
+                                   q.mode == 0 ? static_cast<size_t>(DK) * d.Dv * 2 : 0);
+      const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + e) * d.Dv + q.col0 + (lr & ~3));
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) *reinterpret_cast<uint2*>(dh + static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct) = dhp[it][ct];
+        for (int ct = 0; ct < 2; ++ct) buf_store_u2(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), dhp[it][ct]);
     }
     // dH -= K^T diag(e^g rk) Ehat, K^T read transposed from the ring's k tile
 #pragma unroll
@@ -342,10 +346,10 @@ struct ChunkBwdState {
   }
 
   __device__ static void run_a(const ChunkBwdArgs& p, Smem& sm, const Lane& q) {
-    issue_ring(p, sm, q, q.NC - 1, (q.NC - 1) & 1);
+    issue_ring(p, sm, q, q.ce - 1, (q.ce - 1) & 1);
     wait_vm<0>();
     lds_barrier();  // X: initial dH; first slot complete
-    for (int c = q.NC - 1; c >= 0; --c) step_a(p, sm, q, c);
+    for (int c = q.ce - 1; c >= q.cs; --c) step_a(p, sm, q, c);
     wait_vm<0>();  // no direct-to-LDS load may land after the workgroup ends
   }
 
@@ -355,8 +359,15 @@ struct ChunkBwdState {
     // dH: rows i = 16 (w RTW + it) + 4 lg + r, columns col0 + 16 ct + lr.
     // Unconditional buffer loads; an absent dS_final reads through an empty
     // descriptor, i.e. as zeros (a load under a branch would wait alone).
-    const rsrc_t rsf = make_rsrc(p.dS_final ? static_cast<const void*>(p.dS_final + sbase) : static_cast<const void*>(p.dstate),
-                                 p.dS_final ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
+    // The start: dS_final (last segment), dL/d the state at the segment's end
+    // (other segments), the identity columns (map mode) or zeros (map mode,
+    // value columns).
+    const int nseg = gridDim.y;
+    const float* h0 = q.mode != 0 ? nullptr
+                      : q.seg == nseg - 1 ? p.dS_final
+                                          : p.hseg + static_cast<size_t>(q.seg) * d.B * d.Hv * DK * d.Dv;
+    const rsrc_t rsf = make_rsrc(h0 ? static_cast<const void*>(h0 + sbase) : static_cast<const void*>(p.k),
+                                 h0 ? static_cast<size_t>(DK) * d.Dv * 4 : 0);
     f32x4 dH[RTW][2];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
@@ -366,19 +377,25 @@ struct ChunkBwdState {
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
           dH[it][ct][r] = buf_f1(rsf, 4 * static_cast<uint32_t>(i * d.Dv + q.col0 + 16 * ct + q.lr));
+          if (q.mode == 1) dH[it][ct][r] = i == q.scol + 16 * ct + q.lr ? 1.f : 0.f;
         }
     put_h(sm, q, dH);
     StageB s0, s1;
-    load_b(p, q, q.NC - 1, s0);
+    load_b(p, q, q.ce - 1, s0);
     lds_barrier();  // X
     // The prefetches are unconditional, from a chunk index clamped to the
-    // first chunk: a load under a branch makes the compiler wait for every
-    // outstanding load where the branch joins, which would void the prefetch.
-    for (int c = q.NC - 1; c >= 0; c -= 2) {
-      step_b(p, sm, q, c, s0, dH, s1, max(c - 1, 0));
-      if (c < 1) break;
-      step_b(p, sm, q, c - 1, s1, dH, s0, max(c - 2, 0));
+    // segment's first chunk: a load under a branch makes the compiler wait for
+    // every outstanding load where the branch joins, which would void the
+    // prefetch.
+    for (int c = q.ce - 1; c >= q.cs; c -= 2) {
+      step_b(p, sm, q, c, s0, dH, s1, max(c - 1, q.cs));
+      if (c < q.cs + 1) break;
+      step_b(p, sm, q, c - 1, s1, dH, s0, max(c - 2, q.cs));
     }
+    if (q.mode == 0 && q.cs > 0) return;  // not the first segment: no dstate
+    const int ostride = q.mode == 0 ? d.Dv : DK + d.Dv;
+    float* out = q.mode == 0 ? p.dstate + sbase
+                             : p.maps + (static_cast<size_t>(q.seg) * d.B * d.Hv + q.bh) * DK * ostride;
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
@@ -386,21 +403,28 @@ struct ChunkBwdState {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 16 * (q.w * RTW + it) + 4 * q.lg + r;
-          p.dstate[sbase + static_cast<size_t>(i) * d.Dv + q.col0 + 16 * ct + q.lr] = dH[it][ct][r];
+          out[static_cast<size_t>(i) * ostride + q.scol + 16 * ct + q.lr] = dH[it][ct][r];
         }
   }
 
   __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
     const Dims& d = p.d;
     Lane q;
-    const int nslice = d.Dv / NV;
+    const int nslice = (p.map ? DK + d.Dv : d.Dv) / NV;
     int slice;
     block_coords(d, nslice, q.b, q.h, slice);
     q.NC = d.nchunk();
+    q.seg = blockIdx.y;
+    q.cs = p.seg ? q.seg * p.seg : 0;
+    q.ce = p.seg ? min(q.cs + p.seg, q.NC) : q.NC;
+    q.mode = !p.map ? 0 : slice < DK / NV ? 1 : 2;
     q.j = q.h / d.G();
     q.bh = q.b * d.Hv + q.h;
     q.bj = q.b * d.Hk + q.j;
-    q.col0 = slice * NV;
+    q.scol = slice * NV;
+    q.col0 = q.mode == 0 ? q.scol : q.mode == 1 ? 0 : q.scol - DK;  // dO / dv / eps columns
+    q.ostep = q.mode == 1 ? 0u : static_cast<uint32_t>(d.Hv * d.Dv);
+    q.obase = q.mode == 1 ? 0u : static_cast<uint32_t>(q.h * d.Dv + q.col0);
     const int tid = threadIdx.x, l = tid & 63;
     q.w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
     q.l = l;
@@ -413,14 +437,14 @@ struct ChunkBwdState {
     {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
       q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
-      q.ddo = raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
+      q.ddo = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
       q.dpt = raw_desc(p.cb.PqT, nmat * L * L * 2);
       q.dtt = raw_desc(p.cb.TxT, nmat * L * L * 2);
       q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
       q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
       q.rqt = make_rsrc(p.cb.QT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);
     }
-    if (q.NC == 0) return;
+    if (q.ce <= q.cs) return;
     if (tid < 256)
       run_a(p, sm, q);
     else
@@ -1150,7 +1174,9 @@ hipError_t launch_state_bf16(const StateBf16Args& a, hipStream_t st) {
 }
 
 hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
-  const int nblk = a.d.B * a.d.Hv * (a.d.Dv / ChunkBwdState<64>::NV);
+  const int NV = ChunkBwdState<64>::NV;
+  const int nseg = a.seg ? (a.d.nchunk() + a.seg - 1) / a.seg : 1;
+  const dim3 nblk(a.d.B * a.d.Hv * ((a.map ? a.d.Dk + a.d.Dv : a.d.Dv) / NV), nseg);
   switch (a.d.Dk) {
     case 64: chunk_bwd_state_kernel<64><<<nblk, ChunkBwdState<64>::NTS, 0, st>>>(a); break;
     case 128: chunk_bwd_state_kernel<128><<<nblk, ChunkBwdState<128>::NTS, 0, st>>>(a); break;

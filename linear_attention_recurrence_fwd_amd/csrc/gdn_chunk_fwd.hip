@@ -839,10 +839,14 @@ struct SegChain {
       const int i = e / NCOL, c = e % NCOL;
       sm.h[i * HSTR + c] = p.state0 ? p.state0[(static_cast<size_t>(bh) * DK + i) * d.Dv + c0 + c] : 0.f;
     }
+    // forward: maps 0 .. nseg - 2 give starts 0 .. nseg - 2 (of segments 1 ..);
+    // reverse: maps nseg - 1 .. 1 give hseg nseg - 2 .. 0
+    const int first = p.reverse ? p.nseg - 1 : 0, step = p.reverse ? -1 : 1;
     float ar[APT];
-    load_a(p.maps + static_cast<size_t>(bh) * DK * W, W, 0, ar);
+    load_a(p.maps + (static_cast<size_t>(first) * BH + bh) * DK * W, W, 0, ar);
     for (int s = 0; s + 1 < p.nseg; ++s) {
-      const float* M = p.maps + (static_cast<size_t>(s) * BH + bh) * DK * W;
+      const int ms = first + step * s, os = p.reverse ? ms - 1 : ms;
+      const float* M = p.maps + (static_cast<size_t>(ms) * BH + bh) * DK * W;
       f32x4 acc[RT];
 #pragma unroll
       for (int it = 0; it < RT; ++it)
@@ -861,7 +865,7 @@ struct SegChain {
         if (m0 + 32 < DK)
           load_a(M, W, m0 + 32, ar);
         else if (s + 2 < p.nseg)
-          load_a(M + BH * DK * W, W, 0, ar);
+          load_a(M + step * static_cast<ptrdiff_t>(BH * DK * W), W, 0, ar);
 #pragma unroll
         for (int it = 0; it < RT; ++it)
 #pragma unroll
@@ -869,7 +873,7 @@ struct SegChain {
             acc[it] = mm16f(acc[it], &sm.a[16 * (w + 4 * it) * HSTR + kk], HSTR, &sm.h[(m0 + kk) * HSTR], HSTR);
       }
       __syncthreads();  // every read of H done
-      float* out = p.hseg + (static_cast<size_t>(s) * BH + bh) * DK * d.Dv;
+      float* out = p.hseg + (static_cast<size_t>(os) * BH + bh) * DK * d.Dv;
 #pragma unroll
       for (int it = 0; it < RT; ++it)
 #pragma unroll

@@ -198,6 +198,8 @@ struct SegChainArgs {
   const float* state0;  // may be null
   const float* maps;    // [nseg, B*Hv, Dk, Dk + Dv]
   float* hseg;          // [nseg - 1, B*Hv, Dk, Dv]
+  int reverse;          // 1: from the last segment back (the backward's chain):
+                        // hseg[s - 1] = A_s hseg[s] + B_s, hseg[nseg - 1] = state0
 };
 
 // Chunk-form backward.  The reverse state pass writes dv, eps (dL/d delta) and
@@ -216,6 +218,15 @@ struct ChunkBwdArgs {
   float* dstate;     // [B,Hv,Dk,Dv]
   double* part_dA;   // [B,NC,Hv] per-chunk sums of dl * l
   double* part_ddt;  // [B,NC,Hv] per-chunk sums of da
+  // T-parallel reverse state pass (as ChunkFwdArgs, in reverse): segment s
+  // runs its chunks last to first; output mode starts it from hseg[s] (dL/d
+  // the state at its end, [nseg - 1, B*Hv, Dk, Dv]; the last segment from
+  // dS_final); map mode runs the augmented [I | 0] with dO = [0 | dO] and
+  // stores the segment's map [A | B] (dL/d its start state) to maps.
+  int seg, map;
+  const float* hseg;
+  float* maps;
+  const bf16* vzero;
 };
 
 // bf16 copies of the states at the chunk starts from the fp32 checkpoints:

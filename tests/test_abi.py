@@ -226,5 +226,8 @@ def test_tpar_segments_only_when_they_pay():
     extra = ws(B.ALGO_CHUNK_TPAR, long1) - ws(B.ALGO_CHUNK, long1)
     # 16 segments (512 chunks / 32 each): maps [16, 4, 128, 256] + starts [15, 4, 128, 128]
     assert extra == 4 * (16 * 4 * 128 * 256 + 15 * 4 * 128 * 128) + 256
+    bws = lambda algo, dims: B.bwd_workspace_bytes(B.make_dims(*dims, B.GDN_BF16, algo))
+    assert bws(B.ALGO_CHUNK_TPAR, long1) - bws(B.ALGO_CHUNK, long1) == extra
+    assert bws(B.ALGO_CHUNK_TPAR, head) == bws(B.ALGO_CHUNK, head)
     assert B.ckpt_elems(B.make_dims(*long1, B.GDN_BF16, B.ALGO_CHUNK_TPAR)) == \
         B.ckpt_elems(B.make_dims(*long1, B.GDN_BF16, B.ALGO_CHUNK))

@@ -1,12 +1,13 @@
-"""GPU parity of the T-parallel chunk forward (GDN_ALGO_CHUNK_TPAR: segment
-maps, a chain over the segments, then every segment's outputs) against the
-fp64 oracle, and against the single-pass chunk forward.  Long sequences with
+"""GPU parity of the T-parallel chunk form (GDN_ALGO_CHUNK_TPAR: segment
+maps, a chain over the segments, then every segment's outputs; in the forward
+and, last segment first, in the backward's reverse state pass) against the
+fp64 oracle, and against the single-pass chunk form.  Long sequences with
 few heads, where the library splits the chunks into segments; slow decays
 (A_log in (-7, -4)), so that a segment's start state reaches far into it and
 the segment maps are far from zero (with the default fast decays the state
 forgets a chunk within a few steps and every route gives the same bits);
 ragged tails, masks, initial states, the saved record and the backward that
-follows (which runs the chunk form).  bf16 bar of 2e-2 (normwise), as for every bf16
+follows.  bf16 bar of 2e-2 (normwise), as for every bf16
 workload; repeated runs bit-identical."""
 import numpy as np
 import pytest
@@ -56,6 +57,7 @@ def test_tpar_parity(name, B, T, Hk, Hv, Dk, Dv, seed, masked):
     o, st, ck = gpu_fwd(t, algo=TPAR)
     g = gpu_bwd(t, ck, algo=TPAR)
     o1, st1, ck1 = gpu_fwd(t, algo=CHUNK)
+    g1 = gpu_bwd(t, ck1, algo=CHUNK)
     torch.cuda.synchronize()
     ro, rst, rck, rg = oracle_all(c, nthreads=16)
     errs = {"o": relerr(to64(o), ro), "state": relerr(to64(st), rst), "ckpt": relerr(to64(ck), rck)}
@@ -63,9 +65,12 @@ def test_tpar_parity(name, B, T, Hk, Hv, Dk, Dv, seed, masked):
         errs[n] = relerr(to64(g[n]), rg[n])
     vs_chunk = {"o": relerr(to64(o), to64(o1)), "state": relerr(to64(st), to64(st1)),
                 "ckpt": relerr(to64(ck), to64(ck1))}
+    for n in ("dq", "dk", "dv", "dstate"):
+        vs_chunk[n] = relerr(to64(g[n]), to64(g1[n]))
     say("[tpar] errors " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     say("[tpar] vs single pass " + " ".join("%s=%.2e" % kv for kv in vs_chunk.items()))
     assert vs_chunk["state"] > 0.0, "the segments must change the rounding (long memory)"
+    assert vs_chunk["dstate"] > 0.0, "the backward's segments must change the rounding"
     bad = {n: e for n, e in list(errs.items()) + [("chunk_" + k, v) for k, v in vs_chunk.items()]
            if not e <= TOL["bf16"]}
     assert not bad, bad
