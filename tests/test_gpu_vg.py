@@ -118,3 +118,28 @@ def test_vg_deterministic_repeat():
         for x, y in zip(outs[0], other):
             assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                                y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+
+
+@pytest.mark.parametrize("T", [1, 70])
+def test_vg_state_in_place(T):
+    """state_out may alias state0 exactly: the same bits as a separate output."""
+    c = inputs.make_vg_case("vg_inplace_T%d" % T, 2, T, 2, 4, 64, 32, "f32", 9200 + T)
+    say("[vg in-place] case=%s" % c.name)
+    t = upload_vg(c)
+    o, st, _ = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], None)
+    s = t["state0"].clone()
+    o2, st2, _ = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], s, None, state_out=s)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == s.data_ptr()
+    assert torch.equal(o, o2) and torch.equal(st, s)
+
+
+def test_vg_empty_sequence():
+    """T = 0: the state passes through, dstate = dS_final, nothing else."""
+    c = inputs.make_vg_case("vg_empty", 2, 0, 2, 4, 64, 32, "f32", 9300)
+    say("[vg empty] case=%s" % c.name)
+    t = upload_vg(c)
+    o, st, ck, g = run_vg(t)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and g["dlg"].numel() == 0
+    assert torch.equal(st, t["state0"]) and torch.equal(g["dstate"], t["dS_final"])
