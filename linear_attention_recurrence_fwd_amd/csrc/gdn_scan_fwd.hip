@@ -48,7 +48,7 @@ struct ScanFwd {
     float k[2][TS][DK];
     float q[2][TS][DK];
     float v[2][TS][JS];
-    float ell[2][TS], beta[2][TS], kq[2][TS];
+    float gs[2][TS], beta[2][TS], kq[2][TS];  // gs: the scalar gate e^l
     float g[VG ? 2 : 1][TS][VG ? DK : 1];  // per-channel gates e^lg (1 on masked steps)
     float o[TS][JS];
     float st[DK][JS + 1];
@@ -147,7 +147,7 @@ struct ScanFwd {
       }
     }
     if (tid < TS) {
-      sm.ell[buf][tid] = s.ell;
+      sm.gs[buf][tid] = expf(s.ell);
       sm.beta[buf][tid] = s.beta;
       sm.kq[buf][tid] = s.kq;
     }
@@ -164,6 +164,25 @@ struct ScanFwd {
         }
       }
     }
+  }
+
+  // One step's operands from the staged tile.
+  struct Ops {
+    float kr[RI], qr[RI], gr[RI];  // gr: per-channel gates (unused for the scalar gate)
+    float v0, v1, g, beta, kq;
+  };
+  __device__ static void load_ops(const Smem& sm, int buf, int tt, int li, int lc, Ops& o) {
+#pragma unroll
+    for (int r = 0; r < RI; ++r) {
+      o.kr[r] = sm.k[buf][tt][li * RI + r];
+      o.qr[r] = sm.q[buf][tt][li * RI + r];
+      if constexpr (VG) o.gr[r] = sm.g[buf][tt][li * RI + r];
+    }
+    o.v0 = sm.v[buf][tt][lc];
+    o.v1 = sm.v[buf][tt][lc + 1];
+    o.g = sm.gs[buf][tt];
+    o.beta = sm.beta[buf][tt];
+    o.kq = sm.kq[buf][tt];
   }
 
   // Global [Dk, Dv] state (slice columns) <-> registers, via sm.st.
@@ -224,14 +243,17 @@ struct ScanFwd {
       const int buf = it & 1, t0 = it * TS;
       if (it + 1 < ntile) load_tile(p, b, h, j, col0, t0 + TS, stg);
       const int nsteps = min(TS, d.T - t0);
+      // A step's LDS operands are read one step ahead (their latency hides
+      // behind the previous step); the read past the tile's last step is of a
+      // row of the same buffer and is not used.
+      Ops nx;
+      load_ops(sm, buf, 0, li, lc, nx);
       for (int tt = 0; tt < nsteps; ++tt) {
-        float kr[RI], qr[RI], gr[RI];
-#pragma unroll
-        for (int r = 0; r < RI; ++r) {
-          kr[r] = sm.k[buf][tt][li * RI + r];
-          qr[r] = sm.q[buf][tt][li * RI + r];
-          if constexpr (VG) gr[r] = sm.g[buf][tt][li * RI + r];
-        }
+        const Ops cu = nx;
+        load_ops(sm, buf, min(tt + 1, TS - 1), li, lc, nx);
+        const float(&kr)[RI] = cu.kr;
+        const float(&qr)[RI] = cu.qr;
+        const float(&gr)[RI] = cu.gr;
         // Per-channel gate: both reads see the decayed rows, u = S^T (g o kn),
         // p = S^T (g o qn), and o = p + (kn . qn) delta.
         float pu0 = 0.f, pu1 = 0.f, pp0 = 0.f, pp1 = 0.f;
@@ -248,10 +270,10 @@ struct ScanFwd {
         pu1 = row_sum16(pu1);
         pp0 = row_sum16(pp0);
         pp1 = row_sum16(pp1);
-        const float g = VG ? 1.f : expf(sm.ell[buf][tt]);
-        const float beta = sm.beta[buf][tt], kq = sm.kq[buf][tt];
-        float d0 = beta * (sm.v[buf][tt][lc] - g * pu0);
-        float d1 = beta * (sm.v[buf][tt][lc + 1] - g * pu1);
+        const float g = VG ? 1.f : cu.g;
+        const float beta = cu.beta, kq = cu.kq;
+        float d0 = beta * (cu.v0 - g * pu0);
+        float d1 = beta * (cu.v1 - g * pu1);
         if (beta == 0.f) d0 = d1 = 0.f;  // masked step: v is not read
 #pragma unroll
         for (int r = 0; r < RI; ++r) {
