@@ -95,3 +95,32 @@ def test_tpar_saved_record_and_repeat():
     assert relerr(to64(o), ro) <= TOL["bf16"] and relerr(to64(st), rst) <= TOL["bf16"]
     for n, x in zip(GRADS, runs[0][2:]):
         assert relerr(to64(x), rg[n]) <= TOL["bf16"], n
+
+
+@pytest.mark.parametrize("kind", ["masked_segment", "extreme"])
+def test_tpar_degenerate_segments(kind):
+    """A segment whose steps are all masked (its map is the identity: the
+    state passes through it) and extreme gates (every map close to 0)."""
+    B, T = 1, 4096
+    if kind == "masked_segment":
+        mask = np.ones((B, T), dtype=np.uint8)
+        mask[0, 1024:2048] = 0   # two whole 512-step segments (8 chunks each)
+        c = inputs.make_case("tpar_" + kind, B, T, 1, 2, 128, 64, "bf16", 506, mask=mask,
+                             A_log_range=(-7.0, -4.0))
+    else:
+        c = inputs.make_case("tpar_" + kind, B, T, 1, 2, 128, 64, "bf16", 507, extreme=True)
+    assert segmented(c)
+    say("[tpar] case=%s" % c.name)
+    t = upload(c)
+    o, st, ck = gpu_fwd(t, algo=TPAR)
+    g = gpu_bwd(t, ck, algo=TPAR)
+    torch.cuda.synchronize()
+    ro, rst, rck, rg = oracle_all(c, nthreads=16)
+    errs = {"o": relerr(to64(o), ro), "state": relerr(to64(st), rst), "ckpt": relerr(to64(ck), rck)}
+    for n in GRADS:
+        errs[n] = relerr(to64(g[n]), rg[n])
+    say("[tpar] errors " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    for n, x in list(g.items()) + [("o", o), ("state", st)]:
+        assert torch.isfinite(x.float()).all(), n
+    bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad
