@@ -693,7 +693,7 @@ def main():
                          "(the known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the operation shards by (batch, key-head group) with no exchange); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
