@@ -143,3 +143,16 @@ def test_vg_empty_sequence():
     torch.cuda.synchronize()
     assert o.numel() == 0 and g["dlg"].numel() == 0
     assert torch.equal(st, t["state0"]) and torch.equal(g["dstate"], t["dS_final"])
+
+
+@pytest.mark.parametrize("kind", ["no_decay", "underflow"])
+def test_vg_extreme_gates(kind):
+    """lg = 0 (g = 1: the delta rule without decay) and lg = -200 on every
+    other channel (g underflows to 0: those rows are wiped each step); the
+    gradients stay finite and match the oracle."""
+    c = inputs.make_vg_case("vg_" + kind, 2, 130, 2, 4, 64, 32, "f32", 9400, mask=None)
+    if kind == "no_decay":
+        c.vals["lg"][...] = 0.0
+    else:
+        c.vals["lg"][..., ::2] = -200.0
+    compare_vg(c)
