@@ -31,7 +31,7 @@ size_t state_slots_elems(const Dims& d) {
 // chunk-start states and the chunk matrices (offsets in fp32 elements,
 // 256-byte aligned).
 struct Saved {
-  size_t HB, Tx, TxT, AtT, PqT, KT, QT, SC, total;
+  size_t HB, Tx, TxT, AtT, PqT, KT, QT, SC, X, total;
 };
 
 Saved saved_layout(const Dims& d) {
@@ -53,6 +53,7 @@ Saved saved_layout(const Dims& d) {
   S.KT = take((kts + 1) / 2);
   S.QT = take((kts + 1) / 2);
   S.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
+  S.X = take((static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv + 1) / 2);
   S.total = off;
   return S;
 }
@@ -224,6 +225,7 @@ void saved_bufs(const Dims& d, const float* ckpt, gdn::ChunkBufs& cb) {
   cb.KT = reinterpret_cast<gdn::bf16*>(tail + S.KT);
   cb.QT = reinterpret_cast<gdn::bf16*>(tail + S.QT);
   cb.sc = tail + S.SC;
+  cb.X = reinterpret_cast<gdn::bf16*>(tail + S.X);
 }
 
 gdn::StepScalars scalars(void* ws, const Layout& L) {
@@ -342,6 +344,7 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
       if (!launch(st, [&] { return gdn::launch_fill_zero(vz, 64, st); })) return GDN_ERR_HIP;
       gdn::ChunkBufs mcb = cb;
       mcb.Hb = nullptr;
+      mcb.X = nullptr;
       gdn::ChunkFwdArgs ma{dd, q, k, v, nullptr, mcb, nullptr, nullptr, nullptr,
                            tseg, 1, nullptr, maps, reinterpret_cast<const gdn::bf16*>(vz)};
       if (!launch(st, [&] { return gdn::launch_chunk_fwd(ma, st); })) return GDN_ERR_HIP;

@@ -474,7 +474,10 @@ __device__ __forceinline__ float oct_sum(float v) {
   return v + dpp<kRowHalfMirror>(v);
 }
 
-template <int DK>
+// XSV: X comes from the forward's saved copy (ChunkBufs::X) instead of being
+// recomputed as Tx (V - diag(e^g rk) K H); both variants use X in bf16, so
+// they give the same bits when the saved X is the recomputed one.
+template <int DK, bool XSV>
 struct ChunkBwdGrad {
   static constexpr int NS = 32;          // Dv columns per slab
   static constexpr int IT = DK / 16;     // 16-row tiles of Dk
@@ -576,7 +579,8 @@ struct ChunkBwdGrad {
     for (int a = 0; a < 4; ++a) f.dh[a] = buf_u2(rdh, ho + 2 * a * d.Dv);
     const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv + v0;
     const size_t vrem = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
-    const rsrc_t rs[3] = {make_rsrc(static_cast<const bf16*>(p.v) + vbase, vrem),
+    const bf16* t0src = XSV ? p.cb.X : static_cast<const bf16*>(p.v);  // tile 0: X, or v to recompute it from
+    const rsrc_t rs[3] = {make_rsrc(t0src + vbase, vrem),
                           make_rsrc(static_cast<const bf16*>(p.dO) + vbase, vrem), make_rsrc(p.E + vbase, vrem)};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -648,6 +652,31 @@ struct ChunkBwdGrad {
     f32x4 dox[2], xe[2];
     float pb[4], pa, pdb, phdh;
   };
+  // Contractions over the slab's columns: dQn, dKn (state terms) and the
+  // Grams dO X^T, X eps^T.  xr8 / xs8: rows ta of X and of
+  // diag(e^{gL-g} beta) X; xt: the X tile [t][v].
+  __device__ static void contract(const Smem& sm, const bf16* xt, const bf16* dt, const bf16* et, int ta, int lr,
+                                  int lg, int hw, const bf16x8& xr8, const bf16x8& xs8, f32x4 (&accQ)[IH],
+                                  f32x4 (&accK)[IH], HeadAcc& ac) {
+    const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta];
+    const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
+    const bf16x8 dos8 = scale8(do8, sq), eps8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), se);
+#pragma unroll
+    for (int k = 0; k < IH; ++k) {
+      const int it = hw * IH + k;
+      const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
+      const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
+      accQ[k] = mfma16(dos8, bhv, accQ[k]);
+      accK[k] = mfma16(eps8, bhv, accK[k]);
+      accK[k] = mfma16(xs8, bdh, accK[k]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sr = (16 * (2 * hw + u) + lr) * VS + 8 * lg;
+      ac.dox[u] = mfma16(do8, load_bf16x8(&xt[sr]), ac.dox[u]);
+      ac.xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), ac.xe[u]);
+    }
+  }
   // One 32-column slab of head h: stage the prefetched H, dH', v, dO, eps
   // in LDS, issue the next slab's loads (unconditional, so the prefetch stays
   // in flight), and accumulate.
@@ -666,10 +695,7 @@ struct ChunkBwdGrad {
         *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = pf.dh[a];
         const uint32_t hw2[2] = {pf.h[a].x, pf.h[a].y}, dw2[2] = {pf.dh[a].x, pf.dh[a].y};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          ac.phdh = fmaf(__uint_as_float(hw2[e] << 16), __uint_as_float(dw2[e] << 16), ac.phdh);
-          ac.phdh = fmaf(__uint_as_float(hw2[e] & 0xffff0000u), __uint_as_float(dw2[e] & 0xffff0000u), ac.phdh);
-        }
+        for (int e = 0; e < 2; ++e) ac.phdh = dot2_bf16(hw2[e], dw2[e], ac.phdh);
       }
     }
     put_chunks(sm, q.tid, pf);
@@ -697,63 +723,75 @@ struct ChunkBwdGrad {
       qh = mfma16(qa[kt], bh8, qh);
       kdt = mfma16(as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), ka[kt], kdt);
     }
-    // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
-    {
-      float rv[4];
+    if constexpr (XSV) {
+      // ---- b_r partial sums; X (tile 0) is loaded
+      const bf16* xl = sm.u.s.vt[0];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tc0 + r, o = t * VS + 16 * hw + lr;
         const float eg = sm.eg[t], cr = eg * sm.rk[t];
-        const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), epv = to_f32(et[o]);
-        rv[r] = vv - cr * kh[r];
+        const float dov = to_f32(dt[o]), epv = to_f32(et[o]);
         ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
         ac.pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, ac.pb[r]);
       }
-      *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
-    }
-    lds_barrier();
-    // ---- X^T = R^T Tx^T: the lane holds X[ta][16 hw + 4 lg + r]
-    {
-      f32x4 xt = f4zero();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        xt = mfma16(load_bf16x8(&sm.u.s.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
+      // X[ta][16 hw + 4 lg + r], in the layout of (K dH')^T
       const int vc = 16 * hw + 4 * lg;
-      const float sx = sm.el[ta] * sm.beta[ta];
-      *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
-      *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) = pack4_bf16(sx * xt[0], sx * xt[1], sx * xt[2], sx * xt[3]);
+      const uint2 x4 = *reinterpret_cast<const uint2*>(&xl[ta * VS + vc]);
       const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
+      const float x4f[4] = {__uint_as_float(x4.x << 16), __uint_as_float(x4.x & 0xffff0000u),
+                            __uint_as_float(x4.y << 16), __uint_as_float(x4.y & 0xffff0000u)};
       const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
                             __uint_as_float(e4.y << 16), __uint_as_float(e4.y & 0xffff0000u)};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        ac.pdb = fmaf(e4f[r], xt[r], ac.pdb);
-        ac.pa = fmaf(kdt[r], xt[r], ac.pa);
+        ac.pdb = fmaf(e4f[r], x4f[r], ac.pdb);
+        ac.pa = fmaf(kdt[r], x4f[r], ac.pa);
       }
-    }
-    lds_barrier();
-    // ---- contractions over the slab's columns
-    {
-      const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta];
-      const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
-      const bf16x8 dos8 = scale8(do8, sq), eps8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), se);
-      const bf16x8 xs8 = load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]);
-      const bf16x8 xr8 = load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]);
-#pragma unroll
-      for (int k = 0; k < IH; ++k) {
-        const int it = hw * IH + k;
-        const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
-        const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
-        accQ[k] = mfma16(dos8, bhv, accQ[k]);
-        accK[k] = mfma16(eps8, bhv, accK[k]);
-        accK[k] = mfma16(xs8, bdh, accK[k]);
+      const bf16x8 xr8 = load_bf16x8(&xl[ta * VS + 8 * lg]);
+      contract(sm, xl, dt, et, ta, lr, lg, hw, xr8, scale8(xr8, sm.el[ta] * sm.beta[ta]), accQ, accK, ac);
+    } else {
+      // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
+      {
+        float rv[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tc0 + r, o = t * VS + 16 * hw + lr;
+          const float eg = sm.eg[t], cr = eg * sm.rk[t];
+          const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), epv = to_f32(et[o]);
+          rv[r] = vv - cr * kh[r];
+          ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
+          ac.pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, ac.pb[r]);
+        }
+        *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
       }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int sr = (16 * (2 * hw + u) + lr) * VS + 8 * lg;
-        ac.dox[u] = mfma16(do8, load_bf16x8(&sm.u.s.xr[sr]), ac.dox[u]);
-        ac.xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), ac.xe[u]);
+      lds_barrier();
+      // ---- X^T = R^T Tx^T: the lane holds X[ta][16 hw + 4 lg + r]
+      {
+        f32x4 xt = f4zero();
+  #pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          xt = mfma16(load_bf16x8(&sm.u.s.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
+        const int vc = 16 * hw + 4 * lg;
+        const float sx = sm.el[ta] * sm.beta[ta];
+        // X in bf16, as the forward saves it: the gate terms and the scaled copy
+        // use the rounded values
+        const uint2 x4 = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
+        const float x4f[4] = {__uint_as_float(x4.x << 16), __uint_as_float(x4.x & 0xffff0000u),
+                              __uint_as_float(x4.y << 16), __uint_as_float(x4.y & 0xffff0000u)};
+        *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = x4;
+        *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) = pack4_bf16(sx * x4f[0], sx * x4f[1], sx * x4f[2], sx * x4f[3]);
+        const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
+        const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
+                              __uint_as_float(e4.y << 16), __uint_as_float(e4.y & 0xffff0000u)};
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ac.pdb = fmaf(e4f[r], x4f[r], ac.pdb);
+          ac.pa = fmaf(kdt[r], x4f[r], ac.pa);
+        }
       }
+      lds_barrier();
+      contract(sm, sm.u.s.xr, dt, et, ta, lr, lg, hw, load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]),
+               load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]), accQ, accK, ac);
     }
     lds_barrier();
   }
@@ -1141,10 +1179,10 @@ struct ChunkBwdGrad {
   }
 };
 
-template <int DK>
+template <int DK, bool XSV>
 __global__ void __launch_bounds__(NTG) chunk_bwd_grad_kernel(ChunkBwdArgs p) {
-  __shared__ typename ChunkBwdGrad<DK>::Smem sm;
-  ChunkBwdGrad<DK>::run(p, sm);
+  __shared__ typename ChunkBwdGrad<DK, XSV>::Smem sm;
+  ChunkBwdGrad<DK, XSV>::run(p, sm);
 }
 
 // bf16 copies of the chunk-start states: 8 elements per thread, grid-stride.
@@ -1190,11 +1228,12 @@ hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
 hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t st) {
   if (a.d.T == 0) return hipSuccess;
   dim3 grid(a.d.nchunk(), a.d.B * a.d.Hk);
+  const bool xs = a.cb.X != nullptr;
   switch (a.d.Dk) {
-    case 64: chunk_bwd_grad_kernel<64><<<grid, NTG, 0, st>>>(a); break;
-    case 128: chunk_bwd_grad_kernel<128><<<grid, NTG, 0, st>>>(a); break;
-    case 192: chunk_bwd_grad_kernel<192><<<grid, NTG, 0, st>>>(a); break;
-    case 256: chunk_bwd_grad_kernel<256><<<grid, NTG, 0, st>>>(a); break;
+    case 64: xs ? chunk_bwd_grad_kernel<64, true><<<grid, NTG, 0, st>>>(a) : chunk_bwd_grad_kernel<64, false><<<grid, NTG, 0, st>>>(a); break;
+    case 128: xs ? chunk_bwd_grad_kernel<128, true><<<grid, NTG, 0, st>>>(a) : chunk_bwd_grad_kernel<128, false><<<grid, NTG, 0, st>>>(a); break;
+    case 192: xs ? chunk_bwd_grad_kernel<192, true><<<grid, NTG, 0, st>>>(a) : chunk_bwd_grad_kernel<192, false><<<grid, NTG, 0, st>>>(a); break;
+    case 256: xs ? chunk_bwd_grad_kernel<256, true><<<grid, NTG, 0, st>>>(a) : chunk_bwd_grad_kernel<256, false><<<grid, NTG, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -548,6 +548,7 @@ struct ChunkFwd {
     const Dims& d = p.d;
     const int lr = q.lr, lg = q.lg;
     const Slot& s = sm.ring[c % NSL];
+    store_x(p, sm, q, c - 1, c > q.cs);  // group A rewrites X^T after barrier 1
     lds_barrier();  // 1
     lds_barrier();  // 2: X complete
     const float egl = s.sc[SC_EGL * L];
@@ -599,6 +600,28 @@ struct ChunkFwd {
     }
     if (p.cb.Hb != nullptr) store_hb(p, q, H, slot ? c + 1 : -1);
     lds_barrier();  // 3: H of the next chunk complete
+  }
+
+  // X of chunk c for the backward (bf16 [B, T, Hv, Dv]; dropped when cb.X is
+  // null or `on` is false), from X^T in LDS while group B waits for A: a
+  // transposing read gives the lane four consecutive columns of step
+  // 16 w + lr, stored with one 8-byte non-temporal store.  Steps past the end
+  // of the sequence fall outside the descriptor.  Group B issues no global
+  // loads in its loop, so these stores hold up no wait for a load.
+  __device__ static void store_x(const ChunkFwdArgs& p, const Smem& sm, const Lane& q, int c, bool on) {
+    const Dims& d = p.d;
+    on = on && p.cb.X != nullptr;
+    const int t0 = max(c, 0) * L, Lc = min(L, d.T - t0);
+    const size_t base = ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
+    const rsrc_t r = make_rsrc(on ? static_cast<const void*>(p.cb.X + base) : p.v,
+                               on ? (static_cast<size_t>(Lc - 1) * q.v_row + NV) * 2 : 0);
+    const uint32_t to = 2 * static_cast<uint32_t>(q.ta) * q.v_row;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int v0 = 4 * (4 * n + q.lg);
+      const uint2 x4 = lds_read_tr16(&sm.xb[(v0 + (q.lr >> 2)) * XS + 16 * q.w + 4 * (q.lr & 3)]);
+      buf_store_u2_nt(r, to + 2 * v0, x4);
+    }
   }
 
   // bf16 copy of H as the state at the start of chunk `slot` ([i][v] rows;
@@ -698,6 +721,7 @@ struct ChunkFwd {
     if (p.cb.Hb != nullptr && q.seg == 0) store_hb(p, q, H, 0);
     lds_barrier();  // 0
     for (int c = q.cs; c < q.ce; ++c) step_b(p, sm, q, c, H);
+    store_x(p, sm, q, q.ce - 1, true);  // the last chunk's X (X^T is no longer rewritten)
     if (q.mode == 0 && q.ce < q.NC) return;  // not the last segment: no final state
     const int ostride = q.mode == 0 ? d.Dv : DK + d.Dv;
     float* out = q.mode == 0 ? p.state_out + sbase

@@ -170,6 +170,12 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
 }
 __device__ __forceinline__ bf16 bf16_of(float v) { return from_f32<bf16>(v); }
 __device__ __forceinline__ bf16x8 zero8() { return as_bf16x8(make_uint4(0, 0, 0, 0)); }
+// a.lo b.lo + a.hi b.hi + c for two packed bf16 pairs (one dot2 instruction;
+// the bf16 products are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
 // Every bf16 of x multiplied by s (fp32 product, rounded to nearest even).
 __device__ __forceinline__ bf16x8 scale8(const bf16x8& x, float s) {
   const uint4 u = __builtin_bit_cast(uint4, x);
@@ -277,6 +283,11 @@ __device__ __forceinline__ void buf_store_u4(rsrc_t r, uint32_t off, uint4 v) {
 }
 __device__ __forceinline__ void buf_store_u2(rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 0);
+}
+// The same store marked non-temporal (streamed: data another kernel reads
+// much later, which should not displace what the running kernels reuse).
+__device__ __forceinline__ void buf_store_u2_nt(rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 2);
 }
 
 // Direct-to-LDS buffer loads (lane i of a load writes its 16 or 4 bytes at

@@ -121,6 +121,10 @@ struct ChunkBufs {
   // [NC, B*Hv, Dk, Dv] the state at the start of chunk c, bf16 (the operand
   // precision of the chunk products); written by chunk_fwd when non-null
   bf16* Hb;
+  // [B, T, Hv, Dv] X_t = v_t - u_t of every step, bf16 (the precision of the
+  // chunk products): written by chunk_fwd and read by chunk_bwd_grad in place
+  // of recomputing it, when non-null
+  bf16* X;
 };
 // Rows of ChunkBufs::sc (per chunk, per step t; g = gamma):
 enum : int {
