@@ -58,23 +58,25 @@ VG_METRIC = "fwd+bwd tokens/sec with a per-key-channel gate at Hk16/Hv64/Dk192/D
 def kernel_bytes(B, T, Hk, Hv, Dk, Dv, io, state0=False, dS_final=False):
     """Algorithmic HBM bytes of each chunk-form kernel under gdn_dims.save (the
     benchmarked path): the I/O tensors each kernel reads or writes, each
-    counted once, and the states the forward hands to the backward -- bf16
-    copies of the state at every chunk start, written by chunk_fwd and read by
-    chunk_bwd_grad (in place of the fp32 checkpoints of the method-bytes
-    formula).  Intermediates in the workspace or the checkpoint buffer (chunk
-    matrices, eps, per-chunk state gradients) are not counted."""
+    counted once, and what the forward hands to the backward -- bf16 copies
+    of the state at every chunk start and X = v - u of every step (bf16),
+    written by chunk_fwd and read by chunk_bwd_grad in place of the fp32
+    checkpoints of the method-bytes formula (together they are smaller).
+    Intermediates in the workspace or the checkpoint buffer (chunk matrices,
+    eps, per-chunk state gradients) are not counted."""
     Q1 = B * T * Hk * Dk * io            # one of q, k (or dq, dk)
     V1 = B * T * Hv * Dv * io            # one of v, o, dO, dv
     A1 = B * T * Hv * io                 # one of a, b, da, db
     Par = 2 * Hv * 4
     Sig = B * Hv * Dk * Dv * 4
     HB = math.ceil(T / 64) * Sig // 2    # bf16 chunk-start states
+    XB = B * T * Hv * Dv * 2             # X of every step, bf16
     s0 = Sig if state0 else 0
     return {
         "chunk_prep": 2 * Q1 + 2 * A1 + Par,
-        "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + HB,
+        "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + HB + XB,
         "chunk_bwd_state": Q1 + 2 * V1 + (Sig if dS_final else 0) + Sig,
-        "chunk_bwd_grad": 2 * Q1 + 2 * V1 + A1 + HB + 2 * Q1 + 2 * A1,
+        "chunk_bwd_grad": 2 * Q1 + V1 + XB + A1 + HB + 2 * Q1 + 2 * A1,
         "param_reduce": Par,
     }
 
