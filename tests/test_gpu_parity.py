@@ -176,6 +176,11 @@ def test_chunk_ragged_dk256_g1():
     run_and_compare(c, algo=CHUNK)
 
 
+def test_chunk_dk64_g4():
+    c = inputs.make_case("chunk_dk64_g4", 2, 150, 2, 8, 64, 96, "bf16", 81)
+    run_and_compare(c, algo=CHUNK)
+
+
 def test_chunk_qwen35_9b_t256():
     run_and_compare(inputs.qwen35_9b(256), algo=CHUNK)
 
@@ -232,14 +237,17 @@ def test_chunk_checkpoint_interchange():
         assert all(e <= TOL["bf16"] for e in errs.values()), errs
 
 
-@pytest.mark.parametrize("case", ["9b_t256", "ragged_dk128", "edge65_masked", "edge1"])
+@pytest.mark.parametrize("case", ["9b_t256", "ragged_dk128", "ragged_dk256_g1", "dk64_g4", "edge65_masked", "edge1"])
 def test_chunk_saved_matrices_bitwise(case):
-    """Under gdn_dims.save the forward saves the chunk matrices and the bf16
-    chunk-start states, and the backward uses them instead of recomputing the
-    matrices and converting the fp32 checkpoints: every output and every
-    gradient is bit-identical to the run without save."""
+    """Under gdn_dims.save the forward saves the chunk matrices, the bf16
+    chunk-start states and X of every step, and the backward uses them instead
+    of recomputing the matrices and X and converting the fp32 checkpoints:
+    every output and every gradient is bit-identical to the run without save
+    (each head size has its own gradient-pass kernel for the saved path)."""
     c = {"9b_t256": lambda: inputs.qwen35_9b(256),
          "ragged_dk128": lambda: inputs.make_case("chunk_ragged_dk128", 2, 200, 2, 4, 128, 64, "bf16", 79),
+         "ragged_dk256_g1": lambda: inputs.make_case("chunk_ragged_dk256", 1, 130, 2, 2, 256, 32, "bf16", 80),
+         "dk64_g4": lambda: inputs.make_case("chunk_dk64_g4", 2, 150, 2, 8, 64, 96, "bf16", 81),
          "edge65_masked": lambda: inputs.edge(65, masked=True, extreme=False, dtype="bf16"),
          "edge1": lambda: inputs.edge(1, masked=False, extreme=False, dtype="bf16")}[case]()
     say("[saved] case=%s" % c.name)
