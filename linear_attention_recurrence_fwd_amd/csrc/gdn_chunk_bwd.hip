@@ -23,7 +23,8 @@
 //   dl_t = e^{gL} <dH', H> + sum_{s<t} a_s + sum_{r>=t} b_r
 //          + sum_{r>=t} sum_{s<t} e^{g_r-g_s} beta_s [(qn_r.kn_s)(dO_r.X_s) - beta_r (kn_r.kn_s)(eps_r.X_s)]
 //   a_s = e^{gL-g_s} beta_s kn_s^T dH' X_s,  b_r = e^{g_r} (qn_r^T H dO_r - beta_r kn_r^T H eps_r)
-// with X recomputed from the checkpointed H as in the forward.  Every decay is
+// with X the forward's saved copy, or recomputed from the checkpointed H as in
+// the forward when there is no saved record.  Every decay is
 // e^{-|g_t - g_s|}; nothing is divided by a decay.
 //
 // Kernels:
@@ -34,7 +35,8 @@
 //                    (bf16, transposed) and dstate.
 //   chunk_bwd_grad   one workgroup per (chunk, batch, key head), looping over
 //                    the group's value heads and 32-column slabs of Dv, with H
-//                    read from the bf16 copies of the chunk-start states.
+//                    read from the bf16 copies of the chunk-start states and
+//                    X from the forward's saved copy (else recomputed).
 //                    Writes dq, dk (after the L2-normalisation backward), da,
 //                    db and the per-chunk parameter sums.  Fixed summation
 //                    order throughout; no atomics.

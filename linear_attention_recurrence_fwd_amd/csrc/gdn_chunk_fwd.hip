@@ -29,7 +29,8 @@
 //               only, so the prefetch stays in flight across them).  Blocks
 //               that share a key head run on one XCD, so their K / Q / K^T
 //               reads hit that XCD's L2.  Writes o, the checkpoints and the
-//               final state.
+//               final state, and for the backward's saved record the bf16
+//               chunk-start states and X of every step.
 #include "gdn_dev.h"
 #include "gdn_internal.h"
 

@@ -16,7 +16,7 @@
 // dkn: the lane layout makes those sums lane-local.  One workgroup per (b, h,
 // slice of 8 NW columns); wave w owns 8 columns and lane l the rows l + 64 m
 // (m < RM = Dk/64, rows past Dk held as zeros) of them.  The per-step column
-// sums (u, eps) are wave reductions.
+// sums (u, eps) are wave reductions, eight columns at a time (wave_sum8).
 //
 // The reverse walk needs S_{t-1} at every step.  Per chunk:
 //   phase 1, forward from the chunk's checkpoint: stores the state every NB
