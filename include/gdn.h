@@ -105,7 +105,7 @@ typedef struct gdn_dims {
  * whose contents are private to the library: the state at the start of every
  * chunk (initial state included) rounded to bf16, which is the precision the
  * chunk products consume it in, and the per-chunk matrices the backward needs
- * (the in-chunk inverse and its transpose, the decayed key/key and query/key
+ * (the in-chunk inverse, the decayed key/key and query/key
  * Gram matrices, the chunk's k and q transposed, the per-step chunk scalars)
  * and every step's X = v - u (the value minus the state's prediction of it,
  * bf16), which spares the backward its recomputation:

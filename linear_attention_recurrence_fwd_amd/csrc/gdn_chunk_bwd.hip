@@ -82,7 +82,7 @@ struct ChunkBwdState {
   struct Slot {
     bf16 k[L * DK];    // k rows, swizzle t & 7
     bf16 pt[L * L];    // P^T rows, swizzle t & 7
-    bf16 tt[L * L];    // Tx^T rows, swizzle t & 7
+    bf16 tx[L * L];    // Tx rows, swizzle t & 7 (Tx^T operands by transposing reads)
     bf16 at[L * L];    // A^T rows, swizzle t & 7
     bf16 dO[L * NV];   // dO rows of this slice's columns, swizzle t & 3
     float sc[8 * L];   // chunk scalar rows 0 .. 7
@@ -107,7 +107,7 @@ struct ChunkBwdState {
     uint32_t ostep, obase;       // dO elements per step and offset (0, 0: the zero rows)
     uint32_t v_row;
     rsrc_t rqt;
-    i32x4 dk, dpt, dtt, dat, ddo, dsc;  // raw descriptors of the ring's operands
+    i32x4 dk, dpt, dtx, dat, ddo, dsc;  // raw descriptors of the ring's operands
   };
 
   __device__ static __forceinline__ int kpos(int t, int p) { return 8 * (t * NPK + (p ^ (t & 7))); }
@@ -130,7 +130,7 @@ struct ChunkBwdState {
       const int n = 2 * q.w + jj, pos = 64 * n + l, t = pos / 8, pc = (pos % 8) ^ (t & 7);
       const uint32_t o = 2 * (mat + t * L + 8 * pc);
       dma16(q.dpt, &s.pt[512 * n], o);
-      dma16(q.dtt, &s.tt[512 * n], o);
+      dma16(q.dtx, &s.tx[512 * n], o);
       dma16(q.dat, &s.at[512 * n], o);
     }
     {
@@ -203,7 +203,12 @@ struct ChunkBwdState {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       pqa[kt] = load_bf16x8(&s.pt[xpos(ta, 4 * kt + lg)]);
-      txa[kt] = load_bf16x8(&s.tt[xpos(ta, 4 * kt + lg)]);
+      // row ta of Tx^T: column ta of rows 32 kt + 8 lg .. + 7 of Tx, by two
+      // transposing reads of four rows each
+      const int sr = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * q.w + ((lr >> 1) & 1);
+      const uint2 lo = lds_read_tr16(&s.tx[xpos(sr, pc) + 4 * (lr & 1)]);
+      const uint2 hi = lds_read_tr16(&s.tx[xpos(sr + 4, pc) + 4 * (lr & 1)]);
+      txa[kt] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       ata[kt] = load_bf16x8(&s.at[xpos(ta, 4 * kt + lg)]);
     }
     const float4 kl4 = *reinterpret_cast<const float4*>(&s.sc[SC_KL * L + q.tc0]);
@@ -441,7 +446,7 @@ struct ChunkBwdState {
       q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
       q.ddo = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
       q.dpt = raw_desc(p.cb.PqT, nmat * L * L * 2);
-      q.dtt = raw_desc(p.cb.TxT, nmat * L * L * 2);
+      q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
       q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
       q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
       q.rqt = make_rsrc(p.cb.QT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);

@@ -345,16 +345,6 @@ struct ChunkPrep {
     }
     __syncthreads();
     store_mat(sm, p.cb.Tx + mat, tid);
-    if (bwd_out) {  // Tx^T: row r is column r of the staged Tx
-      for (int u = tid; u < L * L / 8; u += NT) {
-        const int r = u >> 3, c8 = 8 * (u & 7);
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = sm.u.m.st[(c8 + e) * SP + r];
-        *reinterpret_cast<uint4*>(p.cb.TxT + mat + r * L + c8) =
-            make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
-      }
-    }
   }
 };
 
