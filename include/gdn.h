@@ -60,7 +60,11 @@ enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
  *   CHUNK  the chunked matrix form over 64-step chunks: bf16 matrix-core
  *          products with fp32 accumulation and an fp32 state carried between
  *          chunks.  Built for dtype bf16, Dk in {64, 128, 192, 256} and Dv a
- *          multiple of 32 up to 256; other shapes return GDN_ERR_UNSUPPORTED.
+ *          multiple of 32 up to 256, and only while its per-chunk tensors
+ *          stay below 4 GiB each: B * Hv * ceil(T/64) * 8192 bytes (the 64 x 64
+ *          bf16 chunk matrices) and B * Hk * ceil(T/64) * Dk * 128 bytes (the
+ *          transposed k / q rows).  Other shapes return GDN_ERR_UNSUPPORTED
+ *          (AUTO runs SCAN for them).
  *          Its results agree with SCAN to bf16 rounding (about 1e-2 relative,
  *          normwise), not bitwise.
  *   AUTO   CHUNK where it is built and T > 1, else SCAN; the CHUNK forward
@@ -128,7 +132,9 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
  *   mask     [B,T] uint8, nonzero = valid step; NULL = all valid
  *   o        [B,T,Hv,Dv] dtype (out)
  *   state_out[B,Hv,Dk,Dv] fp32 (out); may alias state0 exactly (in-place
- *            decode); no other overlap between outputs and inputs is allowed
+ *            update; such a call runs the single-pass forward, never the
+ *            T-parallel one); no other overlap between outputs and inputs is
+ *            allowed
  *   ckpt     [ceil(T/64)-1, B,Hv,Dk,Dv] fp32 (out): ckpt[c-1] = state before
  *            step 64c; when d->save applies, the library's own record
  *            instead (gdn_ckpt_elems elements).  NULL = not written

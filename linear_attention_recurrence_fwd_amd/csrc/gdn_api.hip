@@ -122,6 +122,25 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
   return L;
 }
 
+// The chunk kernels address their per-(head, chunk) matrices, the transposed
+// k / q rows and the per-step chunk scalars through buffer descriptors whose
+// size and 32-bit byte offsets cover the whole tensor, so each must stay
+// below 4 GiB: the 64 x 64 bf16 matrices (B Hv ceil(T/64) of them) and the
+// transposed rows (B Hk ceil(T/64) Dk x 64, bf16).  q, k, v, o, the saved X
+// and every per-chunk state slot are within that bound once their element
+// counts fit in int32 (2 bytes per element).
+bool chunk_fits(const gdn_dims* p) {
+  const double lim = 4294967296.0;
+  const double nc = static_cast<double>((p->T + 63) / 64);
+  const double mats = static_cast<double>(p->B) * p->Hv * nc * 64.0 * 64.0 * 2.0;
+  const double kts = static_cast<double>(p->B) * p->Hk * nc * p->Dk * 64.0 * 2.0;
+  return mats < lim && kts < lim;
+}
+bool chunk_ok(const gdn_dims* p) {
+  return gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16) &&
+         chunk_fits(p);
+}
+
 // Checks everything that does not depend on pointers.
 int check_dims(const gdn_dims* p, Dims* out) {
   if (!p) return GDN_ERR_INVALID_ARG;
@@ -132,8 +151,7 @@ int check_dims(const gdn_dims* p, Dims* out) {
   if (p->algo != GDN_ALGO_AUTO && p->algo != GDN_ALGO_SCAN && p->algo != GDN_ALGO_CHUNK &&
       p->algo != GDN_ALGO_CHUNK_TPAR)
     return GDN_ERR_INVALID_ARG;
-  if ((p->algo == GDN_ALGO_CHUNK || p->algo == GDN_ALGO_CHUNK_TPAR) &&
-      !gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16))
+  if ((p->algo == GDN_ALGO_CHUNK || p->algo == GDN_ALGO_CHUNK_TPAR) && !chunk_ok(p))
     return GDN_ERR_UNSUPPORTED;
   if (!gdn::scan_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv)))
     return GDN_ERR_UNSUPPORTED;
@@ -183,7 +201,7 @@ P* at(void* ws, size_t off) {
 bool use_chunk(const gdn_dims* p) {
   if (p->algo == GDN_ALGO_CHUNK || p->algo == GDN_ALGO_CHUNK_TPAR) return true;
   if (p->algo == GDN_ALGO_SCAN) return false;
-  return p->T > 1 && gdn::chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16);
+  return p->T > 1 && chunk_ok(p);
 }
 bool use_chunk_fwd(const gdn_dims* p) { return use_chunk(p); }
 // Chunks per segment of the T-parallel forward (0: the single-pass forward).
@@ -315,7 +333,11 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   if (has_t && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
   if (use_saved(d) && !ckpt) return GDN_ERR_INVALID_ARG;  // the matrices are saved there
   const bool chunk = use_chunk_fwd(d);
-  const int tseg = chunk ? tpar_seg(d, dd) : 0;
+  // An in-place update (state_out == state0) runs the single pass: in the
+  // T-parallel output pass the first segment's workgroups read state0 while
+  // the last segment's write state_out, with nothing ordering the two.
+  const bool in_place = state0 != nullptr && state0 == state_out;
+  const int tseg = chunk && !in_place ? tpar_seg(d, dd) : 0;
   const Layout L = layout(dd, false, chunk, use_saved(d), tseg);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;

@@ -48,6 +48,34 @@ def relerr(x, ref):
     return float(num / den)
 
 
+def elemerr(x, ref, floor=0.1):
+    """Elementwise companion of relerr: the 99.9th percentile and the maximum
+    of |x - ref| / (|ref| + floor * rms(ref)) (an absolute floor at a tenth of
+    the tensor's typical magnitude keeps entries near zero, whose relative
+    error says nothing, from dominating)."""
+    x, ref = np.asarray(x, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    if not ref.size:
+        return 0.0, 0.0
+    scale = float(np.sqrt(np.mean(ref * ref)))
+    if scale == 0.0:
+        m = float(np.max(np.abs(x)))
+        return m, m
+    r = np.abs(x - ref) / (np.abs(ref) + floor * scale)
+    return float(np.quantile(r, 0.999)), float(np.max(r))
+
+
+def report(tag, pairs):
+    """Print normwise and elementwise errors of (name, x, ref) triples and
+    return the normwise ones."""
+    errs, lines = {}, []
+    for n, x, ref in pairs:
+        errs[n] = relerr(x, ref)
+        p999, mx = elemerr(x, ref)
+        lines.append("%s=%.2e (elem p99.9 %.2e max %.2e)" % (n, errs[n], p999, mx))
+    say("[%s] normwise (elementwise) errors: %s" % (tag, " ".join(lines)))
+    return errs
+
+
 def gpu_fwd(t, algo=binding.ALGO_AUTO, need_ckpt=True, save=False):
     return binding.fwd(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"],
                        t["state0"], t["mask"], need_ckpt=need_ckpt, algo=algo, save=save)

@@ -232,3 +232,58 @@ def test_tpar_segments_only_when_they_pay():
     assert bws(B.ALGO_CHUNK_TPAR, head) == bws(B.ALGO_CHUNK, head)
     assert B.ckpt_elems(B.make_dims(*long1, B.GDN_BF16, B.ALGO_CHUNK_TPAR)) == \
         B.ckpt_elems(B.make_dims(*long1, B.GDN_BF16, B.ALGO_CHUNK))
+
+
+@pytest.mark.parametrize("dims", [
+    (64, 65536, 4, 8, 64, 32),      # 64x64 chunk matrices: 64*8*1024*8192 B = 4 GiB
+    (24, 262144, 4, 8, 64, 32),     # 6 GiB of chunk matrices
+    (4096, 65, 16, 16, 256, 32),    # transposed k rows of the ragged chunks: 4096*16*2*256*128 B = 4 GiB
+])
+def test_chunk_rejects_tensors_past_4gib(dims):
+    """The chunk kernels reach their per-chunk tensors through buffer
+    descriptors with 32-bit byte offsets; a shape whose chunk matrices or
+    transposed k / q rows would reach 4 GiB is refused by CHUNK and
+    CHUNK_TPAR (GDN_ERR_UNSUPPORTED) and runs the scan under AUTO, instead of
+    wrapping its offsets."""
+    for algo in (B.ALGO_CHUNK, B.ALGO_CHUNK_TPAR):
+        for save in (False, True):
+            d = B.make_dims(*dims, B.GDN_BF16, algo, save=save)
+            for q in (B.fwd_workspace_bytes, B.bwd_workspace_bytes, B.ckpt_elems):
+                with pytest.raises(B.GdnError) as e:
+                    q(d)
+                assert e.value.code == 2
+    auto = B.make_dims(*dims, B.GDN_BF16, B.ALGO_AUTO, save=True)
+    scan = B.make_dims(*dims, B.GDN_BF16, B.ALGO_SCAN)
+    assert B.fwd_workspace_bytes(auto) == B.fwd_workspace_bytes(scan)
+    assert B.ckpt_elems(auto) == B.ckpt_elems(scan)
+
+
+def test_chunk_accepts_just_below_4gib():
+    """One chunk fewer than the 4 GiB matrices: still the chunk form."""
+    d = B.make_dims(64, 65536 - 64, 4, 8, 64, 32, B.GDN_BF16, B.ALGO_CHUNK)
+    assert B.fwd_workspace_bytes(d) > 0
+    auto = B.make_dims(64, 65536 - 64, 4, 8, 64, 32, B.GDN_BF16, B.ALGO_AUTO)
+    assert B.fwd_workspace_bytes(auto) == B.fwd_workspace_bytes(d)
+
+
+def test_in_place_forward_takes_the_single_pass():
+    """state_out == state0 with a long few-head sequence: the T-parallel
+    output pass would read state0 in its first segment while its last segment
+    writes state_out, so the call runs the single pass.  Its workspace is the
+    single pass's, so the T-parallel size is more than enough and a buffer of
+    exactly the single pass's size is accepted (validated on the host; the
+    short workspace check is the only one that depends on the route)."""
+    lib = B.lib()
+    dims = (1, 32768, 2, 4, 128, 128)
+    dt = B.make_dims(*dims, B.GDN_BF16, B.ALGO_CHUNK_TPAR)
+    single = B.fwd_workspace_bytes(B.make_dims(*dims, B.GDN_BF16, B.ALGO_CHUNK))
+    assert B.fwd_workspace_bytes(dt) > single
+    p = _fake(13)  # q k v a b A_log dt_bias state0 mask o state_out ckpt ws
+    args = list(p)
+    args[10] = None  # state_out missing: rejected before any launch either way
+    assert lib.gdn_fwd(ctypes.byref(dt), *args, single, None) == 1
+    args = list(p)
+    args[10] = args[7]  # in place; a workspace one byte short of the single pass is refused
+    assert lib.gdn_fwd(ctypes.byref(dt), *args, single - 1, None) == 3
+    args = list(p)  # not in place: the T-parallel route needs its larger workspace
+    assert lib.gdn_fwd(ctypes.byref(dt), *args, single, None) == 3

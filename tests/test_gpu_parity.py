@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import GRADS, TOL, dev_tensor, gpu_bwd, gpu_fwd, oracle_all, relerr, say, to64, upload
+from helpers import GRADS, TOL, dev_tensor, gpu_bwd, gpu_fwd, oracle_all, relerr, report, say, to64, upload
 from linear_attention_recurrence_fwd_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
@@ -35,12 +35,11 @@ def run_and_compare(case, tol=None, algo=binding.ALGO_AUTO, nthreads=8):
     g = gpu_bwd(t, ck, algo=algo)
     torch.cuda.synchronize()
     ro, rst, rck, rg = oracle_all(case, nthreads=nthreads)
-    errs = {"o": relerr(to64(o), ro), "state": relerr(to64(st), rst)}
+    pairs = [("o", to64(o), ro), ("state", to64(st), rst)]
     if rck.shape[0]:
-        errs["ckpt"] = relerr(to64(ck), rck)
-    for n in GRADS:
-        errs[n] = relerr(to64(g[n]), rg[n])
-    say("[parity] errors " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+        pairs.append(("ckpt", to64(ck), rck))
+    pairs += [(n, to64(g[n]), rg[n]) for n in GRADS]
+    errs = report("parity", pairs)
     for n, x in list(g.items()) + [("o", o), ("state", st)]:
         assert torch.isfinite(x.float()).all(), n
     bad = {n: e for n, e in errs.items() if not e <= tol}
