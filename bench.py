@@ -28,6 +28,7 @@ HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 FP32_VEC_PEAK = 157.3e12     # FLOP/s, MI355X fp32 vector (packed FMA)
 # Metal VJP fwd+bwd on an M4 Max (mlx-lm PR, "Performance" table), for context
 PAGES_FWD_BWD_MS = {256: 13.4, 2048: 149.8}
+PAGES_FWD_BWD_MS_ALL = {256: 13.4, 512: 28.2, 1024: 62.2, 2048: 149.8}
 
 # Kernels launched per step, in order, by kernel family.
 KERNELS = {
@@ -146,94 +147,241 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(self.ev[i]))
 
 
-def cpu_baseline(T, seconds_hint=True):
-    """The fp64 oracle on a bounded sample of the 9B workload: the same T and
-    per-head shape, 8 of the 16 key heads (32 of 64 value heads), fwd + bwd,
-    timed on the host; tokens/s scaled to all heads (work is linear in heads)."""
+class Flush:
+    """A 1 GiB scratch buffer written before every timed repetition, so that
+    no operand of a repetition is served from the previous one's cache lines:
+    the MI355X's memory-side cache (MALL, 256 MB) and the L2s hold the
+    scratch afterwards, not the workload's tensors."""
+
+    def __init__(self, torch, mib=1024):
+        self.buf = torch.empty((mib << 20,), dtype=torch.uint8, device="cuda:0")
+        self.n = 0
+
+    def __call__(self):
+        self.n = (self.n + 1) & 0xff
+        self.buf.fill_(self.n)
+
+
+def _stats(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"median": round(med, 5), "min": round(xs[0], 5), "max": round(xs[-1], 5),
+            "mean": round(sum(xs) / n, 5)}
+
+
+def measure(torch, lib, stream, run, kernels, steps, warmup, flush):
+    """Times `run` (one step: the library calls that make up the hot path).
+
+    1. `steps` repetitions, each after a cache flush, each between two HIP
+       events on the calls' stream (the flush is outside them): the per-step
+       times (median, min, max).  The loop is bracketed by device
+       synchronisations; its wall time includes the flushes.
+    2. The same with every kernel between its own pair of events
+       (gdn_set_kernel_events): per-kernel times (median over the steps).
+    3. `steps` repetitions back to back without flushes, two events around
+       all of them: the mean (the rate of a steady stream of calls, whose
+       operands may partly come from cache)."""
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = HipEvents(2 * steps)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        flush()
+        ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[2 * i]), sp)
+        run()
+        ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[2 * i + 1]), sp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)]
+    ev.close()
+    nk = len(kernels)
+    per_kernel = {k: [] for k in kernels}
+    if nk:
+        ev = HipEvents(2 * nk * steps)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            flush()
+            lib.gdn_set_kernel_events(ev.ptr(2 * nk * i), 2 * nk)
+            run()
+        torch.cuda.synchronize()
+        lib.gdn_set_kernel_events(None, 0)
+        for i in range(steps):
+            for j, k in enumerate(kernels):
+                per_kernel[k].append(ev.elapsed_ms(2 * nk * i + 2 * j, 2 * nk * i + 2 * j + 1))
+        ev.close()
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
+    for _ in range(steps):
+        run()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
+    torch.cuda.synchronize()
+    unflushed = ev.elapsed_ms(0, 1) / steps
+    ev.close()
+    return {"step": _stats(step_ms), "kernels": {k: _stats(v) for k, v in per_kernel.items() if v},
+            "unflushed_ms": round(unflushed, 5), "wall_s": round(wall, 3)}
+
+
+def time_calls(torch, fn, argl, steps, warmup, flush):
+    """Decode-style timing: a step is the calls of `argl` in order (each a
+    single-token call updating the state in place).  Flushed: every call after
+    a cache flush, between its own two HIP events (median, min, max per call);
+    unflushed: `steps` steps back to back, two events around all of them."""
+    def call(a):
+        rc = fn(*a)
+        if rc:
+            raise RuntimeError("library call failed with status %d" % rc)
+    sp = argl[0][-1]
+    for _ in range(warmup):
+        for a in argl:
+            call(a)
+    torch.cuda.synchronize()
+    n = steps * len(argl)
+    ev = HipEvents(2 * n)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    i = 0
+    for _ in range(steps):
+        for a in argl:
+            flush()
+            ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[2 * i]), sp)
+            call(a)
+            ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[2 * i + 1]), sp)
+            i += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    flushed = [ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(n)]
+    ev.close()
+    ev = HipEvents(2)
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
+    for _ in range(steps):
+        for a in argl:
+            call(a)
+    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
+    torch.cuda.synchronize()
+    unflushed = ev.elapsed_ms(0, 1) / n
+    ev.close()
+    return {"flushed_call_ms": _stats(flushed), "unflushed_call_ms": round(unflushed, 5),
+            "wall_s": round(wall, 3)}
+
+
+def copy_bandwidth(torch, mib=1024, reps=5):
+    """Measured device-to-device copy rate (bytes read + written per second)
+    of a `mib` MiB buffer: the attainable counterpart of the nominal 8 TB/s."""
+    n = mib << 20
+    src = torch.empty((n,), dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del src, dst
+    ms = _stats(ts)["median"]
+    return {"bytes_per_copy": 2 * n, "median_ms": ms, "GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(T):
+    """The fp64 oracle (as it stands: plain sequential C, parallel only over
+    independent (batch, value head) pairs) timed on the host on bounded
+    samples of the 9B workload at the same T, fwd + bwd:
+      - all 16 key heads (64 value heads) on min(16, cpu_count) threads;
+      - 2 key heads (8 value heads) on 1 thread, tokens/s scaled to the 64
+        heads (the work is linear in the heads).
+    `value` is the multi-threaded rate."""
     import oracle
     from linear_attention_recurrence_fwd_amd import inputs
     threads = max(1, min(16, os.cpu_count() or 1))
-    c = inputs.make_case("9b_sample", 1, T, 8, 32, 192, 128, "bf16", 3, state_std=None,
-                         dS_final=False)
-    oracle.fwd(*c.oracle_args(), nthreads=threads)  # loads / warms the library
-    t0 = time.perf_counter()
-    oracle.fwd(*c.oracle_args(), nthreads=threads)
-    oracle.bwd(*c.oracle_args(), c.vals["dO"], None, nthreads=threads)
-    dt = time.perf_counter() - t0
-    scale = 64 / 32
-    return {"value": round(c.B * T / (dt * scale), 3), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "fp64 oracle fwd+bwd (64-step checkpointed recompute), B=1 T=%d, "
-                      "Hk=8 Hv=32 Dk=192 Dv=128 (1/2 of the heads), %.2f s wall on %d threads; "
-                      "tokens/s scaled by 2" % (T, dt, threads)}
+
+    def run(Hk, nth):
+        c = inputs.make_case("9b_sample", 1, T, Hk, 4 * Hk, 192, 128, "bf16", 3, state_std=None,
+                             dS_final=False)
+        oracle.fwd(*c.oracle_args(), nthreads=nth)  # loads / warms the library
+        t0 = time.perf_counter()
+        oracle.fwd(*c.oracle_args(), nthreads=nth)
+        oracle.bwd(*c.oracle_args(), c.vals["dO"], None, nthreads=nth)
+        return time.perf_counter() - t0
+
+    dt_n = run(16, threads)
+    dt_1 = run(2, 1)
+    return {"value": round(T / dt_n, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(T / (dt_1 * 8), 3),
+            "cpu_model": cpu_model(), "cpu_count": os.cpu_count(),
+            "sample": "fp64 oracle fwd+bwd (64-step checkpointed recompute), B=1 T=%d Dk=192 "
+                      "Dv=128: Hk=16 Hv=64 (the whole workload) in %.2f s wall on %d threads; "
+                      "Hk=2 Hv=8 (1/8 of the heads) in %.2f s on 1 thread, tokens/s scaled by 1/8"
+                      % (T, dt_n, threads, dt_1)}
+
+
+def upload_case(torch, case, names):
+    import numpy as np
+    dev = torch.device("cuda:0")
+    out = {}
+    for n in names:
+        x = case.store(n)
+        if x is None:
+            out[n] = None
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        out[n] = (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
+    return out
+
+
+TRAIN_NAMES = ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state0", "dO", "dS_final")
+
+
+def train_plan(torch, binding, inputs, T, algo):
+    case = inputs.qwen35_9b(T)
+    t = upload_case(torch, case, TRAIN_NAMES)
+    t["mask"] = None
+    plan = binding.Plan(t, algo=algo)
+
+    def run():
+        plan.fwd()
+        plan.bwd()
+    return case, t, plan, run
 
 
 def bench_train(args, torch, binding, inputs):
     T = {"9b_t2048": 2048, "9b_t256": 256}[args.config]
-    case = inputs.qwen35_9b(T)
-    dev = torch.device("cuda:0")
-
-    def up(n):
-        import numpy as np
-        x = case.store(n)
-        if x is None:
-            return None
-        t = torch.from_numpy(np.ascontiguousarray(x))
-        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
-
-    t = {n: up(n) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state0", "dO",
-                            "dS_final")}
-    t["mask"] = None
     algo = {"auto": binding.ALGO_AUTO, "scan": binding.ALGO_SCAN,
             "chunk": binding.ALGO_CHUNK}[args.algo]
     # the kernel family AUTO picks for this workload (bf16 with a supported
     # head size runs the chunked form)
     family = "scan" if args.algo == "scan" else "chunk"
-    plan = binding.Plan(t, algo=algo)
-    for _ in range(args.warmup):
-        plan.fwd()
-        plan.bwd()
-    torch.cuda.synchronize()
-
     kernels = KERNELS[family]
-    nk = len(kernels)
     lib = binding.lib()
-    sp = ctypes.c_void_p(plan.stream.cuda_stream)
-    # headline: K steps bracketed by two events, no per-kernel events inside
-    ev = HipEvents(2)
-    torch.cuda.synchronize()
-    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
-    wall0 = time.perf_counter()
-    for _ in range(args.steps):
-        plan.fwd()
-        plan.bwd()
-    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = ev.elapsed_ms(0, 1)
-    ev.close()
-    # per-kernel breakdown: the same K steps again, each kernel between events
-    ev = HipEvents(2 * nk * args.steps)
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        lib.gdn_set_kernel_events(ev.ptr(2 * nk * s), 2 * nk)
-        plan.fwd()
-        plan.bwd()
-    torch.cuda.synchronize()
-    lib.gdn_set_kernel_events(None, 0)
-    per_kernel = {k: 0.0 for k in kernels}
-    for s in range(args.steps):
-        for i, k in enumerate(kernels):
-            per_kernel[k] += ev.elapsed_ms(2 * nk * s + 2 * i, 2 * nk * s + 2 * i + 1)
-    ev.close()
-    per_kernel = {k: v / args.steps for k, v in per_kernel.items()}
-    ms = total_ms / args.steps
+    flush = Flush(torch)
+    case, t, plan, run = train_plan(torch, binding, inputs, T, algo)
+    m = measure(torch, lib, plan.stream, run, kernels, args.steps, args.warmup, flush)
+    del plan
+    ms = m["step"]["median"]
+    per_kernel = {k: v["median"] for k, v in m["kernels"].items()}
 
     B, Hk, Hv, Dk, Dv = case.B, case.Hk, case.Hv, case.Dk, case.Dv
     tokens = B * T
     value = tokens / (ms / 1e3)
     fb, bb = method_bytes(B, T, Hk, Hv, Dk, Dv, 2)
-    hbm_frac = (fb + bb) / (ms / 1e3) / HBM_PEAK
     E = B * T * Hv * Dk * Dv
     dom = max(per_kernel, key=lambda k: per_kernel[k])
     if family == "chunk":
@@ -254,6 +402,7 @@ def bench_train(args, torch, binding, inputs):
                     "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
                     "frac": round(achieved * 1e12 / FP32_VEC_PEAK, 4), "traffic": None,
                     "flops_per_launch": flops, "avg_launch_ms": round(per_kernel[dom], 4)}
+    copy = copy_bandwidth(torch)
     pages_ms = PAGES_FWD_BWD_MS.get(T)
     out = {
         "metric": METRIC,
@@ -265,6 +414,7 @@ def bench_train(args, torch, binding, inputs):
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
+        # the pages' Metal fwd+bwd at this shape and T (another machine: context)
         "vs_baseline": round(value / (tokens / (pages_ms / 1e3)), 2) if pages_ms else None,
         # chunk form: bf16 matrix-core products with fp32 accumulation and an
         # fp32 state; scan form: fp32 throughout
@@ -273,14 +423,44 @@ def bench_train(args, torch, binding, inputs):
         "config": {"workload": "gated delta rule fwd+bwd, Qwen3.5-9B GDN layer shape",
                    "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
                    "io_dtype": "bf16", "state_dtype": "f32", "algo": family},
+        "timing": {"protocol": "per step: 1 GiB scratch write (cache flush), then HIP events around "
+                               "gdn_fwd + gdn_bwd; value and ms_per_step from the median",
+                   "step_ms": m["step"], "unflushed_mean_ms": m["unflushed_ms"]},
         "roofline": roofline,
         "hbm_roofline_step": {"method_bytes": fb + bb, "achieved_GBps": round(
             (fb + bb) / (ms / 1e3) / 1e9, 1), "peak_GBps": HBM_PEAK / 1e9,
-            "frac": round(hbm_frac, 5)},
+            "frac": round((fb + bb) / (ms / 1e3) / HBM_PEAK, 5),
+            "compulsory_bytes": compulsory_bytes(B, T, Hk, Hv, Dk, Dv, 2),
+            "compulsory_frac": round(compulsory_bytes(B, T, Hk, Hv, Dk, Dv, 2) / (ms / 1e3) / HBM_PEAK, 5),
+            "copy_GBps": copy["GBps"],
+            "frac_of_copy": round((fb + bb) / (ms / 1e3) / 1e9 / copy["GBps"], 5)},
         "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
-        "wall_s_timed": round(wall, 3),
+        "kernels_ms_range": {k: [v["min"], v["max"]] for k, v in m["kernels"].items()},
+        "pages_context": {"metal_fwd_bwd_ms": pages_ms, "hardware": "Apple M4 Max, MLX 0.31.1"}
+        if pages_ms else None,
+        "wall_s_timed": m["wall_s"],
     }
+    if args.config == "9b_t2048" and family == "chunk" and not args.no_sweep:
+        # the pages' performance table runs T = 256 ... 2048 at this shape
+        sweep = {}
+        for Ts in (256, 512, 1024):
+            _, _, p2, r2 = train_plan(torch, binding, inputs, Ts, algo)
+            m2 = measure(torch, lib, p2.stream, r2, [], 20, 5, flush)
+            del p2
+            sweep[str(Ts)] = {"ms": m2["step"]["median"],
+                              "tokens_per_s": round(Ts / (m2["step"]["median"] / 1e3), 1),
+                              "metal_ms": PAGES_FWD_BWD_MS_ALL.get(Ts)}
+        sweep["2048"] = {"ms": round(ms, 5), "tokens_per_s": round(value, 1),
+                         "metal_ms": PAGES_FWD_BWD_MS_ALL.get(2048)}
+        out["t_sweep"] = sweep
     return out
+
+
+def compulsory_bytes(B, T, Hk, Hv, Dk, Dv, io):
+    """method_bytes without the checkpoints: the I/O tensors of fwd and bwd."""
+    fb, bb = method_bytes(B, T, Hk, Hv, Dk, Dv, io)
+    CK = max(math.ceil(T / 64) - 1, 0) * B * Hv * Dk * Dv * 4
+    return fb + bb - 2 * CK
 
 
 def vg_method_bytes(B, T, Hk, Hv, Dk, Dv, io):
@@ -318,66 +498,45 @@ def cpu_baseline_vg(T):
 
 
 def bench_vg(args, torch, binding, inputs):
-    """The 9B layer shape with a per-key-channel gate (scan kernels, fp32
-    arithmetic, bf16 I/O), fwd + bwd per step."""
+    """The 9B layer shape with a per-key-channel gate, fwd + bwd per step
+    (timing protocol as bench_train)."""
     T = {"vg_t2048": 2048, "vg_t256": 256}[args.config]
     case = inputs.vg_qwen35_9b(T)
-    dev = torch.device("cuda:0")
-
-    def up(n):
-        import numpy as np
-        x = case.store(n)
-        if x is None:
-            return None
-        t = torch.from_numpy(np.ascontiguousarray(x))
-        return (t.view(torch.bfloat16) if x.dtype == np.uint16 else t).to(dev)
-
-    t = {n: up(n) for n in ("q", "k", "v", "lg", "b", "state0", "dO", "dS_final")}
+    t = upload_case(torch, case, ("q", "k", "v", "lg", "b", "state0", "dO", "dS_final"))
     t["mask"] = None
-    plan = binding.PlanVg(t)
-    for _ in range(args.warmup):
-        plan.fwd()
-        plan.bwd()
-    torch.cuda.synchronize()
-    kernels = KERNELS["vg"]
-    nk = len(kernels)
+    algo = {"auto": binding.ALGO_AUTO, "scan": binding.ALGO_SCAN,
+            "chunk": binding.ALGO_CHUNK}[args.algo]
+    plan = binding.PlanVg(t, algo=algo)
+    family = plan.family
+    kernels = KERNELS["vg" if family == "scan" else "vg_chunk"]
     lib = binding.lib()
-    sp = ctypes.c_void_p(plan.stream.cuda_stream)
-    ev = HipEvents(2)
-    torch.cuda.synchronize()
-    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[0]), sp)
-    wall0 = time.perf_counter()
-    for _ in range(args.steps):
+
+    def run():
         plan.fwd()
         plan.bwd()
-    ev.hip.hipEventRecord(ctypes.c_void_p(ev.ev[1]), sp)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = ev.elapsed_ms(0, 1)
-    ev.close()
-    ev = HipEvents(2 * nk * args.steps)
-    torch.cuda.synchronize()
-    for s_ in range(args.steps):
-        lib.gdn_set_kernel_events(ev.ptr(2 * nk * s_), 2 * nk)
-        plan.fwd()
-        plan.bwd()
-    torch.cuda.synchronize()
-    lib.gdn_set_kernel_events(None, 0)
-    per_kernel = {k: 0.0 for k in kernels}
-    for s_ in range(args.steps):
-        for i, k in enumerate(kernels):
-            per_kernel[k] += ev.elapsed_ms(2 * nk * s_ + 2 * i, 2 * nk * s_ + 2 * i + 1)
-    ev.close()
-    per_kernel = {k: v / args.steps for k, v in per_kernel.items()}
-    ms = total_ms / args.steps
+    m = measure(torch, lib, plan.stream, run, kernels, args.steps, args.warmup, Flush(torch))
+    ms = m["step"]["median"]
+    per_kernel = {k: v["median"] for k, v in m["kernels"].items()}
     B, Hk, Hv, Dk, Dv = case.B, case.Hk, case.Hv, case.Dk, case.Dv
     tokens = B * T
     value = tokens / (ms / 1e3)
     E = B * T * Hv * Dk * Dv
     dom = max(per_kernel, key=lambda k: per_kernel[k])
-    flops = FLOPS_PER_ELEM.get(dom, 0) * E
-    achieved = flops / (per_kernel[dom] / 1e3) / 1e12
     fb, bb = vg_method_bytes(B, T, Hk, Hv, Dk, Dv, 2)
+    if family == "scan":
+        flops = FLOPS_PER_ELEM.get(dom, 0) * E
+        achieved = flops / (per_kernel[dom] / 1e3) / 1e12
+        roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
+                    "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
+                    "frac": round(achieved * 1e12 / FP32_VEC_PEAK, 4), "traffic": None,
+                    "flops_per_launch": flops, "avg_launch_ms": round(per_kernel[dom], 4)}
+    else:
+        kb = vg_kernel_bytes(B, T, Hk, Hv, Dk, Dv, 2)
+        achieved = kb[dom] / (per_kernel[dom] / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                    "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+                    "bytes_per_launch": kb[dom], "avg_launch_ms": round(per_kernel[dom], 4)}
     return {
         "metric": VG_METRIC,
         "value": round(value, 1),
@@ -389,21 +548,21 @@ def bench_vg(args, torch, binding, inputs):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if family == "scan" else "bf16",
         "data": "synthetic",
         "config": {"workload": "gated delta rule fwd+bwd with a per-key-channel gate, "
                                "Qwen3.5-9B GDN layer shape",
                    "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": Dk, "Dv": Dv,
-                   "io_dtype": "bf16", "state_dtype": "f32", "algo": "scan"},
-        "roofline": {"bound": "alu", "kernel": dom, "achieved": round(achieved, 3),
-                     "peak": FP32_VEC_PEAK / 1e12, "unit": "TFLOP/s",
-                     "frac": round(achieved * 1e12 / FP32_VEC_PEAK, 4), "traffic": None,
-                     "flops_per_launch": flops, "avg_launch_ms": round(per_kernel[dom], 4)},
+                   "io_dtype": "bf16", "state_dtype": "f32", "algo": family},
+        "timing": {"protocol": "per step: 1 GiB scratch write (cache flush), then HIP events around "
+                               "gdn_fwd_vg + gdn_bwd_vg; value and ms_per_step from the median",
+                   "step_ms": m["step"], "unflushed_mean_ms": m["unflushed_ms"]},
+        "roofline": roofline,
         "hbm_roofline_step": {"method_bytes": fb + bb, "achieved_GBps": round(
             (fb + bb) / (ms / 1e3) / 1e9, 1), "peak_GBps": HBM_PEAK / 1e9,
             "frac": round((fb + bb) / (ms / 1e3) / HBM_PEAK, 5)},
         "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": m["wall_s"],
     }
 
 
@@ -562,32 +721,22 @@ def bench_decode(args, torch, binding, inputs):
              P(t["A_log"]), P(t["dt_bias"]), P(state), None, P(o), P(state), None, P(ws), wsb, sp)
             for c, o in zip(calls, outs)]
     lib = binding.lib()
-
-    def step():
-        for a in argl:
-            rc = lib.gdn_fwd(*a)
-            if rc:
-                raise binding.GdnError("gdn_fwd", rc)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    per_call = ms / case.T
+    calls_t = time_calls(torch, lib.gdn_fwd, argl, args.steps, args.warmup, Flush(torch))
+    per_call = calls_t["flushed_call_ms"]["median"]
+    ms = per_call * case.T
     Sig = case.B * case.Hv * case.Dk * case.Dv * 4
     io = case.B * (2 * case.Hk * case.Dk + 2 * case.Hv * case.Dv + 2 * case.Hv) * 2 + 2 * case.Hv * 4
     call_bytes = 2 * Sig + io
     frac = call_bytes / (per_call / 1e3) / HBM_PEAK
     return {
         "metric": "decode tokens/sec, B=64 Hk16/Hv32/Dk128/Dv128, 1 token per call",
-        "value": round(case.B * case.T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "value": round(case.B / (per_call / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "timing": dict(calls_t, protocol="per call: 1 GiB scratch write (cache flush), then HIP "
+                                         "events around the call; value from the median; unflushed: "
+                                         "the steps' calls back to back (the 134 MB state may stay "
+                                         "in the 256 MB memory-side cache)"),
+        "unflushed_frac": round(call_bytes / (calls_t["unflushed_call_ms"] / 1e3) / HBM_PEAK, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "gated delta rule decode, 64 single-token calls per step",
@@ -597,7 +746,7 @@ def bench_decode(args, torch, binding, inputs):
                      "achieved": round(call_bytes / (per_call / 1e3) / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(frac, 4),
                      "traffic": None, "bytes_per_launch": call_bytes,
-                     "avg_call_ms": round(per_call, 5)},
+                     "median_call_ms": round(per_call, 5)},
     }
 
 
@@ -625,24 +774,9 @@ def bench_decode_conv(args, torch, binding, inputs):
              P(t["A_log"]), P(t["dt_bias"]), P(state), None, P(o), P(state), sp)
             for c, o in zip(calls, outs)]
     lib = binding.lib()
-
-    def step():
-        for a in argl:
-            rc = lib.gdn_decode_conv(*a)
-            if rc:
-                raise binding.GdnError("gdn_decode_conv", rc)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    per_call = ms / case.steps
+    calls_t = time_calls(torch, lib.gdn_decode_conv, argl, args.steps, args.warmup, Flush(torch))
+    per_call = calls_t["flushed_call_ms"]["median"]
+    ms = per_call * case.steps
     Sig = case.B * case.Hv * case.Dk * case.Dv * 4
     # state read + written; conv state read + written, x, taps, a, b, o (bf16); A_log, dt_bias
     io = (2 * case.B * case.C * case.K + case.B * case.C + case.C * case.K + 2 * case.B * case.Hv
@@ -651,8 +785,12 @@ def bench_decode_conv(args, torch, binding, inputs):
     frac = call_bytes / (per_call / 1e3) / HBM_PEAK
     return {
         "metric": "decode tokens/sec with the conv update, B=64 Hk16/Hv32/Dk128/Dv128, 4 taps, 1 token per call",
-        "value": round(case.B * case.steps / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "value": round(case.B / (per_call / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "timing": dict(calls_t, protocol="per call: 1 GiB scratch write (cache flush), then HIP "
+                                         "events around the call; value from the median; unflushed: "
+                                         "the steps' calls back to back"),
+        "unflushed_frac": round(call_bytes / (calls_t["unflushed_call_ms"] / 1e3) / HBM_PEAK, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "gated delta rule decode with conv1d + SiLU update, 64 single-token calls per step",
@@ -662,7 +800,7 @@ def bench_decode_conv(args, torch, binding, inputs):
                      "achieved": round(call_bytes / (per_call / 1e3) / 1e9, 1),
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": round(frac, 4),
                      "traffic": None, "bytes_per_launch": call_bytes,
-                     "avg_call_ms": round(per_call, 5)},
+                     "median_call_ms": round(per_call, 5)},
     }
 
 
@@ -683,8 +821,6 @@ def copy_probe(torch, mib):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the first dozen or so steps after start-up run slower (0.438 ms per step
-    # after 3 warmup steps, 0.414-0.418 ms after 30 or more at the 9B shape)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="9b_t2048",
@@ -692,6 +828,8 @@ def main():
                              "long_t32k"])
     ap.add_argument("--algo", default="auto", choices=["auto", "scan", "chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the T = 256, 512, 1024 sweep of the default workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB device to device 3 times "
                          "(the known-size reference for the FETCH_SIZE / WRITE_SIZE counters)")

@@ -365,9 +365,10 @@ class PlanVg:
     """Plan (above) for the per-key-channel-gate form: `t` maps q, k, v, lg,
     b, state0, mask, dO, dS_final to device tensors."""
 
-    def __init__(self, t, stream=None):
+    def __init__(self, t, algo=ALGO_SCAN, stream=None):
         q, v = t["q"], t["v"]
-        self.d = d = _dims_of(q, v, ALGO_SCAN)
+        self.d = d = _dims_of(q, v, algo)
+        self.family = "scan"
         _check_inputs_vg(d, q, t["k"], v, t["lg"], t["b"], t["state0"], t["mask"])
         dev = q.device
         self.t = t

@@ -22,3 +22,14 @@ def test_method_bytes_9b_t2048():
     fb, bb = bench.method_bytes(1, 2048, 16, 64, 192, 128, 2)
     assert abs((fb + bb) / 1e6 - 660.1) < 0.1
     assert abs(fb / 1e6 - 300.4) < 0.1
+
+
+def test_compulsory_bytes_9b_t2048():
+    """Without the checkpoints the 9B layer at T=2048 moves 270.0 MB per step."""
+    assert abs(bench.compulsory_bytes(1, 2048, 16, 64, 192, 128, 2) / 1e6 - 270.0) < 0.1
+
+
+def test_stats_median_min_max():
+    s = bench._stats([3.0, 1.0, 2.0, 10.0])
+    assert s["median"] == 2.5 and s["min"] == 1.0 and s["max"] == 10.0 and s["mean"] == 4.0
+    assert bench._stats([5.0, 1.0, 4.0])["median"] == 4.0
