@@ -149,6 +149,28 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v,
             void* stream);
 
 /*
+ * gdn_fwd for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, results and errors as gdn_fwd without ws / ws_bytes:
+ * the workspace is a static device array inside the library, one copy per GPU,
+ * of GDN_NOALLOC_SCRATCH_BYTES, held until the process ends.  A call whose
+ * workspace (gdn_fwd_workspace_bytes, or the single pass's when state_out ==
+ * state0) exceeds it returns GDN_ERR_WORKSPACE before anything is enqueued.
+ * The call uses the copy of the current device (hipGetDevice), so `stream`
+ * must belong to that device; the first call on a device looks the copy up
+ * (GDN_ERR_HIP if that fails).  Nothing is allocated or freed.  Every call on
+ * one GPU shares that GPU's copy: calls that overlap in time on one GPU (on
+ * different streams, or from different host threads without ordering) race
+ * on it; calls ordered on one stream do not.  Each call writes every
+ * workspace location it reads, so no state carries over between calls.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdn_fwd_noalloc(const gdn_dims* d, const void* q, const void* k, const void* v,
+                    const void* a, const void* b, const float* A_log,
+                    const float* dt_bias, const float* state0, const uint8_t* mask,
+                    void* o, float* state_out, float* ckpt, void* stream);
+
+/*
  * VJP of gdn_fwd (reverse sweep; PR "Design notes": chunk-wise recompute from
  * the checkpoints, deterministic reductions without atomics).
  *   q ... mask    the inputs given to gdn_fwd (same values)

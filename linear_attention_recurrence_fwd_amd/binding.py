@@ -24,7 +24,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-           "gdn_fwd", "gdn_bwd", "gdn_decode_conv", "gdn_fwd_vg_workspace_bytes",
+           "gdn_fwd", "gdn_fwd_noalloc", "gdn_bwd", "gdn_decode_conv", "gdn_fwd_vg_workspace_bytes",
            "gdn_bwd_vg_workspace_bytes", "gdn_fwd_vg", "gdn_bwd_vg", "gdn_set_kernel_events",
            "gdn_status_string", "gdn_version")
 
@@ -60,6 +60,8 @@ def lib():
             getattr(L, n).restype = ctypes.c_int
         L.gdn_fwd.argtypes = [PD] + [P] * 13 + [S, P]
         L.gdn_fwd.restype = ctypes.c_int
+        L.gdn_fwd_noalloc.argtypes = [PD] + [P] * 13
+        L.gdn_fwd_noalloc.restype = ctypes.c_int
         L.gdn_bwd.argtypes = [PD] + [P] * 21 + [S, P]
         L.gdn_bwd.restype = ctypes.c_int
         L.gdn_decode_conv.argtypes = [PD] + [P] * 4 + [ctypes.c_int32] + [P] * 9
@@ -184,6 +186,30 @@ def fwd(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, need_ckpt=True
                        _p(ws), wsb, _stream(dev))
     if rc:
         raise GdnError("gdn_fwd", rc)
+    return o, state_out, ckpt
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES
+
+
+def fwd_noalloc(q, k, v, a, b, A_log, dt_bias, state0=None, mask=None, *, o, state_out, ckpt=None,
+                algo=ALGO_AUTO, save=False):
+    """gdn_fwd_noalloc: the forward with the library's static workspace.  The
+    caller passes every output (o, state_out and, when wanted, ckpt); nothing
+    is allocated here or in the library."""
+    d = _dims_of(q, v, algo, save)
+    _check_inputs(d, q, k, v, a, b, A_log, dt_bias, state0, mask)
+    dev = q.device
+    _check(o, "o", (d.B, d.T, d.Hv, d.Dv), q.dtype, dev)
+    _check(state_out, "state_out", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
+    nck = ckpt_elems(d)
+    if ckpt is not None and ckpt.numel() != nck:
+        raise ValueError("ckpt must have %d elements" % nck)
+    rc = lib().gdn_fwd_noalloc(ctypes.byref(d), _p(q), _p(k), _p(v), _p(a), _p(b), _p(A_log),
+                               _p(dt_bias), _p(state0), _p(mask), _p(o), _p(state_out),
+                               _p(ckpt) if (ckpt is not None and nck) else None, _stream(dev))
+    if rc:
+        raise GdnError("gdn_fwd_noalloc", rc)
     return o, state_out, ckpt
 
 

@@ -5,6 +5,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 namespace {
 
 using gdn::Dims;
@@ -321,25 +323,47 @@ int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out) {
   return GDN_OK;
 }
 
-int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, const void* a,
-            const void* b, const float* A_log, const float* dt_bias, const float* state0,
-            const uint8_t* mask, void* o, float* state_out, float* ckpt, void* ws,
-            size_t ws_bytes, void* stream) {
-  Dims dd;
-  int rc = check_dims(d, &dd);
-  if (rc) return rc;
+}  // extern "C"
+
+namespace {
+
+// The forward's route and workspace layout for these dims and pointers.  An
+// in-place update (state_out == state0) runs the single pass: in the
+// T-parallel output pass the first segment's workgroups read state0 while the
+// last segment's write state_out, with nothing ordering the two.
+struct FwdRoute {
+  bool chunk;
+  int tseg;
+  Layout L;
+};
+FwdRoute fwd_route(const gdn_dims* d, const Dims& dd, const float* state0, const float* state_out) {
+  FwdRoute r{};
+  r.chunk = use_chunk_fwd(d);
+  const bool in_place = state0 != nullptr && state0 == state_out;
+  r.tseg = r.chunk && !in_place ? tpar_seg(d, dd) : 0;
+  r.L = layout(dd, false, r.chunk, use_saved(d), r.tseg);
+  return r;
+}
+
+// Pointer checks of gdn_fwd (after check_dims).
+int check_fwd_ptrs(const gdn_dims* d, const Dims& dd, const void* q, const void* k, const void* v,
+                   const void* a, const void* b, const float* A_log, const float* dt_bias, const void* o,
+                   const float* state_out, const float* ckpt) {
   const bool has_t = dd.T > 0;
   if (!A_log || !dt_bias || !state_out) return GDN_ERR_INVALID_ARG;
   if (has_t && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_INVALID_ARG;
   if (use_saved(d) && !ckpt) return GDN_ERR_INVALID_ARG;  // the matrices are saved there
-  const bool chunk = use_chunk_fwd(d);
-  // An in-place update (state_out == state0) runs the single pass: in the
-  // T-parallel output pass the first segment's workgroups read state0 while
-  // the last segment's write state_out, with nothing ordering the two.
-  const bool in_place = state0 != nullptr && state0 == state_out;
-  const int tseg = chunk && !in_place ? tpar_seg(d, dd) : 0;
-  const Layout L = layout(dd, false, chunk, use_saved(d), tseg);
-  if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+
+// gdn_fwd after validation: enqueues the route's kernels with the workspace ws.
+int fwd_launch(const gdn_dims* d, const Dims& dd, const FwdRoute& R, const void* q, const void* k,
+               const void* v, const void* a, const void* b, const float* A_log, const float* dt_bias,
+               const float* state0, const uint8_t* mask, void* o, float* state_out, float* ckpt,
+               void* ws, void* stream) {
+  const bool chunk = R.chunk;
+  const int tseg = R.tseg;
+  const Layout& L = R.L;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const gdn::StepScalars s = scalars(ws, L);
@@ -384,6 +408,76 @@ int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
   gdn::ScanFwdArgs fa{dd, q, k, v, state0, s, o, state_out, ckpt};
   if (!launch(st, [&] { return gdn::launch_scan_fwd(fa, bf, st); })) return GDN_ERR_HIP;
   return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_fwd(const gdn_dims* d, const void* q, const void* k, const void* v, const void* a,
+            const void* b, const float* A_log, const float* dt_bias, const float* state0,
+            const uint8_t* mask, void* o, float* state_out, float* ckpt, void* ws,
+            size_t ws_bytes, void* stream) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  rc = check_fwd_ptrs(d, dd, q, k, v, a, b, A_log, dt_bias, o, state_out, ckpt);
+  if (rc) return rc;
+  const FwdRoute R = fwd_route(d, dd, state0, state_out);
+  if (R.L.total > ws_bytes || (R.L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
+  return fwd_launch(d, dd, R, q, k, v, a, b, A_log, dt_bias, state0, mask, o, state_out, ckpt, ws, stream);
+}
+
+}  // extern "C"
+
+// ---- the forward without a workspace argument (gdn_fwd_noalloc)
+//
+// Its workspace is this file-scope device array, one copy per GPU (held until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device, taken once per device on the first call.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// This device's copy of `scratch` (the current device's), or null if HIP
+// cannot name it.
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_fwd_noalloc(const gdn_dims* d, const void* q, const void* k, const void* v, const void* a,
+                    const void* b, const float* A_log, const float* dt_bias, const float* state0,
+                    const uint8_t* mask, void* o, float* state_out, float* ckpt, void* stream) {
+  Dims dd;
+  int rc = check_dims(d, &dd);
+  if (rc) return rc;
+  rc = check_fwd_ptrs(d, dd, q, k, v, a, b, A_log, dt_bias, o, state_out, ckpt);
+  if (rc) return rc;
+  const FwdRoute R = fwd_route(d, dd, state0, state_out);
+  if (R.L.total > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (R.L.total > 0) {
+    ws = scratch_of_current_device();
+    if (!ws) return GDN_ERR_HIP;
+  }
+  return fwd_launch(d, dd, R, q, k, v, a, b, A_log, dt_bias, state0, mask, o, state_out, ckpt, ws, stream);
 }
 
 int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, const void* a,
