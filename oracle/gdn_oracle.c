@@ -15,10 +15,11 @@
  *   For batch b and value head h, the key/query head is j = h / G with
  *   G = Hv / Hk (the op contract's GQA rule: value head h reads q/k head h//G).
  *   q and k are L2-normalised with eps 1e-6 inside the square root, and q is
- *   then scaled by 1/sqrt(Dk) (op contract: "L2-normalizes q/k (eps 1e-6) and
- *   scales q by 1/sqrt(w)").
- *   Gates: x = a + dt_bias, x_c = min(x, 20) (the PR's "softplus-argument
- *   clamp", upper bound only), l = -exp(A_log) * softplus(x_c), g = exp(l),
+ *   then scaled by 1/sqrt(Dk) (the op contract normalises q and k with an
+ *   eps of 1e-6 and scales q by one over the square root of the key width).
+ *   Gates: x = a + dt_bias, x_c = min(x, 20) (the PR clamps the argument of
+ *   the softplus without giving bounds; read: upper bound only),
+ *   l = -exp(A_log) * softplus(x_c), g = exp(l),
  *   beta = sigmoid(b).
  *   Step (valid step):  S' = g*S;  u = S'^T k;  delta = beta*(v - u);
  *                       S  = S' + k delta^T;  o = S^T q.

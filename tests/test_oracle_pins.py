@@ -50,7 +50,7 @@ def test_gate_constants():
 
 
 def test_softplus_clamp_upper_20():
-    """The PR's "softplus-argument clamp": the argument is capped at 20 (read
+    """The PR's clamp of the softplus argument: the argument is capped at 20 (read
     as an upper bound only).  Values at and above 20 give the same gate."""
     g20 = oracle.gates(20.0, 0.0, 0.0, 0.0)
     assert oracle.gates(25.0, 0.0, 0.0, 0.0) == g20
