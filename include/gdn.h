@@ -20,7 +20,8 @@
  *  - All tensor pointers are DEVICE pointers to dense row-major tensors with
  *    the layouts given below.  The caller owns all memory: the library never
  *    allocates or frees device memory and keeps no state between calls
- *    (apart from the optional timing events of gdn_set_kernel_events).
+ *    (apart from the optional timing events of gdn_set_kernel_events, kept
+ *    per host thread, and the static workspace array of gdn_fwd_noalloc).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream): they validate, enqueue kernels and return.  No host sync.
  *  - All arguments are validated before anything is enqueued; on a non-zero
@@ -117,12 +118,16 @@ typedef struct gdn_dims {
  * elements.  It holds no fp32 states; such a checkpoint is read only by a
  * gdn_bwd with the same dims (including save). */
 int gdn_ckpt_elems(const gdn_dims* d, size_t* out);
+/* The same in bytes (gdn_ckpt_elems * 4). */
+int gdn_ckpt_bytes(const gdn_dims* d, size_t* out);
 
 /* Device workspace bytes needed by gdn_fwd / gdn_bwd for these dims (less
  * with d->save set, which moves the chunk matrices and the bf16 states into
  * the checkpoint buffer). */
 int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out);
 int gdn_bwd_workspace_bytes(const gdn_dims* d, size_t* out);
+/* Either of the two: for_bwd = 0 the forward's, nonzero the backward's. */
+int gdn_workspace_bytes(const gdn_dims* d, int for_bwd, size_t* out);
 
 /*
  * Forward scan.
@@ -267,8 +272,10 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
  * just before it and events[2i+1] just after it, for as long as 2i+1 < n;
  * later kernels are not timed.  Each call of this function restarts the count
  * at i = 0.  events are hipEvent_t handles created (and destroyed) by the
- * caller.  NULL turns timing off.  The setting is process-wide and not
- * thread-safe.  Returns GDN_ERR_INVALID_ARG if events is non-NULL and n < 2.
+ * caller.  NULL turns timing off.  The setting belongs to the calling host
+ * thread: it applies to the gdn_fwd / gdn_bwd calls that thread makes, and
+ * other threads are not affected.  Returns GDN_ERR_INVALID_ARG if events is
+ * non-NULL and n < 2.
  */
 int gdn_set_kernel_events(void* const* events, int n);
 

@@ -23,7 +23,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
           3: "GDN_ERR_WORKSPACE", 4: "GDN_ERR_HIP"}
 
 # every entry point declared in include/gdn.h
-EXPORTS = ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
+EXPORTS = ("gdn_ckpt_elems", "gdn_ckpt_bytes", "gdn_workspace_bytes", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
            "gdn_fwd", "gdn_fwd_noalloc", "gdn_bwd", "gdn_decode_conv", "gdn_fwd_vg_workspace_bytes",
            "gdn_bwd_vg_workspace_bytes", "gdn_fwd_vg", "gdn_bwd_vg", "gdn_set_kernel_events",
            "gdn_status_string", "gdn_version")
@@ -58,6 +58,10 @@ def lib():
                   "gdn_fwd_vg_workspace_bytes", "gdn_bwd_vg_workspace_bytes"):
             getattr(L, n).argtypes = [PD, ctypes.POINTER(S)]
             getattr(L, n).restype = ctypes.c_int
+        L.gdn_ckpt_bytes.argtypes = [PD, ctypes.POINTER(S)]
+        L.gdn_ckpt_bytes.restype = ctypes.c_int
+        L.gdn_workspace_bytes.argtypes = [PD, ctypes.c_int, ctypes.POINTER(S)]
+        L.gdn_workspace_bytes.restype = ctypes.c_int
         L.gdn_fwd.argtypes = [PD] + [P] * 13 + [S, P]
         L.gdn_fwd.restype = ctypes.c_int
         L.gdn_fwd_noalloc.argtypes = [PD] + [P] * 13

@@ -169,12 +169,14 @@ int check_dims(const gdn_dims* p, Dims* out) {
   return GDN_OK;
 }
 
-// Per-kernel timing events (gdn_set_kernel_events).
+// Per-kernel timing events (gdn_set_kernel_events), per host thread: a
+// thread's setting applies to the calls that thread makes.
 struct Timing {
   void* const* ev = nullptr;
   int n = 0;
   int next = 0;
-} g_timing;
+};
+thread_local Timing g_timing;
 
 // Launches one kernel through `fn`, bracketed by the timing events if set.
 template <typename F>
@@ -303,6 +305,18 @@ int gdn_ckpt_elems(const gdn_dims* d, size_t* out) {
   if (!out) return GDN_ERR_INVALID_ARG;
   *out = use_saved(d) ? saved_layout(dd).total : ckpt_state_elems(dd);
   return GDN_OK;
+}
+
+int gdn_ckpt_bytes(const gdn_dims* d, size_t* out) {
+  size_t n = 0;
+  const int rc = gdn_ckpt_elems(d, &n);
+  if (rc) return rc;
+  *out = n * sizeof(float);
+  return GDN_OK;
+}
+
+int gdn_workspace_bytes(const gdn_dims* d, int for_bwd, size_t* out) {
+  return for_bwd ? gdn_bwd_workspace_bytes(d, out) : gdn_fwd_workspace_bytes(d, out);
 }
 
 int gdn_fwd_workspace_bytes(const gdn_dims* d, size_t* out) {

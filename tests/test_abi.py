@@ -287,3 +287,22 @@ def test_in_place_forward_takes_the_single_pass():
     assert lib.gdn_fwd(ctypes.byref(dt), *args, single - 1, None) == 3
     args = list(p)  # not in place: the T-parallel route needs its larger workspace
     assert lib.gdn_fwd(ctypes.byref(dt), *args, single, None) == 3
+
+
+def test_byte_and_combined_size_queries():
+    """gdn_ckpt_bytes = 4 * gdn_ckpt_elems; gdn_workspace_bytes(d, for_bwd)
+    is the forward's or the backward's workspace query."""
+    lib = B.lib()
+    out = ctypes.c_size_t(0)
+    for dims in [(1, 2048, 16, 64, 192, 128, B.GDN_BF16), (4, 65, 4, 8, 64, 32, B.GDN_F32)]:
+        for save in (False, True):
+            d = B.make_dims(*dims, save=save)
+            assert lib.gdn_ckpt_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
+            assert out.value == 4 * B.ckpt_elems(d)
+            assert lib.gdn_workspace_bytes(ctypes.byref(d), 0, ctypes.byref(out)) == 0
+            assert out.value == B.fwd_workspace_bytes(d)
+            assert lib.gdn_workspace_bytes(ctypes.byref(d), 1, ctypes.byref(out)) == 0
+            assert out.value == B.bwd_workspace_bytes(d)
+    bad = B.make_dims(1, 8, 3, 4, 16, 8, B.GDN_F32)
+    assert lib.gdn_ckpt_bytes(ctypes.byref(bad), ctypes.byref(out)) == 1
+    assert lib.gdn_workspace_bytes(ctypes.byref(bad), 1, ctypes.byref(out)) == 1
