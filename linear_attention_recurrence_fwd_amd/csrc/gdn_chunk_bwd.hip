@@ -172,18 +172,19 @@ struct ChunkBwdState {
   }
 
   // dv / eps rows of this wave: a transpose inside each quad of lanes gives
-  // every lane 4 consecutive columns of one step; steps past the end of the
-  // sequence fall outside the descriptor and are dropped.
+  // every lane 4 consecutive columns of one step, and a lane move puts one
+  // step's 4 column groups in each quad (coalesced stores); steps past the end
+  // of the sequence fall outside the descriptor and are dropped.
   __device__ static void store_rows(const ChunkBwdArgs& p, const Lane& q, void* dst, int t0, int Lc,
                                     const f32x4 (&x)[2], float sign) {
     const Dims& d = p.d;
     const rsrc_t r = make_rsrc(static_cast<bf16*>(dst) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv,
                                q.mode == 0 ? (static_cast<size_t>(Lc - 1) * q.v_row + d.Dv) * 2 : 0);
-    const uint32_t o = 2 * (static_cast<uint32_t>(q.tc0 + (q.lr & 3)) * q.v_row + q.col0 + (q.lr & ~3));
+    const uint32_t o = 2 * (static_cast<uint32_t>(q.tc0 + (q.lr >> 2)) * q.v_row + q.col0 + 4 * (q.lr & 3));
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const f32x4 tr = quad_transpose(x[ct]);
-      buf_store_u2(r, o + 32 * ct, pack4_bf16(sign * tr[0], sign * tr[1], sign * tr[2], sign * tr[3]));
+      buf_store_u2(r, o + 32 * ct, quads_to_rows(pack4_bf16(sign * tr[0], sign * tr[1], sign * tr[2], sign * tr[3])));
     }
   }
 
@@ -282,7 +283,8 @@ struct ChunkBwdState {
     const Slot& s = sm.ring[c & 1];
     // dH' of this chunk for the gradient pass: [i][v], bf16, the layout of the
     // checkpoints; a transpose inside each quad of lanes gives every lane 4
-    // consecutive columns of one row.  Packed now, stored after barrier Z:
+    // consecutive columns of one row, and quads_to_rows one row per quad
+    // (coalesced stores).  Packed now, stored after barrier Z:
     // stores issued here would wait behind group A's ring loads and hold up
     // the products below.
     uint2 dhp[RTW][2];
@@ -323,14 +325,14 @@ struct ChunkBwdState {
     load_b(p, q, cn, nxt);  // the next chunk's Q^T, issued while waiting for Ehat
     lds_barrier();  // Z: Ehat complete
     {  // map mode: an empty descriptor, nothing stored
-      const int e = lr & 3;
       const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv,
                                    q.mode == 0 ? static_cast<size_t>(DK) * d.Dv * 2 : 0);
-      const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + e) * d.Dv + q.col0 + (lr & ~3));
+      const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + (lr >> 2)) * d.Dv + q.col0 + 4 * (lr & 3));
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) buf_store_u2(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), dhp[it][ct]);
+        for (int ct = 0; ct < 2; ++ct)
+          buf_store_u2(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), quads_to_rows(dhp[it][ct]));
     }
     // dH -= K^T diag(e^g rk) Ehat, K^T read transposed from the ring's k tile
 #pragma unroll

@@ -532,14 +532,18 @@ struct ChunkFwd {
     lds_barrier();  // 3: H of the next chunk complete; slot c + 1 complete
   }
 
-  // Group B, one chunk: H update and checkpoint.  The K^T operand comes from
-  // the ring's k tile through transposing LDS reads: for row tile it and
-  // steps 32 kt + 8 lg .. + 7, lane (lr, lg) gets column i = 16 (w RTW + it) + lr.
+  // Group B, one chunk: H update.  The K^T operand comes from the ring's k
+  // tile through transposing LDS reads: for row tile it and steps
+  // 32 kt + 8 lg .. + 7, lane (lr, lg) gets column i = 16 (w RTW + it) + lr.
+  // The stores of the previous chunk's results -- its X and the state at
+  // this chunk's start (checkpoint and / or bf16 copy) -- are issued in
+  // phase 1, where B waits for group A anyway: issued right after the update
+  // they stall behind the memory pipeline and hold up barrier 3.
   __device__ static void step_b(const ChunkFwdArgs& p, Smem& sm, const Lane& q, int c, f32x4 (&H)[RTW][2]) {
-    const Dims& d = p.d;
     const int lr = q.lr, lg = q.lg;
     const Slot& s = sm.ring[c % NSL];
     store_x(p, sm, q, c - 1, c > q.cs);  // group A rewrites X^T after barrier 1
+    store_states(p, q, H, c - 1, c > q.cs);
     lds_barrier();  // 1
     lds_barrier();  // 2: X complete
     const float egl = s.sc[SC_EGL * L];
@@ -570,10 +574,16 @@ struct ChunkFwd {
         for (int ct = 0; ct < 2; ++ct) H[it][ct] = mfma16(kta[it][kt], bx[ct], H[it][ct]);
     }
     put_h(sm, q, H);
-    // the state at chunk c+1's start: the fp32 checkpoint and / or its bf16
-    // copy.  The stores are unconditional within each kind; without a slot
-    // (last chunk) the descriptor is empty and they are dropped.
-    const bool slot = c + 1 < q.NC;
+    lds_barrier();  // 3: H of the next chunk complete
+  }
+  // The state at the end of chunk c (= the start of chunk c + 1): the fp32
+  // checkpoint and / or its bf16 copy.  The stores are unconditional within
+  // each kind; without a slot (the sequence's last chunk, or `on` false) the
+  // descriptor is empty and they are dropped.
+  __device__ static void store_states(const ChunkFwdArgs& p, const Lane& q, const f32x4 (&H)[RTW][2], int c, bool on) {
+    const Dims& d = p.d;
+    const int lr = q.lr, lg = q.lg;
+    const bool slot = on && c + 1 < q.NC;
     if (p.ckpt != nullptr) {
       const size_t hsz = static_cast<size_t>(DK) * d.Dv;
       const rsrc_t rck = make_rsrc(slot ? static_cast<const void*>(p.ckpt + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * hsz)
@@ -590,13 +600,13 @@ struct ChunkFwd {
         }
     }
     if (p.cb.Hb != nullptr) store_hb(p, q, H, slot ? c + 1 : -1);
-    lds_barrier();  // 3: H of the next chunk complete
   }
 
   // X of chunk c for the backward (bf16 [B, T, Hv, Dv]; dropped when cb.X is
   // null or `on` is false), from X^T in LDS while group B waits for A: a
-  // transposing read gives the lane four consecutive columns of step
-  // 16 w + lr, stored with one 8-byte non-temporal store.  Steps past the end
+  // transposing read gives lane 16 g + s four consecutive columns (group g)
+  // of step 16 w + s, and groups_to_quads puts one step's four groups in each
+  // quad of lanes, stored with 8-byte non-temporal stores.  Steps past the end
   // of the sequence fall outside the descriptor.  Group B issues no global
   // loads in its loop, so these stores hold up no wait for a load.
   __device__ static void store_x(const ChunkFwdArgs& p, const Smem& sm, const Lane& q, int c, bool on) {
@@ -606,30 +616,31 @@ struct ChunkFwd {
     const size_t base = ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv + q.col0;
     const rsrc_t r = make_rsrc(on ? static_cast<const void*>(p.cb.X + base) : p.v,
                                on ? (static_cast<size_t>(Lc - 1) * q.v_row + NV) * 2 : 0);
-    const uint32_t to = 2 * static_cast<uint32_t>(q.ta) * q.v_row;
+    const uint32_t to = 2 * static_cast<uint32_t>(16 * q.w + (q.l >> 2)) * q.v_row;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int v0 = 4 * (4 * n + q.lg);
       const uint2 x4 = lds_read_tr16(&sm.xb[(v0 + (q.lr >> 2)) * XS + 16 * q.w + 4 * (q.lr & 3)]);
-      buf_store_u2_nt(r, to + 2 * v0, x4);
+      buf_store_u2_nt(r, to + 2 * 4 * (4 * n + (q.l & 3)), groups_to_quads(x4));
     }
   }
 
   // bf16 copy of H as the state at the start of chunk `slot` ([i][v] rows;
   // dropped when slot < 0).  A quad transpose gives each lane four
-  // consecutive columns of one row: one 8-byte store per tile.
+  // consecutive columns of one row, quads_to_rows one row per quad of lanes:
+  // one coalesced 8-byte store per tile.
   __device__ static void store_hb(const ChunkFwdArgs& p, const Lane& q, const f32x4 (&H)[RTW][2], int slot) {
     const Dims& d = p.d;
     const size_t hsz = static_cast<size_t>(DK) * d.Dv;
     const rsrc_t r = make_rsrc(p.cb.Hb + (static_cast<size_t>(max(slot, 0)) * d.B * d.Hv + q.bh) * hsz,
                                slot >= 0 ? hsz * 2 : 0);
-    const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * q.lg + (q.lr & 3)) * d.Dv + q.col0 + (q.lr & ~3));
+    const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * q.lg + (q.lr >> 2)) * d.Dv + q.col0 + 4 * (q.lr & 3));
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const f32x4 tr = quad_transpose(H[it][ct]);
-        buf_store_u2(r, o + 2 * (16 * it * d.Dv + 16 * ct), pack4_bf16(tr[0], tr[1], tr[2], tr[3]));
+        buf_store_u2(r, o + 2 * (16 * it * d.Dv + 16 * ct), quads_to_rows(pack4_bf16(tr[0], tr[1], tr[2], tr[3])));
       }
   }
 
@@ -665,9 +676,12 @@ struct ChunkFwd {
     {  // rows past the end of the sequence fall outside the descriptor: dropped
       const rsrc_t ro = make_rsrc(static_cast<bf16*>(p.o) + ((static_cast<size_t>(q.b) * d.T + t0) * d.Hv + q.h) * d.Dv,
                                   (static_cast<size_t>(Lc - 1) * q.v_row + d.Dv) * 2);
-      const uint32_t oo = 2 * (static_cast<uint32_t>(q.ta) * q.v_row + q.col0 + 4 * lg);
+      // lane 16 lg + lr holds step 16 w + lr, columns 16 ct + 4 lg .. + 3;
+      // groups_to_quads gives each quad of lanes one step's four groups
+      const uint32_t oo = 2 * (static_cast<uint32_t>(16 * q.w + (q.l >> 2)) * q.v_row + q.col0 + 4 * (q.l & 3));
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) buf_store_u2(ro, oo + 32 * ct, pack4_bf16(o[ct][0], o[ct][1], o[ct][2], o[ct][3]));
+      for (int ct = 0; ct < 2; ++ct)
+        buf_store_u2(ro, oo + 32 * ct, groups_to_quads(pack4_bf16(o[ct][0], o[ct][1], o[ct][2], o[ct][3])));
     }
     lds_barrier();  // 3
   }
@@ -712,6 +726,7 @@ struct ChunkFwd {
     if (p.cb.Hb != nullptr && q.seg == 0) store_hb(p, q, H, 0);
     lds_barrier();  // 0
     for (int c = q.cs; c < q.ce; ++c) step_b(p, sm, q, c, H);
+    store_states(p, q, H, q.ce - 1, true);  // the last chunk's end: the next segment's start
     store_x(p, sm, q, q.ce - 1, true);  // the last chunk's X (X^T is no longer rewritten)
     if (q.mode == 0 && q.ce < q.NC) return;  // not the last segment: no final state
     const int ostride = q.mode == 0 ? d.Dv : DK + d.Dv;

@@ -204,6 +204,30 @@ __device__ __forceinline__ f32x4 quad_transpose(const f32x4& x) {
   }
   return z;
 }
+// Lane moves that make 8-byte stores coalesce: the memory pipeline handles a
+// quad of lanes at a time, so four consecutive lanes should write one row's
+// 32 contiguous bytes rather than four rows.  Both are ds_bpermute pairs (no
+// LDS memory is used).
+__device__ __forceinline__ uint2 bpermute_u2(int src_lane, uint2 v) {
+  return make_uint2(static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * src_lane, static_cast<int>(v.x))),
+                    static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * src_lane, static_cast<int>(v.y))));
+}
+// Within each group of 16 lanes, lane 4 a + b takes the value of lane 4 b + a.
+// After quad_transpose of an accumulator tile, lane 4 a + b of group g holds
+// row 4 g + b, columns 4 a .. 4 a + 3; after this move it holds row
+// 4 g + a, columns 4 b .. 4 b + 3.
+__device__ __forceinline__ uint2 quads_to_rows(uint2 v) {
+  const int l = threadIdx.x & 63;
+  return bpermute_u2((l & 48) + 4 * (l & 3) + ((l >> 2) & 3), v);
+}
+// Lane l takes the value of lane 16 (l % 4) + l / 4.  When lane 16 g + s holds
+// row s, 4-column group g (a transposing LDS read, or an accumulator tile's
+// column s), lane 4 s + g afterwards holds row s, 4-column group g.
+__device__ __forceinline__ uint2 groups_to_quads(uint2 v) {
+  const int l = threadIdx.x & 63;
+  return bpermute_u2(16 * (l & 3) + (l >> 2), v);
+}
+
 // Sum over the 4 lanes of a DPP quad; every lane of the quad gets the same bits.
 __device__ __forceinline__ float quad_sum(float v) {
   v += dpp<kQuadXor1>(v);
