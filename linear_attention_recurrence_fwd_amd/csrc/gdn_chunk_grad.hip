@@ -99,20 +99,23 @@ struct ChunkGrad {
     const T* kg = static_cast<const T*>(p.k);
     auto qk_row = [&](int t) { return (static_cast<size_t>(b) * d.T + t0 + t) * d.Hk + j; };
 
-    // ---- the thread's own rows of kn / qn, and the Gram matrices of the chunk
-    float kown[4][TI], qown[4][TI];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    // The thread's own TI columns of kn / qn in row 4 tr + a (0 past the end),
+    // read where they are used (after each head and in the normalisation
+    // backward) rather than held in registers across the kernel, where the
+    // accumulators of the key-head group already fill the register file.  The
+    // row index passes through an empty asm statement so that the compiler
+    // cannot prove two reloads equal and keep the values live in between.
+    auto own = [&](const T* src, const float* scale, int a, float (&out)[TI]) {
       const int t = tr * 4 + a;
       const bool in = t < Lc;
-      const size_t row = in ? qk_row(t) : 0;
-      const float rk = in ? p.s.rk[row] : 0.f, rq = in ? p.s.rq[row] : 0.f;
+      int ri = in ? static_cast<int>(qk_row(t)) : 0;
+      asm volatile("" : "+v"(ri));
+      const size_t row = static_cast<size_t>(ri);
+      const float sc = in ? scale[row] : 0.f;
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        kown[a][i] = in ? to_f32(kg[row * DK + tc * TI + i]) * rk : 0.f;
-        qown[a][i] = in ? to_f32(qg[row * DK + tc * TI + i]) * rq : 0.f;
-      }
-    }
+      for (int i = 0; i < TI; ++i) out[i] = to_f32(src[row * DK + tc * TI + i]) * sc;
+    };
+    // ---- the Gram matrices of the chunk
     float gqk[4][4], gkk[4][4];  // qn_r . kn_s, kn_r . kn_s for r = 4tr+a, s = 4tc+s
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -280,10 +283,13 @@ struct ChunkGrad {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         float pa = 0.f, pb = 0.f;
+        float kown[TI], qown[TI];
+        own(kg, p.s.rk, a, kown);
+        own(qg, p.s.rq, a, qown);
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-          pa = fmaf(kown[a][i], accKA[a][i], pa);
-          pb = fmaf(qown[a][i], accQh[a][i], fmaf(kown[a][i], accKE[a][i], pb));
+          pa = fmaf(kown[i], accKA[a][i], pa);
+          pb = fmaf(qown[i], accQh[a][i], fmaf(kown[i], accKE[a][i], pb));
           accQ[a][i] += accQh[a][i];
           accK[a][i] += accKA[a][i] + accKE[a][i];
         }
@@ -446,10 +452,13 @@ struct ChunkGrad {
     for (int a = 0; a < 4; ++a) {
       const int t = tr * 4 + a;
       float dq_dot = 0.f, dk_dot = 0.f;
+      float kown[TI], qown[TI];
+      own(kg, p.s.rk, a, kown);
+      own(qg, p.s.rq, a, qown);
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        dq_dot = fmaf(qown[a][i], accQ[a][i], dq_dot);
-        dk_dot = fmaf(kown[a][i], accK[a][i], dk_dot);
+        dq_dot = fmaf(qown[i], accQ[a][i], dq_dot);
+        dk_dot = fmaf(kown[i], accK[a][i], dk_dot);
       }
       dq_dot = row_sum16(dq_dot);
       dk_dot = row_sum16(dk_dot);
@@ -460,8 +469,8 @@ struct ChunkGrad {
         T* dk = static_cast<T*>(p.dk) + row * DK;
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-          dq[tc * TI + i] = from_f32<T>(rq * (accQ[a][i] - dkf * qown[a][i] * dq_dot));
-          dk[tc * TI + i] = from_f32<T>(rk * (accK[a][i] - kown[a][i] * dk_dot));
+          dq[tc * TI + i] = from_f32<T>(rq * (accQ[a][i] - dkf * qown[i] * dq_dot));
+          dk[tc * TI + i] = from_f32<T>(rk * (accK[a][i] - kown[i] * dk_dot));
         }
       }
     }
