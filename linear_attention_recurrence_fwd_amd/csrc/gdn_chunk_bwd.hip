@@ -856,9 +856,11 @@ struct ChunkBwdGrad {
     // workgroup (loading them inside the slab loop would make each wait for
     // them also wait for the next slab's prefetch, issued before them)
     bf16x8 ka[KS], qa[KS];
-    {
-      const int ta = 16 * ((tid0 >> 6) & 3) + (tid0 & 15), lg = (tid0 & 63) >> 4;
-      const uint32_t o = static_cast<uint32_t>(min(ta, x.tl)) * qk_row + 8 * lg;
+    {  // quad-coalesced (lane m reads piece m % 4 of row m / 4: four lanes cover
+       // 64 contiguous bytes); moved to the operand layout below, once the
+       // first slab's prefetch is issued
+      const int l = tid0 & 63, tr0 = 16 * ((tid0 >> 6) & 3) + coal_row(l);
+      const uint32_t o = static_cast<uint32_t>(min(tr0, x.tl)) * qk_row + 8 * coal_piece(l);
 #pragma unroll
       for (int kt = 0; kt < KS; ++kt) {
         ka[kt] = load_bf16x8(kc + o + 32 * kt);
@@ -870,6 +872,11 @@ struct ChunkBwdGrad {
     const int hlast = x.j * G + G - 1;
     Pf pf;
     prefetch(p, x, tid0, x.j * G, 0, pf);
+#pragma unroll
+    for (int kt = 0; kt < KS; ++kt) {
+      ka[kt] = to_mfma_layout(ka[kt]);
+      qa[kt] = to_mfma_layout(qa[kt]);
+    }
     for (int e = tid0; e < L * WR; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
     if (tid0 < L) {
       sm.rk[tid0] = rk0;
