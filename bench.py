@@ -57,29 +57,49 @@ VG_METRIC = "fwd+bwd tokens/sec with a per-key-channel gate at Hk16/Hv64/Dk192/D
 
 
 def kernel_bytes(B, T, Hk, Hv, Dk, Dv, io, state0=False, dS_final=False):
-    """Algorithmic HBM bytes of each chunk-form kernel under gdn_dims.save (the
-    benchmarked path): the I/O tensors each kernel reads or writes, each
-    counted once, and what the forward hands to the backward -- bf16 copies
-    of the state at every chunk start and X = v - u of every step (bf16),
-    written by chunk_fwd and read by chunk_bwd_grad in place of the fp32
-    checkpoints of the method-bytes formula (together they are smaller).
-    Intermediates in the workspace or the checkpoint buffer (chunk matrices,
-    eps, per-chunk state gradients) are not counted."""
+    """Algorithmic HBM bytes of each chunk-form kernel: the tensors of the
+    method-bytes formula (method_bytes) that the kernel reads or writes, each
+    counted once, with the formula's fp32 checkpoints (written by the forward,
+    read by the backward) standing for what the saved path hands from
+    chunk_fwd to chunk_bwd_grad in their place (bf16 chunk-start states and X,
+    which are smaller).  Intermediates in the workspace or the checkpoint
+    buffer (chunk matrices, eps, per-chunk state gradients) are not counted."""
     Q1 = B * T * Hk * Dk * io            # one of q, k (or dq, dk)
     V1 = B * T * Hv * Dv * io            # one of v, o, dO, dv
     A1 = B * T * Hv * io                 # one of a, b, da, db
     Par = 2 * Hv * 4
     Sig = B * Hv * Dk * Dv * 4
-    HB = math.ceil(T / 64) * Sig // 2    # bf16 chunk-start states
-    XB = B * T * Hv * Dv * 2             # X of every step, bf16
+    CK = max(math.ceil(T / 64) - 1, 0) * Sig
     s0 = Sig if state0 else 0
     return {
         "chunk_prep": 2 * Q1 + 2 * A1 + Par,
-        "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + HB + XB,
+        "chunk_fwd": 2 * Q1 + 2 * V1 + s0 + Sig + CK,
         "chunk_bwd_state": Q1 + 2 * V1 + (Sig if dS_final else 0) + Sig,
-        "chunk_bwd_grad": 2 * Q1 + V1 + XB + A1 + HB + 2 * Q1 + 2 * A1,
+        "chunk_bwd_grad": 2 * Q1 + V1 + A1 + CK + 2 * Q1 + 2 * A1,
         "param_reduce": Par,
     }
+
+
+TRACE_FILE = os.path.join(ROOT, "profiles", "chunk_path_9b_t2048_fwd_bwd.txt")
+
+
+def recorded_trace_median(kernel):
+    """Median duration (ms) of `kernel` in the committed rocprofv3 kernel trace
+    of the default workload, or None when there is none or the library source
+    has changed since it was taken."""
+    from linear_attention_recurrence_fwd_amd.srcsha import source_sha
+    try:
+        lines = open(TRACE_FILE).read().splitlines()
+    except OSError:
+        return None
+    sha = next((l.split()[1] for l in lines if l.startswith("source_sha ")), None)
+    if sha != source_sha():
+        return None
+    for l in lines:
+        if "::%s_kernel<" % kernel in l:
+            f = l.split()
+            return float(f[-5]) / 1e3  # the median column (us)
+    return None
 
 
 def method_bytes(B, T, Hk, Hv, Dk, Dv, io, mask=False, dS_final=False):
@@ -393,7 +413,12 @@ def bench_train(args, torch, binding, inputs):
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                     "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": traffic,
-                    "bytes_per_launch": kb[dom], "avg_launch_ms": round(per_kernel[dom], 4)}
+                    "bytes_per_launch": kb[dom], "avg_launch_ms": round(per_kernel[dom], 4),
+                    "launch_ms_timing": "median over the flushed steps, HIP events around the kernel"}
+        tm = recorded_trace_median(dom) if T == 2048 else None
+        if tm:
+            roofline["trace_median_ms"] = round(tm, 4)
+            roofline["trace_frac"] = round(kb[dom] / (tm / 1e3) / HBM_PEAK, 4)
     else:
         # fp32 vector roofline of the slowest kernel, over its algorithmic flops
         flops = FLOPS_PER_ELEM[dom] * E
