@@ -239,12 +239,19 @@ int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const 
  * no formula that produces g, so the caller passes its logarithm directly
  * (as the torch-to-nnef op contract passes a log-decay):
  *   lg        [B,T,Hv,Dk] fp32, lg = log g (finite; -inf is not allowed)
- * Runs the SCAN family only: d->algo AUTO or SCAN (CHUNK gives
- * GDN_ERR_UNSUPPORTED); d->save is ignored.  Sizes and dtypes as gdn_fwd.
- * ckpt has gdn_fwd's SCAN layout (gdn_ckpt_elems with save unset).  The
- * workspace sizes come from the _vg queries; the backward's holds the
- * states every 4 steps of every chunk being swept and per-slice row partials
- * (about B*Hv*Dv*Dk*64 + B*T*Hv*Dv/8*3*Dk floats for Dk >= 64, Dv % 32 == 0).
+ * Kernel families: SCAN (fp32 per-step scan, every size gdn_fwd's scan
+ * takes) and CHUNK (the chunked bf16 matrix-core form, with the decays
+ * e^{G_t - G_s} of the in-chunk cumulative log-gates taken per channel inside
+ * the chunk products: bf16 I/O, Dk 64, 128 or 192, Dv a multiple of 32 up to
+ * 256, the per-(head, chunk) buffers below 4 GiB).  AUTO takes CHUNK where it
+ * is built and T > 1, else SCAN; CHUNK_TPAR gives GDN_ERR_UNSUPPORTED.  The
+ * chunk form is exact (up to rounding) while every in-chunk factor
+ * e^{|G_t - G_s|} stays within fp32 range, which holds for any lg <= 0 (a
+ * decay); for growing gates (lg > 0) use SCAN.  d->save is ignored.  Sizes
+ * and dtypes as gdn_fwd.  ckpt has gdn_fwd's layout without save (the fp32
+ * states at the chunk boundaries, gdn_ckpt_elems with save unset) in both
+ * families, so a forward of either family pairs with a backward of either.
+ * The workspace sizes come from the _vg queries (they depend on the family).
  */
 int gdn_fwd_vg_workspace_bytes(const gdn_dims* d, size_t* out);
 int gdn_bwd_vg_workspace_bytes(const gdn_dims* d, size_t* out);

@@ -339,10 +339,23 @@ def _check_inputs_vg(d, q, k, v, lg, b, state0, mask):
         _check(mask, "mask", (B, T), torch.uint8, dev)
 
 
-def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=None):
-    """Forward scan with a per-key-channel gate: lg [B,T,Hv,Dk] fp32 holds
-    log g, and g scales the state's rows.  Returns (o, state_out, ckpt)."""
-    d = _dims_of(q, v, ALGO_SCAN)
+def vg_uses_chunk(d) -> bool:
+    """Whether gdn_fwd_vg / gdn_bwd_vg run the chunk form for these dims (the
+    library's rule: bf16, Dk 64 / 128 / 192, Dv a multiple of 32 up to 256,
+    under AUTO more than one step, and the chunk buffers within 4 GiB)."""
+    if d.T == 0 or d.algo == ALGO_SCAN:
+        return False
+    ok = (d.dtype == GDN_BF16 and d.Dk in (64, 128, 192) and d.Dv % 32 == 0 and d.Dv <= 256)
+    bhc = d.B * d.Hv * ((d.T + 63) // 64)
+    ok = ok and max(bhc * 64 * d.Dk * 2, bhc * 64 * 64 * 2, bhc * 8 * 64 * 4) < 1 << 32
+    return d.algo == ALGO_CHUNK or (d.T > 1 and ok)
+
+
+def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=None,
+           algo=ALGO_AUTO):
+    """Forward with a per-key-channel gate: lg [B,T,Hv,Dk] fp32 holds log g,
+    and g scales the state's rows.  Returns (o, state_out, ckpt)."""
+    d = _dims_of(q, v, algo)
     _check_inputs_vg(d, q, k, v, lg, b, state0, mask)
     dev = q.device
     o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
@@ -363,9 +376,9 @@ def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=
     return o, state_out, ckpt
 
 
-def bwd_vg(q, k, v, lg, b, state0, mask, ckpt, dO, dS_final=None):
+def bwd_vg(q, k, v, lg, b, state0, mask, ckpt, dO, dS_final=None, *, algo=ALGO_AUTO):
     """VJP of fwd_vg.  Returns dict(dq, dk, dv, dlg, db, dstate)."""
-    d = _dims_of(q, v, ALGO_SCAN)
+    d = _dims_of(q, v, algo)
     _check_inputs_vg(d, q, k, v, lg, b, state0, mask)
     dev = q.device
     _check(dO, "dO", (d.B, d.T, d.Hv, d.Dv), q.dtype, dev)
@@ -395,10 +408,10 @@ class PlanVg:
     """Plan (above) for the per-key-channel-gate form: `t` maps q, k, v, lg,
     b, state0, mask, dO, dS_final to device tensors."""
 
-    def __init__(self, t, algo=ALGO_SCAN, stream=None):
+    def __init__(self, t, algo=ALGO_AUTO, stream=None):
         q, v = t["q"], t["v"]
         self.d = d = _dims_of(q, v, algo)
-        self.family = "scan"
+        self.family = "chunk" if vg_uses_chunk(d) else "scan"
         _check_inputs_vg(d, q, t["k"], v, t["lg"], t["b"], t["state0"], t["mask"])
         dev = q.device
         self.t = t

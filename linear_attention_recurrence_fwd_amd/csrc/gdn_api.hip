@@ -251,13 +251,39 @@ gdn::StepScalars scalars(void* ws, const Layout& L) {
                           at<float>(ws, L.ell), at<float>(ws, L.beta)};
 }
 
-// ---- per-key-channel gate (scan family only)
+// ---- per-key-channel gate
 
 struct VgLayout {
-  size_t rq, rk, kq, beta, sub, part, pdb, total;
+  size_t rq, rk, kq, beta, sub, part, pdb;
+  size_t Kb, Kh, Qb, KbT, QbT, Tx, Mq, AtT, PqT, vsc;  // chunk form
+  size_t E, dHend;                                     // chunk form, backward
+  size_t total;
 };
 
-VgLayout vg_layout(const Dims& d, bool bwd) {
+// The chunk form of the per-key-channel gate addresses its per-(head, chunk)
+// rows and matrices through 32-bit buffer offsets: each must stay below 4 GiB.
+bool vg_chunk_fits(const gdn_dims* p) {
+  const double lim = 4294967296.0;
+  const double nc = static_cast<double>((p->T + 63) / 64);
+  const double bhc = static_cast<double>(p->B) * p->Hv * nc;
+  return bhc * 64.0 * p->Dk * 2.0 < lim && bhc * 64.0 * 64.0 * 2.0 < lim &&
+         bhc * gdn::VSC_ROWS * 64.0 * 4.0 < lim;
+}
+bool vg_chunk_ok(const gdn_dims* p) {
+  return gdn::vg_chunk_supported(static_cast<int>(p->Dk), static_cast<int>(p->Dv), p->dtype == GDN_BF16) &&
+         vg_chunk_fits(p);
+}
+// Kernel family of a per-channel-gate call: the chunk form where asked for,
+// and under AUTO where it is built and there is more than one step.
+// (An empty sequence takes the scan path, which passes the state through.)
+bool use_vg_chunk(const gdn_dims* p) {
+  if (p->T == 0) return false;
+  if (p->algo == GDN_ALGO_CHUNK) return true;
+  if (p->algo == GDN_ALGO_SCAN) return false;
+  return p->T > 1 && vg_chunk_ok(p);
+}
+
+VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
   VgLayout L{};
   size_t off = 0;
   auto take = [&](size_t nfloat) {
@@ -266,6 +292,24 @@ VgLayout vg_layout(const Dims& d, bool bwd) {
     return o;
   };
   const size_t bt = static_cast<size_t>(d.B) * d.T;
+  if (chunk) {
+    const size_t nc = d.nchunk(), bhc = static_cast<size_t>(d.B) * d.Hv * nc;
+    const size_t rows = (bhc * 64 * d.Dk + 1) / 2, mats = (bhc * 64 * 64 + 1) / 2;  // bf16, in floats
+    L.Kh = take(rows);
+    L.Tx = take(mats);
+    L.vsc = take(bhc * gdn::VSC_ROWS * 64);
+    if (!bwd) {
+      L.Kb = take(rows);
+      L.Qb = take(rows);
+      L.Mq = take(mats);
+      L.total = off;
+      return L;
+    }
+    L.KbT = take(rows);
+    L.QbT = take(rows);
+    L.AtT = take(mats);
+    L.PqT = take(mats);
+  }
   L.rq = take(bt * d.Hk);
   L.rk = take(bt * d.Hk);
   L.kq = take(bt * d.Hk);
@@ -285,10 +329,34 @@ gdn::StepScalars vg_scalars(void* ws, const VgLayout& L) {
                           at<float>(ws, L.beta)};
 }
 
+gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd) {
+  gdn::ChunkBufs cb{};
+  cb.Kh = at<gdn::bf16>(ws, L.Kh);
+  cb.Tx = at<gdn::bf16>(ws, L.Tx);
+  cb.vsc = at<float>(ws, L.vsc);
+  if (bwd) {
+    cb.KbT = at<gdn::bf16>(ws, L.KbT);
+    cb.QbT = at<gdn::bf16>(ws, L.QbT);
+    cb.AtT = at<gdn::bf16>(ws, L.AtT);
+    cb.PqT = at<gdn::bf16>(ws, L.PqT);
+  } else {
+    cb.Kb = at<gdn::bf16>(ws, L.Kb);
+    cb.Qb = at<gdn::bf16>(ws, L.Qb);
+    cb.Mq = at<gdn::bf16>(ws, L.Mq);
+  }
+  return cb;
+}
+
 int check_vg(const gdn_dims* p, Dims* out) {
-  int rc = check_dims(p, out);
+  if (p && p->algo == GDN_ALGO_CHUNK_TPAR) return GDN_ERR_UNSUPPORTED;
+  if (p && p->algo == GDN_ALGO_CHUNK && !vg_chunk_ok(p)) return GDN_ERR_UNSUPPORTED;
+  gdn_dims q;
+  if (p) {  // the scalar checks, without the scalar chunk form's own limits
+    q = *p;
+    if (q.algo == GDN_ALGO_CHUNK) q.algo = GDN_ALGO_SCAN;
+  }
+  int rc = check_dims(p ? &q : nullptr, out);
   if (rc) return rc;
-  if (p->algo == GDN_ALGO_CHUNK) return GDN_ERR_UNSUPPORTED;
   if (static_cast<double>(p->B) * p->T * p->Hv * p->Dk > static_cast<double>(INT_MAX))
     return GDN_ERR_UNSUPPORTED;
   return GDN_OK;
@@ -591,7 +659,7 @@ int gdn_fwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_vg(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = vg_layout(dd, false).total;
+  *out = vg_layout(dd, false, use_vg_chunk(d)).total;
   return GDN_OK;
 }
 
@@ -600,7 +668,7 @@ int gdn_bwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_vg(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = vg_layout(dd, true).total;
+  *out = vg_layout(dd, true, false).total;
   return GDN_OK;
 }
 
@@ -612,10 +680,20 @@ int gdn_fwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
   if (rc) return rc;
   if (!state_out) return GDN_ERR_INVALID_ARG;
   if (dd.T > 0 && (!q || !k || !v || !lg || !b || !o)) return GDN_ERR_INVALID_ARG;
-  const VgLayout L = vg_layout(dd, false);
+  const bool chunk = use_vg_chunk(d);
+  const VgLayout L = vg_layout(dd, false, chunk);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (chunk) {
+    const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, false);
+    gdn::VgChunkPrepArgs pa{dd, q, k, b, lg, mask, cb, 0};
+    if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(pa, st); })) return GDN_ERR_HIP;
+    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, ckpt};
+    fa.vg = 1;
+    if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   const gdn::StepScalars s = vg_scalars(ws, L);
   gdn::PrepArgs pa{dd, q, k, nullptr, b, nullptr, nullptr, mask, s};
   if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
@@ -635,7 +713,7 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
   if (dd.T > 0 && (!q || !k || !v || !lg || !b || !dO || !dq || !dk || !dv || !dlg || !db))
     return GDN_ERR_INVALID_ARG;
   if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
-  const VgLayout L = vg_layout(dd, true);
+  const VgLayout L = vg_layout(dd, true, false);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);

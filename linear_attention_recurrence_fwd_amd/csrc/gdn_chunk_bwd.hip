@@ -55,7 +55,7 @@ constexpr int LP = L + 1;
 
 // ------------------------------------------------------- reverse state pass
 
-template <int DK>
+template <int DK, bool VG = false>
 struct ChunkBwdState {
   // Eight waves in two groups of four (w = wave index within the group):
   //   A (waves 0-3): for row tile w of the chunk, the dependent chain
@@ -69,6 +69,10 @@ struct ChunkBwdState {
   //                  Ehat with K^T read transposed from the ring.
   // Three barriers per chunk: Y (rhs ready), Z (Ehat ready), X (dH of the
   // previous chunk ready, next ring slot complete).
+  // With the per-key-channel gate (VG) the operands come pre-scaled from
+  // vg_chunk_prep: the ring's k tile holds Kh (rhs = Kh dH' + P^T dO), B
+  // takes Qb^T and Kb^T from registers (dH = diag(e^{G_L}) dH' + Qb^T dO -
+  // Kb^T Ehat) and decays dH row-wise.
   static constexpr int NTS = 512;
   static constexpr int NV = 32;        // Dv columns per workgroup
   static constexpr int RTW = DK / 64;  // dH row tiles per group-B wave
@@ -77,6 +81,8 @@ struct ChunkBwdState {
   static constexpr int NPK = DK / 8;   // 16-byte pieces of a k row
   static constexpr int KDMA = DK / 32;
   static constexpr int NDMA = KDMA + 6 + 1 + 2;  // ring loads per group-A wave per chunk
+  static constexpr int SCR = VG ? VSC_ROWS : SC_ROWS;  // chunk scalar rows per chunk
+  static_assert(!VG || DK <= 4 * L, "e^{G_L} of every channel in rows 1 .. 4 of the slot");
   // A ring slot (layouts as in the forward state pass: 16-byte piece p of row
   // t at t * (pieces per row) + (p ^ swizzle(t))).
   struct Slot {
@@ -98,7 +104,8 @@ struct ChunkBwdState {
   // Group B's Q^T operand of one chunk, in registers (quad-coalesced loads,
   // permuted at use), loaded a chunk ahead from clamped addresses.
   struct StageB {
-    bf16x8 qta[RTW][2];  // Q^T rows i = 16 (w RTW + it) + lr
+    bf16x8 qta[RTW][2];            // Q^T (VG: Qb^T) rows i = 16 (w RTW + it) + lr
+    bf16x8 kta[VG ? RTW : 1][2];   // VG: Kb^T rows i
   };
   struct Lane {
     int b, h, j, bh, bj, col0, w, l, lr, lg, ta, tc0, last, NC;
@@ -106,7 +113,7 @@ struct ChunkBwdState {
     int scol;                    // first state column of the slice (Dk + Dv columns in map mode)
     uint32_t ostep, obase;       // dO elements per step and offset (0, 0: the zero rows)
     uint32_t v_row;
-    rsrc_t rqt;
+    rsrc_t rqt, rkt;
     i32x4 dk, dpt, dtx, dat, ddo, dsc;  // raw descriptors of the ring's operands
   };
 
@@ -122,7 +129,9 @@ struct ChunkBwdState {
 #pragma unroll
     for (int jj = 0; jj < KDMA; ++jj) {
       const int n = KDMA * q.w + jj, pos = 64 * n + l, t = pos / NPK, pc = (pos % NPK) ^ (t & 7);
-      dma16(q.dk, &s.k[512 * n], 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hk + q.j) * DK + 8 * pc));
+      const uint32_t o = VG ? 2 * ((static_cast<uint32_t>(q.bh * q.NC + c) * L + t) * DK + 8 * pc)
+                            : 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hk + q.j) * DK + 8 * pc);
+      dma16(q.dk, &s.k[512 * n], o);
     }
     const uint32_t mat = static_cast<uint32_t>(q.bh * q.NC + c) * L * L;
 #pragma unroll
@@ -138,19 +147,22 @@ struct ChunkBwdState {
       dma16(q.ddo, &s.dO[512 * q.w],
             2 * (static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * q.ostep + q.obase + 8 * pc));
     }
-    const uint32_t so = static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L;
+    const uint32_t so = static_cast<uint32_t>(q.bh * q.NC + c) * SCR * L;
 #pragma unroll
     for (int e = 0; e < 2; ++e) dma4(q.dsc, &s.sc[L * (2 * q.w + e)], 4 * (so + L * (2 * q.w + e) + l));
   }
 
   __device__ static void load_b(const ChunkBwdArgs& p, const Lane& q, int c, StageB& st) {
     (void)p;
-    const uint32_t o = 2 * (static_cast<uint32_t>(q.bj * q.NC + c) * DK * L + (16 * q.w * RTW + coal_row(q.l)) * L +
-                            8 * coal_piece(q.l));
+    const uint32_t o = 2 * (static_cast<uint32_t>((VG ? q.bh : q.bj) * q.NC + c) * DK * L +
+                            (16 * q.w * RTW + coal_row(q.l)) * L + 8 * coal_piece(q.l));
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) st.qta[it][kt] = buf_bf16x8(q.rqt, o + 2 * (it * 16 * L) + 64 * kt);
+      for (int kt = 0; kt < 2; ++kt) {
+        st.qta[it][kt] = buf_bf16x8(q.rqt, o + 2 * (it * 16 * L) + 64 * kt);
+        if constexpr (VG) st.kta[it][kt] = buf_bf16x8(q.rkt, o + 2 * (it * 16 * L) + 64 * kt);
+      }
   }
 
   // The B operand of a product with dO^T over the chunk's steps: steps
@@ -212,9 +224,10 @@ struct ChunkBwdState {
       txa[kt] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       ata[kt] = load_bf16x8(&s.at[xpos(ta, 4 * kt + lg)]);
     }
-    const float4 kl4 = *reinterpret_cast<const float4*>(&s.sc[SC_KL * L + q.tc0]);
-    const float4 bt4 = *reinterpret_cast<const float4*>(&s.sc[SC_BETA * L + q.tc0]);
-    const float4 cr4 = *reinterpret_cast<const float4*>(&s.sc[SC_CR * L + q.tc0]);
+    const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
+    const float4 kl4 = VG ? one4 : *reinterpret_cast<const float4*>(&s.sc[SC_KL * L + q.tc0]);
+    const float4 bt4 = *reinterpret_cast<const float4*>(&s.sc[(VG ? VSC_BETA : SC_BETA) * L + q.tc0]);
+    const float4 cr4 = VG ? one4 : *reinterpret_cast<const float4*>(&s.sc[SC_CR * L + q.tc0]);
     const float klv[4] = {kl4.x, kl4.y, kl4.z, kl4.w};
     const float btv[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
     const float crv[4] = {cr4.x, cr4.y, cr4.z, cr4.w};
@@ -277,7 +290,10 @@ struct ChunkBwdState {
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) cur.qta[it][kt] = to_mfma_layout(cur.qta[it][kt]);
+      for (int kt = 0; kt < 2; ++kt) {
+        cur.qta[it][kt] = to_mfma_layout(cur.qta[it][kt]);
+        if constexpr (VG) cur.kta[it][kt] = to_mfma_layout(cur.kta[it][kt]);
+      }
     const Dims& d = p.d;
     const int lr = q.lr, lg = q.lg;
     const Slot& s = sm.ring[c & 1];
@@ -300,23 +316,35 @@ struct ChunkBwdState {
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int r = 0; r < 4; ++r) {
+        // VG: e^{G_L} of row i = 16 (w RTW + it) + 4 lg + r
+        const float e = VG ? s.sc[VSC_EGL * L + 16 * (q.w * RTW + it) + 4 * lg + r] : egl;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dH[it][ct][r] *= egl;
+        for (int ct = 0; ct < 2; ++ct) dH[it][ct][r] *= e;
+      }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const float4 c0 = *reinterpret_cast<const float4*>(&s.sc[SC_CO * L + 32 * kt + 8 * lg]);
-      const float4 c1 = *reinterpret_cast<const float4*>(&s.sc[SC_CO * L + 32 * kt + 8 * lg + 4]);
-      const float cov[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      float cov[8];
+      if constexpr (!VG) {
+        const float4 c0 = *reinterpret_cast<const float4*>(&s.sc[SC_CO * L + 32 * kt + 8 * lg]);
+        const float4 c1 = *reinterpret_cast<const float4*>(&s.sc[SC_CO * L + 32 * kt + 8 * lg + 4]);
+        cov[0] = c0.x, cov[1] = c0.y, cov[2] = c0.z, cov[3] = c0.w;
+        cov[4] = c1.x, cov[5] = c1.y, cov[6] = c1.z, cov[7] = c1.w;
+      }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const uint4 u = dO_operand(s, q, kt, ct);
-        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-        uint32_t o4[4];
+        bf16x8 bq;
+        if constexpr (VG) {
+          bq = as_bf16x8(u);  // Qb^T already carries e^{G_t} / sqrt(Dk)
+        } else {
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+          uint32_t o4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          o4[i] = pack2_bf16(cov[2 * i] * __uint_as_float(w4[i] << 16), cov[2 * i + 1] * __uint_as_float(w4[i] & 0xffff0000u));
-        const bf16x8 bq = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+          for (int i = 0; i < 4; ++i)
+            o4[i] = pack2_bf16(cov[2 * i] * __uint_as_float(w4[i] << 16), cov[2 * i + 1] * __uint_as_float(w4[i] & 0xffff0000u));
+          bq = as_bf16x8(make_uint4(o4[0], o4[1], o4[2], o4[3]));
+        }
 #pragma unroll
         for (int it = 0; it < RTW; ++it) dH[it][ct] = mfma16(cur.qta[it][kt], bq, dH[it][ct]);
       }
@@ -342,10 +370,15 @@ struct ChunkBwdState {
       for (int ct = 0; ct < 2; ++ct) be[ct] = load_bf16x8(&sm.es[(16 * ct + lr) * XS + 32 * kt + 8 * lg]);
 #pragma unroll
       for (int it = 0; it < RTW; ++it) {
-        const int t = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * (q.w * RTW + it) + ((lr >> 1) & 1);
-        const uint2 lo = lds_read_tr16(&s.k[kpos(t, pc) + 4 * (lr & 1)]);
-        const uint2 hi = lds_read_tr16(&s.k[kpos(t + 4, pc) + 4 * (lr & 1)]);
-        const bf16x8 kta = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        bf16x8 kta;
+        if constexpr (VG) {
+          kta = cur.kta[it][kt];  // Kb^T (es holds -Ehat^T)
+        } else {
+          const int t = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * (q.w * RTW + it) + ((lr >> 1) & 1);
+          const uint2 lo = lds_read_tr16(&s.k[kpos(t, pc) + 4 * (lr & 1)]);
+          const uint2 hi = lds_read_tr16(&s.k[kpos(t + 4, pc) + 4 * (lr & 1)]);
+          kta = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) dH[it][ct] = mfma16(kta, be[ct], dH[it][ct]);
       }
@@ -445,13 +478,19 @@ struct ChunkBwdState {
     q.v_row = d.Hv * d.Dv;
     {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
-      q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
+      q.dk = VG ? raw_desc(p.cb.Kh, nmat * L * DK * 2) : raw_desc(p.k, bt * d.Hk * DK * 2);
       q.ddo = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
       q.dpt = raw_desc(p.cb.PqT, nmat * L * L * 2);
       q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
       q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
-      q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
-      q.rqt = make_rsrc(p.cb.QT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);
+      if constexpr (VG) {
+        q.dsc = raw_desc(p.cb.vsc, nmat * VSC_ROWS * L * 4);
+        q.rqt = make_rsrc(p.cb.QbT, nmat * DK * L * 2);
+        q.rkt = make_rsrc(p.cb.KbT, nmat * DK * L * 2);
+      } else {
+        q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
+        q.rqt = q.rkt = make_rsrc(p.cb.QT, static_cast<size_t>(d.B) * d.Hk * q.NC * DK * L * 2);
+      }
     }
     if (q.ce <= q.cs) return;
     if (tid < 256)
@@ -461,10 +500,10 @@ struct ChunkBwdState {
   }
 };
 
-template <int DK>
+template <int DK, bool VG>
 __global__ void __launch_bounds__(512) chunk_bwd_state_kernel(ChunkBwdArgs p) {
-  __shared__ typename ChunkBwdState<DK>::Smem sm;
-  ChunkBwdState<DK>::run(p, sm);
+  __shared__ typename ChunkBwdState<DK, VG>::Smem sm;
+  ChunkBwdState<DK, VG>::run(p, sm);
 }
 
 // ------------------------------------------------------------ gradient pass
@@ -1231,11 +1270,21 @@ hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
   const int NV = ChunkBwdState<64>::NV;
   const int nseg = a.seg ? (a.d.nchunk() + a.seg - 1) / a.seg : 1;
   const dim3 nblk(a.d.B * a.d.Hv * ((a.map ? a.d.Dk + a.d.Dv : a.d.Dv) / NV), nseg);
+  if (a.vg) {
+    if (a.seg || a.map) return hipErrorInvalidValue;
+    switch (a.d.Dk) {
+      case 64: chunk_bwd_state_kernel<64, true><<<nblk, ChunkBwdState<64, true>::NTS, 0, st>>>(a); break;
+      case 128: chunk_bwd_state_kernel<128, true><<<nblk, ChunkBwdState<128, true>::NTS, 0, st>>>(a); break;
+      case 192: chunk_bwd_state_kernel<192, true><<<nblk, ChunkBwdState<192, true>::NTS, 0, st>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.d.Dk) {
-    case 64: chunk_bwd_state_kernel<64><<<nblk, ChunkBwdState<64>::NTS, 0, st>>>(a); break;
-    case 128: chunk_bwd_state_kernel<128><<<nblk, ChunkBwdState<128>::NTS, 0, st>>>(a); break;
-    case 192: chunk_bwd_state_kernel<192><<<nblk, ChunkBwdState<192>::NTS, 0, st>>>(a); break;
-    case 256: chunk_bwd_state_kernel<256><<<nblk, ChunkBwdState<256>::NTS, 0, st>>>(a); break;
+    case 64: chunk_bwd_state_kernel<64, false><<<nblk, ChunkBwdState<64>::NTS, 0, st>>>(a); break;
+    case 128: chunk_bwd_state_kernel<128, false><<<nblk, ChunkBwdState<128>::NTS, 0, st>>>(a); break;
+    case 192: chunk_bwd_state_kernel<192, false><<<nblk, ChunkBwdState<192>::NTS, 0, st>>>(a); break;
+    case 256: chunk_bwd_state_kernel<256, false><<<nblk, ChunkBwdState<256>::NTS, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -31,8 +31,11 @@
 //               reads hit that XCD's L2.  Writes o, the checkpoints and the
 //               final state, and for the backward's saved record the bf16
 //               chunk-start states and X of every step.
+#include <type_traits>
+
 #include "gdn_dev.h"
 #include "gdn_internal.h"
+#include "gdn_tri.h"
 
 namespace gdn {
 namespace {
@@ -45,7 +48,7 @@ constexpr int NT = 256;
 template <int DK>
 struct ChunkPrep {
   static constexpr int RS = DK + 8;  // bf16 row stride of the staged k / q rows (conflict-free operand reads)
-  static constexpr int SP = L + 4;   // fp32 row stride of N and the staging matrix (16-byte aligned rows)
+  static constexpr int SP = tri::SP;  // fp32 row stride of N and the staging matrix
   static constexpr int NLD = L * DK / 8 / NT;  // 16-byte pieces of one of k, q per thread
   static_assert(L * DK / 8 % NT == 0, "whole pieces per thread");
   struct Rows {
@@ -65,16 +68,7 @@ struct ChunkPrep {
     float gam[L], rk[L], rq[L], beta[L], ell[L];
   };
 
-  // st (fp32 [L][SP]) -> dst (bf16 [L][L]), 8 elements per store.
-  __device__ static void store_mat(const Smem& sm, bf16* dst, int tid) {
-    for (int u = tid; u < L * L / 8; u += NT) {
-      const int r = u >> 3, c8 = 8 * (u & 7);
-      const float4 a = *reinterpret_cast<const float4*>(&sm.u.m.st[r * SP + c8]);
-      const float4 b = *reinterpret_cast<const float4*>(&sm.u.m.st[r * SP + c8 + 4]);
-      *reinterpret_cast<uint4*>(dst + r * L + c8) =
-          make_uint4(pack2_bf16(a.x, a.y), pack2_bf16(a.z, a.w), pack2_bf16(b.x, b.y), pack2_bf16(b.z, b.w));
-    }
-  }
+  __device__ static void store_mat(const Smem& sm, bf16* dst, int tid) { tri::store_mat(sm.u.m.st, dst, tid, NT); }
 
   // Rows [t][i] of the staged chunk -> dst [i][t] (bf16, L steps per row).
   __device__ static void store_transposed(const bf16* rows, bf16* dst, int tid) {
@@ -89,51 +83,9 @@ struct ChunkPrep {
     }
   }
 
-  // Tx = (I + N)^-1 in 16x16 blocks (fp32).  N is strictly lower triangular,
-  // so Tx is unit lower triangular with diagonal blocks D_i = (I + N_ii)^-1
-  // and, for i > j, Tx_ij = -D_i (sum over j <= k < i of N_ik Tx_kj) (the
-  // block rows of (I + N) Tx = I).  Wave w inverts D_w by forward
-  // substitution -- lane 4c + q holds rows 4m + q of column c -- and writes it
-  // over N_ww.
-  __device__ static void invert_diagonal_block(Smem& sm, int w, int l) {
-    const int c = l >> 2, q = l & 3;
-    float* nb = &sm.u.m.nf[16 * w * SP + 16 * w];
-    float x[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      // rows s >= t of x are still zero, and N[t][s] = 0 for s >= t
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < (t + 3) / 4; ++m) acc = fmaf(nb[t * SP + 4 * m + q], x[m], acc);
-      const float xt = (t == c ? 1.f : 0.f) - quad_sum(acc);
-      if ((t & 3) == q) x[t >> 2] = xt;
-    }
-    wave_lds_sync();  // every lane's reads of N_ww are done
-#pragma unroll
-    for (int m = 0; m < 4; ++m) nb[(4 * m + q) * SP + c] = x[m];
-  }
-
-  // Block column j < 3 of Tx below the diagonal, top to bottom, on fp32 MFMA,
-  // into the staging matrix.  The partial sums pass through the (zero, unused)
-  // block (0, j + 1) of nf to become an operand.
-  __device__ static void lower_blocks(Smem& sm, int j) {
-    const int l = threadIdx.x & 63, lr = l & 15, lg = l >> 4;
-    float* nf = sm.u.m.nf;
-    float* st = sm.u.m.st;
-    float* part = &nf[16 * (j + 1)];
-    for (int i = j + 1; i < 4; ++i) {
-      f32x4 acc = f4zero();
-      acc = mm16f(acc, &nf[16 * i * SP + 16 * j], SP, &nf[16 * j * SP + 16 * j], SP);
-      for (int k = j + 1; k < i; ++k) acc = mm16f(acc, &nf[16 * i * SP + 16 * k], SP, &st[16 * k * SP + 16 * j], SP);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[(4 * lg + r) * SP + lr] = acc[r];
-      wave_lds_sync();
-      const f32x4 tij = mm16f(f4zero(), &nf[16 * i * SP + 16 * i], SP, part, SP);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st[(16 * i + 4 * lg + r) * SP + 16 * j + lr] = -tij[r];
-      wave_lds_sync();  // Tx_ij is an operand of the next block; part is rewritten
-    }
-  }
+  // Tx = (I + N)^-1 in 16x16 blocks (fp32), gdn_tri.h.
+  __device__ static void invert_diagonal_block(Smem& sm, int w, int l) { tri::invert_diagonal_block(sm.u.m.nf, w, l); }
+  __device__ static void lower_blocks(Smem& sm, int j) { tri::lower_blocks(sm.u.m.nf, sm.u.m.st, j); }
 
   // One workgroup per (chunk, batch, value head).  The G workgroups of a key
   // head recompute its K K^T and Q K^T (cheap on the matrix cores; the k / q
@@ -329,20 +281,10 @@ struct ChunkPrep {
 
     // ---- the blocks of Tx below the diagonal (the diagonal ones are in nf)
     __syncthreads();  // the staging matrix is free (P^T / Mq stored); the D_i are visible
-    if (w < 3) {
+    if (w < 3)
       lower_blocks(sm, w);
-    } else {  // diagonal blocks into the staging matrix, zeros above them
-#pragma unroll
-      for (int blk = 0; blk < 16; ++blk) {
-        const int bi = blk >> 2, bj = blk & 3;
-        if (bi > bj) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * bi + 4 * e + (l >> 4), col = 16 * bj + (l & 15);
-          sm.u.m.st[row * SP + col] = bi == bj ? sm.u.m.nf[row * SP + col] : 0.f;
-        }
-      }
-    }
+    else  // diagonal blocks into the staging matrix, zeros above them
+      tri::diagonal_blocks(sm.u.m.nf, sm.u.m.st, l);
     __syncthreads();
     store_mat(sm, p.cb.Tx + mat, tid);
   }
@@ -356,7 +298,7 @@ __global__ void __launch_bounds__(NT) chunk_prep_kernel(ChunkPrepArgs p) {
 
 // ------------------------------------------------------------ state pass
 
-template <int DK>
+template <int DK, bool VG = false>
 struct ChunkFwd {
   // Twelve waves in three groups of four (w = wave index within the group):
   //   A (waves 0-3):  K H, R and X = Tx R for row tile w.  A also streams the
@@ -372,27 +314,44 @@ struct ChunkFwd {
   //                   tile w (q and Mq prefetched two chunks ahead in
   //                   registers).
   // B and C work at the same time once X is in LDS.
+  // With the per-key-channel gate (VG) the operands come pre-scaled from
+  // vg_chunk_prep: A reads Kb rows (no row scale), B reads Kh^T from a second
+  // k tile of the ring and decays H row-wise by e^{G_L}, C reads Qb rows, and
+  // the weights of X are beta.
   static constexpr int NTS = 768;
   static constexpr int NV = 32;                   // Dv columns per workgroup
   static constexpr int RTW = DK / 64;             // H row tiles per group-B wave
   static constexpr int HS = DK + 8;               // bf16 row stride of H^T
   static constexpr int XS = L + 8;                // bf16 row stride of R^T / X^T
   static constexpr int NPK = DK / 8;              // 16-byte pieces of a k row
-  static constexpr int NSL = DK <= 192 ? 3 : 2;   // ring slots
+  static constexpr int NSL = VG ? (DK <= 128 ? 3 : 2) : (DK <= 192 ? 3 : 2);  // ring slots
   static constexpr int PD = NSL - 1;              // chunks loaded ahead
   static constexpr int KDMA = DK / 32;            // k loads per group-A wave per chunk
-  static constexpr int NDMA = KDMA + 2 + 1 + 1;   // ring loads per group-A wave per chunk
+  static constexpr int NDMA = KDMA * (VG ? 2 : 1) + 2 + 1 + 1;  // ring loads per group-A wave per chunk
+  static constexpr int SCR = VG ? VSC_ROWS : SC_ROWS;  // chunk scalar rows per chunk
   // A ring slot.  Lane i of a direct-to-LDS load writes its 16 (or 4) bytes at
   // the load's base + 16 i (4 i), so the layouts are set through the global
   // addresses: 16-byte piece p of row t sits at t * (pieces per row) +
   // (p ^ swizzle(t)), which keeps the operand reads free of bank conflicts.
-  struct Slot {
-    bf16 k[L * DK];   // k rows [t][i], swizzle t & 7
+  struct SlotBase {
+    bf16 k[L * DK];   // k rows [t][i] (VG: Kb), swizzle t & 7
     bf16 tx[L * L];   // Tx rows, swizzle t & 7
     bf16 v[L * NV];   // v rows of this slice's columns, swizzle t & 3
-    float sc[4 * L];  // chunk scalar rows 0 .. 3 (SC_CR, SC_CO, SC_W, SC_EGL)
+    float sc[4 * L];  // chunk scalar rows 0 .. 3 (SC_CR, SC_CO, SC_W, SC_EGL; VG: beta, e^{G_L})
   };
+  struct SlotVg : SlotBase {
+    bf16 kh[L * DK];  // Kh rows [t][i], swizzle t & 7
+  };
+  using Slot = std::conditional_t<VG, SlotVg, SlotBase>;
   static_assert(SC_CR < 4 && SC_CO < 4 && SC_W < 4 && SC_EGL < 4, "rows held in a ring slot");
+  static_assert(!VG || DK <= 3 * L, "e^{G_L} of every channel in rows 1 .. 3 of the slot");
+  // the k tile group B reads transposed
+  __device__ static __forceinline__ const bf16* b_tile(const Slot& s) {
+    if constexpr (VG)
+      return s.kh;
+    else
+      return s.k;
+  }
   struct Smem {
     alignas(16) Slot ring[NSL];
     alignas(16) bf16 hb[NV * HS];   // H^T (bf16), the B operand of K H and Q H
@@ -421,7 +380,7 @@ struct ChunkFwd {
     uint32_t vstep, vbase;       // v elements per step and offset (0, 0: the zero rows)
     uint32_t qk_row, v_row;   // element strides of one step in q/k and v/o
     rsrc_t rq, rmq;              // buffer descriptors of group C's operands
-    i32x4 dk, dv, dtx, dsc;      // raw descriptors of the ring's operands
+    i32x4 dk, dkh, dv, dtx, dsc; // raw descriptors of the ring's operands
   };
 
   // element offsets of 16-byte piece p of row t in the ring tiles
@@ -438,7 +397,13 @@ struct ChunkFwd {
 #pragma unroll
     for (int jj = 0; jj < KDMA; ++jj) {
       const int n = KDMA * q.w + jj, pos = 64 * n + l, t = pos / NPK, pc = (pos % NPK) ^ (t & 7);
-      dma16(q.dk, &s.k[512 * n], 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hk + q.j) * DK + 8 * pc));
+      if constexpr (VG) {  // Kb and Kh rows of this (head, chunk); rows past the end are zero
+        const uint32_t o = 2 * ((static_cast<uint32_t>(q.bh * q.NC + c) * L + t) * DK + 8 * pc);
+        dma16(q.dk, &s.k[512 * n], o);
+        dma16(q.dkh, &s.kh[512 * n], o);
+      } else {
+        dma16(q.dk, &s.k[512 * n], 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * d.Hk + q.j) * DK + 8 * pc));
+      }
     }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -450,14 +415,15 @@ struct ChunkFwd {
       dma16(q.dv, &s.v[512 * q.w],
             2 * (static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * q.vstep + q.vbase + 8 * pc));
     }
-    dma4(q.dsc, &s.sc[L * q.w], 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SC_ROWS * L + L * q.w + l));
+    dma4(q.dsc, &s.sc[L * q.w], 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SCR * L + L * q.w + l));
   }
 
   __device__ static void load_c(const ChunkFwdArgs& p, const Lane& q, int c, StageC& s) {
     const Dims& d = p.d;
     const int t0 = c * L, tl = q.last - t0;
     const int cr_ = 16 * q.w + coal_row(q.l), cp_ = coal_piece(q.l);  // quad-coalesced (see to_mfma_layout)
-    const uint32_t ko = 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
+    const uint32_t ko = VG ? 2 * ((static_cast<uint32_t>(q.bh * q.NC + c) * L + cr_) * DK + 8 * cp_)
+                           : 2 * ((static_cast<uint32_t>(q.b * d.T + t0 + min(cr_, tl)) * d.Hk + q.j) * DK + 8 * cp_);
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt) s.qa[kt] = buf_bf16x8(q.rq, ko + 64 * kt);
     const uint32_t mo = 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + cr_ * L + 8 * cp_);
@@ -489,8 +455,8 @@ struct ChunkFwd {
     for (int kt = 0; kt < DK / 32; ++kt) ka[kt] = load_bf16x8(&s.k[kpos(ta, 4 * kt + lg)]);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) txa[kt] = load_bf16x8(&s.tx[xpos(ta, 4 * kt + lg)]);
-    const float4 cr = *reinterpret_cast<const float4*>(&s.sc[SC_CR * L + q.tc0]);
-    const float4 wv = *reinterpret_cast<const float4*>(&s.sc[SC_W * L + q.tc0]);
+    const float4 cr = VG ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(&s.sc[SC_CR * L + q.tc0]);
+    const float4 wv = *reinterpret_cast<const float4*>(&s.sc[(VG ? VSC_BETA : SC_W) * L + q.tc0]);
     const float wvv[4] = {wv.x, wv.y, wv.z, wv.w};
     const float crv[4] = {cr.x, cr.y, cr.z, cr.w};
     f32x4 kh[2];
@@ -547,22 +513,26 @@ struct ChunkFwd {
     lds_barrier();  // 1
     lds_barrier();  // 2: X complete
     const float egl = s.sc[SC_EGL * L];
+    const bf16* kb = b_tile(s);
     bf16x8 kta[RTW][2];
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int t = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * (q.w * RTW + it) + ((lr >> 1) & 1);
-        const uint2 lo = lds_read_tr16(&s.k[kpos(t, pc) + 4 * (lr & 1)]);
-        const uint2 hi = lds_read_tr16(&s.k[kpos(t + 4, pc) + 4 * (lr & 1)]);
+        const uint2 lo = lds_read_tr16(&kb[kpos(t, pc) + 4 * (lr & 1)]);
+        const uint2 hi = lds_read_tr16(&kb[kpos(t + 4, pc) + 4 * (lr & 1)]);
         kta[it][kt] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
       }
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+      for (int r = 0; r < 4; ++r) {
+        // VG: e^{G_L} of row i = 16 (w RTW + it) + 4 lg + r
+        const float e = VG ? s.sc[VSC_EGL * L + 16 * (q.w * RTW + it) + 4 * lg + r] : egl;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) H[it][ct][r] *= egl;
+        for (int ct = 0; ct < 2; ++ct) H[it][ct][r] *= e;
+      }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       bf16x8 bx[2];
@@ -654,7 +624,7 @@ struct ChunkFwd {
     const Dims& d = p.d;
     const int t0 = c * L, Lc = min(L, d.T - t0);
     const int lr = q.lr, lg = q.lg;
-    const float co = sm.ring[c % NSL].sc[SC_CO * L + q.ta];
+    const float co = VG ? 1.f : sm.ring[c % NSL].sc[SC_CO * L + q.ta];
     f32x4 o[2];  // rows v = 16 ct + 4 lg + r, column t = 16 w + lr
     o[0] = o[1] = f4zero();
 #pragma unroll
@@ -801,14 +771,20 @@ struct ChunkFwd {
     q.v_row = d.Hv * d.Dv;
     {
       const size_t bt = static_cast<size_t>(d.B) * d.T, nmat = static_cast<size_t>(d.B) * d.Hv * q.NC;
-      q.dk = raw_desc(p.k, bt * d.Hk * DK * 2);
-      q.rq = make_rsrc(p.q, bt * d.Hk * DK * 2);
+      if constexpr (VG) {
+        q.dk = raw_desc(p.cb.Kb, nmat * L * DK * 2);
+        q.dkh = raw_desc(p.cb.Kh, nmat * L * DK * 2);
+        q.rq = make_rsrc(p.cb.Qb, nmat * L * DK * 2);
+      } else {
+        q.dk = q.dkh = raw_desc(p.k, bt * d.Hk * DK * 2);
+        q.rq = make_rsrc(p.q, bt * d.Hk * DK * 2);
+      }
       q.dv = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.v, bt * d.Hv * d.Dv * 2);
       q.vstep = q.mode == 1 ? 0u : static_cast<uint32_t>(d.Hv * d.Dv);
       q.vbase = q.mode == 1 ? 0u : static_cast<uint32_t>(q.h * d.Dv + q.col0);
       q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
       q.rmq = make_rsrc(p.cb.Mq, nmat * L * L * 2);
-      q.dsc = raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
+      q.dsc = VG ? raw_desc(p.cb.vsc, nmat * VSC_ROWS * L * 4) : raw_desc(p.cb.sc, nmat * SC_ROWS * L * 4);
     }
     if (q.ce <= q.cs) return;
     if (tid < 256)
@@ -820,10 +796,10 @@ struct ChunkFwd {
   }
 };
 
-template <int DK>
+template <int DK, bool VG>
 __global__ void __launch_bounds__(768) chunk_fwd_kernel(ChunkFwdArgs p) {
-  __shared__ typename ChunkFwd<DK>::Smem sm;
-  ChunkFwd<DK>::run(p, sm);
+  __shared__ typename ChunkFwd<DK, VG>::Smem sm;
+  ChunkFwd<DK, VG>::run(p, sm);
 }
 
 // ------------------------------------------------ T-parallel segment chain
@@ -965,11 +941,21 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st) {
   const int NV = ChunkFwd<64>::NV;
   const int nseg = a.seg ? (a.d.nchunk() + a.seg - 1) / a.seg : 1;
   const dim3 nblk(a.d.B * a.d.Hv * ((a.map ? a.d.Dk + a.d.Dv : a.d.Dv) / NV), nseg);
+  if (a.vg) {
+    if (a.seg || a.map) return hipErrorInvalidValue;
+    switch (a.d.Dk) {
+      case 64: chunk_fwd_kernel<64, true><<<nblk, ChunkFwd<64, true>::NTS, 0, st>>>(a); break;
+      case 128: chunk_fwd_kernel<128, true><<<nblk, ChunkFwd<128, true>::NTS, 0, st>>>(a); break;
+      case 192: chunk_fwd_kernel<192, true><<<nblk, ChunkFwd<192, true>::NTS, 0, st>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.d.Dk) {
-    case 64: chunk_fwd_kernel<64><<<nblk, ChunkFwd<64>::NTS, 0, st>>>(a); break;
-    case 128: chunk_fwd_kernel<128><<<nblk, ChunkFwd<128>::NTS, 0, st>>>(a); break;
-    case 192: chunk_fwd_kernel<192><<<nblk, ChunkFwd<192>::NTS, 0, st>>>(a); break;
-    case 256: chunk_fwd_kernel<256><<<nblk, ChunkFwd<256>::NTS, 0, st>>>(a); break;
+    case 64: chunk_fwd_kernel<64, false><<<nblk, ChunkFwd<64>::NTS, 0, st>>>(a); break;
+    case 128: chunk_fwd_kernel<128, false><<<nblk, ChunkFwd<128>::NTS, 0, st>>>(a); break;
+    case 192: chunk_fwd_kernel<192, false><<<nblk, ChunkFwd<192>::NTS, 0, st>>>(a); break;
+    case 256: chunk_fwd_kernel<256, false><<<nblk, ChunkFwd<256>::NTS, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

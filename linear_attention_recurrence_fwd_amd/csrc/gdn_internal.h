@@ -124,7 +124,18 @@ struct ChunkBufs {
   // chunk products): written by chunk_fwd and read by chunk_bwd_grad in place
   // of recomputing it, when non-null
   bf16* X;
+  // Per-key-channel gate (vg_chunk_prep), per value head, with G_t the
+  // in-chunk cumulative log-gate vector (G_t = lg_0 + ... + lg_t, masked
+  // steps 0) and rows past the end of the sequence zero:
+  bf16* Kb;   // [B*Hv, NC, L, Dk] kn_t * e^{G_t}            (forward)
+  bf16* Kh;   // [B*Hv, NC, L, Dk] kn_t * e^{G_L - G_t}
+  bf16* Qb;   // [B*Hv, NC, L, Dk] qn_t * e^{G_t} / sqrt(Dk)  (forward)
+  bf16* KbT;  // [B*Hv, NC, Dk, L] Kb transposed              (backward)
+  bf16* QbT;  // [B*Hv, NC, Dk, L] Qb transposed              (backward)
+  float* vsc; // [B*Hv, NC, VSC_ROWS, L] beta_t (row 0), e^{G_L} (rows 1.., Dk values)
 };
+// Rows of ChunkBufs::vsc.
+enum : int { VSC_BETA = 0, VSC_EGL = 1, VSC_ROWS = 8 };
 // Rows of ChunkBufs::sc (per chunk, per step t; g = gamma):
 enum : int {
   SC_CR = 0,     // e^{g_t} rk_t
@@ -173,6 +184,23 @@ struct ChunkPrepArgs {
             // A^T, P^T, K^T, Q^T); 2: both
 };
 
+// Chunk matrices of the per-key-channel gate: Tx, Mq / A^T, P^T (as
+// ChunkBufs, with the decay e^{G_t - G_s} taken per channel inside the
+// products) and the pre-scaled rows Kb, Kh, Qb / KbT, QbT and vsc.
+struct VgChunkPrepArgs {
+  Dims d;
+  const void *q, *k, *b;
+  const float* lg;
+  const uint8_t* mask;
+  ChunkBufs cb;
+  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kh, KbT, QbT, vsc
+};
+// The chunk form of the per-key-channel gate: bf16 I/O, Dk up to 192 (the
+// state passes hold a second k tile in LDS), Dv a multiple of 32.
+inline bool vg_chunk_supported(int Dk, int Dv, bool bf16) {
+  return bf16 && (Dk == 64 || Dk == 128 || Dk == 192) && Dv % 32 == 0 && Dv <= 256;
+}
+
 struct ChunkFwdArgs {
   Dims d;
   const void *q, *k, *v;
@@ -193,6 +221,7 @@ struct ChunkFwdArgs {
   const float* hseg;
   float* maps;
   const bf16* vzero;
+  int vg;  // 1: per-key-channel gate (operands Kb, Kh, Qb and vsc of cb)
 };
 // Start states of the segments: H_{s+1} = A_s H_s + B_s over the segment maps.
 struct SegChainArgs {
@@ -230,6 +259,7 @@ struct ChunkBwdArgs {
   const float* hseg;
   float* maps;
   const bf16* vzero;
+  int vg;  // 1: per-key-channel gate (operands Kh, KbT, QbT and vsc of cb)
 };
 
 // bf16 copies of the states at the chunk starts from the fp32 checkpoints:
@@ -291,6 +321,7 @@ hipError_t launch_scan_bwd_vg(const ScanBwdVgArgs& a, bool bf16, hipStream_t st)
 hipError_t launch_vg_reduce(const VgReduceArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
+hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
 hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);

@@ -84,8 +84,8 @@ static void run_case(int64_t B, int64_t T, int64_t Hk, int64_t Hv, int64_t Dk, i
               wb, bws ? bws - 1 : 0, nullptr);
   EXPECT(bws == 0 || r == GDN_ERR_WORKSPACE, "short bwd workspace rc %d", r);
   EXPECT(T == 0 || gdn_stub_launches() > before, "nothing launched");
-  // the per-key-channel gate (scan family)
-  if (algo == GDN_ALGO_SCAN || algo == GDN_ALGO_AUTO) {
+  // the per-key-channel gate (scan or chunk form, as the dims select)
+  if (algo == GDN_ALGO_SCAN || algo == GDN_ALGO_AUTO || algo == GDN_ALGO_CHUNK) {
     size_t vf = 0, vb = 0;
     if (gdn_fwd_vg_workspace_bytes(&d, &vf) == GDN_OK && gdn_bwd_vg_workspace_bytes(&d, &vb) == GDN_OK) {
       gdn_dims ds = d;

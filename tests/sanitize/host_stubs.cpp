@@ -47,6 +47,8 @@ void touch_chunk(const gdn::Dims& d, const gdn::ChunkBufs& cb) {
   touch(cb.sc, nmat(d) * gdn::SC_ROWS * 64 * 4);
   touch(cb.Hb, slots(d) * 2);
   touch(cb.X, bt(d) * d.Hv * d.Dv * 2);
+  for (const gdn::bf16* r : {cb.Kb, cb.Kh, cb.Qb, cb.KbT, cb.QbT}) touch(r, nmat(d) * 64 * d.Dk * 2);
+  touch(cb.vsc, nmat(d) * gdn::VSC_ROWS * 64 * 4);
 }
 size_t map_floats(const gdn::Dims& d, int seg) {
   return static_cast<size_t>(gdn::tpar_nseg(d, seg)) * d.B * d.Hv * d.Dk * (d.Dk + d.Dv);
@@ -112,6 +114,11 @@ hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t) {
+  touch_chunk(a.d, a.cb);
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t) {
   touch_chunk(a.d, a.cb);
   ++g_launches;
   return hipSuccess;

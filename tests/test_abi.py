@@ -186,14 +186,20 @@ def test_decode_conv_rejects_before_launch():
 
 
 def test_vg_rejects_before_launch():
-    """gdn_fwd_vg / gdn_bwd_vg: the chunk family is not built for the
-    per-channel gate, and required pointers and the workspace are checked
-    before any launch (the pointers here are never dereferenced)."""
+    """gdn_fwd_vg / gdn_bwd_vg: the chunk form of the per-channel gate exists
+    for bf16 with Dk 64 / 128 / 192 only, and not T-parallel; required
+    pointers and the workspace are checked before any launch (the pointers
+    here are never dereferenced)."""
     lib = B.lib()
     out = ctypes.c_size_t(0)
     chunk = B.make_dims(1, 128, 2, 4, 64, 32, B.GDN_BF16, B.ALGO_CHUNK)
-    assert lib.gdn_fwd_vg_workspace_bytes(ctypes.byref(chunk), ctypes.byref(out)) == 2
-    assert lib.gdn_bwd_vg_workspace_bytes(ctypes.byref(chunk), ctypes.byref(out)) == 2
+    assert lib.gdn_fwd_vg_workspace_bytes(ctypes.byref(chunk), ctypes.byref(out)) == 0
+    assert lib.gdn_bwd_vg_workspace_bytes(ctypes.byref(chunk), ctypes.byref(out)) == 0
+    for bad in (B.make_dims(1, 128, 2, 4, 256, 32, B.GDN_BF16, B.ALGO_CHUNK),
+                B.make_dims(1, 128, 2, 4, 64, 32, B.GDN_F32, B.ALGO_CHUNK),
+                B.make_dims(1, 128, 2, 4, 64, 32, B.GDN_BF16, B.ALGO_CHUNK_TPAR)):
+        assert lib.gdn_fwd_vg_workspace_bytes(ctypes.byref(bad), ctypes.byref(out)) == 2
+        assert lib.gdn_bwd_vg_workspace_bytes(ctypes.byref(bad), ctypes.byref(out)) == 2
     d = B.make_dims(1, 128, 2, 4, 64, 32, B.GDN_F32)
     assert lib.gdn_fwd_vg_workspace_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
     fws = out.value
