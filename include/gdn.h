@@ -243,7 +243,7 @@ int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const 
  * takes) and CHUNK (the chunked bf16 matrix-core form, with the decays
  * e^{G_t - G_s} of the in-chunk cumulative log-gates taken per channel inside
  * the chunk products: bf16 I/O, Dk 64, 128 or 192, Dv a multiple of 32 up to
- * 256, the per-(head, chunk) buffers below 4 GiB).  AUTO takes CHUNK where it
+ * 128, the per-(head, chunk) buffers below 4 GiB).  AUTO takes CHUNK where it
  * is built and T > 1, else SCAN; CHUNK_TPAR gives GDN_ERR_UNSUPPORTED.  The
  * chunk form is exact (up to rounding) while every in-chunk factor
  * e^{|G_t - G_s|} stays within fp32 range, which holds for any lg <= 0 (a

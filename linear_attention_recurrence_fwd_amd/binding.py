@@ -341,11 +341,11 @@ def _check_inputs_vg(d, q, k, v, lg, b, state0, mask):
 
 def vg_uses_chunk(d) -> bool:
     """Whether gdn_fwd_vg / gdn_bwd_vg run the chunk form for these dims (the
-    library's rule: bf16, Dk 64 / 128 / 192, Dv a multiple of 32 up to 256,
+    library's rule: bf16, Dk 64 / 128 / 192, Dv a multiple of 32 up to 128,
     under AUTO more than one step, and the chunk buffers within 4 GiB)."""
     if d.T == 0 or d.algo == ALGO_SCAN:
         return False
-    ok = (d.dtype == GDN_BF16 and d.Dk in (64, 128, 192) and d.Dv % 32 == 0 and d.Dv <= 256)
+    ok = (d.dtype == GDN_BF16 and d.Dk in (64, 128, 192) and d.Dv % 32 == 0 and d.Dv <= 128)
     bhc = d.B * d.Hv * ((d.T + 63) // 64)
     ok = ok and max(bhc * 64 * d.Dk * 2, bhc * 64 * 64 * 2, bhc * 8 * 64 * 4) < 1 << 32
     return d.algo == ALGO_CHUNK or (d.T > 1 and ok)

@@ -315,8 +315,15 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
   L.kq = take(bt * d.Hk);
   L.beta = take(bt * d.Hv);
   if (bwd) {
-    const size_t ns = gdn::vg_nslice(d.Dv);
-    L.sub = take(gdn::vg_sub_floats(d));
+    // the chunk form's gradient pass writes one slice of row partials
+    const size_t ns = chunk ? 1 : gdn::vg_nslice(d.Dv);
+    if (chunk) {
+      const size_t nc = d.nchunk();
+      L.E = take((bt * d.Hv * d.Dv + 1) / 2);
+      L.dHend = take((nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv + 1) / 2);
+    } else {
+      L.sub = take(gdn::vg_sub_floats(d));
+    }
     L.part = take(bt * d.Hv * ns * 3 * d.Dk);
     L.pdb = take(bt * d.Hv * ns);
   }
@@ -668,7 +675,7 @@ int gdn_bwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_vg(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = vg_layout(dd, true, false).total;
+  *out = vg_layout(dd, true, use_vg_chunk(d)).total;
   return GDN_OK;
 }
 
@@ -713,13 +720,31 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
   if (dd.T > 0 && (!q || !k || !v || !lg || !b || !dO || !dq || !dk || !dv || !dlg || !db))
     return GDN_ERR_INVALID_ARG;
   if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
-  const VgLayout L = vg_layout(dd, true, false);
+  const bool chunk = use_vg_chunk(d);
+  const VgLayout L = vg_layout(dd, true, chunk);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const gdn::StepScalars s = vg_scalars(ws, L);
   gdn::PrepArgs pa{dd, q, k, nullptr, b, nullptr, nullptr, mask, s};
   if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
+  if (chunk) {
+    const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, true);
+    gdn::VgChunkPrepArgs ca{dd, q, k, b, lg, mask, cb, 1};
+    if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    gdn::bf16* E = at<gdn::bf16>(ws, L.E);
+    gdn::bf16* dHend = at<gdn::bf16>(ws, L.dHend);
+    gdn::ChunkBwdArgs ba{dd, q, k, v, dO, nullptr, nullptr, nullptr, mask, state0, ckpt, dS_final, cb,
+                         E, dHend, dq, dk, dv, nullptr, db, dstate, nullptr, nullptr};
+    ba.vg = 1;
+    if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
+    gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, cb, E, dHend, dv,
+                            at<float>(ws, L.part), at<float>(ws, L.pdb)};
+    if (!launch(st, [&] { return gdn::launch_vg_chunk_grad(ga, st); })) return GDN_ERR_HIP;
+    gdn::VgReduceArgs ra{dd, 1, q, k, s, at<float>(ws, L.part), at<float>(ws, L.pdb), dq, dk, db, dlg};
+    if (!launch(st, [&] { return gdn::launch_vg_reduce(ra, bf, st); })) return GDN_ERR_HIP;
+    return GDN_OK;
+  }
   gdn::ScanBwdVgArgs ba{dd, q, k, v, dO, lg, mask, state0, ckpt, dS_final, s,
                         at<float>(ws, L.sub), at<float>(ws, L.part), at<float>(ws, L.pdb), dv, dstate};
   if (!launch(st, [&] { return gdn::launch_scan_bwd_vg(ba, bf, st); })) return GDN_ERR_HIP;

@@ -195,10 +195,28 @@ struct VgChunkPrepArgs {
   ChunkBufs cb;
   int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kh, KbT, QbT, vsc
 };
+// Gradient pass of the per-key-channel gate's chunk form: one workgroup per
+// (chunk, batch, value head); X recomputed from the fp32 checkpoint; writes
+// the per-head row partials vg_reduce sums (one slice): dL/d(qn / sqrt(Dk)),
+// dL/dkn and dL/dlg per step, and dL/dbeta.
+struct VgChunkGradArgs {
+  Dims d;
+  const void *q, *k, *v, *b, *dO;
+  const float* lg;
+  const uint8_t* mask;
+  const float *state0, *ckpt;  // state0 may be null
+  ChunkBufs cb;                // Tx
+  const bf16* E;               // [B,T,Hv,Dv] eps (dL/d delta)
+  const bf16* dHend;           // [NC, B*Hv, Dk, Dv] dL/d(state at the end of chunk c)
+  const void* dv;              // [B,T,Hv,Dv] dv (= Ehat) from the reverse state pass
+  float* part;                 // [B,T,Hv,1,3,Dk]
+  float* pdb;                  // [B,T,Hv,1]
+};
 // The chunk form of the per-key-channel gate: bf16 I/O, Dk up to 192 (the
-// state passes hold a second k tile in LDS), Dv a multiple of 32.
+// state passes hold a second k tile in LDS), Dv a multiple of 32 up to 128
+// (the gradient pass holds Dv-wide row operands in registers).
 inline bool vg_chunk_supported(int Dk, int Dv, bool bf16) {
-  return bf16 && (Dk == 64 || Dk == 128 || Dk == 192) && Dv % 32 == 0 && Dv <= 256;
+  return bf16 && (Dk == 64 || Dk == 128 || Dk == 192) && Dv % 32 == 0 && Dv <= 128;
 }
 
 struct ChunkFwdArgs {
@@ -322,6 +340,7 @@ hipError_t launch_vg_reduce(const VgReduceArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t st);
+hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
 hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);

@@ -123,6 +123,16 @@ hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t) {
+  touch_chunk(a.d, a.cb);
+  touch(a.E, bt(a.d) * a.d.Hv * a.d.Dv * 2);
+  touch(a.dHend, slots(a.d) * 2);
+  touch_ckpt(a.d, a.ckpt);
+  touch(a.part, bt(a.d) * a.d.Hv * 3 * a.d.Dk * 4);
+  touch(a.pdb, bt(a.d) * a.d.Hv * 4);
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t) {
   touch_chunk(a.d, a.cb);
   touch_ckpt(a.d, a.ckpt);
