@@ -52,6 +52,11 @@ FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
 #                1 fma, dS' = D + kn du^T 1 fma, dkn = D delta + S' du 2 fma,
 #                dlg = <dS', S> along the row 1 fma, carry D = g dS' 1 mul    = 20
 KERNELS["vg"] = ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd_vg", "vg_reduce"]
+# ... and its chunk form (bf16): the forward's vg_chunk_prep and chunk_fwd (VG
+# mode); the backward's step scalars (prep), vg_chunk_prep, chunk_bwd_state (VG
+# mode), the gradient pass and the per-head sums
+KERNELS["vg_chunk"] = ["vg_prep_fwd", "chunk_fwd_vg", "prep_bwd", "vg_prep_bwd", "chunk_bwd_state_vg",
+                       "vg_chunk_grad", "vg_reduce"]
 FLOPS_PER_ELEM.update({"scan_bwd_vg": 20})
 VG_METRIC = "fwd+bwd tokens/sec with a per-key-channel gate at Hk16/Hv64/Dk192/Dv128 bf16, T=2048"
 
@@ -500,6 +505,28 @@ def vg_method_bytes(B, T, Hk, Hv, Dk, Dv, io):
     fwd = 2 * Q + V + LG + Bt + V + Sig + CK
     bwd = (2 * Q + V + LG + Bt + CK + V) + (2 * Q + V + LG + Bt + Sig)
     return fwd, bwd
+
+
+def vg_kernel_bytes(B, T, Hk, Hv, Dk, Dv, io):
+    """Algorithmic HBM bytes of each kernel of the per-channel gate's chunk
+    form: the tensors of vg_method_bytes that the kernel reads or writes, each
+    counted once per kernel (the pre-scaled rows, chunk matrices, eps, dH' and
+    the per-head partials are intermediates and not counted)."""
+    Q1 = B * T * Hk * Dk * io
+    V1 = B * T * Hv * Dv * io
+    Bt = B * T * Hv * io
+    LG = B * T * Hv * Dk * 4
+    Sig = B * Hv * Dk * Dv * 4
+    CK = max(math.ceil(T / 64) - 1, 0) * Sig
+    return {
+        "vg_prep_fwd": 2 * Q1 + LG + Bt,
+        "chunk_fwd_vg": 2 * V1 + Sig + CK,
+        "prep_bwd": 2 * Q1 + Bt,
+        "vg_prep_bwd": 2 * Q1 + LG + Bt,
+        "chunk_bwd_state_vg": 2 * V1 + Sig,
+        "vg_chunk_grad": 2 * Q1 + 2 * V1 + LG + Bt + CK,
+        "vg_reduce": 4 * Q1 + LG + Bt,
+    }
 
 
 def cpu_baseline_vg(T):

@@ -224,12 +224,15 @@ def decode_conv(steps: int = 64) -> ConvCase:
 
 def make_vg_case(name: str, B: int, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
                  dtype: str, seed: int, *, state_std: float | None = 0.1,
-                 dS_final: bool = True, mask: np.ndarray | None = None) -> Case:
+                 dS_final: bool = True, mask: np.ndarray | None = None,
+                 lg_mu: float = -1.5, lg_sigma: float = 1.5) -> Case:
     """Draw a workload of the per-key-channel-gate form: the gate is given as
-    log-gates lg [B,T,Hv,Dk] (fp32), lg = -exp(z) with z ~ N(-1.5, 1.5), so
-    per-channel decays g = e^lg range from nearly 1 (long memory) to nearly 0
-    (median e^-0.22 = 0.80).  q, k, v, b, dO ~ N(0,1); state0 ~ N(0, 0.1);
-    dS_final ~ N(0,1).  Draw order: q, k, v, lg, b, state0, dO, dS_final."""
+    log-gates lg [B,T,Hv,Dk] (fp32), lg = -exp(z) with z ~ N(lg_mu, lg_sigma)
+    (default N(-1.5, 1.5)), so per-channel decays g = e^lg range from nearly 1
+    (long memory) to nearly 0 (median e^-0.22 = 0.80; lg_mu = -6, lg_sigma = 1
+    gives slow decays, median e^-0.0025).  q, k, v, b, dO ~ N(0,1); state0 ~
+    N(0, 0.1); dS_final ~ N(0,1).  Draw order: q, k, v, lg, b, state0, dO,
+    dS_final."""
     assert dtype in DTYPES and Hv % Hk == 0
     rng = np.random.Generator(np.random.PCG64(seed))
     c = Case(name, B, T, Hk, Hv, Dk, Dv, dtype)
@@ -237,7 +240,7 @@ def make_vg_case(name: str, B: int, T: int, Hk: int, Hv: int, Dk: int, Dv: int,
     v["q"] = _round(rng.standard_normal((B, T, Hk, Dk)), dtype)
     v["k"] = _round(rng.standard_normal((B, T, Hk, Dk)), dtype)
     v["v"] = _round(rng.standard_normal((B, T, Hv, Dv)), dtype)
-    v["lg"] = _round(-np.exp(-1.5 + 1.5 * rng.standard_normal((B, T, Hv, Dk))), "f32")
+    v["lg"] = _round(-np.exp(lg_mu + lg_sigma * rng.standard_normal((B, T, Hv, Dk))), "f32")
     v["b"] = _round(rng.standard_normal((B, T, Hv)), dtype)
     if state_std is not None:
         v["state0"] = _round(state_std * rng.standard_normal((B, Hv, Dk, Dv)), "f32")

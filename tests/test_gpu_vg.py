@@ -2,13 +2,17 @@
 the C ABI) against the fp64 oracle (oracle.fwd_vg / oracle.bwd_vg).
 
 Tolerances as for the scalar gate (normwise per tensor, max|x - ref| /
-max|ref|): 1e-4 for fp32 workloads, 2e-2 for bf16.  Shapes cover every lane
-layout of the reverse sweep (Dk = 16 .. 256: one to four rows per lane, rows
-padded below 64; Dv with one or four waves per workgroup), ragged chunk tails
-and recompute blocks, masks, the Qwen3.5-9B layer shape at T = 256 and 2048
-with a per-channel gate, and a Kimi-Linear-like shape (32 heads of 128; the
-pages name the model but not its sizes, so the sizes are an assumption).
-Repeated runs must be bit-identical.
+max|ref|): 1e-4 for fp32 workloads, 2e-2 for bf16.  The fp32 cases run the
+scan kernels and cover every lane layout of the reverse sweep (Dk = 16 .. 256:
+one to four rows per lane, rows padded below 64; Dv with one or four waves
+per workgroup), ragged chunk tails and recompute blocks, masks.  The bf16
+cases run the chunk form (AUTO or CHUNK): every built (Dk, Dv) with ragged
+tails and masks, sequences of 1 .. 129 steps, gates that do not decay, that
+underflow, that decay strongly or slowly over 2048 steps, the Qwen3.5-9B
+layer shape at T = 256 and 2048 with a per-channel gate, a Kimi-Linear-like
+shape (32 heads of 128; the pages name the model but not its sizes, so the
+sizes are an assumption), and a forward of one family with a backward of the
+other.  Repeated runs must be bit-identical.
 """
 import numpy as np
 import pytest
@@ -35,19 +39,20 @@ def upload_vg(case):
     return t
 
 
-def run_vg(t):
-    o, st, ck = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"])
+def run_vg(t, algo=binding.ALGO_AUTO, bwd_algo=None):
+    o, st, ck = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"], algo=algo)
     g = binding.bwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"], ck,
-                       t["dO"], t["dS_final"])
+                       t["dO"], t["dS_final"], algo=algo if bwd_algo is None else bwd_algo)
     return o, st, ck, g
 
 
-def compare_vg(case, nthreads=8):
+def compare_vg(case, nthreads=8, algo=binding.ALGO_AUTO, bwd_algo=None):
     tol = TOL[case.dtype]
-    say("[vg] case=%s B=%d T=%d Hk=%d Hv=%d Dk=%d Dv=%d dtype=%s" % (
-        case.name, case.B, case.T, case.Hk, case.Hv, case.Dk, case.Dv, case.dtype))
+    say("[vg] case=%s B=%d T=%d Hk=%d Hv=%d Dk=%d Dv=%d dtype=%s algo=%d/%d" % (
+        case.name, case.B, case.T, case.Hk, case.Hv, case.Dk, case.Dv, case.dtype, algo,
+        algo if bwd_algo is None else bwd_algo))
     t = upload_vg(case)
-    o, st, ck, g = run_vg(t)
+    o, st, ck, g = run_vg(t, algo, bwd_algo)
     torch.cuda.synchronize()
     v = case.vals
     ro, rst, rck = oracle.fwd_vg(*case.vg_args(), nthreads=nthreads)
@@ -156,3 +161,73 @@ def test_vg_extreme_gates(kind):
     else:
         c.vals["lg"][..., ::2] = -200.0
     compare_vg(c)
+
+
+# ---- the chunk form (bf16)
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 32), (64, 128), (128, 64), (128, 96), (192, 32), (192, 128)])
+def test_vg_chunk_shapes(Dk, Dv):
+    """Three chunks with a ragged tail (64 + 64 + 13 steps) and masked steps,
+    two value heads per key head, for every built head size."""
+    B, T = 2, 141
+    mask = np.ones((B, T), dtype=np.uint8)
+    mask[0, 5] = 0
+    mask[0, 63:66] = 0
+    mask[1, 100:] = 0
+    c = inputs.make_vg_case("vg_chunk_Dk%d_Dv%d" % (Dk, Dv), B, T, 2, 4, Dk, Dv, "bf16",
+                            9600 + Dk + Dv, mask=mask)
+    compare_vg(c, algo=binding.ALGO_CHUNK)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 129])
+def test_vg_chunk_edges(T):
+    compare_vg(inputs.vg_edge(T, masked=True, dtype="bf16"), algo=binding.ALGO_CHUNK)
+
+
+@pytest.mark.parametrize("kind", ["no_decay", "underflow", "strong"])
+def test_vg_chunk_extreme_gates(kind):
+    """lg = 0 (no decay), lg = -200 on every other channel (those rows are
+    wiped every step: e^{G} underflows inside the chunk products) and lg = -30
+    on a third of the channels with slow decays elsewhere."""
+    c = inputs.make_vg_case("vg_chunk_" + kind, 2, 150, 2, 4, 128, 64, "bf16", 9700)
+    if kind == "no_decay":
+        c.vals["lg"][...] = 0.0
+    elif kind == "underflow":
+        c.vals["lg"][..., ::2] = -200.0
+    else:
+        c.vals["lg"][...] = -0.01
+        c.vals["lg"][..., ::3] = -30.0
+    compare_vg(c, algo=binding.ALGO_CHUNK)
+
+
+def test_vg_chunk_long_memory():
+    """Slow decays (median e^-0.0025 per step) over 2048 steps: the bf16
+    rounding of the chunk products carried through 32 chunk boundaries."""
+    c = inputs.make_vg_case("vg_chunk_long_memory", 1, 2048, 2, 4, 128, 128, "bf16", 9800,
+                            lg_mu=-6.0, lg_sigma=1.0)
+    compare_vg(c, nthreads=16, algo=binding.ALGO_CHUNK)
+
+
+@pytest.mark.parametrize("fwd,bwd", [(binding.ALGO_CHUNK, binding.ALGO_SCAN),
+                                     (binding.ALGO_SCAN, binding.ALGO_CHUNK)])
+def test_vg_families_interchange(fwd, bwd):
+    """Both families write the same fp32 checkpoints, so a forward of one pairs
+    with a backward of the other."""
+    mask = np.ones((2, 150), dtype=np.uint8)
+    mask[1, 70:90] = 0
+    c = inputs.make_vg_case("vg_interchange", 2, 150, 2, 4, 128, 64, "bf16", 9900, mask=mask)
+    compare_vg(c, algo=fwd, bwd_algo=bwd)
+
+
+def test_vg_chunk_state_in_place():
+    c = inputs.make_vg_case("vg_chunk_inplace", 2, 70, 2, 4, 64, 32, "bf16", 9950)
+    say("[vg chunk in-place] case=%s" % c.name)
+    t = upload_vg(c)
+    o, st, _ = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], None,
+                              algo=binding.ALGO_CHUNK)
+    s = t["state0"].clone()
+    o2, st2, _ = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], s, None, state_out=s,
+                                algo=binding.ALGO_CHUNK)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == s.data_ptr()
+    assert torch.equal(o, o2) and torch.equal(st, s)
