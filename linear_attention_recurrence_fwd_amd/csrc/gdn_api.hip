@@ -256,7 +256,7 @@ gdn::StepScalars scalars(void* ws, const Layout& L) {
 struct VgLayout {
   size_t rq, rk, kq, beta, sub, part, pdb;
   size_t Kb, Kh, Qb, KbT, QbT, Tx, Mq, AtT, PqT, vsc;  // chunk form
-  size_t E, dHend;                                     // chunk form, backward
+  size_t E, dHend, X, dPA;                             // chunk form, backward
   size_t total;
 };
 
@@ -295,11 +295,11 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
   if (chunk) {
     const size_t nc = d.nchunk(), bhc = static_cast<size_t>(d.B) * d.Hv * nc;
     const size_t rows = (bhc * 64 * d.Dk + 1) / 2, mats = (bhc * 64 * 64 + 1) / 2;  // bf16, in floats
+    L.Kb = take(rows);
     L.Kh = take(rows);
     L.Tx = take(mats);
     L.vsc = take(bhc * gdn::VSC_ROWS * 64);
     if (!bwd) {
-      L.Kb = take(rows);
       L.Qb = take(rows);
       L.Mq = take(mats);
       L.total = off;
@@ -309,6 +309,8 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
     L.QbT = take(rows);
     L.AtT = take(mats);
     L.PqT = take(mats);
+    L.X = take((bhc * 64 * d.Dv + 1) / 2);
+    L.dPA = take(2 * mats);
   }
   L.rq = take(bt * d.Hk);
   L.rk = take(bt * d.Hk);
@@ -338,6 +340,7 @@ gdn::StepScalars vg_scalars(void* ws, const VgLayout& L) {
 
 gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd) {
   gdn::ChunkBufs cb{};
+  cb.Kb = at<gdn::bf16>(ws, L.Kb);
   cb.Kh = at<gdn::bf16>(ws, L.Kh);
   cb.Tx = at<gdn::bf16>(ws, L.Tx);
   cb.vsc = at<float>(ws, L.vsc);
@@ -347,7 +350,6 @@ gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd) {
     cb.AtT = at<gdn::bf16>(ws, L.AtT);
     cb.PqT = at<gdn::bf16>(ws, L.PqT);
   } else {
-    cb.Kb = at<gdn::bf16>(ws, L.Kb);
     cb.Qb = at<gdn::bf16>(ws, L.Qb);
     cb.Mq = at<gdn::bf16>(ws, L.Mq);
   }
@@ -738,8 +740,10 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
                          E, dHend, dq, dk, dv, nullptr, db, dstate, nullptr, nullptr};
     ba.vg = 1;
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
-    gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, cb, E, dHend, dv,
-                            at<float>(ws, L.part), at<float>(ws, L.pdb)};
+    gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, s, cb, E, dHend, dv,
+                            at<gdn::bf16>(ws, L.X), at<gdn::bf16>(ws, L.dPA), at<float>(ws, L.part),
+                            at<float>(ws, L.pdb)};
+    if (!launch(st, [&] { return gdn::launch_vg_chunk_x(ga, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_vg_chunk_grad(ga, st); })) return GDN_ERR_HIP;
     gdn::VgReduceArgs ra{dd, 1, q, k, s, at<float>(ws, L.part), at<float>(ws, L.pdb), dq, dk, db, dlg};
     if (!launch(st, [&] { return gdn::launch_vg_reduce(ra, bf, st); })) return GDN_ERR_HIP;

@@ -127,7 +127,7 @@ struct ChunkBufs {
   // Per-key-channel gate (vg_chunk_prep), per value head, with G_t the
   // in-chunk cumulative log-gate vector (G_t = lg_0 + ... + lg_t, masked
   // steps 0) and rows past the end of the sequence zero:
-  bf16* Kb;   // [B*Hv, NC, L, Dk] kn_t * e^{G_t}            (forward)
+  bf16* Kb;   // [B*Hv, NC, L, Dk] kn_t * e^{G_t}
   bf16* Kh;   // [B*Hv, NC, L, Dk] kn_t * e^{G_L - G_t}
   bf16* Qb;   // [B*Hv, NC, L, Dk] qn_t * e^{G_t} / sqrt(Dk)  (forward)
   bf16* KbT;  // [B*Hv, NC, Dk, L] Kb transposed              (backward)
@@ -193,25 +193,32 @@ struct VgChunkPrepArgs {
   const float* lg;
   const uint8_t* mask;
   ChunkBufs cb;
-  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kh, KbT, QbT, vsc
+  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kb, Kh, KbT, QbT, vsc
 };
-// Gradient pass of the per-key-channel gate's chunk form: one workgroup per
-// (chunk, batch, value head); X recomputed from the fp32 checkpoint; writes
-// the per-head row partials vg_reduce sums (one slice): dL/d(qn / sqrt(Dk)),
-// dL/dkn and dL/dlg per step, and dL/dbeta.
+// Gradient pass of the per-key-channel gate's chunk form, in two kernels:
+// vg_chunk_x (one workgroup per (chunk, batch, value head)) recomputes X from
+// the fp32 checkpoint and writes it with dP, dA and dL/dbeta; vg_chunk_grad
+// (one workgroup per (chunk, batch, value head, 32 channels)) writes the
+// per-head row partials vg_reduce sums (one slice): dL/d(qn / sqrt(Dk)),
+// dL/dkn and dL/dlg per step.
 struct VgChunkGradArgs {
   Dims d;
   const void *q, *k, *v, *b, *dO;
   const float* lg;
   const uint8_t* mask;
   const float *state0, *ckpt;  // state0 may be null
-  ChunkBufs cb;                // Tx
+  StepScalars s;               // rk, rq
+  ChunkBufs cb;                // Tx, Kb, vsc
   const bf16* E;               // [B,T,Hv,Dv] eps (dL/d delta)
   const bf16* dHend;           // [NC, B*Hv, Dk, Dv] dL/d(state at the end of chunk c)
   const void* dv;              // [B,T,Hv,Dv] dv (= Ehat) from the reverse state pass
+  bf16* X;                     // [B*Hv, NC, L, Dv] X_t = v_t - u_t of every step
+  bf16* dPA;                   // [B*Hv, NC, 2, L, L] dP, dA
   float* part;                 // [B,T,Hv,1,3,Dk]
   float* pdb;                  // [B,T,Hv,1]
 };
+// Channels per vg_chunk_grad workgroup.
+constexpr int kVgGradChannels = 32;
 // The chunk form of the per-key-channel gate: bf16 I/O, Dk up to 192 (the
 // state passes hold a second k tile in LDS), Dv a multiple of 32 up to 128
 // (the gradient pass holds Dv-wide row operands in registers).
@@ -340,6 +347,7 @@ hipError_t launch_vg_reduce(const VgReduceArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_param_reduce(const ParamReduceArgs& a, hipStream_t st);
 hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t st);
+hipError_t launch_vg_chunk_x(const VgChunkGradArgs& a, hipStream_t st);
 hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
 hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t st);

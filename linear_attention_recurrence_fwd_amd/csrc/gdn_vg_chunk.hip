@@ -55,6 +55,8 @@ namespace {
 
 constexpr int L = kChunk;
 constexpr int NT = 256;
+// Largest in-block decay exponent the MFMA form of a diagonal block takes.
+constexpr float kDiagSpan = 60.f;
 
 // Tiles (tt, uu), uu <= tt, of a 16 x 16 diagonal sub-block in 4 x 4 steps:
 // index tt (tt + 1) / 2 + uu.
@@ -101,7 +103,10 @@ struct VgPrep {
   struct Smem {
     alignas(16) Big u;
     alignas(16) float dp[NTASK * 32];  // diagonal sub-block partial sums: 16 of A, 16 of P per task
+    alignas(16) float dg[4][2][16][17];  // diagonal sub-blocks over the channels in range (A, P)
     float rk[L], rq[L], beta[L], valid[L];
+    unsigned char far[4][DK];  // channel i decays by more than e^kDiagSpan inside sub-block I
+    int farw[4][4];            // wave w holds such a channel of sub-block I
   };
 
   __device__ static void run(const VgChunkPrepArgs& p, Smem& sm) {
@@ -185,13 +190,27 @@ struct VgPrep {
         sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(qq + kNormEps) : 0.f;
       }
     }
+    int farbits = 0;
     if (tid < DK) {
-      float g = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < L; ++t) {
-        g += sm.valid[t] * sm.u.r.gam[t * GS + tid];
-        sm.u.r.gam[t * GS + tid] = g;
+      float x[L];
+#pragma unroll
+      for (int t = 0; t < L; ++t) x[t] = sm.valid[t] * sm.u.r.gam[t * GS + tid];
+#pragma unroll
+      for (int t = 1; t < L; ++t) x[t] += x[t - 1];
+#pragma unroll
+      for (int t = 0; t < L; ++t) sm.u.r.gam[t * GS + tid] = x[t];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const float gc = I == 0 ? 0.f : x[16 * I - 1];
+        const int f = gc - x[16 * I + 15] > kDiagSpan ? 1 : 0;
+        sm.far[I][tid] = static_cast<unsigned char>(f);
+        farbits |= f << I;
       }
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const unsigned long long m = __ballot((farbits >> I) & 1);
+      if (l == 0) sm.farw[I][w] = m != 0;
     }
     __syncthreads();
 
@@ -234,8 +253,45 @@ struct VgPrep {
       }
     }
 
-    // ---- the diagonal sub-blocks in fp32: task (block I, 4x4 tile, 32
-    // channels); raw-row products, scaled by the norms when summed
+    // ---- the diagonal sub-blocks: wave w takes sub-block w on MFMA with the
+    // split at c = 16 w - 1 (G_{-1} = 0) over the channels that decay by at
+    // most e^kDiagSpan inside it (both factors then stay in the normal range);
+    // the other channels in fp32 below
+    {
+      const int b0 = 16 * w, ta = b0 + lr;
+      const float rkt = sm.rk[ta], rqt = sm.rq[ta];
+      f32x4 da = f4zero(), dpq = f4zero();
+#pragma unroll
+      for (int kt = 0; kt < DK / 32; ++kt) {
+        const int i0 = 32 * kt + 8 * lg;
+        float kf[8], qf[8];
+        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[ta * RS + i0]), kf);
+        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[ta * RS + i0]), qf);
+        float ka[8], kb[8], qa[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float gcx = w == 0 ? 0.f : sm.u.r.gam[(b0 - 1) * GS + i0 + x];
+          const float gx = sm.u.r.gam[ta * GS + i0 + x];
+          const bool near = sm.far[w][i0 + x] == 0;
+          const float dn = near ? __expf(gx - gcx) : 0.f, up = near ? __expf(gcx - gx) : 0.f;
+          ka[x] = kf[x] * rkt * dn;
+          qa[x] = qf[x] * rqt * dn;
+          kb[x] = kf[x] * rkt * up;
+        }
+        const bf16x8 akb = as_bf16x8(pack8(ka)), aqb = as_bf16x8(pack8(qa)), bkb = as_bf16x8(pack8(kb));
+        // the B operand is row s = ta of the same sub-block: each lane holds both
+        da = mfma16(akb, bkb, da);
+        dpq = mfma16(aqb, bkb, dpq);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sm.dg[w][0][4 * lg + r][lr] = da[r];
+        sm.dg[w][1][4 * lg + r][lr] = dpq[r];
+      }
+    }
+
+    // ---- ... and in fp32 for the far channels: task (block I, 4x4 tile,
+    // slice of the channels); raw-row products, scaled by the norms when summed
     if (tid < NTASK) {
       const int sl = tid % NSL, rest = tid / NSL, I = rest / 10, ti = rest % 10;
       const int tt = tile_t(ti), uu = tile_u(ti);
@@ -244,7 +300,9 @@ struct VgPrep {
 #pragma unroll
       for (int x = 0; x < 16; ++x) pa[x] = pp[x] = 0.f;
       const bool split = tt > uu;  // different 4-step groups: split at the end of ub's group
-      for (int i = 32 * sl; i < 32 * sl + 32; ++i) {
+      const bool any = sm.farw[I][0] | sm.farw[I][1] | sm.farw[I][2] | sm.farw[I][3];
+      for (int i = sl; i < (any ? DK : 0); i += NSL) {  // interleaved: adjacent lanes read adjacent channels
+        if (!sm.far[I][i]) continue;
         float gt[4], gu[4], kt_[4], qt_[4], ku[4];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -289,7 +347,7 @@ struct VgPrep {
       }
     }
 
-    // ---- the pre-scaled rows: forward Kb, Kh, Qb ([t][i]); backward Kh and
+    // ---- the pre-scaled rows: Kb, Kh ([t][i]); forward Qb ([t][i]), backward
     // Kb^T, Qb^T ([i][t]); and the chunk scalars (beta, e^{G_L})
     {
       const size_t rowbase = cidx * L * DK;
@@ -309,10 +367,8 @@ struct VgPrep {
         }
         const size_t o = rowbase + static_cast<size_t>(t) * DK + i0;
         *reinterpret_cast<uint4*>(p.cb.Kh + o) = pack8(kh);
-        if (!bwd) {
-          *reinterpret_cast<uint4*>(p.cb.Kb + o) = pack8(kf);
-          *reinterpret_cast<uint4*>(p.cb.Qb + o) = pack8(qf);
-        }
+        *reinterpret_cast<uint4*>(p.cb.Kb + o) = pack8(kf);
+        if (!bwd) *reinterpret_cast<uint4*>(p.cb.Qb + o) = pack8(qf);
       }
       if (bwd) {
         for (int u = tid; u < DK * L / 8; u += NT) {
@@ -374,8 +430,8 @@ struct VgPrep {
           av += sm.dp[(rest * NSL + sl) * 32 + x];
           pv += sm.dp[(rest * NSL + sl) * 32 + 16 + x];
         }
-        av = s < t ? av * sm.rk[t] * sm.rk[s] : 0.f;
-        pv = s <= t ? pv * sm.rq[t] * sm.rk[s] : 0.f;
+        av = s < t ? sm.dg[bi][0][t & 15][s & 15] + av * sm.rk[t] * sm.rk[s] : 0.f;
+        pv = s <= t ? sm.dg[bi][1][t & 15][s & 15] + pv * sm.rq[t] * sm.rk[s] : 0.f;
       }
       const float bs = sm.beta[s];
       nf[t * SP + s] = av * bs;
@@ -416,159 +472,76 @@ __global__ void __launch_bounds__(NT) vg_chunk_prep_kernel(VgChunkPrepArgs p) {
 
 // ------------------------------------------------------------ gradient pass
 
+// vg_chunk_x: X = Tx (V - Kb H) from the fp32 checkpoint H, then
+// dP = lower(dO X^T) diag(beta), dA = -strictlower(Ehat X^T) diag(beta) and
+// dbeta_t = eps_t . X_t.  Writes X, dP, dA (bf16) and dbeta.  Wave w takes
+// steps 16 w .. 16 w + 15.
 template <int DK, int DV>
-struct VgGrad {
-  static constexpr int NV = DV / 32;    // 32-column k-steps over Dv
-  static constexpr int NVT = DV / 16;   // 16-column tiles of Dv
-  static constexpr int NCT = DK / 16;   // 16-channel tiles
-  static constexpr int GS = DK + 4;     // fp32 row stride of Gamma
-  static constexpr int RS = DK + 8;     // bf16 row stride of k / q rows and H^T
-  static constexpr int TS = L + 8;      // bf16 row stride of the L-wide tiles
-  static constexpr int XS = DV + 8;     // bf16 row stride of X
-  static constexpr int AS = 17;         // fp32 row stride of the per-tile sums
-  static constexpr int NLD = L * DK / 8 / NT;
-  static constexpr int NLG = L * DK / 4 / NT;
+struct VgX {
+  static constexpr int NV = DV / 32;
+  static constexpr int NVT = DV / 16;
+  static constexpr int RS = DK + 8;  // bf16 row stride of H^T
+  static constexpr int TS = L + 8;   // bf16 row stride of the L-wide tiles
+  static constexpr int XS = DV + 8;  // bf16 row stride of X
   static constexpr int HVI = DV * RS > L * XS ? DV * RS : L * XS;
-  struct PhaseA {
-    bf16 hvi[HVI];     // H^T [v][i] (bf16); X later takes its place
-    bf16 rT[DV * TS];  // R^T [v][s]
-    bf16 txs[L * TS];  // Tx [t][s]
-  };
-  struct PhaseC {
-    bf16 xs[L * XS];       // X [t][v]
-    bf16 qrow[L * RS];     // raw q rows
-    bf16 dP[L * TS];       // dP [t][s]
-    bf16 dA[L * TS];       // dA [t][s]
-    float acc[3 * L * AS]; // per tile: dq, dkR (then dkn), dkW (then dlg), [t][16 channels]
-  };
-  union U {
-    PhaseA a;
-    PhaseC c;
-  };
+  static constexpr int RTN = (DV > L ? DV : L) * TS;
   struct Smem {
-    alignas(16) float gam[L * GS];
-    alignas(16) bf16 krow[L * RS];
-    alignas(16) U u;
-    float rk[L], rq[L], beta[L], valid[L];
-    float rdot[4][16], rdh[16];
+    alignas(16) bf16 hvi[HVI];  // H^T [v][i]; X [t][v] takes its place
+    alignas(16) bf16 rT[RTN];   // R^T [v][s]; dP [t][s] later
+    alignas(16) bf16 txs[L * TS];  // Tx [t][s]; dA [t][s] later
+    float beta[L];
   };
 
   __device__ static void run(const VgChunkGradArgs& p, Smem& sm) {
     const Dims& d = p.d;
     const int c = blockIdx.x, bh = blockIdx.y;
-    const int G = d.G(), NC = d.nchunk();
-    const int b = bh / d.Hv, h = bh % d.Hv, j = h / G;
+    const int NC = d.nchunk();
+    const int b = bh / d.Hv, h = bh % d.Hv;
     const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const size_t qk0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;
-    const uint32_t qk_row = d.Hk * DK;
-    const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
-    const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
-    const float* lgc = p.lg + ((static_cast<size_t>(b) * d.T + t0) * d.Hv + h) * DK;
-    const uint32_t lg_row = d.Hv * DK;
-    const size_t vrow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hv + h;  // row of step t0 in [B,T,Hv]
+    const size_t vrow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hv + h;
     const size_t cidx = static_cast<size_t>(bh) * NC + c;
     const float* H = c == 0 ? (p.state0 ? p.state0 + static_cast<size_t>(bh) * DK * DV : nullptr)
                             : p.ckpt + (static_cast<size_t>(c - 1) * d.B * d.Hv + bh) * DK * DV;
-    const bf16* dHp = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + bh) * DK * DV;
-    bf16* hvi = sm.u.a.hvi;
-    bf16* rT = sm.u.a.rT;
-    bf16* txs = sm.u.a.txs;
+    bf16* xs = sm.hvi;
+    bf16* dPs = sm.rT;
+    bf16* dAs = sm.txs;
 
-    // ---- A0: k and lg rows, beta, H^T (bf16), Tx
+    // ---- H^T (bf16), Tx, beta
+    for (int u = tid; u < DK * DV / 4; u += NT) {
+      const int i = u / (DV / 4), v4 = 4 * (u % (DV / 4));
+      const float4 x = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(i) * DV + v4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      sm.hvi[(v4 + 0) * RS + i] = bf16_of(x.x);
+      sm.hvi[(v4 + 1) * RS + i] = bf16_of(x.y);
+      sm.hvi[(v4 + 2) * RS + i] = bf16_of(x.z);
+      sm.hvi[(v4 + 3) * RS + i] = bf16_of(x.w);
+    }
     {
-      uint4 kv[NLD];
-      float4 gv[NLG];
-#pragma unroll
-      for (int e = 0; e < NLD; ++e) {
-        const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-        kv[e] = *reinterpret_cast<const uint4*>(kc + static_cast<uint32_t>(min(t, tl)) * qk_row + i8);
-      }
-#pragma unroll
-      for (int e = 0; e < NLG; ++e) {
-        const int u = tid + e * NT, t = u / (DK / 4), i4 = 4 * (u % (DK / 4));
-        gv[e] = *reinterpret_cast<const float4*>(lgc + static_cast<uint32_t>(min(t, tl)) * lg_row + i4);
-      }
-      if (w == 0) {
-        const int t = min(l, tl);
-        const float bv = to_f32(static_cast<const bf16*>(p.b)[vrow0 + static_cast<size_t>(t) * d.Hv]);
-        const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.b,
-                                    p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-        const bool valid = l < Lc && (p.mask == nullptr ||
-                                      __builtin_amdgcn_raw_buffer_load_b8(rm, static_cast<uint32_t>(b * d.T + t0 + t), 0, 0) != 0);
-        sm.beta[l] = valid ? sigmoid_f(bv) : 0.f;
-        sm.valid[l] = valid ? 1.f : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < NLD; ++e) {
-        const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-        *reinterpret_cast<uint4*>(&sm.krow[t * RS + i8]) = kv[e];
-      }
-#pragma unroll
-      for (int e = 0; e < NLG; ++e) {
-        const int u = tid + e * NT, t = u / (DK / 4), i4 = 4 * (u % (DK / 4));
-        *reinterpret_cast<float4*>(&sm.gam[t * GS + i4]) = gv[e];
-      }
-      for (int u = tid; u < DK * DV / 4; u += NT) {
-        const int i = u / (DV / 4), v4 = 4 * (u % (DV / 4));
-        const float4 x = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(i) * DV + v4)
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
-        hvi[(v4 + 0) * RS + i] = bf16_of(x.x);
-        hvi[(v4 + 1) * RS + i] = bf16_of(x.y);
-        hvi[(v4 + 2) * RS + i] = bf16_of(x.z);
-        hvi[(v4 + 3) * RS + i] = bf16_of(x.w);
-      }
       const bf16* txg = p.cb.Tx + cidx * L * L;
       for (int u = tid; u < L * L / 8; u += NT) {
         const int t = u >> 3, s8 = 8 * (u & 7);
-        *reinterpret_cast<uint4*>(&txs[t * TS + s8]) = *reinterpret_cast<const uint4*>(txg + t * L + s8);
+        *reinterpret_cast<uint4*>(&sm.txs[t * TS + s8]) = *reinterpret_cast<const uint4*>(txg + t * L + s8);
       }
+      if (tid < L) sm.beta[tid] = p.cb.vsc[cidx * VSC_ROWS * L + VSC_BETA * L + tid];
     }
     __syncthreads();
 
-    // ---- A1: k norms; Gamma
-    {
-      const int t = tid >> 2, part = tid & 3;
-      float kk = 0.f;
-#pragma unroll
-      for (int e = 0; e < DK / 32; ++e) {
-        float kf[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.krow[t * RS + (DK / 4) * part + 8 * e]), kf);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) kk = fmaf(kf[x], kf[x], kk);
-      }
-      kk = quad_sum(kk);
-      if (part == 0) sm.rk[t] = t < Lc ? 1.f / sqrtf(kk + kNormEps) : 0.f;
-    }
-    if (tid < DK) {
-      float g = 0.f;
-#pragma unroll 8
-      for (int t = 0; t < L; ++t) {
-        g += sm.valid[t] * sm.gam[t * GS + tid];
-        sm.gam[t * GS + tid] = g;
-      }
-    }
-    __syncthreads();
-
-    // ---- A2: R^T = V^T - H^T Kb^T (wave w: steps 16 w .. + 15)
+    // ---- R^T = V^T - H^T Kb^T (Kb rows from the prep: zero past the end)
     {
       const int tb = 16 * w + lr;
-      const float rkt = sm.rk[tb];
+      const bf16* kbr = p.cb.Kb + (cidx * L + tb) * DK;
       f32x4 acc[NVT];
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) acc[vt] = f4zero();
 #pragma unroll
       for (int kt = 0; kt < DK / 32; ++kt) {
         const int i0 = 32 * kt + 8 * lg;
-        float kf[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.krow[tb * RS + i0]), kf);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) kf[x] *= rkt * __expf(sm.gam[tb * GS + i0 + x]);
-        const bf16x8 kb = as_bf16x8(pack8(kf));
+        const bf16x8 kb = as_bf16x8(*reinterpret_cast<const uint4*>(kbr + i0));
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt)
-          acc[vt] = mfma16(load_bf16x8(&hvi[(16 * vt + lr) * RS + i0]), kb, acc[vt]);
+          acc[vt] = mfma16(load_bf16x8(&sm.hvi[(16 * vt + lr) * RS + i0]), kb, acc[vt]);
       }
       const bf16* vg = static_cast<const bf16*>(p.v) + (vrow0 + static_cast<size_t>(min(tb, tl)) * d.Hv) * DV;
 #pragma unroll
@@ -577,23 +550,22 @@ struct VgGrad {
         const float vv[4] = {__uint_as_float(v4.x << 16), __uint_as_float(v4.x & 0xffff0000u),
                              __uint_as_float(v4.y << 16), __uint_as_float(v4.y & 0xffff0000u)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rT[(16 * vt + 4 * lg + r) * TS + tb] = bf16_of(vv[r] - acc[vt][r]);
+        for (int r = 0; r < 4; ++r) sm.rT[(16 * vt + 4 * lg + r) * TS + tb] = bf16_of(vv[r] - acc[vt][r]);
       }
     }
     __syncthreads();
 
-    // ---- A3: X = Tx R (wave w: steps 16 w .. + 15), into X's place (H^T is dead)
-    bf16* xs = sm.u.c.xs;
+    // ---- X = Tx R, into H^T's place
     {
       f32x4 xa[NVT];
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) xa[vt] = f4zero();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = load_bf16x8(&txs[(16 * w + lr) * TS + 32 * kk + 8 * lg]);
+        const bf16x8 a = load_bf16x8(&sm.txs[(16 * w + lr) * TS + 32 * kk + 8 * lg]);
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt)
-          xa[vt] = mfma16(a, load_bf16x8(&rT[(16 * vt + lr) * TS + 32 * kk + 8 * lg]), xa[vt]);
+          xa[vt] = mfma16(a, load_bf16x8(&sm.rT[(16 * vt + lr) * TS + 32 * kk + 8 * lg]), xa[vt]);
       }
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt)
@@ -602,50 +574,34 @@ struct VgGrad {
     }
     __syncthreads();
 
-    // ---- B: q rows; dO, Ehat, X and diag(beta) X rows of this wave as
-    // MFMA operands; dO X^T, Ehat X^T -> dP, dA; dbeta
-    bf16* qrow = sm.u.c.qrow;
-    bf16* dPm = sm.u.c.dP;
-    bf16* dAm = sm.u.c.dA;
-    float* acc = sm.u.c.acc;
-#pragma unroll
-    for (int e = 0; e < NLD; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-      *reinterpret_cast<uint4*>(&qrow[t * RS + i8]) =
-          *reinterpret_cast<const uint4*>(qc + static_cast<uint32_t>(min(t, tl)) * qk_row + i8);
-    }
-    bf16x8 dOf[NV], Ef[NV], bXf[NV];
+    // ---- dO X^T, Ehat X^T -> dP, dA (into R^T's and Tx's places); dbeta; X out
     {
       const int ta = 16 * w + lr;
       const size_t ro = (vrow0 + static_cast<size_t>(min(ta, tl)) * d.Hv) * DV;
       const bf16* dOg = static_cast<const bf16*>(p.dO) + ro;
       const bf16* Eg = static_cast<const bf16*>(p.dv) + ro;
-      const float bt = sm.beta[ta];
-#pragma unroll
-      for (int kv = 0; kv < NV; ++kv) {
-        dOf[kv] = as_bf16x8(*reinterpret_cast<const uint4*>(dOg + 32 * kv + 8 * lg));
-        Ef[kv] = as_bf16x8(*reinterpret_cast<const uint4*>(Eg + 32 * kv + 8 * lg));
-        bXf[kv] = scale8(load_bf16x8(&xs[ta * XS + 32 * kv + 8 * lg]), bt);
-      }
       f32x4 g1[4], g2[4];
 #pragma unroll
       for (int st = 0; st < 4; ++st) g1[st] = g2[st] = f4zero();
 #pragma unroll
-      for (int kv = 0; kv < NV; ++kv)
+      for (int kv = 0; kv < NV; ++kv) {
+        const bf16x8 dof = as_bf16x8(*reinterpret_cast<const uint4*>(dOg + 32 * kv + 8 * lg));
+        const bf16x8 ef = as_bf16x8(*reinterpret_cast<const uint4*>(Eg + 32 * kv + 8 * lg));
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           const bf16x8 bx = load_bf16x8(&xs[(16 * st + lr) * XS + 32 * kv + 8 * lg]);
-          g1[st] = mfma16(dOf[kv], bx, g1[st]);
-          g2[st] = mfma16(Ef[kv], bx, g2[st]);
+          g1[st] = mfma16(dof, bx, g1[st]);
+          g2[st] = mfma16(ef, bx, g2[st]);
         }
+      }
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * w + 4 * lg + r, s = 16 * st + lr;
           const float bs = sm.beta[s];
-          dPm[t * TS + s] = bf16_of(s <= t ? g1[st][r] * bs : 0.f);
-          dAm[t * TS + s] = bf16_of(s < t ? -g2[st][r] * bs : 0.f);
+          dPs[t * TS + s] = bf16_of(s <= t ? g1[st][r] * bs : 0.f);
+          dAs[t * TS + s] = bf16_of(s < t ? -g2[st][r] * bs : 0.f);
         }
     }
     {  // dbeta_t = eps_t . X_t (four lanes per step)
@@ -664,47 +620,278 @@ struct VgGrad {
       sdot = quad_sum(sdot);
       if (part == 0 && t < Lc) p.pdb[vrow0 + static_cast<size_t>(t) * d.Hv] = sdot;
     }
-    __syncthreads();
-    {  // q norms (with 1/sqrt(Dk))
-      const int t = tid >> 2, part = tid & 3;
-      float qq = 0.f;
-#pragma unroll
-      for (int e = 0; e < DK / 32; ++e) {
-        float qf[8];
-        unpack8(*reinterpret_cast<const uint4*>(&qrow[t * RS + (DK / 4) * part + 8 * e]), qf);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) qq = fmaf(qf[x], qf[x], qq);
+    {
+      bf16* xg = p.X + cidx * L * DV;
+      for (int u = tid; u < L * DV / 8; u += NT) {
+        const int t = u / (DV / 8), v8 = 8 * (u % (DV / 8));
+        *reinterpret_cast<uint4*>(xg + t * DV + v8) = *reinterpret_cast<const uint4*>(&xs[t * XS + v8]);
       }
-      qq = quad_sum(qq);
-      if (part == 0) sm.rq[t] = t < Lc ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(qq + kNormEps) : 0.f;
+    }
+    __syncthreads();
+    {
+      bf16* pg = p.dPA + cidx * 2 * L * L;
+      for (int u = tid; u < 2 * L * L / 8; u += NT) {
+        const int m = u / (L * L / 8), r = u % (L * L / 8), t = r >> 3, s8 = 8 * (r & 7);
+        const bf16* src = m ? dAs : dPs;
+        *reinterpret_cast<uint4*>(pg + m * L * L + t * L + s8) = *reinterpret_cast<const uint4*>(&src[t * TS + s8]);
+      }
+    }
+  }
+};
+
+// vg_chunk_grad: the per-channel expansions for CH channels of one (chunk,
+// head).  Every global read of the workgroup is issued at its start (the
+// chunk's dP and dA, the CH channels of lg, k, q, H and dH', this wave's dO,
+// Ehat and diag(beta) X rows), so it waits on memory once; the rest runs from
+// LDS and registers.  Wave w takes the 16-step block w, in the matrix-core
+// output layout: lane (lr, lg) holds steps 16 w + 4 lg + r (r < 4) of channel
+// lr of the current 16-channel tile, as a row (dq, dkR: sums over the earlier
+// steps) and as a column (dkW: sums over the later steps).  The direct terms
+// and the parts off the diagonal blocks are MFMA products (the blocks before
+// w split at r = 16 w - 1, those after it at e = 16 w + 15), the diagonal
+// block too where its decays allow, else fp32 with the decays built step by
+// step.  The in-chunk suffix sums of dG run over r, the lanes of a block and
+// the blocks.  Gamma, k and q are held channel-major (the expansions read 8 or
+// 16 consecutive steps of one channel); the transposed operands of dP and dA
+// come from transposing LDS reads.
+template <int DK, int DV>
+struct VgG {
+  static constexpr int CH = kVgGradChannels;
+  static constexpr int NTL = CH / 16;  // 16-channel tiles per workgroup
+  static constexpr int NV = DV / 32;
+  static constexpr int GT = L + 4;     // fp32 row stride of the channel-major Gamma
+  static constexpr int KT = L + 8;     // bf16 row stride of the channel-major k, q
+  static constexpr int TS = L + 8;     // bf16 row stride of dP, dA
+  static constexpr int HS = DV + 4;    // fp32 row stride of H
+  static constexpr int DS = DV + 8;    // bf16 row stride of dH'
+  static constexpr int NPM = 2 * L * L / 8 / NT;      // 16-byte pieces of dP, dA per thread
+  static constexpr int NLG = L * CH / 4 / NT;         // of lg
+  static constexpr int NKQ = 2 * L * CH / 8 / NT;     // of k and q
+  static constexpr int NH = CH * DV / 4 / NT;         // of H (fp32)
+  static constexpr int NDHP = CH * DV / 8;             // pieces of dH'
+  static constexpr int NDH = (NDHP + NT - 1) / NT;    // of dH' per thread (the last may be idle)
+  static_assert(2 * L * L / 8 % NT == 0 && L * CH / 4 % NT == 0 && 2 * L * CH / 8 % NT == 0 &&
+                CH * DV / 4 % NT == 0, "whole pieces per thread");
+  struct Smem {
+    alignas(16) float gT[CH * GT];
+    alignas(16) bf16 kT[CH * KT];
+    alignas(16) bf16 qT[CH * KT];
+    alignas(16) bf16 dP[L * TS];
+    alignas(16) bf16 dA[L * TS];
+    alignas(16) float hs[CH * HS];
+    alignas(16) bf16 dhs[CH * DS];
+    alignas(16) float rk[L];
+    alignas(16) float rq[L];
+    float valid[L], beta[L];
+    float btot[4][16], rdot[4][16], rdh[16];
+  };
+
+  // 8 consecutive steps s0 .. s0 + 7 of a channel-major row: fp32 and bf16
+  __device__ static __forceinline__ void ld8f(const float* p, float (&f)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x, f[1] = a.y, f[2] = a.z, f[3] = a.w, f[4] = b.x, f[5] = b.y, f[6] = b.z, f[7] = b.w;
+  }
+  __device__ static __forceinline__ void ld8b(const bf16* p, float (&f)[8]) {
+    unpack8(*reinterpret_cast<const uint4*>(p), f);
+  }
+  // Rows t0 .. t0 + 7 of column c0 + lr of a row-major [t][s] tile (stride
+  // TS) as an MFMA operand (its transpose's row c0 + lr), by two transposing
+  // reads; t0 is this lane group's (t0 = base + 8 lg).
+  __device__ static __forceinline__ bf16x8 col8(const bf16* m, int t0, int c0, int lr) {
+    const uint2 lo = lds_read_tr16(&m[(t0 + (lr >> 2)) * TS + c0 + 4 * (lr & 3)]);
+    const uint2 hi = lds_read_tr16(&m[(t0 + 4 + (lr >> 2)) * TS + c0 + 4 * (lr & 3)]);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  }
+
+  // Workgroup n -> (chunk c, head bh, channel group cg).  The DK / CH groups
+  // of one (chunk, head) read the same dO, Ehat, X, dP and dA: they go to one
+  // XCD (workgroups are dealt to the 8 XCDs round-robin in launch order) one
+  // after another, so those reads hit that XCD's L2.  (chunk, head) pairs are
+  // dealt to the XCDs in turn; the grid is padded to a multiple of 8 of them.
+  __device__ static bool coords(const Dims& d, int& c, int& bh, int& cg) {
+    const int NG = DK / CH, NC = d.nchunk();
+    const int n = blockIdx.x, xcd = n & 7, m = n >> 3;
+    cg = m % NG;
+    const int pr = (m / NG) * 8 + xcd;
+    if (pr >= NC * d.B * d.Hv) return false;
+    c = pr % NC;
+    bh = pr / NC;
+    return true;
+  }
+
+  __device__ static void run(const VgChunkGradArgs& p, Smem& sm) {
+    const Dims& d = p.d;
+    int c, bh, cg;
+    if (!coords(d, c, bh, cg)) return;
+    const int G = d.G(), NC = d.nchunk();
+    const int b = bh / d.Hv, h = bh % d.Hv, j = h / G;
+    const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
+    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ch0 = cg * CH;
+    const size_t vrow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hv + h;
+    const size_t krow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;
+    const size_t cidx = static_cast<size_t>(bh) * NC + c;
+    const float* H = c == 0 ? (p.state0 ? p.state0 + static_cast<size_t>(bh) * DK * DV : nullptr)
+                            : p.ckpt + (static_cast<size_t>(c - 1) * d.B * d.Hv + bh) * DK * DV;
+    const bf16* dHp = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + bh) * DK * DV;
+
+    // ---- every global read, issued before any is used
+    uint4 pmv[NPM], kqv[NKQ], dhv[NDH];
+    float4 lgv[NLG], hv[NH];
+    bf16x8 dOf[NV], Ef[NV], bXf[NV];
+    {
+      const bf16* pg = p.dPA + cidx * 2 * L * L;
+#pragma unroll
+      for (int e = 0; e < NPM; ++e) pmv[e] = *reinterpret_cast<const uint4*>(pg + 8 * (tid + e * NT));
+#pragma unroll
+      for (int e = 0; e < NLG; ++e) {
+        const int u = tid + e * NT, t = u / (CH / 4), i4 = 4 * (u % (CH / 4));
+        lgv[e] = *reinterpret_cast<const float4*>(p.lg + (vrow0 + static_cast<size_t>(min(t, tl)) * d.Hv) * DK + ch0 + i4);
+      }
+#pragma unroll
+      for (int e = 0; e < NKQ; ++e) {
+        const int u = tid + e * NT, m = u / (L * CH / 8), r = u % (L * CH / 8), t = r / (CH / 8), i8 = 8 * (r % (CH / 8));
+        const bf16* src = static_cast<const bf16*>(m ? p.q : p.k) + (krow0 + static_cast<size_t>(min(t, tl)) * d.Hk) * DK;
+        kqv[e] = *reinterpret_cast<const uint4*>(src + ch0 + i8);
+      }
+#pragma unroll
+      for (int e = 0; e < NH; ++e) {
+        const int u = tid + e * NT, ch = u / (DV / 4), v4 = 4 * (u % (DV / 4));
+        hv[e] = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(ch0 + ch) * DV + v4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int e = 0; e < NDH; ++e) {  // clamped: a thread past the last piece reloads it
+        const int u = min(tid + e * NT, NDHP - 1), ch = u / (DV / 8), v8 = 8 * (u % (DV / 8));
+        dhv[e] = *reinterpret_cast<const uint4*>(dHp + static_cast<size_t>(ch0 + ch) * DV + v8);
+      }
+      const int ta = 16 * w + lr;
+      const size_t ro = (vrow0 + static_cast<size_t>(min(ta, tl)) * d.Hv) * DV;
+      const bf16* dOg = static_cast<const bf16*>(p.dO) + ro;
+      const bf16* Eg = static_cast<const bf16*>(p.dv) + ro;
+      const bf16* Xg = p.X + (cidx * L + ta) * DV;
+#pragma unroll
+      for (int kv = 0; kv < NV; ++kv) {
+        dOf[kv] = as_bf16x8(*reinterpret_cast<const uint4*>(dOg + 32 * kv + 8 * lg));
+        Ef[kv] = as_bf16x8(*reinterpret_cast<const uint4*>(Eg + 32 * kv + 8 * lg));
+        bXf[kv] = as_bf16x8(*reinterpret_cast<const uint4*>(Xg + 32 * kv + 8 * lg));
+      }
+      if (tid < L) {
+        const int t = tid;
+        const bool in = t < Lc;
+        const size_t kr = krow0 + static_cast<size_t>(min(t, tl)) * d.Hk;
+        sm.rk[t] = in ? p.s.rk[kr] : 0.f;
+        sm.rq[t] = in ? p.s.rq[kr] : 0.f;
+        const bool valid = in && (p.mask == nullptr || p.mask[static_cast<size_t>(b) * d.T + t0 + t] != 0);
+        sm.valid[t] = valid ? 1.f : 0.f;
+        sm.beta[t] = p.cb.vsc[cidx * VSC_ROWS * L + VSC_BETA * L + t];
+      }
+    }
+    // ---- into LDS (k, q and lg channel-major)
+#pragma unroll
+    for (int e = 0; e < NPM; ++e) {
+      const int u = tid + e * NT, m = u / (L * L / 8), r = u % (L * L / 8), t = r >> 3, s8 = 8 * (r & 7);
+      *reinterpret_cast<uint4*>(&(m ? sm.dA : sm.dP)[t * TS + s8]) = pmv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < NLG; ++e) {
+      const int u = tid + e * NT, t = u / (CH / 4), i4 = 4 * (u % (CH / 4));
+      sm.gT[(i4 + 0) * GT + t] = lgv[e].x;
+      sm.gT[(i4 + 1) * GT + t] = lgv[e].y;
+      sm.gT[(i4 + 2) * GT + t] = lgv[e].z;
+      sm.gT[(i4 + 3) * GT + t] = lgv[e].w;
+    }
+#pragma unroll
+    for (int e = 0; e < NKQ; ++e) {
+      const int u = tid + e * NT, m = u / (L * CH / 8), r = u % (L * CH / 8), t = r / (CH / 8), i8 = 8 * (r % (CH / 8));
+      bf16* dst = m ? sm.qT : sm.kT;
+      const uint32_t wv[4] = {kqv[e].x, kqv[e].y, kqv[e].z, kqv[e].w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        dst[(i8 + 2 * x) * KT + t] = __builtin_bit_cast(bf16, static_cast<uint16_t>(wv[x] & 0xffffu));
+        dst[(i8 + 2 * x + 1) * KT + t] = __builtin_bit_cast(bf16, static_cast<uint16_t>(wv[x] >> 16));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NH; ++e) {
+      const int u = tid + e * NT, ch = u / (DV / 4), v4 = 4 * (u % (DV / 4));
+      *reinterpret_cast<float4*>(&sm.hs[ch * HS + v4]) = hv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < NDH; ++e) {
+      const int u = min(tid + e * NT, NDHP - 1), ch = u / (DV / 8), v8 = 8 * (u % (DV / 8));
+      *reinterpret_cast<uint4*>(&sm.dhs[ch * DS + v8]) = dhv[e];  // a duplicate writes the same bytes
+    }
+    __syncthreads();
+    // ---- Gamma (a running sum per channel: 16 lanes of 4 steps each, a
+    // prefix over the lanes); diag(beta) X
+    for (int u = tid; u < CH * 16; u += NT) {
+      const int ch = u >> 4, seg = u & 15;
+      float* g = &sm.gT[ch * GT + 4 * seg];
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = sm.valid[4 * seg + r] * g[r];
+      x[1] += x[0];
+      x[2] += x[1];
+      x[3] += x[2];
+      float run = x[3];
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float y = __shfl_up(run, off, 16);
+        if (seg >= off) run += y;
+      }
+      const float before = run - x[3];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[r] = x[r] + before;
+    }
+    {
+      const float bt = sm.beta[16 * w + lr];
+#pragma unroll
+      for (int kv = 0; kv < NV; ++kv) bXf[kv] = scale8(bXf[kv], bt);
     }
     __syncthreads();
 
-    float* acc0 = acc;
-    float* acc1 = acc + L * AS;
-    float* acc2 = acc + 2 * L * AS;
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int i0c = 16 * ct;
-      // ---- C1: dQb, dKb, dKh for this wave's steps and channels i0c .. + 15;
-      // their direct terms; the row sums of Kh dKh; <dH', H> (wave 0)
+    const int b0 = 16 * w;        // this wave's block
+    const int tr0 = b0 + 4 * lg;  // this lane's first step
+    float dlgv[NTL][4], dqv[NTL][4], dknv[NTL][4];
+
+#pragma unroll
+    for (int tile = 0; tile < NTL; ++tile) {
+      const int cl = 16 * tile + lr;  // channel within the workgroup
+      const float* gch = &sm.gT[cl * GT];
+      const bf16* kch = &sm.kT[cl * KT];
+      const bf16* qch = &sm.qT[cl * KT];
+      float gt[4], knt[4], qst[4];
       {
-        const int ic = i0c + lr;
+        const float4 g4 = *reinterpret_cast<const float4*>(&gch[tr0]);
+        gt[0] = g4.x, gt[1] = g4.y, gt[2] = g4.z, gt[3] = g4.w;
+        const uint2 k4 = *reinterpret_cast<const uint2*>(&kch[tr0]);
+        const uint2 q4 = *reinterpret_cast<const uint2*>(&qch[tr0]);
+        const float4 rk4 = *reinterpret_cast<const float4*>(&sm.rk[tr0]);
+        const float4 rq4 = *reinterpret_cast<const float4*>(&sm.rq[tr0]);
+        knt[0] = __uint_as_float(k4.x << 16) * rk4.x;
+        knt[1] = __uint_as_float(k4.x & 0xffff0000u) * rk4.y;
+        knt[2] = __uint_as_float(k4.y << 16) * rk4.z;
+        knt[3] = __uint_as_float(k4.y & 0xffff0000u) * rk4.w;
+        qst[0] = __uint_as_float(q4.x << 16) * rq4.x;
+        qst[1] = __uint_as_float(q4.x & 0xffff0000u) * rq4.y;
+        qst[2] = __uint_as_float(q4.y << 16) * rq4.z;
+        qst[3] = __uint_as_float(q4.y & 0xffff0000u) * rq4.w;
+      }
+      const float gL = gch[L - 1];
+
+      // direct terms: dQb = dO H^T, dKb = -Ehat H^T, dKh = diag(beta) X dH'^T
+      float dq[4], dkr[4], dkw[4];
+      {
         f32x4 aq = f4zero(), ak = f4zero(), ah = f4zero();
         float rh = 0.f;
 #pragma unroll
         for (int kv = 0; kv < NV; ++kv) {
           const int v0 = 32 * kv + 8 * lg;
           float hf[8];
-          if (H) {
-            const float4 h0 = *reinterpret_cast<const float4*>(H + static_cast<size_t>(ic) * DV + v0);
-            const float4 h1 = *reinterpret_cast<const float4*>(H + static_cast<size_t>(ic) * DV + v0 + 4);
-            hf[0] = h0.x, hf[1] = h0.y, hf[2] = h0.z, hf[3] = h0.w;
-            hf[4] = h1.x, hf[5] = h1.y, hf[6] = h1.z, hf[7] = h1.w;
-          } else {
-#pragma unroll
-            for (int x = 0; x < 8; ++x) hf[x] = 0.f;
-          }
-          const uint4 dhu = *reinterpret_cast<const uint4*>(dHp + static_cast<size_t>(ic) * DV + v0);
+          ld8f(&sm.hs[cl * HS + v0], hf);
+          const uint4 dhu = *reinterpret_cast<const uint4*>(&sm.dhs[cl * DS + v0]);
           const bf16x8 hb = as_bf16x8(pack8(hf));
           aq = mfma16(dOf[kv], hb, aq);
           ak = mfma16(Ef[kv], hb, ak);
@@ -716,16 +903,14 @@ struct VgGrad {
             for (int x = 0; x < 8; ++x) rh = fmaf(df[x], hf[x], rh);
           }
         }
-        const float gL = sm.gam[(L - 1) * GS + ic];
         float rd = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * w + 4 * lg + r;
-          const float g = sm.gam[t * GS + ic], eg = __expf(g), el = __expf(gL - g);
-          acc0[t * AS + lr] = eg * aq[r];
-          acc1[t * AS + lr] = -eg * ak[r];
-          acc2[t * AS + lr] = el * ah[r];
-          rd = fmaf(to_f32(sm.krow[t * RS + ic]) * sm.rk[t] * el, ah[r], rd);
+          const float eg = __expf(gt[r]), el = __expf(gL - gt[r]);
+          dq[r] = eg * aq[r];
+          dkr[r] = -eg * ak[r];
+          dkw[r] = el * ah[r];
+          rd = fmaf(knt[r], dkw[r], rd);  // Kh dKh = kn e^{G_L - G} dKh
         }
         rd += __shfl_xor(rd, 16);
         rd += __shfl_xor(rd, 32);
@@ -736,175 +921,240 @@ struct VgGrad {
           if (lg == 0) sm.rdh[lr] = rh;
         }
       }
-      __syncthreads();
 
-      // ---- C2: the diagonal sub-blocks in fp32 (every wave: lanes = 16
-      // channels x 4 blocks; wave w takes the steps w, w + 4, ... of its block,
-      // as rows and as columns) ...
-      float dqd[4], dkrd[4], dkwd[4];
-      {
-        const int il = l & 15, I = l >> 4, b0 = 16 * I, icd = i0c + il;
-        float Gv[16], kn[16], qs[16], gg[16];
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          Gv[x] = sm.gam[(b0 + x) * GS + icd];
-          kn[x] = to_f32(sm.krow[(b0 + x) * RS + icd]) * sm.rk[b0 + x];
-          qs[x] = to_f32(qrow[(b0 + x) * RS + icd]) * sm.rq[b0 + x];
-        }
-        gg[0] = 1.f;
-#pragma unroll
-        for (int x = 1; x < 16; ++x) gg[x] = __expf(Gv[x] - Gv[x - 1]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int tt = w + 4 * m;  // uniform
-          const bf16* prow = &dPm[(b0 + tt) * TS + b0];
-          const bf16* arow = &dAm[(b0 + tt) * TS + b0];
-          float e = 1.f, sq = 0.f, sr = 0.f;
-#pragma unroll
-          for (int s = 15; s >= 0; --s) {
-            if (s > tt) continue;
-            if (s < tt) e *= gg[s + 1];  // e = e^{G_tt - G_s}
-            const float ke = kn[s] * e;
-            sq = fmaf(to_f32(prow[s]), ke, sq);
-            sr = fmaf(to_f32(arow[s]), ke, sr);
-          }
-          dqd[m] = sq;
-          dkrd[m] = sr;
-          e = 1.f;
-          float sw = 0.f;
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            if (t < tt) continue;
-            if (t > tt) e *= gg[t];  // e = e^{G_t - G_tt}
-            sw = fmaf(fmaf(to_f32(dPm[(b0 + t) * TS + b0 + tt]), qs[t], to_f32(dAm[(b0 + t) * TS + b0 + tt]) * kn[t]), e, sw);
-          }
-          dkwd[m] = sw;
-        }
-      }
-      // ... and off the diagonal on MFMA (wave I = 1 .. 3: rows of block I
-      // against the blocks before it, split at r = 16 I - 1; rows of block
-      // J = I - 1 against the blocks after it, split at e = 16 J + 15)
+      // rows of block w against the blocks before it (split at r0 = 16 w - 1)
       if (w >= 1) {
-        const int I = w, J = I - 1, ic = i0c + lr;
-        const int r0 = 16 * I - 1, e0 = 16 * J + 15;
-        const float Gr = sm.gam[r0 * GS + ic], Ge = sm.gam[e0 * GS + ic];
-        f32x4 oq = f4zero(), orr = f4zero(), ow = f4zero();
+        const int r0 = b0 - 1;
+        const float Gr = gch[r0];
+        f32x4 oq = f4zero(), orr = f4zero();
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          if (32 * kk >= 16 * I) continue;  // uniform
+          if (32 * kk >= b0) continue;  // uniform
+          const int s0 = 32 * kk + 8 * lg;
+          float kf[8], gf[8], rkf[8];
+          ld8b(&kch[s0], kf);
+          ld8f(&gch[s0], gf);
+          ld8f(&sm.rk[s0], rkf);
           float y[8];
 #pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int s = 32 * kk + 8 * lg + x;
-            y[x] = s < 16 * I ? to_f32(sm.krow[s * RS + ic]) * sm.rk[s] * __expf(Gr - sm.gam[s * GS + ic]) : 0.f;
-          }
+          for (int x = 0; x < 8; ++x) y[x] = s0 + x < b0 ? kf[x] * rkf[x] * __expf(Gr - gf[x]) : 0.f;
           const bf16x8 yb = as_bf16x8(pack8(y));
-          oq = mfma16(load_bf16x8(&dPm[(16 * I + lr) * TS + 32 * kk + 8 * lg]), yb, oq);
-          orr = mfma16(load_bf16x8(&dAm[(16 * I + lr) * TS + 32 * kk + 8 * lg]), yb, orr);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          if (16 * I + 32 * kk >= L) continue;  // uniform
-          float yq[8], yk[8], ap[8], aa[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int t = 16 * I + 32 * kk + 8 * lg + x;
-            const bool in = t < L;
-            const int tc = in ? t : L - 1;
-            const float ee = in ? __expf(sm.gam[tc * GS + ic] - Ge) : 0.f;
-            yq[x] = to_f32(qrow[tc * RS + ic]) * sm.rq[tc] * ee;
-            yk[x] = to_f32(sm.krow[tc * RS + ic]) * sm.rk[tc] * ee;
-            ap[x] = to_f32(dPm[tc * TS + 16 * J + lr]);
-            aa[x] = to_f32(dAm[tc * TS + 16 * J + lr]);
-          }
-          ow = mfma16(as_bf16x8(pack8(ap)), as_bf16x8(pack8(yq)), ow);
-          ow = mfma16(as_bf16x8(pack8(aa)), as_bf16x8(pack8(yk)), ow);
+          oq = mfma16(load_bf16x8(&sm.dP[(b0 + lr) * TS + s0]), yb, oq);
+          orr = mfma16(load_bf16x8(&sm.dA[(b0 + lr) * TS + s0]), yb, orr);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * I + 4 * lg + r, s = 16 * J + 4 * lg + r;
-          const float sc = __expf(sm.gam[t * GS + ic] - Gr), sc2 = __expf(Ge - sm.gam[s * GS + ic]);
-          acc0[t * AS + lr] += sc * oq[r];
-          acc1[t * AS + lr] += sc * orr[r];
-          acc2[s * AS + lr] += sc2 * ow[r];
+          const float sc = __expf(gt[r] - Gr);
+          dq[r] = fmaf(sc, oq[r], dq[r]);
+          dkr[r] = fmaf(sc, orr[r], dkr[r]);
         }
       }
-      __syncthreads();
-      {
-        const int il = l & 15, b0 = 16 * (l >> 4);
+      // columns of block w against the blocks after it (split at e0 = 16 w + 15)
+      if (w <= 2) {
+        const int e0 = b0 + 15;
+        const float Ge = gch[e0];
+        f32x4 ow = f4zero();
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int t = b0 + w + 4 * m;
-          acc0[t * AS + il] += dqd[m];
-          acc1[t * AS + il] += dkrd[m];
-          acc2[t * AS + il] += dkwd[m];
+        for (int kk = 0; kk < 2; ++kk) {
+          if (b0 + 16 + 32 * kk >= L) continue;  // uniform
+          const int tbase = b0 + 16 + 32 * kk;
+          const int tb = tbase + 8 * lg;
+          const int tc = tb < L ? tb : L - 8;  // lanes past the end read in range, zeroed below
+          float kf[8], qf[8], gf[8], rkf[8], rqf[8];
+          ld8b(&kch[tc], kf);
+          ld8b(&qch[tc], qf);
+          ld8f(&gch[tc], gf);
+          ld8f(&sm.rk[tc], rkf);
+          ld8f(&sm.rq[tc], rqf);
+          float yq[8], yk[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const float ee = tb < L ? __expf(gf[x] - Ge) : 0.f;
+            yq[x] = qf[x] * rqf[x] * ee;
+            yk[x] = kf[x] * rkf[x] * ee;
+          }
+          // dP^T, dA^T rows b0 + lr over this group's steps tc .. tc + 7
+          const bf16x8 ap = col8(sm.dP, tc, b0, lr), aa = col8(sm.dA, tc, b0, lr);
+          const bool use = tb < L;
+          ow = mfma16(use ? ap : zero8(), as_bf16x8(pack8(yq)), ow);
+          ow = mfma16(use ? aa : zero8(), as_bf16x8(pack8(yk)), ow);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dkw[r] = fmaf(__expf(Ge - gt[r]), ow[r], dkw[r]);
+      }
+      // the diagonal block.  Where every channel of the tile decays by less
+      // than e^60 inside the block, on MFMA with the split at c = 16 w - 1,
+      // the step before the block (G_{-1} = 0): e^{G_t - G_s} =
+      // e^{G_t - G_c} e^{G_c - G_s}, the second factor at most e^60, both in
+      // the normal range of fp32 and bf16.  Else in fp32: rows tr0 + r (over
+      // s <= t) and columns tr0 + r (over t >= s), decays built step by step.
+      const float Gc = b0 == 0 ? 0.f : gch[b0 - 1];
+      if (__all(Gc - gch[b0 + 15] <= kDiagSpan)) {
+        const int s0 = b0 + 8 * lg;
+        const bool in = lg < 2;  // k-steps 16 .. 31 of the MFMA are padding
+        const int sc = in ? s0 : b0;
+        float kf[8], qf[8], gf[8], rkf[8], rqf[8];
+        ld8b(&kch[sc], kf);
+        ld8b(&qch[sc], qf);
+        ld8f(&gch[sc], gf);
+        ld8f(&sm.rk[sc], rkf);
+        ld8f(&sm.rq[sc], rqf);
+        float y[8], yq[8], yk[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float kn = kf[x] * rkf[x];
+          const float up = in ? __expf(Gc - gf[x]) : 0.f, dn = in ? __expf(gf[x] - Gc) : 0.f;
+          y[x] = kn * up;
+          yk[x] = kn * dn;
+          yq[x] = qf[x] * rqf[x] * dn;
+        }
+        const bf16x8 yb = as_bf16x8(pack8(y));
+        const bf16x8 ap = in ? load_bf16x8(&sm.dP[(b0 + lr) * TS + sc]) : zero8();
+        const bf16x8 aa = in ? load_bf16x8(&sm.dA[(b0 + lr) * TS + sc]) : zero8();
+        const bf16x8 apt = in ? col8(sm.dP, sc, b0, lr) : zero8();  // dP^T rows b0 + lr
+        const bf16x8 aat = in ? col8(sm.dA, sc, b0, lr) : zero8();
+        const f32x4 oq = mfma16(ap, yb, f4zero());
+        const f32x4 orr = mfma16(aa, yb, f4zero());
+        f32x4 ow = mfma16(apt, as_bf16x8(pack8(yq)), f4zero());
+        ow = mfma16(aat, as_bf16x8(pack8(yk)), ow);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dn = __expf(gt[r] - Gc), up = __expf(Gc - gt[r]);
+          dq[r] = fmaf(dn, oq[r], dq[r]);
+          dkr[r] = fmaf(dn, orr[r], dkr[r]);
+          dkw[r] = fmaf(up, ow[r], dkw[r]);
+        }
+      } else {
+        float gb[16], kb[16], qb[16], gg[16];
+        ld8f(&gch[b0], *reinterpret_cast<float(*)[8]>(&gb[0]));
+        ld8f(&gch[b0 + 8], *reinterpret_cast<float(*)[8]>(&gb[8]));
+        ld8b(&kch[b0], *reinterpret_cast<float(*)[8]>(&kb[0]));
+        ld8b(&kch[b0 + 8], *reinterpret_cast<float(*)[8]>(&kb[8]));
+        ld8b(&qch[b0], *reinterpret_cast<float(*)[8]>(&qb[0]));
+        ld8b(&qch[b0 + 8], *reinterpret_cast<float(*)[8]>(&qb[8]));
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          kb[x] *= sm.rk[b0 + x];
+          qb[x] *= sm.rq[b0 + x];
+        }
+        gg[0] = 1.f;
+#pragma unroll
+        for (int x = 1; x < 16; ++x) gg[x] = __expf(gb[x] - gb[x - 1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tloc = 4 * lg + r;  // per lane
+          float pr[16], ar[16];
+          ld8b(&sm.dP[(b0 + tloc) * TS + b0], *reinterpret_cast<float(*)[8]>(&pr[0]));
+          ld8b(&sm.dP[(b0 + tloc) * TS + b0 + 8], *reinterpret_cast<float(*)[8]>(&pr[8]));
+          ld8b(&sm.dA[(b0 + tloc) * TS + b0], *reinterpret_cast<float(*)[8]>(&ar[0]));
+          ld8b(&sm.dA[(b0 + tloc) * TS + b0 + 8], *reinterpret_cast<float(*)[8]>(&ar[8]));
+          float e = 0.f, sq = 0.f, sr = 0.f;
+#pragma unroll
+          for (int s = 15; s >= 0; --s) {
+            e = s < tloc ? e * gg[s + 1] : (s == tloc ? 1.f : 0.f);  // e^{G_t - G_s}, 0 above
+            const float ke = kb[s] * e;
+            sq = fmaf(pr[s], ke, sq);
+            sr = fmaf(ar[s], ke, sr);
+          }
+          dq[r] += sq;
+          dkr[r] += sr;
+          float pc[16], ac[16];  // column b0 + tloc of dP, dA
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            pc[t] = to_f32(sm.dP[(b0 + t) * TS + b0 + tloc]);
+            ac[t] = to_f32(sm.dA[(b0 + t) * TS + b0 + tloc]);
+          }
+          e = 0.f;
+          float sw = 0.f;
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            e = t > tloc ? e * gg[t] : (t == tloc ? 1.f : 0.f);  // e^{G_t - G_s}, 0 before
+            sw = fmaf(fmaf(pc[t], qb[t], ac[t] * kb[t]), e, sw);
+          }
+          dkw[r] += sw;
         }
       }
-      __syncthreads();
 
-      // ---- C3: dG, dkn and the reverse cumulative sum (16 lanes per
-      // channel, 4 steps each)
+      // dG, the suffix sums inside the block, and the block total
+      float suf[4];
       {
-        const int il = tid >> 4, seg = tid & 15, ic = i0c + il;
-        const float rowdot = __expf(sm.gam[(L - 1) * GS + ic]) * sm.rdh[il] + sm.rdot[0][il] + sm.rdot[1][il] +
-                             sm.rdot[2][il] + sm.rdot[3][il];
         float dg[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int t = 4 * seg + x;
-          const float dq = acc0[t * AS + il], dkr = acc1[t * AS + il], dkw = acc2[t * AS + il];
-          const float qv = to_f32(qrow[t * RS + ic]) * sm.rq[t], kv = to_f32(sm.krow[t * RS + ic]) * sm.rk[t];
-          dg[x] = fmaf(qv, dq, kv * (dkr - dkw)) + (t == L - 1 ? rowdot : 0.f);
-          acc1[t * AS + il] = dkr + dkw;
+        for (int r = 0; r < 4; ++r) {
+          dg[r] = fmaf(qst[r], dq[r], knt[r] * (dkr[r] - dkw[r]));
+          dqv[tile][r] = dq[r];
+          dknv[tile][r] = dkr[r] + dkw[r];
         }
-        float suf[4];
         suf[3] = dg[3];
         suf[2] = dg[2] + suf[3];
         suf[1] = dg[1] + suf[2];
         suf[0] = dg[0] + suf[1];
-        float run = suf[0];
+        // lanes lg + 1 .. 3 of the same channel hold the later steps of the block
+        const float tot = suf[0];
+        const float n1 = __shfl_down(tot, 16), n2 = __shfl_down(tot, 32), n3 = __shfl_down(tot, 48);
+        const float later = (lg < 3 ? n1 : 0.f) + (lg < 2 ? n2 : 0.f) + (lg < 1 ? n3 : 0.f);
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-          const float y = __shfl_down(run, off, 16);
-          if (seg + off < 16) run += y;
-        }
-        const float later = run - suf[0];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int t = 4 * seg + x;
-          acc2[t * AS + il] = sm.valid[t] != 0.f ? suf[x] + later : 0.f;
-        }
+        for (int r = 0; r < 4; ++r) dlgv[tile][r] = suf[r] + later;
+        if (lg == 0) sm.btot[w][lr] = tot + later;
       }
       __syncthreads();
-      // ---- C4: the partials of this tile's channels
-      for (int e = tid; e < L * 16; e += NT) {
-        const int t = e >> 4, il = e & 15;
-        if (t < Lc) {
-          float* dst = p.part + (vrow0 + static_cast<size_t>(t) * d.Hv) * 3 * DK + i0c + il;
-          dst[0] = acc0[t * AS + il];
-          dst[DK] = acc1[t * AS + il];
-          dst[2 * DK] = acc2[t * AS + il];
-        }
+      {
+        float add = __expf(gL) * sm.rdh[lr] + sm.rdot[0][lr] + sm.rdot[1][lr] + sm.rdot[2][lr] + sm.rdot[3][lr];
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww)
+          if (ww > w) add += sm.btot[ww][lr];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dlgv[tile][r] = sm.valid[tr0 + r] != 0.f ? dlgv[tile][r] + add : 0.f;
       }
-      __syncthreads();
+      __syncthreads();  // btot, rdot, rdh are rewritten by the next tile
     }
+
+    // ---- the partials: rows tr0 .. + 3, channels ch0 + 16 tile + lr
+#pragma unroll
+    for (int tile = 0; tile < NTL; ++tile)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tr0 + r;
+        if (t < Lc) {
+          float* dst = p.part + (vrow0 + static_cast<size_t>(t) * d.Hv) * 3 * DK + ch0 + 16 * tile + lr;
+          dst[0] = dqv[tile][r];
+          dst[DK] = dknv[tile][r];
+          dst[2 * DK] = dlgv[tile][r];
+        }
+      }
   }
 };
 
 template <int DK, int DV>
-__global__ void __launch_bounds__(NT) vg_chunk_grad_kernel(VgChunkGradArgs p) {
-  __shared__ typename VgGrad<DK, DV>::Smem sm;
-  VgGrad<DK, DV>::run(p, sm);
+__global__ void __launch_bounds__(NT) vg_chunk_x_kernel(VgChunkGradArgs p) {
+  __shared__ typename VgX<DK, DV>::Smem sm;
+  VgX<DK, DV>::run(p, sm);
 }
 
-template <int DK>
+template <int DK, int DV>
+__global__ void __launch_bounds__(NT) vg_chunk_grad_kernel(VgChunkGradArgs p) {
+  __shared__ typename VgG<DK, DV>::Smem sm;
+  VgG<DK, DV>::run(p, sm);
+}
+
+template <int DK, bool X>
 hipError_t launch_grad_dk(const VgChunkGradArgs& a, hipStream_t st) {
-  const dim3 grid(a.d.nchunk(), a.d.B * a.d.Hv);
+  const long pairs = static_cast<long>(a.d.nchunk()) * a.d.B * a.d.Hv;
+  const dim3 grid = X ? dim3(a.d.nchunk(), a.d.B * a.d.Hv)
+                      : dim3(static_cast<unsigned>((pairs + 7) / 8 * 8 * (DK / kVgGradChannels)));
   switch (a.d.Dv) {
-    case 32: vg_chunk_grad_kernel<DK, 32><<<grid, NT, 0, st>>>(a); break;
-    case 64: vg_chunk_grad_kernel<DK, 64><<<grid, NT, 0, st>>>(a); break;
-    case 96: vg_chunk_grad_kernel<DK, 96><<<grid, NT, 0, st>>>(a); break;
-    case 128: vg_chunk_grad_kernel<DK, 128><<<grid, NT, 0, st>>>(a); break;
+#define GDN_VG_DV(DV)                                          \
+  case DV:                                                     \
+    if (X)                                                     \
+      vg_chunk_x_kernel<DK, DV><<<grid, NT, 0, st>>>(a);       \
+    else                                                       \
+      vg_chunk_grad_kernel<DK, DV><<<grid, NT, 0, st>>>(a);    \
+    break;
+    GDN_VG_DV(32)
+    GDN_VG_DV(64)
+    GDN_VG_DV(96)
+    GDN_VG_DV(128)
+#undef GDN_VG_DV
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -928,12 +1178,22 @@ hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t st) {
 
 namespace gdn {
 
+hipError_t launch_vg_chunk_x(const VgChunkGradArgs& a, hipStream_t st) {
+  if (a.d.T == 0) return hipSuccess;
+  switch (a.d.Dk) {
+    case 64: return launch_grad_dk<64, true>(a, st);
+    case 128: return launch_grad_dk<128, true>(a, st);
+    case 192: return launch_grad_dk<192, true>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t st) {
   if (a.d.T == 0) return hipSuccess;
   switch (a.d.Dk) {
-    case 64: return launch_grad_dk<64>(a, st);
-    case 128: return launch_grad_dk<128>(a, st);
-    case 192: return launch_grad_dk<192>(a, st);
+    case 64: return launch_grad_dk<64, false>(a, st);
+    case 128: return launch_grad_dk<128, false>(a, st);
+    case 192: return launch_grad_dk<192, false>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
