@@ -80,11 +80,9 @@ struct VgPrep {
   static constexpr int RS = DK + 8;      // bf16 row stride of the staged k / q rows
   static constexpr int GS = DK + 4;      // fp32 row stride of Gamma
   static constexpr int SP = tri::SP;
-  static constexpr int NSL = DK / 32;    // channel slices of the diagonal sub-blocks
-  static constexpr int NTASK = 40 * NSL; // (sub-block, 4x4 tile, slice)
+  static constexpr int NTASK = 40;       // (sub-block, 4x4 tile) tasks of the far channels
   static constexpr int NLD = L * DK / 8 / NT;  // 16-byte pieces of one of k, q per thread
   static constexpr int NLG = L * DK / 4 / NT;  // 16-byte pieces of lg per thread
-  static_assert(NTASK <= NT, "one diagonal task per thread");
   static_assert(L * DK / 8 % NT == 0 && L * DK / 4 % NT == 0, "whole pieces per thread");
   struct Rows {
     bf16 k[L * RS];
@@ -102,11 +100,11 @@ struct VgPrep {
   };
   struct Smem {
     alignas(16) Big u;
-    alignas(16) float dp[NTASK * 32];  // diagonal sub-block partial sums: 16 of A, 16 of P per task
+    alignas(16) float dp[NTASK * 32];  // far-channel sums of the diagonal sub-blocks: 16 of A, 16 of P per task
     alignas(16) float dg[4][2][16][17];  // diagonal sub-blocks over the channels in range (A, P)
     float rk[L], rq[L], beta[L], valid[L];
-    unsigned char far[4][DK];  // channel i decays by more than e^kDiagSpan inside sub-block I
-    int farw[4][4];            // wave w holds such a channel of sub-block I
+    unsigned char far[4][DK];            // channel i decays by more than e^kDiagSpan inside sub-block I
+    unsigned long long fmask[4][4];      // the same as bits: channels 64 w .. 64 w + 63
   };
 
   __device__ static void run(const VgChunkPrepArgs& p, Smem& sm) {
@@ -210,7 +208,7 @@ struct VgPrep {
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       const unsigned long long m = __ballot((farbits >> I) & 1);
-      if (l == 0) sm.farw[I][w] = m != 0;
+      if (l == 0) sm.fmask[I][w] = m;
     }
     __syncthreads();
 
@@ -290,56 +288,59 @@ struct VgPrep {
       }
     }
 
-    // ---- ... and in fp32 for the far channels: task (block I, 4x4 tile,
-    // slice of the channels); raw-row products, scaled by the norms when summed
+    // ---- ... and in fp32 for the far channels: task (block I, 4x4 tile);
+    // raw-row products, scaled by the norms when summed
     if (tid < NTASK) {
-      const int sl = tid % NSL, rest = tid / NSL, I = rest / 10, ti = rest % 10;
+      const int I = tid / 10, ti = tid % 10, rest = tid;
       const int tt = tile_t(ti), uu = tile_u(ti);
       const int tb = 16 * I + 4 * tt, ub = 16 * I + 4 * uu;
       float pa[16], pp[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) pa[x] = pp[x] = 0.f;
       const bool split = tt > uu;  // different 4-step groups: split at the end of ub's group
-      const bool any = sm.farw[I][0] | sm.farw[I][1] | sm.farw[I][2] | sm.farw[I][3];
-      for (int i = sl; i < (any ? DK : 0); i += NSL) {  // interleaved: adjacent lanes read adjacent channels
-        if (!sm.far[I][i]) continue;
-        float gt[4], gu[4], kt_[4], qt_[4], ku[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          gt[a] = sm.u.r.gam[(tb + a) * GS + i];
-          gu[a] = sm.u.r.gam[(ub + a) * GS + i];
-          kt_[a] = to_f32(sm.u.r.k[(tb + a) * RS + i]);
-          qt_[a] = to_f32(sm.u.r.q[(tb + a) * RS + i]);
-          ku[a] = to_f32(sm.u.r.k[(ub + a) * RS + i]);
-        }
-        if (split) {
-          float e1k[4], e1q[4], e2[4];
+      for (int wd = 0; wd < 4; ++wd) {
+        unsigned long long m = sm.fmask[I][wd];
+        while (m) {
+          const int i = 64 * wd + __builtin_ctzll(m);
+          m &= m - 1;
+          float gt[4], gu[4], kt_[4], qt_[4], ku[4];
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            const float e1 = __expf(gt[a] - gu[3]);
-            e1k[a] = kt_[a] * e1;
-            e1q[a] = qt_[a] * e1;
-            e2[a] = ku[a] * __expf(gu[3] - gu[a]);
+            gt[a] = sm.u.r.gam[(tb + a) * GS + i];
+            gu[a] = sm.u.r.gam[(ub + a) * GS + i];
+            kt_[a] = to_f32(sm.u.r.k[(tb + a) * RS + i]);
+            qt_[a] = to_f32(sm.u.r.q[(tb + a) * RS + i]);
+            ku[a] = to_f32(sm.u.r.k[(ub + a) * RS + i]);
           }
+          if (split) {
+            float e1k[4], e1q[4], e2[4];
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-              pa[4 * a + bb] = fmaf(e1k[a], e2[bb], pa[4 * a + bb]);
-              pp[4 * a + bb] = fmaf(e1q[a], e2[bb], pp[4 * a + bb]);
+            for (int a = 0; a < 4; ++a) {
+              const float e1 = __expf(gt[a] - gu[3]);
+              e1k[a] = kt_[a] * e1;
+              e1q[a] = qt_[a] * e1;
+              e2[a] = ku[a] * __expf(gu[3] - gu[a]);
             }
-        } else {
 #pragma unroll
-          for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int bb = 0; bb <= a; ++bb) {
-              const float e = ku[bb] * __expf(gt[a] - gu[bb]);
-              pa[4 * a + bb] = fmaf(kt_[a], e, pa[4 * a + bb]);
-              pp[4 * a + bb] = fmaf(qt_[a], e, pp[4 * a + bb]);
-            }
+              for (int bb = 0; bb < 4; ++bb) {
+                pa[4 * a + bb] = fmaf(e1k[a], e2[bb], pa[4 * a + bb]);
+                pp[4 * a + bb] = fmaf(e1q[a], e2[bb], pp[4 * a + bb]);
+              }
+          } else {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+              for (int bb = 0; bb <= a; ++bb) {
+                const float e = ku[bb] * __expf(gt[a] - gu[bb]);
+                pa[4 * a + bb] = fmaf(kt_[a], e, pa[4 * a + bb]);
+                pp[4 * a + bb] = fmaf(qt_[a], e, pp[4 * a + bb]);
+              }
+          }
         }
       }
-      float* dst = &sm.dp[(rest * NSL + sl) * 32];
+      float* dst = &sm.dp[rest * 32];
 #pragma unroll
       for (int x = 0; x < 16; x += 4) {
         *reinterpret_cast<float4*>(&dst[x]) = make_float4(pa[x], pa[x + 1], pa[x + 2], pa[x + 3]);
@@ -418,21 +419,18 @@ struct VgPrep {
         }
       }
     }
-    for (int e = tid; e < L * L; e += NT) {
-      const int t = e >> 6, s = e & 63, bi = t >> 4, bj = s >> 4;
-      if (bi > bj) continue;
-      float av = 0.f, pv = 0.f;
+    // the diagonal sub-blocks: the MFMA part plus the far channels' sums
+    for (int e = tid; e < 4 * 256; e += NT) {
+      const int bi = e >> 8, t = 16 * bi + ((e >> 4) & 15), s = 16 * bi + (e & 15);
       const int tt = (t >> 2) & 3, uu = (s >> 2) & 3;
-      if (bi == bj && uu <= tt) {
-        const int rest = bi * 10 + tt * (tt + 1) / 2 + uu, x = 4 * (t & 3) + (s & 3);
-#pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) {
-          av += sm.dp[(rest * NSL + sl) * 32 + x];
-          pv += sm.dp[(rest * NSL + sl) * 32 + 16 + x];
-        }
-        av = s < t ? sm.dg[bi][0][t & 15][s & 15] + av * sm.rk[t] * sm.rk[s] : 0.f;
-        pv = s <= t ? sm.dg[bi][1][t & 15][s & 15] + pv * sm.rq[t] * sm.rk[s] : 0.f;
+      float av = sm.dg[bi][0][t & 15][s & 15], pv = sm.dg[bi][1][t & 15][s & 15];
+      if ((sm.fmask[bi][0] | sm.fmask[bi][1] | sm.fmask[bi][2] | sm.fmask[bi][3]) && uu <= tt) {
+        const int x = 4 * (t & 3) + (s & 3), rest = bi * 10 + tt * (tt + 1) / 2 + uu;
+        av += sm.dp[rest * 32 + x] * sm.rk[t] * sm.rk[s];
+        pv += sm.dp[rest * 32 + 16 + x] * sm.rq[t] * sm.rk[s];
       }
+      av = s < t ? av : 0.f;
+      pv = s <= t ? pv : 0.f;
       const float bs = sm.beta[s];
       nf[t * SP + s] = av * bs;
       if (bwd) {
@@ -440,6 +438,18 @@ struct VgPrep {
         st2[s * SP + t] = pv;
       } else {
         st[t * SP + s] = pv * bs;
+      }
+    }
+    // zeros above the diagonal sub-blocks: pairs (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    for (int e = tid; e < 6 * 256; e += NT) {
+      const int pr = e >> 8, bi = (0x211000 >> (4 * pr)) & 15, bj = (0x332321 >> (4 * pr)) & 15;
+      const int t = 16 * bi + ((e >> 4) & 15), s = 16 * bj + (e & 15);
+      nf[t * SP + s] = 0.f;
+      if (bwd) {
+        st[s * SP + t] = 0.f;
+        st2[s * SP + t] = 0.f;
+      } else {
+        st[t * SP + s] = 0.f;
       }
     }
     __syncthreads();
@@ -480,13 +490,13 @@ template <int DK, int DV>
 struct VgX {
   static constexpr int NV = DV / 32;
   static constexpr int NVT = DV / 16;
-  static constexpr int RS = DK + 8;  // bf16 row stride of H^T
+  static constexpr int HS = DV + 8;  // bf16 row stride of H [i][v]
   static constexpr int TS = L + 8;   // bf16 row stride of the L-wide tiles
   static constexpr int XS = DV + 8;  // bf16 row stride of X
-  static constexpr int HVI = DV * RS > L * XS ? DV * RS : L * XS;
+  static constexpr int HN = DK * HS > L * XS ? DK * HS : L * XS;
   static constexpr int RTN = (DV > L ? DV : L) * TS;
   struct Smem {
-    alignas(16) bf16 hvi[HVI];  // H^T [v][i]; X [t][v] takes its place
+    alignas(16) bf16 hs[HN];    // H [i][v] (bf16); X [t][v] takes its place
     alignas(16) bf16 rT[RTN];   // R^T [v][s]; dP [t][s] later
     alignas(16) bf16 txs[L * TS];  // Tx [t][s]; dA [t][s] later
     float beta[L];
@@ -504,19 +514,16 @@ struct VgX {
     const size_t cidx = static_cast<size_t>(bh) * NC + c;
     const float* H = c == 0 ? (p.state0 ? p.state0 + static_cast<size_t>(bh) * DK * DV : nullptr)
                             : p.ckpt + (static_cast<size_t>(c - 1) * d.B * d.Hv + bh) * DK * DV;
-    bf16* xs = sm.hvi;
+    bf16* xs = sm.hs;
     bf16* dPs = sm.rT;
     bf16* dAs = sm.txs;
 
-    // ---- H^T (bf16), Tx, beta
+    // ---- H (bf16, rows [i][v]), Tx, beta
     for (int u = tid; u < DK * DV / 4; u += NT) {
       const int i = u / (DV / 4), v4 = 4 * (u % (DV / 4));
       const float4 x = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(i) * DV + v4)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      sm.hvi[(v4 + 0) * RS + i] = bf16_of(x.x);
-      sm.hvi[(v4 + 1) * RS + i] = bf16_of(x.y);
-      sm.hvi[(v4 + 2) * RS + i] = bf16_of(x.z);
-      sm.hvi[(v4 + 3) * RS + i] = bf16_of(x.w);
+      *reinterpret_cast<uint2*>(&sm.hs[i * HS + v4]) = pack4_bf16(x.x, x.y, x.z, x.w);
     }
     {
       const bf16* txg = p.cb.Tx + cidx * L * L;
@@ -528,7 +535,9 @@ struct VgX {
     }
     __syncthreads();
 
-    // ---- R^T = V^T - H^T Kb^T (Kb rows from the prep: zero past the end)
+    // ---- R^T = V^T - H^T Kb^T (Kb rows from the prep: zero past the end); the
+    // rows of H^T by transposing reads of H: rows i0 .. i0 + 7 of column
+    // 16 vt + lr
     {
       const int tb = 16 * w + lr;
       const bf16* kbr = p.cb.Kb + (cidx * L + tb) * DK;
@@ -540,8 +549,11 @@ struct VgX {
         const int i0 = 32 * kt + 8 * lg;
         const bf16x8 kb = as_bf16x8(*reinterpret_cast<const uint4*>(kbr + i0));
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt)
-          acc[vt] = mfma16(load_bf16x8(&sm.hvi[(16 * vt + lr) * RS + i0]), kb, acc[vt]);
+        for (int vt = 0; vt < NVT; ++vt) {
+          const uint2 lo = lds_read_tr16(&sm.hs[(i0 + (lr >> 2)) * HS + 16 * vt + 4 * (lr & 3)]);
+          const uint2 hi = lds_read_tr16(&sm.hs[(i0 + 4 + (lr >> 2)) * HS + 16 * vt + 4 * (lr & 3)]);
+          acc[vt] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), kb, acc[vt]);
+        }
       }
       const bf16* vg = static_cast<const bf16*>(p.v) + (vrow0 + static_cast<size_t>(min(tb, tl)) * d.Hv) * DV;
 #pragma unroll
