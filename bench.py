@@ -54,10 +54,10 @@ FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
 KERNELS["vg"] = ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd_vg", "vg_reduce"]
 # ... and its chunk form (bf16): the forward's vg_chunk_prep and chunk_fwd (VG
 # mode); the backward's step scalars (prep), vg_chunk_prep, chunk_bwd_state (VG
-# mode), the gradient pass (X and the L x L gradients, then the per-channel
-# expansions) and the per-head sums
+# mode), the gradient pass (X, the L x L gradients and db; the per-channel
+# expansions and dlg; the L2-norm backward of q, k)
 KERNELS["vg_chunk"] = ["vg_prep_fwd", "chunk_fwd_vg", "prep_bwd", "vg_prep_bwd", "chunk_bwd_state_vg",
-                       "vg_chunk_x", "vg_chunk_grad", "vg_reduce"]
+                       "vg_chunk_x", "vg_chunk_grad", "vg_norm_bwd"]
 FLOPS_PER_ELEM.update({"scan_bwd_vg": 20})
 VG_METRIC = "fwd+bwd tokens/sec with a per-key-channel gate at Hk16/Hv64/Dk192/Dv128 bf16, T=2048"
 
@@ -525,9 +525,9 @@ def vg_kernel_bytes(B, T, Hk, Hv, Dk, Dv, io):
         "prep_bwd": 2 * Q1 + Bt,
         "vg_prep_bwd": 2 * Q1 + LG + Bt,
         "chunk_bwd_state_vg": 2 * V1 + Sig,
-        "vg_chunk_x": 3 * V1 + CK,
-        "vg_chunk_grad": 2 * Q1 + 2 * V1 + LG + CK,
-        "vg_reduce": 4 * Q1 + LG + Bt,
+        "vg_chunk_x": 3 * V1 + Bt + CK,
+        "vg_chunk_grad": 2 * Q1 + 2 * V1 + 2 * LG + CK,
+        "vg_norm_bwd": 4 * Q1,
     }
 
 

@@ -316,16 +316,14 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
   L.rk = take(bt * d.Hk);
   L.kq = take(bt * d.Hk);
   L.beta = take(bt * d.Hv);
-  if (bwd) {
-    // the chunk form's gradient pass writes one slice of row partials
-    const size_t ns = chunk ? 1 : gdn::vg_nslice(d.Dv);
-    if (chunk) {
-      const size_t nc = d.nchunk();
-      L.E = take((bt * d.Hv * d.Dv + 1) / 2);
-      L.dHend = take((nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv + 1) / 2);
-    } else {
-      L.sub = take(gdn::vg_sub_floats(d));
-    }
+  if (bwd && chunk) {  // eps, dH', and the value heads' parts of the row gradients
+    const size_t nc = d.nchunk();
+    L.E = take((bt * d.Hv * d.Dv + 1) / 2);
+    L.dHend = take((nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv + 1) / 2);
+    L.part = take(bt * d.Hv * 2 * d.Dk);
+  } else if (bwd) {
+    const size_t ns = gdn::vg_nslice(d.Dv);
+    L.sub = take(gdn::vg_sub_floats(d));
     L.part = take(bt * d.Hv * ns * 3 * d.Dk);
     L.pdb = take(bt * d.Hv * ns);
   }
@@ -742,11 +740,10 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
     gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, s, cb, E, dHend, dv,
                             at<gdn::bf16>(ws, L.X), at<gdn::bf16>(ws, L.dPA), at<float>(ws, L.part),
-                            at<float>(ws, L.pdb)};
+                            dq, dk, db, dlg};
     if (!launch(st, [&] { return gdn::launch_vg_chunk_x(ga, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_vg_chunk_grad(ga, st); })) return GDN_ERR_HIP;
-    gdn::VgReduceArgs ra{dd, 1, q, k, s, at<float>(ws, L.part), at<float>(ws, L.pdb), dq, dk, db, dlg};
-    if (!launch(st, [&] { return gdn::launch_vg_reduce(ra, bf, st); })) return GDN_ERR_HIP;
+    if (!launch(st, [&] { return gdn::launch_vg_norm_bwd(ga, st); })) return GDN_ERR_HIP;
     return GDN_OK;
   }
   gdn::ScanBwdVgArgs ba{dd, q, k, v, dO, lg, mask, state0, ckpt, dS_final, s,

@@ -195,12 +195,12 @@ struct VgChunkPrepArgs {
   ChunkBufs cb;
   int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kb, Kh, KbT, QbT, vsc
 };
-// Gradient pass of the per-key-channel gate's chunk form, in two kernels:
+// Gradient pass of the per-key-channel gate's chunk form, in three kernels:
 // vg_chunk_x (one workgroup per (chunk, batch, value head)) recomputes X from
-// the fp32 checkpoint and writes it with dP, dA and dL/dbeta; vg_chunk_grad
-// (one workgroup per (chunk, batch, value head, 32 channels)) writes the
-// per-head row partials vg_reduce sums (one slice): dL/d(qn / sqrt(Dk)),
-// dL/dkn and dL/dlg per step.
+// the fp32 checkpoint and writes it with dP, dA and db; vg_chunk_grad (one
+// workgroup per (chunk, batch, value head, 32 channels)) writes dlg and the
+// value head's parts of dL/d(s qn) and dL/dkn; vg_norm_bwd sums the parts of
+// a key head's value heads and turns them into dq, dk (the L2-norm backward).
 struct VgChunkGradArgs {
   Dims d;
   const void *q, *k, *v, *b, *dO;
@@ -214,8 +214,9 @@ struct VgChunkGradArgs {
   const void* dv;              // [B,T,Hv,Dv] dv (= Ehat) from the reverse state pass
   bf16* X;                     // [B*Hv, NC, L, Dv] X_t = v_t - u_t of every step
   bf16* dPA;                   // [B*Hv, NC, 2, L, L] dP, dA
-  float* part;                 // [B,T,Hv,1,3,Dk]
-  float* pdb;                  // [B,T,Hv,1]
+  float* qk;                   // [B,T,Hv,2,Dk] each value head's parts of the rows of d(s qn), d(kn)
+  void *dq, *dk, *db;          // outputs (input dtype)
+  float* dlg;                  // [B,T,Hv,Dk]
 };
 // Channels per vg_chunk_grad workgroup.
 constexpr int kVgGradChannels = 32;
@@ -349,6 +350,7 @@ hipError_t launch_chunk_prep(const ChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t st);
 hipError_t launch_vg_chunk_x(const VgChunkGradArgs& a, hipStream_t st);
 hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t st);
+hipError_t launch_vg_norm_bwd(const VgChunkGradArgs& a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st);
 hipError_t launch_seg_chain(const SegChainArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t st);

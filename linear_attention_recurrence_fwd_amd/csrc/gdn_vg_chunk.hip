@@ -71,6 +71,12 @@ __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
     f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
   }
 }
+// Sum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ float lanes_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
 __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]), pack2_bf16(f[6], f[7]));
 }
@@ -616,7 +622,7 @@ struct VgX {
           dAs[t * TS + s] = bf16_of(s < t ? -g2[st][r] * bs : 0.f);
         }
     }
-    {  // dbeta_t = eps_t . X_t (four lanes per step)
+    {  // db_t = (eps_t . X_t) beta_t (1 - beta_t), four lanes per step (0 on masked steps: beta 0)
       const int t = tid >> 2, part = tid & 3;
       const bf16* eg = p.E + (vrow0 + static_cast<size_t>(min(t, tl)) * d.Hv) * DV;
       float sdot = 0.f;
@@ -630,7 +636,8 @@ struct VgX {
         for (int x = 0; x < 8; ++x) sdot = fmaf(ef[x], xf[x], sdot);
       }
       sdot = quad_sum(sdot);
-      if (part == 0 && t < Lc) p.pdb[vrow0 + static_cast<size_t>(t) * d.Hv] = sdot;
+      const float bt = sm.beta[t];
+      if (part == 0 && t < Lc) static_cast<bf16*>(p.db)[vrow0 + static_cast<size_t>(t) * d.Hv] = bf16_of(sdot * bt * (1.f - bt));
     }
     {
       bf16* xg = p.X + cidx * L * DV;
@@ -866,7 +873,7 @@ struct VgG {
 
     const int b0 = 16 * w;        // this wave's block
     const int tr0 = b0 + 4 * lg;  // this lane's first step
-    float dlgv[NTL][4], dqv[NTL][4], dknv[NTL][4];
+    float dqv[NTL][4], dknv[NTL][4];
 
 #pragma unroll
     for (int tile = 0; tile < NTL; ++tile) {
@@ -1063,7 +1070,8 @@ struct VgG {
           float e = 0.f, sq = 0.f, sr = 0.f;
 #pragma unroll
           for (int s = 15; s >= 0; --s) {
-            e = s < tloc ? e * gg[s + 1] : (s == tloc ? 1.f : 0.f);  // e^{G_t - G_s}, 0 above
+            const float gn = s < 15 ? gg[s + 1] : 0.f;  // (s is a constant here: no read past gg)
+            e = s < tloc ? e * gn : (s == tloc ? 1.f : 0.f);  // e^{G_t - G_s}, 0 above
             const float ke = kb[s] * e;
             sq = fmaf(pr[s], ke, sq);
             sr = fmaf(ar[s], ke, sr);
@@ -1106,36 +1114,86 @@ struct VgG {
         const float n1 = __shfl_down(tot, 16), n2 = __shfl_down(tot, 32), n3 = __shfl_down(tot, 48);
         const float later = (lg < 3 ? n1 : 0.f) + (lg < 2 ? n2 : 0.f) + (lg < 1 ? n3 : 0.f);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dlgv[tile][r] = suf[r] + later;
+        for (int r = 0; r < 4; ++r) suf[r] += later;
         if (lg == 0) sm.btot[w][lr] = tot + later;
       }
       __syncthreads();
-      {
+      {  // dlg: rows tr0 .. + 3, channel ch0 + cl (0 on masked steps)
         float add = __expf(gL) * sm.rdh[lr] + sm.rdot[0][lr] + sm.rdot[1][lr] + sm.rdot[2][lr] + sm.rdot[3][lr];
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww)
           if (ww > w) add += sm.btot[ww][lr];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dlgv[tile][r] = sm.valid[tr0 + r] != 0.f ? dlgv[tile][r] + add : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int t = tr0 + r;
+          if (t < Lc)
+            p.dlg[(vrow0 + static_cast<size_t>(t) * d.Hv) * DK + ch0 + cl] = sm.valid[t] != 0.f ? suf[r] + add : 0.f;
+        }
       }
       __syncthreads();  // btot, rdot, rdh are rewritten by the next tile
     }
 
-    // ---- the partials: rows tr0 .. + 3, channels ch0 + 16 tile + lr
+    // ---- this value head's parts of the row gradients of s qn and kn: rows
+    // tr0 .. + 3, channels ch0 + 16 tile + lr
 #pragma unroll
     for (int tile = 0; tile < NTL; ++tile)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tr0 + r;
         if (t < Lc) {
-          float* dst = p.part + (vrow0 + static_cast<size_t>(t) * d.Hv) * 3 * DK + ch0 + 16 * tile + lr;
+          float* dst = p.qk + (vrow0 + static_cast<size_t>(t) * d.Hv) * 2 * DK + ch0 + 16 * tile + lr;
           dst[0] = dqv[tile][r];
           dst[DK] = dknv[tile][r];
-          dst[2 * DK] = dlgv[tile][r];
         }
       }
   }
 };
+
+// vg_norm_bwd: the L2-normalisation backward of q and k (torch-to-nnef GDN
+// page, "Op contract": q, k normalised with eps 1e-6 inside the root).  g, the
+// gradient w.r.t. the normalised row as the chunk form uses it (s qn for q, kn
+// for k), is the sum of the parts of the key head's G value heads (in head
+// order); with r the norm factor (for q also 1 / sqrt(Dk), so that s qn = r q),
+// dx = r (g - x^ (x^ . g)), x^ = x (|x|^2 + eps)^-1/2.  One wave per (b, t, key
+// head), DK / 64 channels per lane.
+template <int DK>
+__global__ void __launch_bounds__(64) vg_norm_bwd_kernel(VgChunkGradArgs p) {
+  constexpr int RM = DK / 64;
+  const Dims& d = p.d;
+  const size_t row = blockIdx.x;  // (b t) Hk + j
+  const int lane = threadIdx.x;
+  const float rq = p.s.rq[row], rk = p.s.rk[row];
+  const float qs = rq * sqrtf(static_cast<float>(DK));  // q^ = q qs
+  const bf16* qg = static_cast<const bf16*>(p.q) + row * DK;
+  const bf16* kg = static_cast<const bf16*>(p.k) + row * DK;
+  const int G = d.G();
+  const float* gq = p.qk + row * G * 2 * DK;  // rows (b t) Hv + j G + hh
+  float qh[RM], kn[RM], dq[RM], dk[RM], pq = 0.f, pk = 0.f;
+#pragma unroll
+  for (int m = 0; m < RM; ++m) dq[m] = dk[m] = 0.f;
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int m = 0; m < RM; ++m) {
+      dq[m] += gq[hh * 2 * DK + lane + 64 * m];
+      dk[m] += gq[hh * 2 * DK + DK + lane + 64 * m];
+    }
+#pragma unroll
+  for (int m = 0; m < RM; ++m) {
+    const int i = lane + 64 * m;
+    qh[m] = to_f32(qg[i]) * qs;
+    kn[m] = to_f32(kg[i]) * rk;
+    pq = fmaf(qh[m], dq[m], pq);
+    pk = fmaf(kn[m], dk[m], pk);
+  }
+  pq = lanes_sum(pq);
+  pk = lanes_sum(pk);
+#pragma unroll
+  for (int m = 0; m < RM; ++m) {
+    const int i = lane + 64 * m;
+    static_cast<bf16*>(p.dq)[row * DK + i] = bf16_of(rq * (dq[m] - qh[m] * pq));
+    static_cast<bf16*>(p.dk)[row * DK + i] = bf16_of(rk * (dk[m] - kn[m] * pk));
+  }
+}
 
 template <int DK, int DV>
 __global__ void __launch_bounds__(NT) vg_chunk_x_kernel(VgChunkGradArgs p) {
@@ -1208,6 +1266,18 @@ hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t st) {
     case 192: return launch_grad_dk<192, false>(a, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_vg_norm_bwd(const VgChunkGradArgs& a, hipStream_t st) {
+  const unsigned n = static_cast<unsigned>(static_cast<size_t>(a.d.B) * a.d.T * a.d.Hk);
+  if (n == 0) return hipSuccess;
+  switch (a.d.Dk) {
+    case 64: vg_norm_bwd_kernel<64><<<n, 64, 0, st>>>(a); break;
+    case 128: vg_norm_bwd_kernel<128><<<n, 64, 0, st>>>(a); break;
+    case 192: vg_norm_bwd_kernel<192><<<n, 64, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace gdn

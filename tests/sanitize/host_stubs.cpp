@@ -130,8 +130,7 @@ void touch_vg_grad(const VgChunkGradArgs& a) {
   touch_ckpt(a.d, a.ckpt);
   touch(a.X, nmat(a.d) * 64 * a.d.Dv * 2);
   touch(a.dPA, nmat(a.d) * 2 * 64 * 64 * 2);
-  touch(a.part, bt(a.d) * a.d.Hv * 3 * a.d.Dk * 4);
-  touch(a.pdb, bt(a.d) * a.d.Hv * 4);
+  touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 4);
   ++g_launches;
 }
 hipError_t launch_vg_chunk_x(const VgChunkGradArgs& a, hipStream_t) {
@@ -140,6 +139,11 @@ hipError_t launch_vg_chunk_x(const VgChunkGradArgs& a, hipStream_t) {
 }
 hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t) {
   touch_vg_grad(a);
+  return hipSuccess;
+}
+hipError_t launch_vg_norm_bwd(const VgChunkGradArgs& a, hipStream_t) {
+  touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 4);
+  ++g_launches;
   return hipSuccess;
 }
 hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t) {
