@@ -52,11 +52,13 @@ FLOPS_PER_ELEM = {"scan_fwd": 7, "scan_bwd": 12, "chunk_grad": 8}
 #                1 fma, dS' = D + kn du^T 1 fma, dkn = D delta + S' du 2 fma,
 #                dlg = <dS', S> along the row 1 fma, carry D = g dS' 1 mul    = 20
 KERNELS["vg"] = ["prep_fwd", "scan_fwd", "prep_bwd", "scan_bwd_vg", "vg_reduce"]
-# ... and its chunk form (bf16): the forward's vg_chunk_prep and chunk_fwd (VG
-# mode); the backward's step scalars (prep), vg_chunk_prep, chunk_bwd_state (VG
-# mode), the gradient pass (X, the L x L gradients and db; the per-channel
+# ... and its chunk form (bf16), with the saved record (gdn_dims.save, as in
+# training): the forward's vg_chunk_prep (which also writes the backward's
+# rows and matrices) and chunk_fwd (VG mode, which also writes X); the
+# backward's step scalars (prep), chunk_bwd_state (VG mode), the gradient
+# pass (the L x L gradients and db from the saved X; the per-channel
 # expansions and dlg; the L2-norm backward of q, k)
-KERNELS["vg_chunk"] = ["vg_prep_fwd", "chunk_fwd_vg", "prep_bwd", "vg_prep_bwd", "chunk_bwd_state_vg",
+KERNELS["vg_chunk"] = ["vg_prep_fwd", "chunk_fwd_vg", "prep_bwd", "chunk_bwd_state_vg",
                        "vg_chunk_x", "vg_chunk_grad", "vg_norm_bwd"]
 FLOPS_PER_ELEM.update({"scan_bwd_vg": 20})
 VG_METRIC = "fwd+bwd tokens/sec with a per-key-channel gate at Hk16/Hv64/Dk192/Dv128 bf16, T=2048"
@@ -511,8 +513,9 @@ def vg_method_bytes(B, T, Hk, Hv, Dk, Dv, io):
 def vg_kernel_bytes(B, T, Hk, Hv, Dk, Dv, io):
     """Algorithmic HBM bytes of each kernel of the per-channel gate's chunk
     form: the tensors of vg_method_bytes that the kernel reads or writes, each
-    counted once per kernel (the pre-scaled rows, chunk matrices, eps, dH' and
-    the per-head partials are intermediates and not counted)."""
+    counted once per kernel (the pre-scaled rows, chunk matrices, X, eps, dH'
+    and the per-head partials are intermediates and not counted; the saved
+    record's fp32 states are the method's checkpoints, read by vg_chunk_grad)."""
     Q1 = B * T * Hk * Dk * io
     V1 = B * T * Hv * Dv * io
     Bt = B * T * Hv * io
@@ -523,9 +526,8 @@ def vg_kernel_bytes(B, T, Hk, Hv, Dk, Dv, io):
         "vg_prep_fwd": 2 * Q1 + LG + Bt,
         "chunk_fwd_vg": 2 * V1 + Sig + CK,
         "prep_bwd": 2 * Q1 + Bt,
-        "vg_prep_bwd": 2 * Q1 + LG + Bt,
         "chunk_bwd_state_vg": 2 * V1 + Sig,
-        "vg_chunk_x": 3 * V1 + Bt + CK,
+        "vg_chunk_x": 2 * V1 + Bt,  # dO, dv, b (X from the saved record)
         "vg_chunk_grad": 2 * Q1 + 2 * V1 + 2 * LG + CK,
         "vg_norm_bwd": 4 * Q1,
     }
@@ -560,7 +562,7 @@ def bench_vg(args, torch, binding, inputs):
     t["mask"] = None
     algo = {"auto": binding.ALGO_AUTO, "scan": binding.ALGO_SCAN,
             "chunk": binding.ALGO_CHUNK}[args.algo]
-    plan = binding.PlanVg(t, algo=algo)
+    plan = binding.PlanVg(t, algo=algo, save=True)
     family = plan.family
     kernels = KERNELS["vg" if family == "scan" else "vg_chunk"]
     lib = binding.lib()

@@ -24,7 +24,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_INVALID_ARG", 2: "GDN_ERR_UNSUPPORTED",
 
 # every entry point declared in include/gdn.h
 EXPORTS = ("gdn_ckpt_elems", "gdn_ckpt_bytes", "gdn_workspace_bytes", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-           "gdn_fwd", "gdn_fwd_noalloc", "gdn_bwd", "gdn_decode_conv", "gdn_fwd_vg_workspace_bytes",
+           "gdn_fwd", "gdn_fwd_noalloc", "gdn_bwd", "gdn_decode_conv", "gdn_vg_ckpt_elems", "gdn_vg_ckpt_bytes",
+           "gdn_fwd_vg_workspace_bytes",
            "gdn_bwd_vg_workspace_bytes", "gdn_fwd_vg", "gdn_bwd_vg", "gdn_set_kernel_events",
            "gdn_status_string", "gdn_version")
 
@@ -54,8 +55,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, S = ctypes.c_void_p, ctypes.c_size_t
         PD = ctypes.POINTER(Dims)
-        for n in ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes",
-                  "gdn_fwd_vg_workspace_bytes", "gdn_bwd_vg_workspace_bytes"):
+        for n in ("gdn_ckpt_elems", "gdn_fwd_workspace_bytes", "gdn_bwd_workspace_bytes", "gdn_vg_ckpt_elems",
+                  "gdn_vg_ckpt_bytes", "gdn_fwd_vg_workspace_bytes", "gdn_bwd_vg_workspace_bytes"):
             getattr(L, n).argtypes = [PD, ctypes.POINTER(S)]
             getattr(L, n).restype = ctypes.c_int
         L.gdn_ckpt_bytes.argtypes = [PD, ctypes.POINTER(S)]
@@ -101,6 +102,10 @@ def ckpt_elems(d: Dims) -> int:
     return _query("gdn_ckpt_elems", d)
 
 
+def vg_ckpt_elems(d: Dims) -> int:
+    return _query("gdn_vg_ckpt_elems", d)
+
+
 def fwd_workspace_bytes(d: Dims) -> int:
     return _query("gdn_fwd_workspace_bytes", d)
 
@@ -134,12 +139,12 @@ def _dims_of(q, v, algo, save=False):
     return make_dims(B, T, Hk, Hv, Dk, Dv, q.dtype, algo, save)
 
 
-def _alloc_ckpt(d, dev):
+def _alloc_ckpt(d, dev, vg=False):
     """The checkpoint buffer: [ceil(T/64)-1, B, Hv, Dk, Dv] fp32, or, when the
-    dims save (chunk family), a flat buffer of gdn_ckpt_elems fp32 elements
-    with contents private to the library."""
+    dims save (chunk family), a flat buffer of gdn_ckpt_elems (vg:
+    gdn_vg_ckpt_elems) fp32 elements with contents private to the library."""
     nslab = max((d.T + CHUNK - 1) // CHUNK - 1, 0)
-    nck = ckpt_elems(d)
+    nck = vg_ckpt_elems(d) if vg else ckpt_elems(d)
     if nck == nslab * d.B * d.Hv * d.Dk * d.Dv:
         return torch.empty((nslab, d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
     return torch.empty((nck,), dtype=torch.float32, device=dev)
@@ -352,10 +357,14 @@ def vg_uses_chunk(d) -> bool:
 
 
 def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=None,
-           algo=ALGO_AUTO):
+           algo=ALGO_AUTO, save=False):
     """Forward with a per-key-channel gate: lg [B,T,Hv,Dk] fp32 holds log g,
-    and g scales the state's rows.  Returns (o, state_out, ckpt)."""
-    d = _dims_of(q, v, algo)
+    and g scales the state's rows.  Returns (o, state_out, ckpt).  With
+    save=True the chunk form writes the backward's rows, matrices and X into
+    ckpt (pass the same save to bwd_vg)."""
+    d = _dims_of(q, v, algo, save)
+    if save and not need_ckpt:
+        raise ValueError("save=True needs the checkpoint buffer (need_ckpt=True)")
     _check_inputs_vg(d, q, k, v, lg, b, state0, mask)
     dev = q.device
     o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
@@ -363,8 +372,8 @@ def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=
         state_out = torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
     else:
         _check(state_out, "state_out", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
-    nck = ckpt_elems(d)
-    ckpt = _alloc_ckpt(d, dev) if need_ckpt else None
+    nck = vg_ckpt_elems(d)
+    ckpt = _alloc_ckpt(d, dev, vg=True) if need_ckpt else None
     wsb = _query("gdn_fwd_vg_workspace_bytes", d)
     ws = torch.empty((max(wsb, 1),), dtype=torch.uint8, device=dev)
     rc = lib().gdn_fwd_vg(ctypes.byref(d), _p(q), _p(k), _p(v), _p(lg), _p(b), _p(state0),
@@ -376,15 +385,16 @@ def fwd_vg(q, k, v, lg, b, state0=None, mask=None, *, need_ckpt=True, state_out=
     return o, state_out, ckpt
 
 
-def bwd_vg(q, k, v, lg, b, state0, mask, ckpt, dO, dS_final=None, *, algo=ALGO_AUTO):
-    """VJP of fwd_vg.  Returns dict(dq, dk, dv, dlg, db, dstate)."""
-    d = _dims_of(q, v, algo)
+def bwd_vg(q, k, v, lg, b, state0, mask, ckpt, dO, dS_final=None, *, algo=ALGO_AUTO, save=False):
+    """VJP of fwd_vg.  Returns dict(dq, dk, dv, dlg, db, dstate).  `save`
+    must match the fwd_vg call that wrote ckpt."""
+    d = _dims_of(q, v, algo, save)
     _check_inputs_vg(d, q, k, v, lg, b, state0, mask)
     dev = q.device
     _check(dO, "dO", (d.B, d.T, d.Hv, d.Dv), q.dtype, dev)
     if dS_final is not None:
         _check(dS_final, "dS_final", (d.B, d.Hv, d.Dk, d.Dv), torch.float32, dev)
-    nck = ckpt_elems(d)
+    nck = vg_ckpt_elems(d)
     if nck:
         if ckpt is None or ckpt.numel() != nck:
             raise ValueError("ckpt from gdn_fwd_vg with %d elements is required" % nck)
@@ -408,16 +418,16 @@ class PlanVg:
     """Plan (above) for the per-key-channel-gate form: `t` maps q, k, v, lg,
     b, state0, mask, dO, dS_final to device tensors."""
 
-    def __init__(self, t, algo=ALGO_AUTO, stream=None):
+    def __init__(self, t, algo=ALGO_AUTO, stream=None, save=False):
         q, v = t["q"], t["v"]
-        self.d = d = _dims_of(q, v, algo)
+        self.d = d = _dims_of(q, v, algo, save)
         self.family = "chunk" if vg_uses_chunk(d) else "scan"
         _check_inputs_vg(d, q, t["k"], v, t["lg"], t["b"], t["state0"], t["mask"])
         dev = q.device
         self.t = t
         self.o = torch.empty((d.B, d.T, d.Hv, d.Dv), dtype=q.dtype, device=dev)
         self.state_out = torch.empty((d.B, d.Hv, d.Dk, d.Dv), dtype=torch.float32, device=dev)
-        self.ckpt = _alloc_ckpt(d, dev)
+        self.ckpt = _alloc_ckpt(d, dev, vg=True)
         nck = self.ckpt.numel()
         self.g = dict(dq=torch.empty_like(q), dk=torch.empty_like(t["k"]), dv=torch.empty_like(v),
                       dlg=torch.empty_like(t["lg"]), db=torch.empty_like(t["b"]),

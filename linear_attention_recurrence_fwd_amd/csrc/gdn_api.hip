@@ -283,7 +283,40 @@ bool use_vg_chunk(const gdn_dims* p) {
   return p->T > 1 && vg_chunk_ok(p);
 }
 
-VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
+// Under gdn_dims.save (chunk form) the checkpoint buffer holds the fp32
+// states at the chunk boundaries (as without save, at its start), then the
+// chunk rows and matrices the backward reads and X of every step, all
+// written by the forward (offsets in fp32 elements, 256-byte aligned).
+struct VgSaved {
+  size_t Kb, Kh, KbT, QbT, Tx, AtT, PqT, vsc, X, total;
+};
+
+VgSaved vg_saved_layout(const Dims& d) {
+  VgSaved S{};
+  size_t off = align_up(ckpt_state_elems(d) * sizeof(float)) / sizeof(float);
+  auto take = [&](size_t nfloat) {
+    size_t o = off;
+    off += align_up(nfloat * sizeof(float)) / sizeof(float);
+    return o;
+  };
+  const size_t bhc = static_cast<size_t>(d.B) * d.Hv * d.nchunk();
+  const size_t rows = (bhc * 64 * d.Dk + 1) / 2, mats = (bhc * 64 * 64 + 1) / 2;  // bf16, in floats
+  S.Kb = take(rows);
+  S.Kh = take(rows);
+  S.KbT = take(rows);
+  S.QbT = take(rows);
+  S.Tx = take(mats);
+  S.AtT = take(mats);
+  S.PqT = take(mats);
+  S.vsc = take(bhc * gdn::VSC_ROWS * 64);
+  S.X = take((static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv + 1) / 2);
+  S.total = off;
+  return S;
+}
+bool use_vg_saved(const gdn_dims* p) { return p->save != 0 && use_vg_chunk(p); }
+
+// `saved`: the chunk rows, matrices and X live in the checkpoint buffer.
+VgLayout vg_layout(const Dims& d, bool bwd, bool chunk, bool saved) {
   VgLayout L{};
   size_t off = 0;
   auto take = [&](size_t nfloat) {
@@ -295,21 +328,25 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk) {
   if (chunk) {
     const size_t nc = d.nchunk(), bhc = static_cast<size_t>(d.B) * d.Hv * nc;
     const size_t rows = (bhc * 64 * d.Dk + 1) / 2, mats = (bhc * 64 * 64 + 1) / 2;  // bf16, in floats
-    L.Kb = take(rows);
-    L.Kh = take(rows);
-    L.Tx = take(mats);
-    L.vsc = take(bhc * gdn::VSC_ROWS * 64);
+    if (!saved) {
+      L.Kb = take(rows);
+      L.Kh = take(rows);
+      L.Tx = take(mats);
+      L.vsc = take(bhc * gdn::VSC_ROWS * 64);
+    }
     if (!bwd) {
       L.Qb = take(rows);
       L.Mq = take(mats);
       L.total = off;
       return L;
     }
-    L.KbT = take(rows);
-    L.QbT = take(rows);
-    L.AtT = take(mats);
-    L.PqT = take(mats);
-    L.X = take((bhc * 64 * d.Dv + 1) / 2);
+    if (!saved) {
+      L.KbT = take(rows);
+      L.QbT = take(rows);
+      L.AtT = take(mats);
+      L.PqT = take(mats);
+      L.X = take((bt * d.Hv * d.Dv + 1) / 2);
+    }
     L.dPA = take(2 * mats);
   }
   L.rq = take(bt * d.Hk);
@@ -336,18 +373,37 @@ gdn::StepScalars vg_scalars(void* ws, const VgLayout& L) {
                           at<float>(ws, L.beta)};
 }
 
-gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd) {
+// The chunk buffers in the workspace, or (saved) in the checkpoint buffer;
+// under save the forward's Qb and Mq stay in its workspace, and cb.X is set,
+// so that the forward's state pass stores X there.
+gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd, const Dims& d, const float* ckpt,
+                             bool saved) {
   gdn::ChunkBufs cb{};
-  cb.Kb = at<gdn::bf16>(ws, L.Kb);
-  cb.Kh = at<gdn::bf16>(ws, L.Kh);
-  cb.Tx = at<gdn::bf16>(ws, L.Tx);
-  cb.vsc = at<float>(ws, L.vsc);
-  if (bwd) {
-    cb.KbT = at<gdn::bf16>(ws, L.KbT);
-    cb.QbT = at<gdn::bf16>(ws, L.QbT);
-    cb.AtT = at<gdn::bf16>(ws, L.AtT);
-    cb.PqT = at<gdn::bf16>(ws, L.PqT);
+  if (saved) {
+    const VgSaved S = vg_saved_layout(d);
+    float* rec = const_cast<float*>(ckpt);
+    cb.Kb = reinterpret_cast<gdn::bf16*>(rec + S.Kb);
+    cb.Kh = reinterpret_cast<gdn::bf16*>(rec + S.Kh);
+    cb.KbT = reinterpret_cast<gdn::bf16*>(rec + S.KbT);
+    cb.QbT = reinterpret_cast<gdn::bf16*>(rec + S.QbT);
+    cb.Tx = reinterpret_cast<gdn::bf16*>(rec + S.Tx);
+    cb.AtT = reinterpret_cast<gdn::bf16*>(rec + S.AtT);
+    cb.PqT = reinterpret_cast<gdn::bf16*>(rec + S.PqT);
+    cb.vsc = rec + S.vsc;
+    cb.X = reinterpret_cast<gdn::bf16*>(rec + S.X);
   } else {
+    cb.Kb = at<gdn::bf16>(ws, L.Kb);
+    cb.Kh = at<gdn::bf16>(ws, L.Kh);
+    cb.Tx = at<gdn::bf16>(ws, L.Tx);
+    cb.vsc = at<float>(ws, L.vsc);
+    if (bwd) {
+      cb.KbT = at<gdn::bf16>(ws, L.KbT);
+      cb.QbT = at<gdn::bf16>(ws, L.QbT);
+      cb.AtT = at<gdn::bf16>(ws, L.AtT);
+      cb.PqT = at<gdn::bf16>(ws, L.PqT);
+    }
+  }
+  if (!bwd) {
     cb.Qb = at<gdn::bf16>(ws, L.Qb);
     cb.Mq = at<gdn::bf16>(ws, L.Mq);
   }
@@ -661,12 +717,29 @@ int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const 
   return GDN_OK;
 }
 
+int gdn_vg_ckpt_elems(const gdn_dims* d, size_t* out) {
+  Dims dd;
+  int rc = check_vg(d, &dd);
+  if (rc) return rc;
+  if (!out) return GDN_ERR_INVALID_ARG;
+  *out = use_vg_saved(d) ? vg_saved_layout(dd).total : ckpt_state_elems(dd);
+  return GDN_OK;
+}
+
+int gdn_vg_ckpt_bytes(const gdn_dims* d, size_t* out) {
+  size_t n = 0;
+  const int rc = gdn_vg_ckpt_elems(d, &n);
+  if (rc) return rc;
+  *out = n * sizeof(float);
+  return GDN_OK;
+}
+
 int gdn_fwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
   Dims dd;
   int rc = check_vg(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = vg_layout(dd, false, use_vg_chunk(d)).total;
+  *out = vg_layout(dd, false, use_vg_chunk(d), use_vg_saved(d)).total;
   return GDN_OK;
 }
 
@@ -675,7 +748,7 @@ int gdn_bwd_vg_workspace_bytes(const gdn_dims* d, size_t* out) {
   int rc = check_vg(d, &dd);
   if (rc) return rc;
   if (!out) return GDN_ERR_INVALID_ARG;
-  *out = vg_layout(dd, true, use_vg_chunk(d)).total;
+  *out = vg_layout(dd, true, use_vg_chunk(d), use_vg_saved(d)).total;
   return GDN_OK;
 }
 
@@ -687,14 +760,17 @@ int gdn_fwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
   if (rc) return rc;
   if (!state_out) return GDN_ERR_INVALID_ARG;
   if (dd.T > 0 && (!q || !k || !v || !lg || !b || !o)) return GDN_ERR_INVALID_ARG;
-  const bool chunk = use_vg_chunk(d);
-  const VgLayout L = vg_layout(dd, false, chunk);
+  const bool chunk = use_vg_chunk(d), saved = use_vg_saved(d);
+  if (saved && !ckpt) return GDN_ERR_INVALID_ARG;  // the record is written there
+  const VgLayout L = vg_layout(dd, false, chunk, saved);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (chunk) {
-    const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, false);
-    gdn::VgChunkPrepArgs pa{dd, q, k, b, lg, mask, cb, 0};
+    // under save the prep also writes the backward's rows and matrices, and
+    // the state pass X, into the record; the fp32 states sit at its start
+    const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, false, dd, ckpt, saved);
+    gdn::VgChunkPrepArgs pa{dd, q, k, b, lg, mask, cb, saved ? 2 : 0};
     if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(pa, st); })) return GDN_ERR_HIP;
     gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, ckpt};
     fa.vg = 1;
@@ -719,9 +795,9 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
   if (!dstate) return GDN_ERR_INVALID_ARG;
   if (dd.T > 0 && (!q || !k || !v || !lg || !b || !dO || !dq || !dk || !dv || !dlg || !db))
     return GDN_ERR_INVALID_ARG;
-  if (dd.nchunk() > 1 && !ckpt) return GDN_ERR_INVALID_ARG;
-  const bool chunk = use_vg_chunk(d);
-  const VgLayout L = vg_layout(dd, true, chunk);
+  const bool chunk = use_vg_chunk(d), saved = use_vg_saved(d);
+  if ((dd.nchunk() > 1 || saved) && !ckpt) return GDN_ERR_INVALID_ARG;
+  const VgLayout L = vg_layout(dd, true, chunk, saved);
   if (L.total > ws_bytes || (L.total > 0 && !ws)) return GDN_ERR_WORKSPACE;
   const bool bf = d->dtype == GDN_BF16;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -729,9 +805,11 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
   gdn::PrepArgs pa{dd, q, k, nullptr, b, nullptr, nullptr, mask, s};
   if (!launch(st, [&] { return gdn::launch_prep(pa, bf, st); })) return GDN_ERR_HIP;
   if (chunk) {
-    const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, true);
-    gdn::VgChunkPrepArgs ca{dd, q, k, b, lg, mask, cb, 1};
-    if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, true, dd, ckpt, saved);
+    if (!saved) {  // else the forward saved the rows and matrices
+      gdn::VgChunkPrepArgs ca{dd, q, k, b, lg, mask, cb, 1};
+      if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(ca, st); })) return GDN_ERR_HIP;
+    }
     gdn::bf16* E = at<gdn::bf16>(ws, L.E);
     gdn::bf16* dHend = at<gdn::bf16>(ws, L.dHend);
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, nullptr, nullptr, nullptr, mask, state0, ckpt, dS_final, cb,
@@ -739,8 +817,8 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
     ba.vg = 1;
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
     gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, s, cb, E, dHend, dv,
-                            at<gdn::bf16>(ws, L.X), at<gdn::bf16>(ws, L.dPA), at<float>(ws, L.part),
-                            dq, dk, db, dlg};
+                            saved ? cb.X : at<gdn::bf16>(ws, L.X), at<gdn::bf16>(ws, L.dPA),
+                            at<float>(ws, L.part), dq, dk, db, dlg, saved ? 1 : 0};
     if (!launch(st, [&] { return gdn::launch_vg_chunk_x(ga, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_vg_chunk_grad(ga, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_vg_norm_bwd(ga, st); })) return GDN_ERR_HIP;

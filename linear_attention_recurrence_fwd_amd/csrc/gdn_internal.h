@@ -193,11 +193,12 @@ struct VgChunkPrepArgs {
   const float* lg;
   const uint8_t* mask;
   ChunkBufs cb;
-  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kb, Kh, KbT, QbT, vsc
+  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kb, Kh, KbT, QbT, vsc; 2: all of them
 };
 // Gradient pass of the per-key-channel gate's chunk form, in three kernels:
 // vg_chunk_x (one workgroup per (chunk, batch, value head)) recomputes X from
-// the fp32 checkpoint and writes it with dP, dA and db; vg_chunk_grad (one
+// the fp32 checkpoint and writes it (or, with xsv, reads the forward's saved
+// copy) and writes dP, dA and db; vg_chunk_grad (one
 // workgroup per (chunk, batch, value head, 32 channels)) writes dlg and the
 // value head's parts of dL/d(s qn) and dL/dkn; vg_norm_bwd sums the parts of
 // a key head's value heads and turns them into dq, dk (the L2-norm backward).
@@ -212,11 +213,12 @@ struct VgChunkGradArgs {
   const bf16* E;               // [B,T,Hv,Dv] eps (dL/d delta)
   const bf16* dHend;           // [NC, B*Hv, Dk, Dv] dL/d(state at the end of chunk c)
   const void* dv;              // [B,T,Hv,Dv] dv (= Ehat) from the reverse state pass
-  bf16* X;                     // [B*Hv, NC, L, Dv] X_t = v_t - u_t of every step
+  bf16* X;                     // [B,T,Hv,Dv] X_t = v_t - u_t of every step
   bf16* dPA;                   // [B*Hv, NC, 2, L, L] dP, dA
   float* qk;                   // [B,T,Hv,2,Dk] each value head's parts of the rows of d(s qn), d(kn)
   void *dq, *dk, *db;          // outputs (input dtype)
   float* dlg;                  // [B,T,Hv,Dk]
+  int xsv = 0;                 // X is the forward's saved copy (vg_chunk_x does not recompute it)
 };
 // Channels per vg_chunk_grad workgroup.
 constexpr int kVgGradChannels = 32;

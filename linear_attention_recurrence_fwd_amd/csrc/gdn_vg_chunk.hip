@@ -120,7 +120,8 @@ struct VgPrep {
     const int b = bh / d.Hv, h = bh % d.Hv, j = h / G;
     const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const bool bwd = p.bwd != 0;
+    // mode 0: the forward's outputs; 1: the backward's; 2: both (saved record)
+    const bool fwd = p.bwd != 1, bwd = p.bwd != 0;
     const size_t qk0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;
     const uint32_t qk_row = d.Hk * DK;
     const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
@@ -375,7 +376,7 @@ struct VgPrep {
         const size_t o = rowbase + static_cast<size_t>(t) * DK + i0;
         *reinterpret_cast<uint4*>(p.cb.Kh + o) = pack8(kh);
         *reinterpret_cast<uint4*>(p.cb.Kb + o) = pack8(kf);
-        if (!bwd) *reinterpret_cast<uint4*>(p.cb.Qb + o) = pack8(qf);
+        if (fwd) *reinterpret_cast<uint4*>(p.cb.Qb + o) = pack8(qf);
       }
       if (bwd) {
         for (int u = tid; u < DK * L / 8; u += NT) {
@@ -400,9 +401,9 @@ struct VgPrep {
     }
     __syncthreads();  // the staged rows and Gamma are dead from here on
 
-    // ---- N = A diag(beta) and Mq = P diag(beta) (forward), or A^T, P^T
-    // (backward); every element written once: the lower off-diagonal
-    // sub-blocks by the MFMA waves, the rest here
+    // ---- N = A diag(beta) and Mq = P diag(beta) (forward only), or A^T, P^T
+    // (backward, and both; Mq then comes from P^T); every element written
+    // once: the lower off-diagonal sub-blocks by the MFMA waves, the rest here
     float* nf = sm.u.m.nf;
     float* st = sm.u.m.st;
     float* st2 = sm.u.m.st2;
@@ -466,6 +467,15 @@ struct VgPrep {
     if (bwd) {
       tri::store_mat(st, p.cb.AtT + mat, tid, NT);
       tri::store_mat(st2, p.cb.PqT + mat, tid, NT);
+      if (fwd) {  // Mq[t][s] = P^T[s][t] beta_s: row t, columns s8 .. s8 + 7 per thread
+        for (int u = tid; u < L * L / 8; u += NT) {
+          const int t = u >> 3, s8 = 8 * (u & 7);
+          float mv[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) mv[x] = st2[(s8 + x) * SP + t] * sm.beta[s8 + x];
+          *reinterpret_cast<uint4*>(p.cb.Mq + mat + t * L + s8) = pack8(mv);
+        }
+      }
     } else {
       tri::store_mat(st, p.cb.Mq + mat, tid, NT);
     }
@@ -488,11 +498,13 @@ __global__ void __launch_bounds__(NT) vg_chunk_prep_kernel(VgChunkPrepArgs p) {
 
 // ------------------------------------------------------------ gradient pass
 
-// vg_chunk_x: X = Tx (V - Kb H) from the fp32 checkpoint H, then
-// dP = lower(dO X^T) diag(beta), dA = -strictlower(Ehat X^T) diag(beta) and
-// dbeta_t = eps_t . X_t.  Writes X, dP, dA (bf16) and dbeta.  Wave w takes
-// steps 16 w .. 16 w + 15.
-template <int DK, int DV>
+// vg_chunk_x: X = Tx (V - Kb H) from the fp32 checkpoint H (XSV: X read
+// from the forward's saved copy instead), then dP = lower(dO X^T) diag(beta),
+// dA = -strictlower(Ehat X^T) diag(beta) and db_t = (eps_t . X_t) beta_t (1 -
+// beta_t).  Writes dP, dA, db (bf16) and, when it computes X, X ([B,T,Hv,Dv]
+// bf16, the layout the forward saves it in).  Wave w takes steps 16 w .. 16 w
+// + 15.
+template <int DK, int DV, bool XSV>
 struct VgX {
   static constexpr int NV = DV / 32;
   static constexpr int NVT = DV / 16;
@@ -501,30 +513,27 @@ struct VgX {
   static constexpr int XS = DV + 8;  // bf16 row stride of X
   static constexpr int HN = DK * HS > L * XS ? DK * HS : L * XS;
   static constexpr int RTN = (DV > L ? DV : L) * TS;
-  struct Smem {
+  struct SmemFull {
     alignas(16) bf16 hs[HN];    // H [i][v] (bf16); X [t][v] takes its place
     alignas(16) bf16 rT[RTN];   // R^T [v][s]; dP [t][s] later
     alignas(16) bf16 txs[L * TS];  // Tx [t][s]; dA [t][s] later
     float beta[L];
   };
+  struct SmemSaved {
+    alignas(16) bf16 xs[L * XS];  // X [t][v]
+    alignas(16) bf16 dP[L * TS];
+    alignas(16) bf16 dA[L * TS];
+    float beta[L];
+  };
+  using Smem = std::conditional_t<XSV, SmemSaved, SmemFull>;
 
-  __device__ static void run(const VgChunkGradArgs& p, Smem& sm) {
+  // X = Tx (V - Kb H) of the chunk into xs (rows [t][v]), from the fp32
+  // checkpoint; every wave has passed the last barrier when it returns.
+  __device__ static void compute_x(const VgChunkGradArgs& p, SmemFull& sm, const float* H, size_t cidx,
+                                   size_t vrow0, int tl, int tid, int w, int lr, int lg) {
     const Dims& d = p.d;
-    const int c = blockIdx.x, bh = blockIdx.y;
-    const int NC = d.nchunk();
-    const int b = bh / d.Hv, h = bh % d.Hv;
-    const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
-    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const size_t vrow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hv + h;
-    const size_t cidx = static_cast<size_t>(bh) * NC + c;
-    const float* H = c == 0 ? (p.state0 ? p.state0 + static_cast<size_t>(bh) * DK * DV : nullptr)
-                            : p.ckpt + (static_cast<size_t>(c - 1) * d.B * d.Hv + bh) * DK * DV;
     bf16* xs = sm.hs;
-    bf16* dPs = sm.rT;
-    bf16* dAs = sm.txs;
-
-    // ---- H (bf16, rows [i][v]), Tx, beta
+    // ---- H (bf16, rows [i][v]) and Tx
     for (int u = tid; u < DK * DV / 4; u += NT) {
       const int i = u / (DV / 4), v4 = 4 * (u % (DV / 4));
       const float4 x = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(i) * DV + v4)
@@ -537,7 +546,6 @@ struct VgX {
         const int t = u >> 3, s8 = 8 * (u & 7);
         *reinterpret_cast<uint4*>(&sm.txs[t * TS + s8]) = *reinterpret_cast<const uint4*>(txg + t * L + s8);
       }
-      if (tid < L) sm.beta[tid] = p.cb.vsc[cidx * VSC_ROWS * L + VSC_BETA * L + tid];
     }
     __syncthreads();
 
@@ -591,8 +599,42 @@ struct VgX {
         for (int r = 0; r < 4; ++r) xs[(16 * w + 4 * lg + r) * XS + 16 * vt + lr] = bf16_of(xa[vt][r]);
     }
     __syncthreads();
+  }
 
-    // ---- dO X^T, Ehat X^T -> dP, dA (into R^T's and Tx's places); dbeta; X out
+  __device__ static void run(const VgChunkGradArgs& p, Smem& sm) {
+    const Dims& d = p.d;
+    const int c = blockIdx.x, bh = blockIdx.y;
+    const int NC = d.nchunk();
+    const int b = bh / d.Hv, h = bh % d.Hv;
+    const int t0 = c * L, Lc = min(L, d.T - t0), tl = Lc - 1;
+    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const size_t vrow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hv + h;
+    const size_t cidx = static_cast<size_t>(bh) * NC + c;
+    bf16 *xs, *dPs, *dAs;
+    if (tid < L) sm.beta[tid] = p.cb.vsc[cidx * VSC_ROWS * L + VSC_BETA * L + tid];
+    if constexpr (XSV) {
+      xs = sm.xs;
+      dPs = sm.dP;
+      dAs = sm.dA;
+      // the saved X rows (clamped into the sequence: rows past the end meet
+      // beta = 0 or a zero norm factor wherever they are used)
+      for (int u = tid; u < L * DV / 8; u += NT) {
+        const int t = u / (DV / 8), v8 = 8 * (u % (DV / 8));
+        *reinterpret_cast<uint4*>(&xs[t * XS + v8]) =
+            *reinterpret_cast<const uint4*>(p.X + (vrow0 + static_cast<size_t>(min(t, tl)) * d.Hv) * DV + v8);
+      }
+      __syncthreads();
+    } else {
+      xs = sm.hs;
+      dPs = sm.rT;
+      dAs = sm.txs;
+      const float* H = c == 0 ? (p.state0 ? p.state0 + static_cast<size_t>(bh) * DK * DV : nullptr)
+                              : p.ckpt + (static_cast<size_t>(c - 1) * d.B * d.Hv + bh) * DK * DV;
+      compute_x(p, sm, H, cidx, vrow0, tl, tid, w, lr, lg);
+    }
+
+    // ---- dO X^T, Ehat X^T -> dP, dA; db; X out
     {
       const int ta = 16 * w + lr;
       const size_t ro = (vrow0 + static_cast<size_t>(min(ta, tl)) * d.Hv) * DV;
@@ -639,11 +681,12 @@ struct VgX {
       const float bt = sm.beta[t];
       if (part == 0 && t < Lc) static_cast<bf16*>(p.db)[vrow0 + static_cast<size_t>(t) * d.Hv] = bf16_of(sdot * bt * (1.f - bt));
     }
-    {
-      bf16* xg = p.X + cidx * L * DV;
+    if constexpr (!XSV) {  // rows of the sequence only
       for (int u = tid; u < L * DV / 8; u += NT) {
         const int t = u / (DV / 8), v8 = 8 * (u % (DV / 8));
-        *reinterpret_cast<uint4*>(xg + t * DV + v8) = *reinterpret_cast<const uint4*>(&xs[t * XS + v8]);
+        if (t < Lc)
+          *reinterpret_cast<uint4*>(p.X + (vrow0 + static_cast<size_t>(t) * d.Hv) * DV + v8) =
+              *reinterpret_cast<const uint4*>(&xs[t * XS + v8]);
       }
     }
     __syncthreads();
@@ -789,7 +832,7 @@ struct VgG {
       const size_t ro = (vrow0 + static_cast<size_t>(min(ta, tl)) * d.Hv) * DV;
       const bf16* dOg = static_cast<const bf16*>(p.dO) + ro;
       const bf16* Eg = static_cast<const bf16*>(p.dv) + ro;
-      const bf16* Xg = p.X + (cidx * L + ta) * DV;
+      const bf16* Xg = p.X + ro;  // [B,T,Hv,Dv], the row of dO's
 #pragma unroll
       for (int kv = 0; kv < NV; ++kv) {
         dOf[kv] = as_bf16x8(*reinterpret_cast<const uint4*>(dOg + 32 * kv + 8 * lg));
@@ -1195,10 +1238,10 @@ __global__ void __launch_bounds__(64) vg_norm_bwd_kernel(VgChunkGradArgs p) {
   }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool XSV>
 __global__ void __launch_bounds__(NT) vg_chunk_x_kernel(VgChunkGradArgs p) {
-  __shared__ typename VgX<DK, DV>::Smem sm;
-  VgX<DK, DV>::run(p, sm);
+  __shared__ typename VgX<DK, DV, XSV>::Smem sm;
+  VgX<DK, DV, XSV>::run(p, sm);
 }
 
 template <int DK, int DV>
@@ -1215,8 +1258,10 @@ hipError_t launch_grad_dk(const VgChunkGradArgs& a, hipStream_t st) {
   switch (a.d.Dv) {
 #define GDN_VG_DV(DV)                                          \
   case DV:                                                     \
-    if (X)                                                     \
-      vg_chunk_x_kernel<DK, DV><<<grid, NT, 0, st>>>(a);       \
+    if (X && a.xsv)                                            \
+      vg_chunk_x_kernel<DK, DV, true><<<grid, NT, 0, st>>>(a); \
+    else if (X)                                                \
+      vg_chunk_x_kernel<DK, DV, false><<<grid, NT, 0, st>>>(a); \
     else                                                       \
       vg_chunk_grad_kernel<DK, DV><<<grid, NT, 0, st>>>(a);    \
     break;

@@ -88,10 +88,9 @@ static void run_case(int64_t B, int64_t T, int64_t Hk, int64_t Hv, int64_t Dk, i
   if (algo == GDN_ALGO_SCAN || algo == GDN_ALGO_AUTO || algo == GDN_ALGO_CHUNK) {
     size_t vf = 0, vb = 0;
     if (gdn_fwd_vg_workspace_bytes(&d, &vf) == GDN_OK && gdn_bwd_vg_workspace_bytes(&d, &vb) == GDN_OK) {
-      gdn_dims ds = d;
-      ds.save = 0;
+      gdn_dims ds = d;  // save as the case gives it: the chunk form's record, or the fp32 states
       size_t nvk = 0;
-      gdn_ckpt_elems(&ds, &nvk);
+      gdn_vg_ckpt_elems(&ds, &nvk);
       float* vck = nvk ? static_cast<float*>(malloc(nvk * sizeof(float))) : nullptr;
       unsigned char* vwf = static_cast<unsigned char*>(malloc(vf ? vf : 1));
       unsigned char* vwb = static_cast<unsigned char*>(malloc(vb ? vb : 1));

@@ -128,7 +128,7 @@ void touch_vg_grad(const VgChunkGradArgs& a) {
   touch(a.E, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dHend, slots(a.d) * 2);
   touch_ckpt(a.d, a.ckpt);
-  touch(a.X, nmat(a.d) * 64 * a.d.Dv * 2);
+  touch(a.X, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dPA, nmat(a.d) * 2 * 64 * 64 * 2);
   touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 4);
   ++g_launches;

@@ -221,6 +221,48 @@ def test_vg_rejects_before_launch():
     assert lib.gdn_bwd_vg(ctypes.byref(d), *g, g[0], bws - 1, None) == 3
 
 
+def test_vg_saved_record_sizes():
+    """gdn_vg_ckpt_elems: the fp32 states without save (and on the scan family,
+    which ignores save); with save on the chunk form, the record: those states
+    first, then per (chunk, head) four bf16 row blocks of 64 x Dk, three 64 x
+    64 bf16 matrices and the chunk scalars, and X of every step (each region
+    256-byte aligned).  The saved workspaces are smaller than the unsaved
+    ones by what moved into the record, and a NULL ckpt is refused."""
+    lib = B.lib()
+    out = ctypes.c_size_t(0)
+    Bn, T, Hk, Hv, Dk, Dv = 1, 200, 2, 4, 128, 64
+    nc = (T + 63) // 64
+    states = (nc - 1) * Bn * Hv * Dk * Dv
+    for dtype, algo, save, want in ((B.GDN_BF16, B.ALGO_CHUNK, 0, states), (B.GDN_F32, B.ALGO_AUTO, 1, states),
+                                    (B.GDN_BF16, B.ALGO_SCAN, 1, states)):
+        d = B.make_dims(Bn, T, Hk, Hv, Dk, Dv, dtype, algo, save)
+        assert lib.gdn_vg_ckpt_elems(ctypes.byref(d), ctypes.byref(out)) == 0
+        assert out.value == want
+    d = B.make_dims(Bn, T, Hk, Hv, Dk, Dv, B.GDN_BF16, B.ALGO_CHUNK, 1)
+    assert lib.gdn_vg_ckpt_elems(ctypes.byref(d), ctypes.byref(out)) == 0
+    bhc = Bn * Hv * nc
+    pieces = [states] + [bhc * 64 * Dk // 2] * 4 + [bhc * 64 * 64 // 2] * 3 + [bhc * 8 * 64, Bn * T * Hv * Dv // 2]
+    assert out.value == sum((p * 4 + 255) // 256 * 64 for p in pieces)
+    assert lib.gdn_vg_ckpt_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
+    assert out.value == sum((p * 4 + 255) // 256 * 256 for p in pieces)
+    ws = {}
+    for save in (0, 1):
+        dd = B.make_dims(Bn, T, Hk, Hv, Dk, Dv, B.GDN_BF16, B.ALGO_CHUNK, save)
+        for fn in ("gdn_fwd_vg_workspace_bytes", "gdn_bwd_vg_workspace_bytes"):
+            assert getattr(lib, fn)(ctypes.byref(dd), ctypes.byref(out)) == 0
+            ws[fn, save] = out.value
+    for fn in ("gdn_fwd_vg_workspace_bytes", "gdn_bwd_vg_workspace_bytes"):
+        assert ws[fn, 1] < ws[fn, 0]
+    f = _fake(10)
+    args = list(f)
+    args[9] = None  # ckpt
+    assert lib.gdn_fwd_vg(ctypes.byref(d), *args, f[0], ws["gdn_fwd_vg_workspace_bytes", 1], None) == 1
+    g = _fake(16)
+    args = list(g)
+    args[7] = None
+    assert lib.gdn_bwd_vg(ctypes.byref(d), *args, g[0], ws["gdn_bwd_vg_workspace_bytes", 1], None) == 1
+
+
 def test_tpar_segments_only_when_they_pay():
     """GDN_ALGO_CHUNK_TPAR splits a long sequence into segments (more
     workspace: the segment maps and start states) only when the single pass

@@ -39,27 +39,28 @@ def upload_vg(case):
     return t
 
 
-def run_vg(t, algo=binding.ALGO_AUTO, bwd_algo=None):
-    o, st, ck = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"], algo=algo)
+def run_vg(t, algo=binding.ALGO_AUTO, bwd_algo=None, save=False):
+    o, st, ck = binding.fwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"], algo=algo,
+                               save=save)
     g = binding.bwd_vg(t["q"], t["k"], t["v"], t["lg"], t["b"], t["state0"], t["mask"], ck,
-                       t["dO"], t["dS_final"], algo=algo if bwd_algo is None else bwd_algo)
+                       t["dO"], t["dS_final"], algo=algo if bwd_algo is None else bwd_algo, save=save)
     return o, st, ck, g
 
 
-def compare_vg(case, nthreads=8, algo=binding.ALGO_AUTO, bwd_algo=None):
+def compare_vg(case, nthreads=8, algo=binding.ALGO_AUTO, bwd_algo=None, save=False):
     tol = TOL[case.dtype]
-    say("[vg] case=%s B=%d T=%d Hk=%d Hv=%d Dk=%d Dv=%d dtype=%s algo=%d/%d" % (
+    say("[vg] case=%s B=%d T=%d Hk=%d Hv=%d Dk=%d Dv=%d dtype=%s algo=%d/%d save=%d" % (
         case.name, case.B, case.T, case.Hk, case.Hv, case.Dk, case.Dv, case.dtype, algo,
-        algo if bwd_algo is None else bwd_algo))
+        algo if bwd_algo is None else bwd_algo, save))
     t = upload_vg(case)
-    o, st, ck, g = run_vg(t, algo, bwd_algo)
+    o, st, ck, g = run_vg(t, algo, bwd_algo, save)
     torch.cuda.synchronize()
     v = case.vals
     ro, rst, rck = oracle.fwd_vg(*case.vg_args(), nthreads=nthreads)
     rg = oracle.bwd_vg(*case.vg_args(), v["dO"], v.get("dS_final"), nthreads=nthreads)
     errs = {"o": relerr(to64(o), ro), "state": relerr(to64(st), rst)}
-    if rck.shape[0]:
-        errs["ckpt"] = relerr(to64(ck), rck)
+    if rck.shape[0]:  # the fp32 states (at the start of the saved record)
+        errs["ckpt"] = relerr(to64(ck.reshape(-1)[:rck.size].reshape(rck.shape)), rck)
     for n in VG_GRADS:
         errs[n] = relerr(to64(g[n]), rg[n])
     say("[vg] errors " + " ".join("%s=%.2e" % kv for kv in errs.items()))
@@ -231,3 +232,55 @@ def test_vg_chunk_state_in_place():
     torch.cuda.synchronize()
     assert st2.data_ptr() == s.data_ptr()
     assert torch.equal(o, o2) and torch.equal(st, s)
+
+
+# ---- the chunk form's saved record (save=True: the forward writes the rows,
+# matrices and X the backward reads, the backward recomputes none of them)
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 32), (128, 64), (192, 128)])
+def test_vg_saved_shapes(Dk, Dv):
+    B, T = 2, 141
+    mask = np.ones((B, T), dtype=np.uint8)
+    mask[0, 5] = 0
+    mask[0, 63:66] = 0
+    mask[1, 100:] = 0
+    c = inputs.make_vg_case("vg_saved_Dk%d_Dv%d" % (Dk, Dv), B, T, 2, 4, Dk, Dv, "bf16",
+                            9600 + Dk + Dv, mask=mask)
+    compare_vg(c, algo=binding.ALGO_CHUNK, save=True)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_vg_saved_edges(T):
+    compare_vg(inputs.vg_edge(T, masked=True, dtype="bf16"), algo=binding.ALGO_CHUNK, save=True)
+
+
+def test_vg_saved_qwen35_9b_t256():
+    compare_vg(inputs.vg_qwen35_9b(256), save=True)
+
+
+def test_vg_saved_long_memory():
+    c = inputs.make_vg_case("vg_saved_long_memory", 1, 2048, 2, 4, 128, 128, "bf16", 9800,
+                            lg_mu=-6.0, lg_sigma=1.0)
+    compare_vg(c, nthreads=16, algo=binding.ALGO_CHUNK, save=True)
+
+
+def test_vg_saved_repeat_and_unsaved():
+    """Saved runs are bit-identical to each other, and agree with the path that
+    recomputes (same tolerance as against the oracle: the two compute X in
+    different kernels, with different accumulation orders)."""
+    c = inputs.vg_qwen35_9b(256)
+    say("[vg saved] case=%s" % c.name)
+    t = upload_vg(c)
+    runs = [run_vg(t, save=True) for _ in range(2)]
+    base = run_vg(t)
+    torch.cuda.synchronize()
+    (o1, s1, c1, g1), (o2, s2, c2, g2) = runs
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and torch.equal(c1, c2)
+    for n in VG_GRADS:
+        assert torch.equal(g1[n], g2[n]), n
+    o0, s0, _, g0 = base
+    errs = {"o": relerr(to64(o1), to64(o0)), "state": relerr(to64(s1), to64(s0))}
+    for n in VG_GRADS:
+        errs[n] = relerr(to64(g1[n]), to64(g0[n]))
+    say("[vg saved vs recomputed] " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
