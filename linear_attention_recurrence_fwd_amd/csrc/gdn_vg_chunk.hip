@@ -83,13 +83,20 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
 
 template <int DK>
 struct VgPrep {
-  static constexpr int RS = DK + 8;      // bf16 row stride of the staged k / q rows
-  static constexpr int GS = DK + 4;      // fp32 row stride of Gamma
+  // The channels go through in passes of CW: the staged k / q / Gamma rows of
+  // one pass (36 KB) share the LDS with the matrices of the last phase (52
+  // KB), which leaves room for two workgroups per compute unit.  The Gram
+  // sums take raw rows times the decays; the norms factor out of every sum
+  // (A[t,s] = rk_t rk_s sum_i k_ti k_si e^{...}) and are applied at the end.
+  static constexpr int CW = 64;          // channels per pass
+  static constexpr int NPASS = DK / CW;
+  static constexpr int RS = CW + 8;      // bf16 row stride of the staged k / q rows
+  static constexpr int GS = CW + 4;      // fp32 row stride of Gamma
   static constexpr int SP = tri::SP;
   static constexpr int NTASK = 40;       // (sub-block, 4x4 tile) tasks of the far channels
-  static constexpr int NLD = L * DK / 8 / NT;  // 16-byte pieces of one of k, q per thread
-  static constexpr int NLG = L * DK / 4 / NT;  // 16-byte pieces of lg per thread
-  static_assert(L * DK / 8 % NT == 0 && L * DK / 4 % NT == 0, "whole pieces per thread");
+  static constexpr int NLD = L * CW / 8 / NT;  // 16-byte pieces of one of k, q per thread and pass
+  static constexpr int NLG = L * CW / 4 / NT;  // 16-byte pieces of lg per thread and pass
+  static_assert(DK % CW == 0 && L * CW / 8 % NT == 0 && L * CW / 4 % NT == 0, "whole pieces per thread");
   struct Rows {
     bf16 k[L * RS];
     bf16 q[L * RS];
@@ -109,8 +116,9 @@ struct VgPrep {
     alignas(16) float dp[NTASK * 32];  // far-channel sums of the diagonal sub-blocks: 16 of A, 16 of P per task
     alignas(16) float dg[4][2][16][17];  // diagonal sub-blocks over the channels in range (A, P)
     float rk[L], rq[L], beta[L], valid[L];
-    unsigned char far[4][DK];            // channel i decays by more than e^kDiagSpan inside sub-block I
-    unsigned long long fmask[4][4];      // the same as bits: channels 64 w .. 64 w + 63
+    unsigned char far[4][CW];            // channel c0 + i decays by more than e^kDiagSpan inside sub-block I
+    unsigned long long fmask[4];         // the same as bits
+    float gtot[4][CW];                   // per wave: the sum of lg over its 16 steps
   };
 
   __device__ static void run(const VgChunkPrepArgs& p, Smem& sm) {
@@ -129,58 +137,20 @@ struct VgPrep {
     const uint32_t lg_row = d.Hv * DK;
     const float* lgc = p.lg + ((static_cast<size_t>(b) * d.T + t0) * d.Hv + h) * DK;
     const size_t cidx = static_cast<size_t>(bh) * NC + c;
+    const size_t rowbase = cidx * L * DK;
 
-    // ---- k / q / lg rows of the chunk (clamped into the sequence), all
-    // loads issued before any is used; beta and the step's validity (wave 0)
-    uint4 kv[NLD], qv[NLD];
-    float4 gv[NLG];
-#pragma unroll
-    for (int e = 0; e < NLD; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-      const uint32_t o = static_cast<uint32_t>(min(t, tl)) * qk_row + i8;
-      kv[e] = *reinterpret_cast<const uint4*>(kc + o);
-      qv[e] = *reinterpret_cast<const uint4*>(qc + o);
-    }
-#pragma unroll
-    for (int e = 0; e < NLG; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 4), i4 = 4 * (u % (DK / 4));
-      gv[e] = *reinterpret_cast<const float4*>(lgc + static_cast<uint32_t>(min(t, tl)) * lg_row + i4);
-    }
-    if (w == 0) {
-      const int t = min(l, tl);
-      const size_t o = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
-      const float bv = to_f32(static_cast<const bf16*>(p.b)[o]);
-      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.b,
-                                  p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-      const uint32_t mrow = static_cast<uint32_t>(b * d.T + t0 + t);
-      const bool valid = l < Lc && (p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, mrow, 0, 0) != 0);
-      sm.beta[l] = valid ? sigmoid_f(bv) : 0.f;
-      sm.valid[l] = valid ? 1.f : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < NLD; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-      *reinterpret_cast<uint4*>(&sm.u.r.k[t * RS + i8]) = kv[e];
-      *reinterpret_cast<uint4*>(&sm.u.r.q[t * RS + i8]) = qv[e];
-    }
-#pragma unroll
-    for (int e = 0; e < NLG; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 4), i4 = 4 * (u % (DK / 4));
-      *reinterpret_cast<float4*>(&sm.u.r.gam[t * GS + i4]) = gv[e];
-    }
-    __syncthreads();
-
-    // ---- norm factors (four lanes per row) and Gamma (one thread per
-    // channel, a running sum over the steps; a masked step or a row past the
-    // end adds 0)
+    // ---- the first pass's rows, then the norm factors (four lanes per row,
+    // from the whole rows) and beta and the step's validity (wave 0)
     {
       const int t = tid >> 2, part = tid & 3;
+      const uint32_t o = static_cast<uint32_t>(min(t, tl)) * qk_row + (DK / 4) * part;
+      constexpr int NQ = DK / 4 / 8;  // 16-byte pieces of a quarter row
       float kk = 0.f, qq = 0.f;
 #pragma unroll
-      for (int e = 0; e < DK / 32; ++e) {
+      for (int e = 0; e < NQ; ++e) {
         float kf[8], qf[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[t * RS + (DK / 4) * part + 8 * e]), kf);
-        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[t * RS + (DK / 4) * part + 8 * e]), qf);
+        unpack8(*reinterpret_cast<const uint4*>(kc + o + 8 * e), kf);
+        unpack8(*reinterpret_cast<const uint4*>(qc + o + 8 * e), qf);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           kk = fmaf(kf[x], kf[x], kk);
@@ -195,120 +165,156 @@ struct VgPrep {
         sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(qq + kNormEps) : 0.f;
       }
     }
-    int farbits = 0;
-    if (tid < DK) {
-      float x[L];
-#pragma unroll
-      for (int t = 0; t < L; ++t) x[t] = sm.valid[t] * sm.u.r.gam[t * GS + tid];
-#pragma unroll
-      for (int t = 1; t < L; ++t) x[t] += x[t - 1];
-#pragma unroll
-      for (int t = 0; t < L; ++t) sm.u.r.gam[t * GS + tid] = x[t];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const float gc = I == 0 ? 0.f : x[16 * I - 1];
-        const int f = gc - x[16 * I + 15] > kDiagSpan ? 1 : 0;
-        sm.far[I][tid] = static_cast<unsigned char>(f);
-        farbits |= f << I;
-      }
+    if (w == 0) {
+      const int t = min(l, tl);
+      const size_t o = (static_cast<size_t>(b) * d.T + t0 + t) * d.Hv + h;
+      const float bv = to_f32(static_cast<const bf16*>(p.b)[o]);
+      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.b,
+                                  p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+      const uint32_t mrow = static_cast<uint32_t>(b * d.T + t0 + t);
+      const bool valid = l < Lc && (p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, mrow, 0, 0) != 0);
+      sm.beta[l] = valid ? sigmoid_f(bv) : 0.f;
+      sm.valid[l] = valid ? 1.f : 0.f;
     }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const unsigned long long m = __ballot((farbits >> I) & 1);
-      if (l == 0) sm.fmask[I][w] = m;
-    }
-    __syncthreads();
 
-    // ---- A and P off the diagonal sub-blocks: wave I (1..3) takes row block
-    // I against the column blocks J < I, reference r = 16 I - 1
-    f32x4 accA[3], accP[3];
+    // sums over the passes: A and P off the diagonal sub-blocks (waves 1..3:
+    // row block I = w against the column blocks J < I, reference r = 16 I - 1),
+    // the diagonal sub-block w over the channels in range, and the far
+    // channels' fp32 tasks (threads < NTASK), all of raw rows
+    f32x4 accA[3], accP[3], da = f4zero(), dpq = f4zero();
 #pragma unroll
     for (int J = 0; J < 3; ++J) accA[J] = accP[J] = f4zero();
-    if (w >= 1) {
-      const int I = w, r = 16 * I - 1, ta = 16 * I + lr;
-      const float rkt = sm.rk[ta], rqt = sm.rq[ta];
+    float pa[16], pp[16];
 #pragma unroll
-      for (int kt = 0; kt < DK / 32; ++kt) {
-        const int i0 = 32 * kt + 8 * lg;
-        float kf[8], qf[8], ex[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[ta * RS + i0]), kf);
-        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[ta * RS + i0]), qf);
-        float gr[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          gr[x] = sm.u.r.gam[r * GS + i0 + x];
-          ex[x] = __expf(sm.u.r.gam[ta * GS + i0 + x] - gr[x]);
-          kf[x] *= rkt * ex[x];
-          qf[x] *= rqt * ex[x];
-        }
-        const bf16x8 ak = as_bf16x8(pack8(kf)), aq = as_bf16x8(pack8(qf));
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-          if (J >= I) continue;
-          const int su = 16 * J + lr;
-          const float rku = sm.rk[su];
-          float uf[8];
-          unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[su * RS + i0]), uf);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) uf[x] *= rku * __expf(gr[x] - sm.u.r.gam[su * GS + i0 + x]);
-          const bf16x8 bk = as_bf16x8(pack8(uf));
-          accA[J] = mfma16(ak, bk, accA[J]);
-          accP[J] = mfma16(aq, bk, accP[J]);
-        }
-      }
-    }
+    for (int x = 0; x < 16; ++x) pa[x] = pp[x] = 0.f;
 
-    // ---- the diagonal sub-blocks: wave w takes sub-block w on MFMA with the
-    // split at c = 16 w - 1 (G_{-1} = 0) over the channels that decay by at
-    // most e^kDiagSpan inside it (both factors then stay in the normal range);
-    // the other channels in fp32 below
-    {
-      const int b0 = 16 * w, ta = b0 + lr;
-      const float rkt = sm.rk[ta], rqt = sm.rq[ta];
-      f32x4 da = f4zero(), dpq = f4zero();
 #pragma unroll
-      for (int kt = 0; kt < DK / 32; ++kt) {
-        const int i0 = 32 * kt + 8 * lg;
-        float kf[8], qf[8];
-        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[ta * RS + i0]), kf);
-        unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[ta * RS + i0]), qf);
-        float ka[8], kb[8], qa[8];
+    for (int pc = 0; pc < NPASS; ++pc) {
+      const int c0 = pc * CW;
+      // the pass's k / q / lg rows (clamped into the sequence), all loads
+      // issued before any is used
+      // (vector-typed registers: arrays of the HIP vector structs would be
+      // copied through private memory)
+      u32x4 kv[NLD], qv[NLD], gv[NLG];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float gcx = w == 0 ? 0.f : sm.u.r.gam[(b0 - 1) * GS + i0 + x];
-          const float gx = sm.u.r.gam[ta * GS + i0 + x];
-          const bool near = sm.far[w][i0 + x] == 0;
-          const float dn = near ? __expf(gx - gcx) : 0.f, up = near ? __expf(gcx - gx) : 0.f;
-          ka[x] = kf[x] * rkt * dn;
-          qa[x] = qf[x] * rqt * dn;
-          kb[x] = kf[x] * rkt * up;
-        }
-        const bf16x8 akb = as_bf16x8(pack8(ka)), aqb = as_bf16x8(pack8(qa)), bkb = as_bf16x8(pack8(kb));
-        // the B operand is row s = ta of the same sub-block: each lane holds both
-        da = mfma16(akb, bkb, da);
-        dpq = mfma16(aqb, bkb, dpq);
+      for (int e = 0; e < NLD; ++e) {
+        const int u = tid + e * NT, t = u / (CW / 8), i8 = 8 * (u % (CW / 8));
+        const uint32_t o = static_cast<uint32_t>(min(t, tl)) * qk_row + c0 + i8;
+        kv[e] = *reinterpret_cast<const u32x4*>(kc + o);
+        qv[e] = *reinterpret_cast<const u32x4*>(qc + o);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sm.dg[w][0][4 * lg + r][lr] = da[r];
-        sm.dg[w][1][4 * lg + r][lr] = dpq[r];
+      for (int e = 0; e < NLG; ++e) {
+        const int u = tid + e * NT, t = u / (CW / 4), i4 = 4 * (u % (CW / 4));
+        gv[e] = *reinterpret_cast<const u32x4*>(lgc + static_cast<uint32_t>(min(t, tl)) * lg_row + c0 + i4);
       }
-    }
+      if (pc > 0) __syncthreads();  // the previous pass is done with the staged rows
+#pragma unroll
+      for (int e = 0; e < NLD; ++e) {
+        const int u = tid + e * NT, t = u / (CW / 8), i8 = 8 * (u % (CW / 8));
+        *reinterpret_cast<u32x4*>(&sm.u.r.k[t * RS + i8]) = kv[e];
+        *reinterpret_cast<u32x4*>(&sm.u.r.q[t * RS + i8]) = qv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < NLG; ++e) {
+        const int u = tid + e * NT, t = u / (CW / 4), i4 = 4 * (u % (CW / 4));
+        *reinterpret_cast<u32x4*>(&sm.u.r.gam[t * GS + i4]) = gv[e];
+      }
+      __syncthreads();
 
-    // ---- ... and in fp32 for the far channels: task (block I, 4x4 tile);
-    // raw-row products, scaled by the norms when summed
-    if (tid < NTASK) {
-      const int I = tid / 10, ti = tid % 10, rest = tid;
-      const int tt = tile_t(ti), uu = tile_u(ti);
-      const int tb = 16 * I + 4 * tt, ub = 16 * I + 4 * uu;
-      float pa[16], pp[16];
+      // ---- Gamma: wave w sums steps 16 w .. 16 w + 15 of channel l of the
+      // pass in turn (a masked step or a row past the end adds 0), then adds
+      // the earlier waves' totals in order; the far flags of sub-block w
+      {
+        float x[16];
 #pragma unroll
-      for (int x = 0; x < 16; ++x) pa[x] = pp[x] = 0.f;
-      const bool split = tt > uu;  // different 4-step groups: split at the end of ub's group
-      for (int wd = 0; wd < 4; ++wd) {
-        unsigned long long m = sm.fmask[I][wd];
+        for (int t = 0; t < 16; ++t) x[t] = sm.valid[16 * w + t] * sm.u.r.gam[(16 * w + t) * GS + l];
+#pragma unroll
+        for (int t = 1; t < 16; ++t) x[t] += x[t - 1];
+        sm.gtot[w][l] = x[15];
+        __syncthreads();
+        float before = 0.f;  // G at the step before the block (0 before the chunk)
+        for (int J = 0; J < w; ++J) before += sm.gtot[J][l];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) sm.u.r.gam[(16 * w + t) * GS + l] = x[t] + before;
+        const int f = before - (x[15] + before) > kDiagSpan ? 1 : 0;
+        sm.far[w][l] = static_cast<unsigned char>(f);
+        const unsigned long long m = __ballot(f);
+        if (l == 0) sm.fmask[w] = m;
+      }
+      __syncthreads();
+
+      // ---- A and P off the diagonal sub-blocks
+      if (w >= 1) {
+        const int I = w, r = 16 * I - 1, ta = 16 * I + lr;
+#pragma unroll
+        for (int kt = 0; kt < CW / 32; ++kt) {
+          const int i0 = 32 * kt + 8 * lg;
+          float kf[8], qf[8];
+          unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[ta * RS + i0]), kf);
+          unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[ta * RS + i0]), qf);
+          float gr[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            gr[x] = sm.u.r.gam[r * GS + i0 + x];
+            const float ex = __expf(sm.u.r.gam[ta * GS + i0 + x] - gr[x]);
+            kf[x] *= ex;
+            qf[x] *= ex;
+          }
+          const bf16x8 ak = as_bf16x8(pack8(kf)), aq = as_bf16x8(pack8(qf));
+#pragma unroll
+          for (int J = 0; J < 3; ++J) {
+            if (J >= I) continue;
+            const int su = 16 * J + lr;
+            float uf[8];
+            unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[su * RS + i0]), uf);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) uf[x] *= __expf(gr[x] - sm.u.r.gam[su * GS + i0 + x]);
+            const bf16x8 bk = as_bf16x8(pack8(uf));
+            accA[J] = mfma16(ak, bk, accA[J]);
+            accP[J] = mfma16(aq, bk, accP[J]);
+          }
+        }
+      }
+
+      // ---- the diagonal sub-blocks: wave w takes sub-block w on MFMA with the
+      // split at c = 16 w - 1 (G_{-1} = 0) over the channels that decay by at
+      // most e^kDiagSpan inside it (both factors then stay in the normal range)
+      {
+        const int b0 = 16 * w, ta = b0 + lr;
+#pragma unroll
+        for (int kt = 0; kt < CW / 32; ++kt) {
+          const int i0 = 32 * kt + 8 * lg;
+          float kf[8], qf[8];
+          unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[ta * RS + i0]), kf);
+          unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[ta * RS + i0]), qf);
+          float ka[8], kb[8], qa[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const float gcx = w == 0 ? 0.f : sm.u.r.gam[(b0 - 1) * GS + i0 + x];
+            const float gx = sm.u.r.gam[ta * GS + i0 + x];
+            const bool near = sm.far[w][i0 + x] == 0;
+            const float dn = near ? __expf(gx - gcx) : 0.f, up = near ? __expf(gcx - gx) : 0.f;
+            ka[x] = kf[x] * dn;
+            qa[x] = qf[x] * dn;
+            kb[x] = kf[x] * up;
+          }
+          const bf16x8 akb = as_bf16x8(pack8(ka)), aqb = as_bf16x8(pack8(qa)), bkb = as_bf16x8(pack8(kb));
+          // the B operand is row s = ta of the same sub-block: each lane holds both
+          da = mfma16(akb, bkb, da);
+          dpq = mfma16(aqb, bkb, dpq);
+        }
+      }
+
+      // ---- ... and in fp32 for the far channels: task (block I, 4x4 tile)
+      if (tid < NTASK) {
+        const int I = tid / 10, ti = tid % 10;
+        const int tt = tile_t(ti), uu = tile_u(ti);
+        const int tb = 16 * I + 4 * tt, ub = 16 * I + 4 * uu;
+        const bool split = tt > uu;  // different 4-step groups: split at the end of ub's group
+        unsigned long long m = sm.fmask[I];
         while (m) {
-          const int i = 64 * wd + __builtin_ctzll(m);
+          const int i = __builtin_ctzll(m);
           m &= m - 1;
           float gt[4], gu[4], kt_[4], qt_[4], ku[4];
 #pragma unroll
@@ -347,20 +353,11 @@ struct VgPrep {
           }
         }
       }
-      float* dst = &sm.dp[rest * 32];
-#pragma unroll
-      for (int x = 0; x < 16; x += 4) {
-        *reinterpret_cast<float4*>(&dst[x]) = make_float4(pa[x], pa[x + 1], pa[x + 2], pa[x + 3]);
-        *reinterpret_cast<float4*>(&dst[16 + x]) = make_float4(pp[x], pp[x + 1], pp[x + 2], pp[x + 3]);
-      }
-    }
 
-    // ---- the pre-scaled rows: Kb, Kh ([t][i]); forward Qb ([t][i]), backward
-    // Kb^T, Qb^T ([i][t]); and the chunk scalars (beta, e^{G_L})
-    {
-      const size_t rowbase = cidx * L * DK;
-      for (int u = tid; u < L * DK / 8; u += NT) {
-        const int t = u / (DK / 8), i0 = 8 * (u % (DK / 8));
+      // ---- the pre-scaled rows of the pass's channels: Kb, Kh ([t][i]);
+      // forward Qb ([t][i]); backward Kb^T, Qb^T ([i][t]); e^{G_L}
+      for (int u = tid; u < L * CW / 8; u += NT) {
+        const int t = u / (CW / 8), i0 = 8 * (u % (CW / 8));
         float kf[8], qf[8], kh[8];
         unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.k[t * RS + i0]), kf);
         unpack8(*reinterpret_cast<const uint4*>(&sm.u.r.q[t * RS + i0]), qf);
@@ -373,14 +370,14 @@ struct VgPrep {
           kf[x] *= rkt * e;
           qf[x] *= rqt * e;
         }
-        const size_t o = rowbase + static_cast<size_t>(t) * DK + i0;
+        const size_t o = rowbase + static_cast<size_t>(t) * DK + c0 + i0;
         *reinterpret_cast<uint4*>(p.cb.Kh + o) = pack8(kh);
         *reinterpret_cast<uint4*>(p.cb.Kb + o) = pack8(kf);
         if (fwd) *reinterpret_cast<uint4*>(p.cb.Qb + o) = pack8(qf);
       }
       if (bwd) {
-        for (int u = tid; u < DK * L / 8; u += NT) {
-          const int i = u % DK, t8 = 8 * (u / DK);
+        for (int u = tid; u < CW * L / 8; u += NT) {
+          const int i = u % CW, t8 = 8 * (u / CW);
           float kf[8], qf[8];
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
@@ -389,18 +386,47 @@ struct VgPrep {
             kf[x] = to_f32(sm.u.r.k[t * RS + i]) * sm.rk[t] * e;
             qf[x] = to_f32(sm.u.r.q[t * RS + i]) * sm.rq[t] * e;
           }
-          const size_t o = rowbase + static_cast<size_t>(i) * L + t8;
+          const size_t o = rowbase + static_cast<size_t>(c0 + i) * L + t8;
           *reinterpret_cast<uint4*>(p.cb.KbT + o) = pack8(kf);
           *reinterpret_cast<uint4*>(p.cb.QbT + o) = pack8(qf);
         }
       }
+      if (tid < CW) p.cb.vsc[cidx * VSC_ROWS * L + VSC_EGL * L + c0 + tid] = __expf(sm.u.r.gam[(L - 1) * GS + tid]);
+    }
+
+    // ---- the chunk scalars beyond the passes: beta, and zeros past e^{G_L}
+    {
       float* vsc = p.cb.vsc + cidx * VSC_ROWS * L;
       if (tid < L) vsc[VSC_BETA * L + tid] = sm.beta[tid];
-      for (int i = tid; i < (VSC_ROWS - 1) * L; i += NT)
-        vsc[VSC_EGL * L + i] = i < DK ? __expf(sm.u.r.gam[(L - 1) * GS + i]) : 0.f;
+      for (int i = DK + tid; i < (VSC_ROWS - 1) * L; i += NT) vsc[VSC_EGL * L + i] = 0.f;
+    }
+    // the norm factors of the sums; the diagonal sub-blocks' MFMA part and the
+    // far channels' raw sums (scaled by the norms where they are added)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * w + 4 * lg + r, s = 16 * w + lr;
+      sm.dg[w][0][4 * lg + r][lr] = da[r] * sm.rk[t] * sm.rk[s];
+      sm.dg[w][1][4 * lg + r][lr] = dpq[r] * sm.rq[t] * sm.rk[s];
+    }
+    if (w >= 1) {
+#pragma unroll
+      for (int J = 0; J < 3; ++J)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * w + 4 * lg + r, s = 16 * J + lr;
+          accA[J][r] *= sm.rk[t] * sm.rk[s];
+          accP[J][r] *= sm.rq[t] * sm.rk[s];
+        }
+    }
+    if (tid < NTASK) {
+      float* dst = &sm.dp[tid * 32];
+#pragma unroll
+      for (int x = 0; x < 16; x += 4) {
+        *reinterpret_cast<float4*>(&dst[x]) = make_float4(pa[x], pa[x + 1], pa[x + 2], pa[x + 3]);
+        *reinterpret_cast<float4*>(&dst[16 + x]) = make_float4(pp[x], pp[x + 1], pp[x + 2], pp[x + 3]);
+      }
     }
     __syncthreads();  // the staged rows and Gamma are dead from here on
-
     // ---- N = A diag(beta) and Mq = P diag(beta) (forward only), or A^T, P^T
     // (backward, and both; Mq then comes from P^T); every element written
     // once: the lower off-diagonal sub-blocks by the MFMA waves, the rest here
@@ -431,7 +457,7 @@ struct VgPrep {
       const int bi = e >> 8, t = 16 * bi + ((e >> 4) & 15), s = 16 * bi + (e & 15);
       const int tt = (t >> 2) & 3, uu = (s >> 2) & 3;
       float av = sm.dg[bi][0][t & 15][s & 15], pv = sm.dg[bi][1][t & 15][s & 15];
-      if ((sm.fmask[bi][0] | sm.fmask[bi][1] | sm.fmask[bi][2] | sm.fmask[bi][3]) && uu <= tt) {
+      if (uu <= tt) {  // the far sums (zero where no channel was far)
         const int x = 4 * (t & 3) + (s & 3), rest = bi * 10 + tt * (tt + 1) / 2 + uu;
         av += sm.dp[rest * 32 + x] * sm.rk[t] * sm.rk[s];
         pv += sm.dp[rest * 32 + 16 + x] * sm.rq[t] * sm.rk[s];
