@@ -18,34 +18,47 @@
 // are taken in 16-step sub-blocks: for t in sub-block I > J (s in J) with
 // r = 16 I - 1 the last step before I,
 //   e^{G_t - G_s} = e^{G_t - G_r} e^{G_r - G_s}    (both factors <= 1),
-// a bf16 MFMA product of rows scaled by each factor; inside a diagonal
-// sub-block every pair is taken in fp32 on the vector units, with the same
-// split at the end of the earlier 4-step group for pairs in different groups
-// and the exact exponential within a group.
+// a bf16 MFMA product of rows scaled by each factor.  Inside a diagonal
+// sub-block the same split at the step before the block holds for every
+// channel that decays by at most e^60 there (both factors stay in the normal
+// range of fp32 and bf16), also on MFMA; the other channels of the block are
+// taken in fp32 on the vector units, with the split at the end of the earlier
+// 4-step group for pairs in different groups and the exact exponential within
+// a group.
 //
 // Kernels:
-//   vg_chunk_prep  one workgroup per (chunk, batch, value head): Gamma by a
-//                  per-channel scan, the norms, A and P (MFMA off the
-//                  diagonal sub-blocks, fp32 on them), Tx by the blocked
-//                  inverse of gdn_tri.h, and the pre-scaled rows the state
-//                  passes read.
-//   vg_chunk_grad  one workgroup per (chunk, batch, value head): the chunk's
-//                  gradients from dH' (= dL/d the state at the chunk end),
-//                  Ehat (= dv) and eps (= dL/d delta) of the reverse state
-//                  pass, with X recomputed from the fp32 checkpoint:
-//     dQb = dO H^T,  dKb = -Ehat H^T,  dKh = diag(beta) X dH'^T,
+//   vg_chunk_prep  one workgroup per (chunk, batch, value head), the channels
+//                  in passes of 64: Gamma by per-wave running sums, the
+//                  norms (factored out of the Gram sums), A and P, Tx by the
+//                  blocked inverse of gdn_tri.h, and the pre-scaled rows and
+//                  matrices the state passes and the gradient pass read (the
+//                  forward's, the backward's, or both for the saved record).
+//   vg_chunk_x     one workgroup per (chunk, batch, value head): X (the
+//                  forward's saved copy, or recomputed from the fp32
+//                  checkpoint), then
 //     dP = lower(dO X^T) diag(beta),  dA = -strictlower(Ehat X^T) diag(beta),
-//     dbeta_t = eps_t . X_t,
-//   then, per channel i, the three roles of the rows (s the 1/sqrt(Dk) scale):
+//     db_t = (eps_t . X_t) beta_t (1 - beta_t),
+//                  with Ehat (= dv) and eps (= dL/d delta) of the reverse
+//                  state pass.
+//   vg_chunk_grad  one workgroup per (chunk, batch, value head, 32 channels):
+//     dQb = dO H^T,  dKb = -Ehat H^T,  dKh = diag(beta) X dH'^T
+//                  (dH' = dL/d the state at the chunk end), then, per channel
+//                  i, the three roles of the rows (s the 1/sqrt(Dk) scale):
 //     dq_t  = e^{G_t} dQb_t + sum_{u<=t} dP[t,u] kn_u e^{G_t-G_u}            (w.r.t. s qn)
 //     dkR_t = e^{G_t} dKb_t + sum_{u<t}  dA[t,u] kn_u e^{G_t-G_u}            (k as a reader)
 //     dkW_u = e^{G_L-G_u} dKh_u + sum_{t>=u} (dP[t,u] s qn_t + dA[t,u] kn_t) e^{G_t-G_u}  (writer)
 //     dG_t  = s qn_t dq_t + kn_t (dkR_t - dkW_t) + [t = L-1] (e^{G_L} <dH', H> + sum_u Kh_u dKh_u)
 //     dlg_t = sum_{t' >= t} dG_t' (0 on masked steps),   dkn = dkR + dkW;
-//   every e^{G} factor enters as e^{G_t - G_u} with u <= t (so lg enters
-//   through G_t - G_u only).  The expansions take the sub-blocks of the
-//   forward: MFMA with the split at the previous block's end off the
-//   diagonal, fp32 with decays built step by step inside it.
+//                  every e^{G} factor enters as e^{G_t - G_u} with u <= t (so
+//                  lg enters through G_t - G_u only).  The expansions take the
+//                  sub-blocks of the prep: MFMA with the split at the
+//                  previous block's end off the diagonal, on the diagonal MFMA
+//                  where the block's decays allow, else fp32 with decays built
+//                  step by step.  Writes dlg and the value head's parts of the
+//                  rows of dq, dkn.
+//   vg_norm_bwd    one wave per (batch, step, key head): the parts of the key
+//                  head's value heads summed, and the L2-normalisation
+//                  backward of q and k.
 #include "gdn_dev.h"
 #include "gdn_internal.h"
 #include "gdn_tri.h"
