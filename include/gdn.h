@@ -251,19 +251,21 @@ int gdn_decode_conv(const gdn_dims* d, const void* x, const void* conv_w, const 
  * gdn_fwd.  Without save, ckpt has gdn_fwd's layout without save (the fp32
  * states at the chunk boundaries) in both families, so a forward of either
  * family pairs with a backward of either.  With d->save set and the call on
- * CHUNK, ckpt is instead the library's own record: those fp32 states at its
- * start, then what the backward would otherwise recompute, written by
- * gdn_fwd_vg (the per-channel decayed k rows and their transposes, the chunk
- * inverse and Gram matrices, the chunk scalars, and X = v - u of every step
- * in bf16); such a record is read only by a gdn_bwd_vg with the same dims
+ * CHUNK, ckpt is instead the library's own record, written by gdn_fwd_vg:
+ * the state at every chunk start (the initial state included) rounded to
+ * bf16, the precision the gradient products take it in, and what the
+ * backward would otherwise recompute (the per-channel decayed k rows and their
+ * transposes, the chunk inverse and Gram matrices, the chunk scalars, and X =
+ * v - u of every step in bf16).  It holds no fp32 states; such a record is
+ * read only by a gdn_bwd_vg with the same dims
  * (including save), and ckpt may then not be NULL in either call
  * (GDN_ERR_INVALID_ARG).  SCAN ignores save.  The sizes of ckpt and of the
  * workspaces come from the _vg queries (they depend on the family and save).
  */
 /* Number of fp32 elements of gdn_fwd_vg's checkpoint buffer: as
  * gdn_ckpt_elems without save, or with d->save set on CHUNK the record's size,
- * about (ceil(T/64) - 1) * B * Hv * Dk * Dv + ceil(T/64) * B * Hv * (128 Dk +
- * 6k + 512) + B * T * Hv * Dv / 2.  gdn_vg_ckpt_bytes: the same in bytes. */
+ * about ceil(T/64) * B * Hv * (Dk * Dv / 2 + 128 Dk + 6k + 512) + B * T * Hv *
+ * Dv / 2.  gdn_vg_ckpt_bytes: the same in bytes. */
 int gdn_vg_ckpt_elems(const gdn_dims* d, size_t* out);
 int gdn_vg_ckpt_bytes(const gdn_dims* d, size_t* out);
 int gdn_fwd_vg_workspace_bytes(const gdn_dims* d, size_t* out);

@@ -283,17 +283,18 @@ bool use_vg_chunk(const gdn_dims* p) {
   return p->T > 1 && vg_chunk_ok(p);
 }
 
-// Under gdn_dims.save (chunk form) the checkpoint buffer holds the fp32
-// states at the chunk boundaries (as without save, at its start), then the
-// chunk rows and matrices the backward reads and X of every step, all
-// written by the forward (offsets in fp32 elements, 256-byte aligned).
+// Under gdn_dims.save (chunk form) the checkpoint buffer holds the state at
+// every chunk start (the initial state included) in bf16, the precision the
+// gradient pass's products take it in, then the chunk rows and matrices the
+// backward reads and X of every step, all written by the forward (offsets in
+// fp32 elements, 256-byte aligned).  It holds no fp32 states.
 struct VgSaved {
-  size_t Kb, Kh, KbT, QbT, Tx, AtT, PqT, vsc, X, total;
+  size_t HB, Kb, Kh, KbT, QbT, Tx, AtT, PqT, vsc, X, total;
 };
 
 VgSaved vg_saved_layout(const Dims& d) {
   VgSaved S{};
-  size_t off = align_up(ckpt_state_elems(d) * sizeof(float)) / sizeof(float);
+  size_t off = 0;
   auto take = [&](size_t nfloat) {
     size_t o = off;
     off += align_up(nfloat * sizeof(float)) / sizeof(float);
@@ -301,6 +302,7 @@ VgSaved vg_saved_layout(const Dims& d) {
   };
   const size_t bhc = static_cast<size_t>(d.B) * d.Hv * d.nchunk();
   const size_t rows = (bhc * 64 * d.Dk + 1) / 2, mats = (bhc * 64 * 64 + 1) / 2;  // bf16, in floats
+  S.HB = take((state_slots_elems(d) + 1) / 2);
   S.Kb = take(rows);
   S.Kh = take(rows);
   S.KbT = take(rows);
@@ -374,14 +376,16 @@ gdn::StepScalars vg_scalars(void* ws, const VgLayout& L) {
 }
 
 // The chunk buffers in the workspace, or (saved) in the checkpoint buffer;
-// under save the forward's Qb and Mq stay in its workspace, and cb.X is set,
-// so that the forward's state pass stores X there.
+// under save the forward's Qb and Mq stay in its workspace, and cb.Hb and
+// cb.X are set, so that the forward's state pass stores the bf16 chunk-start
+// states and X there.
 gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd, const Dims& d, const float* ckpt,
                              bool saved) {
   gdn::ChunkBufs cb{};
   if (saved) {
     const VgSaved S = vg_saved_layout(d);
     float* rec = const_cast<float*>(ckpt);
+    cb.Hb = reinterpret_cast<gdn::bf16*>(rec + S.HB);
     cb.Kb = reinterpret_cast<gdn::bf16*>(rec + S.Kb);
     cb.Kh = reinterpret_cast<gdn::bf16*>(rec + S.Kh);
     cb.KbT = reinterpret_cast<gdn::bf16*>(rec + S.KbT);
@@ -772,7 +776,8 @@ int gdn_fwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
     const gdn::ChunkBufs cb = vg_chunk_bufs(ws, L, false, dd, ckpt, saved);
     gdn::VgChunkPrepArgs pa{dd, q, k, b, lg, mask, cb, saved ? 2 : 0};
     if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(pa, st); })) return GDN_ERR_HIP;
-    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, ckpt};
+    // under save the states go to the record as bf16 only
+    gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, saved ? nullptr : ckpt};
     fa.vg = 1;
     if (!launch(st, [&] { return gdn::launch_chunk_fwd(fa, st); })) return GDN_ERR_HIP;
     return GDN_OK;

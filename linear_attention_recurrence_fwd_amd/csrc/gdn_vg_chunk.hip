@@ -755,7 +755,7 @@ struct VgX {
 // the blocks.  Gamma, k and q are held channel-major (the expansions read 8 or
 // 16 consecutive steps of one channel); the transposed operands of dP and dA
 // come from transposing LDS reads.
-template <int DK, int DV>
+template <int DK, int DV, bool HBF>
 struct VgG {
   static constexpr int CH = kVgGradChannels;
   static constexpr int NTL = CH / 16;  // 16-channel tiles per workgroup
@@ -833,8 +833,10 @@ struct VgG {
     const size_t vrow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hv + h;
     const size_t krow0 = (static_cast<size_t>(b) * d.T + t0) * d.Hk + j;
     const size_t cidx = static_cast<size_t>(bh) * NC + c;
+    // H: the fp32 checkpoint (or state0), or (HBF) the saved bf16 state at the chunk start
     const float* H = c == 0 ? (p.state0 ? p.state0 + static_cast<size_t>(bh) * DK * DV : nullptr)
                             : p.ckpt + (static_cast<size_t>(c - 1) * d.B * d.Hv + bh) * DK * DV;
+    const bf16* Hb = HBF ? p.cb.Hb + (static_cast<size_t>(c) * d.B * d.Hv + bh) * DK * DV : nullptr;
     const bf16* dHp = p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + bh) * DK * DV;
 
     // ---- every global read, issued before any is used
@@ -859,8 +861,14 @@ struct VgG {
 #pragma unroll
       for (int e = 0; e < NH; ++e) {
         const int u = tid + e * NT, ch = u / (DV / 4), v4 = 4 * (u % (DV / 4));
-        hv[e] = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(ch0 + ch) * DV + v4)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (HBF) {
+          const uint2 h4 = *reinterpret_cast<const uint2*>(Hb + static_cast<size_t>(ch0 + ch) * DV + v4);
+          hv[e] = make_float4(__uint_as_float(h4.x << 16), __uint_as_float(h4.x & 0xffff0000u),
+                              __uint_as_float(h4.y << 16), __uint_as_float(h4.y & 0xffff0000u));
+        } else {
+          hv[e] = H ? *reinterpret_cast<const float4*>(H + static_cast<size_t>(ch0 + ch) * DV + v4)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
       }
 #pragma unroll
       for (int e = 0; e < NDH; ++e) {  // clamped: a thread past the last piece reloads it
@@ -1283,10 +1291,10 @@ __global__ void __launch_bounds__(NT) vg_chunk_x_kernel(VgChunkGradArgs p) {
   VgX<DK, DV, XSV>::run(p, sm);
 }
 
-template <int DK, int DV>
+template <int DK, int DV, bool HBF>
 __global__ void __launch_bounds__(NT) vg_chunk_grad_kernel(VgChunkGradArgs p) {
-  __shared__ typename VgG<DK, DV>::Smem sm;
-  VgG<DK, DV>::run(p, sm);
+  __shared__ typename VgG<DK, DV, HBF>::Smem sm;
+  VgG<DK, DV, HBF>::run(p, sm);
 }
 
 template <int DK, bool X>
@@ -1301,8 +1309,10 @@ hipError_t launch_grad_dk(const VgChunkGradArgs& a, hipStream_t st) {
       vg_chunk_x_kernel<DK, DV, true><<<grid, NT, 0, st>>>(a); \
     else if (X)                                                \
       vg_chunk_x_kernel<DK, DV, false><<<grid, NT, 0, st>>>(a); \
+    else if (a.cb.Hb != nullptr)                               \
+      vg_chunk_grad_kernel<DK, DV, true><<<grid, NT, 0, st>>>(a); \
     else                                                       \
-      vg_chunk_grad_kernel<DK, DV><<<grid, NT, 0, st>>>(a);    \
+      vg_chunk_grad_kernel<DK, DV, false><<<grid, NT, 0, st>>>(a); \
     break;
     GDN_VG_DV(32)
     GDN_VG_DV(64)

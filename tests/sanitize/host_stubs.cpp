@@ -127,7 +127,7 @@ void touch_vg_grad(const VgChunkGradArgs& a) {
   touch_chunk(a.d, a.cb);
   touch(a.E, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dHend, slots(a.d) * 2);
-  touch_ckpt(a.d, a.ckpt);
+  if (a.cb.Hb == nullptr) touch_ckpt(a.d, a.ckpt);  // else the bf16 states of the saved record (touch_chunk)
   touch(a.X, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dPA, nmat(a.d) * 2 * 64 * 64 * 2);
   touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 4);
