@@ -47,10 +47,16 @@ constexpr int NT = 256;
 
 template <int DK>
 struct ChunkPrep {
-  static constexpr int RS = DK + 8;  // bf16 row stride of the staged k / q rows (conflict-free operand reads)
+  // The k / q rows are staged in passes of CW channels (18 KB), which share
+  // the LDS with the matrices of the last phase (35 KB): four workgroups fit
+  // on a compute unit at every Dk.  The Gram products accumulate over the
+  // passes in the order of a single pass.
+  static constexpr int CW = 64;      // channels per pass
+  static constexpr int NPASS = DK / CW;
+  static constexpr int RS = CW + 8;  // bf16 row stride of the staged k / q rows (conflict-free operand reads)
   static constexpr int SP = tri::SP;  // fp32 row stride of N and the staging matrix
-  static constexpr int NLD = L * DK / 8 / NT;  // 16-byte pieces of one of k, q per thread
-  static_assert(L * DK / 8 % NT == 0, "whole pieces per thread");
+  static constexpr int NLD = L * CW / 8 / NT;  // 16-byte pieces of one of k, q per thread and pass
+  static_assert(DK % CW == 0 && L * CW / 8 % NT == 0, "whole pieces per thread");
   struct Rows {
     bf16 k[L * RS];
     bf16 q[L * RS];
@@ -70,10 +76,11 @@ struct ChunkPrep {
 
   __device__ static void store_mat(const Smem& sm, bf16* dst, int tid) { tri::store_mat(sm.u.m.st, dst, tid, NT); }
 
-  // Rows [t][i] of the staged chunk -> dst [i][t] (bf16, L steps per row).
+  // Rows [t][i] of the staged pass -> dst [i][t] (bf16, L steps per row; dst
+  // at the pass's first channel).
   __device__ static void store_transposed(const bf16* rows, bf16* dst, int tid) {
-    for (int u = tid; u < DK * L / 8; u += NT) {
-      const int i = u % DK, t8 = 8 * (u / DK);
+    for (int u = tid; u < CW * L / 8; u += NT) {
+      const int i = u % CW, t8 = 8 * (u / CW);
       uint32_t wv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -104,17 +111,7 @@ struct ChunkPrep {
     const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
     const size_t mat = (static_cast<size_t>(bh) * NC + c) * L * L;
 
-    // ---- k / q rows of the chunk (clamped into the sequence), coalesced
-    // 16-byte loads, all issued before any is used; the gate inputs of step
-    // t = l (wave 0)
-    uint4 kv[NLD], qv[NLD];
-#pragma unroll
-    for (int e = 0; e < NLD; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-      const uint32_t o = static_cast<uint32_t>(min(t, tl)) * qk_row + i8;
-      kv[e] = *reinterpret_cast<const uint4*>(kc + o);
-      qv[e] = *reinterpret_cast<const uint4*>(qc + o);
-    }
+    // ---- the gate inputs of step t = l (wave 0)
     float ell = 0.f, beta = 0.f;
     if (w == 0) {
       // l = -e^{A_log} softplus(min(a + dt_bias, 20)), beta = sigmoid(b);
@@ -132,12 +129,6 @@ struct ChunkPrep {
         beta = sigmoid_f(bv);
       }
     }
-#pragma unroll
-    for (int e = 0; e < NLD; ++e) {
-      const int u = tid + e * NT, t = u / (DK / 8), i8 = 8 * (u % (DK / 8));
-      *reinterpret_cast<uint4*>(&sm.u.r.k[t * RS + i8]) = kv[e];
-      *reinterpret_cast<uint4*>(&sm.u.r.q[t * RS + i8]) = qv[e];
-    }
     if (w == 0) {  // gamma by a wave-wide inclusive scan
       float g = ell;
 #pragma unroll
@@ -149,23 +140,50 @@ struct ChunkPrep {
       sm.ell[l] = ell;
       sm.beta[l] = beta;
     }
-    __syncthreads();
+    const bool fwd_out = p.bwd != 1, bwd_out = p.bwd != 0;
 
     // ---- K K^T and Q K^T (raw rows), wave w = row tile w; Q Q^T on the
-    // diagonal tile gives |q_t|^2
+    // diagonal tile gives |q_t|^2; per pass of CW channels: the k / q rows of
+    // the chunk (clamped into the sequence), coalesced 16-byte loads, and the
+    // raw rows transposed for the backward (written once per key head)
     f32x4 akk[4], aqk[4], aqq = f4zero();
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) akk[ct] = aqk[ct] = f4zero();
 #pragma unroll
-    for (int kt = 0; kt < DK / 32; ++kt) {
-      const int oa = (16 * w + lr) * RS + 32 * kt + 8 * lg;
-      const bf16x8 ak = load_bf16x8(&sm.u.r.k[oa]), aq = load_bf16x8(&sm.u.r.q[oa]);
-      aqq = mfma16(aq, aq, aqq);
+    for (int pc = 0; pc < NPASS; ++pc) {
+      const int c0 = pc * CW;
+      u32x4 kv[NLD], qv[NLD];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const bf16x8 bk = load_bf16x8(&sm.u.r.k[(16 * ct + lr) * RS + 32 * kt + 8 * lg]);
-        akk[ct] = mfma16(ak, bk, akk[ct]);
-        aqk[ct] = mfma16(aq, bk, aqk[ct]);
+      for (int e = 0; e < NLD; ++e) {
+        const int u = tid + e * NT, t = u / (CW / 8), i8 = 8 * (u % (CW / 8));
+        const uint32_t o = static_cast<uint32_t>(min(t, tl)) * qk_row + c0 + i8;
+        kv[e] = *reinterpret_cast<const u32x4*>(kc + o);
+        qv[e] = *reinterpret_cast<const u32x4*>(qc + o);
+      }
+      if (pc > 0) __syncthreads();  // the previous pass is done with the staged rows
+#pragma unroll
+      for (int e = 0; e < NLD; ++e) {
+        const int u = tid + e * NT, t = u / (CW / 8), i8 = 8 * (u % (CW / 8));
+        *reinterpret_cast<u32x4*>(&sm.u.r.k[t * RS + i8]) = kv[e];
+        *reinterpret_cast<u32x4*>(&sm.u.r.q[t * RS + i8]) = qv[e];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kt = 0; kt < CW / 32; ++kt) {
+        const int oa = (16 * w + lr) * RS + 32 * kt + 8 * lg;
+        const bf16x8 ak = load_bf16x8(&sm.u.r.k[oa]), aq = load_bf16x8(&sm.u.r.q[oa]);
+        aqq = mfma16(aq, aq, aqq);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const bf16x8 bk = load_bf16x8(&sm.u.r.k[(16 * ct + lr) * RS + 32 * kt + 8 * lg]);
+          akk[ct] = mfma16(ak, bk, akk[ct]);
+          aqk[ct] = mfma16(aq, bk, aqk[ct]);
+        }
+      }
+      if (first && bwd_out) {
+        const size_t base = (static_cast<size_t>(b * d.Hk + j) * NC + c) * DK * L + static_cast<size_t>(c0) * L;
+        store_transposed(sm.u.r.k, p.cb.KT + base, tid);
+        store_transposed(sm.u.r.q, p.cb.QT + base, tid);
       }
     }
     // norm factors from the Gram diagonals: (|x|^2 + eps)^-1/2, q also / sqrt(Dk)
@@ -182,14 +200,6 @@ struct ChunkPrep {
         sm.rk[t] = in ? 1.f / sqrtf(kk + kNormEps) : 0.f;
         sm.rq[t] = in ? (1.f / sqrtf(static_cast<float>(DK))) / sqrtf(aqq[r] + kNormEps) : 0.f;
       }
-    const bool fwd_out = p.bwd != 1, bwd_out = p.bwd != 0;
-    // ---- raw k and q of the chunk, transposed, for the backward (written
-    // once per key head)
-    if (first && bwd_out) {
-      const size_t base = (static_cast<size_t>(b * d.Hk + j) * NC + c) * DK * L;
-      store_transposed(sm.u.r.k, p.cb.KT + base, tid);
-      store_transposed(sm.u.r.q, p.cb.QT + base, tid);
-    }
     __syncthreads();  // the staged rows are dead from here on; rk, rq visible
 
     // ---- per-step chunk scalars
