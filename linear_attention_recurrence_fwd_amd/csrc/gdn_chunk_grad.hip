@@ -38,7 +38,8 @@ namespace gdn {
 namespace {
 
 constexpr int L = kChunk;   // rows per chunk (padded)
-constexpr int NT = 256;
+constexpr int NT = 512;     // 32 x 16 threads: RPT rows x (4 columns or Dk / 16 channels) each
+constexpr int RPT = L / (NT / 16);  // rows per thread
 constexpr int SLAB = 32;    // Dv columns per pass
 constexpr int GB = 64;      // Dk columns per pass of the Gram matrices
 constexpr int LP = L + 1;   // padded row stride of L x L arrays
@@ -91,22 +92,25 @@ struct ChunkGrad {
     const int c = blockIdx.x, bj = blockIdx.y;
     const int b = bj / d.Hk, j = bj % d.Hk, G = d.G();
     const int t0 = c * L, Lc = min(L, d.T - t0);
-    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
-    const int rt = tid >> 2, rq4 = tid & 3;  // row / quarter for slab loads
+    // lane coordinates; the head loop rebuilds them from an opaque copy of the
+    // thread index, so that the addresses derived from them are not all kept
+    // live across it
+    int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    int rt = tid >> 3, rq8 = tid & 7;  // row / eighth for slab loads
     const size_t slab_sz = static_cast<size_t>(d.B) * d.Hv * DK * d.Dv;
     double* gam = reinterpret_cast<double*>(sm + B_GAM);
     const T* qg = static_cast<const T*>(p.q);
     const T* kg = static_cast<const T*>(p.k);
     auto qk_row = [&](int t) { return (static_cast<size_t>(b) * d.T + t0 + t) * d.Hk + j; };
 
-    // The thread's own TI columns of kn / qn in row 4 tr + a (0 past the end),
+    // The thread's own TI columns of kn / qn in row RPT tr + a (0 past the end),
     // read where they are used (after each head and in the normalisation
     // backward) rather than held in registers across the kernel, where the
     // accumulators of the key-head group already fill the register file.  The
     // row index passes through an empty asm statement so that the compiler
     // cannot prove two reloads equal and keep the values live in between.
     auto own = [&](const T* src, const float* scale, int a, float (&out)[TI]) {
-      const int t = tr * 4 + a;
+      const int t = tr * RPT + a;
       const bool in = t < Lc;
       int ri = in ? static_cast<int>(qk_row(t)) : 0;
       asm volatile("" : "+v"(ri));
@@ -116,9 +120,9 @@ struct ChunkGrad {
       for (int i = 0; i < TI; ++i) out[i] = to_f32(src[row * DK + tc * TI + i]) * sc;
     };
     // ---- the Gram matrices of the chunk
-    float gqk[4][4], gkk[4][4];  // qn_r . kn_s, kn_r . kn_s for r = 4tr+a, s = 4tc+s
+    float gqk[RPT][4], gkk[RPT][4];  // qn_r . kn_s, kn_r . kn_s for r = RPT tr + a, s = 4 tc + s
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < RPT; ++a)
 #pragma unroll
       for (int s = 0; s < 4; ++s) gqk[a][s] = gkk[a][s] = 0.f;
     for (int i0 = 0; i0 < DK; i0 += GW) {
@@ -134,16 +138,18 @@ struct ChunkGrad {
         sm[G_QS + t * (GW + 1) + i] = qv;
       }
       __syncthreads();
+#pragma unroll 4
       for (int i = 0; i < GW; ++i) {
-        float qr[4], kr[4], ks[4];
+        float qr[RPT], kr[RPT], ks[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          qr[a] = sm[G_QS + (tr * 4 + a) * (GW + 1) + i];
-          kr[a] = sm[G_KS + (tr * 4 + a) * (GW + 1) + i];
-          ks[a] = sm[G_KS + (tc * 4 + a) * (GW + 1) + i];
+        for (int a = 0; a < RPT; ++a) {
+          qr[a] = sm[G_QS + (tr * RPT + a) * (GW + 1) + i];
+          kr[a] = sm[G_KS + (tr * RPT + a) * (GW + 1) + i];
         }
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) ks[a] = sm[G_KS + (tc * 4 + a) * (GW + 1) + i];
+#pragma unroll
+        for (int a = 0; a < RPT; ++a)
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
             gqk[a][s] = fmaf(qr[a], ks[s], gqk[a][s]);
@@ -153,10 +159,10 @@ struct ChunkGrad {
       __syncthreads();
     }
 
-    float accQ[4][TI], accK[4][TI];
-    float wq[4][4], wk1[4][4], wk2[4][4];
+    float accQ[RPT][TI], accK[RPT][TI];
+    float wq[RPT][4], wk1[RPT][4], wk2[RPT][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < RPT; ++a) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) accQ[a][i] = accK[a][i] = 0.f;
 #pragma unroll
@@ -164,6 +170,12 @@ struct ChunkGrad {
     }
 
     for (int hh = 0; hh < G; ++hh) {
+      tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      tr = tid >> 4;
+      tc = tid & 15;
+      rt = tid >> 3;
+      rq8 = tid & 7;
       const int h = j * G + hh, bh = b * d.Hv + h;
       // ---- per-step scalars of head h, gamma in fp64
       if (tid < L) {
@@ -185,10 +197,10 @@ struct ChunkGrad {
         sm[B_EG + tid] = expf(static_cast<float>(gam[tid]));
         sm[B_EGL + tid] = expf(static_cast<float>(gam[Lc - 1] - gam[tid]));
       }
-      float accQh[4][TI], accKA[4][TI], accKE[4][TI];
-      float acc_xe[4][4], acc_dox[4][4];
+      float accQh[RPT][TI], accKA[RPT][TI], accKE[RPT][TI];
+      float acc_xe[RPT][4], acc_dox[RPT][4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < RPT; ++a) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) accQh[a][i] = accKA[a][i] = accKE[a][i] = 0.f;
 #pragma unroll
@@ -202,6 +214,12 @@ struct ChunkGrad {
       __syncthreads();
 
       for (int s0 = 0; s0 < d.Dv; s0 += SLAB) {
+        tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        tr = tid >> 4;
+        tc = tid & 15;
+        rt = tid >> 3;
+        rq8 = tid & 7;
         const int ns = min(SLAB, d.Dv - s0);
         // H^T and dH^T slabs, and <dH, H> over them
         for (int e = tid; e < DK * SLAB; e += NT) {
@@ -218,8 +236,8 @@ struct ChunkGrad {
         }
         // X = v - U, eps = ein + (kn . qn) dO, dO slabs (transposed)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = rq4 * 8 + e;
+        for (int e = 0; e < 4; ++e) {
+          const int jj = rq8 * 4 + e;
           float x = 0.f, ev = 0.f, dov = 0.f;
           if (rt < Lc && jj < ns) {
             const size_t o = ((static_cast<size_t>(b) * d.T + t0 + rt) * d.Hv + h) * d.Dv + s0 + jj;
@@ -233,15 +251,16 @@ struct ChunkGrad {
           sm[A_DOT + jj * L + rt] = dov;
         }
         __syncthreads();
-        float rs_q[4], rs_x[4], rs_e[4];
+        float rs_q[RPT], rs_x[RPT], rs_e[RPT];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int t = tr * 4 + a;
+        for (int a = 0; a < RPT; ++a) {
+          const int t = tr * RPT + a;
           const float bet = sm[B_BET + t];
           rs_q[a] = sm[B_EG + t];
           rs_x[a] = sm[B_EGL + t] * bet;
           rs_e[a] = -sm[B_EG + t] * bet;
         }
+#pragma unroll 2
         for (int jj = 0; jj < SLAB; ++jj) {
           float hv[TI], dhv[TI];
 #pragma unroll
@@ -249,17 +268,20 @@ struct ChunkGrad {
             hv[i] = sm[A_HT + jj * HS + tc * TI + i];
             dhv[i] = sm[A_DHT + jj * HS + tc * TI + i];
           }
-          float dor[4], xr[4], er[4], xc[4], ec[4];
+          float dor[RPT], xr[RPT], er[RPT], xc[4], ec[4];
+#pragma unroll
+          for (int a = 0; a < RPT; ++a) {
+            dor[a] = sm[A_DOT + jj * L + tr * RPT + a];
+            xr[a] = sm[A_XT + jj * L + tr * RPT + a];
+            er[a] = sm[A_ET + jj * L + tr * RPT + a];
+          }
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            dor[a] = sm[A_DOT + jj * L + tr * 4 + a];
-            xr[a] = sm[A_XT + jj * L + tr * 4 + a];
-            er[a] = sm[A_ET + jj * L + tr * 4 + a];
             xc[a] = sm[A_XT + jj * L + tc * 4 + a];
             ec[a] = sm[A_ET + jj * L + tc * 4 + a];
           }
 #pragma unroll
-          for (int a = 0; a < 4; ++a) {
+          for (int a = 0; a < RPT; ++a) {
             const float qs = dor[a] * rs_q[a];
             const float xs = xr[a] * rs_x[a];
             const float es = er[a] * rs_e[a];
@@ -281,7 +303,7 @@ struct ChunkGrad {
 
       // ---- a_s, b_r from the diagonal terms; merge them into the group sums
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
+      for (int a = 0; a < RPT; ++a) {
         float pa = 0.f, pb = 0.f;
         float kown[TI], qown[TI];
         own(kg, p.s.rk, a, kown);
@@ -296,27 +318,28 @@ struct ChunkGrad {
         pa = row_sum16(pa);
         pb = row_sum16(pb);
         if (tc == 0) {
-          sm[B_AV + tr * 4 + a] = pa;
-          sm[B_BV + tr * 4 + a] = pb;
+          sm[B_AV + tr * RPT + a] = pa;
+          sm[B_BV + tr * RPT + a] = pb;
         }
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < RPT; ++a)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          sm[B_DOX + (tr * 4 + a) * LP + tc * 4 + s] = acc_dox[a][s];
-          sm[B_XE + (tr * 4 + a) * LP + tc * 4 + s] = acc_xe[a][s];
+          sm[B_DOX + (tr * RPT + a) * LP + tc * 4 + s] = acc_dox[a][s];
+          sm[B_XE + (tr * RPT + a) * LP + tc * 4 + s] = acc_xe[a][s];
         }
       part_db += __shfl_xor(part_db, 1);
       part_db += __shfl_xor(part_db, 2);
-      if (rq4 == 0) sm[B_DB + rt] = part_db;
+      part_db += __shfl_xor(part_db, 4);
+      if (rq8 == 0) sm[B_DB + rt] = part_db;
       sm[B_RED + tid] = part_hdh;
       __syncthreads();
 
       // ---- L x L weights of head h and the rectangle terms of dl
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int t = tr * 4 + a;
+      for (int a = 0; a < RPT; ++a) {
+        const int t = tr * RPT + a;
         const float bt = sm[B_BET + t];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
@@ -392,6 +415,10 @@ struct ChunkGrad {
     }
 
     // ---- final products with the shared kn / qn rows
+    tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    tr = tid >> 4;
+    tc = tid & 15;
     auto load_rows = [&](const T* src, const float* scale) {
       for (int e = tid; e < L * DK; e += NT) {
         const int t = e / DK, i = e % DK;
@@ -406,20 +433,21 @@ struct ChunkGrad {
     // pass 1: kn rows; dQn += Wq Kn, dKn += Wk2 Kn
     load_rows(kg, p.s.rk);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < RPT; ++a)
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sm[C_W1 + (tc * 4 + s) * L + tr * 4 + a] = wq[a][s];   // stored [s][t]
-        sm[C_W2 + (tc * 4 + s) * L + tr * 4 + a] = wk2[a][s];
+        sm[C_W1 + (tc * 4 + s) * L + tr * RPT + a] = wq[a][s];   // stored [s][t]
+        sm[C_W2 + (tc * 4 + s) * L + tr * RPT + a] = wk2[a][s];
       }
     __syncthreads();
+#pragma unroll 2
     for (int s = 0; s < L; ++s) {
       float kv[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) kv[i] = sm[C_KS + s * DK + tc * TI + i];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float w1 = sm[C_W1 + s * L + tr * 4 + a], w2 = sm[C_W2 + s * L + tr * 4 + a];
+      for (int a = 0; a < RPT; ++a) {
+        const float w1 = sm[C_W1 + s * L + tr * RPT + a], w2 = sm[C_W2 + s * L + tr * RPT + a];
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           accQ[a][i] = fmaf(w1, kv[i], accQ[a][i]);
@@ -431,17 +459,18 @@ struct ChunkGrad {
     // pass 2: qn rows; dKn += Wk1 Qn
     load_rows(qg, p.s.rq);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < RPT; ++a)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sm[C_W1 + (tc * 4 + s) * L + tr * 4 + a] = wk1[a][s];
+      for (int s = 0; s < 4; ++s) sm[C_W1 + (tc * 4 + s) * L + tr * RPT + a] = wk1[a][s];
     __syncthreads();
+#pragma unroll 2
     for (int s = 0; s < L; ++s) {
       float qv[TI];
 #pragma unroll
       for (int i = 0; i < TI; ++i) qv[i] = sm[C_KS + s * DK + tc * TI + i];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const float w1 = sm[C_W1 + s * L + tr * 4 + a];
+      for (int a = 0; a < RPT; ++a) {
+        const float w1 = sm[C_W1 + s * L + tr * RPT + a];
 #pragma unroll
         for (int i = 0; i < TI; ++i) accK[a][i] = fmaf(w1, qv[i], accK[a][i]);
       }
@@ -449,8 +478,8 @@ struct ChunkGrad {
     // ---- normalisation backward and output
     const float dkf = static_cast<float>(DK);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int t = tr * 4 + a;
+    for (int a = 0; a < RPT; ++a) {
+      const int t = tr * RPT + a;
       float dq_dot = 0.f, dk_dot = 0.f;
       float kown[TI], qown[TI];
       own(kg, p.s.rk, a, kown);
