@@ -237,7 +237,7 @@ def test_vg_chunk_state_in_place():
 # ---- the chunk form's saved record (save=True: the forward writes the rows,
 # matrices and X the backward reads, the backward recomputes none of them)
 
-@pytest.mark.parametrize("Dk,Dv", [(64, 32), (128, 64), (192, 128)])
+@pytest.mark.parametrize("Dk,Dv", [(64, 32), (64, 128), (128, 64), (128, 96), (192, 32), (192, 128)])
 def test_vg_saved_shapes(Dk, Dv):
     B, T = 2, 141
     mask = np.ones((B, T), dtype=np.uint8)
