@@ -18,7 +18,7 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t rq, rk, kq, ell, beta;                 // prep scalars
   size_t U, E, dHend, pdA, pdt;                 // backward only
-  size_t Tx, Mq, KT, AtT, PqT, QT, SC;     // chunk form
+  size_t Tx, Mq, AtT, PqT, QT, SC;         // chunk form
   size_t HB;                                    // chunk backward: bf16 chunk-start states
   size_t maps, hseg, vzero;                     // T-parallel chunk forward
   size_t total;
@@ -33,7 +33,7 @@ size_t state_slots_elems(const Dims& d) {
 // chunk-start states and the chunk matrices (offsets in fp32 elements,
 // 256-byte aligned).
 struct Saved {
-  size_t HB, Tx, AtT, PqT, KT, QT, SC, X, total;
+  size_t HB, Tx, AtT, PqT, QT, SC, X, total;
 };
 
 Saved saved_layout(const Dims& d) {
@@ -51,7 +51,6 @@ Saved saved_layout(const Dims& d) {
   S.Tx = take((mats + 1) / 2);
   S.AtT = take((mats + 1) / 2);
   S.PqT = take((mats + 1) / 2);
-  S.KT = take((kts + 1) / 2);
   S.QT = take((kts + 1) / 2);
   S.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
   S.X = take((static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv + 1) / 2);
@@ -109,7 +108,6 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
       if (bwd) {
         L.AtT = take((mats + 1) / 2);
         L.PqT = take((mats + 1) / 2);
-        L.KT = take((kts + 1) / 2);
         L.QT = take((kts + 1) / 2);
       }
     }
@@ -125,9 +123,9 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
 }
 
 // The chunk kernels address their per-(head, chunk) matrices, the transposed
-// k / q rows and the per-step chunk scalars through buffer descriptors whose
-// size and 32-bit byte offsets cover the whole tensor, so each must stay
-// below 4 GiB: the 64 x 64 bf16 matrices (B Hv ceil(T/64) of them) and the
+// q rows and the per-step chunk scalars through buffer descriptors whose size
+// and 32-bit byte offsets cover the whole tensor, so each must stay below
+// 4 GiB: the 64 x 64 bf16 matrices (B Hv ceil(T/64) of them) and the
 // transposed rows (B Hk ceil(T/64) Dk x 64, bf16).  q, k, v, o, the saved X
 // and every per-chunk state slot are within that bound once their element
 // counts fit in int32 (2 bytes per element).
@@ -226,7 +224,6 @@ gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   if (bwd) {
     cb.AtT = at<gdn::bf16>(ws, L.AtT);
     cb.PqT = at<gdn::bf16>(ws, L.PqT);
-    cb.KT = at<gdn::bf16>(ws, L.KT);
     cb.QT = at<gdn::bf16>(ws, L.QT);
   }
   return cb;
@@ -240,7 +237,6 @@ void saved_bufs(const Dims& d, const float* ckpt, gdn::ChunkBufs& cb) {
   cb.Tx = reinterpret_cast<gdn::bf16*>(tail + S.Tx);
   cb.AtT = reinterpret_cast<gdn::bf16*>(tail + S.AtT);
   cb.PqT = reinterpret_cast<gdn::bf16*>(tail + S.PqT);
-  cb.KT = reinterpret_cast<gdn::bf16*>(tail + S.KT);
   cb.QT = reinterpret_cast<gdn::bf16*>(tail + S.QT);
   cb.sc = tail + S.SC;
   cb.X = reinterpret_cast<gdn::bf16*>(tail + S.X);

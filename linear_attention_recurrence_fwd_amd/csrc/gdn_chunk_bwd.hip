@@ -560,19 +560,32 @@ struct ChunkBwdGrad {
   struct Fin {
     float acc[L * FS];
   };
+  static constexpr int KQS = DK + 8;  // bf16 row stride of the k / q row tiles
+  struct KQ {
+    bf16 k[L * KQS];  // the chunk's k rows   [t][i]
+    bf16 q[L * KQS];  // the chunk's q rows   [t][i]
+  };
   union Big {
     Slab s;
     Head h;
-    Wts w;
+    KQ kq;
     Fin f;
+  };
+  static_assert(sizeof(KQ) <= sizeof(Head) || sizeof(KQ) <= sizeof(Slab), "k / q tiles fit the union");
+  // fp32 sums over the group's heads of Wq, Wk1, Wk2 (rows of WR: 16-byte
+  // aligned); their bf16 copies take the same space for the final products
+  union WsU {
+    struct {
+      alignas(16) float q[L * WR];
+      alignas(16) float k1[L * WR];
+      alignas(16) float k2[L * WR];
+    } f;
+    Wts w;
   };
   static constexpr int HB = 4;  // value heads per batch of the deferred gate-gradient section (one wave each)
   struct Smem {
     alignas(16) Big u;
-    // fp32 sums over the group's heads of Wq, Wk1, Wk2 (rows of WR: 16-byte aligned)
-    alignas(16) float wsq[L * WR];
-    alignas(16) float ws1[L * WR];
-    alignas(16) float ws2[L * WR];
+    alignas(16) WsU ws;
     alignas(16) float rk[L];
     alignas(16) float rq[L];
     alignas(16) float gam[L];
@@ -583,8 +596,8 @@ struct ChunkBwdGrad {
     float red[NTG / 64];
     // per value head (slot = head % HB), for the deferred section: the
     // prefix-summed and suffix-summed terms of dl, the db factor, l, and the
-    // per-head scalars <dH', H> and e^{gamma_L}
-    float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB];
+    // per-head scalars <dH', H>, e^{gamma_L}, A_log and dt_bias
+    float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB], hal[HB], hdt[HB];
     // a (fp32) and the mask (1 = valid step) of the first batch of value heads,
     // loaded when the workgroup starts
     float ha[HB][L], hm[HB][L];
@@ -593,6 +606,7 @@ struct ChunkBwdGrad {
   // and what its tail needs (the chunk's P^T / A^T tiles, a and the mask).
   struct HeadStart {
     float gam, eg, el, beta, ell, egl;  // step t = tid (tid < L)
+    float alog, dtb;                    // the head's A_log, dt_bias
     bf16x8 txb[2];                      // Tx row ta
   };
   struct HeadTail {
@@ -653,6 +667,8 @@ struct ChunkBwdGrad {
     hs.beta = scc[SC_BETA * L + t];
     hs.ell = scc[SC_ELL * L + t];
     hs.egl = scc[SC_EGL * L];
+    hs.alog = p.A_log[h];
+    hs.dtb = p.dt_bias[h];
     const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
     const bf16* txr = p.cb.Tx + (static_cast<size_t>(bh) * x.NC + x.c) * L * L + ta * L + 8 * lg;
     hs.txb[0] = load_bf16x8(txr);
@@ -862,9 +878,11 @@ struct ChunkBwdGrad {
     const uint32_t qk_row = d.Hk * DK;
     const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
     const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
-    const bf16* ktc = p.cb.KT + (static_cast<size_t>(bj) * NC + c) * DK * L;
-    const bf16* qtc = p.cb.QT + (static_cast<size_t>(bj) * NC + c) * DK * L;
     const int tid0 = threadIdx.x;
+    // the first head's scalars, issued first: each later head's are issued
+    // behind the previous head's slabs, so no head start waits on a load
+    HeadStart hs;
+    load_start(p, x, tid0, x.j * G, hs);
     const bool has_blk = tid0 < NB;
     {
       const int blk = min(tid0, NB - 1);
@@ -916,7 +934,7 @@ struct ChunkBwdGrad {
       ka[kt] = to_mfma_layout(ka[kt]);
       qa[kt] = to_mfma_layout(qa[kt]);
     }
-    for (int e = tid0; e < L * WR; e += NTG) sm.wsq[e] = sm.ws1[e] = sm.ws2[e] = 0.f;
+    for (int e = tid0; e < L * WR; e += NTG) sm.ws.f.q[e] = sm.ws.f.k1[e] = sm.ws.f.k2[e] = 0.f;
     if (tid0 < L) {
       sm.rk[tid0] = rk0;
       sm.rq[tid0] = rq0;
@@ -928,8 +946,6 @@ struct ChunkBwdGrad {
     for (int hh = 0; hh < G; ++hh) {
       const int h = x.j * G + hh, slot = hh % HB;
       const Lanes ln;
-      HeadStart hs;
-      load_start(p, x, ln.tid, h, hs);
       HeadTail ht;  // issued now, used after the slabs
       load_tail(p, x, ln.tid, h, ht);
       __syncthreads();  // the previous head is done with every shared array
@@ -941,7 +957,11 @@ struct ChunkBwdGrad {
         sm.beta[t] = hs.beta;
         sm.ell[t] = t < Lc ? hs.ell : 0.f;
       }
-      const float egl = hs.egl;
+      if (ln.tid == 0) {
+        sm.hegl[slot] = hs.egl;
+        sm.hal[slot] = hs.alog;
+        sm.hdt[slot] = hs.dtb;
+      }
       const bf16x8 txb[2] = {hs.txb[0], hs.txb[1]};
       __syncthreads();
       HeadAcc ac;
@@ -949,6 +969,8 @@ struct ChunkBwdGrad {
       ac.pb[0] = ac.pb[1] = ac.pb[2] = ac.pb[3] = ac.pa = ac.pdb = ac.phdh = 0.f;
       for (int si = 0; si < nsl; ++si)
         slab(p, sm, x, has_blk, h, hlast, si, nsl, pf, ka, qa, txb, accQ, accK, ac);
+      // the next head's scalars (the last head reloads its own: unused)
+      load_start(p, x, Lanes().tid, min(h + 1, hlast), hs);
 
       // ---- per-row sums of head h
       {
@@ -991,7 +1013,7 @@ struct ChunkBwdGrad {
         const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
         const bool tv = t < Lc;
         const float gt = sm.gam[t], bt = sm.beta[t];
-        float* pw[3] = {&sm.wsq[t * WR + s0], &sm.ws1[t * WR + s0], &sm.ws2[t * WR + s0]};
+        float* pw[3] = {&sm.ws.f.q[t * WR + s0], &sm.ws.f.k1[t * WR + s0], &sm.ws.f.k2[t * WR + s0]};
         float wv[3][8];
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
@@ -1075,7 +1097,6 @@ struct ChunkBwdGrad {
 #pragma unroll
           for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[i];
           sm.hdh[slot] = hdh;
-          sm.hegl[slot] = egl;
         }
       }
       // ---- deferred section, one wave per value head of the batch:
@@ -1109,8 +1130,8 @@ struct ChunkBwdGrad {
           const float dl = expf(ell) == 0.f ? 0.f : sm.hegl[k] * sm.hdh[k] + pre + suf;
           float da = 0.f, db = 0.f, dll = 0.f;
           if (in && valid) {
-            const float xa = av + p.dt_bias[hd];
-            da = xa <= kClamp ? dl * (-expf(p.A_log[hd])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
+            const float xa = av + sm.hdt[k];
+            da = xa <= kClamp ? dl * (-expf(sm.hal[k])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
             db = sm.hdb[k][t];
             dll = dl != 0.f ? dl * ell : 0.f;
           }
@@ -1131,24 +1152,13 @@ struct ChunkBwdGrad {
       }
     }
 
-    // ---- operands of the final products (K^T, Q^T tiles) and the q / k rows
-    // of the normalisation backward, loaded now (k and q rows of the slabs
-    // are dead) so that their latency overlaps the conversion of the group
-    // sums; the barriers below wait for LDS only
+    // ---- the q / k rows of the normalisation backward, loaded now (the slabs'
+    // loads are done) so that their latency overlaps the final products; the
+    // barriers below wait for LDS only
     constexpr int QW = DK / 8;                // columns per thread in the normalisation backward
-    constexpr int KTP = DK <= 192 ? 2 : 1;    // K^T / Q^T halves loaded ahead (registers permitting)
-    bf16x8 bk[KTP][IH], bq[KTP][IH];
     uint4 qrow[QW / 8], krow[QW / 8];
     {
       const Lanes q;
-#pragma unroll
-      for (int kt = 0; kt < KTP; ++kt)
-#pragma unroll
-        for (int k = 0; k < IH; ++k) {
-          const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
-          bk[kt][k] = load_bf16x8(ktc + o);
-          bq[kt][k] = load_bf16x8(qtc + o);
-        }
       const uint32_t ro = static_cast<uint32_t>(min(q.tid >> 3, x.tl)) * qk_row + (q.tid & 7) * QW;
 #pragma unroll
       for (int u = 0; u < QW / 8; ++u) {
@@ -1157,7 +1167,11 @@ struct ChunkBwdGrad {
       }
     }
 
-    // ---- final products with the group sums: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn
+    // ---- final products with the group sums: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn.
+    // Their Kn / Qn operands are the chunk's k and q rows the waves have held
+    // since the start (each wave its 16-step row tile), put in LDS as [t][i]
+    // tiles and read transposed; the group sums go to bf16 in the space of
+    // the fp32 sums (read into registers first, then a barrier).
     lds_barrier();
     {
       const Lanes q;
@@ -1165,27 +1179,37 @@ struct ChunkBwdGrad {
       uint32_t w0[4], w1[4], w2[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        w0[e >> 1] = pack2_bf16(sm.wsq[t * WR + s0 + e], sm.wsq[t * WR + s0 + e + 1]);
-        w1[e >> 1] = pack2_bf16(sm.ws1[t * WR + s0 + e], sm.ws1[t * WR + s0 + e + 1]);
-        w2[e >> 1] = pack2_bf16(sm.ws2[t * WR + s0 + e], sm.ws2[t * WR + s0 + e + 1]);
+        w0[e >> 1] = pack2_bf16(sm.ws.f.q[t * WR + s0 + e], sm.ws.f.q[t * WR + s0 + e + 1]);
+        w1[e >> 1] = pack2_bf16(sm.ws.f.k1[t * WR + s0 + e], sm.ws.f.k1[t * WR + s0 + e + 1]);
+        w2[e >> 1] = pack2_bf16(sm.ws.f.k2[t * WR + s0 + e], sm.ws.f.k2[t * WR + s0 + e + 1]);
       }
-      *reinterpret_cast<uint4*>(&sm.u.w.wq[t * TS + s0]) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-      *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + s0]) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-      *reinterpret_cast<uint4*>(&sm.u.w.wk[t * WS + L + s0]) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+      // waves 0-3 (hw = 0) put their k rows, waves 4-7 their q rows
+      bf16* kqt = q.hw == 0 ? sm.u.kq.k : sm.u.kq.q;
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt)
+        *reinterpret_cast<uint4*>(&kqt[q.ta * KQS + 32 * kt + 8 * q.lg]) =
+            __builtin_bit_cast(uint4, q.hw == 0 ? ka[kt] : qa[kt]);
+      lds_barrier();
+      *reinterpret_cast<uint4*>(&sm.ws.w.wq[t * TS + s0]) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+      *reinterpret_cast<uint4*>(&sm.ws.w.wk[t * WS + s0]) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      *reinterpret_cast<uint4*>(&sm.ws.w.wk[t * WS + L + s0]) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
     }
     lds_barrier();
     {
       const Lanes q;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 aq = load_bf16x8(&sm.u.w.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
-        const bf16x8 a1 = load_bf16x8(&sm.u.w.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
-        const bf16x8 a2 = load_bf16x8(&sm.u.w.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
+        const bf16x8 aq = load_bf16x8(&sm.ws.w.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
+        const bf16x8 a1 = load_bf16x8(&sm.ws.w.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
+        const bf16x8 a2 = load_bf16x8(&sm.ws.w.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
 #pragma unroll
         for (int k = 0; k < IH; ++k) {
-          const uint32_t o = (16 * (q.hw * IH + k) + q.lr) * L + 32 * kt + 8 * q.lg;
-          const bf16x8 vk = kt < KTP ? bk[kt < KTP ? kt : 0][k] : load_bf16x8(ktc + o);
-          const bf16x8 vq = kt < KTP ? bq[kt < KTP ? kt : 0][k] : load_bf16x8(qtc + o);
+          // steps 32 kt + 8 lg .. + 7 of channel 16 (hw IH + k) + lr
+          const int o0 = (32 * kt + 8 * q.lg + (q.lr >> 2)) * KQS + 16 * (q.hw * IH + k) + 4 * (q.lr & 3);
+          const uint2 k0 = lds_read_tr16(&sm.u.kq.k[o0]), k1 = lds_read_tr16(&sm.u.kq.k[o0 + 4 * KQS]);
+          const uint2 q0 = lds_read_tr16(&sm.u.kq.q[o0]), q1 = lds_read_tr16(&sm.u.kq.q[o0 + 4 * KQS]);
+          const bf16x8 vk = as_bf16x8(make_uint4(k0.x, k0.y, k1.x, k1.y));
+          const bf16x8 vq = as_bf16x8(make_uint4(q0.x, q0.y, q1.x, q1.y));
           accQ[k] = mfma16(aq, vk, accQ[k]);
           accK[k] = mfma16(a1, vq, accK[k]);
           accK[k] = mfma16(a2, vk, accK[k]);

@@ -17,18 +17,18 @@
 //   chunk_prep  one workgroup per (chunk, batch, value head): the chunk's k and
 //               q rows staged in LDS by coalesced loads, K K^T and Q K^T on
 //               MFMA, the gates and gamma by a wave scan, N, Tx by blocked
-//               forward substitution (fp32), Mq and the per-step chunk scalars; the
-//               first value head of each key head also writes K^T.  With
-//               `bwd` set it writes the transposes the backward needs instead
-//               of Mq, and Q^T.  All outputs go to the workspace (bf16 /
-//               fp32), 16 bytes per store.
+//               forward substitution (fp32), Mq and the per-step chunk scalars.
+//               With `bwd` set it writes the transposes the backward needs
+//               instead of Mq, and the first value head of each key head
+//               writes Q^T.  All outputs go to the workspace (bf16 / fp32),
+//               16 bytes per store.
 //   chunk_fwd   one workgroup per (batch, value head, 32-column slice of Dv),
 //               walking the chunks in order with H in MFMA accumulators (fp32),
 //               the next chunk's operands prefetched into registers while the
 //               current chunk computes (the in-chunk barriers wait for LDS
 //               only, so the prefetch stays in flight across them).  Blocks
-//               that share a key head run on one XCD, so their K / Q / K^T
-//               reads hit that XCD's L2.  Writes o, the checkpoints and the
+//               that share a key head run on one XCD, so their K / Q reads
+//               hit that XCD's L2.  Writes o, the checkpoints and the
 //               final state, and for the backward's saved record the bf16
 //               chunk-start states and X of every step.
 #include <type_traits>
@@ -96,7 +96,7 @@ struct ChunkPrep {
 
   // One workgroup per (chunk, batch, value head).  The G workgroups of a key
   // head recompute its K K^T and Q K^T (cheap on the matrix cores; the k / q
-  // rows come from L2) and the first of them writes K^T (and Q^T).
+  // rows come from L2) and, for the backward, the first of them writes Q^T.
   __device__ static void run(const ChunkPrepArgs& p, Smem& sm) {
     const Dims& d = p.d;
     const int c = blockIdx.x, bh = blockIdx.y;
@@ -182,7 +182,6 @@ struct ChunkPrep {
       }
       if (first && bwd_out) {
         const size_t base = (static_cast<size_t>(b * d.Hk + j) * NC + c) * DK * L + static_cast<size_t>(c0) * L;
-        store_transposed(sm.u.r.k, p.cb.KT + base, tid);
         store_transposed(sm.u.r.q, p.cb.QT + base, tid);
       }
     }

@@ -111,7 +111,6 @@ struct ChunkBufs {
   bf16* Tx;   // [B*Hv, NC, L, L] (I + N)^-1, N[t,s] = [s<t] e^{g_t-g_s} rk_t rk_s beta_s (k_t.k_s)
   bf16* Mq;   // [B*Hv, NC, L, L] [s<=t] e^{g_t-g_s} rq_t rk_s beta_s (q_t.k_s)
   // backward only
-  bf16* KT;   // [B*Hk, NC, Dk, L] raw k of the chunk, transposed
   bf16* AtT;  // [B*Hv, NC, L, L] transpose of [s<t] e^{g_t-g_s} rk_t rk_s (k_t.k_s)
   bf16* PqT;  // [B*Hv, NC, L, L] transpose of [s<=t] e^{g_t-g_s} rq_t rk_s (q_t.k_s)
   bf16* QT;   // [B*Hk, NC, Dk, L] raw q of the chunk, transposed
@@ -181,7 +180,7 @@ struct ChunkPrepArgs {
   const uint8_t* mask;
   ChunkBufs cb;
   int bwd;  // 0: the forward's buffers (Tx, Mq, sc); 1: the backward's (Tx, sc,
-            // A^T, P^T, K^T, Q^T); 2: both
+            // A^T, P^T, Q^T); 2: both
 };
 
 // Chunk matrices of the per-key-channel gate: Tx, Mq / A^T, P^T (as

@@ -42,7 +42,6 @@ void touch_chunk(const gdn::Dims& d, const gdn::ChunkBufs& cb) {
   touch(cb.Mq, nmat(d) * 64 * 64 * 2);
   touch(cb.AtT, nmat(d) * 64 * 64 * 2);
   touch(cb.PqT, nmat(d) * 64 * 64 * 2);
-  touch(cb.KT, kts(d) * 2);
   touch(cb.QT, kts(d) * 2);
   touch(cb.sc, nmat(d) * gdn::SC_ROWS * 64 * 4);
   touch(cb.Hb, slots(d) * 2);

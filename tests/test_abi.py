@@ -133,12 +133,12 @@ def test_saved_chunk_matrices_sizes():
     saved = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_BF16, save=True)
     states = 31 * 64 * 192 * 128
     mats = 64 * 32 * 64 * 64 // 2        # one bf16 64x64 matrix per (head, chunk), in fp32 elements
-    kts = 16 * 32 * 192 * 64 // 2
+    qts = 16 * 32 * 192 * 64 // 2       # the chunk's q rows transposed, bf16
     scal = 64 * 32 * 12 * 64
     assert B.ckpt_elems(plain) == states
     slots = 32 * 64 * 192 * 128 // 2     # bf16, in fp32 elements
     xs = 2048 * 64 * 128 // 2            # X of every step, bf16
-    assert B.ckpt_elems(saved) == slots + 3 * mats + 2 * kts + scal + xs
+    assert B.ckpt_elems(saved) == slots + 3 * mats + qts + scal + xs
     assert B.bwd_workspace_bytes(saved) < B.bwd_workspace_bytes(plain)
     assert B.fwd_workspace_bytes(saved) < B.fwd_workspace_bytes(plain)
     f32 = B.make_dims(1, 2048, 16, 64, 192, 128, B.GDN_F32, save=True)
