@@ -85,8 +85,7 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
     const size_t nc = d.nchunk();
     const size_t col = bt * d.Hv * d.Dv;
     const size_t dh = nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv;
-    if (chunk) {  // eps and dH' in bf16
-      L.E = take((col + 1) / 2);
+    if (chunk) {  // dH' in bf16 (the gradient pass reads dv = diag(beta) eps, not eps)
       L.dHend = take((dh + 1) / 2);
       if (!saved) L.HB = take((state_slots_elems(d) + 1) / 2);
     } else {
@@ -660,7 +659,7 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
       if (!launch(st, [&] { return gdn::launch_state_bf16(sa, st); })) return GDN_ERR_HIP;
     }
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
-                         at<gdn::bf16>(ws, L.E), at<gdn::bf16>(ws, L.dHend),
+                         nullptr, at<gdn::bf16>(ws, L.dHend),
                          dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
     if (tseg) {  // T-parallel reverse pass: segment maps, their chain (last to first), then the segments
       const int nseg = gdn::tpar_nseg(dd, tseg);

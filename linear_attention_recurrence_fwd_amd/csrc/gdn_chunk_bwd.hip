@@ -14,15 +14,19 @@
 // e^{gL-g_t} dH' + sum_{r>t} e^{g_r-g_t} (qn_r dO_r^T - beta_r kn_r eps_r^T),
 // and eps_t is its product with kn_t plus (qn_t . kn_t) dO_t.
 //
-// The per-chunk gradients (same expansion as the scan path's chunk assembly):
+// The per-chunk gradients (same expansion as the scan path's chunk assembly),
+// written with dv = diag(beta) eps: eps enters every term with a beta factor
+// (delta_t = beta_t X_t and X_t does not depend on beta_t), so the gradient
+// pass reads the dv output and no eps buffer is kept:
 //   dQn = diag(e^g) dO H^T + Wq Kn
-//   dKn = diag(e^{gL-g} beta) X dH'^T - diag(e^g beta) eps H^T + Wk1 Qn + Wk2 Kn
+//   dKn = diag(e^{gL-g} beta) X dH'^T - diag(e^g) dv H^T + Wk1 Qn + Wk2 Kn
 //   Wq[t,s]  = [s<=t] e^{g_t-g_s} beta_s (dO_t . X_s)
 //   Wk1[t,r] = [r>=t] e^{g_r-g_t} beta_t (dO_r . X_t)
-//   Wk2[t,s] = -beta_t beta_s ([s<t] e^{g_t-g_s} (X_s . eps_t) + [s>t] e^{g_s-g_t} (X_t . eps_s))
+//   Wk2[t,s] = -([s<t] e^{g_t-g_s} beta_s (X_s . dv_t) + [s>t] e^{g_s-g_t} beta_t (X_t . dv_s))
 //   dl_t = e^{gL} <dH', H> + sum_{s<t} a_s + sum_{r>=t} b_r
-//          + sum_{r>=t} sum_{s<t} e^{g_r-g_s} beta_s [(qn_r.kn_s)(dO_r.X_s) - beta_r (kn_r.kn_s)(eps_r.X_s)]
-//   a_s = e^{gL-g_s} beta_s kn_s^T dH' X_s,  b_r = e^{g_r} (qn_r^T H dO_r - beta_r kn_r^T H eps_r)
+//          + sum_{r>=t} sum_{s<t} e^{g_r-g_s} beta_s [(qn_r.kn_s)(dO_r.X_s) - (kn_r.kn_s)(dv_r.X_s)]
+//   a_s = e^{gL-g_s} beta_s kn_s^T dH' X_s,  b_r = e^{g_r} (qn_r^T H dO_r - kn_r^T H dv_r)
+//   db_t = (dv_t . X_t) (1 - beta_t)   (dL/dbeta_t = eps_t . X_t, dbeta/db = beta (1 - beta))
 // with X the forward's saved copy, or recomputed from the checkpointed H as in
 // the forward when there is no saved record.  Every decay is
 // e^{-|g_t - g_s|}; nothing is divided by a decay.
@@ -31,8 +35,9 @@
 //   chunk_bwd_state  one workgroup per (batch, value head, 32-column slice of
 //                    Dv), walking the chunks from last to first with dH in MFMA
 //                    accumulators (fp32) and the next chunk's operands
-//                    prefetched.  Writes dv, eps (bf16), dH' of every chunk
-//                    (bf16, transposed) and dstate.
+//                    prefetched.  Writes dv, dH' of every chunk (bf16,
+//                    transposed) and dstate; eps (bf16) only for the
+//                    per-key-channel gate, whose gradient kernels read it.
 //   chunk_bwd_grad   one workgroup per (chunk, batch, key head), looping over
 //                    the group's value heads and 32-column slabs of Dv, with H
 //                    read from the bf16 copies of the chunk-start states and
@@ -60,8 +65,9 @@ struct ChunkBwdState {
   // Eight waves in two groups of four (w = wave index within the group):
   //   A (waves 0-3): for row tile w of the chunk, the dependent chain
   //                  rhs = diag(e^{gL-g} rk) K dH' + P^T dO, Ehat = Tx^T diag(beta) rhs
-  //                  (= dv), eps = rhs - A^T Ehat.  A also streams the chunk's k
-  //                  rows, P^T, Tx^T, A^T, dO slice and chunk scalars into a
+  //                  (= dv), and for the per-key-channel gate eps = rhs - A^T
+  //                  Ehat.  A also streams the chunk's k rows, P^T, Tx^T (A^T
+  //                  for that gate), dO slice and chunk scalars into a
   //                  2-slot LDS ring with direct-to-LDS loads, one chunk ahead.
   //   B (waves 4-7): dH for its RTW row tiles, in MFMA accumulators: stores dH'
   //                  of the chunk, adds e^{gL} dH' + Q^T diag(e^g rq) dO while A
@@ -80,7 +86,7 @@ struct ChunkBwdState {
   static constexpr int XS = L + 8;     // bf16 row stride of the [v][t] tiles
   static constexpr int NPK = DK / 8;   // 16-byte pieces of a k row
   static constexpr int KDMA = DK / 32;
-  static constexpr int NDMA = KDMA + 6 + 1 + 2;  // ring loads per group-A wave per chunk
+  static constexpr int NDMA = KDMA + (VG ? 6 : 4) + 1 + 2;  // ring loads per group-A wave per chunk
   static constexpr int SCR = VG ? VSC_ROWS : SC_ROWS;  // chunk scalar rows per chunk
   static_assert(!VG || DK <= 4 * L, "e^{G_L} of every channel in rows 1 .. 4 of the slot");
   // A ring slot (layouts as in the forward state pass: 16-byte piece p of row
@@ -140,7 +146,7 @@ struct ChunkBwdState {
       const uint32_t o = 2 * (mat + t * L + 8 * pc);
       dma16(q.dpt, &s.pt[512 * n], o);
       dma16(q.dtx, &s.tx[512 * n], o);
-      dma16(q.dat, &s.at[512 * n], o);
+      if constexpr (VG) dma16(q.dat, &s.at[512 * n], o);
     }
     {
       const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
@@ -222,7 +228,7 @@ struct ChunkBwdState {
       const uint2 lo = lds_read_tr16(&s.tx[xpos(sr, pc) + 4 * (lr & 1)]);
       const uint2 hi = lds_read_tr16(&s.tx[xpos(sr + 4, pc) + 4 * (lr & 1)]);
       txa[kt] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      ata[kt] = load_bf16x8(&s.at[xpos(ta, 4 * kt + lg)]);
+      if constexpr (VG) ata[kt] = load_bf16x8(&s.at[xpos(ta, 4 * kt + lg)]);
     }
     const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
     const float4 kl4 = VG ? one4 : *reinterpret_cast<const float4*>(&s.sc[SC_KL * L + q.tc0]);
@@ -268,19 +274,22 @@ struct ChunkBwdState {
     }
     lds_barrier();  // Z: Ehat complete
     store_rows(p, q, p.dv, t0, Lc, eh, 1.f);
-    // eps = rhs - A^T Ehat
-    f32x4 ng[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ng[ct][r] = -rhs[ct][r];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    if constexpr (VG) {
+      // eps = rhs - A^T Ehat, which the per-key-channel gate's gradient
+      // kernels read (the scalar gate's gradient pass reads dv = diag(beta) eps)
+      f32x4 ng[2];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        ng[ct] = mfma16(ata[kt], load_bf16x8(&sm.eb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), ng[ct]);
-    store_rows(p, q, p.E, t0, Lc, ng, -1.f);
-    wait_vm<4>();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ng[ct][r] = -rhs[ct][r];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          ng[ct] = mfma16(ata[kt], load_bf16x8(&sm.eb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), ng[ct]);
+      store_rows(p, q, p.E, t0, Lc, ng, -1.f);
+    }
+    wait_vm<VG ? 4 : 2>();  // the ring loads (the later stores may stay pending)
     lds_barrier();  // X: dH of the next chunk complete; slot c - 1 complete
   }
 
@@ -544,11 +553,11 @@ struct ChunkBwdGrad {
     bf16 rt[NS * TS];   // R   [v][t]
     bf16 xr[L * VS];    // X   [t][v]
     bf16 xs[L * VS];    // diag(e^{gL-g} beta) X   [t][v]
-    bf16 vt[3][L * VS]; // v, dO, eps of the slab   [t][v]
+    bf16 vt[3][L * VS]; // X (or v), dO, dv of the slab   [t][v]
   };
   struct Head {
     float dox[L * LP];  // dO_t . X_s
-    float xe[L * LP];   // X_t . eps_s
+    float xe[L * LP];   // X_t . dv_s
     float m[L * LP];    // rectangle terms of dl (row r, column s < r)
     bf16 pt[L * L];     // P^T of the chunk   [s][t], 16-byte piece p of row s at p ^ ((s >> 3) & 7)
     bf16 at[L * L];     // A^T of the chunk   [s][t], swizzled alike
@@ -613,11 +622,11 @@ struct ChunkBwdGrad {
     uint4 pt, at;  // chunk tid of P^T / A^T (row tid >> 3, cols 8 (tid & 7) ..)
   };
   // Global data of one slab, loaded a slab ahead.
-  static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the v / dO / eps tiles
+  static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the X / dO / dv tiles
   struct Pf {
     uint2 h[4];    // H rows i0 + a, cols vv0 .. vv0+3 (this thread's block, bf16)
     uint2 dh[4];   // dH' rows i0 + a, cols vv0 .. vv0+3 (bf16)
-    uint4 ch[2];   // chunks tid and tid + NTG of the v / dO / eps tiles
+    uint4 ch[2];   // chunks tid and tid + NTG of the X / dO / dv tiles
   };
   struct Ctx {
     int b, j, c, NC, t0, Lc, tl, i0, vv0;
@@ -643,7 +652,8 @@ struct ChunkBwdGrad {
     const size_t vrem = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
     const bf16* t0src = XSV ? p.cb.X : static_cast<const bf16*>(p.v);  // tile 0: X, or v to recompute it from
     const rsrc_t rs[3] = {make_rsrc(t0src + vbase, vrem),
-                          make_rsrc(static_cast<const bf16*>(p.dO) + vbase, vrem), make_rsrc(p.E + vbase, vrem)};
+                          make_rsrc(static_cast<const bf16*>(p.dO) + vbase, vrem),
+                          make_rsrc(static_cast<const bf16*>(p.dv) + vbase, vrem)};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int ci = min(tid + u * NTG, NCH - 1);
@@ -669,10 +679,14 @@ struct ChunkBwdGrad {
     hs.egl = scc[SC_EGL * L];
     hs.alog = p.A_log[h];
     hs.dtb = p.dt_bias[h];
-    const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
-    const bf16* txr = p.cb.Tx + (static_cast<size_t>(bh) * x.NC + x.c) * L * L + ta * L + 8 * lg;
-    hs.txb[0] = load_bf16x8(txr);
-    hs.txb[1] = load_bf16x8(txr + 32);
+    if constexpr (XSV) {  // X is read, not recomputed: Tx is not needed
+      hs.txb[0] = hs.txb[1] = bf16x8{};
+    } else {
+      const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
+      const bf16* txr = p.cb.Tx + (static_cast<size_t>(bh) * x.NC + x.c) * L * L + ta * L + 8 * lg;
+      hs.txb[0] = load_bf16x8(txr);
+      hs.txb[1] = load_bf16x8(txr + 32);
+    }
   }
   __device__ static void load_tail(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, HeadTail& ht) {
     const Dims& d = p.d;
@@ -717,21 +731,21 @@ struct ChunkBwdGrad {
     float pb[4], pa, pdb, phdh;
   };
   // Contractions over the slab's columns: dQn, dKn (state terms) and the
-  // Grams dO X^T, X eps^T.  xr8 / xs8: rows ta of X and of
+  // Grams dO X^T, X dv^T.  xr8 / xs8: rows ta of X and of
   // diag(e^{gL-g} beta) X; xt: the X tile [t][v].
   __device__ static void contract(const Smem& sm, const bf16* xt, const bf16* dt, const bf16* et, int ta, int lr,
                                   int lg, int hw, const bf16x8& xr8, const bf16x8& xs8, f32x4 (&accQ)[IH],
                                   f32x4 (&accK)[IH], HeadAcc& ac) {
-    const float sq = sm.eg[ta], se = -sm.eg[ta] * sm.beta[ta];
+    const float sq = sm.eg[ta];
     const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
-    const bf16x8 dos8 = scale8(do8, sq), eps8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), se);
+    const bf16x8 dos8 = scale8(do8, sq), dvs8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), -sq);
 #pragma unroll
     for (int k = 0; k < IH; ++k) {
       const int it = hw * IH + k;
       const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
       const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
       accQ[k] = mfma16(dos8, bhv, accQ[k]);
-      accK[k] = mfma16(eps8, bhv, accK[k]);
+      accK[k] = mfma16(dvs8, bhv, accK[k]);
       accK[k] = mfma16(xs8, bdh, accK[k]);
     }
 #pragma unroll
@@ -741,7 +755,7 @@ struct ChunkBwdGrad {
       ac.xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), ac.xe[u]);
     }
   }
-  // One 32-column slab of head h: stage the prefetched H, dH', v, dO, eps
+  // One 32-column slab of head h: stage the prefetched H, dH', X, dO, dv
   // in LDS, issue the next slab's loads (unconditional, so the prefetch stays
   // in flight), and accumulate.
   __device__ static void slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, bool has_blk, int h, int hlast,
@@ -750,7 +764,7 @@ struct ChunkBwdGrad {
                               f32x4 (&accK)[IH], HeadAcc& ac) {
     const Lanes q;
     const int lr = q.lr, lg = q.lg, ta = q.ta, tc0 = q.tc0, hw = q.hw;
-    // ---- this slab's H and dH' into LDS ([i][v]), <dH', H>; v / dO / eps tiles
+    // ---- this slab's H and dH' into LDS ([i][v]), <dH', H>; X / dO / dv tiles
     if (has_blk) {
       const int i0 = x.i0, vv0 = x.vv0;
 #pragma unroll
@@ -794,9 +808,9 @@ struct ChunkBwdGrad {
       for (int r = 0; r < 4; ++r) {
         const int t = tc0 + r, o = t * VS + 16 * hw + lr;
         const float eg = sm.eg[t], cr = eg * sm.rk[t];
-        const float dov = to_f32(dt[o]), epv = to_f32(et[o]);
+        const float dov = to_f32(dt[o]), dvv = to_f32(et[o]);
         ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
-        ac.pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, ac.pb[r]);
+        ac.pb[r] = fmaf(-cr * kh[r], dvv, ac.pb[r]);
       }
       // X[ta][16 hw + 4 lg + r], in the layout of (K dH')^T
       const int vc = 16 * hw + 4 * lg;
@@ -821,10 +835,10 @@ struct ChunkBwdGrad {
         for (int r = 0; r < 4; ++r) {
           const int t = tc0 + r, o = t * VS + 16 * hw + lr;
           const float eg = sm.eg[t], cr = eg * sm.rk[t];
-          const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), epv = to_f32(et[o]);
+          const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), dvv = to_f32(et[o]);
           rv[r] = vv - cr * kh[r];
           ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
-          ac.pb[r] = fmaf(-sm.beta[t] * cr * kh[r], epv, ac.pb[r]);
+          ac.pb[r] = fmaf(-cr * kh[r], dvv, ac.pb[r]);
         }
         *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
       }
@@ -1055,11 +1069,11 @@ struct ChunkBwdGrad {
             const float dec = __expf(-fabsf(gt - gs[e]));  // hardware exp (bf16-level weights)
             const float w0 = dec * bs[e] * doxts[e] * rks[e];
             const float w1 = dec * bt * doxst[e] * rqs[e];
-            const float w2 = -bt * bs[e] * dec * (s < t ? xest[e] : xets[e]) * rks[e];
+            const float w2 = -dec * (s < t ? bs[e] * xest[e] : bt * xets[e]) * rks[e];
             wv[0][ew] += ok && s <= t ? w0 : 0.f;
             wv[1][ew] += ok && s >= t ? w1 : 0.f;
             wv[2][ew] += ok && s != t ? w2 : 0.f;
-            const float m = ok && s < t ? bs[e] * (ptv[e] * doxts[e] - bt * atv[e] * xest[e]) : 0.f;
+            const float m = ok && s < t ? bs[e] * (ptv[e] * doxts[e] - atv[e] * xest[e]) : 0.f;
             sm.u.h.m[t * LP + s] = m;
             rsum += m;
           }
@@ -1089,7 +1103,7 @@ struct ChunkBwdGrad {
           sm.hu[slot][s] = av + csum - sm.rs[s];
           sm.hb[slot][s] = in ? sm.bv[0][s] + sm.bv[1][s] : 0.f;
           const float beta = sm.beta[s];
-          sm.hdb[slot][s] = (sm.pdb[0][s] + sm.pdb[1][s]) * beta * (1.f - beta);
+          sm.hdb[slot][s] = (sm.pdb[0][s] + sm.pdb[1][s]) * (1.f - beta);
           sm.hell[slot][s] = sm.ell[s];
         }
         if (q.tid == 0) {

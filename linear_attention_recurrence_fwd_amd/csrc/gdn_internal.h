@@ -271,7 +271,7 @@ struct ChunkBwdArgs {
   const uint8_t* mask;
   const float *state0, *ckpt, *dS_final;  // state0 / dS_final may be null
   ChunkBufs cb;
-  bf16* E;        // [B,T,Hv,Dv]  eps, rows t < T
+  bf16* E;        // [B,T,Hv,Dv]  eps, rows t < T (per-key-channel gate only; null otherwise)
   bf16* dHend;    // [NC, B*Hv, Dk, Dv]  dL/d(state at the end of chunk c)
   void *dq, *dk, *dv, *da, *db;
   float* dstate;     // [B,Hv,Dk,Dv]
