@@ -110,11 +110,11 @@ typedef struct gdn_dims {
  * whose contents are private to the library: the state at the start of every
  * chunk (initial state included) rounded to bf16, which is the precision the
  * chunk products consume it in, and the per-chunk matrices the backward needs
- * (the in-chunk inverse, the decayed key/key and query/key
- * Gram matrices, the chunk's q rows transposed, the per-step chunk scalars)
- * and every step's X = v - u (the value minus the state's prediction of it,
- * bf16), which spares the backward its recomputation:
- * about ceil(T/64) * (B * Hv * (Dk * Dv / 2 + 32 * Dv + 14k) + B * Hk * Dk * 32)
+ * (the in-chunk inverse, the decayed query/key Gram matrix, the chunk's q rows
+ * transposed, the per-step chunk scalars) and every step's X = v - u (the
+ * value minus the state's prediction of it, bf16), which spares the backward
+ * its recomputation:
+ * about ceil(T/64) * (B * Hv * (Dk * Dv / 2 + 32 * Dv + 4864) + B * Hk * Dk * 32)
  * elements.  It holds no fp32 states; such a checkpoint is read only by a
  * gdn_bwd with the same dims (including save). */
 int gdn_ckpt_elems(const gdn_dims* d, size_t* out);

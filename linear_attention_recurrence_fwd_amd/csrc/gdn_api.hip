@@ -18,7 +18,7 @@ size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t rq, rk, kq, ell, beta;                 // prep scalars
   size_t U, E, dHend, pdA, pdt;                 // backward only
-  size_t Tx, Mq, AtT, PqT, QT, SC;         // chunk form
+  size_t Tx, Mq, PqT, QT, SC;              // chunk form
   size_t HB;                                    // chunk backward: bf16 chunk-start states
   size_t maps, hseg, vzero;                     // T-parallel chunk forward
   size_t total;
@@ -33,7 +33,7 @@ size_t state_slots_elems(const Dims& d) {
 // chunk-start states and the chunk matrices (offsets in fp32 elements,
 // 256-byte aligned).
 struct Saved {
-  size_t HB, Tx, AtT, PqT, QT, SC, X, total;
+  size_t HB, Tx, PqT, QT, SC, X, total;
 };
 
 Saved saved_layout(const Dims& d) {
@@ -49,7 +49,6 @@ Saved saved_layout(const Dims& d) {
   const size_t kts = static_cast<size_t>(d.B) * d.Hk * nc * d.Dk * 64;
   S.HB = take((state_slots_elems(d) + 1) / 2);
   S.Tx = take((mats + 1) / 2);
-  S.AtT = take((mats + 1) / 2);
   S.PqT = take((mats + 1) / 2);
   S.QT = take((kts + 1) / 2);
   S.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
@@ -105,7 +104,6 @@ Layout layout(const Dims& d, bool bwd, bool chunk, bool saved, int tseg = 0) {
       L.Tx = take((mats + 1) / 2);
       L.SC = take(static_cast<size_t>(d.B) * d.Hv * nc * gdn::SC_ROWS * 64);
       if (bwd) {
-        L.AtT = take((mats + 1) / 2);
         L.PqT = take((mats + 1) / 2);
         L.QT = take((kts + 1) / 2);
       }
@@ -221,7 +219,6 @@ gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   cb.sc = at<float>(ws, L.SC);
   if (!bwd) cb.Mq = at<gdn::bf16>(ws, L.Mq);
   if (bwd) {
-    cb.AtT = at<gdn::bf16>(ws, L.AtT);
     cb.PqT = at<gdn::bf16>(ws, L.PqT);
     cb.QT = at<gdn::bf16>(ws, L.QT);
   }
@@ -234,7 +231,6 @@ void saved_bufs(const Dims& d, const float* ckpt, gdn::ChunkBufs& cb) {
   float* tail = const_cast<float*>(ckpt);
   cb.Hb = reinterpret_cast<gdn::bf16*>(tail + S.HB);
   cb.Tx = reinterpret_cast<gdn::bf16*>(tail + S.Tx);
-  cb.AtT = reinterpret_cast<gdn::bf16*>(tail + S.AtT);
   cb.PqT = reinterpret_cast<gdn::bf16*>(tail + S.PqT);
   cb.QT = reinterpret_cast<gdn::bf16*>(tail + S.QT);
   cb.sc = tail + S.SC;

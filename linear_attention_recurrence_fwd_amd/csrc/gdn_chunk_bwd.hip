@@ -56,7 +56,6 @@ namespace gdn {
 namespace {
 
 constexpr int L = kChunk;
-constexpr int LP = L + 1;
 
 // ------------------------------------------------------- reverse state pass
 
@@ -491,7 +490,7 @@ struct ChunkBwdState {
       q.ddo = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
       q.dpt = raw_desc(p.cb.PqT, nmat * L * L * 2);
       q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
-      q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
+      if constexpr (VG) q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
       if constexpr (VG) {
         q.dsc = raw_desc(p.cb.vsc, nmat * VSC_ROWS * L * 4);
         q.rqt = make_rsrc(p.cb.QbT, nmat * DK * L * 2);
@@ -544,7 +543,6 @@ struct ChunkBwdGrad {
   static constexpr int TS = L + 8;       // bf16 row stride of [v][t] tiles and Wq rows
   static constexpr int WS = 2 * L + 8;   // bf16 row stride of [Wk1 | Wk2] rows
   static constexpr int FS = DK + 4;      // fp32 row stride of the final accumulators
-  static constexpr int WR = L + 8;       // fp32 row stride of the weight sums
   static constexpr int NB = (DK / 4) * (NS / 4);  // 4x4 blocks of one slab (<= NTG)
   static_assert(NB <= NTG, "one block per thread");
   struct Slab {
@@ -554,13 +552,6 @@ struct ChunkBwdGrad {
     bf16 xr[L * VS];    // X   [t][v]
     bf16 xs[L * VS];    // diag(e^{gL-g} beta) X   [t][v]
     bf16 vt[3][L * VS]; // X (or v), dO, dv of the slab   [t][v]
-  };
-  struct Head {
-    float dox[L * LP];  // dO_t . X_s
-    float xe[L * LP];   // X_t . dv_s
-    float m[L * LP];    // rectangle terms of dl (row r, column s < r)
-    bf16 pt[L * L];     // P^T of the chunk   [s][t], 16-byte piece p of row s at p ^ ((s >> 3) & 7)
-    bf16 at[L * L];     // A^T of the chunk   [s][t], swizzled alike
   };
   struct Wts {
     bf16 wq[L * TS];    // sum over the group of Wq diag(rk)   [t][s]
@@ -576,32 +567,21 @@ struct ChunkBwdGrad {
   };
   union Big {
     Slab s;
-    Head h;
     KQ kq;
     Fin f;
-  };
-  static_assert(sizeof(KQ) <= sizeof(Head) || sizeof(KQ) <= sizeof(Slab), "k / q tiles fit the union");
-  // fp32 sums over the group's heads of Wq, Wk1, Wk2 (rows of WR: 16-byte
-  // aligned); their bf16 copies take the same space for the final products
-  union WsU {
-    struct {
-      alignas(16) float q[L * WR];
-      alignas(16) float k1[L * WR];
-      alignas(16) float k2[L * WR];
-    } f;
-    Wts w;
   };
   static constexpr int HB = 4;  // value heads per batch of the deferred gate-gradient section (one wave each)
   struct Smem {
     alignas(16) Big u;
-    alignas(16) WsU ws;
+    alignas(16) Wts wt;  // bf16 group sums of the L x L weights, for the final products
     alignas(16) float rk[L];
     alignas(16) float rq[L];
     alignas(16) float gam[L];
     float eg[L], el[L];
     alignas(16) float beta[L];
     float ell[L];
-    float bv[2][L], pa[2][L], pdb[2][L], rs[L];
+    float bv[2][L], pa[2][L], pdb[2][L];
+    float rowp[2][L], colp[4][L];  // row sums (per half of the columns) and column sums (per row tile) of E
     float red[NTG / 64];
     // per value head (slot = head % HB), for the deferred section: the
     // prefix-summed and suffix-summed terms of dl, the db factor, l, and the
@@ -611,15 +591,11 @@ struct ChunkBwdGrad {
     // loaded when the workgroup starts
     float ha[HB][L], hm[HB][L];
   };
-  // Per-head data loaded ahead: the scalars and Tx rows a head starts with,
-  // and what its tail needs (the chunk's P^T / A^T tiles, a and the mask).
+  // Per-head data loaded ahead: the scalars and Tx rows a head starts with.
   struct HeadStart {
     float gam, eg, el, beta, ell, egl;  // step t = tid (tid < L)
     float alog, dtb;                    // the head's A_log, dt_bias
     bf16x8 txb[2];                      // Tx row ta
-  };
-  struct HeadTail {
-    uint4 pt, at;  // chunk tid of P^T / A^T (row tid >> 3, cols 8 (tid & 7) ..)
   };
   // Global data of one slab, loaded a slab ahead.
   static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the X / dO / dv tiles
@@ -687,13 +663,6 @@ struct ChunkBwdGrad {
       hs.txb[0] = load_bf16x8(txr);
       hs.txb[1] = load_bf16x8(txr + 32);
     }
-  }
-  __device__ static void load_tail(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, HeadTail& ht) {
-    const Dims& d = p.d;
-    const size_t mat = (static_cast<size_t>(x.b * d.Hv + h) * x.NC + x.c) * L * L;
-    const int u = tid & (L * L / 8 - 1);
-    ht.pt = *reinterpret_cast<const uint4*>(p.cb.PqT + mat + 8 * u);
-    ht.at = *reinterpret_cast<const uint4*>(p.cb.AtT + mat + 8 * u);
   }
 
   __device__ static void put_chunks(Smem& sm, int tid, const Pf& f) {
@@ -927,6 +896,9 @@ struct ChunkBwdGrad {
     // workgroup (loading them inside the slab loop would make each wait for
     // them also wait for the next slab's prefetch, issued before them)
     bf16x8 ka[KS], qa[KS];
+    // and the k rows of the column tiles 2 hw, 2 hw + 1 of this wave's L x L
+    // terms (the B operands of its Gram tiles)
+    bf16x8 kb[2][KS];
     {  // quad-coalesced (lane m reads piece m % 4 of row m / 4: four lanes cover
        // 64 contiguous bytes); moved to the operand layout below, once the
        // first slab's prefetch is issued
@@ -936,6 +908,13 @@ struct ChunkBwdGrad {
       for (int kt = 0; kt < KS; ++kt) {
         ka[kt] = load_bf16x8(kc + o + 32 * kt);
         qa[kt] = load_bf16x8(qc + o + 32 * kt);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tb = 16 * (2 * (tid0 >> 8) + u) + coal_row(l);
+        const uint32_t ob = static_cast<uint32_t>(min(tb, x.tl)) * qk_row + 8 * coal_piece(l);
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) kb[u][kt] = load_bf16x8(kc + ob + 32 * kt);
       }
     }
 
@@ -948,7 +927,28 @@ struct ChunkBwdGrad {
       ka[kt] = to_mfma_layout(ka[kt]);
       qa[kt] = to_mfma_layout(qa[kt]);
     }
-    for (int e = tid0; e < L * WR; e += NTG) sm.ws.f.q[e] = sm.ws.f.k1[e] = sm.ws.f.k2[e] = 0.f;
+    // The raw Grams of the chunk in the accumulator layout of the L x L terms:
+    // lane register r of [u] holds element (a, b), a = tc0 + r, b = 16 (2 hw +
+    // u) + lr, of kk = K K^T and qk = Q K^T (the products chunk_prep forms
+    // for A and P, in the same order).  With them every L x L term of a head
+    // is formed in registers: A[b][a] = e^{-|g_a - g_b|} rk_a rk_b kk, P[a][b]
+    // = e^{g_a - g_b} rq_a rk_b qk (b <= a).
+    f32x4 kk[2], qk[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      kk[u] = qk[u] = f4zero();
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        const bf16x8 bk = to_mfma_layout(kb[u][kt]);
+        kk[u] = mfma16(ka[kt], bk, kk[u]);
+        qk[u] = mfma16(qa[kt], bk, qk[u]);
+      }
+    }
+    // the group sums of the L x L weights, same layout: Wq diag(rk), V1 (=
+    // (Wk1 diag(rq))^T) and U (Wk2 diag(rk) = (U + U^T) diag(rk))
+    f32x4 wq[2], v1[2], uu[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) wq[u] = v1[u] = uu[u] = f4zero();
     if (tid0 < L) {
       sm.rk[tid0] = rk0;
       sm.rq[tid0] = rq0;
@@ -960,8 +960,6 @@ struct ChunkBwdGrad {
     for (int hh = 0; hh < G; ++hh) {
       const int h = x.j * G + hh, slot = hh % HB;
       const Lanes ln;
-      HeadTail ht;  // issued now, used after the slabs
-      load_tail(p, x, ln.tid, h, ht);
       __syncthreads();  // the previous head is done with every shared array
       if (ln.tid < L) {
         const int t = ln.tid;
@@ -986,7 +984,18 @@ struct ChunkBwdGrad {
       // the next head's scalars (the last head reloads its own: unused)
       load_start(p, x, Lanes().tid, min(h + 1, hlast), hs);
 
-      // ---- per-row sums of head h
+      // ---- per-row sums of head h; its L x L weights (added to the group
+      // sums) and rectangle terms of dl, in the lane's accumulator layout
+      // (a = tc0 + r, b = 16 (2 hw + u) + lr, d = e^{-|g_a - g_b|}; dox =
+      // dO_a . X_b, xe = X_a . dv_b):
+      //   Wq diag(rk): [b <= a] d beta_b dox rk_b
+      //   V1:          [b <= a] d beta_b dox rq_a     (Wk1 diag(rq) = V1^T)
+      //   U:          -[a < b]  d beta_a xe           (Wk2 diag(rk) = (U + U^T) diag(rk))
+      // The rectangle terms m[r][s] = [s < r] beta_s (P[r][s] dox[r][s] -
+      // A[r][s] xe[s][r]) enter dl only through colsum(m) - rowsum(m), which
+      // equals colsum(E) - rowsum(E) for E[a][b] = [b < a] beta_b P[a][b] dox +
+      // [a < b] beta_a A[b][a] xe (the second part is minus the xe term of
+      // m[b][a]).
       {
         const Lanes q;
 #pragma unroll
@@ -1005,108 +1014,62 @@ struct ChunkBwdGrad {
         }
         const float phdh = wave_sum(ac.phdh);
         if (q.l == 0) sm.red[q.w] = phdh;
-        {
-          const int row = q.tid >> 3, c8 = 8 * (q.tid & 7);
-          const int o = row * L + 8 * ((c8 >> 3) ^ ((row >> 3) & 7));
-          *reinterpret_cast<uint4*>(&sm.u.h.pt[o]) = ht.pt;
-          *reinterpret_cast<uint4*>(&sm.u.h.at[o]) = ht.at;
-        }
+
+        const int tc0 = q.tc0;
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[tc0]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[tc0]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&sm.rq[tc0]);
+        const float4 k4 = *reinterpret_cast<const float4*>(&sm.rk[tc0]);
+        const float ga[4] = {g4.x, g4.y, g4.z, g4.w}, ba[4] = {b4.x, b4.y, b4.z, b4.w};
+        const float rqa[4] = {q4.x, q4.y, q4.z, q4.w}, rka[4] = {k4.x, k4.y, k4.z, k4.w};
+        float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) {
+          const int b = 16 * (2 * q.hw + u) + q.lr;
+          const float gb = sm.gam[b], bb = sm.beta[b], rkb = sm.rk[b];
+          float colp = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            sm.u.h.dox[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = ac.dox[u][r];
-            sm.u.h.xe[(q.tc0 + r) * LP + 16 * (2 * q.hw + u) + q.lr] = ac.xe[u][r];
+            const int a = tc0 + r;
+            const bool ok = a < Lc && b < Lc;
+            const bool lo = ok && b <= a, st = ok && b < a, up = ok && a < b;
+            const float dec = __expf(-fabsf(ga[r] - gb));  // hardware exp (bf16-level weights)
+            const float bd = dec * bb * ac.dox[u][r];    // d beta_b dox
+            const float ux = dec * ba[r] * ac.xe[u][r];  // d beta_a xe
+            wq[u][r] += lo ? bd * rkb : 0.f;
+            v1[u][r] += lo ? bd * rqa[r] : 0.f;
+            uu[u][r] -= up ? ux : 0.f;
+            const float e = st ? bd * rqa[r] * rkb * qk[u][r] : up ? ux * rka[r] * rkb * kk[u][r] : 0.f;
+            rowp[r] += e;
+            colp += e;
           }
+          // column b: the lane's four rows, then the wave's four row groups
+          colp += __shfl_xor(colp, 16);
+          colp += __shfl_xor(colp, 32);
+          if (q.lg == 0) sm.colp[q.tt][b] = colp;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = row_sum16(rowp[r]);
+          if (q.lr == 0) sm.rowp[q.hw][tc0 + r] = v;
+        }
       }
       __syncthreads();
-      // ---- L x L weights of head h (added to the group sums), the rectangle
-      // terms of dl and their row sums
+      // ---- this head's inputs of the deferred gate-gradient section
       {
         const Lanes q;
-        const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
-        const bool tv = t < Lc;
-        const float gt = sm.gam[t], bt = sm.beta[t];
-        float* pw[3] = {&sm.ws.f.q[t * WR + s0], &sm.ws.f.k1[t * WR + s0], &sm.ws.f.k2[t * WR + s0]};
-        float wv[3][8];
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-          const float4 lo = *reinterpret_cast<const float4*>(pw[a]), hi = *reinterpret_cast<const float4*>(pw[a] + 4);
-          wv[a][0] = lo.x; wv[a][1] = lo.y; wv[a][2] = lo.z; wv[a][3] = lo.w;
-          wv[a][4] = hi.x; wv[a][5] = hi.y; wv[a][6] = hi.z; wv[a][7] = hi.w;
-        }
-        // per half of the thread's 8 columns, every operand is read before any
-        // is used and the terms are selected, not branched on (a branch would
-        // wait for each element's reads in turn)
-        float rsum = 0.f;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int sb = s0 + 4 * h2;
-          const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[sb]);
-          const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[sb]);
-          const float4 k4 = *reinterpret_cast<const float4*>(&sm.rk[sb]);
-          const float4 q4 = *reinterpret_cast<const float4*>(&sm.rq[sb]);
-          const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, bs[4] = {b4.x, b4.y, b4.z, b4.w};
-          const float rks[4] = {k4.x, k4.y, k4.z, k4.w}, rqs[4] = {q4.x, q4.y, q4.z, q4.w};
-          float doxts[4], doxst[4], xets[4], xest[4], ptv[4], atv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int s = sb + e;
-            doxts[e] = sm.u.h.dox[t * LP + s];
-            doxst[e] = sm.u.h.dox[s * LP + t];
-            xets[e] = sm.u.h.xe[t * LP + s];
-            xest[e] = sm.u.h.xe[s * LP + t];
-            // P[t][s] = P^T[s][t], A[t][s] = A^T[s][t] (decays and norms included)
-            // (the swizzle spreads a column's 64 rows over distinct banks)
-            const int po = s * L + 8 * ((t >> 3) ^ ((s >> 3) & 7)) + (t & 7);
-            ptv[e] = to_f32(sm.u.h.pt[po]);
-            atv[e] = to_f32(sm.u.h.at[po]);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int s = sb + e, ew = 4 * h2 + e;
-            const bool ok = tv && s < Lc;
-            const float dec = __expf(-fabsf(gt - gs[e]));  // hardware exp (bf16-level weights)
-            const float w0 = dec * bs[e] * doxts[e] * rks[e];
-            const float w1 = dec * bt * doxst[e] * rqs[e];
-            const float w2 = -dec * (s < t ? bs[e] * xest[e] : bt * xets[e]) * rks[e];
-            wv[0][ew] += ok && s <= t ? w0 : 0.f;
-            wv[1][ew] += ok && s >= t ? w1 : 0.f;
-            wv[2][ew] += ok && s != t ? w2 : 0.f;
-            const float m = ok && s < t ? bs[e] * (ptv[e] * doxts[e] - atv[e] * xest[e]) : 0.f;
-            sm.u.h.m[t * LP + s] = m;
-            rsum += m;
-          }
-          asm volatile("" ::: "memory");  // keeps the halves' reads apart (register pressure)
-        }
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-          *reinterpret_cast<float4*>(pw[a]) = make_float4(wv[a][0], wv[a][1], wv[a][2], wv[a][3]);
-          *reinterpret_cast<float4*>(pw[a] + 4) = make_float4(wv[a][4], wv[a][5], wv[a][6], wv[a][7]);
-        }
-        rsum = oct_sum(rsum);
-        if ((q.tid & 7) == 0) sm.rs[t] = rsum;
-      }
-      __syncthreads();
-      // ---- column sums of the rectangle terms, and this head's inputs of the
-      // deferred gate-gradient section
-      {
-        const Lanes q;
-        const int s = q.tid >> 3, r0 = 8 * (q.tid & 7);
-        float csum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) csum += sm.u.h.m[(r0 + e) * LP + s];
-        csum = oct_sum(csum);
-        if ((q.tid & 7) == 0) {
+        if (q.tid < L) {
+          const int s = q.tid;
           const bool in = s < Lc;
           const float av = in ? sm.el[s] * sm.beta[s] * sm.rk[s] * (sm.pa[0][s] + sm.pa[1][s]) : 0.f;
-          sm.hu[slot][s] = av + csum - sm.rs[s];
+          const float csum = (sm.colp[0][s] + sm.colp[1][s]) + (sm.colp[2][s] + sm.colp[3][s]);
+          sm.hu[slot][s] = av + (csum - (sm.rowp[0][s] + sm.rowp[1][s]));
           sm.hb[slot][s] = in ? sm.bv[0][s] + sm.bv[1][s] : 0.f;
           const float beta = sm.beta[s];
           sm.hdb[slot][s] = (sm.pdb[0][s] + sm.pdb[1][s]) * (1.f - beta);
           sm.hell[slot][s] = sm.ell[s];
         }
-        if (q.tid == 0) {
+        if (q.tid == 64) {
           float hdh = 0.f;
 #pragma unroll
           for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[i];
@@ -1184,38 +1147,45 @@ struct ChunkBwdGrad {
     // ---- final products with the group sums: dQn += Wq Kn, dKn += Wk1 Qn + Wk2 Kn.
     // Their Kn / Qn operands are the chunk's k and q rows the waves have held
     // since the start (each wave its 16-step row tile), put in LDS as [t][i]
-    // tiles and read transposed; the group sums go to bf16 in the space of
-    // the fp32 sums (read into registers first, then a barrier).
+    // tiles and read transposed; the group sums go from the registers to bf16
+    // [t][s] tiles (Wk1 diag(rq) = V1^T, Wk2 diag(rk) = (U + U^T) diag(rk)
+    // with U strictly upper triangular: the lane of (a, b), a < b, writes
+    // both (a, b) and (b, a), the lane of (a, a) writes the zero diagonal).
     lds_barrier();
     {
       const Lanes q;
-      const int t = q.tid >> 3, s0 = 8 * (q.tid & 7);
-      uint32_t w0[4], w1[4], w2[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        w0[e >> 1] = pack2_bf16(sm.ws.f.q[t * WR + s0 + e], sm.ws.f.q[t * WR + s0 + e + 1]);
-        w1[e >> 1] = pack2_bf16(sm.ws.f.k1[t * WR + s0 + e], sm.ws.f.k1[t * WR + s0 + e + 1]);
-        w2[e >> 1] = pack2_bf16(sm.ws.f.k2[t * WR + s0 + e], sm.ws.f.k2[t * WR + s0 + e + 1]);
-      }
       // waves 0-3 (hw = 0) put their k rows, waves 4-7 their q rows
       bf16* kqt = q.hw == 0 ? sm.u.kq.k : sm.u.kq.q;
 #pragma unroll
       for (int kt = 0; kt < KS; ++kt)
         *reinterpret_cast<uint4*>(&kqt[q.ta * KQS + 32 * kt + 8 * q.lg]) =
             __builtin_bit_cast(uint4, q.hw == 0 ? ka[kt] : qa[kt]);
-      lds_barrier();
-      *reinterpret_cast<uint4*>(&sm.ws.w.wq[t * TS + s0]) = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-      *reinterpret_cast<uint4*>(&sm.ws.w.wk[t * WS + s0]) = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-      *reinterpret_cast<uint4*>(&sm.ws.w.wk[t * WS + L + s0]) = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+      const float4 k4 = *reinterpret_cast<const float4*>(&sm.rk[q.tc0]);
+      const float rka[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int b = 16 * (2 * q.hw + u) + q.lr;
+        const float rkb = sm.rk[b];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a = q.tc0 + r;
+          sm.wt.wq[a * TS + b] = bf16_of(wq[u][r]);
+          sm.wt.wk[b * WS + a] = bf16_of(v1[u][r]);
+          if (a <= b) {
+            sm.wt.wk[a * WS + L + b] = bf16_of(uu[u][r] * rkb);
+            sm.wt.wk[b * WS + L + a] = bf16_of(uu[u][r] * rka[r]);
+          }
+        }
+      }
     }
     lds_barrier();
     {
       const Lanes q;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 aq = load_bf16x8(&sm.ws.w.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
-        const bf16x8 a1 = load_bf16x8(&sm.ws.w.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
-        const bf16x8 a2 = load_bf16x8(&sm.ws.w.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
+        const bf16x8 aq = load_bf16x8(&sm.wt.wq[q.ta * TS + 32 * kt + 8 * q.lg]);
+        const bf16x8 a1 = load_bf16x8(&sm.wt.wk[q.ta * WS + 32 * kt + 8 * q.lg]);
+        const bf16x8 a2 = load_bf16x8(&sm.wt.wk[q.ta * WS + L + 32 * kt + 8 * q.lg]);
 #pragma unroll
         for (int k = 0; k < IH; ++k) {
           // steps 32 kt + 8 lg .. + 7 of channel 16 (hw IH + k) + lr

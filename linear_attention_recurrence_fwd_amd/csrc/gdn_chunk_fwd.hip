@@ -221,7 +221,8 @@ struct ChunkPrep {
       sc[SC_ELL * L + t] = sm.ell[t];
     }
 
-    // ---- N (fp32), and the decayed Grams: Mq (forward) or A^T, P^T (backward).
+    // ---- N (fp32), and the decayed Grams: Mq (forward) or P^T (backward; the
+    // gradient pass forms A and P itself from the raw Grams).
     // The per-step values are read first and the terms selected, not branched
     // on (a branch would wait for each element's reads in turn).
     float gt[4], rkt[4], rqt[4], gs[4], rks[4], bs[4];
@@ -255,7 +256,7 @@ struct ChunkPrep {
         const float pq = le ? dec * rqt[r] * rks[ct] * aqk[ct][r] : 0.f;
         sm.u.m.nf[t * SP + s] = nv;
         if (bwd_out) {
-          sm.u.m.st[s * SP + t] = at;  // A^T
+          sm.u.m.st[s * SP + t] = pq;  // P^T
         } else {
           sm.u.m.st[t * SP + s] = pq * bs[ct];  // Mq
         }
@@ -264,13 +265,6 @@ struct ChunkPrep {
     __syncthreads();
     invert_diagonal_block(sm, w, l);
     if (bwd_out) {
-      store_mat(sm, p.cb.AtT + mat, tid);
-      __syncthreads();
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.u.m.st[(16 * ct + lr) * SP + 16 * w + 4 * lg + r] = mq[ct][r];  // P^T
-      __syncthreads();
       store_mat(sm, p.cb.PqT + mat, tid);
       if (fwd_out) {
         __syncthreads();

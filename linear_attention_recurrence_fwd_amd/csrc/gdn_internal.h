@@ -111,7 +111,7 @@ struct ChunkBufs {
   bf16* Tx;   // [B*Hv, NC, L, L] (I + N)^-1, N[t,s] = [s<t] e^{g_t-g_s} rk_t rk_s beta_s (k_t.k_s)
   bf16* Mq;   // [B*Hv, NC, L, L] [s<=t] e^{g_t-g_s} rq_t rk_s beta_s (q_t.k_s)
   // backward only
-  bf16* AtT;  // [B*Hv, NC, L, L] transpose of [s<t] e^{g_t-g_s} rk_t rk_s (k_t.k_s)
+  bf16* AtT;  // [B*Hv, NC, L, L] transpose of [s<t] e^{g_t-g_s} rk_t rk_s (k_t.k_s) (per-key-channel gate only)
   bf16* PqT;  // [B*Hv, NC, L, L] transpose of [s<=t] e^{g_t-g_s} rq_t rk_s (q_t.k_s)
   bf16* QT;   // [B*Hk, NC, Dk, L] raw q of the chunk, transposed
   // per-step chunk scalars, fp32 [B*Hv, NC, SC_ROWS, L]
