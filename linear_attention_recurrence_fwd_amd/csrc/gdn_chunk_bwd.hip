@@ -48,6 +48,7 @@
 //   state_bf16       the bf16 copies of the chunk-start states from fp32
 //                    checkpoints (when the forward did not write them).
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_dev.h"
 #include "gdn_internal.h"
@@ -539,19 +540,38 @@ struct ChunkBwdGrad {
   static constexpr int IT = DK / 16;     // 16-row tiles of Dk
   static constexpr int IH = IT / 2;      // tiles of Dk per wave
   static constexpr int KS = DK / 32;     // MFMA steps over Dk
-  static constexpr int VS = NS + 8;      // bf16 row stride of [i][v] and [t][v] tiles
+  static constexpr int VS = NS + 8;      // bf16 row stride of the recomputed X tiles
   static constexpr int TS = L + 8;       // bf16 row stride of [v][t] tiles and Wq rows
   static constexpr int WS = 2 * L + 8;   // bf16 row stride of [Wk1 | Wk2] rows
   static constexpr int FS = DK + 4;      // fp32 row stride of the final accumulators
-  static constexpr int NB = (DK / 4) * (NS / 4);  // 4x4 blocks of one slab (<= NTG)
-  static_assert(NB <= NTG, "one block per thread");
-  struct Slab {
-    bf16 hv[DK * VS];   // H   [i][v]
-    bf16 dhv[DK * VS];  // dH' [i][v]
-    bf16 rt[NS * TS];   // R   [v][t]
-    bf16 xr[L * VS];    // X   [t][v]
-    bf16 xs[L * VS];    // diag(e^{gL-g} beta) X   [t][v]
-    bf16 vt[3][L * VS]; // X (or v), dO, dv of the slab   [t][v]
+  // The slabs (value head, 32 columns) stream through a ring of NSLOT LDS
+  // slots, filled by direct-to-LDS loads issued PD = NSLOT - 1 slabs ahead of
+  // their use: one barrier per slab, and the loads of the next PD slabs stay
+  // in flight across the per-head sections.  Three slots (two slabs ahead)
+  // where they fit in LDS.
+  static constexpr int NSLOT = (XSV && DK <= 192) ? 3 : 2;
+  static constexpr int PD = NSLOT - 1;
+  static constexpr int HJ = DK / 16;       // 1 KB loads of one H or dH' slab (DK rows x 64 bytes)
+  static constexpr int NJ = 2 * HJ + 12;   // loads of one slab: H, dH' and three 64 x 32 tiles
+  static constexpr int JW = (NJ + 7) / 8;  // loads per wave (waves >= NJ % 8 issue one fewer)
+  static constexpr int JR = NJ % 8 == 0 ? 8 : NJ % 8;  // waves that issue JW loads
+  // One ring slot.  Rows of 64 bytes (4 pieces of 16 bytes); piece p of row i
+  // sits at 4 i + (p ^ sw(i)), which keeps the 16-byte operand reads of 8
+  // consecutive rows and the transposing reads of 4 rows x 2 pieces free of
+  // bank conflicts.
+  struct Slot {
+    bf16 hv[DK * NS];    // H   [i][v]
+    bf16 dhv[DK * NS];   // dH' [i][v]
+    bf16 vt[3][L * NS];  // X (or v), dO, dv of the slab   [t][v]
+  };
+  struct XRec {          // X recomputed from v (no saved copy)
+    bf16 rt[NS * TS];    // R   [v][t]
+    bf16 xr[L * VS];     // X   [t][v]
+    bf16 xs[L * VS];     // diag(e^{gL-g} beta) X   [t][v]
+  };
+  struct Ring {
+    Slot s[NSLOT];
+    std::conditional_t<XSV, int, XRec> xrec;
   };
   struct Wts {
     bf16 wq[L * TS];    // sum over the group of Wq diag(rk)   [t][s]
@@ -566,7 +586,7 @@ struct ChunkBwdGrad {
     bf16 q[L * KQS];  // the chunk's q rows   [t][i]
   };
   union Big {
-    Slab s;
+    Ring r;
     KQ kq;
     Fin f;
   };
@@ -583,96 +603,121 @@ struct ChunkBwdGrad {
     float bv[2][L], pa[2][L], pdb[2][L];
     float rowp[2][L], colp[4][L];  // row sums (per half of the columns) and column sums (per row tile) of E
     float red[NTG / 64];
-    // per value head (slot = head % HB), for the deferred section: the
-    // prefix-summed and suffix-summed terms of dl, the db factor, l, and the
-    // per-head scalars <dH', H>, e^{gamma_L}, A_log and dt_bias
+    // per value head of a batch (slot = head % HB): the per-step gamma, e^g,
+    // e^{gL-g}, beta and l, loaded when the batch starts; for the deferred
+    // section the prefix-summed and suffix-summed terms of dl, the db factor,
+    // l, and the scalars <dH', H>, e^{gamma_L}, A_log and dt_bias; a (fp32)
+    // and the mask (1 = valid step)
+    float bsc[HB][5][L];
     float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB], hal[HB], hdt[HB];
-    // a (fp32) and the mask (1 = valid step) of the first batch of value heads,
-    // loaded when the workgroup starts
     float ha[HB][L], hm[HB][L];
   };
-  // Per-head data loaded ahead: the scalars and Tx rows a head starts with.
-  struct HeadStart {
-    float gam, eg, el, beta, ell, egl;  // step t = tid (tid < L)
-    float alog, dtb;                    // the head's A_log, dt_bias
-    bf16x8 txb[2];                      // Tx row ta
-  };
-  // Global data of one slab, loaded a slab ahead.
-  static constexpr int NCH = 3 * L * NS / 8;  // 16-byte chunks of the X / dO / dv tiles
-  struct Pf {
-    uint2 h[4];    // H rows i0 + a, cols vv0 .. vv0+3 (this thread's block, bf16)
-    uint2 dh[4];   // dH' rows i0 + a, cols vv0 .. vv0+3 (bf16)
-    uint4 ch[2];   // chunks tid and tid + NTG of the X / dO / dv tiles
-  };
   struct Ctx {
-    int b, j, c, NC, t0, Lc, tl, i0, vv0;
+    int b, j, c, NC, G, t0, Lc, tl;
     uint32_t v_row;
   };
 
-  // All loads are unconditional buffer loads, so no load sits under a branch
-  // (where a branch joins, the compiler waits for every outstanding load).
-  // H is the bf16 copy of the state at the chunk's start, in the layout of dH'.
-  __device__ static void prefetch(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, int v0, Pf& f) {
+  __device__ static __forceinline__ int sw(int i) { return (i & 2) | ((i >> 2) & 1); }
+  // element offset of piece p of row i in a ring tile
+  __device__ static __forceinline__ int rpos(int i, int p) { return 8 * (4 * i + (p ^ sw(i))); }
+
+  // This wave's direct-to-LDS loads of slab n (value head j G + n / nsl,
+  // columns 32 (n % nsl) ..) into ring slot n % NSLOT.  Load jb of the slab
+  // (wave jb % 8) covers 64 pieces: H (jb < HJ) or dH' (jb < 2 HJ) rows
+  // 16 jb' .. + 15, or rows 16 b' .. + 15 of tile (jb - 2 HJ) / 4.  H is the
+  // bf16 copy of the state at the chunk's start, in the layout of dH'; tile
+  // rows past the end of the sequence are clamped to the last.
+  __device__ static void issue_slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n) {
     const Dims& d = p.d;
+    const int nsl = d.Dv / NS;
+    const int h = x.j * x.G + n / nsl, v0 = NS * (n % nsl);
+    Slot& s = sm.u.r.s[n % NSLOT];
     const int bh = x.b * d.Hv + h;
     const size_t hsz = static_cast<size_t>(DK) * d.Dv;
-    const size_t slot = (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * hsz;
-    const rsrc_t rh = make_rsrc(p.cb.Hb + slot, hsz * 2);
-    const rsrc_t rdh = make_rsrc(p.dHend + slot, hsz * 2);
-    const uint32_t ho = 2 * (x.i0 * d.Dv + v0 + x.vv0);
+    const size_t so = (static_cast<size_t>(x.c) * d.B * d.Hv + bh) * hsz;
+    const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv;
+    const size_t vbytes = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int l = threadIdx.x & 63;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) f.h[a] = buf_u2(rh, ho + 2 * a * d.Dv);
-#pragma unroll
-    for (int a = 0; a < 4; ++a) f.dh[a] = buf_u2(rdh, ho + 2 * a * d.Dv);
-    const size_t vbase = ((static_cast<size_t>(x.b) * d.T + x.t0) * d.Hv + h) * d.Dv + v0;
-    const size_t vrem = (static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv - vbase) * 2;
-    const bf16* t0src = XSV ? p.cb.X : static_cast<const bf16*>(p.v);  // tile 0: X, or v to recompute it from
-    const rsrc_t rs[3] = {make_rsrc(t0src + vbase, vrem),
-                          make_rsrc(static_cast<const bf16*>(p.dO) + vbase, vrem),
-                          make_rsrc(static_cast<const bf16*>(p.dv) + vbase, vrem)};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ci = min(tid + u * NTG, NCH - 1);
-      const int row = (ci / (NS / 8)) % L, c8 = 8 * (ci % (NS / 8));
-      // the tensor of a chunk is the same for the 64 lanes of a wave (256
-      // chunks per tensor), so the descriptor stays in scalar registers
-      const int ten = __builtin_amdgcn_readfirstlane(ci / (L * NS / 8));
-      const uint32_t o = 2 * (static_cast<uint32_t>(min(row, x.tl)) * x.v_row + c8);
-      const rsrc_t r = ten == 0 ? rs[0] : ten == 1 ? rs[1] : rs[2];
-      f.ch[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+    for (int k = 0; k < JW; ++k) {
+      const int jb = w + 8 * k;
+      if (jb < 2 * HJ) {
+        const bool isd = jb >= HJ;
+        const int blk = isd ? jb - HJ : jb;
+        const int ps = 64 * blk + l, i = ps >> 2;
+        const uint32_t o = 2 * static_cast<uint32_t>(i * d.Dv + v0 + 8 * ((ps & 3) ^ sw(i)));
+        if (isd)
+          dma16(raw_desc(p.dHend + so, hsz * 2), &s.dhv[512 * blk], o);
+        else
+          dma16(raw_desc(p.cb.Hb + so, hsz * 2), &s.hv[512 * blk], o);
+      } else if (jb < NJ) {
+        const int u = jb - 2 * HJ, ten = u >> 2, blk = u & 3;
+        const int t = 16 * blk + (l >> 2);
+        const uint32_t o = 2 * (static_cast<uint32_t>(min(t, x.tl)) * x.v_row + v0 + 8 * ((l & 3) ^ sw(t)));
+        const bf16* src = ten == 0 ? (XSV ? p.cb.X : static_cast<const bf16*>(p.v))
+                          : ten == 1 ? static_cast<const bf16*>(p.dO) : static_cast<const bf16*>(p.dv);
+        dma16(raw_desc(src + vbase, vbytes), &s.vt[ten][512 * blk], o);
+      }
     }
   }
-  __device__ static void load_start(const ChunkBwdArgs& p, const Ctx& x, int tid, int h, HeadStart& hs) {
-    const Dims& d = p.d;
-    const int bh = x.b * d.Hv + h;
-    const float* scc = p.cb.sc + (static_cast<size_t>(bh) * x.NC + x.c) * SC_ROWS * L;
-    const int t = tid & 63;
-    hs.gam = scc[SC_GAM * L + t];
-    hs.eg = scc[SC_EG * L + t];
-    hs.el = scc[SC_EL * L + t];
-    hs.beta = scc[SC_BETA * L + t];
-    hs.ell = scc[SC_ELL * L + t];
-    hs.egl = scc[SC_EGL * L];
-    hs.alog = p.A_log[h];
-    hs.dtb = p.dt_bias[h];
-    if constexpr (XSV) {  // X is read, not recomputed: Tx is not needed
-      hs.txb[0] = hs.txb[1] = bf16x8{};
+  // Waits for this wave's loads of every slab but the newest `later` ones.
+  __device__ static void wait_slabs(bool later) {
+    if (PD > 1 && later) {
+      if (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) < JR)
+        wait_vm<JW>();
+      else
+        wait_vm<JW - 1>();
     } else {
-      const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
-      const bf16* txr = p.cb.Tx + (static_cast<size_t>(bh) * x.NC + x.c) * L * L + ta * L + 8 * lg;
-      hs.txb[0] = load_bf16x8(txr);
-      hs.txb[1] = load_bf16x8(txr + 32);
+      wait_vm<0>();
     }
   }
 
-  __device__ static void put_chunks(Smem& sm, int tid, const Pf& f) {
+  // The per-step and per-head scalars of value heads hb0 .. hb0 + HB - 1 of
+  // the group (clamped to the group) into the batch arrays.
+  __device__ static void load_batch(const ChunkBwdArgs& p, const Ctx& x, Smem& sm, int hb0) {
+    const Dims& d = p.d;
+    const int tid = threadIdx.x, t = tid & 63, k = tid >> 6;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ci = tid + u * NTG;
-      if (ci < NCH) {
-        const int ten = ci / (L * NS / 8), row = (ci / (NS / 8)) % L, c8 = 8 * (ci % (NS / 8));
-        *reinterpret_cast<uint4*>(&sm.u.s.vt[ten][row * VS + c8]) = f.ch[u];
+    for (int rr0 = 0; rr0 < HB * 5; rr0 += NTG / 64) {
+      const int rr = rr0 + k;
+      if (rr < HB * 5) {
+        const int hk = rr / 5, row = rr % 5;
+        const int h = x.j * x.G + min(hb0 + hk, x.G - 1);
+        const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + h) * x.NC + x.c) * SC_ROWS * L;
+        const int sr = row == 0 ? SC_GAM : row == 1 ? SC_EG : row == 2 ? SC_EL : row == 3 ? SC_BETA : SC_ELL;
+        sm.bsc[hk][row][t] = scc[sr * L + t];
       }
+    }
+    if (tid < HB * 64) {
+      const int hk = k, h = x.j * x.G + min(hb0 + hk, x.G - 1);
+      const int tc = min(t, x.tl);
+      const float av = __uint_as_float(static_cast<uint32_t>(
+          static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + h]) << 16);
+      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
+                                  p.mask ? static_cast<size_t>(d.B) * d.T : 0);
+      const uint32_t mv = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0));
+      sm.ha[hk][t] = av;
+      sm.hm[hk][t] = p.mask == nullptr || mv != 0 ? 1.f : 0.f;
+      if (t == 0) {
+        const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + h) * x.NC + x.c) * SC_ROWS * L;
+        sm.hegl[hk] = scc[SC_EGL * L];
+        sm.hal[hk] = p.A_log[h];
+        sm.hdt[hk] = p.dt_bias[h];
+      }
+    }
+  }
+  // Tx row ta of value head h (only where X is recomputed).
+  __device__ static void load_tx(const ChunkBwdArgs& p, const Ctx& x, int h, bf16x8 (&txb)[2]) {
+    if constexpr (XSV) {
+      txb[0] = txb[1] = bf16x8{};
+    } else {
+      const int tid = threadIdx.x;
+      const int ta = 16 * ((tid >> 6) & 3) + (tid & 15), lg = (tid & 63) >> 4;
+      const size_t bh = static_cast<size_t>(x.b) * p.d.Hv + h;
+      const bf16* txr = p.cb.Tx + (bh * x.NC + x.c) * L * L + ta * L + 8 * lg;
+      txb[0] = load_bf16x8(txr);
+      txb[1] = load_bf16x8(txr + 32);
     }
   }
 
@@ -700,91 +745,88 @@ struct ChunkBwdGrad {
     float pb[4], pa, pdb, phdh;
   };
   // Contractions over the slab's columns: dQn, dKn (state terms) and the
-  // Grams dO X^T, X dv^T.  xr8 / xs8: rows ta of X and of
-  // diag(e^{gL-g} beta) X; xt: the X tile [t][v].
-  __device__ static void contract(const Smem& sm, const bf16* xt, const bf16* dt, const bf16* et, int ta, int lr,
-                                  int lg, int hw, const bf16x8& xr8, const bf16x8& xs8, f32x4 (&accQ)[IH],
+  // Grams dO X^T, X dv^T, and the waves of row tile 0 (one per half of Dk)
+  // <dH', H> from the same operand reads.  xr8 / xs8: rows ta of X and of
+  // diag(e^{gL-g} beta) X; xt: the X tile [t][v] (a ring tile, or with XR
+  // the recomputed one).
+  template <bool XR>
+  __device__ static void contract(const Smem& sm, const Slot& s, const bf16* xt, int ta, int lr, int lg, int hw,
+                                  int tt, const bf16x8& xr8, const bf16x8& xs8, f32x4 (&accQ)[IH],
                                   f32x4 (&accK)[IH], HeadAcc& ac) {
+    const bf16* dt = s.vt[1];
+    const bf16* et = s.vt[2];
     const float sq = sm.eg[ta];
-    const bf16x8 do8 = load_bf16x8(&dt[ta * VS + 8 * lg]);
-    const bf16x8 dos8 = scale8(do8, sq), dvs8 = scale8(load_bf16x8(&et[ta * VS + 8 * lg]), -sq);
+    const bf16x8 do8 = load_bf16x8(&dt[rpos(ta, lg)]);
+    const bf16x8 dos8 = scale8(do8, sq), dvs8 = scale8(load_bf16x8(&et[rpos(ta, lg)]), -sq);
 #pragma unroll
     for (int k = 0; k < IH; ++k) {
       const int it = hw * IH + k;
-      const bf16x8 bhv = load_bf16x8(&sm.u.s.hv[(16 * it + lr) * VS + 8 * lg]);
-      const bf16x8 bdh = load_bf16x8(&sm.u.s.dhv[(16 * it + lr) * VS + 8 * lg]);
+      const bf16x8 bhv = load_bf16x8(&s.hv[rpos(16 * it + lr, lg)]);
+      const bf16x8 bdh = load_bf16x8(&s.dhv[rpos(16 * it + lr, lg)]);
       accQ[k] = mfma16(dos8, bhv, accQ[k]);
       accK[k] = mfma16(dvs8, bhv, accK[k]);
       accK[k] = mfma16(xs8, bdh, accK[k]);
+      if (__builtin_amdgcn_readfirstlane(tt) == 0) {
+        const uint4 hu = __builtin_bit_cast(uint4, bhv), du = __builtin_bit_cast(uint4, bdh);
+        ac.phdh = dot2_bf16(hu.x, du.x, ac.phdh);
+        ac.phdh = dot2_bf16(hu.y, du.y, ac.phdh);
+        ac.phdh = dot2_bf16(hu.z, du.z, ac.phdh);
+        ac.phdh = dot2_bf16(hu.w, du.w, ac.phdh);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int sr = (16 * (2 * hw + u) + lr) * VS + 8 * lg;
-      ac.dox[u] = mfma16(do8, load_bf16x8(&xt[sr]), ac.dox[u]);
-      ac.xe[u] = mfma16(xr8, load_bf16x8(&et[sr]), ac.xe[u]);
+      const int sr = 16 * (2 * hw + u) + lr;
+      const int xo = XR ? sr * VS + 8 * lg : rpos(sr, lg);
+      ac.dox[u] = mfma16(do8, load_bf16x8(&xt[xo]), ac.dox[u]);
+      ac.xe[u] = mfma16(xr8, load_bf16x8(&et[rpos(sr, lg)]), ac.xe[u]);
     }
   }
-  // One 32-column slab of head h: stage the prefetched H, dH', X, dO, dv
-  // in LDS, issue the next slab's loads (unconditional, so the prefetch stays
-  // in flight), and accumulate.
-  __device__ static void slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, bool has_blk, int h, int hlast,
-                              int si, int nsl, Pf& pf, const bf16x8 (&ka)[KS],
-                              const bf16x8 (&qa)[KS], const bf16x8 (&txb)[2], f32x4 (&accQ)[IH],
-                              f32x4 (&accK)[IH], HeadAcc& ac) {
+  // Slab n (of ns in all): wait for its loads, meet the other waves, issue
+  // the loads of slab n + PD into the slot that slab n - 1 used, and
+  // accumulate.
+  __device__ static void slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n, int ns,
+                              const bf16x8 (&ka)[KS], const bf16x8 (&qa)[KS], const bf16x8 (&txb)[2],
+                              f32x4 (&accQ)[IH], f32x4 (&accK)[IH], HeadAcc& ac) {
+    wait_slabs(n + 1 < ns);
+    lds_barrier();  // slab n complete in its slot; every wave is done with slab n - 1
+    if (n + PD < ns) issue_slab(p, sm, x, n + PD);
     const Lanes q;
     const int lr = q.lr, lg = q.lg, ta = q.ta, tc0 = q.tc0, hw = q.hw;
-    // ---- this slab's H and dH' into LDS ([i][v]), <dH', H>; X / dO / dv tiles
-    if (has_blk) {
-      const int i0 = x.i0, vv0 = x.vv0;
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        *reinterpret_cast<uint2*>(&sm.u.s.hv[(i0 + a) * VS + vv0]) = pf.h[a];
-        *reinterpret_cast<uint2*>(&sm.u.s.dhv[(i0 + a) * VS + vv0]) = pf.dh[a];
-        const uint32_t hw2[2] = {pf.h[a].x, pf.h[a].y}, dw2[2] = {pf.dh[a].x, pf.dh[a].y};
-#pragma unroll
-        for (int e = 0; e < 2; ++e) ac.phdh = dot2_bf16(hw2[e], dw2[e], ac.phdh);
-      }
-    }
-    put_chunks(sm, q.tid, pf);
-    {  // the next slab: of this head, or the first of the next head (the last
-       // head's last slab reloads its own first slab: harmless, never used)
-      const bool more = si + 1 < nsl;
-      const int nh = min(h + 1, hlast);
-      prefetch(p, x, q.tid, more ? h : nh, more ? (si + 1) * NS : 0, pf);
-    }
-    lds_barrier();
-    const bf16* vt = sm.u.s.vt[0];
-    const bf16* dt = sm.u.s.vt[1];
-    const bf16* et = sm.u.s.vt[2];
+    const Slot& s = sm.u.r.s[n % NSLOT];
+    const bf16* vt = s.vt[0];
+    const bf16* dt = s.vt[1];
+    const bf16* et = s.vt[2];
     // ---- K H, Q H (rows tc0 + r, cols 16 hw + lr) and (K dH')^T (rows 16 hw + 4 lg + r, col ta).
     // The H and dH' operands (rows 32 kt + 8 lg .. + 7 of column 16 hw + lr)
     // are read transposed from the [i][v] tiles.
     f32x4 kh = f4zero(), qh = f4zero(), kdt = f4zero();
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
-      const int o0 = (32 * kt + 8 * lg + (lr >> 2)) * VS + 16 * hw + 4 * (lr & 3);
-      const uint2 h0 = lds_read_tr16(&sm.u.s.hv[o0]), h1 = lds_read_tr16(&sm.u.s.hv[o0 + 4 * VS]);
-      const uint2 d0 = lds_read_tr16(&sm.u.s.dhv[o0]), d1 = lds_read_tr16(&sm.u.s.dhv[o0 + 4 * VS]);
+      const int r0 = 32 * kt + 8 * lg + (lr >> 2), pc = 2 * hw + ((lr >> 1) & 1), e = 4 * (lr & 1);
+      const uint2 h0 = lds_read_tr16(&s.hv[rpos(r0, pc) + e]), h1 = lds_read_tr16(&s.hv[rpos(r0 + 4, pc) + e]);
+      const uint2 d0 = lds_read_tr16(&s.dhv[rpos(r0, pc) + e]), d1 = lds_read_tr16(&s.dhv[rpos(r0 + 4, pc) + e]);
       const bf16x8 bh8 = as_bf16x8(make_uint4(h0.x, h0.y, h1.x, h1.y));
       kh = mfma16(ka[kt], bh8, kh);
       qh = mfma16(qa[kt], bh8, qh);
       kdt = mfma16(as_bf16x8(make_uint4(d0.x, d0.y, d1.x, d1.y)), ka[kt], kdt);
     }
+    // element (t, 16 hw + lr) and the 4 columns 16 hw + 4 lg .. of row ta in the ring tiles
+    const int pe = 2 * hw + (lr >> 3), ee = lr & 7;
+    const int pv = 2 * hw + (lg >> 1), ev = 4 * (lg & 1);
     if constexpr (XSV) {
       // ---- b_r partial sums; X (tile 0) is loaded
-      const bf16* xl = sm.u.s.vt[0];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = tc0 + r, o = t * VS + 16 * hw + lr;
+        const int t = tc0 + r, o = rpos(t, pe) + ee;
         const float eg = sm.eg[t], cr = eg * sm.rk[t];
         const float dov = to_f32(dt[o]), dvv = to_f32(et[o]);
         ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
         ac.pb[r] = fmaf(-cr * kh[r], dvv, ac.pb[r]);
       }
       // X[ta][16 hw + 4 lg + r], in the layout of (K dH')^T
-      const int vc = 16 * hw + 4 * lg;
-      const uint2 x4 = *reinterpret_cast<const uint2*>(&xl[ta * VS + vc]);
-      const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
+      const uint2 x4 = *reinterpret_cast<const uint2*>(&vt[rpos(ta, pv) + ev]);
+      const uint2 e4 = *reinterpret_cast<const uint2*>(&et[rpos(ta, pv) + ev]);
       const float x4f[4] = {__uint_as_float(x4.x << 16), __uint_as_float(x4.x & 0xffff0000u),
                             __uint_as_float(x4.y << 16), __uint_as_float(x4.y & 0xffff0000u)};
       const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
@@ -794,22 +836,23 @@ struct ChunkBwdGrad {
         ac.pdb = fmaf(e4f[r], x4f[r], ac.pdb);
         ac.pa = fmaf(kdt[r], x4f[r], ac.pa);
       }
-      const bf16x8 xr8 = load_bf16x8(&xl[ta * VS + 8 * lg]);
-      contract(sm, xl, dt, et, ta, lr, lg, hw, xr8, scale8(xr8, sm.el[ta] * sm.beta[ta]), accQ, accK, ac);
+      const bf16x8 xr8 = load_bf16x8(&vt[rpos(ta, lg)]);
+      contract<false>(sm, s, vt, ta, lr, lg, hw, q.tt, xr8, scale8(xr8, sm.el[ta] * sm.beta[ta]), accQ, accK, ac);
     } else {
+      XRec& xr = sm.u.r.xrec;
       // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
       {
         float rv[4];
   #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = tc0 + r, o = t * VS + 16 * hw + lr;
+          const int t = tc0 + r, o = rpos(t, pe) + ee;
           const float eg = sm.eg[t], cr = eg * sm.rk[t];
           const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), dvv = to_f32(et[o]);
           rv[r] = vv - cr * kh[r];
           ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
           ac.pb[r] = fmaf(-cr * kh[r], dvv, ac.pb[r]);
         }
-        *reinterpret_cast<uint2*>(&sm.u.s.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
+        *reinterpret_cast<uint2*>(&xr.rt[(16 * hw + lr) * TS + tc0]) = pack4_bf16(rv[0], rv[1], rv[2], rv[3]);
       }
       lds_barrier();
       // ---- X^T = R^T Tx^T: the lane holds X[ta][16 hw + 4 lg + r]
@@ -817,7 +860,7 @@ struct ChunkBwdGrad {
         f32x4 xt = f4zero();
   #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
-          xt = mfma16(load_bf16x8(&sm.u.s.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
+          xt = mfma16(load_bf16x8(&xr.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
         const int vc = 16 * hw + 4 * lg;
         const float sx = sm.el[ta] * sm.beta[ta];
         // X in bf16, as the forward saves it: the gate terms and the scaled copy
@@ -825,9 +868,9 @@ struct ChunkBwdGrad {
         const uint2 x4 = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
         const float x4f[4] = {__uint_as_float(x4.x << 16), __uint_as_float(x4.x & 0xffff0000u),
                               __uint_as_float(x4.y << 16), __uint_as_float(x4.y & 0xffff0000u)};
-        *reinterpret_cast<uint2*>(&sm.u.s.xr[ta * VS + vc]) = x4;
-        *reinterpret_cast<uint2*>(&sm.u.s.xs[ta * VS + vc]) = pack4_bf16(sx * x4f[0], sx * x4f[1], sx * x4f[2], sx * x4f[3]);
-        const uint2 e4 = *reinterpret_cast<const uint2*>(&et[ta * VS + vc]);
+        *reinterpret_cast<uint2*>(&xr.xr[ta * VS + vc]) = x4;
+        *reinterpret_cast<uint2*>(&xr.xs[ta * VS + vc]) = pack4_bf16(sx * x4f[0], sx * x4f[1], sx * x4f[2], sx * x4f[3]);
+        const uint2 e4 = *reinterpret_cast<const uint2*>(&et[rpos(ta, pv) + ev]);
         const float e4f[4] = {__uint_as_float(e4.x << 16), __uint_as_float(e4.x & 0xffff0000u),
                               __uint_as_float(e4.y << 16), __uint_as_float(e4.y & 0xffff0000u)};
   #pragma unroll
@@ -837,10 +880,9 @@ struct ChunkBwdGrad {
         }
       }
       lds_barrier();
-      contract(sm, sm.u.s.xr, dt, et, ta, lr, lg, hw, load_bf16x8(&sm.u.s.xr[ta * VS + 8 * lg]),
-               load_bf16x8(&sm.u.s.xs[ta * VS + 8 * lg]), accQ, accK, ac);
+      contract<true>(sm, s, xr.xr, ta, lr, lg, hw, q.tt, load_bf16x8(&xr.xr[ta * VS + 8 * lg]),
+                     load_bf16x8(&xr.xs[ta * VS + 8 * lg]), accQ, accK, ac);
     }
-    lds_barrier();
   }
 
   __device__ static void run(const ChunkBwdArgs& p, Smem& sm) {
@@ -852,6 +894,7 @@ struct ChunkBwdGrad {
     x.j = bj % d.Hk;
     const int G = d.G();
     x.NC = d.nchunk();
+    x.G = G;
     x.t0 = x.c * L;
     x.Lc = min(L, d.T - x.t0);
     x.tl = x.Lc - 1;
@@ -862,32 +905,14 @@ struct ChunkBwdGrad {
     const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
     const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
     const int tid0 = threadIdx.x;
-    // the first head's scalars, issued first: each later head's are issued
-    // behind the previous head's slabs, so no head start waits on a load
-    HeadStart hs;
-    load_start(p, x, tid0, x.j * G, hs);
-    const bool has_blk = tid0 < NB;
-    {
-      const int blk = min(tid0, NB - 1);
-      x.i0 = 4 * (blk / (NS / 4));
-      x.vv0 = 4 * (blk % (NS / 4));
-    }
-    // norm factors (the same for every value head of the group; 0 past the
-    // end), loaded first and stored last, so that every load of the start is
-    // in flight before the first wait
-    float rk0, rq0, a0;
-    uint32_t m0;
+    // the first batch of value heads' scalars, and the norm factors (the same
+    // for every value head of the group; 0 past the end)
+    load_batch(p, x, sm, 0);
+    float rk0, rq0;
     {
       const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + x.j * G) * NC + c) * SC_ROWS * L;
       rk0 = scc[SC_RK * L + (tid0 & 63)];
       rq0 = scc[SC_RQ * L + (tid0 & 63)];
-      // a and the mask of step t = lane for value head j G + (wave % HB) of
-      // the group (clamped); every wave loads, waves < HB store
-      const int tc = min(tid0 & 63, x.tl), hd = x.j * G + min((tid0 >> 6) % HB, G - 1);
-      a0 = __uint_as_float(static_cast<uint32_t>(
-               static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + hd]) << 16);
-      const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a, p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-      m0 = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0));
     }
     f32x4 accQ[IH], accK[IH];
 #pragma unroll
@@ -901,7 +926,7 @@ struct ChunkBwdGrad {
     bf16x8 kb[2][KS];
     {  // quad-coalesced (lane m reads piece m % 4 of row m / 4: four lanes cover
        // 64 contiguous bytes); moved to the operand layout below, once the
-       // first slab's prefetch is issued
+       // first slabs' loads are issued
       const int l = tid0 & 63, tr0 = 16 * ((tid0 >> 6) & 3) + coal_row(l);
       const uint32_t o = static_cast<uint32_t>(min(tr0, x.tl)) * qk_row + 8 * coal_piece(l);
 #pragma unroll
@@ -918,10 +943,10 @@ struct ChunkBwdGrad {
       }
     }
 
-    const int nsl = d.Dv / NS;
-    const int hlast = x.j * G + G - 1;
-    Pf pf;
-    prefetch(p, x, tid0, x.j * G, 0, pf);
+    const int ns = G * (d.Dv / NS);  // slabs of the workgroup
+#pragma unroll
+    for (int n = 0; n < PD; ++n)
+      if (n < ns) issue_slab(p, sm, x, n);
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
       ka[kt] = to_mfma_layout(ka[kt]);
@@ -953,36 +978,34 @@ struct ChunkBwdGrad {
       sm.rk[tid0] = rk0;
       sm.rq[tid0] = rq0;
     }
-    if (tid0 < HB * 64) {
-      sm.ha[tid0 >> 6][tid0 & 63] = a0;
-      sm.hm[tid0 >> 6][tid0 & 63] = p.mask == nullptr || m0 != 0 ? 1.f : 0.f;
-    }
+    const int nsl = d.Dv / NS;
+    int n = 0;
     for (int hh = 0; hh < G; ++hh) {
       const int h = x.j * G + hh, slot = hh % HB;
+      if (slot == 0 && hh > 0) {
+        // a later batch of value heads (groups of more than HB): its scalars,
+        // after the previous batch's deferred section (these loads wait for
+        // the ring's, once per batch)
+        __syncthreads();
+        load_batch(p, x, sm, hh);
+      }
+      bf16x8 txb[2];
+      load_tx(p, x, h, txb);
       const Lanes ln;
       __syncthreads();  // the previous head is done with every shared array
       if (ln.tid < L) {
         const int t = ln.tid;
-        sm.gam[t] = hs.gam;
-        sm.eg[t] = hs.eg;
-        sm.el[t] = hs.el;
-        sm.beta[t] = hs.beta;
-        sm.ell[t] = t < Lc ? hs.ell : 0.f;
+        sm.gam[t] = sm.bsc[slot][0][t];
+        sm.eg[t] = sm.bsc[slot][1][t];
+        sm.el[t] = sm.bsc[slot][2][t];
+        sm.beta[t] = sm.bsc[slot][3][t];
+        sm.ell[t] = t < Lc ? sm.bsc[slot][4][t] : 0.f;
       }
-      if (ln.tid == 0) {
-        sm.hegl[slot] = hs.egl;
-        sm.hal[slot] = hs.alog;
-        sm.hdt[slot] = hs.dtb;
-      }
-      const bf16x8 txb[2] = {hs.txb[0], hs.txb[1]};
       __syncthreads();
       HeadAcc ac;
       ac.dox[0] = ac.dox[1] = ac.xe[0] = ac.xe[1] = f4zero();
       ac.pb[0] = ac.pb[1] = ac.pb[2] = ac.pb[3] = ac.pa = ac.pdb = ac.phdh = 0.f;
-      for (int si = 0; si < nsl; ++si)
-        slab(p, sm, x, has_blk, h, hlast, si, nsl, pf, ka, qa, txb, accQ, accK, ac);
-      // the next head's scalars (the last head reloads its own: unused)
-      load_start(p, x, Lanes().tid, min(h + 1, hlast), hs);
+      for (int si = 0; si < nsl; ++si, ++n) slab(p, sm, x, n, ns, ka, qa, txb, accQ, accK, ac);
 
       // ---- per-row sums of head h; its L x L weights (added to the group
       // sums) and rectangle terms of dl, in the lane's accumulator layout
@@ -1085,19 +1108,8 @@ struct ChunkBwdGrad {
         if (q.w < nh) {
           const int k = q.w, hd = x.j * G + hb0 + k, t = q.l;
           const bool in = t < Lc;
-          float av;
-          bool valid;
-          if (hb0 == 0) {  // loaded when the workgroup started
-            av = sm.ha[k][t];
-            valid = sm.hm[k][t] != 0.f;
-          } else {
-            const int tc = min(t, x.tl);
-            av = __uint_as_float(static_cast<uint32_t>(
-                     static_cast<const unsigned short*>(p.a)[(static_cast<size_t>(x.b) * d.T + x.t0 + tc) * d.Hv + hd]) << 16);
-            const rsrc_t rm = make_rsrc(p.mask ? static_cast<const void*>(p.mask) : p.a,
-                                        p.mask ? static_cast<size_t>(d.B) * d.T : 0);
-            valid = p.mask == nullptr || __builtin_amdgcn_raw_buffer_load_b8(rm, x.b * d.T + x.t0 + tc, 0, 0) != 0;
-          }
+          const float av = sm.ha[k][t];
+          const bool valid = sm.hm[k][t] != 0.f;
           // sum over u < t: the prefix sum of the terms shifted by one step;
           // sum over r >= t: the prefix sum of the terms in reverse order,
           // taken back from lane 63 - t
@@ -1126,8 +1138,11 @@ struct ChunkBwdGrad {
             p.part_ddt[pi] = sd;
           }
         }
+        // drained, so that the per-slab waits count only the ring's loads
+        if (hh + 1 < G) wait_vm<0>();
       }
     }
+    wait_vm<0>();  // no direct-to-LDS load may land in the union's later uses
 
     // ---- the q / k rows of the normalisation backward, loaded now (the slabs'
     // loads are done) so that their latency overlaps the final products; the
