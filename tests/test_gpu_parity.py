@@ -259,3 +259,58 @@ def test_chunk_saved_matrices_bitwise(case):
     for x, y in [(o1, o2), (s1, s2)] + [(g1[n], g2[n]) for n in GRADS]:
         assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
                            y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
+
+
+# Groups of more than four value heads per key head: the gradient pass takes
+# the per-head scalars in batches of four, and value heads 4, 8, ... start a
+# new batch.  Ragged T, a mask with invalid steps, with and without the saved
+# record (G = 9 also leaves a last batch of one head).
+GROUPS = {
+    "g6_dk128": (1, 150, 1, 6, 128, 64, 91),
+    "g8_dk192": (2, 100, 1, 8, 192, 32, 92),
+    "g9_dk64": (1, 70, 1, 9, 64, 32, 93),
+    "g5_dk256": (1, 90, 1, 5, 256, 32, 94),
+}
+
+
+def _group_case(name):
+    B, T, Hk, Hv, Dk, Dv, seed = GROUPS[name]
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    mask = (rng.random((B, T)) > 0.2).astype(np.uint8)
+    return inputs.make_case("chunk_" + name, B, T, Hk, Hv, Dk, Dv, "bf16", seed, mask=mask)
+
+
+@pytest.mark.parametrize("save", [False, True])
+@pytest.mark.parametrize("name", list(GROUPS))
+def test_chunk_many_heads_per_group(name, save):
+    c = _group_case(name)
+    say("[groups] case=%s B=%d T=%d Hk=%d Hv=%d Dk=%d Dv=%d save=%d" % (c.name, c.B, c.T, c.Hk, c.Hv, c.Dk,
+                                                                      c.Dv, save))
+    t = upload(c)
+    o, st, ck = gpu_fwd(t, algo=CHUNK, save=save)
+    g = gpu_bwd(t, ck, algo=CHUNK, save=save)
+    torch.cuda.synchronize()
+    ro, rst, rck, rg = oracle_all(c, nthreads=8)
+    pairs = [("o", to64(o), ro), ("state", to64(st), rst)]
+    pairs += [(n, to64(g[n]), rg[n]) for n in GRADS]
+    errs = report("groups", pairs)
+    for n, x in list(g.items()) + [("o", o), ("state", st)]:
+        assert torch.isfinite(x.float()).all(), n
+    bad = {n: e for n, e in errs.items() if not e <= TOL["bf16"]}
+    assert not bad, bad
+
+
+def test_chunk_many_heads_saved_bitwise():
+    """With more than four value heads per key head the saved record still
+    gives the bits of the run without it."""
+    c = _group_case("g6_dk128")
+    say("[groups saved] case=%s" % c.name)
+    t = upload(c)
+    o1, s1, k1 = gpu_fwd(t, algo=CHUNK)
+    g1 = gpu_bwd(t, k1, algo=CHUNK)
+    o2, s2, k2 = gpu_fwd(t, algo=CHUNK, save=True)
+    g2 = gpu_bwd(t, k2, algo=CHUNK, save=True)
+    torch.cuda.synchronize()
+    for x, y in [(o1, o2), (s1, s2)] + [(g1[n], g2[n]) for n in GRADS]:
+        assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.uint8) if y.dtype == torch.bfloat16 else y)
