@@ -596,10 +596,6 @@ struct ChunkBwdGrad {
     alignas(16) Wts wt;  // bf16 group sums of the L x L weights, for the final products
     alignas(16) float rk[L];
     alignas(16) float rq[L];
-    alignas(16) float gam[L];
-    float eg[L], el[L];
-    alignas(16) float beta[L];
-    float ell[L];
     float bv[2][L], pa[2][L], pdb[2][L];
     float rowp[2][L], colp[4][L];  // row sums (per half of the columns) and column sums (per row tile) of E
     float red[NTG / 64];
@@ -608,7 +604,7 @@ struct ChunkBwdGrad {
     // section the prefix-summed and suffix-summed terms of dl, the db factor,
     // l, and the scalars <dH', H>, e^{gamma_L}, A_log and dt_bias; a (fp32)
     // and the mask (1 = valid step)
-    float bsc[HB][5][L];
+    alignas(16) float bsc[HB][5][L];  // rows: gamma, e^g, e^{gL-g}, beta, l (0 past the end)
     float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB], hal[HB], hdt[HB];
     float ha[HB][L], hm[HB][L];
   };
@@ -686,7 +682,8 @@ struct ChunkBwdGrad {
         const int h = x.j * x.G + min(hb0 + hk, x.G - 1);
         const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + h) * x.NC + x.c) * SC_ROWS * L;
         const int sr = row == 0 ? SC_GAM : row == 1 ? SC_EG : row == 2 ? SC_EL : row == 3 ? SC_BETA : SC_ELL;
-        sm.bsc[hk][row][t] = scc[sr * L + t];
+        const float v = scc[sr * L + t];
+        sm.bsc[hk][row][t] = row == 4 && t >= x.Lc ? 0.f : v;
       }
     }
     if (tid < HB * 64) {
@@ -750,12 +747,12 @@ struct ChunkBwdGrad {
   // diag(e^{gL-g} beta) X; xt: the X tile [t][v] (a ring tile, or with XR
   // the recomputed one).
   template <bool XR>
-  __device__ static void contract(const Smem& sm, const Slot& s, const bf16* xt, int ta, int lr, int lg, int hw,
-                                  int tt, const bf16x8& xr8, const bf16x8& xs8, f32x4 (&accQ)[IH],
+  __device__ static void contract(const Smem& sm, int slot, const Slot& s, const bf16* xt, int ta, int lr, int lg,
+                                  int hw, int tt, const bf16x8& xr8, const bf16x8& xs8, f32x4 (&accQ)[IH],
                                   f32x4 (&accK)[IH], HeadAcc& ac) {
     const bf16* dt = s.vt[1];
     const bf16* et = s.vt[2];
-    const float sq = sm.eg[ta];
+    const float sq = sm.bsc[slot][1][ta];
     const bf16x8 do8 = load_bf16x8(&dt[rpos(ta, lg)]);
     const bf16x8 dos8 = scale8(do8, sq), dvs8 = scale8(load_bf16x8(&et[rpos(ta, lg)]), -sq);
 #pragma unroll
@@ -785,7 +782,7 @@ struct ChunkBwdGrad {
   // Slab n (of ns in all): wait for its loads, meet the other waves, issue
   // the loads of slab n + PD into the slot that slab n - 1 used, and
   // accumulate.
-  __device__ static void slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n, int ns,
+  __device__ static void slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n, int ns, int slot,
                               const bf16x8 (&ka)[KS], const bf16x8 (&qa)[KS], const bf16x8 (&txb)[2],
                               f32x4 (&accQ)[IH], f32x4 (&accK)[IH], HeadAcc& ac) {
     wait_slabs(n + 1 < ns);
@@ -819,7 +816,7 @@ struct ChunkBwdGrad {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tc0 + r, o = rpos(t, pe) + ee;
-        const float eg = sm.eg[t], cr = eg * sm.rk[t];
+        const float eg = sm.bsc[slot][1][t], cr = eg * sm.rk[t];
         const float dov = to_f32(dt[o]), dvv = to_f32(et[o]);
         ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
         ac.pb[r] = fmaf(-cr * kh[r], dvv, ac.pb[r]);
@@ -837,7 +834,8 @@ struct ChunkBwdGrad {
         ac.pa = fmaf(kdt[r], x4f[r], ac.pa);
       }
       const bf16x8 xr8 = load_bf16x8(&vt[rpos(ta, lg)]);
-      contract<false>(sm, s, vt, ta, lr, lg, hw, q.tt, xr8, scale8(xr8, sm.el[ta] * sm.beta[ta]), accQ, accK, ac);
+      contract<false>(sm, slot, s, vt, ta, lr, lg, hw, q.tt, xr8, scale8(xr8, sm.bsc[slot][2][ta] * sm.bsc[slot][3][ta]),
+                      accQ, accK, ac);
     } else {
       XRec& xr = sm.u.r.xrec;
       // ---- R = V - diag(e^g rk) K H -> R^T; b_r partial sums
@@ -846,7 +844,7 @@ struct ChunkBwdGrad {
   #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tc0 + r, o = rpos(t, pe) + ee;
-          const float eg = sm.eg[t], cr = eg * sm.rk[t];
+          const float eg = sm.bsc[slot][1][t], cr = eg * sm.rk[t];
           const float vv = to_f32(vt[o]), dov = to_f32(dt[o]), dvv = to_f32(et[o]);
           rv[r] = vv - cr * kh[r];
           ac.pb[r] = fmaf(eg * sm.rq[t] * qh[r], dov, ac.pb[r]);
@@ -862,7 +860,7 @@ struct ChunkBwdGrad {
         for (int kt = 0; kt < 2; ++kt)
           xt = mfma16(load_bf16x8(&xr.rt[(16 * hw + lr) * TS + 32 * kt + 8 * lg]), txb[kt], xt);
         const int vc = 16 * hw + 4 * lg;
-        const float sx = sm.el[ta] * sm.beta[ta];
+        const float sx = sm.bsc[slot][2][ta] * sm.bsc[slot][3][ta];
         // X in bf16, as the forward saves it: the gate terms and the scaled copy
         // use the rounded values
         const uint2 x4 = pack4_bf16(xt[0], xt[1], xt[2], xt[3]);
@@ -880,7 +878,7 @@ struct ChunkBwdGrad {
         }
       }
       lds_barrier();
-      contract<true>(sm, s, xr.xr, ta, lr, lg, hw, q.tt, load_bf16x8(&xr.xr[ta * VS + 8 * lg]),
+      contract<true>(sm, slot, s, xr.xr, ta, lr, lg, hw, q.tt, load_bf16x8(&xr.xr[ta * VS + 8 * lg]),
                      load_bf16x8(&xr.xs[ta * VS + 8 * lg]), accQ, accK, ac);
     }
   }
@@ -991,21 +989,12 @@ struct ChunkBwdGrad {
       }
       bf16x8 txb[2];
       load_tx(p, x, h, txb);
-      const Lanes ln;
-      __syncthreads();  // the previous head is done with every shared array
-      if (ln.tid < L) {
-        const int t = ln.tid;
-        sm.gam[t] = sm.bsc[slot][0][t];
-        sm.eg[t] = sm.bsc[slot][1][t];
-        sm.el[t] = sm.bsc[slot][2][t];
-        sm.beta[t] = sm.bsc[slot][3][t];
-        sm.ell[t] = t < Lc ? sm.bsc[slot][4][t] : 0.f;
-      }
-      __syncthreads();
+      // (the head's scalars are read from the batch arrays; the first slab's
+      // barrier orders them after the batch loads)
       HeadAcc ac;
       ac.dox[0] = ac.dox[1] = ac.xe[0] = ac.xe[1] = f4zero();
       ac.pb[0] = ac.pb[1] = ac.pb[2] = ac.pb[3] = ac.pa = ac.pdb = ac.phdh = 0.f;
-      for (int si = 0; si < nsl; ++si, ++n) slab(p, sm, x, n, ns, ka, qa, txb, accQ, accK, ac);
+      for (int si = 0; si < nsl; ++si, ++n) slab(p, sm, x, n, ns, slot, ka, qa, txb, accQ, accK, ac);
 
       // ---- per-row sums of head h; its L x L weights (added to the group
       // sums) and rectangle terms of dl, in the lane's accumulator layout
@@ -1039,8 +1028,10 @@ struct ChunkBwdGrad {
         if (q.l == 0) sm.red[q.w] = phdh;
 
         const int tc0 = q.tc0;
-        const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[tc0]);
-        const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[tc0]);
+        const float* gam = sm.bsc[slot][0];
+        const float* bet = sm.bsc[slot][3];
+        const float4 g4 = *reinterpret_cast<const float4*>(&gam[tc0]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&bet[tc0]);
         const float4 q4 = *reinterpret_cast<const float4*>(&sm.rq[tc0]);
         const float4 k4 = *reinterpret_cast<const float4*>(&sm.rk[tc0]);
         const float ga[4] = {g4.x, g4.y, g4.z, g4.w}, ba[4] = {b4.x, b4.y, b4.z, b4.w};
@@ -1049,7 +1040,7 @@ struct ChunkBwdGrad {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int b = 16 * (2 * q.hw + u) + q.lr;
-          const float gb = sm.gam[b], bb = sm.beta[b], rkb = sm.rk[b];
+          const float gb = gam[b], bb = bet[b], rkb = sm.rk[b];
           float colp = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -1084,13 +1075,13 @@ struct ChunkBwdGrad {
         if (q.tid < L) {
           const int s = q.tid;
           const bool in = s < Lc;
-          const float av = in ? sm.el[s] * sm.beta[s] * sm.rk[s] * (sm.pa[0][s] + sm.pa[1][s]) : 0.f;
+          const float beta = sm.bsc[slot][3][s];
+          const float av = in ? sm.bsc[slot][2][s] * beta * sm.rk[s] * (sm.pa[0][s] + sm.pa[1][s]) : 0.f;
           const float csum = (sm.colp[0][s] + sm.colp[1][s]) + (sm.colp[2][s] + sm.colp[3][s]);
           sm.hu[slot][s] = av + (csum - (sm.rowp[0][s] + sm.rowp[1][s]));
           sm.hb[slot][s] = in ? sm.bv[0][s] + sm.bv[1][s] : 0.f;
-          const float beta = sm.beta[s];
           sm.hdb[slot][s] = (sm.pdb[0][s] + sm.pdb[1][s]) * (1.f - beta);
-          sm.hell[slot][s] = sm.ell[s];
+          sm.hell[slot][s] = sm.bsc[slot][4][s];
         }
         if (q.tid == 64) {
           float hdh = 0.f;
