@@ -577,13 +577,16 @@ struct ChunkBwdGrad {
     bf16 wq[L * TS];    // sum over the group of Wq diag(rk)   [t][s]
     bf16 wk[L * WS];    // sum over the group of [Wk1 diag(rq) | Wk2 diag(rk)]   [t][r]
   };
-  struct Fin {
-    float acc[L * FS];
-  };
   static constexpr int KQS = DK + 8;  // bf16 row stride of the k / q row tiles
   struct KQ {
     bf16 k[L * KQS];  // the chunk's k rows   [t][i]
     bf16 q[L * KQS];  // the chunk's q rows   [t][i]
+  };
+  // dQn and dKn go through LDS for the L2-norm backward together where both
+  // fit in the space of the ring (else one after the other)
+  static constexpr int NFIN = 2 * L * FS * 4 <= (sizeof(Ring) > sizeof(KQ) ? sizeof(Ring) : sizeof(KQ)) ? 2 : 1;
+  struct Fin {
+    float acc[NFIN][L * FS];
   };
   union Big {
     Ring r;
@@ -1207,44 +1210,51 @@ struct ChunkBwdGrad {
       }
     }
 
-    // ---- L2-normalisation backward: dq = rq (dQn - Dk qn (qn . dQn)), dk = rk (dKn - kn (kn . dKn))
+    // ---- L2-normalisation backward: dq = rq (dQn - Dk qn (qn . dQn)), dk = rk (dKn - kn (kn . dKn)).
+    // dQn and dKn go to LDS (together, or one after the other), then each
+    // thread takes 1/8 of a row: dot product with the row, and the output.
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int p0 = 0; p0 < 2; p0 += NFIN) {
       const Lanes q;
       lds_barrier();
 #pragma unroll
-      for (int k = 0; k < IH; ++k)
+      for (int f = 0; f < NFIN; ++f)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          sm.u.f.acc[(q.tc0 + r) * FS + 16 * (q.hw * IH + k) + q.lr] = pass == 0 ? accQ[k][r] : accK[k][r];
+        for (int k = 0; k < IH; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sm.u.f.acc[f][(q.tc0 + r) * FS + 16 * (q.hw * IH + k) + q.lr] = p0 + f == 0 ? accQ[k][r] : accK[k][r];
       lds_barrier();
       const int t = q.tid >> 3, qd = q.tid & 7;
-      const uint4* xr = pass == 0 ? qrow : krow;
-      const float* ac = &sm.u.f.acc[t * FS + qd * QW];
-      float dot = 0.f;
 #pragma unroll
-      for (int u = 0; u < QW; u += 8) {
-        float xv[8];
-        Vec16<bf16>::unpack(xr[u / 8], xv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(xv[e], ac[u + e], dot);
-      }
-      dot = oct_sum(dot);
-      if (t < Lc) {
-        const float r1 = pass == 0 ? sm.rq[t] : sm.rk[t];
-        const float coef = (pass == 0 ? static_cast<float>(DK) : 1.f) * r1 * r1 * dot;
-        bf16* dst = static_cast<bf16*>(pass == 0 ? p.dq : p.dk) + (qk0 + static_cast<size_t>(t) * d.Hk) * DK + qd * QW;
+      for (int f = 0; f < NFIN; ++f) {
+        const int pass = p0 + f;
+        const uint4* xr = pass == 0 ? qrow : krow;
+        const float* ac = &sm.u.f.acc[f][t * FS + qd * QW];
+        float dot = 0.f;
 #pragma unroll
         for (int u = 0; u < QW; u += 8) {
-          float xv[8], y[8];
+          float xv[8];
           Vec16<bf16>::unpack(xr[u / 8], xv);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = r1 * (ac[u + e] - coef * xv[e]);
-          *reinterpret_cast<uint4*>(dst + u) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
-                                                          pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
+          for (int e = 0; e < 8; ++e) dot = fmaf(xv[e], ac[u + e], dot);
         }
-      }
-    }
+        dot = oct_sum(dot);
+        if (t < Lc) {
+          const float r1 = pass == 0 ? sm.rq[t] : sm.rk[t];
+          const float coef = (pass == 0 ? static_cast<float>(DK) : 1.f) * r1 * r1 * dot;
+          bf16* dst = static_cast<bf16*>(pass == 0 ? p.dq : p.dk) + (qk0 + static_cast<size_t>(t) * d.Hk) * DK + qd * QW;
+#pragma unroll
+          for (int u = 0; u < QW; u += 8) {
+            float xv[8], y[8];
+            Vec16<bf16>::unpack(xr[u / 8], xv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = r1 * (ac[u + e] - coef * xv[e]);
+            *reinterpret_cast<uint4*>(dst + u) = make_uint4(pack2_bf16(y[0], y[1]), pack2_bf16(y[2], y[3]),
+                                                            pack2_bf16(y[4], y[5]), pack2_bf16(y[6], y[7]));
+          }
+        }
+      }    }
   }
 };
 
