@@ -246,8 +246,8 @@ gdn::StepScalars scalars(void* ws, const Layout& L) {
 
 struct VgLayout {
   size_t rq, rk, kq, beta, sub, part, pdb;
-  size_t Kb, Kh, Qb, KbT, QbT, Tx, Mq, AtT, PqT, vsc;  // chunk form
-  size_t E, dHend, X, dPA;                             // chunk form, backward
+  size_t Kb, Kh, Qb, KbT, QbT, Tx, Mq, PqT, vsc;  // chunk form
+  size_t dHend, X, dPA;                           // chunk form, backward
   size_t total;
 };
 
@@ -280,7 +280,7 @@ bool use_vg_chunk(const gdn_dims* p) {
 // backward reads and X of every step, all written by the forward (offsets in
 // fp32 elements, 256-byte aligned).  It holds no fp32 states.
 struct VgSaved {
-  size_t HB, Kb, Kh, KbT, QbT, Tx, AtT, PqT, vsc, X, total;
+  size_t HB, Kb, Kh, KbT, QbT, Tx, PqT, vsc, X, total;
 };
 
 VgSaved vg_saved_layout(const Dims& d) {
@@ -299,7 +299,6 @@ VgSaved vg_saved_layout(const Dims& d) {
   S.KbT = take(rows);
   S.QbT = take(rows);
   S.Tx = take(mats);
-  S.AtT = take(mats);
   S.PqT = take(mats);
   S.vsc = take(bhc * gdn::VSC_ROWS * 64);
   S.X = take((static_cast<size_t>(d.B) * d.T * d.Hv * d.Dv + 1) / 2);
@@ -336,7 +335,6 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk, bool saved) {
     if (!saved) {
       L.KbT = take(rows);
       L.QbT = take(rows);
-      L.AtT = take(mats);
       L.PqT = take(mats);
       L.X = take((bt * d.Hv * d.Dv + 1) / 2);
     }
@@ -346,9 +344,8 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk, bool saved) {
   L.rk = take(bt * d.Hk);
   L.kq = take(bt * d.Hk);
   L.beta = take(bt * d.Hv);
-  if (bwd && chunk) {  // eps, dH', and the value heads' parts of the row gradients
+  if (bwd && chunk) {  // dH', and the value heads' parts of the row gradients
     const size_t nc = d.nchunk();
-    L.E = take((bt * d.Hv * d.Dv + 1) / 2);
     L.dHend = take((nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv + 1) / 2);
     L.part = take(bt * d.Hv * 2 * d.Dk);
   } else if (bwd) {
@@ -382,7 +379,6 @@ gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd, const Dims& 
     cb.KbT = reinterpret_cast<gdn::bf16*>(rec + S.KbT);
     cb.QbT = reinterpret_cast<gdn::bf16*>(rec + S.QbT);
     cb.Tx = reinterpret_cast<gdn::bf16*>(rec + S.Tx);
-    cb.AtT = reinterpret_cast<gdn::bf16*>(rec + S.AtT);
     cb.PqT = reinterpret_cast<gdn::bf16*>(rec + S.PqT);
     cb.vsc = rec + S.vsc;
     cb.X = reinterpret_cast<gdn::bf16*>(rec + S.X);
@@ -394,7 +390,6 @@ gdn::ChunkBufs vg_chunk_bufs(void* ws, const VgLayout& L, bool bwd, const Dims& 
     if (bwd) {
       cb.KbT = at<gdn::bf16>(ws, L.KbT);
       cb.QbT = at<gdn::bf16>(ws, L.QbT);
-      cb.AtT = at<gdn::bf16>(ws, L.AtT);
       cb.PqT = at<gdn::bf16>(ws, L.PqT);
     }
   }
@@ -655,7 +650,7 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
       if (!launch(st, [&] { return gdn::launch_state_bf16(sa, st); })) return GDN_ERR_HIP;
     }
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
-                         nullptr, at<gdn::bf16>(ws, L.dHend),
+                         at<gdn::bf16>(ws, L.dHend),
                          dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
     if (tseg) {  // T-parallel reverse pass: segment maps, their chain (last to first), then the segments
       const int nseg = gdn::tpar_nseg(dd, tseg);
@@ -806,13 +801,12 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
       gdn::VgChunkPrepArgs ca{dd, q, k, b, lg, mask, cb, 1};
       if (!launch(st, [&] { return gdn::launch_vg_chunk_prep(ca, st); })) return GDN_ERR_HIP;
     }
-    gdn::bf16* E = at<gdn::bf16>(ws, L.E);
     gdn::bf16* dHend = at<gdn::bf16>(ws, L.dHend);
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, nullptr, nullptr, nullptr, mask, state0, ckpt, dS_final, cb,
-                         E, dHend, dq, dk, dv, nullptr, db, dstate, nullptr, nullptr};
+                         dHend, dq, dk, dv, nullptr, db, dstate, nullptr, nullptr};
     ba.vg = 1;
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
-    gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, s, cb, E, dHend, dv,
+    gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, s, cb, dHend, dv,
                             saved ? cb.X : at<gdn::bf16>(ws, L.X), at<gdn::bf16>(ws, L.dPA),
                             at<float>(ws, L.part), dq, dk, db, dlg, saved ? 1 : 0};
     if (!launch(st, [&] { return gdn::launch_vg_chunk_x(ga, st); })) return GDN_ERR_HIP;

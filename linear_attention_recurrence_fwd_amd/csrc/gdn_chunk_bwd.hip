@@ -36,8 +36,7 @@
 //                    Dv), walking the chunks from last to first with dH in MFMA
 //                    accumulators (fp32) and the next chunk's operands
 //                    prefetched.  Writes dv, dH' of every chunk (bf16,
-//                    transposed) and dstate; eps (bf16) only for the
-//                    per-key-channel gate, whose gradient kernels read it.
+//                    transposed) and dstate.
 //   chunk_bwd_grad   one workgroup per (chunk, batch, key head), looping over
 //                    the group's value heads and 32-column slabs of Dv, with H
 //                    read from the bf16 copies of the chunk-start states and
@@ -65,9 +64,8 @@ struct ChunkBwdState {
   // Eight waves in two groups of four (w = wave index within the group):
   //   A (waves 0-3): for row tile w of the chunk, the dependent chain
   //                  rhs = diag(e^{gL-g} rk) K dH' + P^T dO, Ehat = Tx^T diag(beta) rhs
-  //                  (= dv), and for the per-key-channel gate eps = rhs - A^T
-  //                  Ehat.  A also streams the chunk's k rows, P^T, Tx^T (A^T
-  //                  for that gate), dO slice and chunk scalars into a
+  //                  (= dv).  A also streams the chunk's k rows, P^T, Tx^T,
+  //                  dO slice and chunk scalars into a
   //                  2-slot LDS ring with direct-to-LDS loads, one chunk ahead.
   //   B (waves 4-7): dH for its RTW row tiles, in MFMA accumulators: stores dH'
   //                  of the chunk, adds e^{gL} dH' + Q^T diag(e^g rq) dO while A
@@ -86,7 +84,7 @@ struct ChunkBwdState {
   static constexpr int XS = L + 8;     // bf16 row stride of the [v][t] tiles
   static constexpr int NPK = DK / 8;   // 16-byte pieces of a k row
   static constexpr int KDMA = DK / 32;
-  static constexpr int NDMA = KDMA + (VG ? 6 : 4) + 1 + 2;  // ring loads per group-A wave per chunk
+  static constexpr int NDMA = KDMA + 4 + 1 + 2;  // ring loads per group-A wave per chunk
   static constexpr int SCR = VG ? VSC_ROWS : SC_ROWS;  // chunk scalar rows per chunk
   static_assert(!VG || DK <= 4 * L, "e^{G_L} of every channel in rows 1 .. 4 of the slot");
   // A ring slot (layouts as in the forward state pass: 16-byte piece p of row
@@ -95,7 +93,6 @@ struct ChunkBwdState {
     bf16 k[L * DK];    // k rows, swizzle t & 7
     bf16 pt[L * L];    // P^T rows, swizzle t & 7
     bf16 tx[L * L];    // Tx rows, swizzle t & 7 (Tx^T operands by transposing reads)
-    bf16 at[L * L];    // A^T rows, swizzle t & 7
     bf16 dO[L * NV];   // dO rows of this slice's columns, swizzle t & 3
     float sc[8 * L];   // chunk scalar rows 0 .. 7
   };
@@ -120,7 +117,7 @@ struct ChunkBwdState {
     uint32_t ostep, obase;       // dO elements per step and offset (0, 0: the zero rows)
     uint32_t v_row;
     rsrc_t rqt, rkt;
-    i32x4 dk, dpt, dtx, dat, ddo, dsc;  // raw descriptors of the ring's operands
+    i32x4 dk, dpt, dtx, ddo, dsc;  // raw descriptors of the ring's operands
   };
 
   __device__ static __forceinline__ int kpos(int t, int p) { return 8 * (t * NPK + (p ^ (t & 7))); }
@@ -146,7 +143,6 @@ struct ChunkBwdState {
       const uint32_t o = 2 * (mat + t * L + 8 * pc);
       dma16(q.dpt, &s.pt[512 * n], o);
       dma16(q.dtx, &s.tx[512 * n], o);
-      if constexpr (VG) dma16(q.dat, &s.at[512 * n], o);
     }
     {
       const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
@@ -216,7 +212,7 @@ struct ChunkBwdState {
     const int t0 = c * L, Lc = min(L, d.T - t0);
     const Slot& s = sm.ring[c & 1];
     const int lr = q.lr, lg = q.lg, ta = q.ta;
-    bf16x8 ka[DK / 32], pqa[2], txa[2], ata[2];
+    bf16x8 ka[DK / 32], pqa[2], txa[2];
 #pragma unroll
     for (int kt = 0; kt < DK / 32; ++kt) ka[kt] = load_bf16x8(&s.k[kpos(ta, 4 * kt + lg)]);
 #pragma unroll
@@ -228,7 +224,6 @@ struct ChunkBwdState {
       const uint2 lo = lds_read_tr16(&s.tx[xpos(sr, pc) + 4 * (lr & 1)]);
       const uint2 hi = lds_read_tr16(&s.tx[xpos(sr + 4, pc) + 4 * (lr & 1)]);
       txa[kt] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      if constexpr (VG) ata[kt] = load_bf16x8(&s.at[xpos(ta, 4 * kt + lg)]);
     }
     const float4 one4 = make_float4(1.f, 1.f, 1.f, 1.f);
     const float4 kl4 = VG ? one4 : *reinterpret_cast<const float4*>(&s.sc[SC_KL * L + q.tc0]);
@@ -274,22 +269,9 @@ struct ChunkBwdState {
     }
     lds_barrier();  // Z: Ehat complete
     store_rows(p, q, p.dv, t0, Lc, eh, 1.f);
-    if constexpr (VG) {
-      // eps = rhs - A^T Ehat, which the per-key-channel gate's gradient
-      // kernels read (the scalar gate's gradient pass reads dv = diag(beta) eps)
-      f32x4 ng[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ng[ct][r] = -rhs[ct][r];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          ng[ct] = mfma16(ata[kt], load_bf16x8(&sm.eb[(16 * ct + lr) * XS + 32 * kt + 8 * lg]), ng[ct]);
-      store_rows(p, q, p.E, t0, Lc, ng, -1.f);
-    }
-    wait_vm<VG ? 4 : 2>();  // the ring loads (the later stores may stay pending)
+    // eps = rhs - A^T Ehat is not formed: the gradient kernels take every eps
+    // term times beta, i.e. read dv = diag(beta) eps
+    wait_vm<2>();  // the ring loads (the 2 later stores may stay pending)
     lds_barrier();  // X: dH of the next chunk complete; slot c - 1 complete
   }
 
@@ -491,7 +473,6 @@ struct ChunkBwdState {
       q.ddo = q.mode == 1 ? raw_desc(p.vzero, 64) : raw_desc(p.dO, bt * d.Hv * d.Dv * 2);
       q.dpt = raw_desc(p.cb.PqT, nmat * L * L * 2);
       q.dtx = raw_desc(p.cb.Tx, nmat * L * L * 2);
-      if constexpr (VG) q.dat = raw_desc(p.cb.AtT, nmat * L * L * 2);
       if constexpr (VG) {
         q.dsc = raw_desc(p.cb.vsc, nmat * VSC_ROWS * L * 4);
         q.rqt = make_rsrc(p.cb.QbT, nmat * DK * L * 2);

@@ -111,7 +111,6 @@ struct ChunkBufs {
   bf16* Tx;   // [B*Hv, NC, L, L] (I + N)^-1, N[t,s] = [s<t] e^{g_t-g_s} rk_t rk_s beta_s (k_t.k_s)
   bf16* Mq;   // [B*Hv, NC, L, L] [s<=t] e^{g_t-g_s} rq_t rk_s beta_s (q_t.k_s)
   // backward only
-  bf16* AtT;  // [B*Hv, NC, L, L] transpose of [s<t] e^{g_t-g_s} rk_t rk_s (k_t.k_s) (per-key-channel gate only)
   bf16* PqT;  // [B*Hv, NC, L, L] transpose of [s<=t] e^{g_t-g_s} rq_t rk_s (q_t.k_s)
   bf16* QT;   // [B*Hk, NC, Dk, L] raw q of the chunk, transposed
   // per-step chunk scalars, fp32 [B*Hv, NC, SC_ROWS, L]
@@ -180,10 +179,10 @@ struct ChunkPrepArgs {
   const uint8_t* mask;
   ChunkBufs cb;
   int bwd;  // 0: the forward's buffers (Tx, Mq, sc); 1: the backward's (Tx, sc,
-            // A^T, P^T, Q^T); 2: both
+            // P^T, Q^T); 2: both
 };
 
-// Chunk matrices of the per-key-channel gate: Tx, Mq / A^T, P^T (as
+// Chunk matrices of the per-key-channel gate: Tx, Mq / P^T (as
 // ChunkBufs, with the decay e^{G_t - G_s} taken per channel inside the
 // products) and the pre-scaled rows Kb, Kh, Qb / KbT, QbT and vsc.
 struct VgChunkPrepArgs {
@@ -192,7 +191,7 @@ struct VgChunkPrepArgs {
   const float* lg;
   const uint8_t* mask;
   ChunkBufs cb;
-  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, A^T, P^T, Kb, Kh, KbT, QbT, vsc; 2: all of them
+  int bwd;  // 0: Tx, Mq, Kb, Kh, Qb, vsc; 1: Tx, P^T, Kb, Kh, KbT, QbT, vsc; 2: all of them
 };
 // Gradient pass of the per-key-channel gate's chunk form, in three kernels:
 // vg_chunk_x (one workgroup per (chunk, batch, value head)) recomputes X from
@@ -209,7 +208,6 @@ struct VgChunkGradArgs {
   const float *state0, *ckpt;  // state0 may be null
   StepScalars s;               // rk, rq
   ChunkBufs cb;                // Tx, Kb, vsc
-  const bf16* E;               // [B,T,Hv,Dv] eps (dL/d delta)
   const bf16* dHend;           // [NC, B*Hv, Dk, Dv] dL/d(state at the end of chunk c)
   const void* dv;              // [B,T,Hv,Dv] dv (= Ehat) from the reverse state pass
   bf16* X;                     // [B,T,Hv,Dv] X_t = v_t - u_t of every step
@@ -271,7 +269,6 @@ struct ChunkBwdArgs {
   const uint8_t* mask;
   const float *state0, *ckpt, *dS_final;  // state0 / dS_final may be null
   ChunkBufs cb;
-  bf16* E;        // [B,T,Hv,Dv]  eps, rows t < T (per-key-channel gate only; null otherwise)
   bf16* dHend;    // [NC, B*Hv, Dk, Dv]  dL/d(state at the end of chunk c)
   void *dq, *dk, *dv, *da, *db;
   float* dstate;     // [B,Hv,Dk,Dv]

@@ -37,9 +37,10 @@
 //                  forward's saved copy, or recomputed from the fp32
 //                  checkpoint), then
 //     dP = lower(dO X^T) diag(beta),  dA = -strictlower(Ehat X^T) diag(beta),
-//     db_t = (eps_t . X_t) beta_t (1 - beta_t),
-//                  with Ehat (= dv) and eps (= dL/d delta) of the reverse
-//                  state pass.
+//     db_t = (Ehat_t . X_t) (1 - beta_t),
+//                  with Ehat = dv of the reverse state pass (dL/d beta_t =
+//                  eps_t . X_t with eps = dL/d delta, and Ehat = diag(beta)
+//                  eps, so eps itself is not needed).
 //   vg_chunk_grad  one workgroup per (chunk, batch, value head, 32 channels):
 //     dQb = dO H^T,  dKb = -Ehat H^T,  dKh = diag(beta) X dH'^T
 //                  (dH' = dL/d the state at the chunk end), then, per channel
@@ -480,7 +481,6 @@ struct VgPrep {
       const float bs = sm.beta[s];
       nf[t * SP + s] = av * bs;
       if (bwd) {
-        st[s * SP + t] = av;
         st2[s * SP + t] = pv;
       } else {
         st[t * SP + s] = pv * bs;
@@ -492,7 +492,6 @@ struct VgPrep {
       const int t = 16 * bi + ((e >> 4) & 15), s = 16 * bj + (e & 15);
       nf[t * SP + s] = 0.f;
       if (bwd) {
-        st[s * SP + t] = 0.f;
         st2[s * SP + t] = 0.f;
       } else {
         st[t * SP + s] = 0.f;
@@ -504,7 +503,6 @@ struct VgPrep {
     tri::invert_diagonal_block(nf, w, l);
     const size_t mat = cidx * L * L;
     if (bwd) {
-      tri::store_mat(st, p.cb.AtT + mat, tid, NT);
       tri::store_mat(st2, p.cb.PqT + mat, tid, NT);
       if (fwd) {  // Mq[t][s] = P^T[s][t] beta_s: row t, columns s8 .. s8 + 7 per thread
         for (int u = tid; u < L * L / 8; u += NT) {
@@ -539,7 +537,7 @@ __global__ void __launch_bounds__(NT) vg_chunk_prep_kernel(VgChunkPrepArgs p) {
 
 // vg_chunk_x: X = Tx (V - Kb H) from the fp32 checkpoint H (XSV: X read
 // from the forward's saved copy instead), then dP = lower(dO X^T) diag(beta),
-// dA = -strictlower(Ehat X^T) diag(beta) and db_t = (eps_t . X_t) beta_t (1 -
+// dA = -strictlower(Ehat X^T) diag(beta) and db_t = (Ehat_t . X_t) (1 -
 // beta_t).  Writes dP, dA, db (bf16) and, when it computes X, X ([B,T,Hv,Dv]
 // bf16, the layout the forward saves it in).  Wave w takes steps 16 w .. 16 w
 // + 15.
@@ -703,9 +701,9 @@ struct VgX {
           dAs[t * TS + s] = bf16_of(s < t ? -g2[st][r] * bs : 0.f);
         }
     }
-    {  // db_t = (eps_t . X_t) beta_t (1 - beta_t), four lanes per step (0 on masked steps: beta 0)
+    {  // db_t = (dv_t . X_t) (1 - beta_t), four lanes per step (0 on masked steps: dv 0)
       const int t = tid >> 2, part = tid & 3;
-      const bf16* eg = p.E + (vrow0 + static_cast<size_t>(min(t, tl)) * d.Hv) * DV;
+      const bf16* eg = static_cast<const bf16*>(p.dv) + (vrow0 + static_cast<size_t>(min(t, tl)) * d.Hv) * DV;
       float sdot = 0.f;
 #pragma unroll
       for (int e = 0; e < DV / 32; ++e) {
@@ -718,7 +716,7 @@ struct VgX {
       }
       sdot = quad_sum(sdot);
       const float bt = sm.beta[t];
-      if (part == 0 && t < Lc) static_cast<bf16*>(p.db)[vrow0 + static_cast<size_t>(t) * d.Hv] = bf16_of(sdot * bt * (1.f - bt));
+      if (part == 0 && t < Lc) static_cast<bf16*>(p.db)[vrow0 + static_cast<size_t>(t) * d.Hv] = bf16_of(sdot * (1.f - bt));
     }
     if constexpr (!XSV) {  // rows of the sequence only
       for (int u = tid; u < L * DV / 8; u += NT) {

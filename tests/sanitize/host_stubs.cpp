@@ -40,7 +40,6 @@ void touch_ckpt(const gdn::Dims& d, const float* ckpt) {
 void touch_chunk(const gdn::Dims& d, const gdn::ChunkBufs& cb) {
   touch(cb.Tx, nmat(d) * 64 * 64 * 2);
   touch(cb.Mq, nmat(d) * 64 * 64 * 2);
-  touch(cb.AtT, nmat(d) * 64 * 64 * 2);
   touch(cb.PqT, nmat(d) * 64 * 64 * 2);
   touch(cb.QT, kts(d) * 2);
   touch(cb.sc, nmat(d) * gdn::SC_ROWS * 64 * 4);
@@ -124,7 +123,6 @@ hipError_t launch_vg_chunk_prep(const VgChunkPrepArgs& a, hipStream_t) {
 }
 void touch_vg_grad(const VgChunkGradArgs& a) {
   touch_chunk(a.d, a.cb);
-  touch(a.E, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dHend, slots(a.d) * 2);
   if (a.cb.Hb == nullptr) touch_ckpt(a.d, a.ckpt);  // else the bf16 states of the saved record (touch_chunk)
   touch(a.X, bt(a.d) * a.d.Hv * a.d.Dv * 2);
@@ -170,7 +168,6 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t) {
 }
 hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t) {
   touch_chunk(a.d, a.cb);
-  touch(a.E, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dHend, slots(a.d) * 2);
   if (a.seg) {
     if (a.map) touch(a.maps, map_floats(a.d, a.seg) * 4);
@@ -182,7 +179,6 @@ hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t) {
 }
 hipError_t launch_chunk_bwd_grad(const ChunkBwdArgs& a, hipStream_t) {
   touch_chunk(a.d, a.cb);
-  touch(a.E, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dHend, slots(a.d) * 2);
   touch(a.part_dA, nmat(a.d) * 8);
   touch(a.part_ddt, nmat(a.d) * 8);

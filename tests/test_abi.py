@@ -225,7 +225,7 @@ def test_vg_saved_record_sizes():
     """gdn_vg_ckpt_elems: the fp32 states without save (and on the scan family,
     which ignores save); with save on the chunk form, the record: the bf16
     state at every chunk start, then per (chunk, head) four bf16 row blocks of
-    64 x Dk, three 64 x 64 bf16 matrices and the chunk scalars, and X of every
+    64 x Dk, two 64 x 64 bf16 matrices (Tx, P^T) and the chunk scalars, and X of every
     step (each region 256-byte aligned).  The saved workspaces are smaller than the unsaved
     ones by what moved into the record, and a NULL ckpt is refused."""
     lib = B.lib()
@@ -241,7 +241,7 @@ def test_vg_saved_record_sizes():
     d = B.make_dims(Bn, T, Hk, Hv, Dk, Dv, B.GDN_BF16, B.ALGO_CHUNK, 1)
     assert lib.gdn_vg_ckpt_elems(ctypes.byref(d), ctypes.byref(out)) == 0
     bhc = Bn * Hv * nc
-    pieces = [bhc * Dk * Dv // 2] + [bhc * 64 * Dk // 2] * 4 + [bhc * 64 * 64 // 2] * 3 + [bhc * 8 * 64, Bn * T * Hv * Dv // 2]
+    pieces = [bhc * Dk * Dv // 2] + [bhc * 64 * Dk // 2] * 4 + [bhc * 64 * 64 // 2] * 2 + [bhc * 8 * 64, Bn * T * Hv * Dv // 2]
     assert out.value == sum((p * 4 + 255) // 256 * 64 for p in pieces)
     assert lib.gdn_vg_ckpt_bytes(ctypes.byref(d), ctypes.byref(out)) == 0
     assert out.value == sum((p * 4 + 255) // 256 * 256 for p in pieces)
