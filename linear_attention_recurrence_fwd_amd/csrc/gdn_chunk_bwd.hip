@@ -569,6 +569,9 @@ struct ChunkBwdGrad {
   struct Fin {
     float acc[NFIN][L * FS];
   };
+  // The start stages the chunk's k rows in the weight tiles' space and its q
+  // rows in ring slot 2 where both fit (else each wave loads its rows itself).
+  static constexpr bool KQL = NSLOT == 3 && L * KQS * 2 <= sizeof(Wts) && L * KQS * 2 <= sizeof(Slot);
   union Big {
     Ring r;
     KQ kq;
@@ -903,37 +906,6 @@ struct ChunkBwdGrad {
     // workgroup (loading them inside the slab loop would make each wait for
     // them also wait for the next slab's prefetch, issued before them)
     bf16x8 ka[KS], qa[KS];
-    // and the k rows of the column tiles 2 hw, 2 hw + 1 of this wave's L x L
-    // terms (the B operands of its Gram tiles)
-    bf16x8 kb[2][KS];
-    {  // quad-coalesced (lane m reads piece m % 4 of row m / 4: four lanes cover
-       // 64 contiguous bytes); moved to the operand layout below, once the
-       // first slabs' loads are issued
-      const int l = tid0 & 63, tr0 = 16 * ((tid0 >> 6) & 3) + coal_row(l);
-      const uint32_t o = static_cast<uint32_t>(min(tr0, x.tl)) * qk_row + 8 * coal_piece(l);
-#pragma unroll
-      for (int kt = 0; kt < KS; ++kt) {
-        ka[kt] = load_bf16x8(kc + o + 32 * kt);
-        qa[kt] = load_bf16x8(qc + o + 32 * kt);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tb = 16 * (2 * (tid0 >> 8) + u) + coal_row(l);
-        const uint32_t ob = static_cast<uint32_t>(min(tb, x.tl)) * qk_row + 8 * coal_piece(l);
-#pragma unroll
-        for (int kt = 0; kt < KS; ++kt) kb[u][kt] = load_bf16x8(kc + ob + 32 * kt);
-      }
-    }
-
-    const int ns = G * (d.Dv / NS);  // slabs of the workgroup
-#pragma unroll
-    for (int n = 0; n < PD; ++n)
-      if (n < ns) issue_slab(p, sm, x, n);
-#pragma unroll
-    for (int kt = 0; kt < KS; ++kt) {
-      ka[kt] = to_mfma_layout(ka[kt]);
-      qa[kt] = to_mfma_layout(qa[kt]);
-    }
     // The raw Grams of the chunk in the accumulator layout of the L x L terms:
     // lane register r of [u] holds element (a, b), a = tc0 + r, b = 16 (2 hw +
     // u) + lr, of kk = K K^T and qk = Q K^T (the products chunk_prep forms
@@ -941,14 +913,90 @@ struct ChunkBwdGrad {
     // is formed in registers: A[b][a] = e^{-|g_a - g_b|} rk_a rk_b kk, P[a][b]
     // = e^{g_a - g_b} rq_a rk_b qk (b <= a).
     f32x4 kk[2], qk[2];
+    const int ns = G * (d.Dv / NS);  // slabs of the workgroup
+    if constexpr (KQL) {
+      // The chunk's k and q rows, each loaded once with coalesced 16-byte
+      // loads into LDS that nothing uses before the first slab (k rows in the
+      // space of the weight tiles, q rows in ring slot 2); every wave reads
+      // its operands (k and q rows of its row tile, k rows of its two Gram
+      // column tiles) from there in the matrix-core layout.
+      constexpr int NP = L * DK / 8, NPT = NP / NTG;
+      static_assert(NP % NTG == 0, "whole pieces per thread");
+      bf16* ks = reinterpret_cast<bf16*>(&sm.wt);
+      bf16* qs = reinterpret_cast<bf16*>(&sm.u.r.s[2]);
+      uint4 kv[NPT], qv[NPT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      kk[u] = qk[u] = f4zero();
+      for (int u = 0; u < NPT; ++u) {
+        const int pc = tid0 + u * NTG, row = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
+        const uint32_t o = static_cast<uint32_t>(min(row, x.tl)) * qk_row + c8;
+        kv[u] = *reinterpret_cast<const uint4*>(kc + o);
+        qv[u] = *reinterpret_cast<const uint4*>(qc + o);
+      }
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int pc = tid0 + u * NTG, row = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
+        *reinterpret_cast<uint4*>(&ks[row * KQS + c8]) = kv[u];
+        *reinterpret_cast<uint4*>(&qs[row * KQS + c8]) = qv[u];
+      }
+#pragma unroll
+      for (int n = 0; n < PD; ++n)
+        if (n < ns) issue_slab(p, sm, x, n);
+      __syncthreads();
+      const Lanes q;
 #pragma unroll
       for (int kt = 0; kt < KS; ++kt) {
-        const bf16x8 bk = to_mfma_layout(kb[u][kt]);
-        kk[u] = mfma16(ka[kt], bk, kk[u]);
-        qk[u] = mfma16(qa[kt], bk, qk[u]);
+        ka[kt] = load_bf16x8(&ks[q.ta * KQS + 32 * kt + 8 * q.lg]);
+        qa[kt] = load_bf16x8(&qs[q.ta * KQS + 32 * kt + 8 * q.lg]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        kk[u] = qk[u] = f4zero();
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+          const bf16x8 bk = load_bf16x8(&ks[(16 * (2 * q.hw + u) + q.lr) * KQS + 32 * kt + 8 * q.lg]);
+          kk[u] = mfma16(ka[kt], bk, kk[u]);
+          qk[u] = mfma16(qa[kt], bk, qk[u]);
+        }
+      }
+    } else {
+      // the k rows of the column tiles 2 hw, 2 hw + 1 of this wave's L x L
+      // terms (the B operands of its Gram tiles)
+      bf16x8 kb[2][KS];
+      {  // quad-coalesced (lane m reads piece m % 4 of row m / 4: four lanes cover
+         // 64 contiguous bytes); moved to the operand layout below, once the
+         // first slabs' loads are issued
+        const int l = tid0 & 63, tr0 = 16 * ((tid0 >> 6) & 3) + coal_row(l);
+        const uint32_t o = static_cast<uint32_t>(min(tr0, x.tl)) * qk_row + 8 * coal_piece(l);
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+          ka[kt] = load_bf16x8(kc + o + 32 * kt);
+          qa[kt] = load_bf16x8(qc + o + 32 * kt);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int tb = 16 * (2 * (tid0 >> 8) + u) + coal_row(l);
+          const uint32_t ob = static_cast<uint32_t>(min(tb, x.tl)) * qk_row + 8 * coal_piece(l);
+#pragma unroll
+          for (int kt = 0; kt < KS; ++kt) kb[u][kt] = load_bf16x8(kc + ob + 32 * kt);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < PD; ++n)
+        if (n < ns) issue_slab(p, sm, x, n);
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        ka[kt] = to_mfma_layout(ka[kt]);
+        qa[kt] = to_mfma_layout(qa[kt]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        kk[u] = qk[u] = f4zero();
+#pragma unroll
+        for (int kt = 0; kt < KS; ++kt) {
+          const bf16x8 bk = to_mfma_layout(kb[u][kt]);
+          kk[u] = mfma16(ka[kt], bk, kk[u]);
+          qk[u] = mfma16(qa[kt], bk, qk[u]);
+        }
       }
     }
     // the group sums of the L x L weights, same layout: Wq diag(rk), V1 (=
