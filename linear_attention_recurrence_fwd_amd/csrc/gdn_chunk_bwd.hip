@@ -583,16 +583,18 @@ struct ChunkBwdGrad {
     alignas(16) Wts wt;  // bf16 group sums of the L x L weights, for the final products
     alignas(16) float rk[L];
     alignas(16) float rq[L];
-    float bv[2][L], pa[2][L], pdb[2][L];
-    float rowp[2][L], colp[4][L];  // row sums (per half of the columns) and column sums (per row tile) of E
-    float red[NTG / 64];
-    // per value head of a batch (slot = head % HB): the per-step gamma, e^g,
-    // e^{gL-g}, beta and l, loaded when the batch starts; for the deferred
-    // section the prefix-summed and suffix-summed terms of dl, the db factor,
-    // l, and the scalars <dH', H>, e^{gamma_L}, A_log and dt_bias; a (fp32)
-    // and the mask (1 = valid step)
+    // per value head of a batch (slot = head % HB): the partial sums of its
+    // gate-gradient terms -- b_r and a_s per half of the columns, the db
+    // factor, the row sums (per half of the columns) and column sums (per row
+    // tile) of E, <dH', H> per wave -- combined in the batch's deferred section
+    float bv[HB][2][L], pa[HB][2][L], pdb[HB][2][L];
+    float rowp[HB][2][L], colp[HB][4][L];
+    float red[HB][NTG / 64];
+    // per value head of a batch, loaded when the batch starts: the per-step
+    // gamma, e^g, e^{gL-g}, beta and l, the scalars e^{gamma_L}, A_log and
+    // dt_bias, a (fp32) and the mask (1 = valid step)
     alignas(16) float bsc[HB][5][L];  // rows: gamma, e^g, e^{gL-g}, beta, l (0 past the end)
-    float hu[HB][L], hb[HB][L], hdb[HB][L], hell[HB][L], hdh[HB], hegl[HB], hal[HB], hdt[HB];
+    float hegl[HB], hal[HB], hdt[HB];
     float ha[HB][L], hm[HB][L];
   };
   struct Ctx {
@@ -1045,7 +1047,7 @@ struct ChunkBwdGrad {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float v = row_sum16(ac.pb[r]);
-          if (q.lr == 0) sm.bv[q.hw][q.tc0 + r] = v;
+          if (q.lr == 0) sm.bv[slot][q.hw][q.tc0 + r] = v;
         }
         float pa = ac.pa, pdb = ac.pdb;
         pa += __shfl_xor(pa, 16);
@@ -1053,11 +1055,11 @@ struct ChunkBwdGrad {
         pdb += __shfl_xor(pdb, 16);
         pdb += __shfl_xor(pdb, 32);
         if (q.lg == 0) {
-          sm.pa[q.hw][q.ta] = pa;
-          sm.pdb[q.hw][q.ta] = pdb;
+          sm.pa[slot][q.hw][q.ta] = pa;
+          sm.pdb[slot][q.hw][q.ta] = pdb;
         }
         const float phdh = wave_sum(ac.phdh);
-        if (q.l == 0) sm.red[q.w] = phdh;
+        if (q.l == 0) sm.red[slot][q.w] = phdh;
 
         const int tc0 = q.tc0;
         const float* gam = sm.bsc[slot][0];
@@ -1092,38 +1094,17 @@ struct ChunkBwdGrad {
           // column b: the lane's four rows, then the wave's four row groups
           colp += __shfl_xor(colp, 16);
           colp += __shfl_xor(colp, 32);
-          if (q.lg == 0) sm.colp[q.tt][b] = colp;
+          if (q.lg == 0) sm.colp[slot][q.tt][b] = colp;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float v = row_sum16(rowp[r]);
-          if (q.lr == 0) sm.rowp[q.hw][tc0 + r] = v;
-        }
-      }
-      __syncthreads();
-      // ---- this head's inputs of the deferred gate-gradient section
-      {
-        const Lanes q;
-        if (q.tid < L) {
-          const int s = q.tid;
-          const bool in = s < Lc;
-          const float beta = sm.bsc[slot][3][s];
-          const float av = in ? sm.bsc[slot][2][s] * beta * sm.rk[s] * (sm.pa[0][s] + sm.pa[1][s]) : 0.f;
-          const float csum = (sm.colp[0][s] + sm.colp[1][s]) + (sm.colp[2][s] + sm.colp[3][s]);
-          sm.hu[slot][s] = av + (csum - (sm.rowp[0][s] + sm.rowp[1][s]));
-          sm.hb[slot][s] = in ? sm.bv[0][s] + sm.bv[1][s] : 0.f;
-          sm.hdb[slot][s] = (sm.pdb[0][s] + sm.pdb[1][s]) * (1.f - beta);
-          sm.hell[slot][s] = sm.bsc[slot][4][s];
-        }
-        if (q.tid == 64) {
-          float hdh = 0.f;
-#pragma unroll
-          for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[i];
-          sm.hdh[slot] = hdh;
+          if (q.lr == 0) sm.rowp[slot][q.hw][tc0 + r] = v;
         }
       }
       // ---- deferred section, one wave per value head of the batch:
       // dl_t = e^{gL} <dH', H> + sum_{u<t} (a_u + cs_u - rs_u) + sum_{r>=t} b_r; da, db
+      // (cs, rs: the column and row sums of E)
       if (slot == HB - 1 || hh == G - 1) {
         __syncthreads();
         const Lanes q;
@@ -1133,18 +1114,27 @@ struct ChunkBwdGrad {
           const bool in = t < Lc;
           const float av = sm.ha[k][t];
           const bool valid = sm.hm[k][t] != 0.f;
+          const float beta = sm.bsc[k][3][t];
+          const float as = in ? sm.bsc[k][2][t] * beta * sm.rk[t] * (sm.pa[k][0][t] + sm.pa[k][1][t]) : 0.f;
+          const float csum = (sm.colp[k][0][t] + sm.colp[k][1][t]) + (sm.colp[k][2][t] + sm.colp[k][3][t]);
+          const float hu = as + (csum - (sm.rowp[k][0][t] + sm.rowp[k][1][t]));
+          const float hbr = in ? sm.bv[k][0][t] + sm.bv[k][1][t] : 0.f;
+          float hdh = 0.f;
+#pragma unroll
+          for (int i = 0; i < NTG / 64; ++i) hdh += sm.red[k][i];
           // sum over u < t: the prefix sum of the terms shifted by one step;
           // sum over r >= t: the prefix sum of the terms in reverse order,
           // taken back from lane 63 - t
-          const float pre = wave_prefix_sum(t > 0 ? sm.hu[k][t - 1] : 0.f);
-          const float suf = __shfl(wave_prefix_sum(sm.hb[k][L - 1 - t]), L - 1 - t);
-          const float ell = sm.hell[k][t];
-          const float dl = expf(ell) == 0.f ? 0.f : sm.hegl[k] * sm.hdh[k] + pre + suf;
+          const float hus = __shfl_up(hu, 1);
+          const float pre = wave_prefix_sum(t > 0 ? hus : 0.f);
+          const float suf = __shfl(wave_prefix_sum(__shfl(hbr, L - 1 - t)), L - 1 - t);
+          const float ell = sm.bsc[k][4][t];
+          const float dl = expf(ell) == 0.f ? 0.f : sm.hegl[k] * hdh + pre + suf;
           float da = 0.f, db = 0.f, dll = 0.f;
           if (in && valid) {
             const float xa = av + sm.hdt[k];
             da = xa <= kClamp ? dl * (-expf(sm.hal[k])) * sigmoid_f(fminf(xa, kClamp)) : 0.f;
-            db = sm.hdb[k][t];
+            db = (sm.pdb[k][0][t] + sm.pdb[k][1][t]) * (1.f - beta);
             dll = dl != 0.f ? dl * ell : 0.f;
           }
           // steps past the end of the sequence fall outside the descriptors
