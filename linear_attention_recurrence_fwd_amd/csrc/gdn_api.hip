@@ -347,7 +347,7 @@ VgLayout vg_layout(const Dims& d, bool bwd, bool chunk, bool saved) {
   if (bwd && chunk) {  // dH', and the value heads' parts of the row gradients
     const size_t nc = d.nchunk();
     L.dHend = take((nc * d.B * d.Hv * static_cast<size_t>(d.Dk) * d.Dv + 1) / 2);
-    L.part = take(bt * d.Hv * 2 * d.Dk);
+    L.part = take((bt * d.Hv * 2 * d.Dk + 1) / 2);  // bf16
   } else if (bwd) {
     const size_t ns = gdn::vg_nslice(d.Dv);
     L.sub = take(gdn::vg_sub_floats(d));
@@ -808,7 +808,7 @@ int gdn_bwd_vg(const gdn_dims* d, const void* q, const void* k, const void* v, c
     if (!launch(st, [&] { return gdn::launch_chunk_bwd_state(ba, st); })) return GDN_ERR_HIP;
     gdn::VgChunkGradArgs ga{dd, q, k, v, b, dO, lg, mask, state0, ckpt, s, cb, dHend, dv,
                             saved ? cb.X : at<gdn::bf16>(ws, L.X), at<gdn::bf16>(ws, L.dPA),
-                            at<float>(ws, L.part), dq, dk, db, dlg, saved ? 1 : 0};
+                            at<gdn::bf16>(ws, L.part), dq, dk, db, dlg, saved ? 1 : 0};
     if (!launch(st, [&] { return gdn::launch_vg_chunk_x(ga, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_vg_chunk_grad(ga, st); })) return GDN_ERR_HIP;
     if (!launch(st, [&] { return gdn::launch_vg_norm_bwd(ga, st); })) return GDN_ERR_HIP;

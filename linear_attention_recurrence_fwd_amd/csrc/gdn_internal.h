@@ -212,7 +212,7 @@ struct VgChunkGradArgs {
   const void* dv;              // [B,T,Hv,Dv] dv (= Ehat) from the reverse state pass
   bf16* X;                     // [B,T,Hv,Dv] X_t = v_t - u_t of every step
   bf16* dPA;                   // [B*Hv, NC, 2, L, L] dP, dA
-  float* qk;                   // [B,T,Hv,2,Dk] each value head's parts of the rows of d(s qn), d(kn)
+  bf16* qk;                    // [B,T,Hv,2,Dk] each value head's parts of the rows of d(s qn), d(kn), bf16
   void *dq, *dk, *db;          // outputs (input dtype)
   float* dlg;                  // [B,T,Hv,Dk]
   int xsv = 0;                 // X is the forward's saved copy (vg_chunk_x does not recompute it)

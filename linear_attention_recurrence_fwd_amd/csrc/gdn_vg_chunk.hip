@@ -1229,9 +1229,9 @@ struct VgG {
       for (int r = 0; r < 4; ++r) {
         const int t = tr0 + r;
         if (t < Lc) {
-          float* dst = p.qk + (vrow0 + static_cast<size_t>(t) * d.Hv) * 2 * DK + ch0 + 16 * tile + lr;
-          dst[0] = dqv[tile][r];
-          dst[DK] = dknv[tile][r];
+          bf16* dst = p.qk + (vrow0 + static_cast<size_t>(t) * d.Hv) * 2 * DK + ch0 + 16 * tile + lr;
+          dst[0] = bf16_of(dqv[tile][r]);
+          dst[DK] = bf16_of(dknv[tile][r]);
         }
       }
   }
@@ -1255,15 +1255,15 @@ __global__ void __launch_bounds__(64) vg_norm_bwd_kernel(VgChunkGradArgs p) {
   const bf16* qg = static_cast<const bf16*>(p.q) + row * DK;
   const bf16* kg = static_cast<const bf16*>(p.k) + row * DK;
   const int G = d.G();
-  const float* gq = p.qk + row * G * 2 * DK;  // rows (b t) Hv + j G + hh
+  const bf16* gq = p.qk + row * G * 2 * DK;  // rows (b t) Hv + j G + hh
   float qh[RM], kn[RM], dq[RM], dk[RM], pq = 0.f, pk = 0.f;
 #pragma unroll
   for (int m = 0; m < RM; ++m) dq[m] = dk[m] = 0.f;
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
     for (int m = 0; m < RM; ++m) {
-      dq[m] += gq[hh * 2 * DK + lane + 64 * m];
-      dk[m] += gq[hh * 2 * DK + DK + lane + 64 * m];
+      dq[m] += to_f32(gq[hh * 2 * DK + lane + 64 * m]);
+      dk[m] += to_f32(gq[hh * 2 * DK + DK + lane + 64 * m]);
     }
 #pragma unroll
   for (int m = 0; m < RM; ++m) {

@@ -127,7 +127,7 @@ void touch_vg_grad(const VgChunkGradArgs& a) {
   if (a.cb.Hb == nullptr) touch_ckpt(a.d, a.ckpt);  // else the bf16 states of the saved record (touch_chunk)
   touch(a.X, bt(a.d) * a.d.Hv * a.d.Dv * 2);
   touch(a.dPA, nmat(a.d) * 2 * 64 * 64 * 2);
-  touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 4);
+  touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 2);
   ++g_launches;
 }
 hipError_t launch_vg_chunk_x(const VgChunkGradArgs& a, hipStream_t) {
@@ -139,7 +139,7 @@ hipError_t launch_vg_chunk_grad(const VgChunkGradArgs& a, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_vg_norm_bwd(const VgChunkGradArgs& a, hipStream_t) {
-  touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 4);
+  touch(a.qk, bt(a.d) * a.d.Hv * 2 * a.d.Dk * 2);
   ++g_launches;
   return hipSuccess;
 }
