@@ -892,15 +892,29 @@ struct ChunkBwdGrad {
     const bf16* kc = static_cast<const bf16*>(p.k) + qk0 * DK;
     const bf16* qc = static_cast<const bf16*>(p.q) + qk0 * DK;
     const int tid0 = threadIdx.x;
-    // the first batch of value heads' scalars, and the norm factors (the same
-    // for every value head of the group; 0 past the end)
-    load_batch(p, x, sm, 0);
+    // The chunk's k and q rows (KQL: coalesced, for LDS), the norm factors
+    // (the same for every value head of the group; 0 past the end) and the
+    // first batch of value heads' scalars: all issued before any is waited
+    // for, so that their latencies overlap.
+    constexpr int NPT = KQL ? L * DK / 8 / NTG : 1;
+    static_assert(!KQL || L * DK / 8 % NTG == 0, "whole pieces per thread");
+    uint4 kv[NPT], qv[NPT];
+    if constexpr (KQL) {
+#pragma unroll
+      for (int u = 0; u < NPT; ++u) {
+        const int pc = tid0 + u * NTG, row = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
+        const uint32_t o = static_cast<uint32_t>(min(row, x.tl)) * qk_row + c8;
+        kv[u] = *reinterpret_cast<const uint4*>(kc + o);
+        qv[u] = *reinterpret_cast<const uint4*>(qc + o);
+      }
+    }
     float rk0, rq0;
     {
       const float* scc = p.cb.sc + (static_cast<size_t>(x.b * d.Hv + x.j * G) * NC + c) * SC_ROWS * L;
       rk0 = scc[SC_RK * L + (tid0 & 63)];
       rq0 = scc[SC_RQ * L + (tid0 & 63)];
     }
+    load_batch(p, x, sm, 0);
     f32x4 accQ[IH], accK[IH];
 #pragma unroll
     for (int k = 0; k < IH; ++k) accQ[k] = accK[k] = f4zero();
@@ -922,18 +936,8 @@ struct ChunkBwdGrad {
       // space of the weight tiles, q rows in ring slot 2); every wave reads
       // its operands (k and q rows of its row tile, k rows of its two Gram
       // column tiles) from there in the matrix-core layout.
-      constexpr int NP = L * DK / 8, NPT = NP / NTG;
-      static_assert(NP % NTG == 0, "whole pieces per thread");
       bf16* ks = reinterpret_cast<bf16*>(&sm.wt);
       bf16* qs = reinterpret_cast<bf16*>(&sm.u.r.s[2]);
-      uint4 kv[NPT], qv[NPT];
-#pragma unroll
-      for (int u = 0; u < NPT; ++u) {
-        const int pc = tid0 + u * NTG, row = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
-        const uint32_t o = static_cast<uint32_t>(min(row, x.tl)) * qk_row + c8;
-        kv[u] = *reinterpret_cast<const uint4*>(kc + o);
-        qv[u] = *reinterpret_cast<const uint4*>(qc + o);
-      }
 #pragma unroll
       for (int u = 0; u < NPT; ++u) {
         const int pc = tid0 + u * NTG, row = pc / (DK / 8), c8 = 8 * (pc % (DK / 8));
