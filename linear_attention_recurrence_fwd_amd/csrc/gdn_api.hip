@@ -212,6 +212,16 @@ int tpar_seg(const gdn_dims* p, const Dims& d) {
 bool use_chunk_bwd(const gdn_dims* p) { return use_chunk(p); }
 // The chunk matrices go through the checkpoint tail.
 bool use_saved(const gdn_dims* p) { return p->save != 0 && use_chunk(p); }
+// Whether the state passes store the bf16 chunk-start states and dH'
+// non-temporal: when the backward's hand-off (those two, and the dO, dv and X
+// rows it reads with them) exceeds the 256 MB memory-side cache, it cannot
+// stay there anyway, and dirty lines of it held in the caches slow the
+// reverse state pass's chain.
+bool stream_handoff(const Dims& d) {
+  const double states = static_cast<double>(d.nchunk()) * d.B * d.Hv * d.Dk * d.Dv * 2;
+  const double rows = 3.0 * d.B * d.T * d.Hv * d.Dv * 2;
+  return 2 * states + rows > 256.0 * 1024 * 1024;
+}
 
 gdn::ChunkBufs chunk_bufs(void* ws, const Layout& L, bool bwd) {
   gdn::ChunkBufs cb{};
@@ -513,6 +523,7 @@ int fwd_launch(const gdn_dims* d, const Dims& dd, const FwdRoute& R, const void*
     if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
     // under save the states go to the checkpoint buffer as bf16 only
     gdn::ChunkFwdArgs fa{dd, q, k, v, state0, cb, o, state_out, save ? nullptr : ckpt};
+    fa.stream = stream_handoff(dd);
     if (tseg) {  // T-parallel: segment maps, their chain, then every segment's outputs
       const int nseg = gdn::tpar_nseg(dd, tseg);
       float* maps = at<float>(ws, L.maps);
@@ -652,6 +663,7 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,
                          at<gdn::bf16>(ws, L.dHend),
                          dq, dk, dv, da, db, dstate, at<double>(ws, L.pdA), at<double>(ws, L.pdt)};
+    ba.stream = stream_handoff(dd);
     if (tseg) {  // T-parallel reverse pass: segment maps, their chain (last to first), then the segments
       const int nseg = gdn::tpar_nseg(dd, tseg);
       float* maps = at<float>(ws, L.maps);

@@ -59,7 +59,8 @@ constexpr int L = kChunk;
 
 // ------------------------------------------------------- reverse state pass
 
-template <int DK, bool VG = false>
+// ST: dH' is stored non-temporal (ChunkBwdArgs::stream).
+template <int DK, bool VG = false, bool ST = false>
 struct ChunkBwdState {
   // Eight waves in two groups of four (w = wave index within the group):
   //   A (waves 0-3): for row tile w of the chunk, the dependent chain
@@ -343,7 +344,10 @@ struct ChunkBwdState {
     lds_barrier();  // Y
     load_b(p, q, cn, nxt);  // the next chunk's Q^T, issued while waiting for Ehat
     lds_barrier();  // Z: Ehat complete
-    {  // map mode: an empty descriptor, nothing stored
+    {  // map mode: an empty descriptor, nothing stored.  Non-temporal under
+       // ST (the hand-off does not fit the memory-side cache):
+       // only the gradient pass reads dH', after this kernel, and dirty lines
+       // held in the caches then cost this chain more than that pass gains
       const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv,
                                    q.mode == 0 ? static_cast<size_t>(DK) * d.Dv * 2 : 0);
       const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + (lr >> 2)) * d.Dv + q.col0 + 4 * (lr & 3));
@@ -351,7 +355,10 @@ struct ChunkBwdState {
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
-          buf_store_u2(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), quads_to_rows(dhp[it][ct]));
+          if constexpr (ST)
+            buf_store_u2_nt(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), quads_to_rows(dhp[it][ct]));
+          else
+            buf_store_u2(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), quads_to_rows(dhp[it][ct]));
     }
     // dH -= K^T diag(e^g rk) Ehat, K^T read transposed from the ring's k tile
 #pragma unroll
@@ -490,10 +497,10 @@ struct ChunkBwdState {
   }
 };
 
-template <int DK, bool VG>
+template <int DK, bool VG, bool ST = false>
 __global__ void __launch_bounds__(512) chunk_bwd_state_kernel(ChunkBwdArgs p) {
-  __shared__ typename ChunkBwdState<DK, VG>::Smem sm;
-  ChunkBwdState<DK, VG>::run(p, sm);
+  __shared__ typename ChunkBwdState<DK, VG, ST>::Smem sm;
+  ChunkBwdState<DK, VG, ST>::run(p, sm);
 }
 
 // ------------------------------------------------------------ gradient pass
@@ -1327,13 +1334,21 @@ hipError_t launch_chunk_bwd_state(const ChunkBwdArgs& a, hipStream_t st) {
     }
     return hipGetLastError();
   }
+#define GDN_BWD_CASE(D)                                                                \
+  case D:                                                                              \
+    if (a.stream)                                                                      \
+      chunk_bwd_state_kernel<D, false, true><<<nblk, ChunkBwdState<D>::NTS, 0, st>>>(a);  \
+    else                                                                               \
+      chunk_bwd_state_kernel<D, false, false><<<nblk, ChunkBwdState<D>::NTS, 0, st>>>(a); \
+    break;
   switch (a.d.Dk) {
-    case 64: chunk_bwd_state_kernel<64, false><<<nblk, ChunkBwdState<64>::NTS, 0, st>>>(a); break;
-    case 128: chunk_bwd_state_kernel<128, false><<<nblk, ChunkBwdState<128>::NTS, 0, st>>>(a); break;
-    case 192: chunk_bwd_state_kernel<192, false><<<nblk, ChunkBwdState<192>::NTS, 0, st>>>(a); break;
-    case 256: chunk_bwd_state_kernel<256, false><<<nblk, ChunkBwdState<256>::NTS, 0, st>>>(a); break;
+    GDN_BWD_CASE(64)
+    GDN_BWD_CASE(128)
+    GDN_BWD_CASE(192)
+    GDN_BWD_CASE(256)
     default: return hipErrorInvalidValue;
   }
+#undef GDN_BWD_CASE
   return hipGetLastError();
 }
 

@@ -301,7 +301,8 @@ __global__ void __launch_bounds__(NT) chunk_prep_kernel(ChunkPrepArgs p) {
 
 // ------------------------------------------------------------ state pass
 
-template <int DK, bool VG = false>
+// ST: the bf16 chunk-start states are stored non-temporal (ChunkFwdArgs::stream).
+template <int DK, bool VG = false, bool ST = false>
 struct ChunkFwd {
   // Twelve waves in three groups of four (w = wave index within the group):
   //   A (waves 0-3):  K H, R and X = Tx R for row tile w.  A also streams the
@@ -601,7 +602,11 @@ struct ChunkFwd {
   // bf16 copy of H as the state at the start of chunk `slot` ([i][v] rows;
   // dropped when slot < 0).  A quad transpose gives each lane four
   // consecutive columns of one row, quads_to_rows one row per quad of lanes:
-  // one coalesced 8-byte store per tile.
+  // one coalesced 8-byte store per tile.  Non-temporal under ST (the
+  // backward's hand-off does not fit the memory-side cache): nothing in
+  // the forward reads them again, and as plain writes they would stay dirty in
+  // the caches until the reverse state pass, whose chain then pays for their
+  // write-back.
   __device__ static void store_hb(const ChunkFwdArgs& p, const Lane& q, const f32x4 (&H)[RTW][2], int slot) {
     const Dims& d = p.d;
     const size_t hsz = static_cast<size_t>(DK) * d.Dv;
@@ -613,7 +618,11 @@ struct ChunkFwd {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const f32x4 tr = quad_transpose(H[it][ct]);
-        buf_store_u2(r, o + 2 * (16 * it * d.Dv + 16 * ct), quads_to_rows(pack4_bf16(tr[0], tr[1], tr[2], tr[3])));
+        const uint2 v = quads_to_rows(pack4_bf16(tr[0], tr[1], tr[2], tr[3]));
+        if constexpr (ST)
+          buf_store_u2_nt(r, o + 2 * (16 * it * d.Dv + 16 * ct), v);
+        else
+          buf_store_u2(r, o + 2 * (16 * it * d.Dv + 16 * ct), v);
       }
   }
 
@@ -799,10 +808,10 @@ struct ChunkFwd {
   }
 };
 
-template <int DK, bool VG>
+template <int DK, bool VG, bool ST = false>
 __global__ void __launch_bounds__(768) chunk_fwd_kernel(ChunkFwdArgs p) {
-  __shared__ typename ChunkFwd<DK, VG>::Smem sm;
-  ChunkFwd<DK, VG>::run(p, sm);
+  __shared__ typename ChunkFwd<DK, VG, ST>::Smem sm;
+  ChunkFwd<DK, VG, ST>::run(p, sm);
 }
 
 // ------------------------------------------------ T-parallel segment chain
@@ -954,13 +963,21 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs& a, hipStream_t st) {
     }
     return hipGetLastError();
   }
+#define GDN_FWD_CASE(D)                                                      \
+  case D:                                                                    \
+    if (a.stream)                                                            \
+      chunk_fwd_kernel<D, false, true><<<nblk, ChunkFwd<D>::NTS, 0, st>>>(a);  \
+    else                                                                     \
+      chunk_fwd_kernel<D, false, false><<<nblk, ChunkFwd<D>::NTS, 0, st>>>(a); \
+    break;
   switch (a.d.Dk) {
-    case 64: chunk_fwd_kernel<64, false><<<nblk, ChunkFwd<64>::NTS, 0, st>>>(a); break;
-    case 128: chunk_fwd_kernel<128, false><<<nblk, ChunkFwd<128>::NTS, 0, st>>>(a); break;
-    case 192: chunk_fwd_kernel<192, false><<<nblk, ChunkFwd<192>::NTS, 0, st>>>(a); break;
-    case 256: chunk_fwd_kernel<256, false><<<nblk, ChunkFwd<256>::NTS, 0, st>>>(a); break;
+    GDN_FWD_CASE(64)
+    GDN_FWD_CASE(128)
+    GDN_FWD_CASE(192)
+    GDN_FWD_CASE(256)
     default: return hipErrorInvalidValue;
   }
+#undef GDN_FWD_CASE
   return hipGetLastError();
 }
 

@@ -247,6 +247,7 @@ struct ChunkFwdArgs {
   float* maps;
   const bf16* vzero;
   int vg;  // 1: per-key-channel gate (operands Kb, Kh, Qb and vsc of cb)
+  int stream;  // 1: the bf16 chunk-start states are stored non-temporal (scalar gate)
 };
 // Start states of the segments: H_{s+1} = A_s H_s + B_s over the segment maps.
 struct SegChainArgs {
@@ -284,6 +285,7 @@ struct ChunkBwdArgs {
   float* maps;
   const bf16* vzero;
   int vg;  // 1: per-key-channel gate (operands Kh, KbT, QbT and vsc of cb)
+  int stream;  // 1: dH' is stored non-temporal (scalar gate)
 };
 
 // bf16 copies of the states at the chunk starts from the fp32 checkpoints:
