@@ -657,7 +657,7 @@ int gdn_bwd(const gdn_dims* d, const void* q, const void* k, const void* v, cons
       gdn::ChunkPrepArgs ca{dd, q, k, a, b, A_log, dt_bias, mask, cb, 1};
       if (!launch(st, [&] { return gdn::launch_chunk_prep(ca, st); })) return GDN_ERR_HIP;
       cb.Hb = at<gdn::bf16>(ws, L.HB);
-      gdn::StateBf16Args sa{dd.nchunk(), static_cast<size_t>(dd.B) * dd.Hv * dd.Dk * dd.Dv, state0, ckpt, cb.Hb};
+      gdn::StateBf16Args sa{dd.nchunk(), static_cast<size_t>(dd.B) * dd.Hv * dd.Dk * dd.Dv, dd.Dk, dd.Dv, state0, ckpt, cb.Hb};
       if (!launch(st, [&] { return gdn::launch_state_bf16(sa, st); })) return GDN_ERR_HIP;
     }
     gdn::ChunkBwdArgs ba{dd, q, k, v, dO, a, A_log, dt_bias, mask, state0, ckpt, dS_final, cb,

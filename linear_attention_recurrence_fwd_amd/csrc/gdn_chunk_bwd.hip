@@ -289,10 +289,10 @@ struct ChunkBwdState {
     const Dims& d = p.d;
     const int lr = q.lr, lg = q.lg;
     const Slot& s = sm.ring[c & 1];
-    // dH' of this chunk for the gradient pass: [i][v], bf16, the layout of the
-    // checkpoints; a transpose inside each quad of lanes gives every lane 4
-    // consecutive columns of one row, and quads_to_rows one row per quad
-    // (coalesced stores).  Packed now, stored after barrier Z:
+    // dH' of this chunk for the gradient pass, bf16 (the hand-off layout, or
+    // row-major [i][v] with the per-key-channel gate); a transpose inside each
+    // quad of lanes gives every lane 4 consecutive columns of one row, and
+    // quads_to_rows one row per quad (coalesced stores).  Packed now, stored after barrier Z:
     // stores issued here would wait behind group A's ring loads and hold up
     // the products below.
     uint2 dhp[RTW][2];
@@ -350,15 +350,21 @@ struct ChunkBwdState {
        // held in the caches then cost this chain more than that pass gains
       const rsrc_t rdh = make_rsrc(p.dHend + (static_cast<size_t>(c) * d.B * d.Hv + q.bh) * DK * d.Dv,
                                    q.mode == 0 ? static_cast<size_t>(DK) * d.Dv * 2 : 0);
-      const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * lg + (lr >> 2)) * d.Dv + q.col0 + 4 * (lr & 3));
+      // the scalar gate's hand-off layout (hand_off); row-major [i][v] blocks
+      // for the per-key-channel gate
+      const int r16 = 4 * lg + (lr >> 2), c4 = 4 * (lr & 3);
+      const uint32_t o = VG ? 2 * (static_cast<uint32_t>(16 * q.w * RTW + r16) * d.Dv + q.col0 + c4)
+                            : 2 * hand_off(DK, 16 * q.w * RTW + r16, q.col0 + c4);
 #pragma unroll
       for (int it = 0; it < RTW; ++it)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 2; ++ct) {
+          const uint32_t ot = o + 2 * (VG ? static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct : 512 * it + 256 * ct);
           if constexpr (ST)
-            buf_store_u2_nt(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), quads_to_rows(dhp[it][ct]));
+            buf_store_u2_nt(rdh, ot, quads_to_rows(dhp[it][ct]));
           else
-            buf_store_u2(rdh, o + 2 * (static_cast<uint32_t>(16 * it) * d.Dv + 16 * ct), quads_to_rows(dhp[it][ct]));
+            buf_store_u2(rdh, ot, quads_to_rows(dhp[it][ct]));
+        }
     }
     // dH -= K^T diag(e^g rk) Ehat, K^T read transposed from the ring's k tile
 #pragma unroll
@@ -617,7 +623,8 @@ struct ChunkBwdGrad {
   // columns 32 (n % nsl) ..) into ring slot n % NSLOT.  Load jb of the slab
   // (wave jb % 8) covers 64 pieces: H (jb < HJ) or dH' (jb < 2 HJ) rows
   // 16 jb' .. + 15, or rows 16 b' .. + 15 of tile (jb - 2 HJ) / 4.  H is the
-  // bf16 copy of the state at the chunk's start, in the layout of dH'; tile
+  // bf16 copy of the state at the chunk's start, in the hand-off layout of dH'
+  // (hand_off: each of these loads reads 1 KB of contiguous memory); tile
   // rows past the end of the sequence are clamped to the last.
   __device__ static void issue_slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n) {
     const Dims& d = p.d;
@@ -638,7 +645,7 @@ struct ChunkBwdGrad {
         const bool isd = jb >= HJ;
         const int blk = isd ? jb - HJ : jb;
         const int ps = 64 * blk + l, i = ps >> 2;
-        const uint32_t o = 2 * static_cast<uint32_t>(i * d.Dv + v0 + 8 * ((ps & 3) ^ sw(i)));
+        const uint32_t o = 2 * hand_off(DK, i, v0 + 8 * ((ps & 3) ^ sw(i)));
         if (isd)
           dma16(raw_desc(p.dHend + so, hsz * 2), &s.dhv[512 * blk], o);
         else
@@ -1305,7 +1312,11 @@ __global__ void __launch_bounds__(256) state_bf16_kernel(StateBf16Args a) {
       x0 = *reinterpret_cast<const float4*>(src + e);
       x1 = *reinterpret_cast<const float4*>(src + e + 4);
     }
-    *reinterpret_cast<uint4*>(a.Hb + sl * a.slot + e) =
+    // into the hand-off layout of the (chunk, head) block (8 columns of a row
+    // stay contiguous there)
+    const size_t blk = static_cast<size_t>(a.dk) * a.dv, bh = e / blk;
+    const int i = static_cast<int>((e % blk) / a.dv), v = static_cast<int>(e % a.dv);
+    *reinterpret_cast<uint4*>(a.Hb + sl * a.slot + bh * blk + hand_off(a.dk, i, v)) =
         make_uint4(pack2_bf16(x0.x, x0.y), pack2_bf16(x0.z, x0.w), pack2_bf16(x1.x, x1.y), pack2_bf16(x1.z, x1.w));
   }
 }

@@ -599,10 +599,11 @@ struct ChunkFwd {
     }
   }
 
-  // bf16 copy of H as the state at the start of chunk `slot` ([i][v] rows;
-  // dropped when slot < 0).  A quad transpose gives each lane four
+  // bf16 copy of H as the state at the start of chunk `slot` (dropped when
+  // slot < 0), in the hand-off layout of gdn_internal.h (row-major [i][v] with
+  // the per-key-channel gate).  A quad transpose gives each lane four
   // consecutive columns of one row, quads_to_rows one row per quad of lanes:
-  // one coalesced 8-byte store per tile.  Non-temporal under ST (the
+  // each store covers a 16 x 16 tile, 512 contiguous bytes.  Non-temporal under ST (the
   // backward's hand-off does not fit the memory-side cache): nothing in
   // the forward reads them again, and as plain writes they would stay dirty in
   // the caches until the reverse state pass, whose chain then pays for their
@@ -612,17 +613,22 @@ struct ChunkFwd {
     const size_t hsz = static_cast<size_t>(DK) * d.Dv;
     const rsrc_t r = make_rsrc(p.cb.Hb + (static_cast<size_t>(max(slot, 0)) * d.B * d.Hv + q.bh) * hsz,
                                slot >= 0 ? hsz * 2 : 0);
-    const uint32_t o = 2 * (static_cast<uint32_t>(16 * q.w * RTW + 4 * q.lg + (q.lr >> 2)) * d.Dv + q.col0 + 4 * (q.lr & 3));
+    // row 16 (w RTW + it) + 4 lg + lr / 4, columns col0 + 16 ct + 4 (lr % 4) ..;
+    // the per-key-channel gate keeps row-major [i][v] blocks
+    const int r16 = 4 * q.lg + (q.lr >> 2), c4 = 4 * (q.lr & 3);
+    const uint32_t o = VG ? 2 * (static_cast<uint32_t>(16 * q.w * RTW + r16) * d.Dv + q.col0 + c4)
+                          : 2 * hand_off(DK, 16 * q.w * RTW + r16, q.col0 + c4);
 #pragma unroll
     for (int it = 0; it < RTW; ++it)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const f32x4 tr = quad_transpose(H[it][ct]);
         const uint2 v = quads_to_rows(pack4_bf16(tr[0], tr[1], tr[2], tr[3]));
+        const uint32_t ot = o + 2 * (VG ? 16 * it * d.Dv + 16 * ct : 512 * it + 256 * ct);
         if constexpr (ST)
-          buf_store_u2_nt(r, o + 2 * (16 * it * d.Dv + 16 * ct), v);
+          buf_store_u2_nt(r, ot, v);
         else
-          buf_store_u2(r, o + 2 * (16 * it * d.Dv + 16 * ct), v);
+          buf_store_u2(r, ot, v);
       }
   }
 

@@ -154,6 +154,17 @@ enum : int {
 // Block index -> (b, h, slice).  Blocks of one (batch, key head) group go to
 // one XCD when the group count is a multiple of the XCD count (8); workgroups
 // are dealt to the XCDs round-robin in launch order.
+// The scalar-gate chunk form's bf16 hand-off from the state passes to the
+// gradient pass (the chunk-start states and dH', each a Dk x Dv block per
+// (chunk, value head)) is stored tile by tile: the 32-column slices one after
+// another, each in groups of 16 rows, each group as its two 16 x 16 tiles
+// (columns 0-15, then 16-31) with rows of 16 elements.  A store of 16 rows x
+// 16 columns and a load of 16 rows x 32 columns then each cover contiguous
+// memory (512 B, 1 KB).  Element offset of (i, v) within the block:
+__device__ __forceinline__ uint32_t hand_off(int dk, int i, int v) {
+  return static_cast<uint32_t>((v >> 5) * dk * 32 + (i >> 4) * 512 + ((v >> 4) & 1) * 256 + (i & 15) * 16 + (v & 15));
+}
+
 __device__ inline void block_coords(const Dims& d, int nslice, int& b, int& h, int& slice) {
   const int n = blockIdx.x, G = d.G(), groups = d.B * d.Hk, per = G * nslice;
   int g, r;
@@ -293,6 +304,7 @@ struct ChunkBwdArgs {
 struct StateBf16Args {
   int nslot;            // chunks
   size_t slot;          // elements per slot (B*Hv*Dk*Dv, a multiple of 8)
+  int dk, dv;           // the block of one head is Dk x Dv (written in the hand-off layout)
   const float *state0, *ckpt;
   bf16* Hb;
 };
