@@ -625,7 +625,8 @@ struct ChunkBwdGrad {
   // 16 jb' .. + 15, or rows 16 b' .. + 15 of tile (jb - 2 HJ) / 4.  H is the
   // bf16 copy of the state at the chunk's start, in the hand-off layout of dH'
   // (hand_off: each of these loads reads 1 KB of contiguous memory); tile
-  // rows past the end of the sequence are clamped to the last.
+  // rows past the end of the sequence are clamped to the last.  Every slab is
+  // read by this workgroup only, once: the loads are non-temporal.
   __device__ static void issue_slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n) {
     const Dims& d = p.d;
     const int nsl = d.Dv / NS;
@@ -647,16 +648,16 @@ struct ChunkBwdGrad {
         const int ps = 64 * blk + l, i = ps >> 2;
         const uint32_t o = 2 * hand_off(DK, i, v0 + 8 * ((ps & 3) ^ sw(i)));
         if (isd)
-          dma16(raw_desc(p.dHend + so, hsz * 2), &s.dhv[512 * blk], o);
+          dma16_nt(raw_desc(p.dHend + so, hsz * 2), &s.dhv[512 * blk], o);
         else
-          dma16(raw_desc(p.cb.Hb + so, hsz * 2), &s.hv[512 * blk], o);
+          dma16_nt(raw_desc(p.cb.Hb + so, hsz * 2), &s.hv[512 * blk], o);
       } else if (jb < NJ) {
         const int u = jb - 2 * HJ, ten = u >> 2, blk = u & 3;
         const int t = 16 * blk + (l >> 2);
         const uint32_t o = 2 * (static_cast<uint32_t>(min(t, x.tl)) * x.v_row + v0 + 8 * ((l & 3) ^ sw(t)));
         const bf16* src = ten == 0 ? (XSV ? p.cb.X : static_cast<const bf16*>(p.v))
                           : ten == 1 ? static_cast<const bf16*>(p.dO) : static_cast<const bf16*>(p.dv);
-        dma16(raw_desc(src + vbase, vbytes), &s.vt[ten][512 * blk], o);
+        dma16_nt(raw_desc(src + vbase, vbytes), &s.vt[ten][512 * blk], o);
       }
     }
   }

@@ -327,6 +327,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(const i32x4& r, const void* lds, uint32_t off) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
 }
+// The same load marked non-temporal: data read once, which should not
+// displace what other workgroups reuse from the caches.
+__device__ __forceinline__ void dma16_nt(const i32x4& r, const void* lds, uint32_t off) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
+}
 __device__ __forceinline__ void dma4(const i32x4& r, const void* lds, uint32_t off) {
   asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds_addr(lds)) : "memory");
 }
