@@ -625,8 +625,10 @@ struct ChunkBwdGrad {
   // 16 jb' .. + 15, or rows 16 b' .. + 15 of tile (jb - 2 HJ) / 4.  H is the
   // bf16 copy of the state at the chunk's start, in the hand-off layout of dH'
   // (hand_off: each of these loads reads 1 KB of contiguous memory); tile
-  // rows past the end of the sequence are clamped to the last.  Every slab is
-  // read by this workgroup only, once: the loads are non-temporal.
+  // rows past the end of the sequence are clamped to the last.  The H and dH'
+  // tiles are read by this workgroup only, once, as whole lines: their loads
+  // are non-temporal.  The X / dO / dv tiles are 64-byte pieces of rows whose
+  // other half the slab of the next columns reads, so those stay cached.
   __device__ static void issue_slab(const ChunkBwdArgs& p, Smem& sm, const Ctx& x, int n) {
     const Dims& d = p.d;
     const int nsl = d.Dv / NS;
@@ -657,7 +659,7 @@ struct ChunkBwdGrad {
         const uint32_t o = 2 * (static_cast<uint32_t>(min(t, x.tl)) * x.v_row + v0 + 8 * ((l & 3) ^ sw(t)));
         const bf16* src = ten == 0 ? (XSV ? p.cb.X : static_cast<const bf16*>(p.v))
                           : ten == 1 ? static_cast<const bf16*>(p.dO) : static_cast<const bf16*>(p.dv);
-        dma16_nt(raw_desc(src + vbase, vbytes), &s.vt[ten][512 * blk], o);
+        dma16(raw_desc(src + vbase, vbytes), &s.vt[ten][512 * blk], o);
       }
     }
   }

@@ -414,9 +414,9 @@ struct ChunkFwd {
       const int n = 2 * q.w + jj, pos = 64 * n + l, t = pos / 8, pc = (pos % 8) ^ (t & 7);
       dma16(q.dtx, &s.tx[512 * n], 2 * (static_cast<uint32_t>(q.bh * q.NC + c) * L * L + t * L + 8 * pc));
     }
-    {
+    {  // the v slice: read by this workgroup only, once (non-temporal)
       const int pos = 64 * q.w + l, t = pos / 4, pc = (pos % 4) ^ (t & 3);
-      dma16(q.dv, &s.v[512 * q.w],
+      dma16_nt(q.dv, &s.v[512 * q.w],
             2 * (static_cast<uint32_t>(q.b * d.T + t0 + min(t, tl)) * q.vstep + q.vbase + 8 * pc));
     }
     dma4(q.dsc, &s.sc[L * q.w], 4 * (static_cast<uint32_t>(q.bh * q.NC + c) * SCR * L + L * q.w + l));
